@@ -1,0 +1,90 @@
+"""Grouped (per-expert) columnwise NVFP4 over a packed token tensor.
+
+Test infrastructure only.
+
+PR, Grouped allocation tail: the grouped kernels write rows only up to the
+last logical row; storage capacity past it is left untouched and its content
+unspecified. PR, Config surface and AUTO: groups are described by a packed
+tensor plus device-side offsets, with at most 64 groups. PR, Correctness: a
+short trailing column group must be handled. Blog, MoE: token copies go into
+optionally padded per-expert buffers.
+
+Reading R-group: group g holds rows offsets[g]..offsets[g+1]-1. It is padded
+with zero rows to P_g = 16 * ceil(n_g / 16) rows; the padded groups sit back to
+back, so group g owns token columns Poff[g]..Poff[g]+P_g-1 of one transposed
+plane (codes [K, Poff[G]/2], scales [K, Poff[G]/16]). The transform (if on) and
+the per-group amax see the zero-padded rows. SR block index (R-blk) is
+col * (Poff[G]/16) + Poff[g]/16 + b, tag 1.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_to_f32, pack_nibbles
+from .philox import block_random_bytes
+from .quantize import global_scales, quantize_blocks
+from .rht import rht16
+
+MAX_GROUPS = 64
+
+
+def padded_offsets(offsets) -> np.ndarray:
+    """offsets[G+1] -> padded offsets Poff[G+1] (exclusive prefix sum of 16-rounded counts)."""
+    off = np.asarray(offsets, dtype=np.int64)
+    n = np.diff(off)
+    assert np.all(n >= 0) and off[0] == 0
+    p = (n + 15) // 16 * 16
+    out = np.zeros(len(off), dtype=np.int64)
+    out[1:] = np.cumsum(p)
+    return out.astype(np.int32)
+
+
+def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr",
+                     seed=0, offset=0, groups=None):
+    """Reference for the grouped columnwise path.
+
+    x: bf16 bits [total_rows, K]. offsets: int32 [G+1]. amax: optional float32 [G].
+    groups: optional iterable restricting which groups are computed (for sampling);
+    columns of other groups are left as 0 in the returned planes.
+    Returns dict with codes [K, Mpad/2], scales [K, Mpad/16], amax [G], s_enc [G],
+    s_dec [G], poff [G+1].
+    """
+    x = np.asarray(x, dtype=np.uint16)
+    T, K = x.shape
+    off = np.asarray(offsets, dtype=np.int64)
+    G = len(off) - 1
+    assert 1 <= G <= MAX_GROUPS and off[-1] == T
+    poff = padded_offsets(off).astype(np.int64)
+    mpad = int(poff[-1])
+    codes = np.zeros((K, mpad // 2), dtype=np.uint8)
+    scales = np.zeros((K, mpad // 16), dtype=np.uint8)
+    amax_out = np.zeros(G, dtype=np.float32)
+    s_enc_out = np.ones(G, dtype=np.float32)
+    s_dec_out = np.ones(G, dtype=np.float32)
+    sel = range(G) if groups is None else groups
+    for g in sel:
+        n = int(off[g + 1] - off[g])
+        pg = int(poff[g + 1] - poff[g])
+        z = np.zeros((pg, K), dtype=np.uint16)
+        z[:n] = x[off[g]:off[g + 1]]
+        zt = np.ascontiguousarray(z.T).reshape(K, pg // 16, 16)     # column blocks along tokens
+        if apply_rht:
+            zt = rht16(zt, rht_mask)
+        zf = bf16_to_f32(zt)
+        a = np.float32(np.max(np.abs(zf))) if zf.size else np.float32(0.0)
+        if amax is not None:
+            a = np.float32(np.asarray(amax, dtype=np.float32)[g])
+        s_enc, s_dec = global_scales(a)
+        amax_out[g], s_enc_out[g], s_dec_out[g] = a, s_enc, s_dec
+        if pg == 0:
+            continue
+        rb = None
+        if rounding == "sr":
+            blk = (np.arange(K, dtype=np.uint64)[:, None] * np.uint64(mpad // 16)
+                   + np.uint64(poff[g] // 16) + np.arange(pg // 16, dtype=np.uint64)[None, :])
+            rb = block_random_bytes(blk, 1, seed, offset)
+        c, sc = quantize_blocks(zf, s_enc, s_dec, rounding, rb)
+        codes[:, poff[g] // 2:(poff[g] + pg) // 2] = pack_nibbles(c.reshape(K, pg))
+        scales[:, poff[g] // 16:(poff[g] + pg) // 16] = sc
+    return {"codes": codes, "scales": scales, "amax": amax_out, "s_enc": s_enc_out,
+            "s_dec": s_dec_out, "poff": poff.astype(np.int32)}

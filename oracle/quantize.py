@@ -1,0 +1,183 @@
+"""NVFP4 block quantization: global scale, block scale, encode, SR, pack.
+
+Test infrastructure only. Each float step is one binary32 operation on
+``numpy.float32`` values, in the order the steps are listed here.
+
+Per tensor (or per group):
+  amax  = max |x|                                 (exact; bf16 values)
+  S_enc = RN(2688 / amax),  S_dec = RN(amax / 2688)           reading R-scale
+Per block of 16 values:
+  bmax  = max |x_i|
+  s     = E4M3_rne_sat(RN(RN(bmax / 6) * S_enc))              reading R-bscale
+  rcp   = RN(1 / RN(f32(s) * S_dec))   (0 if s == 0)          reading R-rcp
+  v_i   = RN(x_i * rcp)
+  code_i = E2M1_rne_sat(v_i)  or  SR(v_i, r_i)                R-e2m1 / R-sr
+
+Sources: PR, Fast math (the encode reciprocal is the correctly rounded
+reciprocal of the decoded FP8 block scale times the global decode scale, and
+the exact path uses a correctly rounded division); PR, Optimization item 1
+(eight bf16-origin values are multiplied by the reciprocal and converted);
+Blog, Blackwell support (NVFP4 takes its amax over 16 elements). The 2688 is
+6 * 448, the largest E2M1 magnitude times the largest E4M3 value, so the
+per-tensor scale is amax / (6 * 448).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_to_f32, e2m1_encode, e2m1_decode, e4m3_decode, e4m3_encode, pack_nibbles, unpack_nibbles
+from .formats import E2M1_VALUES
+from .philox import block_random_bytes
+
+F32 = np.float32
+_FLT_MAX = np.finfo(np.float32).max
+BLOCK = 16
+
+
+def global_scales(amax):
+    """amax (float32, any shape) -> (S_enc, S_dec) float32 arrays. Reading R-scale."""
+    amax = np.asarray(amax, dtype=F32)
+    with np.errstate(divide="ignore", over="ignore"):
+        s_enc = F32(2688.0) / amax
+        s_dec = amax / F32(2688.0)
+    bad = (amax == 0) | ~np.isfinite(s_enc)
+    s_enc = np.where(bad, F32(1.0), s_enc).astype(F32)
+    s_dec = np.where(bad, F32(1.0), s_dec).astype(F32)
+    return s_enc, s_dec
+
+
+def block_scale_codes(bmax, s_enc):
+    """Block amax (float32) and S_enc -> E4M3 scale codes. Reading R-bscale: divide by 6 first."""
+    bmax = np.asarray(bmax, dtype=F32)
+    q = bmax / F32(6.0)
+    with np.errstate(over="ignore"):
+        s = (q * np.asarray(s_enc, dtype=F32)).astype(F32)
+    return e4m3_encode(s)
+
+
+def encode_reciprocal(scodes, s_dec):
+    """Scale codes and S_dec -> encode multiplier. Reading R-rcp."""
+    p = (e4m3_decode(scodes) * np.asarray(s_dec, dtype=F32)).astype(F32)
+    with np.errstate(divide="ignore", over="ignore"):
+        r = F32(1.0) / p
+    r = np.minimum(r, F32(_FLT_MAX))
+    return np.where(np.asarray(scodes) == 0, F32(0.0), r).astype(F32)
+
+
+def sr_round(v, rbytes):
+    """Stochastic rounding of float32 v onto the signed E2M1 grid, given one random byte each.
+
+    Reading R-sr. |v| is clamped to 6; lo <= |v| < hi are the neighbouring
+    magnitudes; frac = (|v| - lo) / (hi - lo) is exact (the gap is a power of
+    two and the subtraction is exact by Sterbenz's lemma); the value moves up
+    to hi iff r + floor(256 * frac) >= 256, so it moves up with probability
+    floor(256 * frac) / 256. Sign as in round-to-nearest (R-e2m1).
+    PR, Correctness and Optimization item 3: one random draw per block, and SR
+    codes stay within one magnitude step of the round-to-nearest code.
+    """
+    v = np.asarray(v, dtype=F32)
+    r = np.asarray(rbytes, dtype=np.int64)
+    a = np.minimum(np.abs(v), F32(6.0))
+    lo_i = np.searchsorted(E2M1_VALUES, a, side="right") - 1       # largest value <= a
+    lo_i = np.clip(lo_i, 0, 7)
+    hi_i = np.minimum(lo_i + 1, 7)
+    lo = E2M1_VALUES[lo_i]
+    hi = E2M1_VALUES[hi_i]
+    gap = np.where(hi_i == lo_i, F32(1.0), hi - lo).astype(F32)
+    frac = ((a - lo) / gap).astype(F32)
+    t = np.floor(frac * F32(256.0)).astype(np.int64)
+    up = (r + t >= 256) & (hi_i != lo_i)
+    mag = np.where(up, hi_i, lo_i).astype(np.uint8)
+    sign = np.signbit(v).astype(np.uint8) << np.uint8(3)
+    return (mag | sign).astype(np.uint8)
+
+
+def quantize_blocks(xb, s_enc, s_dec, rounding="rtne", rbytes=None):
+    """Quantize float32 blocks xb[..., 16] with per-leading-index S_enc/S_dec.
+
+    Returns (codes[..., 16] 4-bit, scale codes[...]).
+    """
+    xb = np.asarray(xb, dtype=F32)
+    assert xb.shape[-1] == BLOCK
+    bmax = np.max(np.abs(xb), axis=-1)
+    sc = block_scale_codes(bmax, s_enc)
+    rcp = encode_reciprocal(sc, s_dec)
+    with np.errstate(over="ignore"):
+        v = (xb * rcp[..., None]).astype(F32)
+    if rounding == "rtne":
+        codes = e2m1_encode(v)
+    elif rounding == "sr":
+        assert rbytes is not None and rbytes.shape == xb.shape
+        codes = sr_round(v, rbytes)
+    else:
+        raise ValueError(rounding)
+    return codes, sc
+
+
+def _as_f32(x_bits_or_f32):
+    a = np.asarray(x_bits_or_f32)
+    return bf16_to_f32(a) if a.dtype == np.uint16 else a.astype(F32)
+
+
+def _amax(xf):
+    return F32(np.max(np.abs(xf))) if xf.size else F32(0.0)
+
+
+def quantize_rowwise(x, amax=None, rounding="rtne", seed=0, offset=0, tag=0):
+    """Rowwise NVFP4 of x[M, K] (bf16 bits or float32 holding bf16 values).
+
+    Blocks are 16 consecutive elements of a row. Reading R-blk: the SR block
+    index is row * (K/16) + kb. Returns a dict with codes [M, K/2] (packed),
+    scales [M, K/16] (E4M3 codes), amax, s_enc, s_dec.
+    """
+    xf = _as_f32(x)
+    M, K = xf.shape
+    assert K % BLOCK == 0
+    a = _amax(xf) if amax is None else F32(amax)
+    s_enc, s_dec = global_scales(a)
+    xb = xf.reshape(M, K // BLOCK, BLOCK)
+    rb = None
+    if rounding == "sr":
+        blk = np.arange(M * (K // BLOCK), dtype=np.uint64).reshape(M, K // BLOCK)
+        rb = block_random_bytes(blk, tag, seed, offset)
+    codes, sc = quantize_blocks(xb, s_enc, s_dec, rounding, rb)
+    return {
+        "codes": pack_nibbles(codes.reshape(M, K)),
+        "scales": sc.reshape(M, K // BLOCK),
+        "amax": F32(a),
+        "s_enc": F32(s_enc),
+        "s_dec": F32(s_dec),
+    }
+
+
+def quantize_colwise(x, amax=None, rounding="rtne", seed=0, offset=0):
+    """Columnwise (transposed) NVFP4 of x[M, K]; reading R-col.
+
+    Blocks are 16 consecutive rows of one column; the output plane is the
+    rowwise quantization of x transposed: codes [K, M/2], scales [K, M/16].
+    Reading R-blk/R-philox: SR block index col * (M/16) + mb, tag 1.
+    """
+    xf = _as_f32(x)
+    M, K = xf.shape
+    assert M % BLOCK == 0
+    a = _amax(xf) if amax is None else F32(amax)
+    return quantize_rowwise(np.ascontiguousarray(xf.T), amax=a, rounding=rounding, seed=seed,
+                            offset=offset, tag=1)
+
+
+def quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0):
+    """Rowwise and columnwise planes of one tensor under one shared per-tensor scale."""
+    xf = _as_f32(x)
+    a = _amax(xf) if amax is None else F32(amax)
+    row = quantize_rowwise(xf, amax=a, rounding=rounding, seed=seed, offset=offset, tag=0)
+    col = quantize_colwise(xf, amax=a, rounding=rounding, seed=seed, offset=offset)
+    return {"row": row, "col": col, "amax": F32(a), "s_enc": row["s_enc"], "s_dec": row["s_dec"]}
+
+
+def dequantize_rowwise(codes, scales, s_dec):
+    """Test helper: x_hat = e2m1(code) * f32(scale) * S_dec, in float64 (no rounding claims)."""
+    c = unpack_nibbles(codes)
+    M, K = c.shape
+    v = e2m1_decode(c).astype(np.float64).reshape(M, K // BLOCK, BLOCK)
+    s = e4m3_decode(scales).astype(np.float64)[..., None]
+    return (v * s * float(s_dec)).reshape(M, K)

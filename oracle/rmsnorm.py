@@ -1,0 +1,46 @@
+"""Per-token RMSNorm feeding the rowwise NVFP4 quantizer.
+
+Test infrastructure only.
+
+Blog, QK Norm: the squared norm is a horizontal sum over the row, the inverse
+RMS is rsqrt(sum / n + EPS), and the output is ((w + WEIGHT_BIAS) * (x * rms))
+cast back to the element type; WEIGHT_BIAS and EPS are compile-time
+constants. The formula printed in that section's prose omits the square root;
+the kernel code printed in the same section includes it and is followed here.
+
+Readings: R-eps (eps is the float32 value the ABI carries), R-bias (the scalar
+weight offset c of the Blog plus an optional per-channel additive beta), R-y
+(the quantizer consumes the bfloat16-rounded output, so the tensor amax is
+max |y_bf16|). The statistics are evaluated in float64 and y is rounded once
+to bfloat16, so this is the exact value for any fp32 evaluation order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_to_f32, f64_to_bf16
+from .quantize import quantize_rowwise
+
+
+def rmsnorm_bf16(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, return_f64=False):
+    """y = bf16_RNE((gamma + c) * (x * r) [+ beta]),  r = 1 / sqrt(mean_k x^2 + eps)."""
+    x64 = bf16_to_f32(x).astype(np.float64)
+    K = x64.shape[-1]
+    g64 = bf16_to_f32(gamma).astype(np.float64) + float(np.float32(weight_offset))
+    eps64 = float(np.float32(eps))
+    ms = np.sum(x64 * x64, axis=-1, keepdims=True) / K
+    r = 1.0 / np.sqrt(ms + eps64)
+    y64 = g64 * (x64 * r)
+    if beta is not None:
+        y64 = y64 + bf16_to_f32(beta).astype(np.float64)
+    y = f64_to_bf16(y64)
+    return (y, y64, r[..., 0]) if return_f64 else y
+
+
+def rmsnorm_quantize(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None,
+                     rounding="rtne", seed=0, offset=0):
+    """Fused reference: RMSNorm to bfloat16, then rowwise NVFP4 of that bfloat16 tensor."""
+    y = rmsnorm_bf16(x, gamma, beta, weight_offset, eps)
+    q = quantize_rowwise(y, amax=amax, rounding=rounding, seed=seed, offset=offset, tag=0)
+    q["y"] = y
+    return q

@@ -1,0 +1,176 @@
+"""Pins for the oracle's quantizer: hand-derived blocks, closed forms, round trips,
+error bounds, stochastic-rounding statistics and layout identities."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import formats as F
+from oracle import quantize as Q
+from oracle.philox import block_random_bytes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_blocks.json")
+
+
+def _bf16(vals):
+    a = np.asarray(vals, dtype=np.float32)
+    bits = F.f32_to_bf16(a)
+    assert np.array_equal(F.bf16_to_f32(bits), a), "golden inputs must be exact bf16 values"
+    return bits
+
+
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_hand_derived_blocks(case):
+    x = _bf16(case["x"]).reshape(1, 16)
+    q = Q.quantize_rowwise(x, amax=case["amax_in"])
+    assert q["codes"].tolist()[0] == case["bytes"]
+    assert F.unpack_nibbles(q["codes"]).tolist()[0] == case["codes4"]
+    assert int(q["scales"][0, 0]) == case["scale"]
+    assert int(np.float32(q["s_dec"]).view(np.uint32)) == case["s_dec_bits"]
+    assert int(np.float32(q["s_enc"]).view(np.uint32)) == case["s_enc_bits"]
+
+
+def test_power_of_two_global_scale_closed_form():
+    for k in range(-20, 20):
+        amax = np.float32(2688.0 * 2.0 ** k)
+        s_enc, s_dec = Q.global_scales(amax)
+        assert s_dec == np.float32(2.0 ** k) and s_enc == np.float32(2.0 ** -k)
+
+
+def test_block_holding_the_amax_gets_scale_448():
+    # RN(RN(amax/6) * RN(2688/amax)) is within a few ulps of 448 and rounds to it.
+    rng = np.random.default_rng(5)
+    amax = F.bf16_to_f32(F.f32_to_bf16(np.exp2(rng.uniform(-30, 30, 20000)).astype(np.float32)))
+    s_enc, _ = Q.global_scales(amax)
+    assert np.all(Q.block_scale_codes(amax, s_enc) == 0x7E)
+
+
+def test_exact_round_trip_of_representable_blocks():
+    # Blocks built as e2m1 * s * S_dec with a +-6 entry re-quantize to the same codes and scale.
+    rng = np.random.default_rng(6)
+    n = 4000
+    codes = rng.integers(0, 16, size=(n, 16)).astype(np.uint8)
+    codes[np.arange(n), rng.integers(0, 16, n)] = rng.choice([7, 15], n)   # one +-6 per block
+    scodes = rng.integers(1, 0x7F, size=n).astype(np.uint8)
+    for k in (-8, 0, 5):
+        s_dec = np.float32(2.0 ** k)
+        amax = np.float32(2688.0) * s_dec
+        vals = F.e2m1_decode(codes) * F.e4m3_decode(scodes)[:, None] * s_dec
+        x = F.f32_to_bf16(vals.astype(np.float32))
+        assert np.array_equal(F.bf16_to_f32(x), vals.astype(np.float32))
+        q = Q.quantize_rowwise(x.reshape(n, 16), amax=amax)
+        got = F.unpack_nibbles(q["codes"])
+        # -0 inputs are 0x8 codes that decode to -0.0: compare decoded values and signs
+        assert np.array_equal(F.e2m1_decode(got), F.e2m1_decode(codes))
+        assert np.array_equal(np.signbit(F.e2m1_decode(got)), np.signbit(vals))
+        assert np.array_equal(q["scales"][:, 0], scodes)
+
+
+def _dequant(q):
+    return Q.dequantize_rowwise(q["codes"], q["scales"], q["s_dec"])
+
+
+def test_rtne_error_bound_and_sqnr():
+    rng = np.random.default_rng(7)
+    x = F.f32_to_bf16(rng.standard_normal((512, 1024)).astype(np.float32))
+    q = Q.quantize_rowwise(x)
+    xf = F.bf16_to_f32(x).astype(np.float64)
+    xh = _dequant(q)
+    # per element: error <= half the local E2M1 gap times the block step (plus the
+    # scale's own rounding); bound it by 1/4 of the block's max plus relative slack
+    blk = np.abs(xf).reshape(512, 64, 16).max(-1)
+    err = np.abs(xf - xh).reshape(512, 64, 16).max(-1)
+    assert np.all(err <= blk * (1.0 / 6.0) * 1.07 + 1e-30)
+    sqnr = 10 * np.log10(np.sum(xf ** 2) / np.sum((xf - xh) ** 2))
+    assert sqnr >= 20.0  # PR, Correctness: round-to-nearest bar
+
+
+def test_rowwise_equals_brute_force_nearest_in_block():
+    # For each element, the chosen code minimizes |x*rcp - e2m1| (ties -> even code).
+    rng = np.random.default_rng(8)
+    x = F.f32_to_bf16((rng.standard_normal((64, 256)) * np.exp2(rng.integers(-10, 10, (64, 1)))).astype(np.float32))
+    q = Q.quantize_rowwise(x)
+    sc = q["scales"].repeat(16, axis=1)
+    rcp = Q.encode_reciprocal(sc, q["s_dec"])
+    v = (F.bf16_to_f32(x) * rcp).astype(np.float32).astype(np.float64)
+    got = F.e2m1_decode(F.unpack_nibbles(q["codes"])).astype(np.float64)
+    grid = np.concatenate([-F.E2M1_VALUES[::-1], F.E2M1_VALUES]).astype(np.float64)
+    d = np.abs(np.minimum(np.abs(v), 6.0)[..., None] * np.sign(v)[..., None] - grid)
+    assert np.all(np.abs(np.minimum(np.abs(v), 6.0) * np.sign(v) - got) <= d.min(-1) + 0.0)
+
+
+def test_colwise_is_rowwise_of_transpose():
+    rng = np.random.default_rng(9)
+    x = F.f32_to_bf16(rng.standard_normal((64, 48)).astype(np.float32))
+    d = Q.quantize_2d(x)
+    r = Q.quantize_rowwise(np.ascontiguousarray(x.T), amax=d["amax"])
+    assert np.array_equal(d["col"]["codes"], r["codes"]) and np.array_equal(d["col"]["scales"], r["scales"])
+    assert d["row"]["s_dec"] == d["col"]["s_dec"]
+
+
+# ---- stochastic rounding (reading R-sr) ----
+
+def test_sr_mean_is_exact_over_all_random_bytes():
+    # For each v, averaging the SR result over all 256 byte values gives
+    # lo + gap * floor(256 frac) / 256 exactly (so the bias is below gap/256).
+    rng = np.random.default_rng(10)
+    v = np.concatenate([rng.uniform(0, 6.5, 3000), rng.uniform(0, 0.01, 200)]).astype(np.float32)
+    r = np.arange(256)
+    codes = Q.sr_round(np.repeat(v, 256), np.tile(r, len(v))).reshape(len(v), 256)
+    mean = F.e2m1_decode(codes).astype(np.float64).mean(axis=1)
+    a = np.minimum(v.astype(np.float64), 6.0)
+    lo = np.array([F.E2M1_VALUES[F.E2M1_VALUES <= t].max() for t in a], dtype=np.float64)
+    hi = np.array([F.E2M1_VALUES[F.E2M1_VALUES >= t].min() for t in a], dtype=np.float64)
+    gap = np.where(hi > lo, hi - lo, 1.0)
+    want = lo + gap * np.floor(256 * (a - lo) / gap) / 256
+    assert np.allclose(mean, want, rtol=0, atol=1e-12)
+    assert np.all(np.abs(mean - a) < gap / 256 + 1e-12)
+
+
+def test_sr_exact_halfway_is_half_up():
+    for lo, hi in [(0, .5), (.5, 1), (1, 1.5), (1.5, 2), (2, 3), (3, 4), (4, 6)]:
+        mid = np.float32((lo + hi) / 2)
+        c = Q.sr_round(np.full(256, mid), np.arange(256))
+        up = F.e2m1_decode(c) == hi
+        assert up.sum() == 128
+
+
+def test_sr_halfway_statistics_on_philox_stream():
+    # 2^20 exact-halfway values through the real block stream: |p - 1/2| <= 5 sigma.
+    n_blk = 1 << 16
+    rb = block_random_bytes(np.arange(n_blk, dtype=np.uint64), 0, 0x5EED, 0)
+    v = np.full((n_blk, 16), 1.25, dtype=np.float32)
+    c = Q.sr_round(v, rb)
+    p = np.mean(F.e2m1_decode(c) == 1.5)
+    assert abs(p - 0.5) <= 5 * 0.5 / np.sqrt(n_blk * 16)
+    # no position in the block is biased either (a correlated stream would show here)
+    per_pos = np.mean(F.e2m1_decode(c) == 1.5, axis=0)
+    assert np.all(np.abs(per_pos - 0.5) <= 5 * 0.5 / np.sqrt(n_blk))
+
+
+def test_sr_within_one_step_of_rtne_and_reproducible():
+    rng = np.random.default_rng(11)
+    x = F.f32_to_bf16(rng.standard_normal((128, 512)).astype(np.float32))
+    a = Q.quantize_rowwise(x, rounding="rtne")
+    s = Q.quantize_rowwise(x, rounding="sr", seed=0x5EED, offset=0)
+    s2 = Q.quantize_rowwise(x, rounding="sr", seed=0x5EED, offset=0)
+    s3 = Q.quantize_rowwise(x, rounding="sr", seed=0x5EED, offset=1)
+    ca, cs = F.unpack_nibbles(a["codes"]), F.unpack_nibbles(s["codes"])
+    assert np.all(np.abs((ca & 7).astype(int) - (cs & 7).astype(int)) <= 1)
+    nz = ((ca & 7) != 0) & ((cs & 7) != 0)
+    assert np.array_equal((ca & 8)[nz], (cs & 8)[nz])
+    assert np.array_equal(a["scales"], s["scales"])         # scales stay round-to-nearest
+    assert np.array_equal(s["codes"], s2["codes"])
+    assert not np.array_equal(s["codes"], s3["codes"])
+    xf = F.bf16_to_f32(x).astype(np.float64)
+    sq = 10 * np.log10(np.sum(xf ** 2) / np.sum((xf - _dequant(s)) ** 2))
+    assert sq >= 15.0   # PR, Correctness: SR reconstruction bar
+
+
+def test_reciprocal_zero_and_clamp():
+    assert Q.encode_reciprocal(np.array([0], np.uint8), np.float32(1.0))[0] == 0.0
+    # tiny S_dec: 1/(2^-9 * S_dec) overflows; the multiplier is clamped to FLT_MAX
+    r = Q.encode_reciprocal(np.array([1], np.uint8), np.float32(1e-38))[0]
+    assert r == np.finfo(np.float32).max

@@ -1,0 +1,144 @@
+"""Pins for the oracle's RMSNorm, Hadamard transform and grouped layout."""
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+from oracle import formats as F
+from oracle import quantize as Q
+from oracle.grouped import grouped_quantize, padded_offsets
+from oracle.rht import rht16, rht16_f32, sign_vector
+from oracle.rmsnorm import rmsnorm_bf16, rmsnorm_quantize
+
+
+def _bits(a):
+    return F.f32_to_bf16(np.asarray(a, dtype=np.float32))
+
+
+# ---- RMSNorm ----
+
+def test_rmsnorm_matches_torch_rms_norm_float64():
+    rng = np.random.default_rng(20)
+    x = _bits(rng.standard_normal((64, 4096)))
+    g = _bits(1 + 0.1 * rng.standard_normal(4096))
+    b = _bits(0.01 * rng.standard_normal(4096))
+    eps = 1e-6
+    y, y64, _ = rmsnorm_bf16(x, g, b, 0.0, eps, return_f64=True)
+    xt = torch.from_numpy(F.bf16_to_f32(x).astype(np.float64))
+    gt = torch.from_numpy(F.bf16_to_f32(g).astype(np.float64))
+    ref = torch.nn.functional.rms_norm(xt, (4096,), gt, eps=float(np.float32(eps))).numpy()
+    ref = ref + F.bf16_to_f32(b).astype(np.float64)
+    assert np.allclose(y64, ref, rtol=1e-13, atol=1e-15)
+    assert np.array_equal(y, F.f64_to_bf16(ref))
+
+
+def test_rmsnorm_weight_offset_is_added_to_gamma():
+    rng = np.random.default_rng(21)
+    x = _bits(rng.standard_normal((4, 256)))
+    g = _bits(0.1 * rng.standard_normal(256))
+    _, a, _ = rmsnorm_bf16(x, g, None, 1.0, 1e-6, return_f64=True)
+    g1 = F.bf16_to_f32(g).astype(np.float64) + 1.0
+    _, b, _ = rmsnorm_bf16(x, _bits(np.ones(256)), None, 0.0, 1e-6, return_f64=True)
+    assert np.allclose(a, b * g1, rtol=1e-14)
+
+
+def test_rmsnorm_constant_row_closed_form():
+    for c in (1.0, -3.0, 0.0078125, 100.0):
+        x = _bits(np.full((1, 512), c))
+        g = _bits(np.full(512, 1.5))
+        eps = np.float32(1e-6)
+        _, y64, _ = rmsnorm_bf16(x, g, None, 0.0, float(eps), return_f64=True)
+        want = 1.5 * c / np.sqrt(c * c + float(eps))
+        assert np.allclose(y64, want, rtol=1e-15)
+
+
+def test_fused_amax_is_max_of_bf16_output():
+    rng = np.random.default_rng(22)
+    x = _bits(rng.standard_t(3, (8, 7168)))
+    g = _bits(1 + 0.1 * rng.standard_normal(7168))
+    b = _bits(0.01 * rng.standard_normal(7168))
+    q = rmsnorm_quantize(x, g, b)
+    assert q["amax"] == np.max(np.abs(F.bf16_to_f32(q["y"])))
+    r = Q.quantize_rowwise(q["y"])
+    assert np.array_equal(r["codes"], q["codes"]) and np.array_equal(r["scales"], q["scales"])
+
+
+# ---- Hadamard transform ----
+
+def test_rht_equals_sylvester_matrix_on_exact_inputs():
+    # Small integers keep every partial sum exact in fp32, so the staged
+    # butterflies must equal (1/4) H D x computed with scipy's Hadamard matrix.
+    H = scipy.linalg.hadamard(16).astype(np.float64)
+    rng = np.random.default_rng(23)
+    for mask in (0, 0xFFFF, 0x1234, 0x8001, int(rng.integers(0, 1 << 16))):
+        x = rng.integers(-64, 65, size=(200, 16)).astype(np.float32)
+        d = sign_vector(mask).astype(np.float64)
+        want = (x.astype(np.float64) * d) @ H.T / 4.0
+        got = rht16_f32(x, mask).astype(np.float64)
+        assert np.array_equal(got, want)
+
+
+def test_rht_sign_bits_index_the_input_positions():
+    # with x = e_i, the output is (1/4) * d_i * column i of H
+    H = scipy.linalg.hadamard(16).astype(np.float64)
+    for i in range(16):
+        e = np.zeros((1, 16), np.float32)
+        e[0, i] = 4.0
+        assert np.array_equal(rht16_f32(e, 1 << i)[0], -H[:, i])
+        assert np.array_equal(rht16_f32(e, 0)[0], H[:, i])
+
+
+def test_rht_is_orthogonal_and_inverts():
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((1000, 16)).astype(np.float32)
+    mask = 0xA5C3
+    y = rht16_f32(x, mask).astype(np.float64)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x.astype(np.float64), axis=1), rtol=1e-6)
+    H = scipy.linalg.hadamard(16).astype(np.float64)
+    back = (y @ H.T / 4.0) * sign_vector(mask).astype(np.float64)
+    assert np.allclose(back, x, rtol=0, atol=4e-6 * np.abs(x).max())
+
+
+def test_rht_bf16_round_through():
+    rng = np.random.default_rng(25)
+    x = _bits(rng.standard_normal((100, 16)))
+    y = rht16(x, 0x0F0F)
+    assert np.array_equal(y, F.f32_to_bf16(rht16_f32(F.bf16_to_f32(x), 0x0F0F)))
+
+
+# ---- grouped layout ----
+
+def test_padded_offsets():
+    off = np.array([0, 0, 5, 21, 21, 53], np.int32)
+    assert padded_offsets(off).tolist() == [0, 0, 16, 32, 32, 64]
+
+
+def test_grouped_single_group_without_rht_equals_colwise():
+    rng = np.random.default_rng(26)
+    x = _bits(rng.standard_normal((64, 32)))
+    g = grouped_quantize(x, np.array([0, 64], np.int32), apply_rht=False, rounding="sr", seed=7, offset=3)
+    c = Q.quantize_colwise(x, rounding="sr", seed=7, offset=3)
+    assert np.array_equal(g["codes"], c["codes"]) and np.array_equal(g["scales"], c["scales"])
+    assert g["amax"][0] == c["amax"]
+
+
+def test_grouped_each_group_equals_its_zero_padded_slice():
+    rng = np.random.default_rng(27)
+    x = _bits(rng.standard_normal((70, 32)))
+    off = np.array([0, 5, 5, 40, 70], np.int32)
+    mask = 0x3C5A
+    g = grouped_quantize(x, off, apply_rht=True, rht_mask=mask, rounding="rtne")
+    poff = g["poff"]
+    for k in range(4):
+        n, pg = off[k + 1] - off[k], poff[k + 1] - poff[k]
+        if pg == 0:
+            assert g["amax"][k] == 0 and g["s_dec"][k] == 1
+            continue
+        z = np.zeros((pg, 32), np.uint16)
+        z[:n] = x[off[k]:off[k + 1]]
+        zt = rht16(np.ascontiguousarray(z.T).reshape(32, pg // 16, 16), mask).reshape(32, pg)
+        r = Q.quantize_rowwise(zt)   # rowwise of the transposed slice
+        assert np.array_equal(g["codes"][:, poff[k] // 2:(poff[k] + pg) // 2], r["codes"])
+        assert np.array_equal(g["scales"][:, poff[k] // 16:(poff[k] + pg) // 16], r["scales"])
+        assert g["amax"][k] == r["amax"]
