@@ -1,0 +1,216 @@
+/*
+ * nvfp4q.h -- C ABI of an MI355X (gfx950) library for per-token RMSNorm and
+ * NVFP4 block quantization.
+ *
+ * Sources (cited by page title and section):
+ *   [PR]   "[nvfp4_training] Optimize CuteDSL kernels for NVFP4 training"
+ *          (pytorch/ao pull request 4798): Optimization items 1-7, Fast math,
+ *          Grouped allocation tail, Config surface and AUTO, Correctness.
+ *   [Blog] "CuTeDSL at Perplexity": QK Norm, Blackwell support, prefill and
+ *          decode specialization, grid synchronization.
+ *
+ * What is computed (NVFP4):
+ *   amax  = max |x| over the tensor, or over one group in grouped mode;
+ *   S_enc = 2688 / amax, S_dec = amax / 2688 (2688 = 6 * 448; both 1 when
+ *           amax is 0 or S_enc would not be finite);
+ *   per block of 16 elements (16 consecutive elements of a row, or 16
+ *   consecutive rows of one column for the columnwise plane):
+ *     scale = E4M3 round-to-nearest-even, saturating, of (bmax / 6) * S_enc,
+ *     each element x -> E2M1 code of x * (1 / (f32(scale) * S_dec)),
+ *     rounded to nearest even (RTNE) or stochastically (SR); codes are packed
+ *     two per byte with the even element in the low nibble.
+ *   [Blog, Blackwell support] (16-element amax), [PR, Optimization 1 and 3]
+ *   (encode multiply and saturating conversion), [PR, Fast math] (the encode
+ *   reciprocal is 1 / (decoded block scale * global decode scale), computed
+ *   exactly; this library has only the exact path).
+ *
+ * Stochastic rounding [PR, Optimization 3; Correctness]: one Philox4x32-10
+ * evaluation per 16-element block, key = (seed lo32, seed hi32), counter =
+ * (block index lo32, block index hi32, tag, offset); tag 0 for a rowwise plane
+ * and 1 for a columnwise plane; the block index is the position of the block's
+ * scale byte in a packed scale plane. Element j of a block uses byte (j & 3) of
+ * output word (j >> 2) and rounds up iff byte + floor(256 * frac) >= 256, frac
+ * being its position between the two neighbouring E2M1 magnitudes. Scales are
+ * always round-to-nearest-even. Output is a pure function of (inputs, seed,
+ * offset), independent of launch geometry.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are caller-owned device memory on the current
+ *     HIP device; struct pointers (nvfp4q_plane*, ...) are host memory read
+ *     only during the call. The library never allocates, frees or
+ *     synchronizes; all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream), so calls may be captured in a HIP graph.
+ *   - `workspace` is device memory of at least nvfp4q_workspace_bytes()
+ *     bytes, 256-byte aligned, that the caller zero-fills once before its first
+ *     use. Every call leaves its counters at zero again, so the same workspace
+ *     serves any number of calls that are ordered on one stream. Calls that can
+ *     run at the same time (different streams) need different workspaces. After
+ *     NVFP4Q_E_LAUNCH the workspace must be zero-filled again.
+ *   - Errors are returned synchronously, before anything is enqueued, except
+ *     NVFP4Q_E_LAUNCH. Device-side data that break a stated rule (for example
+ *     decreasing group offsets) give unspecified output but no out-of-bounds
+ *     access.
+ *   - Shapes: elements per row (`cols`, `hidden`) must be a multiple of 16;
+ *     a columnwise plane needs rows % 16 == 0 (except grouped mode, which pads
+ *     each group). Leading dimensions are in elements for bf16 tensors and in
+ *     bytes for code and scale planes. Input and bf16 output pointers must be
+ *     16-byte aligned with ld a multiple of 8 elements; code planes 16-byte
+ *     aligned with ld_codes a multiple of 8 bytes. Scale planes have no
+ *     alignment rule.
+ *   - Only bfloat16 input is built (NVFP4Q_BF16); anything else returns
+ *     NVFP4Q_E_UNSUPPORTED.
+ */
+#ifndef NVFP4Q_H
+#define NVFP4Q_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4Q_OK = 0,
+  NVFP4Q_E_NULLPTR = 1,     /* a required pointer is NULL */
+  NVFP4Q_E_SHAPE = 2,       /* a size or leading dimension breaks the shape rules */
+  NVFP4Q_E_ALIGN = 3,       /* a pointer or leading dimension breaks the alignment rules */
+  NVFP4Q_E_UNSUPPORTED = 4, /* dtype, rounding mode or option not built */
+  NVFP4Q_E_LAUNCH = 5,      /* a kernel launch failed on the HIP side */
+  NVFP4Q_E_WORKSPACE = 6    /* workspace missing, misaligned or too small */
+} nvfp4q_status;
+
+typedef enum { NVFP4Q_BF16 = 0 } nvfp4q_dtype;
+
+typedef enum { NVFP4Q_RTNE = 0, NVFP4Q_SR = 1 } nvfp4q_rounding;
+
+/* One quantized plane. codes: device, [plane_rows][ld_codes] bytes, two E2M1
+ * codes per byte, even element in the low nibble. scales: device,
+ * [plane_rows][ld_scales] E4M3 bytes, one per 16 elements. A rowwise plane of
+ * an [R, C] input has R plane rows of C/2 code bytes and C/16 scale bytes; a
+ * columnwise plane has C plane rows of R/2 code bytes and R/16 scale bytes
+ * (plane row c holds input column c). */
+typedef struct {
+  uint8_t *codes;
+  int64_t ld_codes;
+  uint8_t *scales;
+  int64_t ld_scales;
+} nvfp4q_plane;
+
+/* Per-tensor (or per-group) scale. All device pointers, each 1 float (G floats
+ * in grouped mode). amax_in: nullable; when given it is used as amax and the
+ * amax pass is skipped ("precomputed amax"). amax_out, scale_out: nullable;
+ * receive the amax used and S_dec = amax / 2688 (1 when amax is 0). */
+typedef struct {
+  const float *amax_in;
+  float *amax_out;
+  float *scale_out;
+} nvfp4q_global;
+
+/* Stochastic-rounding state; ignored under NVFP4Q_RTNE. */
+typedef struct {
+  uint64_t seed;
+  uint32_t offset;
+} nvfp4q_rng;
+
+/* Bytes of workspace every entry point needs (a constant). */
+size_t nvfp4q_workspace_bytes(void);
+
+/* Static description of a status code; never NULL. */
+const char *nvfp4q_status_string(nvfp4q_status s);
+
+/* ABI version: 1. */
+int nvfp4q_version(void);
+
+/*
+ * nvfp4q_quantize -- rowwise NVFP4 of a [rows, cols] bf16 tensor.
+ *   x: device, rows x cols, row stride ld_x elements.
+ *   g: per-tensor scale (amax computed from x unless g->amax_in is given).
+ *   row: the rowwise plane [rows][cols/2] codes, [rows][cols/16] scales.
+ *   rounding: NVFP4Q_RTNE or NVFP4Q_SR (rng used, tag 0,
+ *             block index = row * (cols/16) + col/16).
+ * rows == 0 writes amax_out = 0 and scale_out = 1 and nothing else.
+ * [PR, Optimization 1, 4, 6, 7; Blog, Blackwell support]
+ */
+nvfp4q_status nvfp4q_quantize(const void *x, nvfp4q_dtype dtype, int64_t rows, int64_t cols,
+                              int64_t ld_x, const nvfp4q_global *g, const nvfp4q_plane *row,
+                              nvfp4q_rounding rounding, const nvfp4q_rng *rng, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * rmsnorm_nvfp4q -- per-token RMSNorm feeding rowwise NVFP4.
+ *   y = bf16_rne((gamma + weight_offset) * (x * r) [+ beta]),
+ *   r = 1 / sqrt(sum_k x_k^2 / hidden + eps), evaluated in fp32;
+ *   the quantizer consumes the bf16 y and amax = max |y|.
+ *   [Blog, QK Norm: rsqrt of the mean square plus EPS, weight plus a
+ *   compile-time WEIGHT_BIAS, cast back to the element type]
+ *   x: device [tokens, hidden] bf16, row stride ld_x.
+ *   gamma: device [hidden] bf16 (required). beta: device [hidden] bf16 or
+ *     NULL (no-bias variant, compiled separately).
+ *   weight_offset: added to gamma (the page's WEIGHT_BIAS); must be 0 or 1.
+ *   eps: added to the mean square.
+ *   y_out: device [tokens, hidden] bf16 with row stride ld_y, or NULL.
+ *   row: the rowwise plane, or row->codes == NULL to produce only y_out.
+ *   rounding / rng as for nvfp4q_quantize.
+ */
+nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, int64_t hidden,
+                             int64_t ld_x, const void *gamma, const void *beta, float weight_offset,
+                             float eps, void *y_out, int64_t ld_y, const nvfp4q_global *g,
+                             const nvfp4q_plane *row, nvfp4q_rounding rounding,
+                             const nvfp4q_rng *rng, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
+ * nvfp4q_quantize_2d -- rowwise and columnwise (transposed) planes of one
+ * [rows, cols] bf16 tensor under one shared per-tensor scale (weights).
+ *   row: rowwise plane or row->codes == NULL; col: columnwise plane
+ *   [cols][rows/2] codes, [cols][rows/16] scales, or col->codes == NULL.
+ *   rows % 16 == 0 when the columnwise plane is requested.
+ *   SR: rowwise blocks use tag 0 and index row * (cols/16) + col/16;
+ *   columnwise blocks use tag 1 and index col * (rows/16) + row/16.
+ *   [PR, Optimization 2 (2D weight kernel, staged columnwise reads);
+ *    Performance (2D weights against a precomputed amax)]
+ */
+nvfp4q_status nvfp4q_quantize_2d(const void *x, nvfp4q_dtype dtype, int64_t rows, int64_t cols,
+                                 int64_t ld_x, const nvfp4q_global *g, const nvfp4q_plane *row,
+                                 const nvfp4q_plane *col, nvfp4q_rounding rounding,
+                                 const nvfp4q_rng *rng, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
+ * nvfp4q_grouped -- per-group columnwise NVFP4 of a packed [total_rows, cols]
+ * bf16 tensor, optionally after a 16-point random Hadamard transform along
+ * the rows of each 16-row block.
+ *   offsets: device int32 [num_groups + 1]; offsets[0] = 0, non-decreasing,
+ *     offsets[num_groups] = total_rows; group g is rows offsets[g] ..
+ *     offsets[g+1] - 1. 1 <= num_groups <= 64.
+ *   Each group is zero-padded to P_g = 16 * ceil(n_g / 16) rows; padded
+ *   groups are laid out back to back: group g owns plane columns
+ *   Poff[g] .. Poff[g] + P_g - 1, Poff = exclusive prefix sum of P_g.
+ *   padded_offsets_out: device int32 [num_groups + 1] receives Poff (nullable).
+ *   apply_rht: 0 or 1. With 1, each 16-row block of one column becomes
+ *     bf16_rne(0.25 * H16 * D * v): D = diag(d), d_i = -1 iff bit i of
+ *     rht_sign_mask is set, H16 the Sylvester Hadamard matrix evaluated as
+ *     four butterfly stages (h = 1, 2, 4, 8) of fp32 (a + b, a - b).
+ *     The transform and the per-group amax see the zero-padded rows.
+ *   g: G floats each (amax_in optional, amax_out, scale_out).
+ *   col: the columnwise plane, `cols` plane rows; ld_codes * 2 and
+ *     ld_scales * 16 must be >= total_rows + 15 * num_groups (the largest
+ *     possible padded length). Plane columns at and past Poff[G] are never
+ *     written [PR, Grouped allocation tail].
+ *   SR: tag 1, block index = plane_row * (Poff[G] / 16) + plane_col / 16.
+ *   [PR, Optimization 2, 3, 5; Fast math (bf16 round-through of the
+ *    transform); Config surface and AUTO (64 groups, device offsets)]
+ */
+nvfp4q_status nvfp4q_grouped(const void *x, nvfp4q_dtype dtype, int64_t total_rows, int64_t cols,
+                             int64_t ld_x, const int32_t *offsets, int32_t num_groups,
+                             int32_t *padded_offsets_out, int apply_rht, uint32_t rht_sign_mask,
+                             const nvfp4q_global *g, const nvfp4q_plane *col,
+                             nvfp4q_rounding rounding, const nvfp4q_rng *rng, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4Q_H */

@@ -1,0 +1,247 @@
+"""Python binding of the gfx950 RMSNorm + NVFP4 block-quantization library.
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the computation runs in the HIP kernels of
+``libnvfp4q.so`` through its C ABI (``include/nvfp4q.h``). The functions carry
+the C entry points' names. There is no CPU fallback: if the shared library is
+missing, :func:`load` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "load", "lib_path", "workspace", "NVFP4QError",
+    "nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_grouped",
+    "nvfp4q_workspace_bytes", "nvfp4q_status_string", "SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libnvfp4q.so")
+
+SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_grouped",
+           "nvfp4q_workspace_bytes", "nvfp4q_status_string", "nvfp4q_version")
+
+RTNE, SR = 0, 1
+
+
+class Plane(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("ld_scales", ctypes.c_int64)]
+
+
+class Global(ctypes.Structure):
+    _fields_ = [("amax_in", ctypes.c_void_p), ("amax_out", ctypes.c_void_p), ("scale_out", ctypes.c_void_p)]
+
+
+class Rng(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("offset", ctypes.c_uint32)]
+
+
+class NVFP4QError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load():
+    """Load ``libnvfp4q.so`` (built by ``rmsnorm_nvfp4_block_amd.build``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise NVFP4QError(f"{lib_path} not found: build it with `python -m rmsnorm_nvfp4_block_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    vp, i64, f32, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int32, ctypes.c_uint32
+    P = ctypes.POINTER
+    lib.nvfp4q_workspace_bytes.restype = ctypes.c_size_t
+    lib.nvfp4q_status_string.restype = ctypes.c_char_p
+    lib.nvfp4q_status_string.argtypes = [ctypes.c_int]
+    lib.nvfp4q_version.restype = ctypes.c_int
+    lib.nvfp4q_quantize.restype = ctypes.c_int
+    lib.nvfp4q_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(Global), P(Plane), ctypes.c_int, P(Rng),
+                                    vp, ctypes.c_size_t, vp]
+    lib.rmsnorm_nvfp4q.restype = ctypes.c_int
+    lib.rmsnorm_nvfp4q.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, f32, f32, vp, i64, P(Global), P(Plane),
+                                   ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
+    lib.nvfp4q_quantize_2d.restype = ctypes.c_int
+    lib.nvfp4q_quantize_2d.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(Global), P(Plane), P(Plane), ctypes.c_int,
+                                       P(Rng), vp, ctypes.c_size_t, vp]
+    lib.nvfp4q_grouped.restype = ctypes.c_int
+    lib.nvfp4q_grouped.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, ctypes.c_int, u32, P(Global),
+                                   P(Plane), ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
+    _lib = lib
+    return lib
+
+
+def nvfp4q_workspace_bytes() -> int:
+    return int(load().nvfp4q_workspace_bytes())
+
+
+def nvfp4q_status_string(status: int) -> str:
+    return load().nvfp4q_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise NVFP4QError(f"nvfp4q status {status}: {nvfp4q_status_string(status)}")
+
+
+_ws = {}
+
+
+def workspace(device=None):
+    """Per-device zero-filled workspace, allocated once (torch memory) and reused on every call."""
+    import torch
+
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index or 0)
+    if dev not in _ws:
+        _ws[dev] = torch.zeros(max(nvfp4q_workspace_bytes(), 4096), dtype=torch.uint8, device=dev)
+    return _ws[dev]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _rounding(r: str) -> int:
+    if r not in ("rtne", "sr"):
+        raise ValueError(f"rounding must be 'rtne' or 'sr', not {r!r}")
+    return SR if r == "sr" else RTNE
+
+
+def _check_bf16_2d(x):
+    import torch
+
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a 2-D row-contiguous bfloat16 CUDA tensor")
+
+
+def _plane(rows: int, cols: int, device, codes=None, scales=None):
+    """Allocate (or wrap) a plane of `rows` plane rows of `cols` elements."""
+    import torch
+
+    if codes is None:
+        ldc = ((cols // 2) + 15) // 16 * 16
+        codes = torch.empty((rows, ldc), dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty((rows, max(cols // 16, 1)), dtype=torch.uint8, device=device)
+    return codes, scales, Plane(codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0))
+
+
+def _global(amax_in, amax_out, scale_out):
+    return Global(_ptr(amax_in), _ptr(amax_out), _ptr(scale_out))
+
+
+def nvfp4q_quantize(x, amax=None, rounding="rtne", seed=0, offset=0, codes=None, scales=None):
+    """Rowwise NVFP4 of a bf16 [rows, cols] tensor. Returns dict(codes, scales, amax, scale)."""
+    import torch
+
+    _check_bf16_2d(x)
+    lib = load()
+    R, C = x.shape
+    c, s, plane = _plane(R, C, x.device, codes, scales)
+    amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = workspace(x.device)
+    st = lib.nvfp4q_quantize(x.data_ptr(), 0, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
+                             ctypes.byref(plane), _rounding(rounding), ctypes.byref(Rng(seed, offset)),
+                             ws.data_ptr(), ws.numel(), _stream(x))
+    _check(st)
+    return {"codes": c, "scales": s, "amax": amax_out, "scale": scale_out}
+
+
+def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, rounding="rtne", seed=0, offset=0,
+                   y_out=False, quantize=True, codes=None, scales=None):
+    """RMSNorm of bf16 x [tokens, hidden] then rowwise NVFP4 of the bf16 output.
+
+    Returns dict(codes, scales, amax, scale, y) (y only when y_out=True).
+    """
+    import torch
+
+    _check_bf16_2d(x)
+    lib = load()
+    T, H = x.shape
+    y = torch.empty_like(x) if y_out else None
+    if quantize:
+        c, s, plane = _plane(T, H, x.device, codes, scales)
+    else:
+        c, s, plane = None, None, Plane(None, 0, None, 0)
+    amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = workspace(x.device)
+    st = lib.rmsnorm_nvfp4q(x.data_ptr(), 0, T, H, x.stride(0), gamma.data_ptr(), _ptr(beta),
+                            float(weight_offset), float(eps), _ptr(y), y.stride(0) if y is not None else 0,
+                            ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(plane),
+                            _rounding(rounding), ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(),
+                            _stream(x))
+    _check(st)
+    return {"codes": c, "scales": s, "amax": amax_out, "scale": scale_out, "y": y}
+
+
+def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=True, colwise=True):
+    """Rowwise and columnwise planes of bf16 x [rows, cols] under one per-tensor scale."""
+    import torch
+
+    _check_bf16_2d(x)
+    lib = load()
+    R, C = x.shape
+    rc = rs = cc = cs = None
+    rp = Plane(None, 0, None, 0)
+    cp = Plane(None, 0, None, 0)
+    if rowwise:
+        rc, rs, rp = _plane(R, C, x.device)
+    if colwise:
+        cc, cs, cp = _plane(C, R, x.device)
+    amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    ws = workspace(x.device)
+    st = lib.nvfp4q_quantize_2d(x.data_ptr(), 0, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
+                                ctypes.byref(rp), ctypes.byref(cp), _rounding(rounding),
+                                ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(), _stream(x))
+    _check(st)
+    return {"row_codes": rc, "row_scales": rs, "col_codes": cc, "col_scales": cs, "amax": amax_out,
+            "scale": scale_out}
+
+
+def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr", seed=0, offset=0,
+                   codes=None, scales=None):
+    """Per-group columnwise NVFP4 (optionally after the 16-point RHT) of bf16 x [total_rows, cols].
+
+    offsets: int32 CUDA tensor [G+1]. The plane is allocated for the largest padded
+    length (total_rows + 15 G) unless given. Returns dict(codes, scales, amax, scale, poff).
+    """
+    import torch
+
+    _check_bf16_2d(x)
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1:
+        raise ValueError("offsets must be a 1-D int32 CUDA tensor")
+    lib = load()
+    T, C = x.shape
+    G = offsets.numel() - 1
+    cap = T + 15 * G
+    cap16 = (cap + 15) // 16 * 16
+    if codes is None:
+        codes = torch.empty((C, (cap16 // 2 + 15) // 16 * 16), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((C, cap16 // 16), dtype=torch.uint8, device=x.device)
+    plane = Plane(codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0))
+    amax_out = torch.empty(G, dtype=torch.float32, device=x.device)
+    scale_out = torch.empty(G, dtype=torch.float32, device=x.device)
+    poff = torch.empty(G + 1, dtype=torch.int32, device=x.device)
+    ws = workspace(x.device)
+    st = lib.nvfp4q_grouped(x.data_ptr(), 0, T, C, x.stride(0), offsets.data_ptr(), G, poff.data_ptr(),
+                            1 if apply_rht else 0, int(rht_mask), ctypes.byref(_global(amax, amax_out, scale_out)),
+                            ctypes.byref(plane), _rounding(rounding), ctypes.byref(Rng(seed, offset)),
+                            ws.data_ptr(), ws.numel(), _stream(x))
+    _check(st)
+    return {"codes": codes, "scales": scales, "amax": amax_out, "scale": scale_out, "poff": poff}

@@ -1,0 +1,205 @@
+// C ABI of the library: argument validation and dispatch to the gfx950 kernels.
+// Every check happens on the host before anything is enqueued; the only error
+// reported after enqueueing is NVFP4Q_E_LAUNCH.
+#include "../../include/nvfp4q.h"
+
+#include "device.hpp"
+#include "launch.hpp"
+
+using namespace nvfp4q;
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+nvfp4q_status check_ws(void* ws, size_t bytes) {
+  if (!ws || bytes < sizeof(Workspace) || !aligned(ws, 256)) return NVFP4Q_E_WORKSPACE;
+  return NVFP4Q_OK;
+}
+
+nvfp4q_status check_input(const void* x, nvfp4q_dtype dt, int64_t rows, int64_t cols, int64_t ld) {
+  if (dt != NVFP4Q_BF16) return NVFP4Q_E_UNSUPPORTED;
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld < cols) return NVFP4Q_E_SHAPE;
+  if (rows > 0x7FFFFFFF || cols > 0x7FFFFFFF) return NVFP4Q_E_SHAPE;
+  if (rows > 0 && !x) return NVFP4Q_E_NULLPTR;
+  if (!aligned(x, 16) || ld % 8 != 0) return NVFP4Q_E_ALIGN;
+  return NVFP4Q_OK;
+}
+
+// A plane of `prows` plane rows holding `pcols` elements each (an empty plane
+// may have NULL pointers).
+nvfp4q_status check_plane(const nvfp4q_plane* p, int64_t prows, int64_t pcols) {
+  if (prows > 0 && (!p->codes || !p->scales)) return NVFP4Q_E_NULLPTR;
+  if (p->ld_codes < pcols / 2 || p->ld_scales < pcols / 16) return NVFP4Q_E_SHAPE;
+  if (!aligned(p->codes, 16) || p->ld_codes % 8 != 0) return NVFP4Q_E_ALIGN;
+  return NVFP4Q_OK;
+}
+
+nvfp4q_status check_rounding(nvfp4q_rounding r, const nvfp4q_rng* rng) {
+  if (r != NVFP4Q_RTNE && r != NVFP4Q_SR) return NVFP4Q_E_UNSUPPORTED;
+  if (r == NVFP4Q_SR && !rng) return NVFP4Q_E_NULLPTR;
+  return NVFP4Q_OK;
+}
+
+nvfp4q_status done(hipError_t e) { return e == hipSuccess ? NVFP4Q_OK : NVFP4Q_E_LAUNCH; }
+
+#define TRY(expr)                             \
+  do {                                        \
+    nvfp4q_status st_ = (expr);               \
+    if (st_ != NVFP4Q_OK) return st_;         \
+  } while (0)
+
+const nvfp4q_global kNoGlobal = {nullptr, nullptr, nullptr};
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4q_workspace_bytes(void) { return sizeof(Workspace); }
+
+int nvfp4q_version(void) { return 1; }
+
+const char* nvfp4q_status_string(nvfp4q_status s) {
+  switch (s) {
+    case NVFP4Q_OK: return "ok";
+    case NVFP4Q_E_NULLPTR: return "a required pointer is NULL";
+    case NVFP4Q_E_SHAPE: return "a size or leading dimension breaks the shape rules";
+    case NVFP4Q_E_ALIGN: return "a pointer or leading dimension breaks the alignment rules";
+    case NVFP4Q_E_UNSUPPORTED: return "dtype, rounding mode or option not supported";
+    case NVFP4Q_E_LAUNCH: return "a kernel launch failed";
+    case NVFP4Q_E_WORKSPACE: return "workspace missing, misaligned or too small";
+  }
+  return "unknown status";
+}
+
+nvfp4q_status nvfp4q_quantize(const void* x, nvfp4q_dtype dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                              const nvfp4q_global* g, const nvfp4q_plane* row, nvfp4q_rounding rounding,
+                              const nvfp4q_rng* rng, void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_input(x, dtype, rows, cols, ld_x));
+  if (!row) return NVFP4Q_E_NULLPTR;
+  TRY(check_plane(row, rows, cols));
+  TRY(check_rounding(rounding, rng));
+  TRY(check_ws(workspace, workspace_bytes));
+  const nvfp4q_global& gg = g ? *g : kNoGlobal;
+  hipStream_t s = (hipStream_t)stream;
+  if (rows == 0) return done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s));
+  RowArgs a = {};
+  a.x = x; a.rows = rows; a.cols = cols; a.ld_x = ld_x;
+  a.codes = row->codes; a.ldc = row->ld_codes; a.scales = row->scales; a.lds = row->ld_scales;
+  a.ws = (Workspace*)workspace;
+  a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
+  a.sr = rounding == NVFP4Q_SR;
+  a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
+  if (!a.amax_in) {
+    hipError_t e = launch_amax_rows(a, s);
+    if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
+  }
+  return done(launch_quant_rows(a, s));
+}
+
+nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, int64_t hidden, int64_t ld_x,
+                             const void* gamma, const void* beta, float weight_offset, float eps, void* y_out,
+                             int64_t ld_y, const nvfp4q_global* g, const nvfp4q_plane* row,
+                             nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  TRY(check_input(x, dtype, tokens, hidden, ld_x));
+  if (!gamma) return NVFP4Q_E_NULLPTR;
+  if (!aligned(gamma, 16) || !aligned(beta, 16)) return NVFP4Q_E_ALIGN;
+  if (weight_offset != 0.0f && weight_offset != 1.0f) return NVFP4Q_E_UNSUPPORTED;
+  if (!(eps >= 0.0f)) return NVFP4Q_E_SHAPE;
+  if (hidden > rms_max_cols()) return NVFP4Q_E_UNSUPPORTED;
+  const bool codes = row && (row->codes || tokens == 0);
+  if (!codes && !y_out) return NVFP4Q_E_NULLPTR;
+  if (codes) TRY(check_plane(row, tokens, hidden));
+  if (y_out) {
+    if (ld_y < hidden) return NVFP4Q_E_SHAPE;
+    if (!aligned(y_out, 16) || ld_y % 8 != 0) return NVFP4Q_E_ALIGN;
+  }
+  TRY(check_rounding(rounding, rng));
+  TRY(check_ws(workspace, workspace_bytes));
+  const nvfp4q_global& gg = g ? *g : kNoGlobal;
+  hipStream_t s = (hipStream_t)stream;
+  if (tokens == 0) return codes ? done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s)) : NVFP4Q_OK;
+  RowArgs a = {};
+  a.x = x; a.rows = tokens; a.cols = hidden; a.ld_x = ld_x;
+  a.gamma = gamma; a.beta = beta; a.woff = weight_offset; a.eps = eps;
+  a.y = y_out; a.ld_y = ld_y;
+  a.codes = codes ? row->codes : nullptr; a.ldc = codes ? row->ld_codes : 0;
+  a.scales = codes ? row->scales : nullptr; a.lds = codes ? row->ld_scales : 0;
+  a.ws = (Workspace*)workspace;
+  a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
+  a.sr = rounding == NVFP4Q_SR;
+  a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
+  if (codes && !a.amax_in) {
+    hipError_t e = launch_rmsnorm_pass(a, true, s);
+    if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
+  }
+  return done(launch_rmsnorm_pass(a, false, s));
+}
+
+nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                 const nvfp4q_global* g, const nvfp4q_plane* row, const nvfp4q_plane* col,
+                                 nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  TRY(check_input(x, dtype, rows, cols, ld_x));
+  const bool has_row = row && row->codes, has_col = col && col->codes;
+  if (!has_row && !has_col) return NVFP4Q_E_NULLPTR;
+  if (has_row) TRY(check_plane(row, rows, cols));
+  if (has_col) {
+    if (rows % 16 != 0) return NVFP4Q_E_SHAPE;
+    TRY(check_plane(col, cols, rows));
+  }
+  TRY(check_rounding(rounding, rng));
+  TRY(check_ws(workspace, workspace_bytes));
+  const nvfp4q_global& gg = g ? *g : kNoGlobal;
+  hipStream_t s = (hipStream_t)stream;
+  if (rows == 0) return done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s));
+  if (!gg.amax_in) {
+    RowArgs r = {};
+    r.x = x; r.rows = rows; r.cols = cols; r.ld_x = ld_x;
+    r.ws = (Workspace*)workspace; r.amax_out = gg.amax_out; r.scale_out = gg.scale_out;
+    hipError_t e = launch_amax_rows(r, s);
+    if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
+  }
+  TwoDArgs a = {};
+  a.x = x; a.rows = rows; a.cols = cols; a.ld_x = ld_x;
+  if (has_row) { a.rcodes = row->codes; a.rldc = row->ld_codes; a.rscales = row->scales; a.rlds = row->ld_scales; }
+  if (has_col) { a.ccodes = col->codes; a.cldc = col->ld_codes; a.cscales = col->scales; a.clds = col->ld_scales; }
+  a.ws = (Workspace*)workspace;
+  a.amax_in = gg.amax_in;
+  a.amax_out = gg.amax_in ? gg.amax_out : nullptr;
+  a.scale_out = gg.amax_in ? gg.scale_out : nullptr;
+  a.sr = rounding == NVFP4Q_SR;
+  a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
+  return done(launch_quant_2d(a, s));
+}
+
+nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_rows, int64_t cols, int64_t ld_x,
+                             const int32_t* offsets, int32_t num_groups, int32_t* padded_offsets_out,
+                             int apply_rht, uint32_t rht_sign_mask, const nvfp4q_global* g,
+                             const nvfp4q_plane* col, nvfp4q_rounding rounding, const nvfp4q_rng* rng,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_input(x, dtype, total_rows, cols, ld_x));
+  if (!offsets || !col) return NVFP4Q_E_NULLPTR;
+  if (num_groups < 1 || num_groups > 64) return NVFP4Q_E_SHAPE;
+  if (apply_rht != 0 && apply_rht != 1) return NVFP4Q_E_UNSUPPORTED;
+  if (rht_sign_mask > 0xFFFFu) return NVFP4Q_E_UNSUPPORTED;
+  const int64_t cap = total_rows + 15 * (int64_t)num_groups;
+  TRY(check_plane(col, cols, 0));
+  if (col->ld_codes * 2 < cap || col->ld_scales * 16 < cap) return NVFP4Q_E_SHAPE;
+  TRY(check_rounding(rounding, rng));
+  TRY(check_ws(workspace, workspace_bytes));
+  const nvfp4q_global& gg = g ? *g : kNoGlobal;
+  GroupArgs a = {};
+  a.x = x; a.rows = total_rows; a.cols = cols; a.ld_x = ld_x;
+  a.offsets = offsets; a.groups = num_groups; a.poff_out = padded_offsets_out;
+  a.rht = apply_rht != 0; a.mask = rht_sign_mask;
+  a.codes = col->codes; a.ldc = col->ld_codes; a.scales = col->scales; a.lds = col->ld_scales;
+  a.ws = (Workspace*)workspace;
+  a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
+  a.sr = rounding == NVFP4Q_SR;
+  a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
+  return done(launch_grouped(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

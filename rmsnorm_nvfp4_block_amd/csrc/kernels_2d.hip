@@ -1,0 +1,176 @@
+// 2D NVFP4 for gfx950: rowwise and columnwise (transposed) planes of one bf16
+// tensor under one per-tensor scale, read once from HBM.
+//
+// One workgroup (256 threads) owns a 128 x 128 tile.
+//  * Load: thread t reads 8 consecutive columns (16 B) of rows t/16 + 16j,
+//    j = 0..7, so a wave reads 4 rows x 256 B per instruction. The lane pair
+//    (t, t^1) holds one rowwise 16-element block; rowwise codes leave as 4-byte
+//    stores that are 64 contiguous bytes per row.
+//  * The raw tile is staged in LDS (32 KiB) with the 16-byte chunk index of a
+//    row XOR-ed by 4 * ((row / 16) mod 4), which spreads the eight 16-row
+//    blocks a wave reads at one time over all banks.
+//  * Columnwise: thread t owns columns 4 * (t / 8) .. +3 of rows
+//    16 * (t % 8) .. +15 (16 LDS reads of 8 bytes), i.e. four columnwise blocks;
+//    eight consecutive threads write 64 contiguous code bytes of one plane row.
+// "[nvfp4_training] Optimize CuteDSL kernels for NVFP4 training", Optimization
+// item 2 (the 2D weight kernel: wide shared-memory reads instead of 16-bit
+// ones, paired columnwise reads) and item 5 (scale bytes).
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace nvfp4q {
+
+namespace {
+
+constexpr int kT = 256;
+constexpr int kTileR = 128, kTileC = 128;
+constexpr int kRowBytes = kTileC * 2;  // 256 B per staged row
+
+__device__ __forceinline__ uint32_t swz_chunk(uint32_t chunk, uint32_t row) {
+  return chunk ^ (((row >> 4) & 3u) << 2);
+}
+
+template <bool ROW, bool COL, bool SR>
+__global__ __launch_bounds__(kT) void k_quant_2d(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols,
+                                                 int64_t ld_x, uint8_t* __restrict__ rcodes, int64_t rldc,
+                                                 uint8_t* __restrict__ rscales, int64_t rlds,
+                                                 uint8_t* __restrict__ ccodes, int64_t cldc,
+                                                 uint8_t* __restrict__ cscales, int64_t clds, const Workspace* ws,
+                                                 const float* amax_in, float* amax_out, float* scale_out,
+                                                 uint64_t seed, uint32_t offset, uint32_t tiles_c) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTileR * kRowBytes];
+  GScale g;
+  if (amax_in) {
+    float a = *amax_in;
+    g = global_scale(a);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      if (amax_out) *amax_out = a;
+      if (scale_out) *scale_out = g.dec;
+    }
+  } else {
+    g.enc = ws->enc[0];
+    g.dec = ws->dec[0];
+  }
+  const uint32_t t = threadIdx.x;
+  const uint32_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
+  const uint32_t row0 = tr * kTileR, col0 = tc * kTileC;
+
+  // ---- load 8 rows x 16 B per thread
+  const uint32_t chunk = t & 15, rsub = t >> 4;
+  const uint32_t col = col0 + chunk * 8;
+  uint4 q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t r = row0 + rsub + 16 * j;
+    const bool ok = r < rows && col < cols;
+    uint4 z = {0u, 0u, 0u, 0u};
+    q[j] = ok ? *reinterpret_cast<const uint4*>(x + (int64_t)r * ld_x + col) : z;
+  }
+  if constexpr (COL) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t lr = rsub + 16 * j;
+      *reinterpret_cast<uint4*>(tile + lr * kRowBytes + swz_chunk(chunk, lr) * 16) = q[j];
+    }
+  }
+  // ---- rowwise plane from registers
+  if constexpr (ROW) {
+    const uint32_t nbr = cols >> 4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t r = row0 + rsub + 16 * j;
+      const bool ok = r < rows && col < cols;
+      float v[8];
+      widen8(q[j], v);
+      float m = max8_abs(v);
+      float bm = fmaxf(m, swap_pair(m));
+      uint32_t sc = block_scale(bm, g.enc);
+      float rc = encode_mult(sc, g.dec);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] * rc;
+      uint32_t word;
+      if constexpr (SR) {
+        U4 w = block_random((uint64_t)r * nbr + (col >> 4), 0, seed, offset);
+        const bool odd = (t & 1) != 0;
+        word = sr_pack8(v, odd ? w.z : w.x, odd ? w.w : w.y);
+      } else {
+        word = rtne_pack8(v);
+      }
+      if (ok) {
+        *reinterpret_cast<uint32_t*>(rcodes + (int64_t)r * rldc + (col >> 1)) = word;
+        if ((t & 1) == 0) rscales[(int64_t)r * rlds + (col >> 4)] = (uint8_t)sc;
+      }
+    }
+  }
+  // ---- columnwise plane from the staged tile
+  if constexpr (COL) {
+    __syncthreads();
+    const uint32_t mb = t & 7, cg = t >> 3;           // 8 row blocks x 32 column quads
+    const uint32_t lc = cg * 4;                        // first local column
+    const uint32_t cchunk = lc >> 3, chalf = (lc >> 2) & 1;
+    uint2 d[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t lr = mb * 16 + i;
+      d[i] = *reinterpret_cast<const uint2*>(tile + lr * kRowBytes + swz_chunk(cchunk, lr) * 16 + chalf * 8);
+    }
+    const uint32_t grow = row0 + mb * 16;              // first row of the block
+    const bool rok = grow < rows;
+    const uint32_t nbc = rows >> 4;                    // column blocks per plane row
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t gc = col0 + lc + c;
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t w = (c < 2) ? d[i].x : d[i].y;
+        v[i] = (c & 1) ? bf_hi(w) : bf_lo(w);
+      }
+      float m = fmaxf(max8_abs(v), max8_abs(v + 8));
+      uint32_t sc = block_scale(m, g.enc);
+      float rc = encode_mult(sc, g.dec);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
+      uint2 out;
+      if constexpr (SR) {
+        U4 w = block_random((uint64_t)gc * nbc + (grow >> 4), 1, seed, offset);
+        out.x = sr_pack8(v, w.x, w.y);
+        out.y = sr_pack8(v + 8, w.z, w.w);
+      } else {
+        out.x = rtne_pack8(v);
+        out.y = rtne_pack8(v + 8);
+      }
+      if (rok && gc < cols) {
+        *reinterpret_cast<uint2*>(ccodes + (int64_t)gc * cldc + (grow >> 1)) = out;
+        cscales[(int64_t)gc * clds + (grow >> 4)] = (uint8_t)sc;
+      }
+    }
+  }
+}
+
+template <bool ROW, bool COL>
+void launch_2d_rc(const TwoDArgs& a, hipStream_t s) {
+  const uint32_t tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
+  const uint32_t tiles_c = (uint32_t)((a.cols + kTileC - 1) / kTileC);
+  dim3 grid(tiles_r * tiles_c), block(kT);
+  if (a.sr)
+    hipLaunchKernelGGL((k_quant_2d<ROW, COL, true>), grid, block, 0, s, (const uint16_t*)a.x, (uint32_t)a.rows,
+                       (uint32_t)a.cols, a.ld_x, a.rcodes, a.rldc, a.rscales, a.rlds, a.ccodes, a.cldc, a.cscales,
+                       a.clds, a.ws, a.amax_in, a.amax_out, a.scale_out, a.seed, a.offset, tiles_c);
+  else
+    hipLaunchKernelGGL((k_quant_2d<ROW, COL, false>), grid, block, 0, s, (const uint16_t*)a.x, (uint32_t)a.rows,
+                       (uint32_t)a.cols, a.ld_x, a.rcodes, a.rldc, a.rscales, a.rlds, a.ccodes, a.cldc, a.cscales,
+                       a.clds, a.ws, a.amax_in, a.amax_out, a.scale_out, a.seed, a.offset, tiles_c);
+}
+
+}  // namespace
+
+hipError_t launch_quant_2d(const TwoDArgs& a, hipStream_t s) {
+  const bool row = a.rcodes != nullptr, col = a.ccodes != nullptr;
+  if (row && col) launch_2d_rc<true, true>(a, s);
+  else if (row) launch_2d_rc<true, false>(a, s);
+  else if (col) launch_2d_rc<false, true>(a, s);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4q

@@ -1,0 +1,310 @@
+// Grouped (per-expert) columnwise NVFP4 for gfx950, optionally after a
+// 16-point random Hadamard transform along the tokens of each 16-token block.
+//
+// Work unit: a workgroup (4 waves) owns 128 tokens x 256 columns of one group;
+// wave w takes columns 64w .. 64w+63 of that range. Lane l holds columns
+// 8 * (l / 8) .. +7 (16-byte loads) of the 16 tokens of token block l % 8, so
+// the transform and the block amax of a column are entirely in-lane, and eight
+// consecutive lanes write 64 contiguous code bytes of one plane row.
+//
+// The group of a workgroup is found on the device from the offsets: each lane of
+// wave 0 takes one group, the padded lengths and tile counts are prefix-summed
+// across the wave, and a ballot locates the group whose tile range holds the
+// workgroup's slot. Workgroups past the last tile only take part in the
+// arrival count. The grid is sized on the host for the largest possible number
+// of tiles, (rows + 15 G) / 128 + G, since the offsets live on the device.
+//
+// "[nvfp4_training] Optimize CuteDSL kernels for NVFP4 training": Grouped
+// allocation tail (stop at the last padded row, leave the tail untouched);
+// Config surface and AUTO (64 groups, device offsets); Fast math (the
+// transform's bf16 round-through on the columnwise path); Optimization item 3
+// (one Philox draw per 16-element block).
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace nvfp4q {
+
+namespace {
+
+constexpr int kT = 256;
+constexpr int kTileTok = 128;   // tokens per workgroup tile (8 blocks of 16)
+constexpr int kTileCol = 256;   // columns per workgroup tile
+
+struct GroupTile {
+  int g;          // group index, or -1 when the slot holds no tile
+  int tok0;       // first padded token of the tile within the group
+  int n;          // real tokens of the group
+  int pg;         // padded tokens of the group
+  int row0;       // first row of the group in x
+  int poff;       // first plane column of the group
+  int mpad;       // total padded tokens (plane length)
+};
+
+// Wave 0 of the workgroup locates the tile; the result is shared through LDS.
+// Offsets are clamped to [0, rows] so that malformed device offsets cannot
+// lead to reads outside x.
+__device__ __forceinline__ void group_range(const int32_t* __restrict__ offsets, int g, int rows, int& lo, int& n) {
+  lo = min(max(offsets[g], 0), rows);
+  const int hi = min(max(offsets[g + 1], lo), rows);
+  n = hi - lo;
+}
+
+__device__ GroupTile locate_tile(const int32_t* __restrict__ offsets, int groups, int rows, uint32_t slot) {
+  __shared__ GroupTile s;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int lo = 0, n = 0;
+    if (lane < groups) group_range(offsets, lane, rows, lo, n);
+    const int p = (n + 15) & ~15;
+    const int tiles = (p + kTileTok - 1) / kTileTok;
+    int ps = p, ts = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int a = __shfl_up(ps, o, 64), b = __shfl_up(ts, o, 64);
+      if (lane >= o) {
+        ps += a;
+        ts += b;
+      }
+    }
+    const uint64_t before = __ballot(lane < groups && (uint32_t)ts <= slot);
+    const int g = __popcll(before);
+    const int gs = g < 64 ? g : 63;
+    const int ts_g = __shfl(ts, gs, 64), tiles_g = __shfl(tiles, gs, 64);
+    const int ps_g = __shfl(ps, gs, 64), p_g = __shfl(p, gs, 64);
+    const int n_g = __shfl(n, gs, 64), lo_g = __shfl(lo, gs, 64);
+    const int mpad = __shfl(ps, 63, 64);
+    if (lane == 0) {
+      GroupTile t;
+      t.g = (g < groups) ? g : -1;
+      t.tok0 = (int)(slot - (uint32_t)(ts_g - tiles_g)) * kTileTok;
+      t.n = n_g;
+      t.pg = p_g;
+      t.row0 = lo_g;
+      t.poff = ps_g - p_g;
+      t.mpad = mpad;
+      s = t;
+    }
+  }
+  __syncthreads();
+  return s;
+}
+
+// Padded offsets of all groups (wave 0, lanes 0..groups): Poff[0] = 0,
+// Poff[g + 1] = Poff[g] + 16 * ceil(n_g / 16).
+__device__ void write_poff(const int32_t* __restrict__ offsets, int groups, int rows, int32_t* out_a,
+                           int32_t* out_b) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int lo = 0, n = 0;
+    if (lane < groups) group_range(offsets, lane, rows, lo, n);
+    int ps = (n + 15) & ~15;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int a = __shfl_up(ps, o, 64);
+      if (lane >= o) ps += a;
+    }
+    if (lane < groups) {
+      if (out_a) out_a[lane + 1] = ps;
+      if (out_b) out_b[lane + 1] = ps;
+    }
+    if (lane == 0) {
+      if (out_a) out_a[0] = 0;
+      if (out_b) out_b[0] = 0;
+    }
+  }
+}
+
+// Load the lane's 16 tokens x 8 columns (zero for padding rows and columns
+// past the end).
+__device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t ld_x, const GroupTile& t,
+                                           uint32_t blk_tok0, uint32_t col, uint32_t cols, uint4 q[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int lt = (int)blk_tok0 + i;
+    const bool ok = lt < t.n && col < cols;
+    uint4 z = {0u, 0u, 0u, 0u};
+    q[i] = ok ? *reinterpret_cast<const uint4*>(x + (int64_t)(t.row0 + lt) * ld_x + col) : z;
+  }
+}
+
+// Column c (0..7) of the lane's 16 x 8 block as fp32.
+__device__ __forceinline__ void column(const uint4 q[16], int c, float v[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t w = (c >> 1) == 0 ? q[i].x : (c >> 1) == 1 ? q[i].y : (c >> 1) == 2 ? q[i].z : q[i].w;
+    v[i] = (c & 1) ? bf_hi(w) : bf_lo(w);
+  }
+}
+
+// t = D v (sign flips from the mask), then four butterfly stages in Sylvester
+// order: for h = 1, 2, 4, 8 the pairs (i, i + h) with (i & h) == 0 become
+// (a + b, a - b). The caller applies the 0.25 scaling.
+__device__ __forceinline__ void signed_fwht16(float v[16], uint32_t mask) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((mask >> i) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i & h) continue;
+      const float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
+// Pass 1: per-group amax of the (transformed, bf16-rounded) columnwise values.
+template <bool RHT>
+__global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict__ x, int rows, uint32_t cols, int64_t ld_x,
+                                                     const int32_t* __restrict__ offsets, int groups, uint32_t mask,
+                                                     Workspace* ws, float* amax_out, float* scale_out,
+                                                     int32_t* poff_out) {
+  const GroupTile t = locate_tile(offsets, groups, rows, blockIdx.x);
+  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float m = 0.0f;
+  if (t.g >= 0) {
+    const uint32_t mb = lane & 7, cg = lane >> 3;
+    const uint32_t col = blockIdx.y * kTileCol + wv * 64 + cg * 8;
+    const uint32_t blk_tok0 = (uint32_t)t.tok0 + mb * 16;
+    if ((int)blk_tok0 < t.pg) {
+      uint4 q[16];
+      load_block(x, ld_x, t, blk_tok0, col, cols, q);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float v[16];
+        column(q, c, v);
+        if constexpr (RHT) signed_fwht16(v, mask);
+        m = fmaxf(m, fmaxf(max8_abs(v), max8_abs(v + 8)));
+      }
+      // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
+      // round-to-nearest-even are both monotone.
+      if constexpr (RHT) m = bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
+    }
+  }
+  __shared__ float red[kT / 64];
+  m = wave_max(m);
+  if (lane == 0) red[wv] = m;
+  __syncthreads();
+  __shared__ bool last;
+  if (threadIdx.x == 0) {
+    const float wm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (t.g >= 0) atomic_max_f32_nonneg(&ws->amax_bits[t.g], wm);
+    last = arrive_last(&ws->count, gridDim.x * gridDim.y);
+  }
+  __syncthreads();
+  if (last) {
+    if (threadIdx.x < 64 && (int)threadIdx.x < groups) {
+      const int g = threadIdx.x;
+      const float a = load_amax(&ws->amax_bits[g]);
+      const GScale s = global_scale(a);
+      ws->enc[g] = s.enc;
+      ws->dec[g] = s.dec;
+      ws->amax[g] = a;
+      if (amax_out) amax_out[g] = a;
+      if (scale_out) scale_out[g] = s.dec;
+      __hip_atomic_store(&ws->amax_bits[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    write_poff(offsets, groups, rows, poff_out, nullptr);
+  }
+}
+
+// Pass 2: transform (optional), bf16 round-through, per-block scale and codes.
+template <bool RHT, bool SR>
+__global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict__ x, int rows, uint32_t cols, int64_t ld_x,
+                                                      const int32_t* __restrict__ offsets, int groups,
+                                                      uint32_t mask, uint8_t* __restrict__ codes, int64_t ldc,
+                                                      uint8_t* __restrict__ scales, int64_t lds,
+                                                      const Workspace* ws, const float* amax_in, float* amax_out,
+                                                      float* scale_out, int32_t* poff_out, uint64_t seed,
+                                                      uint32_t offset, int64_t cap) {
+  const GroupTile t = locate_tile(offsets, groups, rows, blockIdx.x);
+  if (amax_in && blockIdx.x == 0 && blockIdx.y == 0) {
+    if (threadIdx.x < 64 && (int)threadIdx.x < groups) {
+      const float a = amax_in[threadIdx.x];
+      if (amax_out) amax_out[threadIdx.x] = a;
+      if (scale_out) scale_out[threadIdx.x] = global_scale(a).dec;
+    }
+    write_poff(offsets, groups, rows, poff_out, nullptr);
+  }
+  if (t.g < 0) return;
+  GScale g;
+  if (amax_in) {
+    g = global_scale(amax_in[t.g]);
+  } else {
+    g.enc = ws->enc[t.g];
+    g.dec = ws->dec[t.g];
+  }
+  const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t mb = lane & 7, cg = lane >> 3;
+  const uint32_t col = blockIdx.y * kTileCol + wv * 64 + cg * 8;
+  const uint32_t blk_tok0 = (uint32_t)t.tok0 + mb * 16;
+  if ((int)blk_tok0 >= t.pg || col >= cols) return;
+  // Plane capacity guard: only malformed offsets can reach it.
+  if ((int64_t)t.poff + blk_tok0 + 16 > cap) return;
+  uint4 q[16];
+  load_block(x, ld_x, t, blk_tok0, col, cols, q);
+  const uint32_t pcol = (uint32_t)t.poff + blk_tok0;      // plane column of the block's first token
+  const uint64_t nbp = (uint64_t)(t.mpad >> 4);            // blocks per plane row
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t gc = col + c;
+    float v[16];
+    column(q, c, v);
+    if constexpr (RHT) {
+      signed_fwht16(v, mask);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const uint32_t p = pack_bf16(v[i] * 0.25f, v[i + 1] * 0.25f);
+        v[i] = bf_lo(p);
+        v[i + 1] = bf_hi(p);
+      }
+    }
+    const float m = fmaxf(max8_abs(v), max8_abs(v + 8));
+    const uint32_t sc = block_scale(m, g.enc);
+    const float rc = encode_mult(sc, g.dec);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
+    uint2 out;
+    if constexpr (SR) {
+      const U4 w = block_random((uint64_t)gc * nbp + (pcol >> 4), 1, seed, offset);
+      out.x = sr_pack8(v, w.x, w.y);
+      out.y = sr_pack8(v + 8, w.z, w.w);
+    } else {
+      out.x = rtne_pack8(v);
+      out.y = rtne_pack8(v + 8);
+    }
+    *reinterpret_cast<uint2*>(codes + (int64_t)gc * ldc + (pcol >> 1)) = out;
+    scales[(int64_t)gc * lds + (pcol >> 4)] = (uint8_t)sc;
+  }
+}
+
+template <bool RHT>
+void launch_grouped_r(const GroupArgs& a, dim3 grid, hipStream_t s) {
+  const uint16_t* x = (const uint16_t*)a.x;
+  const int64_t cap = a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16;
+  if (!a.amax_in)
+    hipLaunchKernelGGL((k_grouped_amax<RHT>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets,
+                       a.groups, a.mask, a.ws, a.amax_out, a.scale_out, a.poff_out);
+  if (a.sr)
+    hipLaunchKernelGGL((k_grouped_quant<RHT, true>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets,
+                       a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in, a.amax_out,
+                       a.scale_out, a.poff_out, a.seed, a.offset, cap);
+  else
+    hipLaunchKernelGGL((k_grouped_quant<RHT, false>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x,
+                       a.offsets, a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in,
+                       a.amax_out, a.scale_out, a.poff_out, a.seed, a.offset, cap);
+}
+
+}  // namespace
+
+hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {
+  const int64_t max_tiles = (a.rows + 15 * (int64_t)a.groups + kTileTok - 1) / kTileTok + a.groups;
+  const uint32_t col_tiles = (uint32_t)((a.cols + kTileCol - 1) / kTileCol);
+  dim3 grid((uint32_t)max_tiles, col_tiles);
+  if (a.rht) launch_grouped_r<true>(a, grid, s);
+  else launch_grouped_r<false>(a, grid, s);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4q

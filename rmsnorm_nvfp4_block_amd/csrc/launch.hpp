@@ -1,0 +1,80 @@
+// Host-side launch interface between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4q {
+
+struct Workspace;
+
+// Arguments of the rowwise paths (quantize and RMSNorm).
+struct RowArgs {
+  const void* x;
+  int64_t rows, cols, ld_x;
+  const void* gamma;
+  const void* beta;
+  float woff, eps;
+  void* y;
+  int64_t ld_y;
+  uint8_t* codes;
+  int64_t ldc;
+  uint8_t* scales;
+  int64_t lds;
+  Workspace* ws;
+  const float* amax_in;
+  float* amax_out;
+  float* scale_out;
+  bool sr;
+  uint64_t seed;
+  uint32_t offset;
+};
+
+// Arguments of the 2D (rowwise + columnwise) path.
+struct TwoDArgs {
+  const void* x;
+  int64_t rows, cols, ld_x;
+  uint8_t *rcodes, *rscales;
+  int64_t rldc, rlds;
+  uint8_t *ccodes, *cscales;
+  int64_t cldc, clds;
+  Workspace* ws;
+  const float* amax_in;
+  float* amax_out;
+  float* scale_out;
+  bool sr;
+  uint64_t seed;
+  uint32_t offset;
+};
+
+// Arguments of the grouped columnwise path.
+struct GroupArgs {
+  const void* x;
+  int64_t rows, cols, ld_x;
+  const int32_t* offsets;
+  int32_t groups;
+  int32_t* poff_out;
+  bool rht;
+  uint32_t mask;
+  uint8_t *codes, *scales;
+  int64_t ldc, lds;
+  Workspace* ws;
+  const float* amax_in;
+  float* amax_out;
+  float* scale_out;
+  bool sr;
+  uint64_t seed;
+  uint32_t offset;
+};
+
+hipError_t launch_empty_scale(float* amax_out, float* scale_out, int n, hipStream_t s);
+hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s);
+hipError_t launch_quant_rows(const RowArgs& a, hipStream_t s);
+hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s);
+int rms_max_cols();
+
+hipError_t launch_quant_2d(const TwoDArgs& a, hipStream_t s);
+
+hipError_t launch_grouped(const GroupArgs& a, hipStream_t s);
+
+}  // namespace nvfp4q

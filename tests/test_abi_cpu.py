@@ -1,0 +1,141 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function that
+include/nvfp4q.h declares, and rejects bad arguments before touching the GPU.
+Nothing here launches a kernel (every call below fails validation first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4q.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4q_\w+|rmsnorm_nvfp4q)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import rmsnorm_nvfp4_block_amd as q
+
+    if not os.path.exists(q.lib_path):
+        pytest.fail("libnvfp4q.so is not built (run __graft_entry__.build())")
+    return q.load()
+
+
+def test_header_declares_the_four_entry_points():
+    d = _declared()
+    for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_grouped"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_names_match_the_abi():
+    import rmsnorm_nvfp4_block_amd as q
+
+    for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_grouped"):
+        assert callable(getattr(q, name))
+
+
+def test_status_strings_and_workspace(lib):
+    import rmsnorm_nvfp4_block_amd as q
+
+    assert lib.nvfp4q_version() == 1
+    assert q.nvfp4q_workspace_bytes() == 4096
+    for s in range(7):
+        assert q.nvfp4q_status_string(s)
+    assert q.nvfp4q_status_string(99) == "unknown status"
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call fails validation
+
+
+def _quant(lib, x=FAKE, dtype=0, rows=4, cols=32, ld=32, codes=FAKE, ldc=16, scales=FAKE, lds=2, rnd=0,
+           rng=True, ws=FAKE, wsb=4096):
+    import rmsnorm_nvfp4_block_amd as q
+
+    plane = q.Plane(codes, ldc, scales, lds)
+    g = q.Global(None, None, None)
+    r = q.Rng(1, 0)
+    return lib.nvfp4q_quantize(x, dtype, rows, cols, ld, ctypes.byref(g), ctypes.byref(plane), rnd,
+                               ctypes.byref(r) if rng else None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=1), 4),                  # only bf16
+    (dict(cols=24, ld=24), 2),           # cols % 16
+    (dict(ld=16), 2),                    # ld < cols
+    (dict(rows=-1), 2),
+    (dict(x=0), 1),                      # NULL input
+    (dict(x=FAKE + 2), 3),               # misaligned input
+    (dict(ld=36, cols=32), 3),           # ld not a multiple of 8 elements
+    (dict(codes=0), 1),
+    (dict(ldc=8), 2),                    # plane row too short
+    (dict(codes=FAKE + 8), 3),
+    (dict(ldc=20), 3),
+    (dict(rnd=2), 4),
+    (dict(rnd=1, rng=False), 1),         # SR needs an rng
+    (dict(ws=0), 6),
+    (dict(ws=FAKE + 16), 6),             # workspace alignment
+    (dict(wsb=100), 6),
+])
+def test_quantize_validation(lib, kw, status):
+    assert _quant(lib, **kw) == status
+
+
+def test_rmsnorm_validation(lib):
+    import rmsnorm_nvfp4_block_amd as q
+
+    plane = q.Plane(FAKE, 16, FAKE, 2)
+    g = q.Global(None, None, None)
+    r = q.Rng(0, 0)
+
+    def call(gamma=FAKE, beta=None, woff=0.0, eps=1e-6, y=None, ldy=0, hidden=32, p=plane, ws=FAKE):
+        return lib.rmsnorm_nvfp4q(FAKE, 0, 4, hidden, hidden, gamma, beta, woff, eps, y, ldy, ctypes.byref(g),
+                                  ctypes.byref(p), 0, ctypes.byref(r), ws, 4096, None)
+
+    assert call(gamma=None) == 1
+    assert call(beta=FAKE + 4) == 3
+    assert call(woff=0.5) == 4
+    assert call(eps=-1.0) == 2
+    assert call(hidden=40) == 2
+    assert call(hidden=32 * 512 + 16, p=q.Plane(FAKE, 8208, FAKE, 1026)) == 4   # beyond the register-resident row
+    assert call(p=q.Plane(None, 0, None, 0)) == 1                               # nothing to produce
+    assert call(p=q.Plane(None, 0, None, 0), y=FAKE, ldy=16) == 2
+    assert call(p=q.Plane(None, 0, None, 0), y=FAKE + 2, ldy=32) == 3
+    assert call(ws=None) == 6
+
+
+def test_2d_and_grouped_validation(lib):
+    import rmsnorm_nvfp4_block_amd as q
+
+    g = q.Global(None, None, None)
+    r = q.Rng(0, 0)
+    none = q.Plane(None, 0, None, 0)
+    row = q.Plane(FAKE, 16, FAKE, 2)
+    col = q.Plane(FAKE, 16, FAKE, 2)
+    # columnwise plane needs rows % 16 == 0
+    assert lib.nvfp4q_quantize_2d(FAKE, 0, 24, 32, 32, ctypes.byref(g), ctypes.byref(row), ctypes.byref(col), 0,
+                                  ctypes.byref(r), FAKE, 4096, None) == 2
+    assert lib.nvfp4q_quantize_2d(FAKE, 0, 32, 32, 32, ctypes.byref(g), ctypes.byref(none), ctypes.byref(none), 0,
+                                  ctypes.byref(r), FAKE, 4096, None) == 1
+
+    def grouped(groups=4, rht=1, mask=0x1234, ldc=64, lds=8, offs=FAKE, rows=64):
+        p = q.Plane(FAKE, ldc, FAKE, lds)
+        return lib.nvfp4q_grouped(FAKE, 0, rows, 32, 32, offs, groups, None, rht, mask, ctypes.byref(g),
+                                  ctypes.byref(p), 1, ctypes.byref(r), FAKE, 4096, None)
+
+    assert grouped(groups=0) == 2
+    assert grouped(groups=65) == 2
+    assert grouped(rht=2) == 4
+    assert grouped(mask=0x10000) == 4
+    assert grouped(offs=0) == 1
+    assert grouped(ldc=48) == 2       # 2 * 48 < 64 + 15 * 4
+    assert grouped(lds=7) == 2        # 16 * 7 < 124

@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Quantize-only paths (rowwise, 2D, grouped) must be bit-exact in codes, scales,
+amax and S_dec. The fused RMSNorm path follows the rules of its contract: y
+within 1e-2 relative (+2^-20 absolute) of the float64 oracle; the codes equal,
+bit for bit, the oracle's quantization of the GPU's own bf16 y; against the
+float64 oracle at most 1e-4 of the codes differ, each by at most one magnitude
+step. Full-size workloads are checked on sampled rows, columns or groups.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import formats as F
+from tests.gpu_helpers import (assert_f32_bits, assert_same_bits, code_step_mismatch, f32, np_u8, to_dev,
+                               to_np_bf16)
+
+pytestmark = pytest.mark.gpu
+
+SEEDS = [0, 1, 2, 224]
+
+
+def _bf16(rng, shape, scale=1.0):
+    return workloads.to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def _check_rowwise(q, got, cols, name=""):
+    assert_same_bits(name + " codes", np_u8(got["codes"], cols // 2), q["codes"])
+    assert_same_bits(name + " scales", np_u8(got["scales"], cols // 16), q["scales"])
+    assert_f32_bits(name + " amax", f32(got["amax"])[0], q["amax"])
+    assert_f32_bits(name + " scale", f32(got["scale"])[0], q["s_dec"])
+
+
+# ---------------------------------------------------------------- quantize
+@pytest.mark.parametrize("seed", SEEDS)
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_quantize_256x1024(gpu_lib, seed, rounding):
+    w = workloads.quantize_only(seed=seed)
+    got = gpu_lib.nvfp4q_quantize(to_dev(w.x), rounding=rounding, seed=0x5EED, offset=seed)
+    q = oracle.quantize_rowwise(w.x, rounding=rounding, seed=0x5EED, offset=seed)
+    _check_rowwise(q, got, 1024)
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (37, 1040), (130, 2064), (5, 7168), (1000, 512), (2, 16400)])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_quantize_ragged(gpu_lib, shape, rounding):
+    rng = np.random.default_rng(hash(shape) % 1000)
+    x = _bf16(rng, shape, 3.0)
+    got = gpu_lib.nvfp4q_quantize(to_dev(x), rounding=rounding, seed=77, offset=3)
+    _check_rowwise(oracle.quantize_rowwise(x, rounding=rounding, seed=77, offset=3), got, shape[1])
+
+
+def test_quantize_extremes(gpu_lib):
+    # every finite bf16 value, including subnormals and the largest magnitudes
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    bits = bits[np.isfinite(F.bf16_to_f32(bits))]
+    bits = bits[: len(bits) // 16 * 16]
+    rng = np.random.default_rng(5)
+    x = rng.permutation(bits).reshape(-1, 256)
+    for rounding in ("rtne", "sr"):
+        got = gpu_lib.nvfp4q_quantize(to_dev(x), rounding=rounding, seed=9)
+        _check_rowwise(oracle.quantize_rowwise(x, rounding=rounding, seed=9), got, 256, rounding)
+    # one block per magnitude band: small blocks meet large global scales
+    xs = (F.bf16_to_f32(x) * np.float32(1.0)).reshape(-1, 16)
+    order = np.argsort(np.abs(xs).max(1))
+    x2 = F.f32_to_bf16(xs[order]).reshape(-1, 256)
+    got = gpu_lib.nvfp4q_quantize(to_dev(x2))
+    _check_rowwise(oracle.quantize_rowwise(x2), got, 256, "sorted")
+
+
+@pytest.mark.parametrize("amax", [2688.0, 1.0, 0.37, 1e-30, 1e-38, 3e38])
+def test_quantize_given_amax(gpu_lib, amax):
+    import torch
+
+    rng = np.random.default_rng(6)
+    x = _bf16(rng, (64, 256), 2.0)
+    a = torch.tensor([amax], dtype=torch.float32, device="cuda")
+    for rounding in ("rtne", "sr"):
+        got = gpu_lib.nvfp4q_quantize(to_dev(x), amax=a, rounding=rounding, seed=1)
+        q = oracle.quantize_rowwise(x, amax=np.float32(amax), rounding=rounding, seed=1)
+        _check_rowwise(q, got, 256, f"amax={amax} {rounding}")
+
+
+def test_quantize_zero_and_empty(gpu_lib):
+    import torch
+
+    x = np.zeros((4, 64), np.uint16)
+    got = gpu_lib.nvfp4q_quantize(to_dev(x))
+    _check_rowwise(oracle.quantize_rowwise(x), got, 64, "zeros")
+    e = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    got = gpu_lib.nvfp4q_quantize(e)
+    assert f32(got["amax"])[0] == 0.0 and f32(got["scale"])[0] == 1.0
+
+
+def test_golden_blocks(gpu_lib):
+    import json, os, torch
+
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_blocks.json")))["cases"]
+    for c in cases:
+        x = F.f32_to_bf16(np.array(c["x"], np.float32)).reshape(1, 16)
+        a = None if c["amax_in"] is None else torch.tensor([c["amax_in"]], dtype=torch.float32, device="cuda")
+        got = gpu_lib.nvfp4q_quantize(to_dev(x), amax=a)
+        assert np_u8(got["codes"], 8).tolist()[0] == c["bytes"], c["name"]
+        assert int(np_u8(got["scales"], 1)[0, 0]) == c["scale"], c["name"]
+        assert int(f32(got["scale"]).view(np.uint32)[0]) == c["s_dec_bits"], c["name"]
+
+
+def test_repeated_calls_share_the_workspace(gpu_lib):
+    rng = np.random.default_rng(7)
+    xs = [_bf16(rng, (97, 528), s) for s in (1.0, 100.0, 0.01)]
+    for _ in range(2):
+        for x in xs:
+            got = gpu_lib.nvfp4q_quantize(to_dev(x))
+            _check_rowwise(oracle.quantize_rowwise(x), got, 528)
+
+
+def test_graph_capture_replays(gpu_lib):
+    import ctypes, torch
+    q = gpu_lib
+    rng = np.random.default_rng(8)
+    x1, x2 = _bf16(rng, (128, 1024)), _bf16(rng, (128, 1024), 7.0)
+    xd = to_dev(x1)
+    codes = torch.empty((128, 512), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((128, 64), dtype=torch.uint8, device="cuda")
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    q.nvfp4q_quantize(xd, codes=codes, scales=scales)   # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            out = q.nvfp4q_quantize(xd, codes=codes, scales=scales)
+    for rep, x in enumerate([x1, x2, x1, x2]):
+        xd.copy_(to_dev(x))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle.quantize_rowwise(x)
+        assert_same_bits(f"replay {rep} codes", np_u8(codes), ref["codes"])
+        assert_same_bits(f"replay {rep} scales", np_u8(scales), ref["scales"])
+        assert_f32_bits(f"replay {rep} amax", f32(out["amax"])[0], ref["amax"])
+        # eager work between replays
+        e = q.nvfp4q_quantize(to_dev(x2))
+        _check_rowwise(oracle.quantize_rowwise(x2), e, 1024, "eager")
+
+
+# ---------------------------------------------------------------- RMSNorm
+def _check_rms(w, got, rounding="rtne", seed=0, offset=0, amax_given=None):
+    """Contract rules for the fused path (see module docstring)."""
+    cols = w.cols
+    y_gpu = to_np_bf16(got["y"])
+    y_ref, y64, _ = oracle.rmsnorm_bf16(w.x, w.gamma, w.beta, w.weight_offset, w.eps, return_f64=True)
+    yg = F.bf16_to_f32(y_gpu).astype(np.float64)
+    err = np.abs(yg - y64)
+    assert np.all(err <= 1e-2 * np.abs(y64) + 2.0 ** -20), f"y error max {err.max()}"
+    # codes are the exact quantization of the GPU's own y
+    amax = amax_given if amax_given is not None else np.float32(np.max(np.abs(yg)))
+    q_own = oracle.quantize_rowwise(y_gpu, amax=amax, rounding=rounding, seed=seed, offset=offset)
+    _check_rowwise(q_own, got, cols, "quantize(y_gpu)")
+    # against the float64 oracle
+    q_ref = oracle.quantize_rowwise(y_ref, amax=amax_given, rounding=rounding, seed=seed, offset=offset)
+    n, ok = code_step_mismatch(np_u8(got["codes"], cols // 2), q_ref["codes"])
+    assert ok, "a code differs by more than one step"
+    assert n <= 1e-4 * w.rows * cols, f"{n} codes differ from the float64 oracle"
+    return n
+
+
+@pytest.mark.parametrize("seed", [3, 224])
+def test_rmsnorm_decode_8x7168(gpu_lib, seed):
+    w = workloads.decode(seed=seed)
+    got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), to_dev(w.beta), eps=w.eps, y_out=True)
+    _check_rms(w, got)
+
+
+@pytest.mark.parametrize("seed", [2, 224])
+def test_rmsnorm_prefill_4096x4096(gpu_lib, seed):
+    w = workloads.prefill(seed=seed)
+    got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), eps=w.eps, y_out=True)
+    _check_rms(w, got)
+
+
+@pytest.mark.parametrize("shape,bias,woff", [((5, 1040), True, 1.0), ((64, 16), False, 0.0), ((3, 16384), True, 0.0),
+                                             ((33, 4096), False, 1.0), ((1, 7168), True, 0.0),
+                                             ((300, 2560), True, 0.0)])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_rmsnorm_ragged(gpu_lib, shape, bias, woff, rounding):
+    rng = np.random.default_rng(shape[0] * 31 + shape[1])
+    T, H = shape
+    w = workloads.Workload("t", _bf16(rng, shape, 2.0), gamma=_bf16(rng, (H,), 0.3),
+                           beta=_bf16(rng, (H,), 0.05) if bias else None, weight_offset=woff, eps=1e-5)
+    got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), to_dev(w.beta) if bias else None,
+                                 weight_offset=woff, eps=w.eps, y_out=True, rounding=rounding, seed=11, offset=1)
+    _check_rms(w, got, rounding, 11, 1)
+
+
+def test_rmsnorm_given_amax_and_y_only(gpu_lib):
+    import torch
+
+    w = workloads.decode(seed=9)
+    q = oracle.rmsnorm_quantize(w.x, w.gamma, w.beta, 0.0, w.eps)
+    a = torch.tensor([q["amax"]], dtype=torch.float32, device="cuda")
+    got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), to_dev(w.beta), eps=w.eps, amax=a, y_out=True)
+    _check_rms(w, got, amax_given=np.float32(q["amax"]))
+    y_only = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), to_dev(w.beta), eps=w.eps, y_out=True,
+                                    quantize=False)
+    assert np.array_equal(to_np_bf16(y_only["y"]), to_np_bf16(got["y"]))
+
+
+# ---------------------------------------------------------------- 2D
+@pytest.mark.parametrize("shape", [(16, 16), (64, 48), (256, 384), (144, 272), (16, 2064), (528, 16)])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_2d_small(gpu_lib, shape, rounding):
+    rng = np.random.default_rng(shape[0] + 7 * shape[1])
+    x = _bf16(rng, shape, 0.02)
+    got = gpu_lib.nvfp4q_quantize_2d(to_dev(x), rounding=rounding, seed=0x5EED, offset=4)
+    q = oracle.quantize_2d(x, rounding=rounding, seed=0x5EED, offset=4)
+    R, C = shape
+    assert_same_bits("row codes", np_u8(got["row_codes"], C // 2), q["row"]["codes"])
+    assert_same_bits("row scales", np_u8(got["row_scales"], C // 16), q["row"]["scales"])
+    assert_same_bits("col codes", np_u8(got["col_codes"], R // 2), q["col"]["codes"])
+    assert_same_bits("col scales", np_u8(got["col_scales"], R // 16), q["col"]["scales"])
+    assert_f32_bits("amax", f32(got["amax"])[0], q["amax"])
+    assert_f32_bits("scale", f32(got["scale"])[0], q["s_dec"])
+
+
+def test_2d_single_planes_and_given_amax(gpu_lib):
+    import torch
+
+    rng = np.random.default_rng(10)
+    x = _bf16(rng, (96, 160))
+    q = oracle.quantize_2d(x, rounding="sr", seed=3)
+    a = torch.tensor([q["amax"]], dtype=torch.float32, device="cuda")
+    r = gpu_lib.nvfp4q_quantize_2d(to_dev(x), rounding="sr", seed=3, colwise=False)
+    c = gpu_lib.nvfp4q_quantize_2d(to_dev(x), rounding="sr", seed=3, rowwise=False, amax=a)
+    assert_same_bits("row codes", np_u8(r["row_codes"], 80), q["row"]["codes"])
+    assert_same_bits("col codes", np_u8(c["col_codes"], 48), q["col"]["codes"])
+    assert_same_bits("col scales", np_u8(c["col_scales"], 6), q["col"]["scales"])
+    assert_f32_bits("scale", f32(c["scale"])[0], q["s_dec"])
+
+
+def test_2d_weight_8192x8192_sampled(gpu_lib):
+    w = workloads.weight_2d()
+    got = gpu_lib.nvfp4q_quantize_2d(to_dev(w.x), rounding="sr", seed=w.seed, offset=w.offset)
+    amax = np.float32(np.max(np.abs(F.bf16_to_f32(w.x))))
+    assert_f32_bits("amax", f32(got["amax"])[0], amax)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 8191], rng.choice(8192, 40, replace=False)]))
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, 8191], rng.choice(8192, 40, replace=False)]))
+    qr = oracle.quantize_rowwise(w.x[rows], amax=amax, rounding="sr", seed=w.seed, offset=w.offset, row_ids=rows)
+    qc = oracle.quantize_colwise(w.x[:, cols], amax=amax, rounding="sr", seed=w.seed, offset=w.offset, col_ids=cols)
+    assert_same_bits("row codes", np_u8(got["row_codes"], 4096)[rows], qr["codes"])
+    assert_same_bits("row scales", np_u8(got["row_scales"], 512)[rows], qr["scales"])
+    assert_same_bits("col codes", np_u8(got["col_codes"], 4096)[cols], qc["codes"])
+    assert_same_bits("col scales", np_u8(got["col_scales"], 512)[cols], qc["scales"])
+    assert_f32_bits("scale", f32(got["scale"])[0], qr["s_dec"])
+
+
+# ---------------------------------------------------------------- grouped
+def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offset=2, groups=None, amax=None):
+    import torch
+
+    T, C = x.shape
+    G = len(offsets) - 1
+    cap = T + 15 * G
+    cap16 = (cap + 15) // 16 * 16
+    codes = torch.full((C, (cap16 // 2 + 15) // 16 * 16), 0xAA, dtype=torch.uint8, device="cuda")
+    scales = torch.full((C, cap16 // 16), 0x55, dtype=torch.uint8, device="cuda")
+    a = None if amax is None else torch.tensor(amax, dtype=torch.float32, device="cuda")
+    got = gpu_lib.nvfp4q_grouped(to_dev(x), torch.tensor(offsets, dtype=torch.int32, device="cuda"),
+                                 apply_rht=apply_rht, rht_mask=mask, amax=a, rounding=rounding, seed=seed,
+                                 offset=offset, codes=codes, scales=scales)
+    ref = oracle.grouped_quantize(x, np.asarray(offsets, np.int32), apply_rht=apply_rht, rht_mask=mask,
+                                  amax=None if amax is None else np.asarray(amax, np.float32),
+                                  rounding=rounding, seed=seed, offset=offset, groups=groups)
+    poff = ref["poff"]
+    mpad = int(poff[-1])
+    assert np.array_equal(got["poff"].cpu().numpy(), poff)
+    gc, gs = np_u8(got["codes"]), np_u8(got["scales"])
+    for g in (range(G) if groups is None else groups):
+        a0, a1 = int(poff[g]), int(poff[g + 1])
+        assert_same_bits(f"group {g} codes", gc[:, a0 // 2:a1 // 2], ref["codes"][:, a0 // 2:a1 // 2])
+        assert_same_bits(f"group {g} scales", gs[:, a0 // 16:a1 // 16], ref["scales"][:, a0 // 16:a1 // 16])
+        assert_f32_bits(f"group {g} amax", f32(got["amax"])[g], ref["amax"][g])
+        assert_f32_bits(f"group {g} scale", f32(got["scale"])[g], ref["s_dec"][g])
+    # the tail past the last padded column is never written
+    assert np.all(gc[:, mpad // 2:] == 0xAA) and np.all(gs[:, mpad // 16:] == 0x55)
+
+
+@pytest.mark.parametrize("apply_rht", [True, False])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_grouped_small(gpu_lib, apply_rht, rounding):
+    rng = np.random.default_rng(12)
+    x = _bf16(rng, (203, 272))
+    offsets = [0, 0, 5, 21, 21, 150, 203]          # empty groups, short trailing groups
+    _grouped_check(gpu_lib, x, offsets, apply_rht, 0x9C35, rounding)
+
+
+def test_grouped_one_group_and_given_amax(gpu_lib):
+    rng = np.random.default_rng(13)
+    x = _bf16(rng, (300, 528), 4.0)
+    _grouped_check(gpu_lib, x, [0, 300], True, 0xFFFF, "sr")
+    _grouped_check(gpu_lib, x, [0, 7, 300], True, 0x0001, "rtne", amax=[1.5, 30.0])
+
+
+def test_grouped_64_groups_many_empty(gpu_lib):
+    rng = np.random.default_rng(14)
+    counts = rng.multinomial(1000, np.full(64, 1 / 64))
+    counts[::7] = 0
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = _bf16(rng, (int(offsets[-1]), 256))
+    _grouped_check(gpu_lib, x, offsets.tolist(), True, 0x5A5A, "sr")
+
+
+def test_grouped_moe_16384x7168_sampled(gpu_lib):
+    w = workloads.grouped_moe()
+    G = len(w.offsets) - 1
+    _grouped_check(gpu_lib, w.x, w.offsets.tolist(), w.apply_rht, w.rht_mask, "sr", seed=w.seed,
+                   offset=w.offset, groups=[0, 17, 40, G - 1])

@@ -174,3 +174,16 @@ def test_reciprocal_zero_and_clamp():
     # tiny S_dec: 1/(2^-9 * S_dec) overflows; the multiplier is clamped to FLT_MAX
     r = Q.encode_reciprocal(np.array([1], np.uint8), np.float32(1e-38))[0]
     assert r == np.finfo(np.float32).max
+
+
+def test_sampled_rows_keep_their_block_indices():
+    rng = np.random.default_rng(12)
+    x = F.f32_to_bf16(rng.standard_normal((64, 96)).astype(np.float32))
+    full = Q.quantize_rowwise(x, rounding="sr", seed=5, offset=2)
+    rows = np.array([3, 17, 40, 63])
+    part = Q.quantize_rowwise(x[rows], amax=full["amax"], rounding="sr", seed=5, offset=2, row_ids=rows)
+    assert np.array_equal(part["codes"], full["codes"][rows])
+    cols = np.array([0, 5, 95])
+    fc = Q.quantize_colwise(x, rounding="sr", seed=5, offset=2)
+    pc = Q.quantize_colwise(x[:, cols], amax=fc["amax"], rounding="sr", seed=5, offset=2, col_ids=cols)
+    assert np.array_equal(pc["codes"], fc["codes"][cols])
