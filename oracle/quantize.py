@@ -123,22 +123,28 @@ def _amax(xf):
     return F32(np.max(np.abs(xf))) if xf.size else F32(0.0)
 
 
-def quantize_rowwise(x, amax=None, rounding="rtne", seed=0, offset=0, tag=0):
+def quantize_rowwise(x, amax=None, rounding="rtne", seed=0, offset=0, tag=0, row_ids=None):
     """Rowwise NVFP4 of x[M, K] (bf16 bits or float32 holding bf16 values).
 
     Blocks are 16 consecutive elements of a row. Reading R-blk: the SR block
     index is row * (K/16) + kb. Returns a dict with codes [M, K/2] (packed),
     scales [M, K/16] (E4M3 codes), amax, s_enc, s_dec.
+
+    row_ids (sampling only): when x holds selected rows of a larger tensor, their
+    row indices in that tensor, so SR block indices stay those of the full tensor;
+    amax must then be given.
     """
     xf = _as_f32(x)
     M, K = xf.shape
     assert K % BLOCK == 0
+    assert row_ids is None or amax is not None, "a sampled quantization needs the full tensor's amax"
     a = _amax(xf) if amax is None else F32(amax)
     s_enc, s_dec = global_scales(a)
     xb = xf.reshape(M, K // BLOCK, BLOCK)
     rb = None
     if rounding == "sr":
-        blk = np.arange(M * (K // BLOCK), dtype=np.uint64).reshape(M, K // BLOCK)
+        rid = np.arange(M, dtype=np.uint64) if row_ids is None else np.asarray(row_ids, dtype=np.uint64)
+        blk = rid[:, None] * np.uint64(K // BLOCK) + np.arange(K // BLOCK, dtype=np.uint64)[None, :]
         rb = block_random_bytes(blk, tag, seed, offset)
     codes, sc = quantize_blocks(xb, s_enc, s_dec, rounding, rb)
     return {
@@ -150,19 +156,20 @@ def quantize_rowwise(x, amax=None, rounding="rtne", seed=0, offset=0, tag=0):
     }
 
 
-def quantize_colwise(x, amax=None, rounding="rtne", seed=0, offset=0):
+def quantize_colwise(x, amax=None, rounding="rtne", seed=0, offset=0, col_ids=None):
     """Columnwise (transposed) NVFP4 of x[M, K]; reading R-col.
 
     Blocks are 16 consecutive rows of one column; the output plane is the
     rowwise quantization of x transposed: codes [K, M/2], scales [K, M/16].
     Reading R-blk/R-philox: SR block index col * (M/16) + mb, tag 1.
+    col_ids (sampling only): x holds selected columns of a larger tensor.
     """
     xf = _as_f32(x)
     M, K = xf.shape
     assert M % BLOCK == 0
     a = _amax(xf) if amax is None else F32(amax)
     return quantize_rowwise(np.ascontiguousarray(xf.T), amax=a, rounding=rounding, seed=seed,
-                            offset=offset, tag=1)
+                            offset=offset, tag=1, row_ids=col_ids)
 
 
 def quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0):
