@@ -1,0 +1,301 @@
+"""Benchmark: achieved HBM bandwidth of RMSNorm + NVFP4 quantization on one MI355X.
+
+Default workload (the one the metric is quoted on): prefill, 4096 tokens x
+hidden 4096 bf16, RMSNorm (eps 1e-6, gamma, no bias) feeding rowwise NVFP4 with
+round-to-nearest-even. One step = one full ``rmsnorm_nvfp4q`` call: the tensor
+amax, the normalization and the quantized output. Other workloads
+(``--config quantize|decode|weight|grouped``) are available for measurement.
+
+Bytes are the compulsory bytes of the format: every input read once and every
+output written once (x, gamma[, beta], codes, scales, amax, S_dec). Inputs sit in
+HBM before timing starts; the step rotates over enough copies of the input and
+output buffers (>= 512 MiB in total) that no step finds its data in the 256 MB
+Infinity Cache left behind by the previous steps.
+
+Output: one JSON line on stdout (rank 0 only; this benchmark is one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published peak
+ROTATE_BYTES = 512 << 20   # total bytes cycled between steps (twice the 256 MB Infinity Cache)
+METRIC = "achieved HBM GB/s and % of peak, RMSNorm+NVFP4 quantize (tokens×hidden)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- workloads
+class Case:
+    """Device buffers and launch closures for one workload."""
+
+    def __init__(self, name, torch, q, workloads):
+        import numpy as np
+
+        self.name = name
+        self.w = w = workloads.make(name)
+        dev = torch.device("cuda", 0)
+
+        def d(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        R, C = w.x.shape
+        self.rows, self.cols = R, C
+        x_bytes = R * C * 2
+        if name in ("quantize", "prefill", "decode"):
+            out_bytes = R * C // 2 + R * C // 16
+            param_bytes = (C * 2 if w.gamma is not None else 0) + (C * 2 if w.beta is not None else 0)
+        elif name == "weight":
+            out_bytes = 2 * (R * C // 2 + R * C // 16)
+            param_bytes = 0
+        else:  # grouped
+            G = len(w.offsets) - 1
+            counts = np.diff(w.offsets)
+            mpad = int(np.sum((counts + 15) // 16 * 16))
+            self.mpad = mpad
+            out_bytes = C * mpad // 2 + C * mpad // 16 + 4 * (G + 1) + 8 * G
+            param_bytes = 4 * (G + 1)
+        self.bytes = x_bytes + out_bytes + param_bytes + (8 if name != "grouped" else 0)
+        set_bytes = x_bytes + out_bytes
+        self.nsets = max(1, math.ceil(ROTATE_BYTES / set_bytes))
+        x0 = d(w.x)
+        self.xs = [x0] + [x0.clone() for _ in range(self.nsets - 1)]
+        self.gamma = d(w.gamma) if w.gamma is not None else None
+        self.beta = d(w.beta) if w.beta is not None else None
+        self.q = q
+        self.torch = torch
+        if name == "grouped":
+            self.offsets = torch.tensor(w.offsets, dtype=torch.int32, device=dev)
+            G = len(w.offsets) - 1
+            cap16 = (R + 15 * G + 15) // 16 * 16
+            self.outs = [(torch.empty((C, (cap16 // 2 + 15) // 16 * 16), dtype=torch.uint8, device=dev),
+                          torch.empty((C, cap16 // 16), dtype=torch.uint8, device=dev)) for _ in range(self.nsets)]
+        elif name == "weight":
+            self.outs = [None] * self.nsets
+        else:
+            ldc = (C // 2 + 15) // 16 * 16
+            self.outs = [(torch.empty((R, ldc), dtype=torch.uint8, device=dev),
+                          torch.empty((R, C // 16), dtype=torch.uint8, device=dev)) for _ in range(self.nsets)]
+        self.amax_given = None
+
+    def describe(self):
+        w = self.w
+        d = {"workload": self.name, "rows": self.rows, "cols": self.cols, "rounding": w.rounding,
+             "compulsory_bytes_per_step": self.bytes, "rotated_buffer_sets": self.nsets}
+        if self.name in ("prefill", "decode"):
+            d.update({"tokens": self.rows, "hidden": self.cols, "op": "rmsnorm+nvfp4 rowwise",
+                      "bias": w.beta is not None, "eps": w.eps})
+        elif self.name == "weight":
+            d.update({"op": "nvfp4 rowwise+columnwise (2D weight)", "seed": w.seed})
+        elif self.name == "grouped":
+            d.update({"op": "grouped columnwise nvfp4 after 16-pt RHT", "groups": len(w.offsets) - 1,
+                      "padded_tokens": self.mpad})
+        else:
+            d.update({"op": "nvfp4 rowwise"})
+        return d
+
+    def step(self, i, amax=None):
+        q, w = self.q, self.w
+        x = self.xs[i % self.nsets]
+        o = self.outs[i % self.nsets]
+        if self.name in ("prefill", "decode"):
+            return q.rmsnorm_nvfp4q(x, self.gamma, self.beta, eps=w.eps, amax=amax, codes=o[0], scales=o[1])
+        if self.name == "quantize":
+            return q.nvfp4q_quantize(x, amax=amax, codes=o[0], scales=o[1])
+        if self.name == "weight":
+            return q.nvfp4q_quantize_2d(x, amax=amax, rounding=w.rounding, seed=w.seed, offset=w.offset)
+        return q.nvfp4q_grouped(x, self.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, amax=amax,
+                                rounding=w.rounding, seed=w.seed, offset=w.offset, codes=o[0], scales=o[1])
+
+
+# ----------------------------------------------------------------------------- timing
+def time_steps(case, steps, warmup, amax=None, eager=False):
+    """Average ms per step over `steps` timed steps.
+
+    The steps are captured once in a HIP graph (the library allocates nothing and
+    records no memsets, so a call is capture-safe) and the graph is replayed
+    between two synchronizations with HIP events around it, on the stream the
+    kernels run on. This removes the Python and launch overhead of each call,
+    which would otherwise exceed the GPU time of a step. `eager` times plain
+    calls instead.
+    """
+    torch = case.torch
+    if eager:
+        for i in range(warmup):
+            case.step(i, amax)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            case.step(warmup + i, amax)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(3):                      # eager warm-up before capture
+            case.step(i, amax)
+        torch.cuda.synchronize()
+        gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=s):
+            for i in range(max(warmup, 1)):
+                case.step(i, amax)
+        with torch.cuda.graph(gt, stream=s):
+            for i in range(steps):
+                case.step(i, amax)
+        torch.cuda.synchronize()
+        gw.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        gt.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The CPU oracle on a bounded sample of the same workload (rows of the tensor)."""
+    import numpy as np
+
+    import oracle
+
+    w = case.w
+    name = case.name
+    t0 = time.perf_counter()
+    done_bytes = 0
+    passes = 0
+    R, C = w.x.shape
+    chunk = max(16, min(R, (1 << 22) // C // 16 * 16))    # about 4 M elements per oracle call
+    r0 = 0
+    while time.perf_counter() - t0 < budget_s:
+        if name == "grouped":
+            G = len(w.offsets) - 1
+            g = passes % G
+            oracle.grouped_quantize(w.x, w.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, rounding=w.rounding,
+                                    seed=w.seed, offset=w.offset, groups=[g])
+            n = int(w.offsets[g + 1] - w.offsets[g])
+            done_bytes += case.bytes * n / R
+        else:
+            rows = np.arange(r0, min(R, r0 + chunk))
+            xs = w.x[rows]
+            if name in ("prefill", "decode"):
+                oracle.rmsnorm_quantize(xs, w.gamma, w.beta, w.weight_offset, w.eps)
+            elif name == "quantize":
+                oracle.quantize_rowwise(xs)
+            else:
+                oracle.quantize_rowwise(xs, amax=np.float32(1.0), rounding=w.rounding, seed=w.seed, row_ids=rows)
+                oracle.quantize_colwise(w.x[:, rows], amax=np.float32(1.0), rounding=w.rounding, seed=w.seed,
+                                        col_ids=rows)
+            done_bytes += case.bytes * len(rows) / R
+            r0 = (r0 + chunk) % R
+        passes += 1
+    el = time.perf_counter() - t0
+    if name == "grouped":
+        sample = f"{passes} groups of the grouped workload, one oracle call each"
+    elif name == "weight":
+        sample = f"{passes} calls of {chunk} rows + {chunk} columns of the 2D workload (both planes)"
+    else:
+        sample = f"{passes} calls of {min(chunk, R)} consecutive rows of the {name} workload"
+    threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": sample + f"; {el:.1f} s, {done_bytes / 1e6:.1f} MB of compulsory bytes",
+            "host_cpus": os.cpu_count()}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="prefill", choices=["quantize", "prefill", "decode", "weight", "grouped"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-only", action="store_true", help="time only the quantize stage (given amax)")
+    ap.add_argument("--eager", action="store_true", help="time plain calls instead of a HIP graph replay")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no multi-GPU "
+                                   "component (a sharded run would add one amax all-reduce, not built)"}))
+        sys.exit(2)
+
+    # the CPU oracle is single-threaded numpy; pin BLAS/OpenMP pools before numpy loads
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[k] = "1"
+
+    import torch
+
+    import rmsnorm_nvfp4_block_amd as q
+    import workloads
+
+    q.load()
+    torch.cuda.set_device(0)
+    case = Case(args.config, torch, q, workloads)
+    log(f"[bench] {case.describe()}")
+
+    # whole step (amax + quantize), the figure the metric is quoted on
+    ms = None
+    if not args.stage_only:
+        ms = time_steps(case, args.steps, args.warmup, eager=args.eager)
+        log(f"[bench] full step: {ms * 1e3:.2f} us/step")
+
+    # quantize stage alone against the amax the full step produced
+    amax_t = case.step(0)["amax"].clone()
+    torch.cuda.synchronize()
+    sms = time_steps(case, args.steps, args.warmup, amax=amax_t, eager=args.eager)
+    stage_gbs = case.bytes / (sms * 1e-3) / 1e9
+    log(f"[bench] quantize stage (given amax): {sms * 1e3:.2f} us/launch, {stage_gbs:.1f} GB/s")
+
+    if ms is None:
+        ms = sms
+    value = case.bytes / (ms * 1e-3) / 1e9
+    kernel_name = {"prefill": "k_rmsnorm (quantize pass)", "decode": "k_rmsnorm (quantize pass)",
+                   "quantize": "k_quant_rows", "weight": "k_quant_2d", "grouped": "k_grouped_quant"}[args.config]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "config": dict(case.describe(), timing="hip graph of `steps` steps, replayed once between syncs"
+                       if not args.eager else "eager calls"),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel_name + ", launched with a precomputed amax",
+            "achieved": round(stage_gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(stage_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "launch_us": round(sms * 1e3, 3),
+            "bytes_per_launch": case.bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -40,12 +40,13 @@
  *     only during the call. The library never allocates, frees or
  *     synchronizes; all work is enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream), so calls may be captured in a HIP graph.
- *   - `workspace` is device memory of at least nvfp4q_workspace_bytes()
- *     bytes, 256-byte aligned, that the caller zero-fills once before its first
- *     use. Every call leaves its counters at zero again, so the same workspace
- *     serves any number of calls that are ordered on one stream. Calls that can
- *     run at the same time (different streams) need different workspaces. After
- *     NVFP4Q_E_LAUNCH the workspace must be zero-filled again.
+ *   - `workspace` is device scratch memory of at least nvfp4q_workspace_bytes()
+ *     bytes (1 MiB), 256-byte aligned, owned by the caller. Its contents need no
+ *     initialization and carry nothing from one call to the next (an amax pass
+ *     writes per-workgroup partial maxima there and the encode pass of the
+ *     same call reads them), so one workspace serves any number of calls that
+ *     are ordered on one stream; calls that can run at the same time (different
+ *     streams) need different workspaces.
  *   - Errors are returned synchronously, before anything is enqueued, except
  *     NVFP4Q_E_LAUNCH. Device-side data that break a stated rule (for example
  *     decreasing group offsets) give unspecified output but no out-of-bounds
@@ -113,7 +114,7 @@ typedef struct {
   uint32_t offset;
 } nvfp4q_rng;
 
-/* Bytes of workspace every entry point needs (a constant). */
+/* Bytes of workspace every entry point needs (a constant, 1 MiB). */
 size_t nvfp4q_workspace_bytes(void);
 
 /* Static description of a status code; never NULL. */
@@ -199,6 +200,10 @@ nvfp4q_status nvfp4q_quantize_2d(const void *x, nvfp4q_dtype dtype, int64_t rows
  *     possible padded length). Plane columns at and past Poff[G] are never
  *     written [PR, Grouped allocation tail].
  *   SR: tag 1, block index = plane_row * (Poff[G] / 16) + plane_col / 16.
+ *   Without amax_in the amax pass keeps one partial per 128-row x 256-column
+ *   tile slot; shapes needing more slots than the workspace holds
+ *   (((total_rows + 15 G) / 128 + G) * cols / 256 > 262112) return
+ *   NVFP4Q_E_UNSUPPORTED.
  *   [PR, Optimization 2, 3, 5; Fast math (bf16 round-through of the
  *    transform); Config surface and AUTO (64 groups, device offsets)]
  */

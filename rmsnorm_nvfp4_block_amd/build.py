@@ -3,8 +3,9 @@
 Usage: ``python -m rmsnorm_nvfp4_block_amd.build`` (or ``build()`` from Python).
 Each ``.hip`` translation unit is compiled in parallel into ``_build/`` and
 linked into ``rmsnorm_nvfp4_block_amd/libnvfp4q.so``. Flags: -O3, gfx950 only,
-no FMA contraction (the quantizer's products must round on their own), and the
-packed-FP32 feature disabled for all device code.
+no FMA contraction (the quantizer's products must round on their own), NaN
+handling off (inputs are finite by contract; it removes NaN canonicalization
+around max), and the packed-FP32 feature disabled for all device code.
 """
 from __future__ import annotations
 
@@ -19,11 +20,14 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnvfp4q.so")
-SOURCES = ["api.hip", "kernels_rows.hip", "kernels_2d.hip", "kernels_grouped.hip"]
+SOURCES = [
+    "api.hip", "kernels_rows.hip", "kernels_rms_a.hip", "kernels_rms_b.hip", "kernels_rms_c.hip",
+    "kernels_2d.hip", "kernels_grouped.hip",
+]
 ARCH = "gfx950"
 
 COMMON = [
-    "-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument",
 ]

@@ -91,7 +91,7 @@ nvfp4q_status nvfp4q_quantize(const void* x, nvfp4q_dtype dtype, int64_t rows, i
   a.sr = rounding == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   if (!a.amax_in) {
-    hipError_t e = launch_amax_rows(a, s);
+    hipError_t e = launch_amax_rows(a, s, &a.nparts);
     if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
   }
   return done(launch_quant_rows(a, s));
@@ -131,10 +131,10 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   a.sr = rounding == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   if (codes && !a.amax_in) {
-    hipError_t e = launch_rmsnorm_pass(a, true, s);
+    hipError_t e = launch_rmsnorm_pass(a, true, s, &a.nparts);
     if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
   }
-  return done(launch_rmsnorm_pass(a, false, s));
+  return done(launch_rmsnorm_pass(a, false, s, nullptr));
 }
 
 nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows, int64_t cols, int64_t ld_x,
@@ -154,21 +154,21 @@ nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows
   const nvfp4q_global& gg = g ? *g : kNoGlobal;
   hipStream_t s = (hipStream_t)stream;
   if (rows == 0) return done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s));
+  uint32_t nparts = 0;
   if (!gg.amax_in) {
     RowArgs r = {};
     r.x = x; r.rows = rows; r.cols = cols; r.ld_x = ld_x;
-    r.ws = (Workspace*)workspace; r.amax_out = gg.amax_out; r.scale_out = gg.scale_out;
-    hipError_t e = launch_amax_rows(r, s);
+    r.ws = (Workspace*)workspace;
+    hipError_t e = launch_amax_rows(r, s, &nparts);
     if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
   }
   TwoDArgs a = {};
+  a.nparts = nparts;
   a.x = x; a.rows = rows; a.cols = cols; a.ld_x = ld_x;
   if (has_row) { a.rcodes = row->codes; a.rldc = row->ld_codes; a.rscales = row->scales; a.rlds = row->ld_scales; }
   if (has_col) { a.ccodes = col->codes; a.cldc = col->ld_codes; a.cscales = col->scales; a.clds = col->ld_scales; }
   a.ws = (Workspace*)workspace;
-  a.amax_in = gg.amax_in;
-  a.amax_out = gg.amax_in ? gg.amax_out : nullptr;
-  a.scale_out = gg.amax_in ? gg.scale_out : nullptr;
+  a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
   a.sr = rounding == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   return done(launch_quant_2d(a, s));
@@ -189,6 +189,7 @@ nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_ro
   if (col->ld_codes * 2 < cap || col->ld_scales * 16 < cap) return NVFP4Q_E_SHAPE;
   TRY(check_rounding(rounding, rng));
   TRY(check_ws(workspace, workspace_bytes));
+  if (!(g && g->amax_in) && grouped_partials(total_rows, cols, num_groups) > kPartials) return NVFP4Q_E_UNSUPPORTED;
   const nvfp4q_global& gg = g ? *g : kNoGlobal;
   GroupArgs a = {};
   a.x = x; a.rows = total_rows; a.cols = cols; a.ld_x = ld_x;

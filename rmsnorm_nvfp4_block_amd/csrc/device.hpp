@@ -19,22 +19,18 @@ constexpr int kWave = 64;
 constexpr float kFltMax = 3.40282347e+38f;
 
 // ---------------------------------------------------------------- workspace
-// Self-resetting device state. Every counter and accumulator is zero between
-// calls: the last workgroup of a reduction returns it to zero. Result slots are
-// written before they are read within a call and carry no state across calls.
+// Device memory shared by the kernels of one call, in a caller-owned buffer.
+// An amax pass writes one partial maximum per workgroup into `partial` with a
+// plain store; the encode pass that follows reduces the partials it needs at its
+// start (the kernel boundary orders the two). Every slot an encode pass reads is
+// written earlier in the same call, so the buffer carries no state between
+// calls and needs no reset, and no workgroup waits on another.
+constexpr int kPartials = 262144 - 32;
 struct Workspace {
-  uint32_t count;          // arrival counter of the last-workgroup reduction
-  uint32_t bar_count;      // grid-barrier arrival counter
-  uint32_t bar_gen;        // grid-barrier generation (monotone, wraps)
-  uint32_t status;         // sticky device-side error flags (bit 0: barrier timeout)
-  uint32_t amax_bits[64];  // per-tensor / per-group amax accumulators (fp32 bits, >= 0)
-  float enc[64];           // S_enc per tensor / group (result slot)
-  float dec[64];           // S_dec per tensor / group (result slot)
-  float amax[64];          // amax used per tensor / group (result slot)
-  int32_t poff[72];        // padded group offsets (result slot)
-  uint32_t rsv[1024 - 4 - 64 * 4 - 72];
+  uint32_t status[32];          // reserved (one 128-byte line)
+  float partial[kPartials];     // per-workgroup partial maxima of the last amax pass
 };
-static_assert(sizeof(Workspace) == 4096, "workspace layout");
+static_assert(sizeof(Workspace) == 1 << 20, "workspace layout");
 
 // ---------------------------------------------------------------- bf16
 // bfloat16 -> float32 is a 16-bit shift (PR, Optimization item 6).
@@ -85,10 +81,22 @@ __device__ __forceinline__ GScale global_scale(float amax) {
   return g;
 }
 
+// RN(b / 6) for b >= 0. For normal b, q0 = RN(b * RN(1/6)) is corrected once
+// with the exact remainder fma(-q0, 6, b) (Markstein's correction); this equals
+// the correctly rounded quotient for every normal float32 (checked
+// exhaustively). Subnormal b takes the division.
+__device__ __forceinline__ float div6(float b) {
+  const float y = 0.166666672f;  // RN(1/6)
+  const float q0 = b * y;
+  const float r = __builtin_fmaf(-q0, 6.0f, b);
+  const float q1 = __builtin_fmaf(r, y, q0);
+  if (__builtin_expect(b < 1.17549435e-38f, 0)) return b / 6.0f;
+  return q1;
+}
+
 // Block scale code: E4M3(RN(RN(bmax / 6) * S_enc)).
 __device__ __forceinline__ uint32_t block_scale(float bmax, float s_enc) {
-  float q = bmax / 6.0f;
-  return e4m3_code(q * s_enc);
+  return e4m3_code(div6(bmax) * s_enc);
 }
 
 // Encode multiplier for a block scale code: RN(1 / RN(f32(s) * S_dec)),
@@ -195,15 +203,39 @@ __device__ __forceinline__ uint32_t swap_pair_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
 }
 
+// DPP lane moves (row = 16 lanes). bound_ctrl keeps the source value for
+// lanes whose source is outside the row mask.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // reverse within 8 lanes
+constexpr int kDppMirror = 0x140;       // reverse within 16 lanes
+constexpr int kDppBcast15 = 0x142;      // lane 15 of each row to the next row
+constexpr int kDppBcast31 = 0x143;      // lane 31 to rows 2 and 3
+
+// Sum / max over the 64 lanes, returned as a wave-uniform value: reductions
+// within each 16-lane row by DPP, then across rows with the row broadcasts;
+// lane 63 holds the total.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppBcast15, 0xA, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppBcast31, 0xC, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppBcast15, 0xA, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kDppBcast31, 0xC, 0xF, false)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ float max8_abs(const float v[8]) {
@@ -221,25 +253,94 @@ __device__ __forceinline__ void widen8(const uint4 q, float v[8]) {
   v[6] = bf_lo(q.w); v[7] = bf_hi(q.w);
 }
 
-// ---------------------------------------------------------------- atomics
-__device__ __forceinline__ void atomic_max_f32_nonneg(uint32_t* p, float v) {
-  __hip_atomic_fetch_max(p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ---------------------------------------------------------------- loads
+// 16-byte load of 8 bf16 values, zero when !ok. The if-form keeps the access a
+// single global_load_dwordx4 (a select between the load and a zero vector is
+// split into four dword loads by the compiler).
+__device__ __forceinline__ uint4 ld16(const void* p, bool ok) {
+  uint4 q = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) q = *reinterpret_cast<const uint4*>(p);
+  return q;
 }
 
-// Last-workgroup election: every workgroup calls this once from thread 0 after
-// its atomics; returns true in exactly one workgroup, which then sees all of
-// them. The counter is returned to zero by that workgroup.
-__device__ __forceinline__ bool arrive_last(uint32_t* count, uint32_t nwg) {
-  uint32_t prev = __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  if (prev == nwg - 1) {
-    __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
+// Encode-reciprocal table for the 127 finite non-negative E4M3 codes (index
+// 127 is never produced), filled by threads 0..127 of a workgroup.
+__device__ __forceinline__ void fill_rcp_table(float* tab, float s_dec) {
+  if (threadIdx.x < 128) tab[threadIdx.x] = encode_mult(threadIdx.x, s_dec);
+}
+
+constexpr int kWGThreads = 256;  // every kernel runs 4-wave workgroups
+constexpr int kWavesPerWG = kWGThreads / kWave;
+
+// ---------------------------------------------------------------- consumers
+// Workgroup-wide max of a per-lane value over NW waves (all threads must call).
+template <int NW = kWavesPerWG>
+__device__ __forceinline__ float wg_max(float m) {
+  __shared__ float red[NW];
+  m = wave_max(m);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wid] = m;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// Max over partial[first .. first + n) with all threads of the workgroup.
+__device__ __forceinline__ float reduce_partials(const Workspace* ws, uint32_t first, uint32_t n) {
+  float m = 0.0f;
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, ws->partial[first + i]);
+  return wg_max(m);
+}
+
+// Per-tensor scales for an encode kernel, into every thread, and the encode
+// reciprocal table into LDS: from amax_in when given, otherwise the max of the
+// `nparts` partials of the amax pass. Workgroup 0 reports amax and S_dec.
+__device__ __forceinline__ GScale consume_scales(const Workspace* ws, uint32_t nparts, const float* amax_in,
+                                                 float* amax_out, float* scale_out, float* rcp_tab) {
+  const float a = amax_in ? *amax_in : reduce_partials(ws, 0, nparts);
+  const GScale g = global_scale(a);
+  if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
+    if (amax_out) *amax_out = a;
+    if (scale_out) *scale_out = g.dec;
   }
-  return false;
+  fill_rcp_table(rcp_tab, g.dec);
+  __syncthreads();
+  return g;
 }
 
-__device__ __forceinline__ float load_amax(uint32_t* p) {
-  return __uint_as_float(__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+// Amax pass epilogue: the workgroup's maximum into its partial slot.
+__device__ __forceinline__ void publish_partial(Workspace* ws, float m) {
+  m = wg_max(m);
+  if (threadIdx.x == 0) ws->partial[blockIdx.y * gridDim.x + blockIdx.x] = m;
+}
+
+__device__ __forceinline__ float max16_abs(const float v[16]) { return fmaxf(max8_abs(v), max8_abs(v + 8)); }
+
+// Encode one 16-element block held by one lane (fp32 values that are bf16
+// values): block scale from the block max, encode multiplier from the table,
+// 16 codes in two words (element 2i in the low nibble of byte i). SR draws one
+// Philox evaluation for the block: elements 0-3 take word 0, 4-7 word 1,
+// 8-11 word 2, 12-15 word 3.
+template <bool SR>
+__device__ __forceinline__ uint2 encode_block16(float v[16], GScale g, const float* rcp_tab, uint32_t& sc,
+                                                uint64_t blk, uint64_t seed, uint32_t offset, uint32_t tag) {
+  sc = block_scale(max16_abs(v), g.enc);
+  const float rc = rcp_tab[sc];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
+  uint2 out;
+  if constexpr (SR) {
+    const U4 w = block_random(blk, tag, seed, offset);
+    out.x = sr_pack8(v, w.x, w.y);
+    out.y = sr_pack8(v + 8, w.z, w.w);
+  } else {
+    out.x = rtne_pack8(v);
+    out.y = rtne_pack8(v + 8);
+  }
+  return out;
 }
 
 }  // namespace nvfp4q

@@ -2,10 +2,10 @@
 // tensor under one per-tensor scale, read once from HBM.
 //
 // One workgroup (256 threads) owns a 128 x 128 tile.
-//  * Load: thread t reads 8 consecutive columns (16 B) of rows t/16 + 16j,
-//    j = 0..7, so a wave reads 4 rows x 256 B per instruction. The lane pair
-//    (t, t^1) holds one rowwise 16-element block; rowwise codes leave as 4-byte
-//    stores that are 64 contiguous bytes per row.
+//  * Load: thread t reads one rowwise 16-element block (two adjacent 16-byte
+//    loads) of rows t/8 + 32j, j = 0..3, so a wave reads 8 rows x 256 B per
+//    instruction pair. The block's amax, scale and codes are computed in-lane;
+//    rowwise codes leave as 8-byte stores, 64 contiguous bytes per row.
 //  * The raw tile is staged in LDS (32 KiB) with the 16-byte chunk index of a
 //    row XOR-ed by 4 * ((row / 16) mod 4), which spreads the eight 16-row
 //    blocks a wave reads at one time over all banks.
@@ -31,74 +31,60 @@ __device__ __forceinline__ uint32_t swz_chunk(uint32_t chunk, uint32_t row) {
 }
 
 template <bool ROW, bool COL, bool SR>
-__global__ __launch_bounds__(kT) void k_quant_2d(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols,
-                                                 int64_t ld_x, uint8_t* __restrict__ rcodes, int64_t rldc,
-                                                 uint8_t* __restrict__ rscales, int64_t rlds,
-                                                 uint8_t* __restrict__ ccodes, int64_t cldc,
-                                                 uint8_t* __restrict__ cscales, int64_t clds, const Workspace* ws,
-                                                 const float* amax_in, float* amax_out, float* scale_out,
-                                                 uint64_t seed, uint32_t offset, uint32_t tiles_c) {
+__global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tiles_c) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileR * kRowBytes];
-  GScale g;
-  if (amax_in) {
-    float a = *amax_in;
-    g = global_scale(a);
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      if (amax_out) *amax_out = a;
-      if (scale_out) *scale_out = g.dec;
-    }
-  } else {
-    g.enc = ws->enc[0];
-    g.dec = ws->dec[0];
-  }
+  __shared__ float rcp_tab[128];
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  const int64_t ld_x = a.ld_x;
+  uint8_t* __restrict__ rcodes = a.rcodes;
+  uint8_t* __restrict__ rscales = a.rscales;
+  uint8_t* __restrict__ ccodes = a.ccodes;
+  uint8_t* __restrict__ cscales = a.cscales;
+  const int64_t rldc = a.rldc, rlds = a.rlds, cldc = a.cldc, clds = a.clds;
+  const uint64_t seed = a.seed;
+  const uint32_t offset = a.offset;
   const uint32_t t = threadIdx.x;
   const uint32_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
   const uint32_t row0 = tr * kTileR, col0 = tc * kTileC;
 
-  // ---- load 8 rows x 16 B per thread
-  const uint32_t chunk = t & 15, rsub = t >> 4;
-  const uint32_t col = col0 + chunk * 8;
-  uint4 q[8];
+  // ---- load 4 rows x 32 B per thread
+  const uint32_t bsub = t & 7, rsub = t >> 3;
+  const uint32_t col = col0 + bsub * 16;
+  uint4 q[4][2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t r = row0 + rsub + 16 * j;
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t r = row0 + rsub + 32 * j;
     const bool ok = r < rows && col < cols;
-    uint4 z = {0u, 0u, 0u, 0u};
-    q[j] = ok ? *reinterpret_cast<const uint4*>(x + (int64_t)r * ld_x + col) : z;
+    const uint16_t* p = x + (int64_t)r * ld_x + col;
+    q[j][0] = ld16(p, ok);
+    q[j][1] = ld16(p + 8, ok);
   }
+  const GScale g = consume_scales(a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
   if constexpr (COL) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t lr = rsub + 16 * j;
-      *reinterpret_cast<uint4*>(tile + lr * kRowBytes + swz_chunk(chunk, lr) * 16) = q[j];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lr = rsub + 32 * j;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<uint4*>(tile + lr * kRowBytes + swz_chunk(2 * bsub + h, lr) * 16) = q[j][h];
     }
   }
   // ---- rowwise plane from registers
   if constexpr (ROW) {
     const uint32_t nbr = cols >> 4;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t r = row0 + rsub + 16 * j;
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t r = row0 + rsub + 32 * j;
       const bool ok = r < rows && col < cols;
-      float v[8];
-      widen8(q[j], v);
-      float m = max8_abs(v);
-      float bm = fmaxf(m, swap_pair(m));
-      uint32_t sc = block_scale(bm, g.enc);
-      float rc = encode_mult(sc, g.dec);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = v[i] * rc;
-      uint32_t word;
-      if constexpr (SR) {
-        U4 w = block_random((uint64_t)r * nbr + (col >> 4), 0, seed, offset);
-        const bool odd = (t & 1) != 0;
-        word = sr_pack8(v, odd ? w.z : w.x, odd ? w.w : w.y);
-      } else {
-        word = rtne_pack8(v);
-      }
+      float v[16];
+      widen8(q[j][0], v);
+      widen8(q[j][1], v + 8);
+      uint32_t sc;
+      const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)r * nbr + (col >> 4), seed, offset, 0);
       if (ok) {
-        *reinterpret_cast<uint32_t*>(rcodes + (int64_t)r * rldc + (col >> 1)) = word;
-        if ((t & 1) == 0) rscales[(int64_t)r * rlds + (col >> 4)] = (uint8_t)sc;
+        *reinterpret_cast<uint2*>(rcodes + (int64_t)r * rldc + (col >> 1)) = w;
+        rscales[(int64_t)r * rlds + (col >> 4)] = (uint8_t)sc;
       }
     }
   }
@@ -128,7 +114,7 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const uint16_t* __restrict__ x,
       }
       float m = fmaxf(max8_abs(v), max8_abs(v + 8));
       uint32_t sc = block_scale(m, g.enc);
-      float rc = encode_mult(sc, g.dec);
+      float rc = rcp_tab[sc];
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
       uint2 out;
@@ -153,14 +139,8 @@ void launch_2d_rc(const TwoDArgs& a, hipStream_t s) {
   const uint32_t tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
   const uint32_t tiles_c = (uint32_t)((a.cols + kTileC - 1) / kTileC);
   dim3 grid(tiles_r * tiles_c), block(kT);
-  if (a.sr)
-    hipLaunchKernelGGL((k_quant_2d<ROW, COL, true>), grid, block, 0, s, (const uint16_t*)a.x, (uint32_t)a.rows,
-                       (uint32_t)a.cols, a.ld_x, a.rcodes, a.rldc, a.rscales, a.rlds, a.ccodes, a.cldc, a.cscales,
-                       a.clds, a.ws, a.amax_in, a.amax_out, a.scale_out, a.seed, a.offset, tiles_c);
-  else
-    hipLaunchKernelGGL((k_quant_2d<ROW, COL, false>), grid, block, 0, s, (const uint16_t*)a.x, (uint32_t)a.rows,
-                       (uint32_t)a.cols, a.ld_x, a.rcodes, a.rldc, a.rscales, a.rlds, a.ccodes, a.cldc, a.cscales,
-                       a.clds, a.ws, a.amax_in, a.amax_out, a.scale_out, a.seed, a.offset, tiles_c);
+  if (a.sr) hipLaunchKernelGGL((k_quant_2d<ROW, COL, true>), grid, block, 0, s, a, tiles_c);
+  else hipLaunchKernelGGL((k_quant_2d<ROW, COL, false>), grid, block, 0, s, a, tiles_c);
 }
 
 }  // namespace

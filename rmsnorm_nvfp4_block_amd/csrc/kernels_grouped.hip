@@ -38,41 +38,54 @@ struct GroupTile {
   int row0;       // first row of the group in x
   int poff;       // first plane column of the group
   int mpad;       // total padded tokens (plane length)
+  int tile0;      // first tile slot of the group
+  int tiles;      // tile slots of the group
 };
 
-// Wave 0 of the workgroup locates the tile; the result is shared through LDS.
-// Offsets are clamped to [0, rows] so that malformed device offsets cannot
-// lead to reads outside x.
-__device__ __forceinline__ void group_range(const int32_t* __restrict__ offsets, int g, int rows, int& lo, int& n) {
-  lo = min(max(offsets[g], 0), rows);
-  const int hi = min(max(offsets[g + 1], lo), rows);
-  n = hi - lo;
+// Per-group layout, one group per lane of a wave (lanes >= groups hold empty
+// groups): row range, padded length, tile count and their inclusive prefix sums
+// across the wave. Offsets are clamped to [0, rows], so malformed device
+// offsets cannot lead to reads outside x.
+struct GroupScan {
+  int lo, n, p, tiles, ps, ts;
+};
+__device__ __forceinline__ GroupScan group_scan(const int32_t* __restrict__ offsets, int groups, int rows) {
+  const int lane = threadIdx.x & 63;
+  GroupScan s;
+  s.lo = 0;
+  s.n = 0;
+  if (lane < groups) {
+    s.lo = min(max(offsets[lane], 0), rows);
+    s.n = min(max(offsets[lane + 1], s.lo), rows) - s.lo;
+  }
+  s.p = (s.n + 15) & ~15;
+  s.tiles = (s.p + kTileTok - 1) / kTileTok;
+  s.ps = s.p;
+  s.ts = s.tiles;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(s.ps, o, 64), b = __shfl_up(s.ts, o, 64);
+    if (lane >= o) {
+      s.ps += a;
+      s.ts += b;
+    }
+  }
+  return s;
 }
 
+// Wave 0 locates the workgroup's tile; the result is shared through LDS.
 __device__ GroupTile locate_tile(const int32_t* __restrict__ offsets, int groups, int rows, uint32_t slot) {
   __shared__ GroupTile s;
   if (threadIdx.x < 64) {
+    const GroupScan q = group_scan(offsets, groups, rows);
     const int lane = threadIdx.x;
-    int lo = 0, n = 0;
-    if (lane < groups) group_range(offsets, lane, rows, lo, n);
-    const int p = (n + 15) & ~15;
-    const int tiles = (p + kTileTok - 1) / kTileTok;
-    int ps = p, ts = tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int a = __shfl_up(ps, o, 64), b = __shfl_up(ts, o, 64);
-      if (lane >= o) {
-        ps += a;
-        ts += b;
-      }
-    }
-    const uint64_t before = __ballot(lane < groups && (uint32_t)ts <= slot);
+    const uint64_t before = __ballot(lane < groups && (uint32_t)q.ts <= slot);
     const int g = __popcll(before);
     const int gs = g < 64 ? g : 63;
-    const int ts_g = __shfl(ts, gs, 64), tiles_g = __shfl(tiles, gs, 64);
-    const int ps_g = __shfl(ps, gs, 64), p_g = __shfl(p, gs, 64);
-    const int n_g = __shfl(n, gs, 64), lo_g = __shfl(lo, gs, 64);
-    const int mpad = __shfl(ps, 63, 64);
+    const int ts_g = __shfl(q.ts, gs, 64), tiles_g = __shfl(q.tiles, gs, 64);
+    const int ps_g = __shfl(q.ps, gs, 64), p_g = __shfl(q.p, gs, 64);
+    const int n_g = __shfl(q.n, gs, 64), lo_g = __shfl(q.lo, gs, 64);
+    const int mpad = __shfl(q.ps, 63, 64);
     if (lane == 0) {
       GroupTile t;
       t.g = (g < groups) ? g : -1;
@@ -82,6 +95,8 @@ __device__ GroupTile locate_tile(const int32_t* __restrict__ offsets, int groups
       t.row0 = lo_g;
       t.poff = ps_g - p_g;
       t.mpad = mpad;
+      t.tile0 = ts_g - tiles_g;
+      t.tiles = tiles_g;
       s = t;
     }
   }
@@ -89,29 +104,43 @@ __device__ GroupTile locate_tile(const int32_t* __restrict__ offsets, int groups
   return s;
 }
 
-// Padded offsets of all groups (wave 0, lanes 0..groups): Poff[0] = 0,
-// Poff[g + 1] = Poff[g] + 16 * ceil(n_g / 16).
-__device__ void write_poff(const int32_t* __restrict__ offsets, int groups, int rows, int32_t* out_a,
-                           int32_t* out_b) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int lo = 0, n = 0;
-    if (lane < groups) group_range(offsets, lane, rows, lo, n);
-    int ps = (n + 15) & ~15;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int a = __shfl_up(ps, o, 64);
-      if (lane >= o) ps += a;
-    }
-    if (lane < groups) {
-      if (out_a) out_a[lane + 1] = ps;
-      if (out_b) out_b[lane + 1] = ps;
-    }
-    if (lane == 0) {
-      if (out_a) out_a[0] = 0;
-      if (out_b) out_b[0] = 0;
-    }
+// Workgroup (0, 0) of the encode pass, wave 0: padded offsets Poff[0] = 0,
+// Poff[g + 1] = Poff[g] + 16 * ceil(n_g / 16), and each group's amax and S_dec
+// (lane g reduces its group's partials: tile slots tile0 .. tile0 + tiles - 1
+// of every column tile, `stride` slots apart).
+// Max over the partials of tile slots tile0 .. tile0 + tiles - 1 of every
+// column tile (all threads of the workgroup).
+__device__ __forceinline__ float reduce_partials_2d(const Workspace* ws, uint32_t tile0, uint32_t tiles,
+                                                    uint32_t stride, uint32_t coltiles) {
+  float m = 0.0f;
+  const uint32_t n = tiles * coltiles;
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint32_t y = i / tiles, k = i - y * tiles;
+    m = fmaxf(m, ws->partial[y * stride + tile0 + k]);
   }
+  return wg_max(m);
+}
+
+__device__ void report_groups(const int32_t* __restrict__ offsets, int groups, int rows, const Workspace* ws,
+                              uint32_t stride, uint32_t coltiles, const float* amax_in, float* amax_out,
+                              float* scale_out, int32_t* poff_out) {
+  if (threadIdx.x >= 64) return;
+  const GroupScan q = group_scan(offsets, groups, rows);
+  const int lane = threadIdx.x;
+  if (lane < groups) {
+    float a = 0.0f;
+    if (amax_in) {
+      a = amax_in[lane];
+    } else {
+      const uint32_t t0 = (uint32_t)(q.ts - q.tiles);
+      for (uint32_t y = 0; y < coltiles; ++y)
+        for (int i = 0; i < q.tiles; ++i) a = fmaxf(a, ws->partial[y * stride + t0 + i]);
+    }
+    if (amax_out) amax_out[lane] = a;
+    if (scale_out) scale_out[lane] = global_scale(a).dec;
+    if (poff_out) poff_out[lane + 1] = q.ps;
+  }
+  if (lane == 0 && poff_out) poff_out[0] = 0;
 }
 
 // Load the lane's 16 tokens x 8 columns (zero for padding rows and columns
@@ -122,8 +151,7 @@ __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64
   for (int i = 0; i < 16; ++i) {
     const int lt = (int)blk_tok0 + i;
     const bool ok = lt < t.n && col < cols;
-    uint4 z = {0u, 0u, 0u, 0u};
-    q[i] = ok ? *reinterpret_cast<const uint4*>(x + (int64_t)(t.row0 + lt) * ld_x + col) : z;
+    q[i] = ld16(x + (int64_t)(t.row0 + lt) * ld_x + col, ok);
   }
 }
 
@@ -158,8 +186,7 @@ __device__ __forceinline__ void signed_fwht16(float v[16], uint32_t mask) {
 template <bool RHT>
 __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict__ x, int rows, uint32_t cols, int64_t ld_x,
                                                      const int32_t* __restrict__ offsets, int groups, uint32_t mask,
-                                                     Workspace* ws, float* amax_out, float* scale_out,
-                                                     int32_t* poff_out) {
+                                                     Workspace* ws) {
   const GroupTile t = locate_tile(offsets, groups, rows, blockIdx.x);
   const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float m = 0.0f;
@@ -182,31 +209,7 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
       if constexpr (RHT) m = bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
     }
   }
-  __shared__ float red[kT / 64];
-  m = wave_max(m);
-  if (lane == 0) red[wv] = m;
-  __syncthreads();
-  __shared__ bool last;
-  if (threadIdx.x == 0) {
-    const float wm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (t.g >= 0) atomic_max_f32_nonneg(&ws->amax_bits[t.g], wm);
-    last = arrive_last(&ws->count, gridDim.x * gridDim.y);
-  }
-  __syncthreads();
-  if (last) {
-    if (threadIdx.x < 64 && (int)threadIdx.x < groups) {
-      const int g = threadIdx.x;
-      const float a = load_amax(&ws->amax_bits[g]);
-      const GScale s = global_scale(a);
-      ws->enc[g] = s.enc;
-      ws->dec[g] = s.dec;
-      ws->amax[g] = a;
-      if (amax_out) amax_out[g] = a;
-      if (scale_out) scale_out[g] = s.dec;
-      __hip_atomic_store(&ws->amax_bits[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    write_poff(offsets, groups, rows, poff_out, nullptr);
-  }
+  publish_partial(ws, m);   // one slot per (token tile, column tile); 0 for slots past the last tile
 }
 
 // Pass 2: transform (optional), bf16 round-through, per-block scale and codes.
@@ -219,22 +222,16 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
                                                       float* scale_out, int32_t* poff_out, uint64_t seed,
                                                       uint32_t offset, int64_t cap) {
   const GroupTile t = locate_tile(offsets, groups, rows, blockIdx.x);
-  if (amax_in && blockIdx.x == 0 && blockIdx.y == 0) {
-    if (threadIdx.x < 64 && (int)threadIdx.x < groups) {
-      const float a = amax_in[threadIdx.x];
-      if (amax_out) amax_out[threadIdx.x] = a;
-      if (scale_out) scale_out[threadIdx.x] = global_scale(a).dec;
-    }
-    write_poff(offsets, groups, rows, poff_out, nullptr);
-  }
+  __shared__ float rcp_tab[128];
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    report_groups(offsets, groups, rows, ws, gridDim.x, gridDim.y, amax_in, amax_out, scale_out, poff_out);
   if (t.g < 0) return;
-  GScale g;
-  if (amax_in) {
-    g = global_scale(amax_in[t.g]);
-  } else {
-    g.enc = ws->enc[t.g];
-    g.dec = ws->dec[t.g];
-  }
+  // this group's amax: its tile slots of every column tile of the amax pass
+  const float amax = amax_in ? amax_in[t.g]
+                             : reduce_partials_2d(ws, (uint32_t)t.tile0, (uint32_t)t.tiles, gridDim.x, gridDim.y);
+  const GScale g = global_scale(amax);
+  fill_rcp_table(rcp_tab, g.dec);
+  __syncthreads();
   const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint32_t mb = lane & 7, cg = lane >> 3;
   const uint32_t col = blockIdx.y * kTileCol + wv * 64 + cg * 8;
@@ -262,7 +259,7 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
     }
     const float m = fmaxf(max8_abs(v), max8_abs(v + 8));
     const uint32_t sc = block_scale(m, g.enc);
-    const float rc = encode_mult(sc, g.dec);
+    const float rc = rcp_tab[sc];
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
     uint2 out;
@@ -285,7 +282,7 @@ void launch_grouped_r(const GroupArgs& a, dim3 grid, hipStream_t s) {
   const int64_t cap = a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16;
   if (!a.amax_in)
     hipLaunchKernelGGL((k_grouped_amax<RHT>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets,
-                       a.groups, a.mask, a.ws, a.amax_out, a.scale_out, a.poff_out);
+                       a.groups, a.mask, a.ws);
   if (a.sr)
     hipLaunchKernelGGL((k_grouped_quant<RHT, true>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets,
                        a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in, a.amax_out,
@@ -297,6 +294,14 @@ void launch_grouped_r(const GroupArgs& a, dim3 grid, hipStream_t s) {
 }
 
 }  // namespace
+
+// Tile slots x column tiles of the grid, which is also the number of partials
+// the amax pass writes: the grid covers the largest possible number of tiles,
+// (rows + 15 G) / 128 + G, since the offsets live on the device.
+int64_t grouped_partials(int64_t rows, int64_t cols, int groups) {
+  const int64_t max_tiles = (rows + 15 * (int64_t)groups + kTileTok - 1) / kTileTok + groups;
+  return max_tiles * ((cols + kTileCol - 1) / kTileCol);
+}
 
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {
   const int64_t max_tiles = (a.rows + 15 * (int64_t)a.groups + kTileTok - 1) / kTileTok + a.groups;

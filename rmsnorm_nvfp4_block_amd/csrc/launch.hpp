@@ -22,6 +22,7 @@ struct RowArgs {
   uint8_t* scales;
   int64_t lds;
   Workspace* ws;
+  uint32_t nparts;          // partial maxima written by the amax pass (set by the launcher)
   const float* amax_in;
   float* amax_out;
   float* scale_out;
@@ -39,6 +40,7 @@ struct TwoDArgs {
   uint8_t *ccodes, *cscales;
   int64_t cldc, clds;
   Workspace* ws;
+  uint32_t nparts;
   const float* amax_in;
   float* amax_out;
   float* scale_out;
@@ -68,13 +70,19 @@ struct GroupArgs {
 };
 
 hipError_t launch_empty_scale(float* amax_out, float* scale_out, int n, hipStream_t s);
-hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s);
+// Amax pass over a [rows, cols] tensor; returns the number of partials it
+// writes through `nparts`.
+hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s, uint32_t* nparts);
 hipError_t launch_quant_rows(const RowArgs& a, hipStream_t s);
-hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s);
+// Two-pass RMSNorm: with amax_pass, the amax pass (sets *nparts); otherwise the
+// encode pass (reads a.nparts partials when a.amax_in is NULL).
+hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, uint32_t* nparts);
 int rms_max_cols();
 
 hipError_t launch_quant_2d(const TwoDArgs& a, hipStream_t s);
 
+// Grouped path; hipErrorInvalidValue when the tile grid exceeds the workspace.
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s);
+int64_t grouped_partials(int64_t rows, int64_t cols, int groups);
 
 }  // namespace nvfp4q
