@@ -6,6 +6,9 @@
 #include "device.hpp"
 #include "launch.hpp"
 
+#include <cstddef>
+#include <cstdlib>
+
 using namespace nvfp4q;
 
 namespace {
@@ -50,6 +53,16 @@ nvfp4q_status done(hipError_t e) { return e == hipSuccess ? NVFP4Q_OK : NVFP4Q_E
   } while (0)
 
 const nvfp4q_global kNoGlobal = {nullptr, nullptr, nullptr};
+
+// NVFP4Q_RMS_STREAM=0 selects the full-row RMSNorm encode pass everywhere
+// (for comparison; both give identical results).
+bool rms_stream_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("NVFP4Q_RMS_STREAM");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
 
 }  // namespace
 
@@ -130,11 +143,16 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
   a.sr = rounding == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
+  // With the amax pass and a row count that fits the workspace's row-scale
+  // slots, the encode pass streams rows using the 1/rms the amax pass stored.
+  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled();
+  if (streamed) a.rs = reinterpret_cast<float*>(static_cast<char*>(workspace) + offsetof(Workspace, partial)) + kRowPartials;
   if (codes && !a.amax_in) {
-    hipError_t e = launch_rmsnorm_pass(a, true, s, &a.nparts);
+    const hipError_t e = (streamed && !beta) ? launch_rms_stream_amax(a, s, &a.nparts)
+                                           : launch_rmsnorm_pass(a, true, s, &a.nparts);
     if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
   }
-  return done(launch_rmsnorm_pass(a, false, s, nullptr));
+  return done(streamed ? launch_rms_stream_quant(a, s) : launch_rmsnorm_pass(a, false, s, nullptr));
 }
 
 nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows, int64_t cols, int64_t ld_x,

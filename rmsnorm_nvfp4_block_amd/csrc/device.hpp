@@ -25,7 +25,13 @@ constexpr float kFltMax = 3.40282347e+38f;
 // start (the kernel boundary orders the two). Every slot an encode pass reads is
 // written earlier in the same call, so the buffer carries no state between
 // calls and needs no reset, and no workgroup waits on another.
+//
+// The rowwise RMSNorm amax pass launches at most kRowPartials workgroups and
+// also leaves each row's 1/rms in partial[kRowPartials + row] (rows up to
+// kRowScaleCap), so that the encode pass can stream the row in pieces.
 constexpr int kPartials = 262144 - 32;
+constexpr int kRowPartials = 4096;
+constexpr int kRowScaleCap = kPartials - kRowPartials;
 struct Workspace {
   uint32_t status[32];          // reserved (one 128-byte line)
   float partial[kPartials];     // per-workgroup partial maxima of the last amax pass
@@ -298,9 +304,7 @@ __device__ __forceinline__ float reduce_partials(const Workspace* ws, uint32_t f
 // Per-tensor scales for an encode kernel, into every thread, and the encode
 // reciprocal table into LDS: from amax_in when given, otherwise the max of the
 // `nparts` partials of the amax pass. Workgroup 0 reports amax and S_dec.
-__device__ __forceinline__ GScale consume_scales(const Workspace* ws, uint32_t nparts, const float* amax_in,
-                                                 float* amax_out, float* scale_out, float* rcp_tab) {
-  const float a = amax_in ? *amax_in : reduce_partials(ws, 0, nparts);
+__device__ __forceinline__ GScale scales_from(float a, float* amax_out, float* scale_out, float* rcp_tab) {
   const GScale g = global_scale(a);
   if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
     if (amax_out) *amax_out = a;
@@ -309,6 +313,42 @@ __device__ __forceinline__ GScale consume_scales(const Workspace* ws, uint32_t n
   fill_rcp_table(rcp_tab, g.dec);
   __syncthreads();
   return g;
+}
+
+__device__ __forceinline__ GScale consume_scales(const Workspace* ws, uint32_t nparts, const float* amax_in,
+                                                 float* amax_out, float* scale_out, float* rcp_tab) {
+  return scales_from(amax_in ? *amax_in : reduce_partials(ws, 0, nparts), amax_out, scale_out, rcp_tab);
+}
+
+// The same in two steps, so that a kernel can issue these loads before its
+// bulk loads (loads complete in issue order, so a wait for a later load also
+// waits for every earlier one): the first 4 partials of this thread ...
+struct PartialsPre {
+  float m[4];
+};
+__device__ __forceinline__ PartialsPre partials_issue(const Workspace* ws, uint32_t nparts, const float* amax_in) {
+  PartialsPre p;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t i = threadIdx.x + k * kWGThreads;
+    p.m[k] = 0.0f;
+    if (amax_in == nullptr && i < nparts) p.m[k] = ws->partial[i];
+  }
+  return p;
+}
+// ... then the rest, the workgroup maximum and the scales.
+__device__ __forceinline__ GScale partials_finish(const PartialsPre& p, const Workspace* ws, uint32_t nparts,
+                                                  const float* amax_in, float* amax_out, float* scale_out,
+                                                  float* rcp_tab) {
+  float a;
+  if (amax_in) {
+    a = *amax_in;
+  } else {
+    float m = fmaxf(fmaxf(p.m[0], p.m[1]), fmaxf(p.m[2], p.m[3]));
+    for (uint32_t i = threadIdx.x + 4 * kWGThreads; i < nparts; i += kWGThreads) m = fmaxf(m, ws->partial[i]);
+    a = wg_max(m);
+  }
+  return scales_from(a, amax_out, scale_out, rcp_tab);
 }
 
 // Amax pass epilogue: the workgroup's maximum into its partial slot.

@@ -1,0 +1,274 @@
+// Streaming form of the two RMSNorm + rowwise NVFP4 passes.
+//
+// The full-row kernels hold a whole token row in registers because 1/rms is
+// known only after the row's sum of squares. Here the amax pass writes each
+// row's 1/rms into the workspace, so neither pass needs a whole row at once:
+// a wave walks its rows one 1024-column superchunk at a time (lane l: the
+// 16-element block at columns 16l..16l+15) with kDepth superchunks in flight,
+// and compute overlaps the loads of the superchunks behind it.
+//
+//  * Amax pass (no bias): per lane, the running sum of squares and the
+//    running max |RN(x * (gamma + c))| of the current row; at the row's last
+//    superchunk, r = 1/rms from the wave sum, r goes to the workspace, and
+//    RN(max * r) joins the wave's maximum. Since y = RN(RN(x * g) * r) is
+//    monotone in |RN(x * g)| for the row's fixed r > 0, that is the row's
+//    max |y|. With a bias the max depends on r element by element; that case
+//    keeps the full-row amax pass (which also stores r).
+//  * Encode pass: y = RN(RN(x * g) * r) [+ beta, fused], rounded to bf16, then
+//    the block encode, as in the full-row pass; codes leave with non-temporal
+//    stores (they are not read again by this call). Lane k of a wave holds r
+//    of the wave's k-th row (a wave has at most 64 rows; the launcher sizes
+//    the grid for it).
+//
+// The ring of superchunks is refilled only in iterations that have a next
+// one, and the last iteration issues no loads: a refill that may or may not
+// happen makes the compiler copy the ring at the loop back edge, and the copy
+// waits for the refill loads to land.
+//
+// "CuTeDSL at Perplexity", QK Norm (the normalization) and grid
+// synchronization (the kernel boundary between the amax and the encode pass).
+#include "rows.hpp"
+
+namespace nvfp4q {
+
+namespace {
+
+constexpr int kDepth = 4;              // superchunks in flight per wave
+constexpr uint32_t kMaxWaveRows = 64;  // rows per wave in the encode pass
+
+// Row and superchunk of a wave's next load or next block to process; the
+// wave's rows are wave, wave + nwaves, ...; k counts the wave's rows.
+struct Cursor {
+  uint32_t row, sc, k;
+  __device__ __forceinline__ void next(uint32_t nsc, uint32_t nwaves) {
+    if (++sc == nsc) {
+      sc = 0;
+      row += nwaves;
+      ++k;
+    }
+  }
+};
+
+template <bool FULL>
+__device__ __forceinline__ Blk load_at(const RowArgs& a, Cursor c, uint32_t cols, int lane) {
+  const uint16_t* xr = (const uint16_t*)a.x + (int64_t)c.row * a.ld_x;
+  return load_blk<FULL>(xr, c.sc * kSuper + lane * 16, cols);
+}
+
+// Refill of a slot with the item at `ld` (item number `item`); past the
+// wave's last item `ld` stays on that item (a cache hit).
+template <bool FULL>
+__device__ __forceinline__ void refill(const RowArgs& a, Blk& slot, Cursor& ld, uint32_t item, uint32_t n,
+                                       uint32_t nsc, uint32_t nwaves, uint32_t cols, int lane) {
+  slot = load_at<FULL>(a, ld, cols, lane);
+  if (item + 1 < n) ld.next(nsc, nwaves);
+}
+
+// Wave index with the wave-uniform part kept in scalar registers.
+__device__ __forceinline__ uint32_t wave_id() {
+  return blockIdx.x * kWavesPerWG + (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+__device__ __forceinline__ uint32_t wave_rows(uint32_t wave, uint32_t nwaves, uint32_t rows) {
+  return wave < rows ? (rows - 1 - wave) / nwaves + 1 : 0;
+}
+
+// ------------------------------------------------------------------ amax pass
+struct AmaxAcc {
+  float ss, m, macc;
+};
+
+template <bool FULL>
+__device__ __forceinline__ void amax_item(const RowArgs& a, const Blk& b, const Cursor& pc, const float* gsh,
+                                          uint32_t nsc, uint32_t cols, float inv_k, int lane, AmaxAcc& acc) {
+  acc.ss = sumsq8(b.hi, sumsq8(b.lo, acc.ss));
+  float v[16], gv[16];
+  widen16(b, v);
+  const uint32_t col = pc.sc * kSuper + lane * 16;
+  lds16(gsh, (FULL || col < cols) ? col : 0, gv);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = v[k] * gv[k];
+  acc.m = fmaxf(acc.m, max16_abs(v));
+  if (pc.sc == nsc - 1) {
+    const float r = inv_rms(wave_sum(acc.ss), inv_k, a.eps);
+    if (lane == 0) a.rs[pc.row] = r;
+    acc.macc = fmaxf(acc.macc, acc.m * r);
+    acc.ss = 0.0f;
+    acc.m = 0.0f;
+  }
+}
+
+template <bool FULL>
+__global__ __launch_bounds__(kThreads) void k_rms_amax_stream(const RowArgs a) {
+  extern __shared__ float gsh[];  // gamma + c [cols]
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = wave_id(), nwaves = gridDim.x * kWavesPerWG;
+  const uint32_t nsc = (cols + kSuper - 1) / kSuper;
+  const uint32_t n = wave_rows(wave, nwaves, rows) * nsc;
+  // the prologue's loads first: loads complete in issue order
+  const ParamsPre pp = params_issue<false>((const uint16_t*)a.gamma, nullptr, cols);
+  // unconditional fill (a wave without rows reads the last row): a fill that
+  // may be skipped would make every later wait a wait for all loads
+  Blk ring[kDepth];
+  Cursor ld{wave < rows ? wave : rows - 1, 0, 0};
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) refill<FULL>(a, ring[d], ld, d, n, nsc, nwaves, cols, lane);
+  params_finish<false>(pp, (const uint16_t*)a.gamma, nullptr, a.woff, cols, gsh, nullptr);
+  __syncthreads();
+  const float inv_k = 1.0f / (float)cols;
+  AmaxAcc acc{0.0f, 0.0f, 0.0f};
+  Cursor pc{wave, 0, 0};
+  for (uint32_t base = 0; base < n; base += kDepth) {
+    if (base + kDepth < n) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        amax_item<FULL>(a, ring[d], pc, gsh, nsc, cols, inv_k, lane, acc);
+        refill<FULL>(a, ring[d], ld, base + kDepth + d, n, nsc, nwaves, cols, lane);
+        pc.next(nsc, nwaves);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        if (base + d < n) {
+          amax_item<FULL>(a, ring[d], pc, gsh, nsc, cols, inv_k, lane, acc);
+          pc.next(nsc, nwaves);
+        }
+      }
+    }
+  }
+  // max |bf16(y)| = bf16(max |y|): round-to-nearest-even is monotone.
+  publish_partial(a.ws, bf_lo(pack_bf16(acc.macc, acc.macc) & 0xFFFFu));
+}
+
+// ------------------------------------------------------------------ encode pass
+__device__ __forceinline__ void st_nt8(uint8_t* p, uint2 w) {
+  __builtin_nontemporal_store((uint64_t)w.x | ((uint64_t)w.y << 32), reinterpret_cast<uint64_t*>(p));
+}
+
+template <bool FULL, bool BIAS, bool SR>
+__device__ __forceinline__ void quant_item(const RowArgs& a, const Blk& b, const Cursor& pc, float r_lane,
+                                           const float* gsh, const float* bsh, GScale g, const float* rcp_tab,
+                                           uint32_t cols, int lane) {
+  const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_lane), (int)pc.k));
+  const uint32_t col = pc.sc * kSuper + lane * 16;
+  const bool ok = FULL || col < cols;
+  const uint32_t lcol = ok ? col : 0;
+  float v[16], gv[16];
+  widen16(b, v);
+  lds16(gsh, lcol, gv);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = v[k] * gv[k];
+  if constexpr (BIAS) {
+    float bv[16];
+    lds16(bsh, lcol, bv);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = __builtin_fmaf(v[k], r, bv[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = v[k] * r;
+  }
+  const uint4 y0 = pack8_bf16(v), y1 = pack8_bf16(v + 8);
+  if (a.y != nullptr && ok) {
+    uint16_t* yr = (uint16_t*)a.y + (int64_t)pc.row * a.ld_y + col;
+    *reinterpret_cast<uint4*>(yr) = y0;
+    *reinterpret_cast<uint4*>(yr + 8) = y1;
+  }
+  widen8(y0, v);
+  widen8(y1, v + 8);
+  uint32_t sc;
+  const uint2 w =
+      encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)pc.row * (cols >> 4) + (col >> 4), a.seed, a.offset, 0);
+  if (ok) {
+    st_nt8(a.codes + (int64_t)pc.row * a.ldc + (col >> 1), w);
+    __builtin_nontemporal_store((uint8_t)sc, a.scales + (int64_t)pc.row * a.lds + (col >> 4));
+  }
+}
+
+template <bool FULL, bool BIAS, bool SR>
+__global__ __launch_bounds__(kThreads) void k_rms_quant_stream(const RowArgs a) {
+  extern __shared__ float params[];  // gamma + c [cols], then beta [cols]
+  __shared__ float rcp_tab[128];
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = wave_id(), nwaves = gridDim.x * kWavesPerWG;
+  const uint32_t nsc = (cols + kSuper - 1) / kSuper;
+  const uint32_t wr = wave_rows(wave, nwaves, rows);  // <= kMaxWaveRows
+  const uint32_t n = wr * nsc;
+  // the prologue's loads first: loads complete in issue order
+  const PartialsPre pm = partials_issue(a.ws, a.nparts, a.amax_in);
+  const ParamsPre pp = params_issue<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, cols);
+  const float r_lane = (uint32_t)lane < wr ? a.rs[wave + lane * nwaves] : 0.0f;
+  // unconditional fill (a wave without rows reads the last row): a fill that
+  // may be skipped would make every later wait a wait for all loads
+  Blk ring[kDepth];
+  Cursor ld{wave < rows ? wave : rows - 1, 0, 0};
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) refill<FULL>(a, ring[d], ld, d, n, nsc, nwaves, cols, lane);
+  float* gsh = params;
+  float* bsh = params + param_floats(cols);
+  params_finish<BIAS>(pp, (const uint16_t*)a.gamma, (const uint16_t*)a.beta, a.woff, cols, gsh, bsh);
+  const GScale g = partials_finish(pm, a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
+  Cursor pc{wave, 0, 0};
+  for (uint32_t base = 0; base < n; base += kDepth) {
+    if (base + kDepth < n) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        quant_item<FULL, BIAS, SR>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
+        refill<FULL>(a, ring[d], ld, base + kDepth + d, n, nsc, nwaves, cols, lane);
+        pc.next(nsc, nwaves);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        if (base + d < n) {
+          quant_item<FULL, BIAS, SR>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
+          pc.next(nsc, nwaves);
+        }
+      }
+    }
+  }
+}
+
+// Workgroups per streaming launch: rows / 4 up to NVFP4Q_RMS_STREAM_WGS
+// (default 1024).
+int64_t stream_wgs() {
+  static int64_t v = [] {
+    const char* e = getenv("NVFP4Q_RMS_STREAM_WGS");
+    return e ? (int64_t)atoll(e) : (int64_t)1024;
+  }();
+  return v;
+}
+
+bool full_cols(int64_t cols) { return cols % kSuper == 0; }
+
+}  // namespace
+
+hipError_t launch_rms_stream_amax(const RowArgs& a, hipStream_t s, uint32_t* nparts) {
+  const uint32_t wgs = grid_rows(a.rows, stream_wgs() < kRowPartials ? stream_wgs() : kRowPartials);
+  *nparts = wgs;
+  const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float);
+  if (full_cols(a.cols)) hipLaunchKernelGGL(k_rms_amax_stream<true>, dim3(wgs), dim3(kThreads), lds, s, a);
+  else hipLaunchKernelGGL(k_rms_amax_stream<false>, dim3(wgs), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <bool FULL, bool BIAS>
+static hipError_t launch_qs(const RowArgs& a, hipStream_t s) {
+  // at most kMaxWaveRows rows per wave: lane k holds the k-th row's 1/rms
+  const int64_t min_wgs = (a.rows + kMaxWaveRows * kWavesPerWG - 1) / (kMaxWaveRows * kWavesPerWG);
+  const uint32_t wgs = grid_rows(a.rows, stream_wgs() > min_wgs ? stream_wgs() : min_wgs);
+  if ((int64_t)wgs * kWavesPerWG * kMaxWaveRows < a.rows) return hipErrorInvalidValue;
+  const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
+  if (a.sr) hipLaunchKernelGGL((k_rms_quant_stream<FULL, BIAS, true>), dim3(wgs), dim3(kThreads), lds, s, a);
+  else hipLaunchKernelGGL((k_rms_quant_stream<FULL, BIAS, false>), dim3(wgs), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_stream_quant(const RowArgs& a, hipStream_t s) {
+  const bool full = full_cols(a.cols);
+  if (a.beta) return full ? launch_qs<true, true>(a, s) : launch_qs<false, true>(a, s);
+  return full ? launch_qs<true, false>(a, s) : launch_qs<false, false>(a, s);
+}
+
+}  // namespace nvfp4q

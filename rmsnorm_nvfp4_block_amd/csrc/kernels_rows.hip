@@ -137,7 +137,7 @@ extern template void launch_rms_nsc<16>(const RowArgs&, bool, hipStream_t);
 int rms_max_cols() { return 16 * kSuper; }
 
 hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, uint32_t* nparts) {
-  if (amax_pass) *nparts = grid_rows(a.rows, rms_wgs());
+  if (amax_pass) *nparts = grid_rows(a.rows, rms_wgs() > kRowPartials ? kRowPartials : rms_wgs());
   const int64_t need = (a.cols + kSuper - 1) / kSuper;
   if (need <= 1) launch_rms_nsc<1>(a, amax_pass, s);
   else if (need <= 2) launch_rms_nsc<2>(a, amax_pass, s);

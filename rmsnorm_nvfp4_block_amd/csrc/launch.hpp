@@ -23,6 +23,7 @@ struct RowArgs {
   int64_t lds;
   Workspace* ws;
   uint32_t nparts;          // partial maxima written by the amax pass (set by the launcher)
+  float* rs;                // RMSNorm: per-row 1/rms written by the amax pass, or NULL
   const float* amax_in;
   float* amax_out;
   float* scale_out;
@@ -77,6 +78,10 @@ hipError_t launch_quant_rows(const RowArgs& a, hipStream_t s);
 // Two-pass RMSNorm: with amax_pass, the amax pass (sets *nparts); otherwise the
 // encode pass (reads a.nparts partials when a.amax_in is NULL).
 hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, uint32_t* nparts);
+// Streaming RMSNorm passes (need a.rs): the amax pass without a bias, which
+// also writes a.rs, and the encode pass, which reads it.
+hipError_t launch_rms_stream_amax(const RowArgs& a, hipStream_t s, uint32_t* nparts);
+hipError_t launch_rms_stream_quant(const RowArgs& a, hipStream_t s);
 int rms_max_cols();
 
 hipError_t launch_quant_2d(const TwoDArgs& a, hipStream_t s);

@@ -47,6 +47,19 @@ inline uint32_t grid_rows(int64_t rows, int64_t max_wgs = 4096) {
 // ------------------------------------------------------------------ RMSNorm
 // y = bf16_rne(((gamma + c) * x) * r [+ beta]), r = 1/sqrt(ss/K + eps), ss the
 // fp32 sum of squares of the row ("CuTeDSL at Perplexity", QK Norm).
+__device__ __forceinline__ float inv_rms(float ss, float inv_k, float eps) {
+  return __builtin_amdgcn_rsqf(ss * inv_k + eps);  // v_rsq_f32, within 1 ulp
+}
+
+// Sum of squares of 8 bf16 pairs added to ss (v_dot2c_f32_bf16).
+__device__ __forceinline__ float sumsq8(const uint4 q, float ss) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), __builtin_bit_cast(bf16x2, w[i]), ss, false);
+  return ss;
+}
+
 template <int NSC>
 __device__ __forceinline__ float row_rs(const Blk (&q)[NSC], float inv_k, float eps) {
   float ss = 0.0f;
@@ -57,8 +70,7 @@ __device__ __forceinline__ float row_rs(const Blk (&q)[NSC], float inv_k, float 
     for (int i = 0; i < 8; ++i)
       ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]), __builtin_bit_cast(bf16x2, w[i]), ss, false);
   }
-  ss = wave_sum(ss);
-  return __builtin_amdgcn_rsqf(ss * inv_k + eps);  // v_rsq_f32, within 1 ulp
+  return inv_rms(wave_sum(ss), inv_k, eps);
 }
 
 __device__ __forceinline__ uint4 pack8_bf16(const float v[8]) {
@@ -72,30 +84,87 @@ __device__ __forceinline__ uint4 pack8_bf16(const float v[8]) {
 
 // Row parameters in LDS as fp32, filled once per workgroup: RN(gamma + c)
 // (c the weight offset) and beta when present.
+//
+// LDS layout: the 16 values lane l needs for superchunk c (columns
+// c*1024 + 16l .. +15) sit as four 16-byte quads at quad index
+// (4c + q) * 64 + l, q = 0..3. One ds_read_b128 of a wave then reads 1 KiB
+// contiguous (no bank conflicts; with the plain layout the lanes' 64-byte
+// stride made every read a multi-way conflict). The area holds whole
+// superchunks: param_floats(cols) floats per parameter.
+__host__ __device__ constexpr uint32_t param_floats(uint32_t cols) { return (cols + kSuper - 1) / kSuper * kSuper; }
+__device__ __forceinline__ uint32_t pidx(uint32_t col) {
+  return ((((col >> 10) * 4 + ((col >> 2) & 3)) * 64 + ((col >> 4) & 63)) << 2) + (col & 3);
+}
+
+// 8 columns starting at column c8 * 8.
+template <bool BIAS>
+__device__ __forceinline__ void put_params(uint4 gq, uint4 bq, uint32_t c8, float woff, float* gsh, float* bsh) {
+  float gv[8];
+  widen8(gq, gv);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) gv[i] = gv[i] + woff;
+  const uint32_t i0 = pidx(c8 * 8), i1 = pidx(c8 * 8 + 4);
+  *reinterpret_cast<float4*>(gsh + i0) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+  *reinterpret_cast<float4*>(gsh + i1) = make_float4(gv[4], gv[5], gv[6], gv[7]);
+  if constexpr (BIAS) {
+    float bv[8];
+    widen8(bq, bv);
+    *reinterpret_cast<float4*>(bsh + i0) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+    *reinterpret_cast<float4*>(bsh + i1) = make_float4(bv[4], bv[5], bv[6], bv[7]);
+  }
+}
+
 template <bool BIAS>
 __device__ __forceinline__ void stage_params(const uint16_t* __restrict__ gamma, const uint16_t* __restrict__ beta,
                                              float woff, uint32_t cols, float* gsh, float* bsh) {
   for (uint32_t c8 = threadIdx.x; c8 * 8 < cols; c8 += blockDim.x) {
-    float gv[8];
-    widen8(*reinterpret_cast<const uint4*>(gamma + c8 * 8), gv);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) gv[i] = gv[i] + woff;
-    *reinterpret_cast<float4*>(gsh + c8 * 8) = make_float4(gv[0], gv[1], gv[2], gv[3]);
-    *reinterpret_cast<float4*>(gsh + c8 * 8 + 4) = make_float4(gv[4], gv[5], gv[6], gv[7]);
-    if constexpr (BIAS) {
-      float bv[8];
-      widen8(*reinterpret_cast<const uint4*>(beta + c8 * 8), bv);
-      *reinterpret_cast<float4*>(bsh + c8 * 8) = make_float4(bv[0], bv[1], bv[2], bv[3]);
-      *reinterpret_cast<float4*>(bsh + c8 * 8 + 4) = make_float4(bv[4], bv[5], bv[6], bv[7]);
-    }
+    const uint4 gq = *reinterpret_cast<const uint4*>(gamma + c8 * 8);
+    uint4 bq = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (BIAS) bq = *reinterpret_cast<const uint4*>(beta + c8 * 8);
+    put_params<BIAS>(gq, bq, c8, woff, gsh, bsh);
   }
 }
 
-__device__ __forceinline__ void lds16(const float* p, float v[16]) {
+// The same in two steps (see partials_issue): the loads of the first
+// 2 * kThreads * 8 columns, then the LDS stores and the remaining columns.
+struct ParamsPre {
+  uint4 g[2], b[2];
+};
+template <bool BIAS>
+__device__ __forceinline__ ParamsPre params_issue(const uint16_t* gamma, const uint16_t* beta, uint32_t cols) {
+  ParamsPre p;
 #pragma unroll
-  for (int i = 0; i < 16; i += 4) {
-    const float4 a = *reinterpret_cast<const float4*>(p + i);
-    v[i] = a.x; v[i + 1] = a.y; v[i + 2] = a.z; v[i + 3] = a.w;
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t c8 = threadIdx.x + k * kThreads;
+    p.g[k] = ld16(gamma + c8 * 8, c8 * 8 < cols);
+    p.b[k] = BIAS ? ld16(beta + c8 * 8, c8 * 8 < cols) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  return p;
+}
+template <bool BIAS>
+__device__ __forceinline__ void params_finish(const ParamsPre& p, const uint16_t* gamma, const uint16_t* beta,
+                                              float woff, uint32_t cols, float* gsh, float* bsh) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t c8 = threadIdx.x + k * kThreads;
+    if (c8 * 8 < cols) put_params<BIAS>(p.g[k], p.b[k], c8, woff, gsh, bsh);
+  }
+  for (uint32_t c8 = threadIdx.x + 2 * kThreads; c8 * 8 < cols; c8 += kThreads) {
+    const uint4 gq = *reinterpret_cast<const uint4*>(gamma + c8 * 8);
+    uint4 bq = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (BIAS) bq = *reinterpret_cast<const uint4*>(beta + c8 * 8);
+    put_params<BIAS>(gq, bq, c8, woff, gsh, bsh);
+  }
+}
+
+// The 16 parameter values of the block starting at column `col` (a multiple
+// of 16).
+__device__ __forceinline__ void lds16(const float* base, uint32_t col, float v[16]) {
+  const float* p = base + pidx(col);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 a = *reinterpret_cast<const float4*>(p + q * 256);
+    v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
   }
 }
 
@@ -120,6 +189,9 @@ __device__ __forceinline__ float rms_row(const RowArgs& a, uint32_t r, const Blk
   const uint32_t cols = (uint32_t)a.cols;
   const uint32_t nbr = cols >> 4;
   const float rs = row_rs<NSC>(q, inv_k, a.eps);
+  if constexpr (AMAX) {
+    if (a.rs != nullptr && lane == 0) a.rs[r] = rs;
+  }
   float mrow = 0.0f;
 #pragma unroll
   for (int c = 0; c < NSC; ++c) {
@@ -128,7 +200,7 @@ __device__ __forceinline__ float rms_row(const RowArgs& a, uint32_t r, const Blk
     const uint32_t lcol = ok ? col : 0;
     float v[16], gv[16];
     widen16(q[c], v);
-    lds16(gsh + lcol, gv);
+    lds16(gsh, lcol, gv);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = v[i] * gv[i];
     if constexpr (AMAX && !BIAS) {
@@ -137,7 +209,7 @@ __device__ __forceinline__ float rms_row(const RowArgs& a, uint32_t r, const Blk
     }
     if constexpr (BIAS) {
       float bv[16];
-      lds16(bsh + lcol, bv);
+      lds16(bsh, lcol, bv);
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(v[i], rs, bv[i]);
     } else {
@@ -186,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void k_rmsnorm(const RowArgs a) {
   Blk qa[NSC], qb[NSC];
   load_row<NSC, FULL>(x, a.ld_x, wave, rows, cols, lane, qa);  // first row in flight before the staging
   float* gsh = params;
-  float* bsh = params + cols;
+  float* bsh = params + param_floats(cols);
   stage_params<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, a.woff, cols, gsh, bsh);
   GScale g = {1.0f, 1.0f};
   if constexpr (!AMAX && CODES) g = consume_scales(a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
@@ -223,8 +295,9 @@ inline int64_t rms_wgs() {
 
 template <int NSC, bool BIAS, bool AMAX, bool SR, bool CODES>
 static void launch_rms_t(const RowArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)a.cols * sizeof(float) * (BIAS ? 2 : 1);
-  const dim3 grid(grid_rows(a.rows, rms_wgs())), block(kThreads);
+  const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
+  const int64_t max_wgs = AMAX && rms_wgs() > kRowPartials ? kRowPartials : rms_wgs();
+  const dim3 grid(grid_rows(a.rows, max_wgs)), block(kThreads);
   if (a.cols == NSC * (int64_t)kSuper)
     hipLaunchKernelGGL((k_rmsnorm<NSC, true, BIAS, AMAX, SR, CODES>), grid, block, lds, s, a);
   else

@@ -194,6 +194,28 @@ def test_rmsnorm_ragged(gpu_lib, shape, bias, woff, rounding):
     _check_rms(w, got, rounding, 11, 1)
 
 
+@pytest.mark.parametrize("shape,bias,woff,rounding", [((24579, 32), False, 0.0, "rtne"), ((8197, 1040), True, 1.0, "sr"),
+                                                      ((8197, 1040), False, 1.0, "rtne")])
+def test_rmsnorm_many_rows_per_wave(gpu_lib, shape, bias, woff, rounding):
+    """Several rows per wave: the streaming passes refill their ring across rows."""
+    rng = np.random.default_rng(shape[0] + shape[1])
+    H = shape[1]
+    w = workloads.Workload("t", _bf16(rng, shape, 1.5), gamma=_bf16(rng, (H,), 0.4),
+                           beta=_bf16(rng, (H,), 0.1) if bias else None, weight_offset=woff, eps=1e-6)
+    got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), to_dev(w.beta) if bias else None,
+                                 weight_offset=woff, eps=w.eps, y_out=True, rounding=rounding, seed=5, offset=2)
+    _check_rms(w, got, rounding, 5, 2)
+
+
+def test_rmsnorm_rows_past_row_scale_slots(gpu_lib):
+    """More rows than the workspace keeps per-row 1/rms for: the full-row passes."""
+    rng = np.random.default_rng(77)
+    shape = (258017, 16)
+    w = workloads.Workload("t", _bf16(rng, shape, 1.0), gamma=_bf16(rng, (16,), 0.5), eps=1e-6)
+    got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), eps=w.eps, y_out=True)
+    _check_rms(w, got)
+
+
 def test_rmsnorm_given_amax_and_y_only(gpu_lib):
     import torch
 
