@@ -215,6 +215,133 @@ def cpu_baseline(case, budget_s=12.0):
             "host_cpus": os.cpu_count()}
 
 
+# ----------------------------------------------------------------------------- roofline
+# The kernel each workload's roofline entry describes, how it is timed, and the
+# pattern of its kernel names in a rocprofv3 trace. "step": the hot path is two
+# kernels with a grid-wide dependency between them (amax pass, encode pass);
+# both are timed together as one step. "stage": the encode kernel alone, launched
+# with the amax the full step produced (the same kernel the full step runs).
+DOMINANT = {
+    "prefill": ("step", "k_rms_amax_stream + k_rms_quant_stream", r"k_rms_amax_stream|k_rms_quant_stream"),
+    "decode": ("step", "k_rmsnorm (amax pass) + k_rms_quant_stream", r"k_rmsnorm<|k_rms_quant_stream"),
+    "quantize": ("stage", "k_quant_rows", r"k_quant_rows"),
+    "weight": ("stage", "k_quant_2d", r"k_quant_2d"),
+    "grouped": ("stage", "k_grouped_quant", r"k_grouped_quant"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest():
+    """sha256 of the kernel sources and header: traffic figures are valid only for the code they were taken on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rmsnorm_nvfp4_block_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    files.append(os.path.join(ROOT, "include", "nvfp4q.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_pmc(directory, counter):
+    """{kernel name: [value per dispatch]} for one counter from a rocprofv3 --pmc csv directory."""
+    import csv
+    import glob
+    import re
+
+    out = {}
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = re.sub(r"\(anonymous namespace\)::", "", row["Kernel_Name"])
+                key = (name, row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def ingest_pmc(config, fetch_dir, write_dir, command):
+    """Per-step FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel(s) into profiles/traffic.json."""
+    import re
+
+    pat = re.compile(DOMINANT[config][2])
+    entry = {"kernels": {}, "source_sha256": source_digest(), "command": command}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for name, vals in read_pmc(d, counter).items():
+            if pat.search(name):
+                k = entry["kernels"].setdefault(name.split("(")[0], {})
+                k[counter.lower() + "_kib"] = sum(vals) / len(vals)
+                k["dispatches"] = len(vals)
+    if not entry["kernels"]:
+        raise SystemExit("no dispatch of the dominant kernel in the counter files")
+    if DOMINANT[config][0] == "stage" and len(entry["kernels"]) != 1:
+        raise SystemExit(f"expected one kernel, found {list(entry['kernels'])}")
+    entry["fetch_kib"] = sum(k.get("fetch_size_kib", 0.0) for k in entry["kernels"].values())
+    entry["write_kib"] = sum(k.get("write_size_kib", 0.0) for k in entry["kernels"].values())
+    _update_traffic(config, entry)
+
+
+def ingest_copy(fetch_dir, write_dir, nbytes, command):
+    """Counter readings of a plain device-to-device copy of `nbytes`: the calibration of FETCH/WRITE_SIZE."""
+    best = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        cands = [(n, sorted(v)[len(v) // 2]) for n, v in read_pmc(d, counter).items() if "copy" in n.lower()]
+        if not cands:
+            raise SystemExit("no copy kernel in the counter files")
+        # the calibration copies are the largest copy dispatches of the run
+        best[counter] = max(cands, key=lambda t: t[1])[1]
+    kib = nbytes / 1024.0
+    _update_traffic("copy_calibration", {
+        "bytes": nbytes, "fetch_kib": best["FETCH_SIZE"], "write_kib": best["WRITE_SIZE"],
+        "fetch_factor": kib / best["FETCH_SIZE"], "write_factor": kib / best["WRITE_SIZE"], "command": command})
+
+
+def _update_traffic(key, entry):
+    d = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    d[key] = entry
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(d, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({key: entry}))
+
+
+def traffic_bytes(config):
+    """Calibrated HBM bytes per launch of the dominant kernel(s), or None (no figures, or the code changed since)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        d = json.load(fh)
+    e, cal = d.get(config), d.get("copy_calibration")
+    if not e or not cal or e.get("source_sha256") != source_digest():
+        return None
+    return e["fetch_kib"] * 1024.0 * cal["fetch_factor"] + e["write_kib"] * 1024.0 * cal["write_factor"]
+
+
+def copy_calibration(torch, nbytes, reps):
+    """Plain copies of a known size, for the FETCH_SIZE / WRITE_SIZE calibration runs."""
+    n = nbytes // 4
+    bufs = [torch.full((n,), float(i), dtype=torch.float32, device="cuda") for i in range(4)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        bufs[(2 * r + 1) % 4].copy_(bufs[(2 * r) % 4])
+    torch.cuda.synchronize()
+    log(f"[bench] {reps} copies of {nbytes} bytes done")
+
+
 # ----------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -223,9 +350,22 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="prefill", choices=["quantize", "prefill", "decode", "weight", "grouped"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stage-only", action="store_true", help="time only the quantize stage (given amax)")
     ap.add_argument("--eager", action="store_true", help="time plain calls instead of a HIP graph replay")
+    ap.add_argument("--copy-calibration", type=int, metavar="BYTES",
+                    help="only run plain copies of BYTES (for the counter calibration runs)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="record the dominant kernel's FETCH_SIZE/WRITE_SIZE from two rocprofv3 --pmc runs")
+    ap.add_argument("--ingest-copy", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="record the copy calibration from two rocprofv3 --pmc runs of --copy-calibration")
+    ap.add_argument("--command", default="", help="the command the ingested counter runs used")
     args = ap.parse_args()
+
+    if args.ingest_pmc:
+        ingest_pmc(args.config, *args.ingest_pmc, command=args.command)
+        return
+    if args.ingest_copy:
+        ingest_copy(*args.ingest_copy, nbytes=args.copy_calibration or (256 << 20), command=args.command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no multi-GPU "
@@ -238,6 +378,10 @@ def main():
 
     import torch
 
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration, 8)
+        return
+
     import rmsnorm_nvfp4_block_amd as q
     import workloads
 
@@ -247,23 +391,21 @@ def main():
     log(f"[bench] {case.describe()}")
 
     # whole step (amax + quantize), the figure the metric is quoted on
-    ms = None
-    if not args.stage_only:
-        ms = time_steps(case, args.steps, args.warmup, eager=args.eager)
-        log(f"[bench] full step: {ms * 1e3:.2f} us/step")
-
-    # quantize stage alone against the amax the full step produced
-    amax_t = case.step(0)["amax"].clone()
-    torch.cuda.synchronize()
-    sms = time_steps(case, args.steps, args.warmup, amax=amax_t, eager=args.eager)
-    stage_gbs = case.bytes / (sms * 1e-3) / 1e9
-    log(f"[bench] quantize stage (given amax): {sms * 1e3:.2f} us/launch, {stage_gbs:.1f} GB/s")
-
-    if ms is None:
-        ms = sms
+    ms = time_steps(case, args.steps, args.warmup, eager=args.eager)
+    log(f"[bench] full step: {ms * 1e3:.2f} us/step")
     value = case.bytes / (ms * 1e-3) / 1e9
-    kernel_name = {"prefill": "k_rmsnorm (quantize pass)", "decode": "k_rmsnorm (quantize pass)",
-                   "quantize": "k_quant_rows", "weight": "k_quant_2d", "grouped": "k_grouped_quant"}[args.config]
+
+    how, kname, _ = DOMINANT[args.config]
+    if how == "stage":
+        # the encode kernel alone against the amax the full step produced
+        amax_t = case.step(0)["amax"].clone()
+        torch.cuda.synchronize()
+        kms = time_steps(case, args.steps, args.warmup, amax=amax_t, eager=args.eager)
+        log(f"[bench] {kname} alone (given amax): {kms * 1e3:.2f} us/launch")
+    else:
+        kms = ms
+    achieved = case.bytes / (kms * 1e-3) / 1e9
+    traffic = traffic_bytes(args.config)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -282,13 +424,13 @@ def main():
                        if not args.eager else "eager calls"),
         "roofline": {
             "bound": "hbm",
-            "kernel": kernel_name + ", launched with a precomputed amax",
-            "achieved": round(stage_gbs, 2),
+            "kernel": kname + (" (one step)" if how == "step" else ", launched with a precomputed amax"),
+            "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(stage_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
-            "launch_us": round(sms * 1e3, 3),
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": round(traffic) if traffic is not None else None,
+            "launch_us": round(kms * 1e3, 3),
             "bytes_per_launch": case.bytes,
         },
     }

@@ -146,8 +146,41 @@ __device__ __forceinline__ void st_nt8(uint8_t* p, uint2 w) {
   __builtin_nontemporal_store((uint64_t)w.x | ((uint64_t)w.y << 32), reinterpret_cast<uint64_t*>(p));
 }
 
+// One block of the encode pass: lane's 16 values of row `row` at column `col`,
+// gamma + c and beta of those columns in registers, r the row's 1/rms.
+// (v: the block's 16 inputs, already widened to fp32)
+template <bool BIAS, bool SR>
+__device__ __forceinline__ void quant_item(const RowArgs& a, float (&v)[16], uint32_t row, uint32_t col, bool ok,
+                                           float r, const float (&gv)[16], const float (&bv)[16], GScale g,
+                                           const float* rcp_tab, uint32_t cols) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = v[k] * gv[k];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = __builtin_fmaf(v[k], r, bv[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = v[k] * r;
+  }
+  const uint4 y0 = pack8_bf16(v), y1 = pack8_bf16(v + 8);
+  if (a.y != nullptr && ok) {
+    uint16_t* yr = (uint16_t*)a.y + (int64_t)row * a.ld_y + col;
+    *reinterpret_cast<uint4*>(yr) = y0;
+    *reinterpret_cast<uint4*>(yr + 8) = y1;
+  }
+  widen8(y0, v);
+  widen8(y1, v + 8);
+  uint32_t sc;
+  const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)row * (cols >> 4) + (col >> 4), a.seed, a.offset, 0);
+  if (ok) {
+    st_nt8(a.codes + (int64_t)row * a.ldc + (col >> 1), w);
+    __builtin_nontemporal_store((uint8_t)sc, a.scales + (int64_t)row * a.lds + (col >> 4));
+  }
+}
+
+// One block of the row-per-wave encode pass (gamma + c and beta from LDS).
 template <bool FULL, bool BIAS, bool SR>
-__device__ __forceinline__ void quant_item(const RowArgs& a, const Blk& b, const Cursor& pc, float r_lane,
+__device__ __forceinline__ void quant_item_rw(const RowArgs& a, const Blk& b, const Cursor& pc, float r_lane,
                                            const float* gsh, const float* bsh, GScale g, const float* rcp_tab,
                                            uint32_t cols, int lane) {
   const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_lane), (int)pc.k));
@@ -185,8 +218,12 @@ __device__ __forceinline__ void quant_item(const RowArgs& a, const Blk& b, const
   }
 }
 
+// Encode pass, one row per wave at a time (rows wave, wave + nwaves, ...; at
+// most 64 per wave, lane k holding 1/rms of the wave's k-th row): the row's
+// superchunks stream through a kDepth ring with gamma + c (and beta) in LDS.
+// Used when there are enough rows to give every SIMD several waves.
 template <bool FULL, bool BIAS, bool SR>
-__global__ __launch_bounds__(kThreads) void k_rms_quant_stream(const RowArgs a) {
+__global__ __launch_bounds__(kThreads) void k_rms_quant_rowwave(const RowArgs a) {
   extern __shared__ float params[];  // gamma + c [cols], then beta [cols]
   __shared__ float rcp_tab[128];
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
@@ -214,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void k_rms_quant_stream(const RowArgs a) 
     if (base + kDepth < n) {
 #pragma unroll
       for (int d = 0; d < kDepth; ++d) {
-        quant_item<FULL, BIAS, SR>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
+        quant_item_rw<FULL, BIAS, SR>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
         refill<FULL>(a, ring[d], ld, base + kDepth + d, n, nsc, nwaves, cols, lane);
         pc.next(nsc, nwaves);
       }
@@ -222,8 +259,87 @@ __global__ __launch_bounds__(kThreads) void k_rms_quant_stream(const RowArgs a) 
 #pragma unroll
       for (int d = 0; d < kDepth; ++d) {
         if (base + d < n) {
-          quant_item<FULL, BIAS, SR>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
+          quant_item_rw<FULL, BIAS, SR>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
           pc.next(nsc, nwaves);
+        }
+      }
+    }
+  }
+}
+
+// Encode pass, one superchunk column per wave (for few rows: decode-sized
+// calls get nsc times as many waves as rows). Wave w owns one superchunk column, sc = w mod nsc, and the rows
+// w / nsc + j * wps, j = 0 .. nr-1 (wps waves per superchunk column, nr <= 64):
+// its lanes keep their 16 values of gamma + c (and beta) in registers for the
+// whole kernel, and lane j holds 1/rms of the wave's j-th row. D rows in flight.
+template <int D, bool FULL, bool BIAS, bool SR>
+__global__ __launch_bounds__(kThreads) void k_rms_quant_colwave(const RowArgs a, uint32_t wps) {
+  __shared__ float rcp_tab[128];
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = wave_id();
+  const uint32_t nsc = (cols + kSuper - 1) / kSuper;
+  const uint32_t sc = wave % nsc, row0 = wave / nsc;
+  const uint32_t nr = (row0 < wps && row0 < rows) ? (rows - 1 - row0) / wps + 1 : 0;
+  const uint32_t col = sc * kSuper + lane * 16;
+  const bool ok = FULL || col < cols;
+  const uint16_t* __restrict__ xc = (const uint16_t*)a.x + col;
+  const uint16_t* gamma = (const uint16_t*)a.gamma + col;
+  const uint16_t* beta = (const uint16_t*)a.beta + col;
+  // the prologue's loads first: loads complete in issue order
+  const PartialsPre pm = partials_issue(a.ws, a.nparts, a.amax_in);
+  const uint4 g0 = ld16(gamma, ok), g1 = ld16(gamma + 8, ok);
+  uint4 b0 = make_uint4(0u, 0u, 0u, 0u), b1 = b0;
+  if constexpr (BIAS) {
+    b0 = ld16(beta, ok);
+    b1 = ld16(beta + 8, ok);
+  }
+  const float r_lane = (uint32_t)lane < nr ? a.rs[row0 + lane * wps] : 0.0f;
+  // unconditional fill (a wave without rows reads the last row; past the
+  // wave's last row the ring re-reads it): a fill that may be skipped would
+  // turn every later wait into a wait for all loads
+  uint32_t ldr = nr > 0 ? row0 : rows - 1;
+  Blk ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    ring[d] = load_blk<FULL>(xc - col + (int64_t)ldr * a.ld_x, col, cols);
+    if ((uint32_t)d + 1 < nr) ldr += wps;
+  }
+  const GScale g = partials_finish(pm, a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
+  float gv[16], bv[16];
+  widen8(g0, gv);
+  widen8(g1, gv + 8);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) gv[k] = gv[k] + a.woff;
+  widen8(b0, bv);
+  widen8(b1, bv + 8);
+  uint32_t row = row0;
+  for (uint32_t base = 0; base < nr; base += D) {
+    if (base + D < nr) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const float r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_lane), base + d));
+        float v[16];
+        widen16(ring[d], v);
+        // refill before this item's stores: loads and stores share one
+        // in-order counter, so a load issued after a store could not be
+        // waited for without also waiting for the store
+        ring[d] = load_blk<FULL>(xc - col + (int64_t)ldr * a.ld_x, col, cols);
+        if (base + D + d + 1 < nr) ldr += wps;
+        __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of the stores
+        quant_item<BIAS, SR>(a, v, row, col, ok, r, gv, bv, g, rcp_tab, cols);
+        row += wps;
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (base + d < nr) {
+          const float r =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r_lane), base + d));
+          float v[16];
+          widen16(ring[d], v);
+          quant_item<BIAS, SR>(a, v, row, col, ok, r, gv, bv, g, rcp_tab, cols);
+          row += wps;
         }
       }
     }
@@ -253,15 +369,34 @@ hipError_t launch_rms_stream_amax(const RowArgs& a, hipStream_t s, uint32_t* npa
   return hipGetLastError();
 }
 
+// Encode-pass choice: with at least NVFP4Q_RMS_ROWWAVE_MIN rows (default
+// 2048, i.e. two waves per SIMD) one row per wave with up to 1024 workgroups;
+// below that one superchunk column per wave and one row per wave.
+int64_t rowwave_min() {
+  static int64_t v = [] {
+    const char* e = getenv("NVFP4Q_RMS_ROWWAVE_MIN");
+    return e ? (int64_t)atoll(e) : (int64_t)2048;
+  }();
+  return v;
+}
+
 template <bool FULL, bool BIAS>
 static hipError_t launch_qs(const RowArgs& a, hipStream_t s) {
-  // at most kMaxWaveRows rows per wave: lane k holds the k-th row's 1/rms
-  const int64_t min_wgs = (a.rows + kMaxWaveRows * kWavesPerWG - 1) / (kMaxWaveRows * kWavesPerWG);
-  const uint32_t wgs = grid_rows(a.rows, stream_wgs() > min_wgs ? stream_wgs() : min_wgs);
-  if ((int64_t)wgs * kWavesPerWG * kMaxWaveRows < a.rows) return hipErrorInvalidValue;
-  const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
-  if (a.sr) hipLaunchKernelGGL((k_rms_quant_stream<FULL, BIAS, true>), dim3(wgs), dim3(kThreads), lds, s, a);
-  else hipLaunchKernelGGL((k_rms_quant_stream<FULL, BIAS, false>), dim3(wgs), dim3(kThreads), lds, s, a);
+  if (a.rows >= rowwave_min()) {
+    // at most kMaxWaveRows rows per wave: lane k holds the k-th row's 1/rms
+    const int64_t min_wgs = (a.rows + kMaxWaveRows * kWavesPerWG - 1) / (kMaxWaveRows * kWavesPerWG);
+    const uint32_t wgs = grid_rows(a.rows, stream_wgs() > min_wgs ? stream_wgs() : min_wgs);
+    const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
+    if (a.sr) hipLaunchKernelGGL((k_rms_quant_rowwave<FULL, BIAS, true>), dim3(wgs), dim3(kThreads), lds, s, a);
+    else hipLaunchKernelGGL((k_rms_quant_rowwave<FULL, BIAS, false>), dim3(wgs), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+  }
+  const int64_t nsc = (a.cols + kSuper - 1) / kSuper;
+  const int64_t wps = a.rows;  // one row per wave
+  const int64_t wgs = (wps * nsc + kWavesPerWG - 1) / kWavesPerWG;
+  const dim3 grid((uint32_t)wgs), block(kThreads);
+  if (a.sr) hipLaunchKernelGGL((k_rms_quant_colwave<2, FULL, BIAS, true>), grid, block, 0, s, a, (uint32_t)wps);
+  else hipLaunchKernelGGL((k_rms_quant_colwave<2, FULL, BIAS, false>), grid, block, 0, s, a, (uint32_t)wps);
   return hipGetLastError();
 }
 
