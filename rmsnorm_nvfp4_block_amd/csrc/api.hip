@@ -66,6 +66,18 @@ bool rms_stream_enabled() {
 
 }  // namespace
 
+namespace nvfp4q {
+static bool xcd_order() {
+  static const bool on = [] {
+    const char* e = getenv("NVFP4Q_XCD_ORDER");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+uint32_t xcd_chunk(uint64_t items) { return xcd_order() ? (uint32_t)((items + kXcds - 1) / kXcds) : 0u; }
+uint32_t xcd_grid(uint64_t items) { return xcd_order() ? kXcds * xcd_chunk(items) : (uint32_t)items; }
+}  // namespace nvfp4q
+
 extern "C" {
 
 size_t nvfp4q_workspace_bytes(void) { return sizeof(Workspace); }

@@ -121,14 +121,23 @@ __device__ __forceinline__ float encode_mult(uint32_t scode, float s_dec) {
 struct U4 {
   uint32_t x, y, z, w;
 };
+// a ^ b ^ k in one v_bitop3_b32 (truth table 0x96; the compiler emits two XORs); k is
+// wave-uniform (a key word), so it is passed in a scalar register.
+__device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
+// The key (the seed) must be the same for every lane of the wave.
 __device__ __forceinline__ U4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                        uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    uint32_t n0 = xor3_key((uint32_t)(p1 >> 32), c1, k0);
+    uint32_t n2 = xor3_key((uint32_t)(p0 >> 32), c3, k1);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -150,30 +159,32 @@ __device__ __forceinline__ U4 block_random(uint64_t blk, uint32_t tag, uint64_t 
 // lo <= |v| < hi the neighbouring magnitudes (|v| clamped to 6) and frac the
 // position of |v| between them, the magnitude becomes hi iff
 // r + floor(256 * frac) >= 256 for the element's random byte r; the sign is
-// kept as in round-to-nearest. v_cvt_scalef32_sr_pk_fp4_f32 adds its 32-bit
-// random operand to the bits below the E2M1 step and keeps the carry; with the
-// byte in bits 31..24 and zeros below, that is exactly the rule above (checked
-// against the definition on every float32 input and every byte). Its second
-// source reuses the same random bits, so each element gets its own instruction
-// with a zero partner. The instruction writes only the selected byte of its
-// destination, while the compiler treats the whole register as written, so
-// only byte 0 of the result is meaningful: the element's code in the low
-// nibble and the zero partner's code (0) in the high nibble. Bytes are gathered
-// with v_perm_b32, which reads byte 0 alone.
-__device__ __forceinline__ uint32_t e2m1_sr(float v, uint32_t rand_top) {
-  f32x2 ab = {v, 0.0f};
-  return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, ab, rand_top, 1.0f, 0);
+// kept as in round-to-nearest.
+//
+// v_cvt_scalef32_sr_pk_fp4_f32 converts a pair (a, b) with one 32-bit random
+// operand R: for a it adds R to the bits below the E2M1 step and keeps the
+// carry, for b it does the same with R << 1 (measured: b follows the rule with
+// byte r exactly when R = r << 23, a when R = r << 24, zeros below; checked
+// against the definition on 4096 values x 256 bytes). Each element has its own
+// byte, so a pair is converted twice: once with a's byte in bits 31..24 (the
+// low nibble, a's code, is kept) and once with b's byte in bits 30..23 (the
+// high nibble, b's code, is kept). The instruction writes only the selected
+// byte of its destination while the compiler treats the whole register as
+// written, so only byte 0 of a result is used; bytes are gathered with
+// v_perm_b32.
+template <int BA, int BB>
+__device__ __forceinline__ uint32_t e2m1_sr_pair(float a, float b, uint32_t wa, uint32_t wb) {
+  const f32x2 ab = {a, b};
+  const uint32_t ra = ((wa >> (8 * BA)) & 0xFFu) << 24;
+  const uint32_t rb = ((wb >> (8 * BB)) & 0xFFu) << 23;
+  const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, ab, ra, 1.0f, 0);
+  const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, ab, rb, 1.0f, 0);
+  return (lo & 0x0Fu) | (hi & ~0x0Fu);  // v_bfi_b32; bytes 1..3 are don't-care
 }
 
-// Byte b of w moved to bits 31..24, zeros below (v_perm_b32 selects bytes of
+// Byte 0 of a, b, c, d gathered into bytes 0..3 (v_perm_b32 selects bytes of
 // its second operand with indices 0..3, of its first with 4..7; 0x0C yields a
 // zero byte).
-template <int B>
-__device__ __forceinline__ uint32_t byte_to_top(uint32_t w) {
-  return __builtin_amdgcn_perm(0u, w, ((uint32_t)B << 24) | 0x000C0C0Cu);
-}
-
-// Byte 0 of a, b, c, d gathered into bytes 0..3.
 __device__ __forceinline__ uint32_t gather_b0(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
   const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
@@ -183,11 +194,8 @@ __device__ __forceinline__ uint32_t gather_b0(uint32_t a, uint32_t b, uint32_t c
 // Eight SR codes packed in a word (element 2i in the low nibble of byte i).
 // Element e takes byte (e & 3) of w0 (e < 4) or of w1 (e >= 4).
 __device__ __forceinline__ uint32_t sr_pack8(const float v[8], uint32_t w0, uint32_t w1) {
-  const uint32_t ev = gather_b0(e2m1_sr(v[0], byte_to_top<0>(w0)), e2m1_sr(v[2], byte_to_top<2>(w0)),
-                                e2m1_sr(v[4], byte_to_top<0>(w1)), e2m1_sr(v[6], byte_to_top<2>(w1)));
-  const uint32_t od = gather_b0(e2m1_sr(v[1], byte_to_top<1>(w0)), e2m1_sr(v[3], byte_to_top<3>(w0)),
-                                e2m1_sr(v[5], byte_to_top<1>(w1)), e2m1_sr(v[7], byte_to_top<3>(w1)));
-  return ev | (od << 4);
+  return gather_b0(e2m1_sr_pair<0, 1>(v[0], v[1], w0, w0), e2m1_sr_pair<2, 3>(v[2], v[3], w0, w0),
+                   e2m1_sr_pair<0, 1>(v[4], v[5], w1, w1), e2m1_sr_pair<2, 3>(v[6], v[7], w1, w1));
 }
 
 // Eight RTNE codes packed in a word.
@@ -351,11 +359,34 @@ __device__ __forceinline__ GScale partials_finish(const PartialsPre& p, const Wo
   return scales_from(a, amax_out, scale_out, rcp_tab);
 }
 
-// Amax pass epilogue: the workgroup's maximum into its partial slot.
+// Amax pass epilogue: the workgroup's maximum into its partial slot (by
+// default the workgroup's linear index).
 __device__ __forceinline__ void publish_partial(Workspace* ws, float m) {
   m = wg_max(m);
   if (threadIdx.x == 0) ws->partial[blockIdx.y * gridDim.x + blockIdx.x] = m;
 }
+__device__ __forceinline__ void publish_partial_at(Workspace* ws, float m, uint32_t slot) {
+  m = wg_max(m);
+  if (threadIdx.x == 0) ws->partial[slot] = m;
+}
+
+// ---------------------------------------------------------------- XCD order
+// The GPU dispatches the workgroups of a launch round-robin over its 8 XCDs
+// (workgroup b to XCD b mod 8), and each XCD has its own L2. Tiles that are
+// neighbours in a plane share partially written cache lines (a 128-token tile
+// writes half a line of columnwise codes and 8 bytes of a scale line);
+// written through different L2s those lines reach memory in pieces. Giving
+// XCD x the contiguous work items x * chunk .. x * chunk + chunk - 1 keeps
+// neighbours on one L2, where the pieces merge. The grid has kXcds * chunk
+// workgroups; items past the end are idle.
+// (chunk 0: plain order, work item = workgroup index; NVFP4Q_XCD_ORDER=0
+// selects it, for comparison.)
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_work_item(uint32_t chunk) {
+  return chunk ? (blockIdx.x % kXcds) * chunk + blockIdx.x / kXcds : blockIdx.x;
+}
+uint32_t xcd_chunk(uint64_t items);     // 0 when the plain order is selected
+uint32_t xcd_grid(uint64_t items);      // workgroups to launch for `items` work items
 
 __device__ __forceinline__ float max16_abs(const float v[16]) { return fmaxf(max8_abs(v), max8_abs(v + 8)); }
 

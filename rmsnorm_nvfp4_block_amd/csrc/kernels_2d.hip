@@ -31,7 +31,7 @@ __device__ __forceinline__ uint32_t swz_chunk(uint32_t chunk, uint32_t row) {
 }
 
 template <bool ROW, bool COL, bool SR>
-__global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tiles_c) {
+__global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tiles_c, uint32_t ntiles, uint32_t chunk) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileR * kRowBytes];
   __shared__ float rcp_tab[128];
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
@@ -45,7 +45,9 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
   const uint64_t seed = a.seed;
   const uint32_t offset = a.offset;
   const uint32_t t = threadIdx.x;
-  const uint32_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
+  const uint32_t item = xcd_work_item(chunk);  // row-major tile index, contiguous per XCD
+  if (item >= ntiles) return;                  // idle: no barrier or partial depends on it
+  const uint32_t tr = item / tiles_c, tc = item - tr * tiles_c;
   const uint32_t row0 = tr * kTileR, col0 = tc * kTileC;
 
   // ---- load 4 rows x 32 B per thread
@@ -138,9 +140,12 @@ template <bool ROW, bool COL>
 void launch_2d_rc(const TwoDArgs& a, hipStream_t s) {
   const uint32_t tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
   const uint32_t tiles_c = (uint32_t)((a.cols + kTileC - 1) / kTileC);
-  dim3 grid(tiles_r * tiles_c), block(kT);
-  if (a.sr) hipLaunchKernelGGL((k_quant_2d<ROW, COL, true>), grid, block, 0, s, a, tiles_c);
-  else hipLaunchKernelGGL((k_quant_2d<ROW, COL, false>), grid, block, 0, s, a, tiles_c);
+  // Plain row-major tile order: the per-XCD ranges used by the grouped path
+  // measured slower here (66.8 vs 69.5 us on 8192 x 8192 with SR).
+  const uint32_t ntiles = tiles_r * tiles_c, chunk = 0;
+  dim3 grid(ntiles), block(kT);
+  if (a.sr) hipLaunchKernelGGL((k_quant_2d<ROW, COL, true>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+  else hipLaunchKernelGGL((k_quant_2d<ROW, COL, false>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
 }
 
 }  // namespace

@@ -186,13 +186,17 @@ __device__ __forceinline__ void signed_fwht16(float v[16], uint32_t mask) {
 template <bool RHT>
 __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict__ x, int rows, uint32_t cols, int64_t ld_x,
                                                      const int32_t* __restrict__ offsets, int groups, uint32_t mask,
-                                                     Workspace* ws) {
-  const GroupTile t = locate_tile(offsets, groups, rows, blockIdx.x);
+                                                     Workspace* ws, uint32_t gx, uint32_t gy, uint32_t chunk) {
+  // work item = column tile * gx + tile slot, contiguous per XCD
+  const uint32_t item = xcd_work_item(chunk);
+  if (item >= gx * gy) return;
+  const uint32_t slot = item % gx, ctile = item / gx;
+  const GroupTile t = locate_tile(offsets, groups, rows, slot);
   const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float m = 0.0f;
   if (t.g >= 0) {
     const uint32_t mb = lane & 7, cg = lane >> 3;
-    const uint32_t col = blockIdx.y * kTileCol + wv * 64 + cg * 8;
+    const uint32_t col = ctile * kTileCol + wv * 64 + cg * 8;
     const uint32_t blk_tok0 = (uint32_t)t.tok0 + mb * 16;
     if ((int)blk_tok0 < t.pg) {
       uint4 q[16];
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
       if constexpr (RHT) m = bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
     }
   }
-  publish_partial(ws, m);   // one slot per (token tile, column tile); 0 for slots past the last tile
+  publish_partial_at(ws, m, item);   // one slot per (token tile, column tile); 0 for slots past the last tile
 }
 
 // Pass 2: transform (optional), bf16 round-through, per-block scale and codes.
@@ -220,21 +224,23 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
                                                       uint8_t* __restrict__ scales, int64_t lds,
                                                       const Workspace* ws, const float* amax_in, float* amax_out,
                                                       float* scale_out, int32_t* poff_out, uint64_t seed,
-                                                      uint32_t offset, int64_t cap) {
-  const GroupTile t = locate_tile(offsets, groups, rows, blockIdx.x);
+                                                      uint32_t offset, int64_t cap, uint32_t gx, uint32_t gy,
+                                                      uint32_t chunk) {
+  const uint32_t item = xcd_work_item(chunk);
+  if (item >= gx * gy) return;
+  const uint32_t slot = item % gx, ctile = item / gx;
+  const GroupTile t = locate_tile(offsets, groups, rows, slot);
   __shared__ float rcp_tab[128];
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    report_groups(offsets, groups, rows, ws, gridDim.x, gridDim.y, amax_in, amax_out, scale_out, poff_out);
+  if (item == 0) report_groups(offsets, groups, rows, ws, gx, gy, amax_in, amax_out, scale_out, poff_out);
   if (t.g < 0) return;
   // this group's amax: its tile slots of every column tile of the amax pass
-  const float amax = amax_in ? amax_in[t.g]
-                             : reduce_partials_2d(ws, (uint32_t)t.tile0, (uint32_t)t.tiles, gridDim.x, gridDim.y);
+  const float amax = amax_in ? amax_in[t.g] : reduce_partials_2d(ws, (uint32_t)t.tile0, (uint32_t)t.tiles, gx, gy);
   const GScale g = global_scale(amax);
   fill_rcp_table(rcp_tab, g.dec);
   __syncthreads();
   const uint32_t lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint32_t mb = lane & 7, cg = lane >> 3;
-  const uint32_t col = blockIdx.y * kTileCol + wv * 64 + cg * 8;
+  const uint32_t col = ctile * kTileCol + wv * 64 + cg * 8;
   const uint32_t blk_tok0 = (uint32_t)t.tok0 + mb * 16;
   if ((int)blk_tok0 >= t.pg || col >= cols) return;
   // Plane capacity guard: only malformed offsets can reach it.
@@ -277,20 +283,22 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
 }
 
 template <bool RHT>
-void launch_grouped_r(const GroupArgs& a, dim3 grid, hipStream_t s) {
+void launch_grouped_r(const GroupArgs& a, uint32_t gx, uint32_t gy, hipStream_t s) {
   const uint16_t* x = (const uint16_t*)a.x;
   const int64_t cap = a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16;
+  const uint32_t chunk = xcd_chunk((uint64_t)gx * gy);
+  const dim3 grid(xcd_grid((uint64_t)gx * gy));
   if (!a.amax_in)
     hipLaunchKernelGGL((k_grouped_amax<RHT>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets,
-                       a.groups, a.mask, a.ws);
+                       a.groups, a.mask, a.ws, gx, gy, chunk);
   if (a.sr)
     hipLaunchKernelGGL((k_grouped_quant<RHT, true>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets,
                        a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in, a.amax_out,
-                       a.scale_out, a.poff_out, a.seed, a.offset, cap);
+                       a.scale_out, a.poff_out, a.seed, a.offset, cap, gx, gy, chunk);
   else
     hipLaunchKernelGGL((k_grouped_quant<RHT, false>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x,
                        a.offsets, a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in,
-                       a.amax_out, a.scale_out, a.poff_out, a.seed, a.offset, cap);
+                       a.amax_out, a.scale_out, a.poff_out, a.seed, a.offset, cap, gx, gy, chunk);
 }
 
 }  // namespace
@@ -306,9 +314,8 @@ int64_t grouped_partials(int64_t rows, int64_t cols, int groups) {
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {
   const int64_t max_tiles = (a.rows + 15 * (int64_t)a.groups + kTileTok - 1) / kTileTok + a.groups;
   const uint32_t col_tiles = (uint32_t)((a.cols + kTileCol - 1) / kTileCol);
-  dim3 grid((uint32_t)max_tiles, col_tiles);
-  if (a.rht) launch_grouped_r<true>(a, grid, s);
-  else launch_grouped_r<false>(a, grid, s);
+  if (a.rht) launch_grouped_r<true>(a, (uint32_t)max_tiles, col_tiles, s);
+  else launch_grouped_r<false>(a, (uint32_t)max_tiles, col_tiles, s);
   return hipGetLastError();
 }
 
