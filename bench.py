@@ -222,8 +222,8 @@ def cpu_baseline(case, budget_s=12.0):
 # both are timed together as one step. "stage": the encode kernel alone, launched
 # with the amax the full step produced (the same kernel the full step runs).
 DOMINANT = {
-    "prefill": ("step", "k_rms_amax_stream + k_rms_quant_stream", r"k_rms_amax_stream|k_rms_quant_stream"),
-    "decode": ("step", "k_rmsnorm (amax pass) + k_rms_quant_stream", r"k_rmsnorm<|k_rms_quant_stream"),
+    "prefill": ("step", "k_rms_amax_stream + k_rms_quant_rowwave", r"k_rms_amax_stream|k_rms_quant_rowwave"),
+    "decode": ("step", "k_rmsnorm (amax pass) + k_rms_quant_colwave", r"k_rmsnorm<|k_rms_quant_colwave"),
     "quantize": ("stage", "k_quant_rows", r"k_quant_rows"),
     "weight": ("stage", "k_quant_2d", r"k_quant_2d"),
     "grouped": ("stage", "k_grouped_quant", r"k_grouped_quant"),
