@@ -217,13 +217,14 @@ def cpu_baseline(case, budget_s=12.0):
 
 # ----------------------------------------------------------------------------- roofline
 # The kernel each workload's roofline entry describes, how it is timed, and the
-# pattern of its kernel names in a rocprofv3 trace. "step": the hot path is two
-# kernels with a grid-wide dependency between them (amax pass, encode pass);
-# both are timed together as one step. "stage": the encode kernel alone, launched
-# with the amax the full step produced (the same kernel the full step runs).
+# pattern of its kernel names in a rocprofv3 trace. "stage": the encode kernel
+# alone, launched with the amax the full step produced (for quantize, weight
+# and grouped the same kernel the full step runs; for RMSNorm the single-pass
+# encode that a given amax selects, since the full step's encode pass reads the
+# amax pass's per-row 1/rms). "step": both passes timed together.
 DOMINANT = {
-    "prefill": ("step", "k_rms_amax_stream + k_rms_quant_rowwave", r"k_rms_amax_stream|k_rms_quant_rowwave"),
-    "decode": ("step", "k_rmsnorm (amax pass) + k_rms_quant_colwave", r"k_rmsnorm<|k_rms_quant_colwave"),
+    "prefill": ("stage", "k_rms_coop (encode mode)", r"k_rms_coop<\d+, \d+, \w+, \w+, 1, \w+>"),
+    "decode": ("stage", "k_rms_coop (encode mode)", r"k_rms_coop<\d+, \d+, \w+, \w+, 1, \w+>"),
     "quantize": ("stage", "k_quant_rows", r"k_quant_rows"),
     "weight": ("stage", "k_quant_2d", r"k_quant_2d"),
     "grouped": ("stage", "k_grouped_quant", r"k_grouped_quant"),

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnvfp4q.so")
 SOURCES = [
-    "api.hip", "kernels_rows.hip", "kernels_rms_a.hip", "kernels_rms_b.hip", "kernels_rms_c.hip",
+    "api.hip", "kernels_rows.hip", "kernels_rms_coop.hip",
     "kernels_rms_stream.hip",
     "kernels_2d.hip", "kernels_grouped.hip",
 ]

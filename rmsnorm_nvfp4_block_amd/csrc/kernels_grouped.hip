@@ -144,14 +144,22 @@ __device__ void report_groups(const int32_t* __restrict__ offsets, int groups, i
 }
 
 // Load the lane's 16 tokens x 8 columns (zero for padding rows and columns
-// past the end).
+// past the end). A block with all 16 rows inside the group (every block but a
+// group's last) takes unconditional loads from one base address with the row
+// stride added as a scalar; only the last block pays per-row guards.
 __device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t ld_x, const GroupTile& t,
                                            uint32_t blk_tok0, uint32_t col, uint32_t cols, uint4 q[16]) {
+  if ((int)blk_tok0 + 16 <= t.n && col < cols) {
+    const uint16_t* p = x + (int64_t)(t.row0 + (int)blk_tok0) * ld_x + col;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int lt = (int)blk_tok0 + i;
-    const bool ok = lt < t.n && col < cols;
-    q[i] = ld16(x + (int64_t)(t.row0 + lt) * ld_x + col, ok);
+    for (int i = 0; i < 16; ++i) q[i] = *reinterpret_cast<const uint4*>(p + i * ld_x);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int lt = (int)blk_tok0 + i;
+      const bool ok = lt < t.n && col < cols;
+      q[i] = ld16(x + (int64_t)(t.row0 + lt) * ld_x + col, ok);
+    }
   }
 }
 

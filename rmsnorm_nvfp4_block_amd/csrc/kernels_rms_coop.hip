@@ -1,0 +1,211 @@
+// Cooperative-row RMSNorm kernels: the amax pass when a bias is present, the
+// encode pass when the amax is given (or when there are more rows than the
+// workspace keeps 1/rms for), and the y-only normalization.
+//
+// The four waves of a workgroup share each token row: wave w takes the
+// 1024-column superchunks w, w + 4, ... of the row (lane l: the 16-element
+// block at columns 16l..16l+15 of each), forms its partial sum of squares,
+// and the four partials meet in LDS behind one barrier per row; every wave
+// then has 1/rms and normalizes and encodes its own superchunks. A workgroup
+// walks its rows (b, b + G, b + 2G, ...) with D rows in flight, so a wave
+// holds one superchunk per row and per slot instead of a whole row, and rows
+// complete in the order their loads were issued.
+//
+// "CuTeDSL at Perplexity", QK Norm (the normalization: r = 1/sqrt(mean x^2 +
+// eps), y = RN((gamma + c) x r) [+ beta]) and Prefill and decode (one token
+// row per thread group, reductions kept inside the group).
+#include "rows.hpp"
+
+namespace nvfp4q {
+
+namespace {
+
+enum CoopMode { kCoopAmax = 0, kCoopEncode = 1, kCoopYOnly = 2 };
+
+// The wave's NPW superchunks of one row (zero past the row's end).
+template <int NPW, bool FULL>
+__device__ __forceinline__ void coop_load(const RowArgs& a, uint32_t row, uint32_t wid, int lane, uint32_t cols,
+                                          Blk (&q)[NPW]) {
+  const uint16_t* xr = (const uint16_t*)a.x + (int64_t)row * a.ld_x;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) q[j] = load_blk<FULL>(xr, (wid + 4 * j) * kSuper + lane * 16, cols);
+}
+
+// One row: partial sums of squares, the barrier, 1/rms, then the mode's work.
+// Returns the contribution to the amax pass's maximum (kCoopAmax).
+template <int NPW, bool FULL, bool BIAS, int MODE, bool SR>
+__device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32_t k, const Blk (&q)[NPW],
+                                          float (*ssp)[kWavesPerWG], const float* gsh, const float* bsh, GScale g,
+                                          const float* rcp_tab, float inv_k, uint32_t wid, int lane, uint32_t cols) {
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) ss = sumsq8(q[j].hi, sumsq8(q[j].lo, ss));
+  ss = wave_sum(ss);
+  if (lane == 0) ssp[k & 1][wid] = ss;
+  // Double-buffered partials: a wave writes row k + 1's partial only after
+  // every wave has passed row k's barrier and read row k - 1's buffer.
+  __syncthreads();
+  const float* sp = ssp[k & 1];
+  const float r = inv_rms((sp[0] + sp[1]) + (sp[2] + sp[3]), inv_k, a.eps);
+  float mrow = 0.0f;
+  if constexpr (MODE == kCoopAmax) {
+    if (a.rs != nullptr && wid == 0 && lane == 0) a.rs[row] = r;
+  }
+  const uint32_t nbr = cols >> 4;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const uint32_t col = (wid + 4 * j) * kSuper + lane * 16;
+    const bool ok = FULL || col < cols;
+    const uint32_t lcol = ok ? col : 0;
+    float v[16], gv[16];
+    widen16(q[j], v);
+    lds16(gsh, lcol, gv);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = v[i] * gv[i];
+    if constexpr (MODE == kCoopAmax && !BIAS) {
+      // y = RN(RN(x * g) * r) is monotone in |RN(x * g)| for this row's r
+      mrow = fmaxf(mrow, max16_abs(v));
+      continue;
+    }
+    if constexpr (BIAS) {
+      float bv[16];
+      lds16(bsh, lcol, bv);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(v[i], r, bv[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = v[i] * r;
+    }
+    if constexpr (MODE == kCoopAmax) {
+      mrow = fmaxf(mrow, max16_abs(v));
+    } else {
+      const uint4 y0 = pack8_bf16(v), y1 = pack8_bf16(v + 8);
+      if (a.y != nullptr && ok) {
+        uint16_t* yr = (uint16_t*)a.y + (int64_t)row * a.ld_y + col;
+        *reinterpret_cast<uint4*>(yr) = y0;
+        *reinterpret_cast<uint4*>(yr + 8) = y1;
+      }
+      if constexpr (MODE == kCoopEncode) {
+        widen8(y0, v);
+        widen8(y1, v + 8);
+        uint32_t sc;
+        const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)row * nbr + (col >> 4), a.seed, a.offset, 0);
+        if (ok) {
+          *reinterpret_cast<uint2*>(a.codes + (int64_t)row * a.ldc + (col >> 1)) = w;
+          a.scales[(int64_t)row * a.lds + (col >> 4)] = (uint8_t)sc;
+        }
+      }
+    }
+  }
+  if constexpr (MODE == kCoopAmax) return BIAS ? mrow : mrow * r;
+  return 0.0f;
+}
+
+template <int NPW, int D, bool FULL, bool BIAS, int MODE, bool SR>
+__global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
+  extern __shared__ float params[];  // gamma + c, then beta (param_floats(cols) each)
+  __shared__ float ssp[2][kWavesPerWG];
+  __shared__ float rcp_tab[128];
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t G = gridDim.x, b = blockIdx.x;
+  const uint32_t nr = b < rows ? (rows - 1 - b) / G + 1 : 0;  // this workgroup's rows
+  const uint32_t last = nr > 0 ? b + (nr - 1) * G : rows - 1;
+  // the prologue's loads first: loads complete in issue order
+  PartialsPre pm;
+  if constexpr (MODE == kCoopEncode) pm = partials_issue(a.ws, a.nparts, a.amax_in);
+  const ParamsPre pp = params_issue<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, cols);
+  // unconditional fill (row index clamped to the workgroup's last row): a
+  // fill that may be skipped would turn every later wait into a wait for all
+  Blk ring[D][NPW];
+#pragma unroll
+  for (int d = 0; d < D; ++d) coop_load<NPW, FULL>(a, (uint32_t)d < nr ? b + d * G : last, wid, lane, cols, ring[d]);
+  float* gsh = params;
+  float* bsh = params + param_floats(cols);
+  params_finish<BIAS>(pp, (const uint16_t*)a.gamma, (const uint16_t*)a.beta, a.woff, cols, gsh, bsh);
+  GScale g = {1.0f, 1.0f};
+  if constexpr (MODE == kCoopEncode) g = partials_finish(pm, a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
+  else __syncthreads();
+  const float inv_k = 1.0f / (float)cols;
+  float mloc = 0.0f;
+  for (uint32_t k = 0; k < nr; k += D) {
+    if (k + D < nr) {
+      // a slot is refilled (row k + D + d, clamped) as soon as its row is done
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const uint32_t kk = k + d;
+        mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g, rcp_tab,
+                                                               inv_k, wid, lane, cols));
+        coop_load<NPW, FULL>(a, kk + D < nr ? b + (kk + D) * G : last, wid, lane, cols, ring[d]);
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const uint32_t kk = k + d;
+        if (kk < nr)
+          mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g,
+                                                                 rcp_tab, inv_k, wid, lane, cols));
+      }
+    }
+  }
+  if constexpr (MODE == kCoopAmax) {
+    // max |bf16(y)| = bf16(max |y|): round-to-nearest-even is monotone.
+    publish_partial(a.ws, bf_lo(pack_bf16(mloc, mloc) & 0xFFFFu));
+  }
+}
+
+// Workgroups per launch: min(rows, NVFP4Q_RMS_COOP_WGS), default 1024.
+int64_t coop_wgs() {
+  static int64_t v = [] {
+    const char* e = getenv("NVFP4Q_RMS_COOP_WGS");
+    return e ? (int64_t)atoll(e) : (int64_t)1024;
+  }();
+  return v;
+}
+
+// Two rows in flight per workgroup: three or four measured slower on the
+// 4096 x 4096 prefill (11.3 us at two, 11.7-12.5 us deeper).
+constexpr int kCoopDepth = 2;
+
+template <int NPW, bool BIAS, int MODE, bool SR>
+hipError_t launch_coop_t(const RowArgs& a, uint32_t wgs, hipStream_t s) {
+  const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
+  if (a.cols == (int64_t)NPW * 4 * kSuper)
+    hipLaunchKernelGGL((k_rms_coop<NPW, kCoopDepth, true, BIAS, MODE, SR>), dim3(wgs), dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_rms_coop<NPW, kCoopDepth, false, BIAS, MODE, SR>), dim3(wgs), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int NPW, bool BIAS>
+hipError_t launch_coop_mode(const RowArgs& a, int mode, uint32_t wgs, hipStream_t s) {
+  if (mode == kCoopAmax) return launch_coop_t<NPW, BIAS, kCoopAmax, false>(a, wgs, s);
+  if (mode == kCoopYOnly) return launch_coop_t<NPW, BIAS, kCoopYOnly, false>(a, wgs, s);
+  if (a.sr) return launch_coop_t<NPW, BIAS, kCoopEncode, true>(a, wgs, s);
+  return launch_coop_t<NPW, BIAS, kCoopEncode, false>(a, wgs, s);
+}
+
+template <int NPW>
+hipError_t launch_coop_npw(const RowArgs& a, int mode, uint32_t wgs, hipStream_t s) {
+  return a.beta ? launch_coop_mode<NPW, true>(a, mode, wgs, s) : launch_coop_mode<NPW, false>(a, mode, wgs, s);
+}
+
+}  // namespace
+
+int rms_max_cols() { return 16 * kSuper; }
+
+hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, uint32_t* nparts) {
+  int64_t wgs = a.rows < coop_wgs() ? a.rows : coop_wgs();
+  if (amax_pass && wgs > kRowPartials) wgs = kRowPartials;
+  if (wgs < 1) wgs = 1;
+  if (amax_pass) *nparts = (uint32_t)wgs;
+  const int mode = amax_pass ? kCoopAmax : (a.codes != nullptr ? kCoopEncode : kCoopYOnly);
+  const int64_t nsc = (a.cols + kSuper - 1) / kSuper;
+  if (nsc <= 4) return launch_coop_npw<1>(a, mode, (uint32_t)wgs, s);
+  if (nsc <= 8) return launch_coop_npw<2>(a, mode, (uint32_t)wgs, s);
+  if (nsc <= 16) return launch_coop_npw<4>(a, mode, (uint32_t)wgs, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nvfp4q

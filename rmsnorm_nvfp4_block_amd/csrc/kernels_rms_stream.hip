@@ -356,6 +356,16 @@ int64_t stream_wgs() {
   return v;
 }
 
+// Workgroups of the row-per-wave encode pass: NVFP4Q_RMS_ENCODE_WGS, default
+// the same as the amax pass.
+int64_t encode_wgs() {
+  static int64_t v = [] {
+    const char* e = getenv("NVFP4Q_RMS_ENCODE_WGS");
+    return e ? (int64_t)atoll(e) : stream_wgs();
+  }();
+  return v;
+}
+
 bool full_cols(int64_t cols) { return cols % kSuper == 0; }
 
 }  // namespace
@@ -385,7 +395,7 @@ static hipError_t launch_qs(const RowArgs& a, hipStream_t s) {
   if (a.rows >= rowwave_min()) {
     // at most kMaxWaveRows rows per wave: lane k holds the k-th row's 1/rms
     const int64_t min_wgs = (a.rows + kMaxWaveRows * kWavesPerWG - 1) / (kMaxWaveRows * kWavesPerWG);
-    const uint32_t wgs = grid_rows(a.rows, stream_wgs() > min_wgs ? stream_wgs() : min_wgs);
+    const uint32_t wgs = grid_rows(a.rows, encode_wgs() > min_wgs ? encode_wgs() : min_wgs);
     const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
     if (a.sr) hipLaunchKernelGGL((k_rms_quant_rowwave<FULL, BIAS, true>), dim3(wgs), dim3(kThreads), lds, s, a);
     else hipLaunchKernelGGL((k_rms_quant_rowwave<FULL, BIAS, false>), dim3(wgs), dim3(kThreads), lds, s, a);

@@ -1,5 +1,4 @@
-// Rowwise kernels for gfx950: tensor amax, rowwise NVFP4 quantization and the
-// fused RMSNorm + rowwise NVFP4 passes.
+// Rowwise kernels for gfx950: tensor amax and rowwise NVFP4 quantization.
 //
 // Layout: one wave owns one row at a time. A row is cut into superchunks of
 // 1024 columns; in each superchunk lane l holds one whole 16-element block,
@@ -18,12 +17,12 @@
 // product takes at most 127 values per tensor ("[nvfp4_training] ...", Fast
 // math).
 //
-// Fused RMSNorm: an amax pass, then a pass that normalizes again and encodes
-// ("CuTeDSL at Perplexity", grid synchronization: the kernel boundary is the
-// grid-wide barrier between the two). A single launch with an in-kernel grid
-// barrier was measured slower on MI355X: cooperative launches add about 20 us
-// between kernels, and the barrier is a chain of device-scope atomic round
-// trips. The second pass finds x in the 256 MB Infinity Cache.
+// The amax pass and the encode pass are two launches: the kernel boundary is
+// the grid-wide barrier between them ("CuTeDSL at Perplexity", grid
+// synchronization). A single launch with an in-kernel grid barrier was
+// measured slower on MI355X: cooperative launches add about 20 us between
+// kernels, and the barrier is a chain of device-scope atomic round trips.
+// The RMSNorm passes are in kernels_rms_stream.hip and kernels_rms_coop.hip.
 #include "rows.hpp"
 
 namespace nvfp4q {
@@ -122,31 +121,6 @@ hipError_t launch_quant_rows(const RowArgs& a, hipStream_t s) {
   dim3 grid(grid_rows(a.rows)), block(kThreads);
   if (a.sr) hipLaunchKernelGGL(k_quant_rows<true>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(k_quant_rows<false>, grid, block, 0, s, a);
-  return hipGetLastError();
-}
-
-// Instantiated in kernels_rms_*.hip.
-extern template void launch_rms_nsc<1>(const RowArgs&, bool, hipStream_t);
-extern template void launch_rms_nsc<2>(const RowArgs&, bool, hipStream_t);
-extern template void launch_rms_nsc<4>(const RowArgs&, bool, hipStream_t);
-extern template void launch_rms_nsc<7>(const RowArgs&, bool, hipStream_t);
-extern template void launch_rms_nsc<8>(const RowArgs&, bool, hipStream_t);
-extern template void launch_rms_nsc<12>(const RowArgs&, bool, hipStream_t);
-extern template void launch_rms_nsc<16>(const RowArgs&, bool, hipStream_t);
-
-int rms_max_cols() { return 16 * kSuper; }
-
-hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, uint32_t* nparts) {
-  if (amax_pass) *nparts = grid_rows(a.rows, rms_wgs() > kRowPartials ? kRowPartials : rms_wgs());
-  const int64_t need = (a.cols + kSuper - 1) / kSuper;
-  if (need <= 1) launch_rms_nsc<1>(a, amax_pass, s);
-  else if (need <= 2) launch_rms_nsc<2>(a, amax_pass, s);
-  else if (need <= 4) launch_rms_nsc<4>(a, amax_pass, s);
-  else if (need <= 7) launch_rms_nsc<7>(a, amax_pass, s);
-  else if (need <= 8) launch_rms_nsc<8>(a, amax_pass, s);
-  else if (need <= 12) launch_rms_nsc<12>(a, amax_pass, s);
-  else if (need <= 16) launch_rms_nsc<16>(a, amax_pass, s);
-  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
