@@ -43,8 +43,10 @@
  *   - `workspace` is device scratch memory of at least nvfp4q_workspace_bytes()
  *     bytes (1 MiB), 256-byte aligned, owned by the caller. Its contents need no
  *     initialization and carry nothing from one call to the next (an amax pass
- *     writes per-workgroup partial maxima there and the encode pass of the
- *     same call reads them), so one workspace serves any number of calls that
+ *     writes per-workgroup partial maxima there, and for RMSNorm each row's
+ *     1/rms, and the encode pass of the same call reads them; every slot read
+ *     is written earlier in the same call), so one workspace serves any number
+ *     of calls that
  *     are ordered on one stream; calls that can run at the same time (different
  *     streams) need different workspaces.
  *   - Errors are returned synchronously, before anything is enqueued, except
@@ -153,6 +155,9 @@ nvfp4q_status nvfp4q_quantize(const void *x, nvfp4q_dtype dtype, int64_t rows, i
  *   y_out: device [tokens, hidden] bf16 with row stride ld_y, or NULL.
  *   row: the rowwise plane, or row->codes == NULL to produce only y_out.
  *   rounding / rng as for nvfp4q_quantize.
+ *   g: as for nvfp4q_quantize; with g->amax_in the call is one pass over x
+ *     (the amax is not computed), otherwise an amax pass precedes the encode
+ *     pass. hidden <= 16384 (NVFP4Q_E_UNSUPPORTED above that).
  */
 nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, int64_t hidden,
                              int64_t ld_x, const void *gamma, const void *beta, float weight_offset,

@@ -121,12 +121,10 @@ __device__ __forceinline__ float encode_mult(uint32_t scode, float s_dec) {
 struct U4 {
   uint32_t x, y, z, w;
 };
-// a ^ b ^ k in one v_bitop3_b32 (truth table 0x96; the compiler emits two XORs); k is
-// wave-uniform (a key word), so it is passed in a scalar register.
+// a ^ b ^ k in one v_bitop3_b32 (truth table 0x96 = three-input XOR; the
+// compiler emits two XORs for the plain expression).
 __device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
-  uint32_t r;
-  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-  return r;
+  return __builtin_amdgcn_bitop3_b32(a, b, k, 0x96);
 }
 
 // The key (the seed) must be the same for every lane of the wave.

@@ -54,13 +54,22 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
   const uint32_t bsub = t & 7, rsub = t >> 3;
   const uint32_t col = col0 + bsub * 16;
   uint4 q[4][2];
+  const uint16_t* xp = x + (int64_t)(row0 + rsub) * ld_x + col;
+  if (row0 + kTileR <= rows && col0 + kTileC <= cols) {
+    // a whole tile (all but the edge tiles): no guards, one base address
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t r = row0 + rsub + 32 * j;
-    const bool ok = r < rows && col < cols;
-    const uint16_t* p = x + (int64_t)r * ld_x + col;
-    q[j][0] = ld16(p, ok);
-    q[j][1] = ld16(p + 8, ok);
+    for (int j = 0; j < 4; ++j) {
+      q[j][0] = *reinterpret_cast<const uint4*>(xp + (int64_t)(32 * j) * ld_x);
+      q[j][1] = *reinterpret_cast<const uint4*>(xp + (int64_t)(32 * j) * ld_x + 8);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t r = row0 + rsub + 32 * j;
+      const bool ok = r < rows && col < cols;
+      q[j][0] = ld16(xp + (int64_t)(32 * j) * ld_x, ok);
+      q[j][1] = ld16(xp + (int64_t)(32 * j) * ld_x + 8, ok);
+    }
   }
   const GScale g = consume_scales(a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
   if constexpr (COL) {
@@ -74,19 +83,25 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
   }
   // ---- rowwise plane from registers
   if constexpr (ROW) {
+    // block index, code and scale addresses of row r0 once; rows 32 apart
+    // then differ by uniform strides (64-bit products cost several cycles)
     const uint32_t nbr = cols >> 4;
+    const uint32_t r0 = row0 + rsub;
+    const uint64_t blk0 = (uint64_t)r0 * nbr + (col >> 4);
+    uint8_t* cp = rcodes + (int64_t)r0 * rldc + (col >> 1);
+    uint8_t* sp = rscales + (int64_t)r0 * rlds + (col >> 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t r = row0 + rsub + 32 * j;
+      const uint32_t r = r0 + 32 * j;
       const bool ok = r < rows && col < cols;
       float v[16];
       widen8(q[j][0], v);
       widen8(q[j][1], v + 8);
       uint32_t sc;
-      const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)r * nbr + (col >> 4), seed, offset, 0);
+      const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, blk0 + (uint64_t)(32 * j) * nbr, seed, offset, 0);
       if (ok) {
-        *reinterpret_cast<uint2*>(rcodes + (int64_t)r * rldc + (col >> 1)) = w;
-        rscales[(int64_t)r * rlds + (col >> 4)] = (uint8_t)sc;
+        *reinterpret_cast<uint2*>(cp + (int64_t)(32 * j) * rldc) = w;
+        sp[(int64_t)(32 * j) * rlds] = (uint8_t)sc;
       }
     }
   }
@@ -105,9 +120,13 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
     const uint32_t grow = row0 + mb * 16;              // first row of the block
     const bool rok = grow < rows;
     const uint32_t nbc = rows >> 4;                    // column blocks per plane row
+    const uint32_t gc0 = col0 + lc;
+    const uint64_t cblk0 = (uint64_t)gc0 * nbc + (grow >> 4);
+    uint8_t* ccp = ccodes + (int64_t)gc0 * cldc + (grow >> 1);
+    uint8_t* csp = cscales + (int64_t)gc0 * clds + (grow >> 4);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t gc = col0 + lc + c;
+      const uint32_t gc = gc0 + c;
       float v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -121,7 +140,7 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
       for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
       uint2 out;
       if constexpr (SR) {
-        U4 w = block_random((uint64_t)gc * nbc + (grow >> 4), 1, seed, offset);
+        U4 w = block_random(cblk0 + (uint64_t)c * nbc, 1, seed, offset);
         out.x = sr_pack8(v, w.x, w.y);
         out.y = sr_pack8(v + 8, w.z, w.w);
       } else {
@@ -129,8 +148,8 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
         out.y = rtne_pack8(v + 8);
       }
       if (rok && gc < cols) {
-        *reinterpret_cast<uint2*>(ccodes + (int64_t)gc * cldc + (grow >> 1)) = out;
-        cscales[(int64_t)gc * clds + (grow >> 4)] = (uint8_t)sc;
+        *reinterpret_cast<uint2*>(ccp + (int64_t)c * cldc) = out;
+        csp[(int64_t)c * clds] = (uint8_t)sc;
       }
     }
   }

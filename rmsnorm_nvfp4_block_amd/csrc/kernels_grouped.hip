@@ -172,12 +172,26 @@ __device__ __forceinline__ void column(const uint4 q[16], int c, float v[16]) {
   }
 }
 
-// t = D v (sign flips from the mask), then four butterfly stages in Sylvester
-// order: for h = 1, 2, 4, 8 the pairs (i, i + h) with (i & h) == 0 become
-// (a + b, a - b). The caller applies the 0.25 scaling.
-__device__ __forceinline__ void signed_fwht16(float v[16], uint32_t mask) {
+// D: flips the sign of token row i of the lane's block where bit i of the
+// mask is set. Row i's 16 bytes hold 8 bf16 columns, so one XOR with
+// 0x80008000 per word flips all 8 (the bf16 sign bit becomes the fp32 sign
+// bit when the value is widened). The mask is wave-uniform, so the per-row
+// constants are scalar.
+__device__ __forceinline__ void apply_signs(uint4 q[16], uint32_t mask) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((mask >> i) & 1u) << 31));
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t f = ((mask >> i) & 1u) ? 0x80008000u : 0u;
+    q[i].x ^= f;
+    q[i].y ^= f;
+    q[i].z ^= f;
+    q[i].w ^= f;
+  }
+}
+
+// Four butterfly stages in Sylvester order on D v: for h = 1, 2, 4, 8 the
+// pairs (i, i + h) with (i & h) == 0 become (a + b, a - b). The caller
+// applies the 0.25 scaling.
+__device__ __forceinline__ void fwht16(float v[16]) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1) {
 #pragma unroll
@@ -209,11 +223,12 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
     if ((int)blk_tok0 < t.pg) {
       uint4 q[16];
       load_block(x, ld_x, t, blk_tok0, col, cols, q);
+      if constexpr (RHT) apply_signs(q, mask);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         float v[16];
         column(q, c, v);
-        if constexpr (RHT) signed_fwht16(v, mask);
+        if constexpr (RHT) fwht16(v);
         m = fmaxf(m, fmaxf(max8_abs(v), max8_abs(v + 8)));
       }
       // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
@@ -255,15 +270,20 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
   if ((int64_t)t.poff + blk_tok0 + 16 > cap) return;
   uint4 q[16];
   load_block(x, ld_x, t, blk_tok0, col, cols, q);
+  if constexpr (RHT) apply_signs(q, mask);
   const uint32_t pcol = (uint32_t)t.poff + blk_tok0;      // plane column of the block's first token
   const uint64_t nbp = (uint64_t)(t.mpad >> 4);            // blocks per plane row
+  // block index and addresses of column `col` once; the lane's next columns
+  // differ by uniform strides (64-bit products cost several cycles)
+  const uint64_t blk0 = (uint64_t)col * nbp + (pcol >> 4);
+  uint8_t* cp = codes + (int64_t)col * ldc + (pcol >> 1);
+  uint8_t* sp = scales + (int64_t)col * lds + (pcol >> 4);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const uint32_t gc = col + c;
     float v[16];
     column(q, c, v);
     if constexpr (RHT) {
-      signed_fwht16(v, mask);
+      fwht16(v);
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const uint32_t p = pack_bf16(v[i] * 0.25f, v[i + 1] * 0.25f);
@@ -278,15 +298,15 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
     for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
     uint2 out;
     if constexpr (SR) {
-      const U4 w = block_random((uint64_t)gc * nbp + (pcol >> 4), 1, seed, offset);
+      const U4 w = block_random(blk0 + (uint64_t)c * nbp, 1, seed, offset);
       out.x = sr_pack8(v, w.x, w.y);
       out.y = sr_pack8(v + 8, w.z, w.w);
     } else {
       out.x = rtne_pack8(v);
       out.y = rtne_pack8(v + 8);
     }
-    *reinterpret_cast<uint2*>(codes + (int64_t)gc * ldc + (pcol >> 1)) = out;
-    scales[(int64_t)gc * lds + (pcol >> 4)] = (uint8_t)sc;
+    *reinterpret_cast<uint2*>(cp + (int64_t)c * ldc) = out;
+    sp[(int64_t)c * lds] = (uint8_t)sc;
   }
 }
 

@@ -216,6 +216,17 @@ def test_rmsnorm_rows_past_row_scale_slots(gpu_lib):
     _check_rms(w, got)
 
 
+def test_rmsnorm_prefill_given_amax(gpu_lib):
+    """Prefill size with a precomputed amax: the single-pass encode."""
+    import torch
+
+    w = workloads.prefill(seed=7)
+    q = oracle.rmsnorm_quantize(w.x, w.gamma, None, 0.0, w.eps)
+    a = torch.tensor([q["amax"]], dtype=torch.float32, device="cuda")
+    got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), eps=w.eps, amax=a, y_out=True)
+    _check_rms(w, got, amax_given=np.float32(q["amax"]))
+
+
 def test_rmsnorm_given_amax_and_y_only(gpu_lib):
     import torch
 
