@@ -205,10 +205,12 @@ nvfp4q_status nvfp4q_quantize_2d(const void *x, nvfp4q_dtype dtype, int64_t rows
  *     possible padded length). Plane columns at and past Poff[G] are never
  *     written [PR, Grouped allocation tail].
  *   SR: tag 1, block index = plane_row * (Poff[G] / 16) + plane_col / 16.
- *   Without amax_in the amax pass keeps one partial per 128-row x 256-column
- *   tile slot; shapes needing more slots than the workspace holds
- *   (((total_rows + 15 G) / 128 + G) * cols / 256 > 262112) return
+ *   Without amax_in the amax pass keeps one partial per 16-row block x
+ *   256-column tile; shapes needing more slots than the workspace holds
+ *   (floor((total_rows + 15 G) / 16) * ceil(cols / 256) > 262112) return
  *   NVFP4Q_E_UNSUPPORTED.
+ *   ld_x above 2^24 returns NVFP4Q_E_SHAPE (the kernels address 32 rows of x
+ *   with 32-bit byte offsets).
  *   [PR, Optimization 2, 3, 5; Fast math (bf16 round-through of the
  *    transform); Config surface and AUTO (64 groups, device offsets)]
  */

@@ -214,6 +214,7 @@ nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_ro
   if (num_groups < 1 || num_groups > 64) return NVFP4Q_E_SHAPE;
   if (apply_rht != 0 && apply_rht != 1) return NVFP4Q_E_UNSUPPORTED;
   if (rht_sign_mask > 0xFFFFu) return NVFP4Q_E_UNSUPPORTED;
+  if (ld_x > kGroupedMaxLd) return NVFP4Q_E_SHAPE;
   const int64_t cap = total_rows + 15 * (int64_t)num_groups;
   TRY(check_plane(col, cols, 0));
   if (col->ld_codes * 2 < cap || col->ld_scales * 16 < cap) return NVFP4Q_E_SHAPE;

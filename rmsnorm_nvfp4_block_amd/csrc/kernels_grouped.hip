@@ -3,20 +3,25 @@
 //
 // Work unit: the padded token axis of all groups together is a sequence of
 // 16-token blocks (group g occupies blocks Poff_g/16 .. Poff_{g+1}/16 - 1).
-// A workgroup takes 8 consecutive blocks of that sequence and 256 columns;
-// half-wave h of wave w takes block 2w + h, and lane l of the half takes
-// columns 8l .. 8l+7 (16-byte loads of each of the block's 16 tokens), so the
-// transform and the block amax of a column are in-lane and 32 lanes read 512
-// contiguous bytes of a token row. Blocks run on across group boundaries, so
-// no lane idles at a group's ragged end (with 128-token tiles inside each
-// group, 18% of the lanes of the 16384 x 7168, 64-group workload idled); each
-// half-wave finds its group by a ballot over the groups' block ranges, held
-// one group per lane.
+// A work item, one per wave, is a pair of consecutive blocks and a tile of
+// 32 CPL columns: half-wave h takes block 2p + h of pair p, and lane l of the
+// half takes columns CPL l .. CPL l + CPL - 1 (one 2 CPL-byte load per token
+// row), so the transform and the block amax of a column are in-lane and 32
+// lanes read 64 CPL contiguous bytes of a token row. Blocks run on across
+// group boundaries, so no lane idles at a group's ragged end; each half-wave
+// finds its group by a ballot over the groups' block ranges, held one group
+// per lane. The work is arithmetic-heavy (the transform, the block scales,
+// one Philox draw per block): small per-lane tiles keep the register count
+// low, so that many waves per SIMD hide the load latency.
+//
+// Loads go through a buffer resource whose range ends with x; rows of a block
+// past its group's end, and lanes without data, take an offset past the range
+// and read zero without touching memory.
 //
 // Amax: the amax pass writes one partial maximum per (block, column tile);
-// the encode pass reduces, for each group its wave touches, the partials of
-// the group's blocks (contiguous slots). Per-group encode reciprocal tables
-// live in LDS, two per wave.
+// the encode pass reduces, for each of its two groups, the partials of the
+// group's blocks (contiguous slots). Per-group encode reciprocal tables live
+// in LDS, two per wave, written and read by that wave only.
 //
 // "[nvfp4_training] Optimize CuteDSL kernels for NVFP4 training": Grouped
 // allocation tail (stop at the last padded row, leave the tail untouched);
@@ -31,8 +36,14 @@ namespace nvfp4q {
 namespace {
 
 constexpr int kT = 256;
-constexpr int kTileCol = 256;      // columns per workgroup (32 lanes x 8)
-constexpr int kBlocksPerWG = 8;    // token blocks per workgroup (2 per wave)
+constexpr int kWaves = kT / 64;
+
+// Buffer loads: byte offsets at or past kOutOfRange are never in range.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Workspace slots of the per-group amax written by the reduce kernel (after
+// the amax pass's partials).
+constexpr int kGroupAmax = kPartials - 64;
 
 // Per-group layout, one group per lane of a wave (lanes >= groups hold empty
 // groups): first row in x, real and padded length, and the inclusive prefix
@@ -68,14 +79,15 @@ struct Blk16 {
   int start;      // first padded token of the group (its first plane column)
   int n;          // real tokens of the group
   int row0;       // first row of the group in x
-  bool valid;     // block inside the padded length of all groups, column inside cols
+  bool valid;     // block inside the padded length of all groups
 };
 
 // The group holding padded token block tb (wave-uniform: every lane's test
-// enters the ballot): the last group whose first padded token is <= 16 tb. Empty groups share their start with the next group, so
-// counting every group that starts at or before the block gives it.
-__device__ __forceinline__ Blk16 locate(const GroupScan& q, int groups, uint32_t tb, uint32_t mpad, uint32_t col,
-                                        uint32_t cols) {
+// enters the ballot): the last group whose first padded token is <= 16 tb.
+// Empty groups share their start with the next group, so counting every
+// group that starts at or before the block gives it. A valid block holds at
+// least one real token of its group.
+__device__ __forceinline__ Blk16 locate(const GroupScan& q, int groups, uint32_t tb, uint32_t mpad) {
   const int lane = threadIdx.x & 63;
   const uint64_t bal = __ballot(lane < groups && (uint32_t)(q.ps - q.p) <= tb * 16u);
   const int g = (int)__popcll(bal) - 1;
@@ -85,51 +97,107 @@ __device__ __forceinline__ Blk16 locate(const GroupScan& q, int groups, uint32_t
   b.start = lane_int(q.ps - q.p, gs);
   b.n = lane_int(q.n, gs);
   b.row0 = lane_int(q.lo, gs);
-  b.valid = tb * 16u < mpad && col < cols && g >= 0;
+  b.valid = tb * 16u < mpad && g >= 0;
   return b;
 }
 
-// The lane's 16 tokens x 8 columns (zero for padding tokens). A block with all
-// 16 tokens inside its group (every block but a group's last) takes
-// unconditional loads from one base address with a scalar row stride.
-__device__ __forceinline__ void load_block(const uint16_t* __restrict__ x, int64_t ld_x, const Blk16& b, uint32_t tb,
-                                           uint32_t col, uint4 q[16]) {
-  const int t0 = (int)(tb * 16u) - b.start;  // token of the block's first row within its group
-  if (b.valid && t0 + 16 <= b.n) {
-    const uint16_t* p = x + (int64_t)(b.row0 + t0) * ld_x + col;
+// A buffer resource over x from row `row` to the end of x (record count
+// capped below kOutOfRange).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_from_row(const uint16_t* x, int64_t ld_x, int rows, int row) {
+  int64_t left = ((int64_t)rows - row) * ld_x * 2;
+  left = left < 0 ? 0 : left > (int64_t)(kOutOfRange - 16) ? (int64_t)(kOutOfRange - 16) : left;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)row * ld_x), (short)0, (int)left, 0x00020000);
+}
+
+// Work items: a workgroup takes 4 consecutive block pairs (wave w: pair
+// 4 quad + w; half-wave h: block 2 pair + h) and one column tile of 32 CPL
+// columns, so it writes 64 contiguous bytes of every plane row of its tile;
+// block quads are the fast index, and workgroups are ordered XCD by XCD
+// (xcd_work_item), so neighbouring quads, which fill the rest of those plane
+// lines, run on the same L2.
+struct Item {
+  uint32_t ctile;   // column tile
+  uint32_t tb0;     // the pair's first block (half 0); tb0 + 1 is half 1's
+  Blk16 b0, b1;     // the two blocks' groups
+  uint32_t tb;      // this lane's block
+  uint32_t col;     // this lane's first column
+  bool ok;          // this lane's block and columns hold data
+};
+// Workgroup item v (< nq * ntc), nq block quads: column tile and the wave's
+// block pair (wave-uniform; may be past the last pair).
+__device__ __forceinline__ void wg_item(uint32_t v, uint32_t nq, uint32_t& ctile, uint32_t& pair) {
+  ctile = v / nq;
+  pair = (v - ctile * nq) * kWaves + (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+template <int CPL>
+__device__ __forceinline__ Item item_of(uint32_t ctile, uint32_t pair, const GroupScan& q, int groups, uint32_t mpad,
+                                        uint32_t cols) {
+  Item it;
+  const uint32_t lane = threadIdx.x & 63;
+  it.ctile = ctile;
+  it.tb0 = 2 * pair;
+  it.b0 = locate(q, groups, it.tb0, mpad);
+  it.b1 = locate(q, groups, it.tb0 + 1, mpad);
+  it.tb = it.tb0 + (lane >> 5);
+  it.col = it.ctile * (32 * CPL) + (lane & 31) * CPL;
+  it.ok = ((lane >> 5) ? it.b1.valid : it.b0.valid) && it.col < cols;
+  return it;
+}
+
+// The lane's 16 tokens x CPL columns as bf16 pairs: r[i][j] holds columns
+// 2j, 2j + 1 of token row i.
+template <int CPL>
+using Tile = uint32_t[16][CPL / 2];
+
+// Issues the item's loads: one resource based at the first block's first row,
+// row offsets in the per-lane offset (so the range check covers them).
+template <int CPL>
+__device__ __forceinline__ void load_item(const uint16_t* __restrict__ x, int64_t ld_x, int rows, const Item& it,
+                                          Tile<CPL>& r) {
+  const bool h = (threadIdx.x >> 5) & 1;
+  // first row in x of each block: its group's row0 plus the block's first
+  // token within the group
+  const int t0a = (int)(it.tb0 * 16u) - it.b0.start, t0b = (int)((it.tb0 + 1) * 16u) - it.b1.start;
+  const int ra = it.b0.valid ? it.b0.row0 + t0a : 0;
+  const int rb = it.b1.row0 + t0b;
+  const __amdgpu_buffer_rsrc_t rs = x_from_row(x, ld_x, rows, ra);
+  const uint32_t ldb = (uint32_t)ld_x * 2u;
+  const int left = it.ok ? (h ? it.b1.n - t0b : it.b0.n - t0a) : 0;  // real tokens of the lane's block
+  const uint32_t v0 = (uint32_t)(h ? rb - ra : 0) * ldb + it.col * 2u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = *reinterpret_cast<const uint4*>(p + i * ld_x);
-  } else {
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t off = i < left ? v0 + (uint32_t)i * ldb : kOutOfRange;
+    if constexpr (CPL == 8) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const bool ok = b.valid && t0 + i < b.n;
-      q[i] = ld16(x + (int64_t)(b.row0 + t0 + i) * ld_x + col, ok);
+      for (int j = 0; j < 4; ++j) r[i][j] = t[j];
+    } else {
+      static_assert(CPL == 4, "4 or 8 columns per lane");
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+      r[i][0] = t[0];
+      r[i][1] = t[1];
     }
   }
 }
 
-// Column c (0..7) of the lane's 16 x 8 block as fp32.
-__device__ __forceinline__ void column(const uint4 q[16], int c, float v[16]) {
+// Column c of the lane's tile as fp32.
+template <int CPL>
+__device__ __forceinline__ void column(const Tile<CPL>& r, int c, float v[16]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t w = (c >> 1) == 0 ? q[i].x : (c >> 1) == 1 ? q[i].y : (c >> 1) == 2 ? q[i].z : q[i].w;
-    v[i] = (c & 1) ? bf_hi(w) : bf_lo(w);
-  }
+  for (int i = 0; i < 16; ++i) v[i] = (c & 1) ? bf_hi(r[i][c >> 1]) : bf_lo(r[i][c >> 1]);
 }
 
-// D: flips the sign of token row i of the lane's block where bit i of the
-// mask is set. Row i's 16 bytes hold 8 bf16 columns, so one XOR with
-// 0x80008000 per word flips all 8 (the bf16 sign bit becomes the fp32 sign
-// bit when the value is widened). The mask is wave-uniform, so the per-row
-// constants are scalar.
-__device__ __forceinline__ void apply_signs(uint4 q[16], uint32_t mask) {
+// D: flips the sign of token row i of the lane's tile where bit i of the mask
+// is set: one XOR with 0x80008000 per bf16 pair (the bf16 sign bit becomes
+// the fp32 sign bit when the value is widened). The mask is wave-uniform, so
+// the per-row constants are scalar.
+template <int CPL>
+__device__ __forceinline__ void apply_signs(Tile<CPL>& r, uint32_t mask) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t f = ((mask >> i) & 1u) ? 0x80008000u : 0u;
-    q[i].x ^= f;
-    q[i].y ^= f;
-    q[i].z ^= f;
-    q[i].w ^= f;
+#pragma unroll
+    for (int j = 0; j < CPL / 2; ++j) r[i][j] ^= f;
   }
 }
 
@@ -156,159 +224,126 @@ __device__ __forceinline__ float half_wave_max(float m) {
   return m;
 }
 
-// Geometry of one workgroup's work item (column tile, 8 blocks).
-struct Work {
-  uint32_t ctile;   // column tile
-  uint32_t tb0;     // the wave's first block (half 0); tb0 + 1 is half 1's
-  uint32_t tb;      // this lane's block
-  uint32_t col;     // this lane's first column
-};
-__device__ __forceinline__ Work work_of(uint32_t item, uint32_t nwb) {
-  Work w;
-  const uint32_t lane = threadIdx.x & 63;
-  const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  w.ctile = item / nwb;
-  w.tb0 = (item - w.ctile * nwb) * kBlocksPerWG + 2 * wid;
-  w.tb = w.tb0 + (lane >> 5);
-  w.col = w.ctile * kTileCol + (lane & 31) * 8;
-  return w;
-}
-
-// Pass 1: per-(block, column tile) maximum of the (transformed, bf16-rounded)
-// columnwise values, into partial[tb * ntc + ctile].
-template <bool RHT>
+// Pass 1: per-(block, column tile) maximum of the (transformed,
+// bf16-rounded) columnwise values, into partial[tb * ntc + ctile].
+template <int CPL, bool RHT>
 __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict__ x, int rows, uint32_t cols,
                                                      int64_t ld_x, const int32_t* __restrict__ offsets, int groups,
-                                                     uint32_t mask, Workspace* ws, uint32_t nwb, uint32_t ntiles,
-                                                     uint32_t nb_max, uint32_t chunk) {
-  const uint32_t item = xcd_work_item(chunk);
-  if (item >= ntiles) return;
-  const Work wk = work_of(item, nwb);
-  const uint32_t ntc = ntiles / nwb;
+                                                     uint32_t mask, Workspace* ws, uint32_t nq, uint32_t ntc,
+                                                     uint32_t npairs, uint32_t nb_max, uint32_t chunk) {
+  const uint32_t v = xcd_work_item(chunk);
+  if (v >= nq * ntc) return;
+  uint32_t ctile, pair;
+  wg_item(v, nq, ctile, pair);
+  if (pair >= npairs) return;
   const GroupScan q = group_scan(offsets, groups, rows);
   const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
-  // locate takes a wave-uniform block: the ballot reads every lane's test
-  const Blk16 b0 = locate(q, groups, wk.tb0, mpad, wk.col, cols);
-  const Blk16 b1 = locate(q, groups, wk.tb0 + 1, mpad, wk.col, cols);
-  const Blk16 b = (threadIdx.x & 32) ? b1 : b0;
+  const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
+  Tile<CPL> r;
+  load_item<CPL>(x, ld_x, rows, it, r);
+  if constexpr (RHT) apply_signs<CPL>(r, mask);
   float m = 0.0f;
-  if (b.valid) {
-    uint4 v16[16];
-    load_block(x, ld_x, b, wk.tb, wk.col, v16);
-    if constexpr (RHT) apply_signs(v16, mask);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float v[16];
-      column(v16, c, v);
-      if constexpr (RHT) fwht16(v);
-      m = fmaxf(m, fmaxf(max8_abs(v), max8_abs(v + 8)));
-    }
-    // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
-    // round-to-nearest-even are both monotone.
-    if constexpr (RHT) m = bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
+  for (int c = 0; c < CPL; ++c) {
+    float v[16];
+    column<CPL>(r, c, v);
+    if constexpr (RHT) fwht16(v);
+    m = fmaxf(m, fmaxf(max8_abs(v), max8_abs(v + 8)));
   }
-  m = half_wave_max(m);
-  if ((threadIdx.x & 31) == 0 && wk.tb < nb_max) ws->partial[wk.tb * ntc + wk.ctile] = m;
+  // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
+  // round-to-nearest-even are both monotone.
+  if constexpr (RHT) m = bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
+  m = half_wave_max(m);  // lanes without data hold zeros
+  if ((threadIdx.x & 31) == 0 && it.tb < nb_max) ws->partial[it.tb * ntc + it.ctile] = m;
 }
 
-// Amax of group g (wave-uniform): the partials of its blocks over every
-// column tile (contiguous slots), reduced by the whole wave, four loads in
-// flight per lane. Slots stop at lim, the slots the amax pass writes (only
-// malformed offsets can reach past it).
-__device__ __forceinline__ float group_amax(const Workspace* ws, const GroupScan& q, int g, uint32_t ntc,
-                                            uint32_t lim) {
-  const uint32_t lane = threadIdx.x & 63;
+// Between the passes, one workgroup per group: the maximum of the partials of
+// the group's blocks over every column tile (contiguous slots, clamped to the
+// lim slots the amax pass writes), into the workspace for the encode pass and
+// into amax_out / scale_out. Empty groups get 0.
+constexpr int kReduceThreads = 512;
+__global__ __launch_bounds__(kReduceThreads) void k_grouped_reduce(const int32_t* __restrict__ offsets, int groups,
+                                                                   int rows, Workspace* ws, uint32_t ntc,
+                                                                   uint32_t lim, float* amax_out, float* scale_out) {
+  const int g = blockIdx.x;
+  const GroupScan q = group_scan(offsets, groups, rows);
   const uint32_t lo = min(((uint32_t)lane_int(q.ps - q.p, g) >> 4) * ntc, lim);
   const uint32_t n = min(((uint32_t)lane_int(q.p, g) >> 4) * ntc, lim - lo);
+  const float* src = ws->partial + lo;
   float m = 0.0f;
-  for (uint32_t i = lane; i < n; i += 256) {
+  for (uint32_t i = threadIdx.x; i < n; i += 4 * kReduceThreads) {
     float t[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) t[u] = i + 64 * u < n ? ws->partial[lo + i + 64 * u] : 0.0f;
+    for (int u = 0; u < 4; ++u) t[u] = i + u * kReduceThreads < n ? src[i + u * kReduceThreads] : 0.0f;
     m = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
   }
-  return wave_max(m);
+  m = wg_max<kReduceThreads / 64>(m);
+  if (threadIdx.x == 0) {
+    ws->partial[kGroupAmax + g] = m;
+    if (amax_out) amax_out[g] = m;
+    if (scale_out) scale_out[g] = global_scale(m).dec;
+  }
 }
 
 // Pass 2: transform (optional), bf16 round-through, per-block scale and codes.
-template <bool RHT, bool SR>
+// The group amax comes from amax_in, else from the reduce kernel.
+template <int CPL, bool RHT, bool SR>
 __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict__ x, int rows, uint32_t cols,
                                                       int64_t ld_x, const int32_t* __restrict__ offsets, int groups,
                                                       uint32_t mask, uint8_t* __restrict__ codes, int64_t ldc,
                                                       uint8_t* __restrict__ scales, int64_t lds,
                                                       const Workspace* ws, const float* amax_in, float* amax_out,
                                                       float* scale_out, int32_t* poff_out, uint64_t seed,
-                                                      uint32_t offset, int64_t cap, uint32_t nwb, uint32_t ntiles,
-                                                      uint32_t nb_max, uint32_t chunk) {
-  __shared__ float rcp_tab[kT / 64][2][128];  // per wave: the tables of its two blocks' groups
-  const uint32_t item = xcd_work_item(chunk);
-  if (item >= ntiles) return;
-  const Work wk = work_of(item, nwb);
-  const uint32_t ntc = ntiles / nwb;
+                                                      uint32_t offset, int64_t cap, uint32_t nq, uint32_t ntc,
+                                                      uint32_t npairs, uint32_t chunk) {
+  __shared__ float rcp_tab[kWaves][2][128];  // per wave: the tables of its two blocks' groups
   const uint32_t lane = threadIdx.x & 63;
-  const uint32_t wid = threadIdx.x >> 6, half = lane >> 5;
+  const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t half = lane >> 5;
+  const uint32_t v = xcd_work_item(chunk);
+  if (v >= nq * ntc) return;
+  uint32_t ctile, pair;
+  wg_item(v, nq, ctile, pair);
+  if (pair >= npairs) return;
   const GroupScan q = group_scan(offsets, groups, rows);
-  const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
-  // Workgroup 0, wave 0: padded offsets, and amax / S_dec of the groups no
-  // encode wave reports (all of them with amax_in, else the empty ones).
-  if (item == 0 && wid == 0 && lane < (uint32_t)groups) {
-    if (amax_in != nullptr || q.p == 0) {
-      const float a = amax_in ? amax_in[lane] : 0.0f;
-      if (amax_out) amax_out[lane] = a;
-      if (scale_out) scale_out[lane] = global_scale(a).dec;
+  // The first wave: padded offsets, and with amax_in the groups' amax / S_dec
+  // (otherwise the reduce kernel wrote them).
+  if (v == 0 && wid == 0 && lane < (uint32_t)groups) {
+    if (amax_in != nullptr) {
+      if (amax_out) amax_out[lane] = amax_in[lane];
+      if (scale_out) scale_out[lane] = global_scale(amax_in[lane]).dec;
     }
     if (poff_out) poff_out[lane + 1] = q.ps;
     if (lane == 0 && poff_out) poff_out[0] = 0;
   }
-  // The wave's two blocks and their groups (wave-uniform).
-  const Blk16 b0 = locate(q, groups, wk.tb0, mpad, wk.col, cols);
-  const Blk16 b1 = locate(q, groups, wk.tb0 + 1, mpad, wk.col, cols);
-  const Blk16 b = half ? b1 : b0;
-  uint4 v16[16];
-  load_block(x, ld_x, b, wk.tb, wk.col, v16);
-  float a0, a1;
-  if (amax_in) {
-    a0 = amax_in[b0.g];
-    a1 = amax_in[b1.g];
-  } else {
-    a0 = group_amax(ws, q, b0.g, ntc, nb_max * ntc);
-    a1 = b1.g == b0.g ? a0 : group_amax(ws, q, b1.g, ntc, nb_max * ntc);
-  }
-  const GScale g0 = global_scale(a0), g1 = global_scale(a1);
-  // The wave whose half holds a nonempty group's first block, in column tile
-  // 0, reports that group's amax and S_dec.
-  if (!amax_in && wk.ctile == 0 && lane == 0) {
-    if (b0.valid && wk.tb0 * 16u == (uint32_t)b0.start) {
-      if (amax_out) amax_out[b0.g] = a0;
-      if (scale_out) scale_out[b0.g] = g0.dec;
-    }
-    if (b1.valid && (wk.tb0 + 1) * 16u == (uint32_t)b1.start) {
-      if (amax_out) amax_out[b1.g] = a1;
-      if (scale_out) scale_out[b1.g] = g1.dec;
-    }
-  }
-  rcp_tab[wid][0][lane] = encode_mult(lane, g0.dec);
-  rcp_tab[wid][0][lane + 64] = encode_mult(lane + 64, g0.dec);
-  rcp_tab[wid][1][lane] = encode_mult(lane, g1.dec);
-  rcp_tab[wid][1][lane + 64] = encode_mult(lane + 64, g1.dec);
-  __syncthreads();
-  if (!b.valid) return;
-  const float* tab = rcp_tab[wid][half];
-  const float enc = half ? g1.enc : g0.enc;
-  const uint32_t pcol = wk.tb * 16u;                     // plane column of the block's first token
+  const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
+  const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
+  Tile<CPL> r;
+  load_item<CPL>(x, ld_x, rows, it, r);
+  const float* gam = amax_in ? amax_in : ws->partial + kGroupAmax;
+  const GScale g0 = global_scale(gam[it.b0.g]), g1 = global_scale(gam[it.b1.g]);
+  // the wave's own tables: its LDS writes precede its reads, no barrier
+  float* tabs = &rcp_tab[wid][0][0];
+  tabs[lane] = encode_mult(lane, g0.dec);
+  tabs[lane + 64] = encode_mult(lane + 64, g0.dec);
+  tabs[128 + lane] = encode_mult(lane, g1.dec);
+  tabs[128 + lane + 64] = encode_mult(lane + 64, g1.dec);
+  const uint32_t pcol = it.tb * 16u;  // plane column of the block's first token
   // Plane capacity guard: only malformed offsets can reach it.
-  if ((int64_t)pcol + 16 > cap) return;
-  if constexpr (RHT) apply_signs(v16, mask);
-  const uint64_t nbp = (uint64_t)(mpad >> 4);            // blocks per plane row
+  if (!it.ok || (int64_t)pcol + 16 > cap) return;
+  if constexpr (RHT) apply_signs<CPL>(r, mask);
+  const float* tab = tabs + half * 128;
+  const float enc = half ? g1.enc : g0.enc;
+  const uint64_t nbp = (uint64_t)(mpad >> 4);  // blocks per plane row
   // block index and addresses of column `col` once; the lane's next columns
   // differ by uniform strides (64-bit products cost several cycles)
-  const uint64_t blk0 = (uint64_t)wk.col * nbp + (pcol >> 4);
-  uint8_t* cp = codes + (int64_t)wk.col * ldc + (pcol >> 1);
-  uint8_t* sp = scales + (int64_t)wk.col * lds + (pcol >> 4);
+  const uint64_t blk0 = (uint64_t)it.col * nbp + (pcol >> 4);
+  uint8_t* cp = codes + (int64_t)it.col * ldc + (pcol >> 1);
+  uint8_t* sp = scales + (int64_t)it.col * lds + (pcol >> 4);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < CPL; ++c) {
     float v[16];
-    column(v16, c, v);
+    column<CPL>(r, c, v);
     if constexpr (RHT) {
       fwht16(v);
 #pragma unroll
@@ -325,9 +360,9 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
     for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
     uint2 out;
     if constexpr (SR) {
-      const U4 w = block_random(blk0 + (uint64_t)c * nbp, 1, seed, offset);
-      out.x = sr_pack8(v, w.x, w.y);
-      out.y = sr_pack8(v + 8, w.z, w.w);
+      const U4 wr = block_random(blk0 + (uint64_t)c * nbp, 1, seed, offset);
+      out.x = sr_pack8(v, wr.x, wr.y);
+      out.y = sr_pack8(v + 8, wr.z, wr.w);
     } else {
       out.x = rtne_pack8(v);
       out.y = rtne_pack8(v + 8);
@@ -341,34 +376,78 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
 // sum ceil(n_g / 16) <= (rows + 15 G) / 16.
 int64_t grouped_blocks(int64_t rows, int groups) { return (rows + 15 * (int64_t)groups) / 16; }
 
+// Columns per lane of the two passes (4 or 8 each), from NVFP4Q_GROUPED_CPL
+// ("48": amax pass 4, encode pass 8).
+int grouped_cpl(int pass) {
+  static const char* e = getenv("NVFP4Q_GROUPED_CPL");
+  if (e && e[0] && e[1]) return e[pass] == '8' ? 8 : 4;
+  return pass == 0 ? 4 : 8;
+}
+
+template <int CPL>
+uint32_t tiles_of(int64_t cols) { return (uint32_t)((cols + 32 * CPL - 1) / (32 * CPL)); }
+
+// Launch geometry of a pass: block pairs, block quads (one per workgroup and
+// column tile), column tiles, and the XCD chunk.
+struct Geo {
+  uint32_t npairs, nq, ntc, chunk;
+  dim3 grid;
+};
+template <int CPL>
+Geo geo_of(int64_t cols, uint32_t nb_max) {
+  Geo g;
+  g.npairs = (nb_max + 1) / 2 < 1 ? 1 : (nb_max + 1) / 2;
+  g.nq = (g.npairs + kWaves - 1) / kWaves;
+  g.ntc = tiles_of<CPL>(cols);
+  g.chunk = xcd_chunk((uint64_t)g.nq * g.ntc);
+  g.grid = dim3(xcd_grid((uint64_t)g.nq * g.ntc));
+  return g;
+}
+
+template <int CPLA, bool RHT>
+void launch_amax(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
+  const Geo g = geo_of<CPLA>(a.cols, nb_max);
+  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT>), g.grid, dim3(kT), 0, s, (const uint16_t*)a.x, (int)a.rows,
+                     (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.ws, g.nq, g.ntc, g.npairs, nb_max,
+                     g.chunk);
+  hipLaunchKernelGGL(k_grouped_reduce, dim3(a.groups), dim3(kReduceThreads), 0, s, a.offsets, a.groups, (int)a.rows,
+                     a.ws, g.ntc, nb_max * g.ntc, a.amax_out, a.scale_out);
+}
+
+template <int CPLE, bool RHT, bool SR>
+void launch_quant(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
+  const int64_t cap = a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16;
+  const Geo g = geo_of<CPLE>(a.cols, nb_max);
+  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR>), g.grid, dim3(kT), 0, s, (const uint16_t*)a.x, (int)a.rows,
+                     (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws,
+                     a.amax_in, a.amax_out, a.scale_out, a.poff_out, a.seed, a.offset, cap, g.nq, g.ntc, g.npairs,
+                     g.chunk);
+}
+
 template <bool RHT>
 void launch_grouped_r(const GroupArgs& a, hipStream_t s) {
-  const uint16_t* x = (const uint16_t*)a.x;
-  const int64_t cap = a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16;
   const uint32_t nb_max = (uint32_t)grouped_blocks(a.rows, a.groups);
-  const uint32_t nwb = (nb_max + kBlocksPerWG - 1) / kBlocksPerWG < 1 ? 1 : (nb_max + kBlocksPerWG - 1) / kBlocksPerWG;
-  const uint32_t ntc = (uint32_t)((a.cols + kTileCol - 1) / kTileCol);
-  const uint32_t ntiles = nwb * ntc;  // work items: column tile major, blocks contiguous per XCD
-  const uint32_t chunk = xcd_chunk(ntiles);
-  const dim3 grid(xcd_grid(ntiles));
-  if (!a.amax_in)
-    hipLaunchKernelGGL((k_grouped_amax<RHT>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x,
-                       a.offsets, a.groups, a.mask, a.ws, nwb, ntiles, nb_max, chunk);
-  if (a.sr)
-    hipLaunchKernelGGL((k_grouped_quant<RHT, true>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols, a.ld_x,
-                       a.offsets, a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in, a.amax_out,
-                       a.scale_out, a.poff_out, a.seed, a.offset, cap, nwb, ntiles, nb_max, chunk);
-  else
-    hipLaunchKernelGGL((k_grouped_quant<RHT, false>), grid, dim3(kT), 0, s, x, (int)a.rows, (uint32_t)a.cols,
-                       a.ld_x, a.offsets, a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in,
-                       a.amax_out, a.scale_out, a.poff_out, a.seed, a.offset, cap, nwb, ntiles, nb_max, chunk);
+  if (!a.amax_in) {
+    if (grouped_cpl(0) == 8) launch_amax<8, RHT>(a, nb_max, s);
+    else launch_amax<4, RHT>(a, nb_max, s);
+  }
+  const bool e8 = grouped_cpl(1) == 8;
+  if (a.sr) {
+    if (e8) launch_quant<8, RHT, true>(a, nb_max, s);
+    else launch_quant<4, RHT, true>(a, nb_max, s);
+  } else {
+    if (e8) launch_quant<8, RHT, false>(a, nb_max, s);
+    else launch_quant<4, RHT, false>(a, nb_max, s);
+  }
 }
 
 }  // namespace
 
-// Partial slots of the amax pass: one per (padded token block, column tile).
+// Workspace slots the grouped path needs: the amax pass's partials, one per
+// (padded token block, column tile) at the narrowest tile (128 columns), and
+// the per-group amax after them.
 int64_t grouped_partials(int64_t rows, int64_t cols, int groups) {
-  return grouped_blocks(rows, groups) * ((cols + kTileCol - 1) / kTileCol);
+  return grouped_blocks(rows, groups) * tiles_of<4>(cols) + 64;
 }
 
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {

@@ -50,6 +50,10 @@ struct TwoDArgs {
   uint32_t offset;
 };
 
+// Largest row stride (elements) of the grouped path's input: its loads reach
+// 32 rows past a base row with 32-bit byte offsets.
+constexpr int64_t kGroupedMaxLd = (int64_t)1 << 24;
+
 // Arguments of the grouped columnwise path.
 struct GroupArgs {
   const void* x;

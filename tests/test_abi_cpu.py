@@ -127,9 +127,9 @@ def test_2d_and_grouped_validation(lib):
     assert lib.nvfp4q_quantize_2d(FAKE, 0, 32, 32, 32, ctypes.byref(g), ctypes.byref(none), ctypes.byref(none), 0,
                                   ctypes.byref(r), FAKE, 1 << 16, None) == 1
 
-    def grouped(groups=4, rht=1, mask=0x1234, ldc=64, lds=8, offs=FAKE, rows=64):
+    def grouped(groups=4, rht=1, mask=0x1234, ldc=64, lds=8, offs=FAKE, rows=64, ld=32):
         p = q.Plane(FAKE, ldc, FAKE, lds)
-        return lib.nvfp4q_grouped(FAKE, 0, rows, 32, 32, offs, groups, None, rht, mask, ctypes.byref(g),
+        return lib.nvfp4q_grouped(FAKE, 0, rows, 32, ld, offs, groups, None, rht, mask, ctypes.byref(g),
                                   ctypes.byref(p), 1, ctypes.byref(r), FAKE, 1 << 16, None)
 
     assert grouped(groups=0) == 2
@@ -139,3 +139,4 @@ def test_2d_and_grouped_validation(lib):
     assert grouped(offs=0) == 1
     assert grouped(ldc=48) == 2       # 2 * 48 < 64 + 15 * 4
     assert grouped(lds=7) == 2        # 16 * 7 < 124
+    assert grouped(ld=(1 << 24) + 8) == 2   # row stride past the 32-bit offsets of the loads
