@@ -3,25 +3,25 @@
 //
 // Work unit: the padded token axis of all groups together is a sequence of
 // 16-token blocks (group g occupies blocks Poff_g/16 .. Poff_{g+1}/16 - 1).
-// A work item, one per wave, is a pair of consecutive blocks and a tile of
-// 32 CPL columns: half-wave h takes block 2p + h of pair p, and lane l of the
-// half takes columns CPL l .. CPL l + CPL - 1 (one 2 CPL-byte load per token
-// row), so the transform and the block amax of a column are in-lane and 32
-// lanes read 64 CPL contiguous bytes of a token row. Blocks run on across
-// group boundaries, so no lane idles at a group's ragged end; each half-wave
-// finds its group by a ballot over the groups' block ranges, held one group
-// per lane. The work is arithmetic-heavy (the transform, the block scales,
-// one Philox draw per block): small per-lane tiles keep the register count
-// low, so that many waves per SIMD hide the load latency.
+// A wave takes a pair of consecutive blocks and a tile of 32 CPL columns:
+// half-wave h takes block 2p + h of pair p, and lane l of the half takes
+// columns CPL l .. CPL l + CPL - 1 (one 2 CPL-byte load per token row), so
+// the transform and the block amax of a column are in-lane and 32 lanes read
+// 64 CPL contiguous bytes of a token row. Blocks run on across group
+// boundaries, so no lane idles at a group's ragged end; each half-wave finds
+// its group by a ballot over the groups' block ranges, held one group per
+// lane.
 //
 // Loads go through a buffer resource whose range ends with x; rows of a block
 // past its group's end, and lanes without data, take an offset past the range
 // and read zero without touching memory.
 //
-// Amax: the amax pass writes one partial maximum per (block, column tile);
-// the encode pass reduces, for each of its two groups, the partials of the
-// group's blocks (contiguous slots). Per-group encode reciprocal tables live
-// in LDS, two per wave, written and read by that wave only.
+// Three kernels: the amax pass writes one partial maximum per (block, column
+// tile); a reduce kernel (one workgroup per group) takes each group's maximum
+// over its blocks' partials; the encode pass reads one amax per group, keeps
+// per-group encode reciprocal tables in LDS (two per wave, written and read by
+// that wave only), stages its codes and scales in LDS and writes them out in
+// coalesced pieces of the transposed planes.
 //
 // "[nvfp4_training] Optimize CuteDSL kernels for NVFP4 training": Grouped
 // allocation tail (stop at the last padded row, leave the tail untouched);
@@ -153,7 +153,7 @@ using Tile = uint32_t[16][CPL / 2];
 // row offsets in the per-lane offset (so the range check covers them).
 template <int CPL>
 __device__ __forceinline__ void load_item(const uint16_t* __restrict__ x, int64_t ld_x, int rows, const Item& it,
-                                          Tile<CPL>& r) {
+                                          bool live, Tile<CPL>& r) {
   const bool h = (threadIdx.x >> 5) & 1;
   // first row in x of each block: its group's row0 plus the block's first
   // token within the group
@@ -162,7 +162,9 @@ __device__ __forceinline__ void load_item(const uint16_t* __restrict__ x, int64_
   const int rb = it.b1.row0 + t0b;
   const __amdgpu_buffer_rsrc_t rs = x_from_row(x, ld_x, rows, ra);
   const uint32_t ldb = (uint32_t)ld_x * 2u;
-  const int left = it.ok ? (h ? it.b1.n - t0b : it.b0.n - t0a) : 0;  // real tokens of the lane's block
+  // real tokens of the lane's block (none for an item that is only a refill
+  // past the end of a run: its loads are issued but read nothing)
+  const int left = live && it.ok ? (h ? it.b1.n - t0b : it.b0.n - t0a) : 0;
   const uint32_t v0 = (uint32_t)(h ? rb - ra : 0) * ldb + it.col * 2u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
   const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
   const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
   Tile<CPL> r;
-  load_item<CPL>(x, ld_x, rows, it, r);
+  load_item<CPL>(x, ld_x, rows, it, true, r);
   if constexpr (RHT) apply_signs<CPL>(r, mask);
   float m = 0.0f;
 #pragma unroll
@@ -287,24 +289,134 @@ __global__ __launch_bounds__(kReduceThreads) void k_grouped_reduce(const int32_t
 
 // Pass 2: transform (optional), bf16 round-through, per-block scale and codes.
 // The group amax comes from amax_in, else from the reduce kernel.
+//
+// A work item is kItemBlocks consecutive blocks (wave w: pair
+// kQuantWaves bg + w) of one column tile. Its codes and scales are staged in
+// LDS and written out once the workgroup has encoded it: every plane row of
+// the tile then receives 8 kItemBlocks code bytes and kItemBlocks scale bytes
+// in single coalesced stores (written from the lanes that computed them, the
+// pieces were 8 bytes and 1 byte, 8.7 KB apart, and those stores alone cost as
+// much as the reads). Workgroups take items in XCD order (xcd_work_item), the
+// blocks fastest, so the workgroups that complete a plane line share an L2.
+// Measured on the 16384 x 7168, 64-group workload: four waves per workgroup
+// (8 blocks, 64-byte line halves) beat two and eight; persistent workgroups
+// that prefetch their next item were slower (the item barrier keeps the waves
+// in step, and the second register set halves the waves per SIMD).
+constexpr int kQuantWaves = 4;
+constexpr int kQuantThreads = 64 * kQuantWaves;
+constexpr int kItemBlocks = 2 * kQuantWaves;  // blocks of a work item
+// bytes per staged code row: 8 per block, plus 8 to spread the LDS banks
+constexpr int kStagePitch = 8 * kItemBlocks + 8;
+
+template <int CPL>
+struct Stage {
+  uint8_t codes[32 * CPL * kStagePitch];
+  uint8_t scales[32 * CPL * kItemBlocks];
+};
+
+// The group scales of a wave's current item and its LDS tables (recomputed
+// when the item's groups change).
+struct GroupTabs {
+  int g0, g1;
+  GScale s0, s1;
+};
+
 template <int CPL, bool RHT, bool SR>
-__global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict__ x, int rows, uint32_t cols,
-                                                      int64_t ld_x, const int32_t* __restrict__ offsets, int groups,
-                                                      uint32_t mask, uint8_t* __restrict__ codes, int64_t ldc,
-                                                      uint8_t* __restrict__ scales, int64_t lds,
-                                                      const Workspace* ws, const float* amax_in, float* amax_out,
-                                                      float* scale_out, int32_t* poff_out, uint64_t seed,
-                                                      uint32_t offset, int64_t cap, uint32_t nq, uint32_t ntc,
-                                                      uint32_t npairs, uint32_t chunk) {
-  __shared__ float rcp_tab[kWaves][2][128];  // per wave: the tables of its two blocks' groups
+__device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32_t mask, const float* gam,
+                                            GroupTabs& gt, float* tabs, Stage<CPL>& st, uint32_t mpad,
+                                            uint64_t seed, uint32_t offset) {
+  const uint32_t lane = threadIdx.x & 63, half = lane >> 5;
+  const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (it.b0.g != gt.g0 || it.b1.g != gt.g1) {
+    gt.g0 = it.b0.g;
+    gt.g1 = it.b1.g;
+    gt.s0 = global_scale(gam[gt.g0]);
+    gt.s1 = global_scale(gam[gt.g1]);
+    // the wave's own tables: its LDS writes precede its reads
+    tabs[lane] = encode_mult(lane, gt.s0.dec);
+    tabs[lane + 64] = encode_mult(lane + 64, gt.s0.dec);
+    tabs[128 + lane] = encode_mult(lane, gt.s1.dec);
+    tabs[128 + lane + 64] = encode_mult(lane + 64, gt.s1.dec);
+  }
+  if constexpr (RHT) apply_signs<CPL>(r, mask);
+  const float* tab = tabs + half * 128;
+  const float enc = half ? gt.s1.enc : gt.s0.enc;
+  const uint64_t nbp = (uint64_t)(mpad >> 4);  // blocks per plane row
+  uint64_t blk = (uint64_t)it.col * nbp + it.tb;
+  // staging slot of the lane's block: byte 8 j of code row r, byte j of
+  // scale row r, j = the block's place among the item's 16
+  const uint32_t j = 2 * wid + half;
+  uint8_t* cst = st.codes + (lane & 31) * CPL * kStagePitch + 8 * j;
+  uint8_t* sst = st.scales + (lane & 31) * CPL * kItemBlocks + j;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    float v16[16];
+    column<CPL>(r, c, v16);
+    if constexpr (RHT) {
+      fwht16(v16);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const uint32_t p = pack_bf16(v16[i] * 0.25f, v16[i + 1] * 0.25f);
+        v16[i] = bf_lo(p);
+        v16[i + 1] = bf_hi(p);
+      }
+    }
+    const float m = fmaxf(max8_abs(v16), max8_abs(v16 + 8));
+    const uint32_t sc = block_scale(m, enc);
+    const float rc = tab[sc];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v16[i] = v16[i] * rc;
+    uint2 out;
+    if constexpr (SR) {
+      const U4 wr = block_random(blk, 1, seed, offset);
+      out.x = sr_pack8(v16, wr.x, wr.y);
+      out.y = sr_pack8(v16 + 8, wr.z, wr.w);
+    } else {
+      out.x = rtne_pack8(v16);
+      out.y = rtne_pack8(v16 + 8);
+    }
+    *reinterpret_cast<uint2*>(cst + c * kStagePitch) = out;
+    sst[c * kItemBlocks] = (uint8_t)sc;
+    blk += nbp;
+  }
+}
+
+// Write-out of a staged item: plane rows of column tile ctile, blocks
+// kItemBlocks bg onwards; only blocks inside the padded length (and the plane
+// capacity, which only malformed offsets reach) and rows inside cols.
+template <int CPL>
+__device__ __forceinline__ void write_item(const Stage<CPL>& st, uint32_t ctile, uint32_t bg, uint32_t cols,
+                                           uint32_t mpad, int64_t cap, uint8_t* __restrict__ codes, int64_t ldc,
+                                           uint8_t* __restrict__ scales, int64_t lds) {
+  constexpr int kRows = 32 * CPL;
+  const uint32_t row0 = ctile * kRows, blkb = bg * kItemBlocks;
+  const int64_t nvalid = min((int64_t)(mpad >> 4), cap >> 4) - (int64_t)blkb;  // valid blocks of the item
+#pragma unroll
+  for (int k = 0; k < kRows * kItemBlocks / kQuantThreads; ++k) {
+    const uint32_t i = threadIdx.x + k * kQuantThreads;
+    const uint32_t rr = i / kItemBlocks, jj = i % kItemBlocks;
+    if (row0 + rr < cols && (int64_t)jj < nvalid) {
+      *reinterpret_cast<uint2*>(codes + (int64_t)(row0 + rr) * ldc + (int64_t)(blkb + jj) * 8) =
+          *reinterpret_cast<const uint2*>(st.codes + rr * kStagePitch + jj * 8);
+      scales[(int64_t)(row0 + rr) * lds + blkb + jj] = st.scales[rr * kItemBlocks + jj];
+    }
+  }
+}
+
+template <int CPL, bool RHT, bool SR>
+__global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(
+    const uint16_t* __restrict__ x, int rows, uint32_t cols, int64_t ld_x, const int32_t* __restrict__ offsets,
+    int groups, uint32_t mask, uint8_t* __restrict__ codes, int64_t ldc, uint8_t* __restrict__ scales, int64_t lds,
+    const Workspace* ws, const float* amax_in, float* amax_out, float* scale_out, int32_t* poff_out, uint64_t seed,
+    uint32_t offset, int64_t cap, uint32_t nbg, uint32_t ntc, uint32_t npairs, uint32_t chunk) {
+  __shared__ __align__(16) Stage<CPL> stage;
+  __shared__ float rcp_tab[kQuantWaves][2][128];  // per wave: the tables of its two blocks' groups
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const uint32_t half = lane >> 5;
   const uint32_t v = xcd_work_item(chunk);
-  if (v >= nq * ntc) return;
-  uint32_t ctile, pair;
-  wg_item(v, nq, ctile, pair);
-  if (pair >= npairs) return;
+  if (v >= nbg * ntc) return;  // whole workgroup
+  const uint32_t ctile = v / nbg, bg = v - ctile * nbg;
+  const uint32_t pair = bg * kQuantWaves + wid;
   const GroupScan q = group_scan(offsets, groups, rows);
   // The first wave: padded offsets, and with amax_in the groups' amax / S_dec
   // (otherwise the reduce kernel wrote them).
@@ -317,59 +429,18 @@ __global__ __launch_bounds__(kT) void k_grouped_quant(const uint16_t* __restrict
     if (lane == 0 && poff_out) poff_out[0] = 0;
   }
   const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
-  const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
-  Tile<CPL> r;
-  load_item<CPL>(x, ld_x, rows, it, r);
-  const float* gam = amax_in ? amax_in : ws->partial + kGroupAmax;
-  const GScale g0 = global_scale(gam[it.b0.g]), g1 = global_scale(gam[it.b1.g]);
-  // the wave's own tables: its LDS writes precede its reads, no barrier
-  float* tabs = &rcp_tab[wid][0][0];
-  tabs[lane] = encode_mult(lane, g0.dec);
-  tabs[lane + 64] = encode_mult(lane + 64, g0.dec);
-  tabs[128 + lane] = encode_mult(lane, g1.dec);
-  tabs[128 + lane + 64] = encode_mult(lane + 64, g1.dec);
-  const uint32_t pcol = it.tb * 16u;  // plane column of the block's first token
-  // Plane capacity guard: only malformed offsets can reach it.
-  if (!it.ok || (int64_t)pcol + 16 > cap) return;
-  if constexpr (RHT) apply_signs<CPL>(r, mask);
-  const float* tab = tabs + half * 128;
-  const float enc = half ? g1.enc : g0.enc;
-  const uint64_t nbp = (uint64_t)(mpad >> 4);  // blocks per plane row
-  // block index and addresses of column `col` once; the lane's next columns
-  // differ by uniform strides (64-bit products cost several cycles)
-  const uint64_t blk0 = (uint64_t)it.col * nbp + (pcol >> 4);
-  uint8_t* cp = codes + (int64_t)it.col * ldc + (pcol >> 1);
-  uint8_t* sp = scales + (int64_t)it.col * lds + (pcol >> 4);
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    float v[16];
-    column<CPL>(r, c, v);
-    if constexpr (RHT) {
-      fwht16(v);
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const uint32_t p = pack_bf16(v[i] * 0.25f, v[i + 1] * 0.25f);
-        v[i] = bf_lo(p);
-        v[i + 1] = bf_hi(p);
-      }
-    }
-    const float m = fmaxf(max8_abs(v), max8_abs(v + 8));
-    const uint32_t sc = block_scale(m, enc);
-    const float rc = tab[sc];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
-    uint2 out;
-    if constexpr (SR) {
-      const U4 wr = block_random(blk0 + (uint64_t)c * nbp, 1, seed, offset);
-      out.x = sr_pack8(v, wr.x, wr.y);
-      out.y = sr_pack8(v + 8, wr.z, wr.w);
-    } else {
-      out.x = rtne_pack8(v);
-      out.y = rtne_pack8(v + 8);
-    }
-    *reinterpret_cast<uint2*>(cp + (int64_t)c * ldc) = out;
-    sp[(int64_t)c * lds] = (uint8_t)sc;
+  if (pair < npairs) {  // wave-uniform; every wave reaches the barrier below
+    const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
+    Tile<CPL> r;
+    load_item<CPL>(x, ld_x, rows, it, true, r);
+    GroupTabs gt;
+    gt.g0 = -1;
+    gt.g1 = -1;
+    encode_item<CPL, RHT, SR>(it, r, mask, amax_in ? amax_in : ws->partial + kGroupAmax, gt, &rcp_tab[wid][0][0],
+                              stage, mpad, seed, offset);
   }
+  __syncthreads();
+  write_item<CPL>(stage, ctile, bg, cols, mpad, cap, codes, ldc, scales, lds);
 }
 
 // Upper bound of the padded token blocks of all groups:
@@ -417,11 +488,14 @@ void launch_amax(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
 template <int CPLE, bool RHT, bool SR>
 void launch_quant(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
   const int64_t cap = a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16;
-  const Geo g = geo_of<CPLE>(a.cols, nb_max);
-  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR>), g.grid, dim3(kT), 0, s, (const uint16_t*)a.x, (int)a.rows,
-                     (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws,
-                     a.amax_in, a.amax_out, a.scale_out, a.poff_out, a.seed, a.offset, cap, g.nq, g.ntc, g.npairs,
-                     g.chunk);
+  const uint32_t npairs = (nb_max + 1) / 2 < 1 ? 1 : (nb_max + 1) / 2;
+  const uint32_t nbg = (npairs + kQuantWaves - 1) / kQuantWaves;  // items per column tile
+  const uint32_t ntc = tiles_of<CPLE>(a.cols);
+  const uint32_t chunk = xcd_chunk((uint64_t)nbg * ntc);
+  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR>), dim3(xcd_grid((uint64_t)nbg * ntc)), dim3(kQuantThreads), 0,
+                     s, (const uint16_t*)a.x, (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask,
+                     a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in, a.amax_out, a.scale_out, a.poff_out, a.seed,
+                     a.offset, cap, nbg, ntc, npairs, chunk);
 }
 
 template <bool RHT>
