@@ -166,34 +166,57 @@ __device__ __forceinline__ U4 block_random(uint64_t blk, uint32_t tag, uint64_t 
 // against the definition on 4096 values x 256 bytes). Each element has its own
 // byte, so a pair is converted twice: once with a's byte in bits 31..24 (the
 // low nibble, a's code, is kept) and once with b's byte in bits 30..23 (the
-// high nibble, b's code, is kept). The instruction writes only the selected
-// byte of its destination while the compiler treats the whole register as
-// written, so only byte 0 of a result is used; bytes are gathered with
-// v_perm_b32.
-template <int BA, int BB>
-__device__ __forceinline__ uint32_t e2m1_sr_pair(float a, float b, uint32_t wa, uint32_t wb) {
-  const f32x2 ab = {a, b};
-  const uint32_t ra = ((wa >> (8 * BA)) & 0xFFu) << 24;
-  const uint32_t rb = ((wb >> (8 * BB)) & 0xFFu) << 23;
-  const uint32_t lo = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, ab, ra, 1.0f, 0);
-  const uint32_t hi = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, ab, rb, 1.0f, 0);
-  return (lo & 0x0Fu) | (hi & ~0x0Fu);  // v_bfi_b32; bytes 1..3 are don't-care
+// high nibble, b's code, is kept).
+//
+// The instruction writes only the byte of its destination that op_sel[3:2]
+// selects, so four conversions fill one register; the compiler's builtin does
+// not tie the destination's other bytes to its `old` operand, so bytes 1..3
+// are written through inline assembly with the register as an in-out operand
+// (byte 0 by the builtin, whose other bytes are then overwritten).
+template <int SEL>
+__device__ __forceinline__ uint32_t sr_byte(uint32_t acc, f32x2 ab, uint32_t r) {
+  if constexpr (SEL == 0) {
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(acc, ab, r, 1.0f, 0);
+  } else if constexpr (SEL == 1) {
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,0]" : "+v"(acc) : "v"(ab), "v"(r));
+  } else if constexpr (SEL == 2) {
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,0,1]" : "+v"(acc) : "v"(ab), "v"(r));
+  } else {
+    asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, 1.0 op_sel:[0,0,1,1]" : "+v"(acc) : "v"(ab), "v"(r));
+  }
+  return acc;
 }
 
-// Byte 0 of a, b, c, d gathered into bytes 0..3 (v_perm_b32 selects bytes of
-// its second operand with indices 0..3, of its first with 4..7; 0x0C yields a
-// zero byte).
-__device__ __forceinline__ uint32_t gather_b0(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
-  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
-  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+// Byte K of w in bits 31..24, zeros below (the random operand of a pair's
+// first element).
+template <int K>
+__device__ __forceinline__ uint32_t rand_first(uint32_t w) {
+  if constexpr (K == 0) return w << 24;
+  else if constexpr (K == 3) return w & 0xFF000000u;
+  else return __builtin_amdgcn_perm(0u, w, (uint32_t)(K << 24) | 0x000C0C0Cu);  // 0x0C: a zero byte
+}
+// Byte K of w in bits 30..23, zeros below (the operand of a pair's second
+// element, which the instruction shifts left by one).
+template <int K>
+__device__ __forceinline__ uint32_t rand_second(uint32_t w) {
+  return ((w >> (8 * K)) & 0xFFu) << 23;
 }
 
 // Eight SR codes packed in a word (element 2i in the low nibble of byte i).
-// Element e takes byte (e & 3) of w0 (e < 4) or of w1 (e >= 4).
+// Element e takes byte (e & 3) of w0 (e < 4) or of w1 (e >= 4). Register a
+// collects the conversions for the first elements (low nibbles kept), b those
+// for the second elements (high nibbles kept).
 __device__ __forceinline__ uint32_t sr_pack8(const float v[8], uint32_t w0, uint32_t w1) {
-  return gather_b0(e2m1_sr_pair<0, 1>(v[0], v[1], w0, w0), e2m1_sr_pair<2, 3>(v[2], v[3], w0, w0),
-                   e2m1_sr_pair<0, 1>(v[4], v[5], w1, w1), e2m1_sr_pair<2, 3>(v[6], v[7], w1, w1));
+  const f32x2 p0 = {v[0], v[1]}, p1 = {v[2], v[3]}, p2 = {v[4], v[5]}, p3 = {v[6], v[7]};
+  uint32_t a = sr_byte<0>(0u, p0, rand_first<0>(w0));
+  uint32_t b = sr_byte<0>(0u, p0, rand_second<1>(w0));
+  a = sr_byte<1>(a, p1, rand_first<2>(w0));
+  b = sr_byte<1>(b, p1, rand_second<3>(w0));
+  a = sr_byte<2>(a, p2, rand_first<0>(w1));
+  b = sr_byte<2>(b, p2, rand_second<1>(w1));
+  a = sr_byte<3>(a, p3, rand_first<2>(w1));
+  b = sr_byte<3>(b, p3, rand_second<3>(w1));
+  return (a & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);  // v_bfi_b32
 }
 
 // Eight RTNE codes packed in a word.
