@@ -203,12 +203,13 @@ __device__ __forceinline__ void apply_signs(Tile<CPL>& r, uint32_t mask) {
   }
 }
 
-// Four butterfly stages in Sylvester order on D v: for h = 1, 2, 4, 8 the
-// pairs (i, i + h) with (i & h) == 0 become (a + b, a - b). The caller
-// applies the 0.25 scaling.
+// Butterfly stages in Sylvester order on D v: for h = 1, 2, 4, 8 (the
+// first STAGES of them) the pairs (i, i + h) with (i & h) == 0 become
+// (a + b, a - b). The caller applies the 0.25 scaling.
+template <int STAGES = 4>
 __device__ __forceinline__ void fwht16(float v[16]) {
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
+  for (int h = 1; h < (1 << STAGES); h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i & h) continue;
@@ -249,8 +250,18 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
   for (int c = 0; c < CPL; ++c) {
     float v[16];
     column<CPL>(r, c, v);
-    if constexpr (RHT) fwht16(v);
-    m = fmaxf(m, fmaxf(max8_abs(v), max8_abs(v + 8)));
+    if constexpr (RHT) {
+      // The last stage only feeds the maximum: max(|RN(a + b)|, |RN(a - b)|)
+      // = RN(|a| + |b|), since one of a + b, a - b has magnitude |a| + |b|,
+      // the other at most that, and rounding is odd and monotone.
+      fwht16<3>(v);
+      float s8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s8[i] = fabsf(v[i]) + fabsf(v[i + 8]);
+      m = fmaxf(m, max8_abs(s8));
+    } else {
+      m = fmaxf(m, fmaxf(max8_abs(v), max8_abs(v + 8)));
+    }
   }
   // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
   // round-to-nearest-even are both monotone.

@@ -28,30 +28,38 @@
 namespace nvfp4q {
 
 // ------------------------------------------------------------------ amax
-constexpr int kAmaxUnroll = 4;
+// A wave takes one span of kAmaxLoads * 512 columns of one row at a time and
+// issues all of its 16-byte loads at once (16 KB in flight per wave) through
+// a buffer resource that ends at the row's last column, so reads past cols
+// return zero without guards.
+constexpr int kAmaxLoads = 16;
+constexpr uint32_t kAmaxSpan = kAmaxLoads * 512;
+constexpr int kAmaxMaxWGs = 2048;
 __global__ __launch_bounds__(kThreads) void k_amax_rows(const RowArgs a) {
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
-  const int lane = threadIdx.x & 63;
-  const uint32_t wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)((blockIdx.x * kThreads + threadIdx.x) >> 6));
   const uint32_t nwaves = (gridDim.x * kThreads) >> 6;
-  const uint32_t nch = (cols + 511) >> 9;
+  const uint32_t ngrp = (cols + kAmaxSpan - 1) / kAmaxSpan;  // spans per row
+  const uint64_t units = (uint64_t)rows * ngrp;
   float m = 0.0f;
-  for (uint32_t r = wave; r < rows; r += nwaves) {
-    const uint16_t* xr = x + (int64_t)r * a.ld_x;
-    for (uint32_t c0 = 0; c0 < nch; c0 += kAmaxUnroll) {
-      uint4 q[kAmaxUnroll];
+  for (uint64_t u = wave; u < units; u += nwaves) {
+    const uint32_t r = (uint32_t)(u / ngrp), c0 = (uint32_t)(u - (uint64_t)r * ngrp) * kAmaxSpan;
+    const uint32_t left = cols - c0 < kAmaxSpan ? cols - c0 : kAmaxSpan;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)r * a.ld_x + c0), (short)0, (int)(left * 2), 0x00020000);
+    uint4 q[kAmaxLoads];
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) {
-        const uint32_t col = (c0 + u) * 512 + lane * 8;
-        q[u] = ld16(xr + col, (c0 + u) < nch && col < cols);
-      }
+    for (int k = 0; k < kAmaxLoads; ++k) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)k * 1024u + lane * 16u, 0, 0);
+      q[k] = make_uint4(t[0], t[1], t[2], t[3]);
+    }
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) {
-        float v[8];
-        widen8(q[u], v);
-        m = fmaxf(m, max8_abs(v));
-      }
+    for (int k = 0; k < kAmaxLoads; ++k) {
+      float v[8];
+      widen8(q[k], v);
+      m = fmaxf(m, max8_abs(v));
     }
   }
   publish_partial(a.ws, m);
@@ -109,8 +117,9 @@ hipError_t launch_empty_scale(float* amax_out, float* scale_out, int n, hipStrea
 }
 
 hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s, uint32_t* nparts) {
-  int64_t wgs = (a.rows + kWavesPerWG - 1) / kWavesPerWG;
-  if (wgs > 1024) wgs = 1024;
+  const int64_t units = a.rows * ((a.cols + kAmaxSpan - 1) / kAmaxSpan);  // one per wave at most
+  int64_t wgs = (units + kWavesPerWG - 1) / kWavesPerWG;
+  if (wgs > kAmaxMaxWGs) wgs = kAmaxMaxWGs;
   if (wgs < 1) wgs = 1;
   *nparts = (uint32_t)wgs;
   hipLaunchKernelGGL(k_amax_rows, dim3((uint32_t)wgs), dim3(kThreads), 0, s, a);
