@@ -330,35 +330,22 @@ struct Stage {
 struct GroupTabs {
   int g0, g1;
   GScale s0, s1;
+  bool fold;  // the transform's 0.25 is folded into the block maximum and the tables
 };
 
-template <int CPL, bool RHT, bool SR>
-__device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32_t mask, const float* gam,
-                                            GroupTabs& gt, float* tabs, Stage<CPL>& st, uint32_t mpad,
-                                            uint64_t seed, uint32_t offset) {
-  const uint32_t lane = threadIdx.x & 63, half = lane >> 5;
-  const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  if (it.b0.g != gt.g0 || it.b1.g != gt.g1) {
-    gt.g0 = it.b0.g;
-    gt.g1 = it.b1.g;
-    gt.s0 = global_scale(gam[gt.g0]);
-    gt.s1 = global_scale(gam[gt.g1]);
-    // the wave's own tables: its LDS writes precede its reads
-    tabs[lane] = encode_mult(lane, gt.s0.dec);
-    tabs[lane + 64] = encode_mult(lane + 64, gt.s0.dec);
-    tabs[128 + lane] = encode_mult(lane, gt.s1.dec);
-    tabs[128 + lane + 64] = encode_mult(lane + 64, gt.s1.dec);
-  }
-  if constexpr (RHT) apply_signs<CPL>(r, mask);
-  const float* tab = tabs + half * 128;
-  const float enc = half ? gt.s1.enc : gt.s0.enc;
-  const uint64_t nbp = (uint64_t)(mpad >> 4);  // blocks per plane row
-  uint64_t blk = (uint64_t)it.col * nbp + it.tb;
-  // staging slot of the lane's block: byte 8 j of code row r, byte j of
-  // scale row r, j = the block's place among the item's 16
-  const uint32_t j = 2 * wid + half;
-  uint8_t* cst = st.codes + (lane & 31) * CPL * kStagePitch + 8 * j;
-  uint8_t* sst = st.scales + (lane & 31) * CPL * kItemBlocks + j;
+// Folding the transform's factor 0.25: bf16(0.25 t) = 0.25 bf16(t) whenever
+// 0.25 t is a normal number, so the block maximum can be taken over bf16(t)
+// and scaled once, and the 0.25 can join the encode multiplier (exactly, while
+// that stays normal). With the group amax in [2^-90, 2^120] the cases where
+// 0.25 t is subnormal cannot change a code (such an element times any encode
+// multiplier of the group stays below 2^-9, so it encodes as a signed zero
+// either way, and a block made only of them gets scale code 0 either way),
+// and the tables stay normal. Outside that range the unfolded path runs.
+__device__ __forceinline__ bool fold_ok(float amax) { return amax >= 0x1p-90f && amax <= 0x1p120f; }
+
+template <int CPL, bool RHT, bool SR, bool FOLD>
+__device__ __forceinline__ void encode_columns(Tile<CPL>& r, const float* tab, float enc, uint64_t blk, uint64_t nbp,
+                                               uint8_t* cst, uint8_t* sst, uint64_t seed, uint32_t offset) {
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     float v16[16];
@@ -367,12 +354,13 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32
       fwht16(v16);
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const uint32_t p = pack_bf16(v16[i] * 0.25f, v16[i + 1] * 0.25f);
+        const uint32_t p = FOLD ? pack_bf16(v16[i], v16[i + 1]) : pack_bf16(v16[i] * 0.25f, v16[i + 1] * 0.25f);
         v16[i] = bf_lo(p);
         v16[i + 1] = bf_hi(p);
       }
     }
-    const float m = fmaxf(max8_abs(v16), max8_abs(v16 + 8));
+    float m = fmaxf(max8_abs(v16), max8_abs(v16 + 8));
+    if constexpr (FOLD) m *= 0.25f;
     const uint32_t sc = block_scale(m, enc);
     const float rc = tab[sc];
 #pragma unroll
@@ -390,6 +378,42 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32
     sst[c * kItemBlocks] = (uint8_t)sc;
     blk += nbp;
   }
+}
+
+template <int CPL, bool RHT, bool SR>
+__device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32_t mask, const float* gam,
+                                            GroupTabs& gt, float* tabs, Stage<CPL>& st, uint32_t mpad,
+                                            uint64_t seed, uint32_t offset) {
+  const uint32_t lane = threadIdx.x & 63, half = lane >> 5;
+  const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (it.b0.g != gt.g0 || it.b1.g != gt.g1) {
+    gt.g0 = it.b0.g;
+    gt.g1 = it.b1.g;
+    const float a0 = gam[gt.g0], a1 = gam[gt.g1];
+    gt.s0 = global_scale(a0);
+    gt.s1 = global_scale(a1);
+    gt.fold = RHT && fold_ok(a0) && fold_ok(a1);
+    const float f = gt.fold ? 0.25f : 1.0f;
+    // the wave's own tables: its LDS writes precede its reads
+    tabs[lane] = encode_mult(lane, gt.s0.dec) * f;
+    tabs[lane + 64] = encode_mult(lane + 64, gt.s0.dec) * f;
+    tabs[128 + lane] = encode_mult(lane, gt.s1.dec) * f;
+    tabs[128 + lane + 64] = encode_mult(lane + 64, gt.s1.dec) * f;
+  }
+  if constexpr (RHT) apply_signs<CPL>(r, mask);
+  const float* tab = tabs + half * 128;
+  const float enc = half ? gt.s1.enc : gt.s0.enc;
+  const uint64_t nbp = (uint64_t)(mpad >> 4);  // blocks per plane row
+  const uint64_t blk = (uint64_t)it.col * nbp + it.tb;
+  // staging slot of the lane's block: byte 8 j of code row r, byte j of
+  // scale row r, j = the block's place among the item's blocks
+  const uint32_t j = 2 * wid + half;
+  uint8_t* cst = st.codes + (lane & 31) * CPL * kStagePitch + 8 * j;
+  uint8_t* sst = st.scales + (lane & 31) * CPL * kItemBlocks + j;
+  if (RHT && gt.fold)
+    encode_columns<CPL, RHT, SR, true>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
+  else
+    encode_columns<CPL, RHT, SR, false>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
 }
 
 // Write-out of a staged item: plane rows of column tile ctile, blocks

@@ -336,6 +336,19 @@ def test_grouped_one_group_and_given_amax(gpu_lib):
     _grouped_check(gpu_lib, x, [0, 7, 300], True, 0x0001, "rtne", amax=[1.5, 30.0])
 
 
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_grouped_extreme_group_scales(gpu_lib, rounding):
+    # Groups whose amax lies below 2^-90, is exactly zero, is ordinary, and lies
+    # above 2^120: the encode folds the transform's 0.25 into the block maximum
+    # only inside [2^-90, 2^120] and must agree with the oracle on both sides.
+    rng = np.random.default_rng(15)
+    parts = [(_bf16(rng, (40, 288), 1e-30)), np.zeros((23, 288), np.uint16), _bf16(rng, (37, 288)),
+             _bf16(rng, (50, 288), 1e37), _bf16(rng, (19, 288), 3e-28)]
+    x = np.concatenate(parts, axis=0)
+    offsets = np.concatenate([[0], np.cumsum([p.shape[0] for p in parts])]).tolist()
+    _grouped_check(gpu_lib, x, offsets, True, 0x6A5C, rounding)
+
+
 def test_grouped_64_groups_many_empty(gpu_lib):
     rng = np.random.default_rng(14)
     counts = rng.multinomial(1000, np.full(64, 1 / 64))
