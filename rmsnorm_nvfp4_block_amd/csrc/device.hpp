@@ -304,7 +304,7 @@ __device__ __forceinline__ void fill_rcp_table(float* tab, float s_dec) {
   if (threadIdx.x < 128) tab[threadIdx.x] = encode_mult(threadIdx.x, s_dec);
 }
 
-constexpr int kWGThreads = 256;  // every kernel runs 4-wave workgroups
+constexpr int kWGThreads = 256;  // the usual workgroup; kernels of other sizes pass their wave count
 constexpr int kWavesPerWG = kWGThreads / kWave;
 
 // ---------------------------------------------------------------- consumers
@@ -324,10 +324,12 @@ __device__ __forceinline__ float wg_max(float m) {
 }
 
 // Max over partial[first .. first + n) with all threads of the workgroup.
+// (NW: the waves of the calling workgroup.)
+template <int NW = kWavesPerWG>
 __device__ __forceinline__ float reduce_partials(const Workspace* ws, uint32_t first, uint32_t n) {
   float m = 0.0f;
-  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, ws->partial[first + i]);
-  return wg_max(m);
+  for (uint32_t i = threadIdx.x; i < n; i += 64 * NW) m = fmaxf(m, ws->partial[first + i]);
+  return wg_max<NW>(m);
 }
 
 // Per-tensor scales for an encode kernel, into every thread, and the encode
@@ -344,9 +346,10 @@ __device__ __forceinline__ GScale scales_from(float a, float* amax_out, float* s
   return g;
 }
 
+template <int NW = kWavesPerWG>
 __device__ __forceinline__ GScale consume_scales(const Workspace* ws, uint32_t nparts, const float* amax_in,
                                                  float* amax_out, float* scale_out, float* rcp_tab) {
-  return scales_from(amax_in ? *amax_in : reduce_partials(ws, 0, nparts), amax_out, scale_out, rcp_tab);
+  return scales_from(amax_in ? *amax_in : reduce_partials<NW>(ws, 0, nparts), amax_out, scale_out, rcp_tab);
 }
 
 // The same in two steps, so that a kernel can issue these loads before its

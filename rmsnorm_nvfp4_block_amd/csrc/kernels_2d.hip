@@ -22,7 +22,6 @@ namespace nvfp4q {
 
 namespace {
 
-constexpr int kT = 256;
 constexpr int kTileR = 128, kTileC = 128;
 constexpr int kRowBytes = kTileC * 2;  // 256 B per staged row
 
@@ -30,8 +29,13 @@ __device__ __forceinline__ uint32_t swz_chunk(uint32_t chunk, uint32_t row) {
   return chunk ^ (((row >> 4) & 3u) << 2);
 }
 
-template <bool ROW, bool COL, bool SR>
-__global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tiles_c, uint32_t ntiles, uint32_t chunk) {
+// T threads per tile: 128 / (T / 8) rows (rowwise) and 1024 / T columns
+// (columnwise) per thread.
+template <int T, bool ROW, bool COL, bool SR>
+__global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles_c, uint32_t ntiles, uint32_t chunk) {
+  constexpr int kRpt = kTileR / (T / 8);  // rows per thread
+  constexpr int kRs = T / 8;              // row stride between a thread's rows
+  constexpr int kCpt = 1024 / T;          // columns per thread (columnwise)
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileR * kRowBytes];
   __shared__ float rcp_tab[128];
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
@@ -50,32 +54,32 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
   const uint32_t tr = item / tiles_c, tc = item - tr * tiles_c;
   const uint32_t row0 = tr * kTileR, col0 = tc * kTileC;
 
-  // ---- load 4 rows x 32 B per thread
+  // ---- load kRpt rows x 32 B per thread
   const uint32_t bsub = t & 7, rsub = t >> 3;
   const uint32_t col = col0 + bsub * 16;
-  uint4 q[4][2];
+  uint4 q[kRpt][2];
   const uint16_t* xp = x + (int64_t)(row0 + rsub) * ld_x + col;
   if (row0 + kTileR <= rows && col0 + kTileC <= cols) {
     // a whole tile (all but the edge tiles): no guards, one base address
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      q[j][0] = *reinterpret_cast<const uint4*>(xp + (int64_t)(32 * j) * ld_x);
-      q[j][1] = *reinterpret_cast<const uint4*>(xp + (int64_t)(32 * j) * ld_x + 8);
+    for (int j = 0; j < kRpt; ++j) {
+      q[j][0] = *reinterpret_cast<const uint4*>(xp + (int64_t)(kRs * j) * ld_x);
+      q[j][1] = *reinterpret_cast<const uint4*>(xp + (int64_t)(kRs * j) * ld_x + 8);
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t r = row0 + rsub + 32 * j;
+    for (int j = 0; j < kRpt; ++j) {
+      const uint32_t r = row0 + rsub + kRs * j;
       const bool ok = r < rows && col < cols;
-      q[j][0] = ld16(xp + (int64_t)(32 * j) * ld_x, ok);
-      q[j][1] = ld16(xp + (int64_t)(32 * j) * ld_x + 8, ok);
+      q[j][0] = ld16(xp + (int64_t)(kRs * j) * ld_x, ok);
+      q[j][1] = ld16(xp + (int64_t)(kRs * j) * ld_x + 8, ok);
     }
   }
-  const GScale g = consume_scales(a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
+  const GScale g = consume_scales<T / 64>(a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
   if constexpr (COL) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lr = rsub + 32 * j;
+    for (int j = 0; j < kRpt; ++j) {
+      const uint32_t lr = rsub + kRs * j;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         *reinterpret_cast<uint4*>(tile + lr * kRowBytes + swz_chunk(2 * bsub + h, lr) * 16) = q[j][h];
@@ -91,31 +95,38 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
     uint8_t* cp = rcodes + (int64_t)r0 * rldc + (col >> 1);
     uint8_t* sp = rscales + (int64_t)r0 * rlds + (col >> 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t r = r0 + 32 * j;
+    for (int j = 0; j < kRpt; ++j) {
+      const uint32_t r = r0 + kRs * j;
       const bool ok = r < rows && col < cols;
       float v[16];
       widen8(q[j][0], v);
       widen8(q[j][1], v + 8);
       uint32_t sc;
-      const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, blk0 + (uint64_t)(32 * j) * nbr, seed, offset, 0);
+      const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, blk0 + (uint64_t)(kRs * j) * nbr, seed, offset, 0);
       if (ok) {
-        *reinterpret_cast<uint2*>(cp + (int64_t)(32 * j) * rldc) = w;
-        sp[(int64_t)(32 * j) * rlds] = (uint8_t)sc;
+        *reinterpret_cast<uint2*>(cp + (int64_t)(kRs * j) * rldc) = w;
+        sp[(int64_t)(kRs * j) * rlds] = (uint8_t)sc;
       }
     }
   }
   // ---- columnwise plane from the staged tile
   if constexpr (COL) {
     __syncthreads();
-    const uint32_t mb = t & 7, cg = t >> 3;           // 8 row blocks x 32 column quads
-    const uint32_t lc = cg * 4;                        // first local column
-    const uint32_t cchunk = lc >> 3, chalf = (lc >> 2) & 1;
-    uint2 d[16];
+    const uint32_t mb = t & 7, cg = t >> 3;           // 8 row blocks x T/8 column groups
+    const uint32_t lc = cg * kCpt;                     // first local column
+    const uint32_t cchunk = lc >> 3;                   // its 16-byte chunk of a staged row
+    uint32_t d[16][kCpt / 2];                          // bf16 pairs: columns lc + 2k, lc + 2k + 1
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t lr = mb * 16 + i;
-      d[i] = *reinterpret_cast<const uint2*>(tile + lr * kRowBytes + swz_chunk(cchunk, lr) * 16 + chalf * 8);
+      const uint8_t* src = tile + lr * kRowBytes + swz_chunk(cchunk, lr) * 16 + (lc & 7) * 2;
+      if constexpr (kCpt == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(src);
+        d[i][0] = u.x;
+        d[i][1] = u.y;
+      } else {
+        d[i][0] = *reinterpret_cast<const uint32_t*>(src);
+      }
     }
     const uint32_t grow = row0 + mb * 16;              // first row of the block
     const bool rok = grow < rows;
@@ -125,14 +136,11 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
     uint8_t* ccp = ccodes + (int64_t)gc0 * cldc + (grow >> 1);
     uint8_t* csp = cscales + (int64_t)gc0 * clds + (grow >> 4);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kCpt; ++c) {
       const uint32_t gc = gc0 + c;
       float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t w = (c < 2) ? d[i].x : d[i].y;
-        v[i] = (c & 1) ? bf_hi(w) : bf_lo(w);
-      }
+      for (int i = 0; i < 16; ++i) v[i] = (c & 1) ? bf_hi(d[i][c >> 1]) : bf_lo(d[i][c >> 1]);
       float m = fmaxf(max8_abs(v), max8_abs(v + 8));
       uint32_t sc = block_scale(m, g.enc);
       float rc = rcp_tab[sc];
@@ -155,16 +163,31 @@ __global__ __launch_bounds__(kT) void k_quant_2d(const TwoDArgs a, uint32_t tile
   }
 }
 
-template <bool ROW, bool COL>
-void launch_2d_rc(const TwoDArgs& a, hipStream_t s) {
+// Threads per tile: NVFP4Q_2D_THREADS (256 or 512), default 512.
+int threads_2d() {
+  static const int v = [] {
+    const char* e = getenv("NVFP4Q_2D_THREADS");
+    return e && atoi(e) == 256 ? 256 : 512;
+  }();
+  return v;
+}
+
+template <int T, bool ROW, bool COL>
+void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
   const uint32_t tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
   const uint32_t tiles_c = (uint32_t)((a.cols + kTileC - 1) / kTileC);
   // Plain row-major tile order: the per-XCD ranges used by the grouped path
-  // measured slower here (66.8 vs 69.5 us on 8192 x 8192 with SR).
+  // measured slower here (8192 x 8192 with SR: 97.5 vs 91.3 us per step).
   const uint32_t ntiles = tiles_r * tiles_c, chunk = 0;
-  dim3 grid(ntiles), block(kT);
-  if (a.sr) hipLaunchKernelGGL((k_quant_2d<ROW, COL, true>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
-  else hipLaunchKernelGGL((k_quant_2d<ROW, COL, false>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+  dim3 grid(ntiles), block(T);
+  if (a.sr) hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, true>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+  else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+}
+
+template <bool ROW, bool COL>
+void launch_2d_rc(const TwoDArgs& a, hipStream_t s) {
+  if (threads_2d() == 256) launch_2d_t<256, ROW, COL>(a, s);
+  else launch_2d_t<512, ROW, COL>(a, s);
 }
 
 }  // namespace
