@@ -273,12 +273,39 @@ __device__ __forceinline__ float wave_max(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Maxima of magnitudes with v_max3_f32 and absolute-value source modifiers:
+// 16 values in 7 three-input maxima and one two-input maximum (the compiler,
+// left to fmaxf, adds a canonicalizing max per value, and every max is a
+// slow VALU instruction on gfx950). For finite inputs the result equals the
+// fmaxf form; non-finite inputs are outside the method's definition.
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max(m, |a|, |b|) for m >= 0
+__device__ __forceinline__ float max3_m_abs(float m, float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_pos(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float max8_abs(const float v[8]) {
-  float a = fmaxf(fabsf(v[0]), fabsf(v[1]));
-  float b = fmaxf(fabsf(v[2]), fabsf(v[3]));
-  float c = fmaxf(fabsf(v[4]), fabsf(v[5]));
-  float d = fmaxf(fabsf(v[6]), fabsf(v[7]));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+  const float a = max3_abs(v[0], v[1], v[2]);
+  const float b = max3_abs(v[3], v[4], v[5]);
+  return fmaxf(b, max3_m_abs(a, v[6], v[7]));
+}
+__device__ __forceinline__ float max16_abs(const float v[16]) {
+  const float a = max3_abs(v[0], v[1], v[2]);
+  const float b = max3_abs(v[3], v[4], v[5]);
+  const float c = max3_abs(v[6], v[7], v[8]);
+  const float d = max3_abs(v[9], v[10], v[11]);
+  const float e = max3_abs(v[12], v[13], v[14]);
+  return fmaxf(max3_pos(a, b, c), max3_m_abs(d, e, v[15]));
 }
 
 __device__ __forceinline__ void widen8(const uint4 q, float v[8]) {
@@ -412,7 +439,6 @@ __device__ __forceinline__ uint32_t xcd_work_item(uint32_t chunk) {
 uint32_t xcd_chunk(uint64_t items);     // 0 when the plain order is selected
 uint32_t xcd_grid(uint64_t items);      // workgroups to launch for `items` work items
 
-__device__ __forceinline__ float max16_abs(const float v[16]) { return fmaxf(max8_abs(v), max8_abs(v + 8)); }
 
 // Encode one 16-element block held by one lane (fp32 values that are bf16
 // values): block scale from the block max, encode multiplier from the table,

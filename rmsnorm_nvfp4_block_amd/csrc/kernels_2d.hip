@@ -141,7 +141,7 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
       float v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = (c & 1) ? bf_hi(d[i][c >> 1]) : bf_lo(d[i][c >> 1]);
-      float m = fmaxf(max8_abs(v), max8_abs(v + 8));
+      float m = max16_abs(v);
       uint32_t sc = block_scale(m, g.enc);
       float rc = rcp_tab[sc];
 #pragma unroll

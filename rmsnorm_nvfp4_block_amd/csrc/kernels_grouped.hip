@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
       for (int i = 0; i < 8; ++i) s8[i] = fabsf(v[i]) + fabsf(v[i + 8]);
       m = fmaxf(m, max8_abs(s8));
     } else {
-      m = fmaxf(m, fmaxf(max8_abs(v), max8_abs(v + 8)));
+      m = fmaxf(m, max16_abs(v));
     }
   }
   // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
@@ -359,7 +359,7 @@ __device__ __forceinline__ void encode_columns(Tile<CPL>& r, const float* tab, f
         v16[i + 1] = bf_hi(p);
       }
     }
-    float m = fmaxf(max8_abs(v16), max8_abs(v16 + 8));
+    float m = max16_abs(v16);
     if constexpr (FOLD) m *= 0.25f;
     const uint32_t sc = block_scale(m, enc);
     const float rc = tab[sc];
