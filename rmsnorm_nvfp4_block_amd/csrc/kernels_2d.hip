@@ -163,15 +163,6 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   }
 }
 
-// Threads per tile: NVFP4Q_2D_THREADS (256 or 512), default 512.
-int threads_2d() {
-  static const int v = [] {
-    const char* e = getenv("NVFP4Q_2D_THREADS");
-    return e && atoi(e) == 256 ? 256 : 512;
-  }();
-  return v;
-}
-
 template <int T, bool ROW, bool COL>
 void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
   const uint32_t tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
@@ -184,10 +175,12 @@ void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
   else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
 }
 
+// 512 threads per tile (two rows and two columns each): the tile's LDS
+// limits a CU to four workgroups, which then hold 32 waves (256 threads: 16
+// waves, 3 us slower on 8192 x 8192 with SR).
 template <bool ROW, bool COL>
 void launch_2d_rc(const TwoDArgs& a, hipStream_t s) {
-  if (threads_2d() == 256) launch_2d_t<256, ROW, COL>(a, s);
-  else launch_2d_t<512, ROW, COL>(a, s);
+  launch_2d_t<512, ROW, COL>(a, s);
 }
 
 }  // namespace

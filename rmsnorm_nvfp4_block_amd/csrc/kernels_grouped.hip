@@ -482,13 +482,10 @@ __global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(
 // sum ceil(n_g / 16) <= (rows + 15 G) / 16.
 int64_t grouped_blocks(int64_t rows, int groups) { return (rows + 15 * (int64_t)groups) / 16; }
 
-// Columns per lane of the two passes (4 or 8 each), from NVFP4Q_GROUPED_CPL
-// ("48": amax pass 4, encode pass 8).
-int grouped_cpl(int pass) {
-  static const char* e = getenv("NVFP4Q_GROUPED_CPL");
-  if (e && e[0] && e[1]) return e[pass] == '8' ? 8 : 4;
-  return pass == 0 ? 4 : 8;
-}
+// Columns per lane: the amax pass 4 (65 registers, many waves per SIMD for
+// its loads), the encode 8 (measured on the 16384 x 7168 workload: the 4/4,
+// 4/8, 8/4 and 8/8 pairs were within 2 us, 4/8 fastest).
+constexpr int kCplAmax = 4, kCplQuant = 8;
 
 template <int CPL>
 uint32_t tiles_of(int64_t cols) { return (uint32_t)((cols + 32 * CPL - 1) / (32 * CPL)); }
@@ -536,27 +533,17 @@ void launch_quant(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
 template <bool RHT>
 void launch_grouped_r(const GroupArgs& a, hipStream_t s) {
   const uint32_t nb_max = (uint32_t)grouped_blocks(a.rows, a.groups);
-  if (!a.amax_in) {
-    if (grouped_cpl(0) == 8) launch_amax<8, RHT>(a, nb_max, s);
-    else launch_amax<4, RHT>(a, nb_max, s);
-  }
-  const bool e8 = grouped_cpl(1) == 8;
-  if (a.sr) {
-    if (e8) launch_quant<8, RHT, true>(a, nb_max, s);
-    else launch_quant<4, RHT, true>(a, nb_max, s);
-  } else {
-    if (e8) launch_quant<8, RHT, false>(a, nb_max, s);
-    else launch_quant<4, RHT, false>(a, nb_max, s);
-  }
+  if (!a.amax_in) launch_amax<kCplAmax, RHT>(a, nb_max, s);
+  if (a.sr) launch_quant<kCplQuant, RHT, true>(a, nb_max, s);
+  else launch_quant<kCplQuant, RHT, false>(a, nb_max, s);
 }
 
 }  // namespace
 
 // Workspace slots the grouped path needs: the amax pass's partials, one per
-// (padded token block, column tile) at the narrowest tile (128 columns), and
-// the per-group amax after them.
+// (padded token block, column tile), and the per-group amax after them.
 int64_t grouped_partials(int64_t rows, int64_t cols, int groups) {
-  return grouped_blocks(rows, groups) * tiles_of<4>(cols) + 64;
+  return grouped_blocks(rows, groups) * tiles_of<kCplAmax>(cols) + 64;
 }
 
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {
