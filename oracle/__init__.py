@@ -46,6 +46,11 @@ that implements it. Readings are:
   R-rht      D = diag(d), d_i = -1 iff bit i of a 16-bit mask is set; FWHT in
              Sylvester order, stages h = 1, 2, 4, 8 of fp32 (a+b, a-b);
              times 0.25; bfloat16 round-through. Same D for every block.
+  R-fast     fast math (grouped, with the transform): the transform's fp32
+             output RN(0.25 * FWHT(D x)) is quantized and enters the group
+             amax without the bf16 round-through; the encode reciprocal stays
+             RN(1 / RN(f32(s) * S_dec)) (on this hardware it comes from a
+             127-entry table, so an approximate reciprocal would save nothing).
   R-group    each group is zero-padded to a multiple of 16 rows, groups are
              laid out back to back in one transposed plane; storage past the
              last padded column is never written.

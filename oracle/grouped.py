@@ -23,7 +23,7 @@ import numpy as np
 from .formats import bf16_to_f32, pack_nibbles
 from .philox import block_random_bytes
 from .quantize import global_scales, quantize_blocks
-from .rht import rht16
+from .rht import rht16, rht16_f32
 
 MAX_GROUPS = 64
 
@@ -40,12 +40,14 @@ def padded_offsets(offsets) -> np.ndarray:
 
 
 def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr",
-                     seed=0, offset=0, groups=None):
+                     seed=0, offset=0, groups=None, fast_math=False):
     """Reference for the grouped columnwise path.
 
     x: bf16 bits [total_rows, K]. offsets: int32 [G+1]. amax: optional float32 [G].
     groups: optional iterable restricting which groups are computed (for sampling);
     columns of other groups are left as 0 in the returned planes.
+    fast_math: PR, Fast math -- the transform's output enters the amax and the
+    quantization in float32, without the bf16 round-through (reading R-fast).
     Returns dict with codes [K, Mpad/2], scales [K, Mpad/16], amax [G], s_enc [G],
     s_dec [G], poff [G+1].
     """
@@ -68,9 +70,12 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
         z = np.zeros((pg, K), dtype=np.uint16)
         z[:n] = x[off[g]:off[g + 1]]
         zt = np.ascontiguousarray(z.T).reshape(K, pg // 16, 16)     # column blocks along tokens
-        if apply_rht:
-            zt = rht16(zt, rht_mask)
-        zf = bf16_to_f32(zt)
+        if apply_rht and fast_math:
+            zf = rht16_f32(bf16_to_f32(zt), rht_mask)
+        elif apply_rht:
+            zf = bf16_to_f32(rht16(zt, rht_mask))
+        else:
+            zf = bf16_to_f32(zt)
         a = np.float32(np.max(np.abs(zf))) if zf.size else np.float32(0.0)
         if amax is not None:
             a = np.float32(np.asarray(amax, dtype=np.float32)[g])

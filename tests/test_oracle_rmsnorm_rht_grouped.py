@@ -142,3 +142,39 @@ def test_grouped_each_group_equals_its_zero_padded_slice():
         assert np.array_equal(g["codes"][:, poff[k] // 2:(poff[k] + pg) // 2], r["codes"])
         assert np.array_equal(g["scales"][:, poff[k] // 16:(poff[k] + pg) // 16], r["scales"])
         assert g["amax"][k] == r["amax"]
+
+
+# ---------------------------------------------------------------- R-fast (no bf16 round-through)
+def test_fast_math_equals_exact_when_the_transform_is_bf16_exact():
+    # Integer inputs in [-2, 2]: every transformed value is 0.25 * (a sum of 16 terms of magnitude <= 2),
+    # a multiple of 0.25 below 8 in magnitude, hence exactly a bfloat16; dropping the round-through then
+    # changes nothing.
+    rng = np.random.default_rng(44)
+    x = F.f32_to_bf16(rng.integers(-2, 3, size=(77, 64)).astype(np.float32))
+    offsets = np.array([0, 5, 40, 77], np.int32)
+    for rounding in ("rtne", "sr"):
+        ex = grouped_quantize(x, offsets, apply_rht=True, rht_mask=0x5A3C, rounding=rounding, seed=3)
+        fa = grouped_quantize(x, offsets, apply_rht=True, rht_mask=0x5A3C, rounding=rounding, seed=3,
+                              fast_math=True)
+        for k in ("codes", "scales", "amax", "s_dec"):
+            assert np.array_equal(ex[k], fa[k]), k
+
+
+def test_fast_math_codes_stay_within_one_step_of_exact():
+    # On Gaussian data the fp32 and the bf16-rounded transform differ by at most half a bf16 ulp, so the
+    # codes differ rarely and then by one magnitude step with the same sign; without the transform the
+    # option changes nothing.
+    rng = np.random.default_rng(45)
+    x = F.f32_to_bf16(rng.standard_normal((200, 96)).astype(np.float32))
+    offsets = np.array([0, 70, 130, 200], np.int32)
+    ex = grouped_quantize(x, offsets, apply_rht=True, rht_mask=0x1234, rounding="rtne")
+    fa = grouped_quantize(x, offsets, apply_rht=True, rht_mask=0x1234, rounding="rtne", fast_math=True)
+    a = F.unpack_nibbles(ex["codes"]).astype(np.int16)
+    b = F.unpack_nibbles(fa["codes"]).astype(np.int16)
+    diff = a != b
+    assert 0 < diff.mean() < 0.02
+    assert np.all((a[diff] & 8) == (b[diff] & 8))                      # same sign
+    assert np.all(np.abs((a[diff] & 7) - (b[diff] & 7)) == 1)          # one magnitude step
+    plain = grouped_quantize(x, offsets, apply_rht=False, rounding="rtne")
+    plain_f = grouped_quantize(x, offsets, apply_rht=False, rounding="rtne", fast_math=True)
+    assert np.array_equal(plain["codes"], plain_f["codes"])
