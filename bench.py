@@ -40,10 +40,11 @@ def log(*a):
 class Case:
     """Device buffers and launch closures for one workload."""
 
-    def __init__(self, name, torch, q, workloads):
+    def __init__(self, name, torch, q, workloads, fast_math=False):
         import numpy as np
 
         self.name = name
+        self.fast_math = fast_math
         self.w = w = workloads.make(name)
         dev = torch.device("cuda", 0)
 
@@ -101,6 +102,8 @@ class Case:
         elif self.name == "grouped":
             d.update({"op": "grouped columnwise nvfp4 after 16-pt RHT", "groups": len(w.offsets) - 1,
                       "padded_tokens": self.mpad})
+            if self.fast_math:
+                d["fast_math"] = "transform output quantized in fp32 (no bf16 round-through)"
         else:
             d.update({"op": "nvfp4 rowwise"})
         return d
@@ -116,7 +119,8 @@ class Case:
         if self.name == "weight":
             return q.nvfp4q_quantize_2d(x, amax=amax, rounding=w.rounding, seed=w.seed, offset=w.offset)
         return q.nvfp4q_grouped(x, self.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, amax=amax,
-                                rounding=w.rounding, seed=w.seed, offset=w.offset, codes=o[0], scales=o[1])
+                                rounding=w.rounding, seed=w.seed, offset=w.offset, codes=o[0], scales=o[1],
+                                fast_math=self.fast_math)
 
 
 # ----------------------------------------------------------------------------- timing
@@ -185,7 +189,7 @@ def cpu_baseline(case, budget_s=12.0):
             G = len(w.offsets) - 1
             g = passes % G
             oracle.grouped_quantize(w.x, w.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, rounding=w.rounding,
-                                    seed=w.seed, offset=w.offset, groups=[g])
+                                    seed=w.seed, offset=w.offset, groups=[g], fast_math=case.fast_math)
             n = int(w.offsets[g + 1] - w.offsets[g])
             done_bytes += case.bytes * n / R
         else:
@@ -350,6 +354,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="prefill", choices=["quantize", "prefill", "decode", "weight", "grouped"])
+    ap.add_argument("--fast-math", action="store_true",
+                    help="grouped: NVFP4Q_FAST_MATH (no bf16 round-through of the transform's output)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time plain calls instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES",
@@ -388,7 +394,9 @@ def main():
 
     q.load()
     torch.cuda.set_device(0)
-    case = Case(args.config, torch, q, workloads)
+    if args.fast_math and args.config != "grouped":
+        raise SystemExit("--fast-math applies to the grouped workload (the only one with the transform)")
+    case = Case(args.config, torch, q, workloads, fast_math=args.fast_math)
     log(f"[bench] {case.describe()}")
 
     # whole step (amax + quantize), the figure the metric is quoted on

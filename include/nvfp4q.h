@@ -85,7 +85,15 @@ typedef enum {
 
 typedef enum { NVFP4Q_BF16 = 0 } nvfp4q_dtype;
 
+/* Rounding of the E2M1 codes. NVFP4Q_FAST_MATH may be OR-ed into the value
+ * passed as `rounding` ([PR, Fast math]): with the grouped transform on, the
+ * transform's fp32 output is quantized (and enters the group amax) without
+ * its bf16 round-through; the encode reciprocal stays correctly rounded (it
+ * comes from a 127-entry table per workgroup, so an approximate reciprocal
+ * would save nothing). On paths without the transform the flag changes
+ * nothing. Other bits: NVFP4Q_E_UNSUPPORTED. */
 typedef enum { NVFP4Q_RTNE = 0, NVFP4Q_SR = 1 } nvfp4q_rounding;
+#define NVFP4Q_FAST_MATH 0x100
 
 /* One quantized plane. codes: device, [plane_rows][ld_codes] bytes, two E2M1
  * codes per byte, even element in the low nibble. scales: device,

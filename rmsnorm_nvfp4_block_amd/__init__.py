@@ -25,6 +25,7 @@ SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_gr
            "nvfp4q_workspace_bytes", "nvfp4q_status_string", "nvfp4q_version")
 
 RTNE, SR = 0, 1
+FAST_MATH = 0x100  # NVFP4Q_FAST_MATH, OR-ed into the rounding argument
 
 
 class Plane(ctypes.Structure):
@@ -214,11 +215,13 @@ def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=
 
 
 def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr", seed=0, offset=0,
-                   codes=None, scales=None):
+                   codes=None, scales=None, fast_math=False):
     """Per-group columnwise NVFP4 (optionally after the 16-point RHT) of bf16 x [total_rows, cols].
 
     offsets: int32 CUDA tensor [G+1]. The plane is allocated for the largest padded
-    length (total_rows + 15 G) unless given. Returns dict(codes, scales, amax, scale, poff).
+    length (total_rows + 15 G) unless given. fast_math: NVFP4Q_FAST_MATH (the transform's
+    output is quantized without its bf16 round-through). Returns dict(codes, scales, amax,
+    scale, poff).
     """
     import torch
 
@@ -241,7 +244,8 @@ def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="
     ws = workspace(x.device)
     st = lib.nvfp4q_grouped(x.data_ptr(), 0, T, C, x.stride(0), offsets.data_ptr(), G, poff.data_ptr(),
                             1 if apply_rht else 0, int(rht_mask), ctypes.byref(_global(amax, amax_out, scale_out)),
-                            ctypes.byref(plane), _rounding(rounding), ctypes.byref(Rng(seed, offset)),
+                            ctypes.byref(plane), _rounding(rounding) | (FAST_MATH if fast_math else 0),
+                            ctypes.byref(Rng(seed, offset)),
                             ws.data_ptr(), ws.numel(), _stream(x))
     _check(st)
     return {"codes": codes, "scales": scales, "amax": amax_out, "scale": scale_out, "poff": poff}

@@ -38,9 +38,14 @@ nvfp4q_status check_plane(const nvfp4q_plane* p, int64_t prows, int64_t pcols) {
   return NVFP4Q_OK;
 }
 
+// The rounding mode without option bits.
+nvfp4q_rounding base_rounding(nvfp4q_rounding r) { return (nvfp4q_rounding)((int)r & ~NVFP4Q_FAST_MATH); }
+bool fast_math(nvfp4q_rounding r) { return ((int)r & NVFP4Q_FAST_MATH) != 0; }
+
 nvfp4q_status check_rounding(nvfp4q_rounding r, const nvfp4q_rng* rng) {
-  if (r != NVFP4Q_RTNE && r != NVFP4Q_SR) return NVFP4Q_E_UNSUPPORTED;
-  if (r == NVFP4Q_SR && !rng) return NVFP4Q_E_NULLPTR;
+  const nvfp4q_rounding b = base_rounding(r);
+  if (b != NVFP4Q_RTNE && b != NVFP4Q_SR) return NVFP4Q_E_UNSUPPORTED;
+  if (b == NVFP4Q_SR && !rng) return NVFP4Q_E_NULLPTR;
   return NVFP4Q_OK;
 }
 
@@ -113,7 +118,7 @@ nvfp4q_status nvfp4q_quantize(const void* x, nvfp4q_dtype dtype, int64_t rows, i
   a.codes = row->codes; a.ldc = row->ld_codes; a.scales = row->scales; a.lds = row->ld_scales;
   a.ws = (Workspace*)workspace;
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
-  a.sr = rounding == NVFP4Q_SR;
+  a.sr = base_rounding(rounding) == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   if (!a.amax_in) {
     hipError_t e = launch_amax_rows(a, s, &a.nparts);
@@ -153,7 +158,7 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   a.scales = codes ? row->scales : nullptr; a.lds = codes ? row->ld_scales : 0;
   a.ws = (Workspace*)workspace;
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
-  a.sr = rounding == NVFP4Q_SR;
+  a.sr = base_rounding(rounding) == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   // With the amax pass and a row count that fits the workspace's row-scale
   // slots, the encode pass streams rows using the 1/rms the amax pass stored.
@@ -199,7 +204,7 @@ nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows
   if (has_col) { a.ccodes = col->codes; a.cldc = col->ld_codes; a.cscales = col->scales; a.clds = col->ld_scales; }
   a.ws = (Workspace*)workspace;
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
-  a.sr = rounding == NVFP4Q_SR;
+  a.sr = base_rounding(rounding) == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   return done(launch_quant_2d(a, s));
 }
@@ -229,7 +234,8 @@ nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_ro
   a.codes = col->codes; a.ldc = col->ld_codes; a.scales = col->scales; a.lds = col->ld_scales;
   a.ws = (Workspace*)workspace;
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
-  a.sr = rounding == NVFP4Q_SR;
+  a.sr = base_rounding(rounding) == NVFP4Q_SR;
+  a.fast = fast_math(rounding);
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   return done(launch_grouped(a, (hipStream_t)stream));
 }

@@ -229,7 +229,7 @@ __device__ __forceinline__ float half_wave_max(float m) {
 
 // Pass 1: per-(block, column tile) maximum of the (transformed,
 // bf16-rounded) columnwise values, into partial[tb * ntc + ctile].
-template <int CPL, bool RHT>
+template <int CPL, bool RHT, bool FAST>
 __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict__ x, int rows, uint32_t cols,
                                                      int64_t ld_x, const int32_t* __restrict__ offsets, int groups,
                                                      uint32_t mask, Workspace* ws, uint32_t nq, uint32_t ntc,
@@ -264,8 +264,8 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
     }
   }
   // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
-  // round-to-nearest-even are both monotone.
-  if constexpr (RHT) m = bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
+  // round-to-nearest-even are both monotone (fast math: no bf16 rounding).
+  if constexpr (RHT) m = FAST ? m * 0.25f : bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
   m = half_wave_max(m);  // lanes without data hold zeros
   if ((threadIdx.x & 31) == 0 && it.tb < nb_max) ws->partial[it.tb * ntc + it.ctile] = m;
 }
@@ -343,7 +343,7 @@ struct GroupTabs {
 // and the tables stay normal. Outside that range the unfolded path runs.
 __device__ __forceinline__ bool fold_ok(float amax) { return amax >= 0x1p-90f && amax <= 0x1p120f; }
 
-template <int CPL, bool RHT, bool SR, bool FOLD>
+template <int CPL, bool RHT, bool SR, bool FOLD, bool FAST>
 __device__ __forceinline__ void encode_columns(Tile<CPL>& r, const float* tab, float enc, uint64_t blk, uint64_t nbp,
                                                uint8_t* cst, uint8_t* sst, uint64_t seed, uint32_t offset) {
 #pragma unroll
@@ -352,11 +352,17 @@ __device__ __forceinline__ void encode_columns(Tile<CPL>& r, const float* tab, f
     column<CPL>(r, c, v16);
     if constexpr (RHT) {
       fwht16(v16);
+      if constexpr (!FAST) {
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const uint32_t p = FOLD ? pack_bf16(v16[i], v16[i + 1]) : pack_bf16(v16[i] * 0.25f, v16[i + 1] * 0.25f);
-        v16[i] = bf_lo(p);
-        v16[i + 1] = bf_hi(p);
+        for (int i = 0; i < 16; i += 2) {
+          const uint32_t p =
+              FOLD ? pack_bf16(v16[i], v16[i + 1]) : pack_bf16(v16[i] * 0.25f, v16[i + 1] * 0.25f);
+          v16[i] = bf_lo(p);
+          v16[i + 1] = bf_hi(p);
+        }
+      } else if constexpr (!FOLD) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v16[i] *= 0.25f;
       }
     }
     float m = max16_abs(v16);
@@ -380,7 +386,7 @@ __device__ __forceinline__ void encode_columns(Tile<CPL>& r, const float* tab, f
   }
 }
 
-template <int CPL, bool RHT, bool SR>
+template <int CPL, bool RHT, bool SR, bool FAST>
 __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32_t mask, const float* gam,
                                             GroupTabs& gt, float* tabs, Stage<CPL>& st, uint32_t mpad,
                                             uint64_t seed, uint32_t offset) {
@@ -411,9 +417,9 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32
   uint8_t* cst = st.codes + (lane & 31) * CPL * kStagePitch + 8 * j;
   uint8_t* sst = st.scales + (lane & 31) * CPL * kItemBlocks + j;
   if (RHT && gt.fold)
-    encode_columns<CPL, RHT, SR, true>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
+    encode_columns<CPL, RHT, SR, true, FAST>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
   else
-    encode_columns<CPL, RHT, SR, false>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
+    encode_columns<CPL, RHT, SR, false, FAST>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
 }
 
 // Write-out of a staged item: plane rows of column tile ctile, blocks
@@ -438,7 +444,7 @@ __device__ __forceinline__ void write_item(const Stage<CPL>& st, uint32_t ctile,
   }
 }
 
-template <int CPL, bool RHT, bool SR>
+template <int CPL, bool RHT, bool SR, bool FAST>
 __global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(
     const uint16_t* __restrict__ x, int rows, uint32_t cols, int64_t ld_x, const int32_t* __restrict__ offsets,
     int groups, uint32_t mask, uint8_t* __restrict__ codes, int64_t ldc, uint8_t* __restrict__ scales, int64_t lds,
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(
     GroupTabs gt;
     gt.g0 = -1;
     gt.g1 = -1;
-    encode_item<CPL, RHT, SR>(it, r, mask, amax_in ? amax_in : ws->partial + kGroupAmax, gt, &rcp_tab[wid][0][0],
+    encode_item<CPL, RHT, SR, FAST>(it, r, mask, amax_in ? amax_in : ws->partial + kGroupAmax, gt, &rcp_tab[wid][0][0],
                               stage, mpad, seed, offset);
   }
   __syncthreads();
@@ -507,35 +513,37 @@ Geo geo_of(int64_t cols, uint32_t nb_max) {
   return g;
 }
 
-template <int CPLA, bool RHT>
+template <int CPLA, bool RHT, bool FAST>
 void launch_amax(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
   const Geo g = geo_of<CPLA>(a.cols, nb_max);
-  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT>), g.grid, dim3(kT), 0, s, (const uint16_t*)a.x, (int)a.rows,
+  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT, FAST>), g.grid, dim3(kT), 0, s, (const uint16_t*)a.x, (int)a.rows,
                      (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.ws, g.nq, g.ntc, g.npairs, nb_max,
                      g.chunk);
   hipLaunchKernelGGL(k_grouped_reduce, dim3(a.groups), dim3(kReduceThreads), 0, s, a.offsets, a.groups, (int)a.rows,
                      a.ws, g.ntc, nb_max * g.ntc, a.amax_out, a.scale_out);
 }
 
-template <int CPLE, bool RHT, bool SR>
+template <int CPLE, bool RHT, bool SR, bool FAST>
 void launch_quant(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
   const int64_t cap = a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16;
   const uint32_t npairs = (nb_max + 1) / 2 < 1 ? 1 : (nb_max + 1) / 2;
   const uint32_t nbg = (npairs + kQuantWaves - 1) / kQuantWaves;  // items per column tile
   const uint32_t ntc = tiles_of<CPLE>(a.cols);
   const uint32_t chunk = xcd_chunk((uint64_t)nbg * ntc);
-  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR>), dim3(xcd_grid((uint64_t)nbg * ntc)), dim3(kQuantThreads), 0,
-                     s, (const uint16_t*)a.x, (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask,
-                     a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in, a.amax_out, a.scale_out, a.poff_out, a.seed,
-                     a.offset, cap, nbg, ntc, npairs, chunk);
+  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR, FAST>), dim3(xcd_grid((uint64_t)nbg * ntc)),
+                     dim3(kQuantThreads), 0, s, (const uint16_t*)a.x, (int)a.rows, (uint32_t)a.cols, a.ld_x,
+                     a.offsets, a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in, a.amax_out,
+                     a.scale_out, a.poff_out, a.seed, a.offset, cap, nbg, ntc, npairs, chunk);
 }
 
-template <bool RHT>
+// FAST (no bf16 round-through of the transform's output) exists only with
+// the transform.
+template <bool RHT, bool FAST>
 void launch_grouped_r(const GroupArgs& a, hipStream_t s) {
   const uint32_t nb_max = (uint32_t)grouped_blocks(a.rows, a.groups);
-  if (!a.amax_in) launch_amax<kCplAmax, RHT>(a, nb_max, s);
-  if (a.sr) launch_quant<kCplQuant, RHT, true>(a, nb_max, s);
-  else launch_quant<kCplQuant, RHT, false>(a, nb_max, s);
+  if (!a.amax_in) launch_amax<kCplAmax, RHT, FAST>(a, nb_max, s);
+  if (a.sr) launch_quant<kCplQuant, RHT, true, FAST>(a, nb_max, s);
+  else launch_quant<kCplQuant, RHT, false, FAST>(a, nb_max, s);
 }
 
 }  // namespace
@@ -547,8 +555,9 @@ int64_t grouped_partials(int64_t rows, int64_t cols, int groups) {
 }
 
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {
-  if (a.rht) launch_grouped_r<true>(a, s);
-  else launch_grouped_r<false>(a, s);
+  if (a.rht && a.fast) launch_grouped_r<true, true>(a, s);
+  else if (a.rht) launch_grouped_r<true, false>(a, s);
+  else launch_grouped_r<false, false>(a, s);
   return hipGetLastError();
 }
 

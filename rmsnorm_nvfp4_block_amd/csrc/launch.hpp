@@ -70,6 +70,7 @@ struct GroupArgs {
   float* amax_out;
   float* scale_out;
   bool sr;
+  bool fast;  // fast math: no bf16 round-through of the transform's output
   uint64_t seed;
   uint32_t offset;
 };

@@ -140,3 +140,22 @@ def test_2d_and_grouped_validation(lib):
     assert grouped(ldc=48) == 2       # 2 * 48 < 64 + 15 * 4
     assert grouped(lds=7) == 2        # 16 * 7 < 124
     assert grouped(ld=(1 << 24) + 8) == 2   # row stride past the 32-bit offsets of the loads
+
+
+def test_rounding_option_bits(lib):
+    import rmsnorm_nvfp4_block_amd as q
+
+    hdr = open(os.path.join(ROOT, "include", "nvfp4q.h")).read()
+    assert "#define NVFP4Q_FAST_MATH 0x100" in hdr and q.FAST_MATH == 0x100
+    g = q.Global(None, None, None)
+    r = q.Rng(0, 0)
+
+    def grouped(rounding):
+        p = q.Plane(FAKE, 64, FAKE, 8)
+        # a workspace smaller than required: accepted rounding values pass their check and stop at the
+        # workspace check (6); others stop at the rounding check (4). Nothing is launched.
+        return lib.nvfp4q_grouped(FAKE, 0, 64, 32, 32, FAKE, 4, None, 1, 0x1234, ctypes.byref(g),
+                                  ctypes.byref(p), rounding, ctypes.byref(r), FAKE, 1 << 16, None)
+
+    assert grouped(q.RTNE | q.FAST_MATH) == 6 and grouped(q.SR | q.FAST_MATH) == 6
+    assert grouped(2) == 4 and grouped(0x200) == 4 and grouped(q.SR | 0x200) == 4

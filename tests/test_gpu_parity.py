@@ -290,7 +290,8 @@ def test_2d_weight_8192x8192_sampled(gpu_lib):
 
 
 # ---------------------------------------------------------------- grouped
-def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offset=2, groups=None, amax=None):
+def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offset=2, groups=None, amax=None,
+                   fast_math=False):
     import torch
 
     T, C = x.shape
@@ -302,10 +303,10 @@ def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offs
     a = None if amax is None else torch.tensor(amax, dtype=torch.float32, device="cuda")
     got = gpu_lib.nvfp4q_grouped(to_dev(x), torch.tensor(offsets, dtype=torch.int32, device="cuda"),
                                  apply_rht=apply_rht, rht_mask=mask, amax=a, rounding=rounding, seed=seed,
-                                 offset=offset, codes=codes, scales=scales)
+                                 offset=offset, codes=codes, scales=scales, fast_math=fast_math)
     ref = oracle.grouped_quantize(x, np.asarray(offsets, np.int32), apply_rht=apply_rht, rht_mask=mask,
                                   amax=None if amax is None else np.asarray(amax, np.float32),
-                                  rounding=rounding, seed=seed, offset=offset, groups=groups)
+                                  rounding=rounding, seed=seed, offset=offset, groups=groups, fast_math=fast_math)
     poff = ref["poff"]
     mpad = int(poff[-1])
     assert np.array_equal(got["poff"].cpu().numpy(), poff)
@@ -347,6 +348,27 @@ def test_grouped_extreme_group_scales(gpu_lib, rounding):
     x = np.concatenate(parts, axis=0)
     offsets = np.concatenate([[0], np.cumsum([p.shape[0] for p in parts])]).tolist()
     _grouped_check(gpu_lib, x, offsets, True, 0x6A5C, rounding)
+
+
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_grouped_fast_math(gpu_lib, rounding):
+    # NVFP4Q_FAST_MATH: the transform's fp32 output, without its bf16 round-through (reading R-fast),
+    # bit-exact against the oracle's fast mode; ragged groups, an empty group, a given amax, and groups
+    # outside the folding range of the encode.
+    rng = np.random.default_rng(16)
+    x = _bf16(rng, (203, 272))
+    _grouped_check(gpu_lib, x, [0, 0, 5, 21, 21, 150, 203], True, 0x9C35, rounding, fast_math=True)
+    _grouped_check(gpu_lib, x, [0, 7, 203], True, 0x0F0F, rounding, amax=[1.5, 30.0], fast_math=True)
+    parts = [_bf16(rng, (40, 288), 1e-30), _bf16(rng, (37, 288)), _bf16(rng, (50, 288), 1e37)]
+    x = np.concatenate(parts, axis=0)
+    _grouped_check(gpu_lib, x, [0, 40, 77, 127], True, 0x6A5C, rounding, fast_math=True)
+
+
+def test_grouped_moe_16384x7168_fast_math_sampled(gpu_lib):
+    w = workloads.grouped_moe()
+    G = len(w.offsets) - 1
+    _grouped_check(gpu_lib, w.x, w.offsets.tolist(), w.apply_rht, w.rht_mask, "sr", seed=w.seed,
+                   offset=w.offset, groups=[3, 33, G - 2], fast_math=True)
 
 
 def test_grouped_64_groups_many_empty(gpu_lib):
