@@ -51,6 +51,9 @@ that implements it. Readings are:
              amax without the bf16 round-through; the encode reciprocal stays
              RN(1 / RN(f32(s) * S_dec)) (on this hardware it comes from a
              127-entry table, so an approximate reciprocal would save nothing).
+  R-rowcol   grouped rowwise + columnwise: the rowwise plane of x's rows,
+             no transform, one amax per group (max|x| over its rows), SR tag
+             0 with block index row * (K/16) + k/16 in x's row numbering.
   R-group    each group is zero-padded to a multiple of 16 rows, groups are
              laid out back to back in one transposed plane; storage past the
              last padded column is never written.

@@ -22,7 +22,7 @@ import numpy as np
 
 from .formats import bf16_to_f32, pack_nibbles
 from .philox import block_random_bytes
-from .quantize import global_scales, quantize_blocks
+from .quantize import global_scales, quantize_blocks, quantize_rowwise
 from .rht import rht16, rht16_f32
 
 MAX_GROUPS = 64
@@ -40,7 +40,7 @@ def padded_offsets(offsets) -> np.ndarray:
 
 
 def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr",
-                     seed=0, offset=0, groups=None, fast_math=False):
+                     seed=0, offset=0, groups=None, fast_math=False, rowwise=False, row_amax=None):
     """Reference for the grouped columnwise path.
 
     x: bf16 bits [total_rows, K]. offsets: int32 [G+1]. amax: optional float32 [G].
@@ -48,6 +48,11 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
     columns of other groups are left as 0 in the returned planes.
     fast_math: PR, Fast math -- the transform's output enters the amax and the
     quantization in float32, without the bf16 round-through (reading R-fast).
+    rowwise: also the rowwise plane of the same input (reading R-rowcol): each
+    group's rows quantized rowwise, without the transform, under the group's own
+    amax max|x| (row_amax: optional float32 [G] given instead); SR tag 0, block
+    index row * (K/16) + k/16 with the row's index in x. Adds row_codes
+    [total_rows, K/2], row_scales [total_rows, K/16], row_amax, row_s_dec [G].
     Returns dict with codes [K, Mpad/2], scales [K, Mpad/16], amax [G], s_enc [G],
     s_dec [G], poff [G+1].
     """
@@ -91,5 +96,23 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
         c, sc = quantize_blocks(zf, s_enc, s_dec, rounding, rb)
         codes[:, poff[g] // 2:(poff[g] + pg) // 2] = pack_nibbles(c.reshape(K, pg))
         scales[:, poff[g] // 16:(poff[g] + pg) // 16] = sc
-    return {"codes": codes, "scales": scales, "amax": amax_out, "s_enc": s_enc_out,
-            "s_dec": s_dec_out, "poff": poff.astype(np.int32)}
+    out = {"codes": codes, "scales": scales, "amax": amax_out, "s_enc": s_enc_out,
+           "s_dec": s_dec_out, "poff": poff.astype(np.int32)}
+    if rowwise:
+        row_codes = np.zeros((T, K // 2), dtype=np.uint8)
+        row_scales = np.zeros((T, K // 16), dtype=np.uint8)
+        ra_out = np.zeros(G, dtype=np.float32)
+        rd_out = np.ones(G, dtype=np.float32)
+        for g in sel:
+            lo, hi = int(off[g]), int(off[g + 1])
+            seg = x[lo:hi]
+            a = (np.float32(np.max(np.abs(bf16_to_f32(seg)))) if hi > lo else np.float32(0.0)) \
+                if row_amax is None else np.float32(np.asarray(row_amax, dtype=np.float32)[g])
+            ra_out[g] = a
+            rd_out[g] = global_scales(a)[1]
+            if hi > lo:
+                q = quantize_rowwise(seg, amax=a, rounding=rounding, seed=seed, offset=offset, tag=0,
+                                     row_ids=np.arange(lo, hi))
+                row_codes[lo:hi], row_scales[lo:hi] = q["codes"], q["scales"]
+        out.update({"row_codes": row_codes, "row_scales": row_scales, "row_amax": ra_out, "row_s_dec": rd_out})
+    return out

@@ -178,3 +178,34 @@ def test_fast_math_codes_stay_within_one_step_of_exact():
     plain = grouped_quantize(x, offsets, apply_rht=False, rounding="rtne")
     plain_f = grouped_quantize(x, offsets, apply_rht=False, rounding="rtne", fast_math=True)
     assert np.array_equal(plain["codes"], plain_f["codes"])
+
+
+# ---------------------------------------------------------------- R-rowcol (rowwise plane of the grouped input)
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_grouped_rowwise_single_group_is_the_rowwise_quantizer(rounding):
+    rng = np.random.default_rng(46)
+    x = F.f32_to_bf16((rng.standard_normal((53, 80)) * 2).astype(np.float32))
+    ref = Q.quantize_rowwise(x, rounding=rounding, seed=11, offset=5)
+    got = grouped_quantize(x, np.array([0, 53], np.int32), apply_rht=True, rht_mask=0x77, rounding=rounding,
+                           seed=11, offset=5, rowwise=True)
+    assert np.array_equal(got["row_codes"], ref["codes"]) and np.array_equal(got["row_scales"], ref["scales"])
+    assert got["row_amax"][0] == ref["amax"] and got["row_s_dec"][0] == ref["s_dec"]
+
+
+def test_grouped_rowwise_uses_each_groups_own_amax_and_ignores_the_transform():
+    rng = np.random.default_rng(47)
+    parts = [rng.standard_normal((9, 48)) * s for s in (1.0, 1e3, 1e-3)]
+    x = F.f32_to_bf16(np.concatenate(parts).astype(np.float32))
+    offsets = np.array([0, 9, 9, 18, 27], np.int32)                      # an empty group in the middle
+    a = grouped_quantize(x, offsets, apply_rht=True, rht_mask=0x1, rounding="sr", seed=4, rowwise=True)
+    b = grouped_quantize(x, offsets, apply_rht=False, rounding="sr", seed=4, rowwise=True)
+    for k in ("row_codes", "row_scales", "row_amax", "row_s_dec"):
+        assert np.array_equal(a[k], b[k]), k
+    xf = F.bf16_to_f32(x)
+    assert a["row_amax"][1] == 0 and a["row_s_dec"][1] == 1
+    for g, (lo, hi) in enumerate(zip(offsets[:-1], offsets[1:])):
+        if hi > lo:
+            assert a["row_amax"][g] == np.max(np.abs(xf[lo:hi]))
+            # a block holding its group's amax gets the saturating scale code 0x7E (448)
+            r, c = np.unravel_index(np.argmax(np.abs(xf[lo:hi])), xf[lo:hi].shape)
+            assert a["row_scales"][lo + r, c // 16] == 0x7E
