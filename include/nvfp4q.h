@@ -192,31 +192,41 @@ nvfp4q_status nvfp4q_quantize_2d(const void *x, nvfp4q_dtype dtype, int64_t rows
                                  void *stream);
 
 /*
- * nvfp4q_grouped -- per-group columnwise NVFP4 of a packed [total_rows, cols]
- * bf16 tensor, optionally after a 16-point random Hadamard transform along
- * the rows of each 16-row block.
+ * nvfp4q_grouped -- per-group NVFP4 of a packed [total_rows, cols] bf16
+ * tensor: the columnwise plane, optionally after a 16-point random Hadamard
+ * transform along the rows of each 16-row block, and/or the rowwise plane,
+ * each with one global scale per group, from one read of x.
  *   offsets: device int32 [num_groups + 1]; offsets[0] = 0, non-decreasing,
  *     offsets[num_groups] = total_rows; group g is rows offsets[g] ..
  *     offsets[g+1] - 1. 1 <= num_groups <= 64.
- *   Each group is zero-padded to P_g = 16 * ceil(n_g / 16) rows; padded
- *   groups are laid out back to back: group g owns plane columns
+ *   Columnwise: each group is zero-padded to P_g = 16 * ceil(n_g / 16) rows;
+ *   padded groups are laid out back to back: group g owns plane columns
  *   Poff[g] .. Poff[g] + P_g - 1, Poff = exclusive prefix sum of P_g.
  *   padded_offsets_out: device int32 [num_groups + 1] receives Poff (nullable).
  *   apply_rht: 0 or 1. With 1, each 16-row block of one column becomes
  *     bf16_rne(0.25 * H16 * D * v): D = diag(d), d_i = -1 iff bit i of
  *     rht_sign_mask is set, H16 the Sylvester Hadamard matrix evaluated as
  *     four butterfly stages (h = 1, 2, 4, 8) of fp32 (a + b, a - b).
- *     The transform and the per-group amax see the zero-padded rows.
- *   g: G floats each (amax_in optional, amax_out, scale_out).
- *   col: the columnwise plane, `cols` plane rows; ld_codes * 2 and
+ *     The transform and the columnwise amax see the zero-padded rows. With
+ *     NVFP4Q_FAST_MATH in `rounding` the bf16 rounding is left out.
+ *   g, col: the columnwise scales (G floats each: amax_in optional, amax_out,
+ *     scale_out; g nullable) and plane, `cols` plane rows; ld_codes * 2 and
  *     ld_scales * 16 must be >= total_rows + 15 * num_groups (the largest
  *     possible padded length). Plane columns at and past Poff[G] are never
- *     written [PR, Grouped allocation tail].
- *   SR: tag 1, block index = plane_row * (Poff[G] / 16) + plane_col / 16.
- *   Without amax_in the amax pass keeps one partial per 16-row block x
- *   256-column tile; shapes needing more slots than the workspace holds
- *   (floor((total_rows + 15 G) / 16) * ceil(cols / 256) > 262112) return
- *   NVFP4Q_E_UNSUPPORTED.
+ *     written [PR, Grouped allocation tail]. col NULL (or col->codes NULL):
+ *     no columnwise plane.
+ *   g_row, row: the rowwise scales (G floats each, nullable) and plane
+ *     ([total_rows, cols/2] codes, [total_rows, cols/16] scales), as
+ *     nvfp4q_quantize of each group's rows under the group's own amax
+ *     max|x| (no transform) [PR, Performance (grouped rowwise + columnwise
+ *     in one pass)]. row NULL (or row->codes NULL while total_rows > 0):
+ *     no rowwise plane. At least one plane must be given.
+ *   SR: columnwise tag 1, block index = plane_row * (Poff[G] / 16) +
+ *   plane_col / 16; rowwise tag 0, block index = row * (cols / 16) + col / 16.
+ *   Without amax_in (for a requested plane) the amax pass keeps one partial
+ *   per 16-row block x 128-column tile and plane; shapes needing more slots
+ *   than the workspace holds (planes * floor((total_rows + 15 G) / 16) *
+ *   ceil(cols / 128) + 128 > 262112) return NVFP4Q_E_UNSUPPORTED.
  *   ld_x above 2^24 returns NVFP4Q_E_SHAPE (the kernels address 32 rows of x
  *   with 32-bit byte offsets).
  *   [PR, Optimization 2, 3, 5; Fast math (bf16 round-through of the
@@ -226,6 +236,7 @@ nvfp4q_status nvfp4q_grouped(const void *x, nvfp4q_dtype dtype, int64_t total_ro
                              int64_t ld_x, const int32_t *offsets, int32_t num_groups,
                              int32_t *padded_offsets_out, int apply_rht, uint32_t rht_sign_mask,
                              const nvfp4q_global *g, const nvfp4q_plane *col,
+                             const nvfp4q_global *g_row, const nvfp4q_plane *row,
                              nvfp4q_rounding rounding, const nvfp4q_rng *rng, void *workspace,
                              size_t workspace_bytes, void *stream);
 

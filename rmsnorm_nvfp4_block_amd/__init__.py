@@ -73,7 +73,7 @@ def load():
                                        P(Rng), vp, ctypes.c_size_t, vp]
     lib.nvfp4q_grouped.restype = ctypes.c_int
     lib.nvfp4q_grouped.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, ctypes.c_int, u32, P(Global),
-                                   P(Plane), ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
+                                   P(Plane), P(Global), P(Plane), ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -215,37 +215,60 @@ def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=
 
 
 def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr", seed=0, offset=0,
-                   codes=None, scales=None, fast_math=False):
-    """Per-group columnwise NVFP4 (optionally after the 16-point RHT) of bf16 x [total_rows, cols].
+                   codes=None, scales=None, fast_math=False, colwise=True, rowwise=False, row_amax=None,
+                   row_codes=None, row_scales=None):
+    """Per-group NVFP4 of bf16 x [total_rows, cols]: the columnwise plane (optionally
+    after the 16-point RHT) and/or the rowwise plane (no transform), one amax per
+    group and plane.
 
-    offsets: int32 CUDA tensor [G+1]. The plane is allocated for the largest padded
-    length (total_rows + 15 G) unless given. fast_math: NVFP4Q_FAST_MATH (the transform's
-    output is quantized without its bf16 round-through). Returns dict(codes, scales, amax,
-    scale, poff).
+    offsets: int32 CUDA tensor [G+1]. The columnwise plane is allocated for the largest
+    padded length (total_rows + 15 G) unless given. fast_math: NVFP4Q_FAST_MATH (the
+    transform's output is quantized without its bf16 round-through). row_amax: the
+    rowwise plane's per-group amax (computed when None). Returns dict(codes, scales, amax,
+    scale, poff) for the columnwise plane and row_codes, row_scales, row_amax, row_scale
+    for the rowwise one (None where a plane is not asked for).
     """
     import torch
 
     _check_bf16_2d(x)
     if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1:
         raise ValueError("offsets must be a 1-D int32 CUDA tensor")
+    if not colwise and not rowwise:
+        raise ValueError("ask for at least one plane")
     lib = load()
     T, C = x.shape
     G = offsets.numel() - 1
-    cap = T + 15 * G
-    cap16 = (cap + 15) // 16 * 16
-    if codes is None:
-        codes = torch.empty((C, (cap16 // 2 + 15) // 16 * 16), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((C, cap16 // 16), dtype=torch.uint8, device=x.device)
-    plane = Plane(codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0))
-    amax_out = torch.empty(G, dtype=torch.float32, device=x.device)
-    scale_out = torch.empty(G, dtype=torch.float32, device=x.device)
+    amax_out = scale_out = ramax_out = rscale_out = rc = rs = None
+    plane = rplane = None
+    if colwise:
+        cap = T + 15 * G
+        cap16 = (cap + 15) // 16 * 16
+        if codes is None:
+            codes = torch.empty((C, (cap16 // 2 + 15) // 16 * 16), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            scales = torch.empty((C, cap16 // 16), dtype=torch.uint8, device=x.device)
+        plane = Plane(codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0))
+        amax_out = torch.empty(G, dtype=torch.float32, device=x.device)
+        scale_out = torch.empty(G, dtype=torch.float32, device=x.device)
+    else:
+        codes = scales = None
+    if rowwise:
+        rc, rs, rplane = _plane(T, C, x.device, row_codes, row_scales)
+        ramax_out = torch.empty(G, dtype=torch.float32, device=x.device)
+        rscale_out = torch.empty(G, dtype=torch.float32, device=x.device)
     poff = torch.empty(G + 1, dtype=torch.int32, device=x.device)
     ws = workspace(x.device)
+    gcol = _global(amax, amax_out, scale_out) if colwise else None
+    grow = _global(row_amax, ramax_out, rscale_out) if rowwise else None
     st = lib.nvfp4q_grouped(x.data_ptr(), 0, T, C, x.stride(0), offsets.data_ptr(), G, poff.data_ptr(),
-                            1 if apply_rht else 0, int(rht_mask), ctypes.byref(_global(amax, amax_out, scale_out)),
-                            ctypes.byref(plane), _rounding(rounding) | (FAST_MATH if fast_math else 0),
+                            1 if apply_rht else 0, int(rht_mask),
+                            ctypes.byref(gcol) if gcol is not None else None,
+                            ctypes.byref(plane) if plane is not None else None,
+                            ctypes.byref(grow) if grow is not None else None,
+                            ctypes.byref(rplane) if rplane is not None else None,
+                            _rounding(rounding) | (FAST_MATH if fast_math else 0),
                             ctypes.byref(Rng(seed, offset)),
                             ws.data_ptr(), ws.numel(), _stream(x))
     _check(st)
-    return {"codes": codes, "scales": scales, "amax": amax_out, "scale": scale_out, "poff": poff}
+    return {"codes": codes, "scales": scales, "amax": amax_out, "scale": scale_out, "poff": poff,
+            "row_codes": rc, "row_scales": rs, "row_amax": ramax_out, "row_scale": rscale_out}

@@ -212,28 +212,42 @@ nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows
 nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_rows, int64_t cols, int64_t ld_x,
                              const int32_t* offsets, int32_t num_groups, int32_t* padded_offsets_out,
                              int apply_rht, uint32_t rht_sign_mask, const nvfp4q_global* g,
-                             const nvfp4q_plane* col, nvfp4q_rounding rounding, const nvfp4q_rng* rng,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             const nvfp4q_plane* col, const nvfp4q_global* g_row, const nvfp4q_plane* row,
+                             nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   TRY(check_input(x, dtype, total_rows, cols, ld_x));
-  if (!offsets || !col) return NVFP4Q_E_NULLPTR;
+  // an empty rowwise plane (no rows) may come with NULL pointers
+  const bool want_col = col && col->codes, want_row = row && (row->codes || total_rows == 0);
+  if (!offsets || (!want_col && !want_row)) return NVFP4Q_E_NULLPTR;
   if (num_groups < 1 || num_groups > 64) return NVFP4Q_E_SHAPE;
   if (apply_rht != 0 && apply_rht != 1) return NVFP4Q_E_UNSUPPORTED;
   if (rht_sign_mask > 0xFFFFu) return NVFP4Q_E_UNSUPPORTED;
   if (ld_x > kGroupedMaxLd) return NVFP4Q_E_SHAPE;
   const int64_t cap = total_rows + 15 * (int64_t)num_groups;
-  TRY(check_plane(col, cols, 0));
-  if (col->ld_codes * 2 < cap || col->ld_scales * 16 < cap) return NVFP4Q_E_SHAPE;
+  if (want_col) {
+    TRY(check_plane(col, cols, 0));
+    if (col->ld_codes * 2 < cap || col->ld_scales * 16 < cap) return NVFP4Q_E_SHAPE;
+  }
+  if (want_row) TRY(check_plane(row, total_rows, cols));
   TRY(check_rounding(rounding, rng));
   TRY(check_ws(workspace, workspace_bytes));
-  if (!(g && g->amax_in) && grouped_partials(total_rows, cols, num_groups) > kPartials) return NVFP4Q_E_UNSUPPORTED;
   const nvfp4q_global& gg = g ? *g : kNoGlobal;
+  const nvfp4q_global& gr = g_row ? *g_row : kNoGlobal;
+  const bool col_amax = want_col && !gg.amax_in, row_amax = want_row && !gr.amax_in;
+  if ((col_amax || row_amax) &&
+      grouped_partials(total_rows, cols, num_groups, (col_amax ? 1 : 0) + (row_amax ? 1 : 0)) > kPartials)
+    return NVFP4Q_E_UNSUPPORTED;
   GroupArgs a = {};
   a.x = x; a.rows = total_rows; a.cols = cols; a.ld_x = ld_x;
   a.offsets = offsets; a.groups = num_groups; a.poff_out = padded_offsets_out;
   a.rht = apply_rht != 0; a.mask = rht_sign_mask;
-  a.codes = col->codes; a.ldc = col->ld_codes; a.scales = col->scales; a.lds = col->ld_scales;
-  a.ws = (Workspace*)workspace;
+  a.col = want_col;
+  if (want_col) { a.codes = col->codes; a.ldc = col->ld_codes; a.scales = col->scales; a.lds = col->ld_scales; }
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
+  a.row = want_row;
+  if (want_row) { a.rcodes = row->codes; a.rldc = row->ld_codes; a.rscales = row->scales; a.rlds = row->ld_scales; }
+  a.ramax_in = gr.amax_in; a.ramax_out = gr.amax_out; a.rscale_out = gr.scale_out;
+  a.ws = (Workspace*)workspace;
   a.sr = base_rounding(rounding) == NVFP4Q_SR;
   a.fast = fast_math(rounding);
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;

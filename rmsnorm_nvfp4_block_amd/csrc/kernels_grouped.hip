@@ -42,8 +42,9 @@ constexpr int kWaves = kT / 64;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // Workspace slots of the per-group amax written by the reduce kernel (after
-// the amax pass's partials).
-constexpr int kGroupAmax = kPartials - 64;
+// the amax pass's partials): columnwise, then rowwise.
+constexpr int kGroupAmax = kPartials - 128;
+constexpr int kGroupAmaxRow = kPartials - 64;
 
 // Per-group layout, one group per lane of a wave (lanes >= groups hold empty
 // groups): first row in x, real and padded length, and the inclusive prefix
@@ -227,13 +228,23 @@ __device__ __forceinline__ float half_wave_max(float m) {
   return m;
 }
 
-// Pass 1: per-(block, column tile) maximum of the (transformed,
-// bf16-rounded) columnwise values, into partial[tb * ntc + ctile].
-template <int CPL, bool RHT, bool FAST>
+// Magnitude bits of the larger of two bf16 per half (sign bits cleared: for
+// finite values the u16 order of |x| is the order of the magnitudes).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_mag(uint32_t acc, uint32_t w) {
+  const u16x2 m = __builtin_elementwise_max(__builtin_bit_cast(u16x2, acc), __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
+  return __builtin_bit_cast(uint32_t, m);
+}
+
+// Pass 1: per-(block, column tile) maxima. COL: of the (transformed,
+// bf16-rounded) columnwise values, into partial[tb * ntc + ctile]. ROW: of
+// |x| itself (the rowwise plane has no transform), into partial[rbase + tb *
+// ntc + ctile].
+template <int CPL, bool RHT, bool FAST, bool COL, bool ROW>
 __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict__ x, int rows, uint32_t cols,
                                                      int64_t ld_x, const int32_t* __restrict__ offsets, int groups,
                                                      uint32_t mask, Workspace* ws, uint32_t nq, uint32_t ntc,
-                                                     uint32_t npairs, uint32_t nb_max, uint32_t chunk) {
+                                                     uint32_t npairs, uint32_t nb_max, uint32_t chunk, uint32_t rbase) {
   const uint32_t v = xcd_work_item(chunk);
   if (v >= nq * ntc) return;
   uint32_t ctile, pair;
@@ -244,57 +255,86 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
   const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
   Tile<CPL> r;
   load_item<CPL>(x, ld_x, rows, it, true, r);
-  if constexpr (RHT) apply_signs<CPL>(r, mask);
-  float m = 0.0f;
+  const bool writer = (threadIdx.x & 31) == 0 && it.tb < nb_max;
+  if constexpr (ROW) {
+    uint32_t mm = 0;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    float v[16];
-    column<CPL>(r, c, v);
-    if constexpr (RHT) {
-      // The last stage only feeds the maximum: max(|RN(a + b)|, |RN(a - b)|)
-      // = RN(|a| + |b|), since one of a + b, a - b has magnitude |a| + |b|,
-      // the other at most that, and rounding is odd and monotone.
-      fwht16<3>(v);
-      float s8[8];
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s8[i] = fabsf(v[i]) + fabsf(v[i + 8]);
-      m = fmaxf(m, max8_abs(s8));
-    } else {
-      m = fmaxf(m, max16_abs(v));
-    }
+      for (int j = 0; j < CPL / 2; ++j) mm = pk_max_mag(mm, r[i][j]);
+    const uint32_t hi = mm >> 16, lo = mm & 0xFFFFu;
+    const float mr = half_wave_max(__uint_as_float((hi > lo ? hi : lo) << 16));  // lanes without data: 0
+    if (writer) ws->partial[rbase + it.tb * ntc + it.ctile] = mr;
   }
-  // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
-  // round-to-nearest-even are both monotone (fast math: no bf16 rounding).
-  if constexpr (RHT) m = FAST ? m * 0.25f : bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
-  m = half_wave_max(m);  // lanes without data hold zeros
-  if ((threadIdx.x & 31) == 0 && it.tb < nb_max) ws->partial[it.tb * ntc + it.ctile] = m;
+  if constexpr (COL) {
+    if constexpr (RHT) apply_signs<CPL>(r, mask);
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float v16[16];
+      column<CPL>(r, c, v16);
+      if constexpr (RHT) {
+        // The last stage only feeds the maximum: max(|RN(a + b)|, |RN(a - b)|)
+        // = RN(|a| + |b|), since one of a + b, a - b has magnitude |a| + |b|,
+        // the other at most that, and rounding is odd and monotone.
+        fwht16<3>(v16);
+        float s8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s8[i] = fabsf(v16[i]) + fabsf(v16[i + 8]);
+        m = fmaxf(m, max8_abs(s8));
+      } else {
+        m = fmaxf(m, max16_abs(v16));
+      }
+    }
+    // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
+    // round-to-nearest-even are both monotone (fast math: no bf16 rounding).
+    if constexpr (RHT) m = FAST ? m * 0.25f : bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
+    m = half_wave_max(m);  // lanes without data hold zeros
+    if (writer) ws->partial[it.tb * ntc + it.ctile] = m;
+  }
 }
 
 // Between the passes, one workgroup per group: the maximum of the partials of
 // the group's blocks over every column tile (contiguous slots, clamped to the
-// lim slots the amax pass writes), into the workspace for the encode pass and
-// into amax_out / scale_out. Empty groups get 0.
+// lim slots per plane the amax pass writes), into the workspace for the encode
+// pass and into amax_out / scale_out (rowwise: from rbase on, into ramax_out /
+// rscale_out). Empty groups get 0.
 constexpr int kReduceThreads = 512;
+template <bool COL, bool ROW>
 __global__ __launch_bounds__(kReduceThreads) void k_grouped_reduce(const int32_t* __restrict__ offsets, int groups,
                                                                    int rows, Workspace* ws, uint32_t ntc,
-                                                                   uint32_t lim, float* amax_out, float* scale_out) {
+                                                                   uint32_t lim, uint32_t rbase, float* amax_out,
+                                                                   float* scale_out, float* ramax_out,
+                                                                   float* rscale_out) {
   const int g = blockIdx.x;
   const GroupScan q = group_scan(offsets, groups, rows);
   const uint32_t lo = min(((uint32_t)lane_int(q.ps - q.p, g) >> 4) * ntc, lim);
   const uint32_t n = min(((uint32_t)lane_int(q.p, g) >> 4) * ntc, lim - lo);
-  const float* src = ws->partial + lo;
-  float m = 0.0f;
-  for (uint32_t i = threadIdx.x; i < n; i += 4 * kReduceThreads) {
-    float t[4];
+  auto reduce = [&](const float* src) {
+    float m = 0.0f;
+    for (uint32_t i = threadIdx.x; i < n; i += 4 * kReduceThreads) {
+      float t[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) t[u] = i + u * kReduceThreads < n ? src[i + u * kReduceThreads] : 0.0f;
-    m = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
+      for (int u = 0; u < 4; ++u) t[u] = i + u * kReduceThreads < n ? src[i + u * kReduceThreads] : 0.0f;
+      m = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
+    }
+    return wg_max<kReduceThreads / 64>(m);
+  };
+  if constexpr (COL) {
+    const float m = reduce(ws->partial + lo);
+    if (threadIdx.x == 0) {
+      ws->partial[kGroupAmax + g] = m;
+      if (amax_out) amax_out[g] = m;
+      if (scale_out) scale_out[g] = global_scale(m).dec;
+    }
   }
-  m = wg_max<kReduceThreads / 64>(m);
-  if (threadIdx.x == 0) {
-    ws->partial[kGroupAmax + g] = m;
-    if (amax_out) amax_out[g] = m;
-    if (scale_out) scale_out[g] = global_scale(m).dec;
+  if constexpr (ROW) {
+    const float m = reduce(ws->partial + rbase + lo);
+    if (threadIdx.x == 0) {
+      ws->partial[kGroupAmaxRow + g] = m;
+      if (ramax_out) ramax_out[g] = m;
+      if (rscale_out) rscale_out[g] = global_scale(m).dec;
+    }
   }
 }
 
@@ -444,44 +484,121 @@ __device__ __forceinline__ void write_item(const Stage<CPL>& st, uint32_t ctile,
   }
 }
 
-template <int CPL, bool RHT, bool SR, bool FAST>
-__global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(
-    const uint16_t* __restrict__ x, int rows, uint32_t cols, int64_t ld_x, const int32_t* __restrict__ offsets,
-    int groups, uint32_t mask, uint8_t* __restrict__ codes, int64_t ldc, uint8_t* __restrict__ scales, int64_t lds,
-    const Workspace* ws, const float* amax_in, float* amax_out, float* scale_out, int32_t* poff_out, uint64_t seed,
-    uint32_t offset, int64_t cap, uint32_t nbg, uint32_t ntc, uint32_t npairs, uint32_t chunk) {
+// Rowwise plane from the lane's raw tile (before the transform's signs): token
+// row t of the lane's block is columns col .. col + 7 of x row row_first + t,
+// and with the neighbouring lane (lane ^ 1) it forms the 16-column block at
+// columns col & ~15. Both lanes take the block maximum through a DPP swap and
+// encode their own 8 elements (4 code bytes each; the even lane stores the
+// scale). SR: for the token pair (i, i + 8) the even lane draws block i and the
+// odd lane block i + 8, and each passes the other the two Philox words it needs
+// (elements 0..7 of a block use words 0 and 1, elements 8..15 words 2 and 3).
+template <bool SR>
+__device__ __forceinline__ void encode_rows(const Tile<8>& r, uint32_t col, bool ok, int row_first, int left,
+                                            const float* tab, float enc, uint32_t cols,
+                                            uint8_t* __restrict__ rcodes, int64_t rldc,
+                                            uint8_t* __restrict__ rscales, int64_t rlds, uint64_t seed,
+                                            uint32_t offset) {
+  const bool odd = threadIdx.x & 1;
+  const uint32_t kb = col >> 4, nbr = cols >> 4;  // the block's index in its row; blocks per row
+  uint8_t* cp = rcodes + (int64_t)row_first * rldc + (col >> 1);
+  uint8_t* sp = rscales + (int64_t)row_first * rlds + kb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t wa[2], wb[2];  // words for tokens i and i + 8
+    if constexpr (SR) {
+      const U4 w = block_random((uint64_t)(row_first + i + (odd ? 8 : 0)) * nbr + kb, 0, seed, offset);
+      const uint32_t ga = swap_pair_u(odd ? w.x : w.z), gb = swap_pair_u(odd ? w.y : w.w);
+      wa[0] = odd ? ga : w.x;
+      wb[0] = odd ? gb : w.y;
+      wa[1] = odd ? w.z : ga;
+      wb[1] = odd ? w.w : gb;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = i + 8 * h;
+      float v[8];
+      widen8(make_uint4(r[t][0], r[t][1], r[t][2], r[t][3]), v);
+      float m = max8_abs(v);
+      m = fmaxf(m, swap_pair(m));
+      const uint32_t sc = block_scale(m, enc);
+      const float rc = tab[sc];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = v[e] * rc;
+      uint32_t code;
+      if constexpr (SR) code = sr_pack8(v, wa[h], wb[h]);
+      else code = rtne_pack8(v);
+      if (ok && t < left) {
+        *reinterpret_cast<uint32_t*>(cp + (int64_t)t * rldc) = code;
+        if (!odd) sp[(int64_t)t * rlds] = (uint8_t)sc;
+      }
+    }
+  }
+}
+
+// Encode kernel. COL: the columnwise plane (transform if RHT), staged and
+// written as described above. ROW: the rowwise plane (CPL 8: a lane pair
+// holds one 16-column block of each of its 16 token rows).
+template <int CPL, bool RHT, bool SR, bool FAST, bool COL, bool ROW>
+__global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(const uint16_t* __restrict__ x, const GroupArgs a,
+                                                                 const Workspace* ws, int64_t cap, uint32_t nbg,
+                                                                 uint32_t ntc, uint32_t npairs, uint32_t chunk) {
+  static_assert(!ROW || CPL == 8, "the rowwise encode pairs lanes of 8 columns");
   __shared__ __align__(16) Stage<CPL> stage;
-  __shared__ float rcp_tab[kQuantWaves][2][128];  // per wave: the tables of its two blocks' groups
-  const uint32_t lane = threadIdx.x & 63;
+  __shared__ float rcp_tab[kQuantWaves][2][128];   // per wave: columnwise tables of its two blocks' groups
+  __shared__ float rcp_row[kQuantWaves][2][128];   // per wave: rowwise tables
+  const uint32_t lane = threadIdx.x & 63, half = lane >> 5;
   const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   const uint32_t v = xcd_work_item(chunk);
   if (v >= nbg * ntc) return;  // whole workgroup
   const uint32_t ctile = v / nbg, bg = v - ctile * nbg;
   const uint32_t pair = bg * kQuantWaves + wid;
-  const GroupScan q = group_scan(offsets, groups, rows);
-  // The first wave: padded offsets, and with amax_in the groups' amax / S_dec
-  // (otherwise the reduce kernel wrote them).
-  if (v == 0 && wid == 0 && lane < (uint32_t)groups) {
-    if (amax_in != nullptr) {
-      if (amax_out) amax_out[lane] = amax_in[lane];
-      if (scale_out) scale_out[lane] = global_scale(amax_in[lane]).dec;
+  const GroupScan q = group_scan(a.offsets, a.groups, (int)rows);
+  // The first wave: padded offsets, and the groups' amax / S_dec of each plane
+  // whose amax was given (otherwise the reduce kernel wrote them).
+  if (v == 0 && wid == 0 && lane < (uint32_t)a.groups) {
+    if (COL && a.amax_in != nullptr) {
+      if (a.amax_out) a.amax_out[lane] = a.amax_in[lane];
+      if (a.scale_out) a.scale_out[lane] = global_scale(a.amax_in[lane]).dec;
     }
-    if (poff_out) poff_out[lane + 1] = q.ps;
-    if (lane == 0 && poff_out) poff_out[0] = 0;
+    if (ROW && a.ramax_in != nullptr) {
+      if (a.ramax_out) a.ramax_out[lane] = a.ramax_in[lane];
+      if (a.rscale_out) a.rscale_out[lane] = global_scale(a.ramax_in[lane]).dec;
+    }
+    if (a.poff_out) a.poff_out[lane + 1] = q.ps;
+    if (lane == 0 && a.poff_out) a.poff_out[0] = 0;
   }
   const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
   if (pair < npairs) {  // wave-uniform; every wave reaches the barrier below
-    const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
+    const Item it = item_of<CPL>(ctile, pair, q, a.groups, mpad, cols);
     Tile<CPL> r;
-    load_item<CPL>(x, ld_x, rows, it, true, r);
-    GroupTabs gt;
-    gt.g0 = -1;
-    gt.g1 = -1;
-    encode_item<CPL, RHT, SR, FAST>(it, r, mask, amax_in ? amax_in : ws->partial + kGroupAmax, gt, &rcp_tab[wid][0][0],
-                              stage, mpad, seed, offset);
+    load_item<CPL>(x, a.ld_x, (int)rows, it, true, r);
+    if constexpr (ROW) {
+      const float* gr = a.ramax_in ? a.ramax_in : ws->partial + kGroupAmaxRow;
+      const GScale s0 = global_scale(gr[it.b0.g]), s1 = global_scale(gr[it.b1.g]);
+      float* rt = &rcp_row[wid][0][0];
+      rt[lane] = encode_mult(lane, s0.dec);
+      rt[lane + 64] = encode_mult(lane + 64, s0.dec);
+      rt[128 + lane] = encode_mult(lane, s1.dec);
+      rt[128 + lane + 64] = encode_mult(lane + 64, s1.dec);
+      const int t0 = (int)(it.tb * 16u) - (half ? it.b1.start : it.b0.start);
+      const int row_first = (half ? it.b1.row0 : it.b0.row0) + t0;
+      const int left = (half ? it.b1.n : it.b0.n) - t0;  // real tokens of the lane's block
+      encode_rows<SR>(r, it.col, it.ok, row_first, left, rt + half * 128, half ? s1.enc : s0.enc, cols, a.rcodes,
+                      a.rldc, a.rscales, a.rlds, a.seed, a.offset);
+    }
+    if constexpr (COL) {
+      GroupTabs gt;
+      gt.g0 = -1;
+      gt.g1 = -1;
+      encode_item<CPL, RHT, SR, FAST>(it, r, a.mask, a.amax_in ? a.amax_in : ws->partial + kGroupAmax, gt,
+                                      &rcp_tab[wid][0][0], stage, mpad, a.seed, a.offset);
+    }
   }
-  __syncthreads();
-  write_item<CPL>(stage, ctile, bg, cols, mpad, cap, codes, ldc, scales, lds);
+  if constexpr (COL) {
+    __syncthreads();
+    write_item<CPL>(stage, ctile, bg, cols, mpad, cap, a.codes, a.ldc, a.scales, a.lds);
+  }
 }
 
 // Upper bound of the padded token blocks of all groups:
@@ -513,51 +630,64 @@ Geo geo_of(int64_t cols, uint32_t nb_max) {
   return g;
 }
 
-template <int CPLA, bool RHT, bool FAST>
+// Amax pass and reduce kernel for the planes whose amax is not given (COL,
+// ROW); rowwise partials follow the columnwise ones when both are computed.
+template <int CPLA, bool RHT, bool FAST, bool COL, bool ROW>
 void launch_amax(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
   const Geo g = geo_of<CPLA>(a.cols, nb_max);
-  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT, FAST>), g.grid, dim3(kT), 0, s, (const uint16_t*)a.x, (int)a.rows,
-                     (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.ws, g.nq, g.ntc, g.npairs, nb_max,
-                     g.chunk);
-  hipLaunchKernelGGL(k_grouped_reduce, dim3(a.groups), dim3(kReduceThreads), 0, s, a.offsets, a.groups, (int)a.rows,
-                     a.ws, g.ntc, nb_max * g.ntc, a.amax_out, a.scale_out);
+  const uint32_t lim = nb_max * g.ntc, rbase = COL ? lim : 0;
+  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT, FAST, COL, ROW>), g.grid, dim3(kT), 0, s, (const uint16_t*)a.x,
+                     (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.ws, g.nq, g.ntc, g.npairs,
+                     nb_max, g.chunk, rbase);
+  hipLaunchKernelGGL((k_grouped_reduce<COL, ROW>), dim3(a.groups), dim3(kReduceThreads), 0, s, a.offsets, a.groups,
+                     (int)a.rows, a.ws, g.ntc, lim, rbase, a.amax_out, a.scale_out, a.ramax_out, a.rscale_out);
 }
 
-template <int CPLE, bool RHT, bool SR, bool FAST>
+template <int CPLE, bool RHT, bool SR, bool FAST, bool COL, bool ROW>
 void launch_quant(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
-  const int64_t cap = a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16;
+  const int64_t cap = COL ? (a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16) : 0;
   const uint32_t npairs = (nb_max + 1) / 2 < 1 ? 1 : (nb_max + 1) / 2;
   const uint32_t nbg = (npairs + kQuantWaves - 1) / kQuantWaves;  // items per column tile
   const uint32_t ntc = tiles_of<CPLE>(a.cols);
   const uint32_t chunk = xcd_chunk((uint64_t)nbg * ntc);
-  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR, FAST>), dim3(xcd_grid((uint64_t)nbg * ntc)),
-                     dim3(kQuantThreads), 0, s, (const uint16_t*)a.x, (int)a.rows, (uint32_t)a.cols, a.ld_x,
-                     a.offsets, a.groups, a.mask, a.codes, a.ldc, a.scales, a.lds, a.ws, a.amax_in, a.amax_out,
-                     a.scale_out, a.poff_out, a.seed, a.offset, cap, nbg, ntc, npairs, chunk);
+  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR, FAST, COL, ROW>), dim3(xcd_grid((uint64_t)nbg * ntc)),
+                     dim3(kQuantThreads), 0, s, (const uint16_t*)a.x, a, a.ws, cap, nbg, ntc, npairs, chunk);
 }
 
-// FAST (no bf16 round-through of the transform's output) exists only with
-// the transform.
-template <bool RHT, bool FAST>
-void launch_grouped_r(const GroupArgs& a, hipStream_t s) {
+template <bool RHT, bool FAST, bool COL, bool ROW>
+void launch_planes(const GroupArgs& a, hipStream_t s) {
   const uint32_t nb_max = (uint32_t)grouped_blocks(a.rows, a.groups);
-  if (!a.amax_in) launch_amax<kCplAmax, RHT, FAST>(a, nb_max, s);
-  if (a.sr) launch_quant<kCplQuant, RHT, true, FAST>(a, nb_max, s);
-  else launch_quant<kCplQuant, RHT, false, FAST>(a, nb_max, s);
+  const bool col_amax = COL && !a.amax_in, row_amax = ROW && !a.ramax_in;
+  if (col_amax && row_amax) launch_amax<kCplAmax, RHT, FAST, true, true>(a, nb_max, s);
+  else if (col_amax) launch_amax<kCplAmax, RHT, FAST, true, false>(a, nb_max, s);
+  else if (row_amax) launch_amax<kCplAmax, false, false, false, true>(a, nb_max, s);
+  if (a.sr) launch_quant<kCplQuant, RHT, true, FAST, COL, ROW>(a, nb_max, s);
+  else launch_quant<kCplQuant, RHT, false, FAST, COL, ROW>(a, nb_max, s);
 }
 
 }  // namespace
 
 // Workspace slots the grouped path needs: the amax pass's partials, one per
-// (padded token block, column tile), and the per-group amax after them.
-int64_t grouped_partials(int64_t rows, int64_t cols, int groups) {
-  return grouped_blocks(rows, groups) * tiles_of<kCplAmax>(cols) + 64;
+// (padded token block, column tile) and plane, then the per-group amax of
+// both planes.
+int64_t grouped_partials(int64_t rows, int64_t cols, int groups, int planes) {
+  return planes * grouped_blocks(rows, groups) * tiles_of<kCplAmax>(cols) + 128;
 }
 
+// FAST (no bf16 round-through of the transform's output) exists only with the
+// transform and a columnwise plane; the rowwise plane alone has no transform.
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {
-  if (a.rht && a.fast) launch_grouped_r<true, true>(a, s);
-  else if (a.rht) launch_grouped_r<true, false>(a, s);
-  else launch_grouped_r<false, false>(a, s);
+  if (a.col && a.row) {
+    if (a.rht && a.fast) launch_planes<true, true, true, true>(a, s);
+    else if (a.rht) launch_planes<true, false, true, true>(a, s);
+    else launch_planes<false, false, true, true>(a, s);
+  } else if (a.col) {
+    if (a.rht && a.fast) launch_planes<true, true, true, false>(a, s);
+    else if (a.rht) launch_planes<true, false, true, false>(a, s);
+    else launch_planes<false, false, true, false>(a, s);
+  } else {
+    launch_planes<false, false, false, true>(a, s);
+  }
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ struct TwoDArgs {
 // 32 rows past a base row with 32-bit byte offsets.
 constexpr int64_t kGroupedMaxLd = (int64_t)1 << 24;
 
-// Arguments of the grouped columnwise path.
+// Arguments of the grouped path (columnwise and/or rowwise planes).
 struct GroupArgs {
   const void* x;
   int64_t rows, cols, ld_x;
@@ -63,12 +63,19 @@ struct GroupArgs {
   int32_t* poff_out;
   bool rht;
   uint32_t mask;
+  bool col;                       // columnwise plane requested
   uint8_t *codes, *scales;
   int64_t ldc, lds;
-  Workspace* ws;
   const float* amax_in;
   float* amax_out;
   float* scale_out;
+  bool row;                       // rowwise plane requested
+  uint8_t *rcodes, *rscales;
+  int64_t rldc, rlds;
+  const float* ramax_in;
+  float* ramax_out;
+  float* rscale_out;
+  Workspace* ws;
   bool sr;
   bool fast;  // fast math: no bf16 round-through of the transform's output
   uint64_t seed;
@@ -93,6 +100,7 @@ hipError_t launch_quant_2d(const TwoDArgs& a, hipStream_t s);
 
 // Grouped path; hipErrorInvalidValue when the tile grid exceeds the workspace.
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s);
-int64_t grouped_partials(int64_t rows, int64_t cols, int groups);
+// Workspace slots the grouped path's amax pass needs for `planes` planes.
+int64_t grouped_partials(int64_t rows, int64_t cols, int groups, int planes);
 
 }  // namespace nvfp4q

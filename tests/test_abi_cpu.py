@@ -127,10 +127,12 @@ def test_2d_and_grouped_validation(lib):
     assert lib.nvfp4q_quantize_2d(FAKE, 0, 32, 32, 32, ctypes.byref(g), ctypes.byref(none), ctypes.byref(none), 0,
                                   ctypes.byref(r), FAKE, 1 << 16, None) == 1
 
-    def grouped(groups=4, rht=1, mask=0x1234, ldc=64, lds=8, offs=FAKE, rows=64, ld=32):
+    def grouped(groups=4, rht=1, mask=0x1234, ldc=64, lds=8, offs=FAKE, rows=64, ld=32, colp=True, rowp=None):
         p = q.Plane(FAKE, ldc, FAKE, lds)
         return lib.nvfp4q_grouped(FAKE, 0, rows, 32, ld, offs, groups, None, rht, mask, ctypes.byref(g),
-                                  ctypes.byref(p), 1, ctypes.byref(r), FAKE, 1 << 16, None)
+                                  ctypes.byref(p) if colp else None, ctypes.byref(g),
+                                  ctypes.byref(rowp) if rowp is not None else None, 1, ctypes.byref(r), FAKE,
+                                  1 << 16, None)
 
     assert grouped(groups=0) == 2
     assert grouped(groups=65) == 2
@@ -140,6 +142,13 @@ def test_2d_and_grouped_validation(lib):
     assert grouped(ldc=48) == 2       # 2 * 48 < 64 + 15 * 4
     assert grouped(lds=7) == 2        # 16 * 7 < 124
     assert grouped(ld=(1 << 24) + 8) == 2   # row stride past the 32-bit offsets of the loads
+    assert grouped(colp=False) == 1                                        # no plane at all
+    assert grouped(colp=False, rowp=q.Plane(None, 16, None, 2)) == 1       # rows but no rowwise buffers
+    assert grouped(colp=False, rowp=q.Plane(FAKE, 8, FAKE, 2)) == 2        # 8 < 32 / 2 code bytes per row
+    assert grouped(colp=False, rowp=q.Plane(FAKE, 16, FAKE, 1)) == 2       # 1 < 32 / 16 scale bytes per row
+    assert grouped(colp=False, rowp=q.Plane(FAKE, 16, FAKE, 2)) == 6       # valid; stops at the small workspace
+    assert grouped(rowp=q.Plane(FAKE, 16, FAKE, 2)) == 6
+    assert grouped(rows=0, colp=False, rowp=q.Plane(None, 16, None, 2)) == 6   # an empty rowwise plane
 
 
 def test_rounding_option_bits(lib):
@@ -155,7 +164,7 @@ def test_rounding_option_bits(lib):
         # a workspace smaller than required: accepted rounding values pass their check and stop at the
         # workspace check (6); others stop at the rounding check (4). Nothing is launched.
         return lib.nvfp4q_grouped(FAKE, 0, 64, 32, 32, FAKE, 4, None, 1, 0x1234, ctypes.byref(g),
-                                  ctypes.byref(p), rounding, ctypes.byref(r), FAKE, 1 << 16, None)
+                                  ctypes.byref(p), None, None, rounding, ctypes.byref(r), FAKE, 1 << 16, None)
 
     assert grouped(q.RTNE | q.FAST_MATH) == 6 and grouped(q.SR | q.FAST_MATH) == 6
     assert grouped(2) == 4 and grouped(0x200) == 4 and grouped(q.SR | 0x200) == 4

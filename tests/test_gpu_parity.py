@@ -291,7 +291,7 @@ def test_2d_weight_8192x8192_sampled(gpu_lib):
 
 # ---------------------------------------------------------------- grouped
 def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offset=2, groups=None, amax=None,
-                   fast_math=False):
+                   fast_math=False, colwise=True, rowwise=False, row_amax=None):
     import torch
 
     T, C = x.shape
@@ -300,25 +300,45 @@ def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offs
     cap16 = (cap + 15) // 16 * 16
     codes = torch.full((C, (cap16 // 2 + 15) // 16 * 16), 0xAA, dtype=torch.uint8, device="cuda")
     scales = torch.full((C, cap16 // 16), 0x55, dtype=torch.uint8, device="cuda")
+    rcodes = torch.full((T, (C // 2 + 15) // 16 * 16), 0xAA, dtype=torch.uint8, device="cuda")
+    rscales = torch.full((T, C // 16 + 3), 0x55, dtype=torch.uint8, device="cuda")
     a = None if amax is None else torch.tensor(amax, dtype=torch.float32, device="cuda")
+    ra = None if row_amax is None else torch.tensor(row_amax, dtype=torch.float32, device="cuda")
     got = gpu_lib.nvfp4q_grouped(to_dev(x), torch.tensor(offsets, dtype=torch.int32, device="cuda"),
                                  apply_rht=apply_rht, rht_mask=mask, amax=a, rounding=rounding, seed=seed,
-                                 offset=offset, codes=codes, scales=scales, fast_math=fast_math)
+                                 offset=offset, codes=codes, scales=scales, fast_math=fast_math, colwise=colwise,
+                                 rowwise=rowwise, row_amax=ra, row_codes=rcodes, row_scales=rscales)
     ref = oracle.grouped_quantize(x, np.asarray(offsets, np.int32), apply_rht=apply_rht, rht_mask=mask,
                                   amax=None if amax is None else np.asarray(amax, np.float32),
-                                  rounding=rounding, seed=seed, offset=offset, groups=groups, fast_math=fast_math)
+                                  rounding=rounding, seed=seed, offset=offset, groups=groups, fast_math=fast_math,
+                                  rowwise=rowwise,
+                                  row_amax=None if row_amax is None else np.asarray(row_amax, np.float32))
     poff = ref["poff"]
     mpad = int(poff[-1])
     assert np.array_equal(got["poff"].cpu().numpy(), poff)
-    gc, gs = np_u8(got["codes"]), np_u8(got["scales"])
+    gc, gs = np_u8(codes), np_u8(scales)
+    rc, rs = np_u8(rcodes), np_u8(rscales)
     for g in (range(G) if groups is None else groups):
-        a0, a1 = int(poff[g]), int(poff[g + 1])
-        assert_same_bits(f"group {g} codes", gc[:, a0 // 2:a1 // 2], ref["codes"][:, a0 // 2:a1 // 2])
-        assert_same_bits(f"group {g} scales", gs[:, a0 // 16:a1 // 16], ref["scales"][:, a0 // 16:a1 // 16])
-        assert_f32_bits(f"group {g} amax", f32(got["amax"])[g], ref["amax"][g])
-        assert_f32_bits(f"group {g} scale", f32(got["scale"])[g], ref["s_dec"][g])
-    # the tail past the last padded column is never written
-    assert np.all(gc[:, mpad // 2:] == 0xAA) and np.all(gs[:, mpad // 16:] == 0x55)
+        if colwise:
+            a0, a1 = int(poff[g]), int(poff[g + 1])
+            assert_same_bits(f"group {g} codes", gc[:, a0 // 2:a1 // 2], ref["codes"][:, a0 // 2:a1 // 2])
+            assert_same_bits(f"group {g} scales", gs[:, a0 // 16:a1 // 16], ref["scales"][:, a0 // 16:a1 // 16])
+            assert_f32_bits(f"group {g} amax", f32(got["amax"])[g], ref["amax"][g])
+            assert_f32_bits(f"group {g} scale", f32(got["scale"])[g], ref["s_dec"][g])
+        if rowwise:
+            r0, r1 = int(offsets[g]), int(offsets[g + 1])
+            assert_same_bits(f"group {g} row codes", rc[r0:r1, :C // 2], ref["row_codes"][r0:r1])
+            assert_same_bits(f"group {g} row scales", rs[r0:r1, :C // 16], ref["row_scales"][r0:r1])
+            assert_f32_bits(f"group {g} row amax", f32(got["row_amax"])[g], ref["row_amax"][g])
+            assert_f32_bits(f"group {g} row scale", f32(got["row_scale"])[g], ref["row_s_dec"][g])
+    if colwise:
+        # the tail past the last padded column is never written
+        assert np.all(gc[:, mpad // 2:] == 0xAA) and np.all(gs[:, mpad // 16:] == 0x55)
+    else:
+        assert np.all(gc == 0xAA) and np.all(gs == 0x55)
+    if rowwise:
+        # nothing past a row's C / 2 code bytes and C / 16 scale bytes
+        assert np.all(rc[:, C // 2:] == 0xAA) and np.all(rs[:, C // 16:] == 0x55)
 
 
 @pytest.mark.parametrize("apply_rht", [True, False])
@@ -385,3 +405,42 @@ def test_grouped_moe_16384x7168_sampled(gpu_lib):
     G = len(w.offsets) - 1
     _grouped_check(gpu_lib, w.x, w.offsets.tolist(), w.apply_rht, w.rht_mask, "sr", seed=w.seed,
                    offset=w.offset, groups=[0, 17, 40, G - 1])
+
+
+@pytest.mark.parametrize("apply_rht", [True, False])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_grouped_rowwise_and_columnwise(gpu_lib, apply_rht, rounding):
+    # Both planes of the grouped input in one call (reading R-rowcol): ragged and empty groups, the
+    # rowwise plane without the transform under its own per-group amax.
+    rng = np.random.default_rng(17)
+    x = _bf16(rng, (203, 272))
+    _grouped_check(gpu_lib, x, [0, 0, 5, 21, 21, 150, 203], apply_rht, 0x9C35, rounding, rowwise=True)
+
+
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_grouped_rowwise_only_and_given_amax(gpu_lib, rounding):
+    rng = np.random.default_rng(18)
+    x = _bf16(rng, (300, 528), 4.0)
+    _grouped_check(gpu_lib, x, [0, 7, 300], True, 0x0001, rounding, colwise=False, rowwise=True)
+    _grouped_check(gpu_lib, x, [0, 7, 300], True, 0x0001, rounding, colwise=False, rowwise=True,
+                   row_amax=[1.5, 30.0])
+    # one plane's amax given, the other's computed
+    _grouped_check(gpu_lib, x, [0, 0, 131, 300], True, 0xF00F, rounding, amax=[0.0, 2.0, 5.0], rowwise=True)
+    _grouped_check(gpu_lib, x, [0, 0, 131, 300], True, 0xF00F, rounding, rowwise=True, row_amax=[1.0, 2.0, 5.0],
+                   fast_math=True)
+
+
+def test_grouped_rowwise_extreme_group_scales(gpu_lib):
+    rng = np.random.default_rng(19)
+    parts = [_bf16(rng, (40, 288), 1e-30), np.zeros((23, 288), np.uint16), _bf16(rng, (37, 288)),
+             _bf16(rng, (50, 288), 1e37)]
+    x = np.concatenate(parts, axis=0)
+    offsets = np.concatenate([[0], np.cumsum([p.shape[0] for p in parts])]).tolist()
+    _grouped_check(gpu_lib, x, offsets, True, 0x6A5C, "sr", rowwise=True)
+
+
+def test_grouped_moe_16384x7168_rowwise_sampled(gpu_lib):
+    w = workloads.grouped_moe()
+    G = len(w.offsets) - 1
+    _grouped_check(gpu_lib, w.x, w.offsets.tolist(), w.apply_rht, w.rht_mask, "sr", seed=w.seed,
+                   offset=w.offset, groups=[1, 30, G - 1], rowwise=True)
