@@ -40,11 +40,14 @@ def log(*a):
 class Case:
     """Device buffers and launch closures for one workload."""
 
-    def __init__(self, name, torch, q, workloads, fast_math=False):
+    def __init__(self, name, torch, q, workloads, fast_math=False, planes="col"):
         import numpy as np
 
         self.name = name
         self.fast_math = fast_math
+        self.planes = planes  # grouped: which planes a step writes
+        self.colwise = name != "grouped" or planes in ("col", "both")
+        self.rowwise = name == "grouped" and planes in ("row", "both")
         self.w = w = workloads.make(name)
         dev = torch.device("cuda", 0)
 
@@ -65,7 +68,11 @@ class Case:
             counts = np.diff(w.offsets)
             mpad = int(np.sum((counts + 15) // 16 * 16))
             self.mpad = mpad
-            out_bytes = C * mpad // 2 + C * mpad // 16 + 4 * (G + 1) + 8 * G
+            out_bytes = 4 * (G + 1)                     # padded offsets
+            if self.colwise:  # the columnwise plane and its per-group amax and S_dec
+                out_bytes += C * mpad // 2 + C * mpad // 16 + 8 * G
+            if self.rowwise:  # the rowwise plane and its per-group amax and S_dec
+                out_bytes += R * C // 2 + R * C // 16 + 8 * G
             param_bytes = 4 * (G + 1)
         self.bytes = x_bytes + out_bytes + param_bytes + (8 if name != "grouped" else 0)
         set_bytes = x_bytes + out_bytes
@@ -82,13 +89,16 @@ class Case:
             cap16 = (R + 15 * G + 15) // 16 * 16
             self.outs = [(torch.empty((C, (cap16 // 2 + 15) // 16 * 16), dtype=torch.uint8, device=dev),
                           torch.empty((C, cap16 // 16), dtype=torch.uint8, device=dev)) for _ in range(self.nsets)]
+            ldr = (C // 2 + 15) // 16 * 16
+            self.row_outs = [(torch.empty((R, ldr), dtype=torch.uint8, device=dev),
+                              torch.empty((R, C // 16), dtype=torch.uint8, device=dev)) if self.rowwise else (None, None)
+                             for _ in range(self.nsets)]
         elif name == "weight":
             self.outs = [None] * self.nsets
         else:
             ldc = (C // 2 + 15) // 16 * 16
             self.outs = [(torch.empty((R, ldc), dtype=torch.uint8, device=dev),
                           torch.empty((R, C // 16), dtype=torch.uint8, device=dev)) for _ in range(self.nsets)]
-        self.amax_given = None
 
     def describe(self):
         w = self.w
@@ -102,14 +112,27 @@ class Case:
         elif self.name == "grouped":
             d.update({"op": "grouped columnwise nvfp4 after 16-pt RHT", "groups": len(w.offsets) - 1,
                       "padded_tokens": self.mpad})
+            if self.planes == "both":
+                d["op"] = "grouped rowwise nvfp4 + columnwise nvfp4 after 16-pt RHT, one pass"
+            elif self.planes == "row":
+                d["op"] = "grouped rowwise nvfp4 (per-group amax)"
             if self.fast_math:
                 d["fast_math"] = "transform output quantized in fp32 (no bf16 round-through)"
         else:
             d.update({"op": "nvfp4 rowwise"})
         return d
 
-    def step(self, i, amax=None):
+    def given(self, out):
+        """The amax arguments that make a call skip its amax pass, from a call's outputs."""
+        g = {"amax": out["amax"].clone()} if self.colwise else {}
+        if self.rowwise:
+            g["row_amax"] = out["row_amax"].clone()
+        return g
+
+    def step(self, i, given=None):
         q, w = self.q, self.w
+        given = given or {}
+        amax = given.get("amax")
         x = self.xs[i % self.nsets]
         o = self.outs[i % self.nsets]
         if self.name in ("prefill", "decode"):
@@ -120,11 +143,14 @@ class Case:
             return q.nvfp4q_quantize_2d(x, amax=amax, rounding=w.rounding, seed=w.seed, offset=w.offset)
         return q.nvfp4q_grouped(x, self.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, amax=amax,
                                 rounding=w.rounding, seed=w.seed, offset=w.offset, codes=o[0], scales=o[1],
-                                fast_math=self.fast_math)
+                                fast_math=self.fast_math, colwise=self.colwise, rowwise=self.rowwise,
+                                row_amax=given.get("row_amax"),
+                                row_codes=self.row_outs[i % self.nsets][0],
+                                row_scales=self.row_outs[i % self.nsets][1])
 
 
 # ----------------------------------------------------------------------------- timing
-def time_steps(case, steps, warmup, amax=None, eager=False):
+def time_steps(case, steps, warmup, given=None, eager=False):
     """Average ms per step over `steps` timed steps.
 
     The steps are captured once in a HIP graph (the library allocates nothing and
@@ -137,12 +163,12 @@ def time_steps(case, steps, warmup, amax=None, eager=False):
     torch = case.torch
     if eager:
         for i in range(warmup):
-            case.step(i, amax)
+            case.step(i, given)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
-            case.step(warmup + i, amax)
+            case.step(warmup + i, given)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
@@ -150,15 +176,15 @@ def time_steps(case, steps, warmup, amax=None, eager=False):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for i in range(3):                      # eager warm-up before capture
-            case.step(i, amax)
+            case.step(i, given)
         torch.cuda.synchronize()
         gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(gw, stream=s):
             for i in range(max(warmup, 1)):
-                case.step(i, amax)
+                case.step(i, given)
         with torch.cuda.graph(gt, stream=s):
             for i in range(steps):
-                case.step(i, amax)
+                case.step(i, given)
         torch.cuda.synchronize()
         gw.replay()
         torch.cuda.synchronize()
@@ -189,7 +215,8 @@ def cpu_baseline(case, budget_s=12.0):
             G = len(w.offsets) - 1
             g = passes % G
             oracle.grouped_quantize(w.x, w.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, rounding=w.rounding,
-                                    seed=w.seed, offset=w.offset, groups=[g], fast_math=case.fast_math)
+                                    seed=w.seed, offset=w.offset, groups=[g], fast_math=case.fast_math,
+                                    colwise=case.colwise, rowwise=case.rowwise)
             n = int(w.offsets[g + 1] - w.offsets[g])
             done_bytes += case.bytes * n / R
         else:
@@ -275,7 +302,12 @@ def read_pmc(directory, counter):
     return out
 
 
-def ingest_pmc(config, fetch_dir, write_dir, command):
+def traffic_key(config, fast_math=False, planes="col"):
+    """The profiles/traffic.json entry of a workload variant."""
+    return config + ("" if planes == "col" else "_" + planes) + ("_fast" if fast_math else "")
+
+
+def ingest_pmc(config, fetch_dir, write_dir, command, key=None):
     """Per-step FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel(s) into profiles/traffic.json."""
     import re
 
@@ -293,7 +325,7 @@ def ingest_pmc(config, fetch_dir, write_dir, command):
         raise SystemExit(f"expected one kernel, found {list(entry['kernels'])}")
     entry["fetch_kib"] = sum(k.get("fetch_size_kib", 0.0) for k in entry["kernels"].values())
     entry["write_kib"] = sum(k.get("write_size_kib", 0.0) for k in entry["kernels"].values())
-    _update_traffic(config, entry)
+    _update_traffic(key or config, entry)
 
 
 def ingest_copy(fetch_dir, write_dir, nbytes, command):
@@ -356,6 +388,8 @@ def main():
     ap.add_argument("--config", default="prefill", choices=["quantize", "prefill", "decode", "weight", "grouped"])
     ap.add_argument("--fast-math", action="store_true",
                     help="grouped: NVFP4Q_FAST_MATH (no bf16 round-through of the transform's output)")
+    ap.add_argument("--planes", default="col", choices=["col", "row", "both"],
+                    help="grouped: the columnwise plane, the rowwise plane, or both in one pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time plain calls instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES",
@@ -368,7 +402,8 @@ def main():
     args = ap.parse_args()
 
     if args.ingest_pmc:
-        ingest_pmc(args.config, *args.ingest_pmc, command=args.command)
+        ingest_pmc(args.config, *args.ingest_pmc, command=args.command,
+                   key=traffic_key(args.config, args.fast_math, args.planes))
         return
     if args.ingest_copy:
         ingest_copy(*args.ingest_copy, nbytes=args.copy_calibration or (256 << 20), command=args.command)
@@ -396,7 +431,11 @@ def main():
     torch.cuda.set_device(0)
     if args.fast_math and args.config != "grouped":
         raise SystemExit("--fast-math applies to the grouped workload (the only one with the transform)")
-    case = Case(args.config, torch, q, workloads, fast_math=args.fast_math)
+    if args.planes != "col" and args.config != "grouped":
+        raise SystemExit("--planes applies to the grouped workload (the others name their planes already)")
+    if args.fast_math and args.planes == "row":
+        raise SystemExit("--fast-math concerns the transform, which the rowwise plane does not take")
+    case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes)
     log(f"[bench] {case.describe()}")
 
     # whole step (amax + quantize), the figure the metric is quoted on
@@ -407,14 +446,14 @@ def main():
     how, kname, _ = DOMINANT[args.config]
     if how == "stage":
         # the encode kernel alone against the amax the full step produced
-        amax_t = case.step(0)["amax"].clone()
+        given = case.given(case.step(0))
         torch.cuda.synchronize()
-        kms = time_steps(case, args.steps, args.warmup, amax=amax_t, eager=args.eager)
+        kms = time_steps(case, args.steps, args.warmup, given=given, eager=args.eager)
         log(f"[bench] {kname} alone (given amax): {kms * 1e3:.2f} us/launch")
     else:
         kms = ms
     achieved = case.bytes / (kms * 1e-3) / 1e9
-    traffic = traffic_bytes(args.config)
+    traffic = traffic_bytes(traffic_key(args.config, args.fast_math, args.planes))
     out = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -40,8 +40,9 @@ def padded_offsets(offsets) -> np.ndarray:
 
 
 def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr",
-                     seed=0, offset=0, groups=None, fast_math=False, rowwise=False, row_amax=None):
-    """Reference for the grouped columnwise path.
+                     seed=0, offset=0, groups=None, fast_math=False, rowwise=False, row_amax=None,
+                     colwise=True):
+    """Reference for the grouped path: the columnwise plane, optionally the rowwise one.
 
     x: bf16 bits [total_rows, K]. offsets: int32 [G+1]. amax: optional float32 [G].
     groups: optional iterable restricting which groups are computed (for sampling);
@@ -53,6 +54,7 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
     amax max|x| (row_amax: optional float32 [G] given instead); SR tag 0, block
     index row * (K/16) + k/16 with the row's index in x. Adds row_codes
     [total_rows, K/2], row_scales [total_rows, K/16], row_amax, row_s_dec [G].
+    colwise=False skips the columnwise plane (its arrays stay zero).
     Returns dict with codes [K, Mpad/2], scales [K, Mpad/16], amax [G], s_enc [G],
     s_dec [G], poff [G+1].
     """
@@ -69,7 +71,7 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
     s_enc_out = np.ones(G, dtype=np.float32)
     s_dec_out = np.ones(G, dtype=np.float32)
     sel = range(G) if groups is None else groups
-    for g in sel:
+    for g in (sel if colwise else ()):
         n = int(off[g + 1] - off[g])
         pg = int(poff[g + 1] - poff[g])
         z = np.zeros((pg, K), dtype=np.uint16)
