@@ -54,6 +54,10 @@ that implements it. Readings are:
   R-rowcol   grouped rowwise + columnwise: the rowwise plane of x's rows,
              no transform, one amax per group (max|x| over its rows), SR tag
              0 with block index row * (K/16) + k/16 in x's row numbering.
+  R-2dblk    "2D" weight scaling: one E4M3 scale per 16 x 16 tile (the tile
+             amax through R-bscale), used by every element of the tile in
+             both planes; the planes keep the 1D scale layout with the
+             tile's code repeated on its 16 rows / 16 columns.
   R-group    each group is zero-padded to a multiple of 16 rows, groups are
              laid out back to back in one transposed plane; storage past the
              last padded column is never written.
@@ -65,7 +69,7 @@ from .formats import (  # noqa: F401
 from .philox import philox4x32_10  # noqa: F401
 from .quantize import (  # noqa: F401
     global_scales, block_scale_codes, encode_reciprocal, quantize_blocks, quantize_rowwise,
-    quantize_colwise, quantize_2d, dequantize_rowwise, sr_round,
+    quantize_colwise, quantize_2d, quantize_2d_block, encode_blocks, dequantize_rowwise, sr_round,
 )
 from .rmsnorm import rmsnorm_bf16, rmsnorm_quantize  # noqa: F401
 from .rht import rht16, rht16_f32  # noqa: F401

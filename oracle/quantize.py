@@ -101,6 +101,12 @@ def quantize_blocks(xb, s_enc, s_dec, rounding="rtne", rbytes=None):
     assert xb.shape[-1] == BLOCK
     bmax = np.max(np.abs(xb), axis=-1)
     sc = block_scale_codes(bmax, s_enc)
+    return encode_blocks(xb, sc, s_dec, rounding, rbytes), sc
+
+
+def encode_blocks(xb, sc, s_dec, rounding="rtne", rbytes=None):
+    """Codes of float32 blocks xb[..., 16] under given scale codes sc[...] (R-rcp, R-e2m1 / R-sr)."""
+    xb = np.asarray(xb, dtype=F32)
     rcp = encode_reciprocal(sc, s_dec)
     with np.errstate(over="ignore"):
         v = (xb * rcp[..., None]).astype(F32)
@@ -111,7 +117,7 @@ def quantize_blocks(xb, s_enc, s_dec, rounding="rtne", rbytes=None):
         codes = sr_round(v, rbytes)
     else:
         raise ValueError(rounding)
-    return codes, sc
+    return codes
 
 
 def _as_f32(x_bits_or_f32):
@@ -179,6 +185,53 @@ def quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0):
     row = quantize_rowwise(xf, amax=a, rounding=rounding, seed=seed, offset=offset, tag=0)
     col = quantize_colwise(xf, amax=a, rounding=rounding, seed=seed, offset=offset)
     return {"row": row, "col": col, "amax": F32(a), "s_enc": row["s_enc"], "s_dec": row["s_dec"]}
+
+
+def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0):
+    """Rowwise and columnwise planes under one E4M3 scale per 16 x 16 tile (reading R-2dblk).
+
+    PR, Optimization item 2 describes the 2D weight kernel's columnwise reads as
+    paired so that neighbouring rows of the transposed plane share one amax and
+    one reciprocal, and the Performance section measures "2D weights" beside
+    the 1D paths, but the pages never define the tile. Reading R-2dblk: the block
+    amax is taken over the 16 x 16 tile (rows 16i..16i+15, columns 16j..16j+15),
+    its scale code is R-bscale of that tile amax, and every element of the tile
+    is encoded with it (R-rcp, R-e2m1 / R-sr) in both planes, so a weight and its
+    transpose decode to the same values. The planes keep the 1D layout: the
+    rowwise scales [M, K/16] repeat the tile's code on its 16 rows, the
+    columnwise scales [K, M/16] on its 16 columns. SR bytes are drawn per plane
+    exactly as in quantize_2d (tag 0 rowwise with block row*(K/16)+j, tag 1
+    columnwise with block col*(M/16)+i).
+    """
+    xf = _as_f32(x)
+    M, K = xf.shape
+    assert M % BLOCK == 0 and K % BLOCK == 0
+    a = _amax(xf) if amax is None else F32(amax)
+    s_enc, s_dec = global_scales(a)
+    tiles = np.abs(xf).reshape(M // BLOCK, BLOCK, K // BLOCK, BLOCK)
+    tmax = tiles.max(axis=(1, 3)) if xf.size else np.zeros((M // BLOCK, K // BLOCK), F32)   # [M/16, K/16]
+    tsc = block_scale_codes(tmax, s_enc)
+    # rowwise: block (r, j) takes tile (r // 16, j)
+    row_sc = np.repeat(tsc, BLOCK, axis=0)                                                  # [M, K/16]
+    rb = None
+    if rounding == "sr":
+        blk = (np.arange(M, dtype=np.uint64)[:, None] * np.uint64(K // BLOCK)
+               + np.arange(K // BLOCK, dtype=np.uint64)[None, :])
+        rb = block_random_bytes(blk, 0, seed, offset)
+    rcodes = encode_blocks(xf.reshape(M, K // BLOCK, BLOCK), row_sc, s_dec, rounding, rb)
+    # columnwise: block (c, i) of the transposed plane takes tile (i, c // 16)
+    xt = np.ascontiguousarray(xf.T)
+    col_sc = np.repeat(tsc.T, BLOCK, axis=0)                                                # [K, M/16]
+    cb = None
+    if rounding == "sr":
+        blk = (np.arange(K, dtype=np.uint64)[:, None] * np.uint64(M // BLOCK)
+               + np.arange(M // BLOCK, dtype=np.uint64)[None, :])
+        cb = block_random_bytes(blk, 1, seed, offset)
+    ccodes = encode_blocks(xt.reshape(K, M // BLOCK, BLOCK), col_sc, s_dec, rounding, cb)
+    row = {"codes": pack_nibbles(rcodes.reshape(M, K)), "scales": row_sc.astype(np.uint8)}
+    col = {"codes": pack_nibbles(ccodes.reshape(K, M)), "scales": col_sc.astype(np.uint8)}
+    return {"row": row, "col": col, "tile_scales": tsc, "amax": F32(a), "s_enc": F32(s_enc),
+            "s_dec": F32(s_dec)}
 
 
 def dequantize_rowwise(codes, scales, s_dec):

@@ -187,3 +187,66 @@ def test_sampled_rows_keep_their_block_indices():
     fc = Q.quantize_colwise(x, rounding="sr", seed=5, offset=2)
     pc = Q.quantize_colwise(x[:, cols], amax=fc["amax"], rounding="sr", seed=5, offset=2, col_ids=cols)
     assert np.array_equal(pc["codes"], fc["codes"][cols])
+
+
+# ---------------------------------------------------------------- 16 x 16 tile scales (reading R-2dblk)
+def test_2d_block_hand_tile():
+    # amax 2688 gives S_enc = S_dec = 1. Tile (0, 0) holds 12 at (0, 0), 3 at (5, 3) and -0.5 at (9, 15):
+    # tile max 12, RN(12 / 6) = 2 = E4M3 0x40, multiplier 0.5, so 12 -> 6 (code 7), 3 -> 1.5 (code 3) and
+    # -0.5 -> -0.25, a tie between 0 and 0.5 that goes to the even code 0 with the sign kept (0x8). With
+    # 1D blocks row 5 would take its own maximum 3 (scale 0.5 = 0x30, 3 -> 6, code 7). Tile (1, 1) holds
+    # only 1 at (20, 17): RN(1 / 6) = 0.16666667 lies above the midpoint 0.1640625 of the E4M3 neighbours
+    # 0.15625 and 0.171875, so its scale is 0.171875 = 0x23; RN(1 / 0.171875) = 5.818182 rounds to 6.
+    x = np.zeros((32, 32), np.float32)
+    x[0, 0], x[5, 3], x[9, 15], x[20, 17] = 12.0, 3.0, -0.5, 1.0
+    q = Q.quantize_2d_block(_bf16(x), amax=np.float32(2688.0))
+    assert q["tile_scales"].tolist() == [[0x40, 0], [0, 0x23]]
+    rc, cc = F.unpack_nibbles(q["row"]["codes"]), F.unpack_nibbles(q["col"]["codes"])
+    expect = np.zeros((32, 32), np.uint8)
+    expect[0, 0], expect[5, 3], expect[9, 15], expect[20, 17] = 7, 3, 0x8, 7
+    assert np.array_equal(rc, expect)
+    assert np.array_equal(cc, expect.T)
+    assert np.all(q["row"]["scales"][:16, 0] == 0x40) and np.all(q["row"]["scales"][16:, 1] == 0x23)
+    assert np.all(q["col"]["scales"][:16, 0] == 0x40) and np.all(q["col"]["scales"][16:, 1] == 0x23)
+    assert np.all(q["row"]["scales"][:16, 1] == 0) and np.all(q["col"]["scales"][16:, 0] == 0)
+    one_d = Q.quantize_rowwise(_bf16(x), amax=np.float32(2688.0))
+    assert int(one_d["scales"][5, 0]) == 0x30 and F.unpack_nibbles(one_d["codes"])[5, 3] == 7
+
+
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_2d_block_reduces_to_1d_blocks(rounding):
+    # Rows repeated within each 16-row band: every tile maximum is each row block's maximum, so the
+    # rowwise plane is the 1D rowwise quantization; columns repeated within each 16-column band give
+    # the 1D columnwise plane. SR streams are those of the 1D planes (same tags and block indices).
+    rng = np.random.default_rng(31)
+    band = rng.standard_normal((3, 1, 80)).astype(np.float32) * np.float32(3.0)
+    xr = F.f32_to_bf16(np.repeat(band, 16, axis=1).reshape(48, 80))
+    q = Q.quantize_2d_block(xr, rounding=rounding, seed=77, offset=4)
+    r1 = Q.quantize_rowwise(xr, rounding=rounding, seed=77, offset=4)
+    assert np.array_equal(q["row"]["codes"], r1["codes"]) and np.array_equal(q["row"]["scales"], r1["scales"])
+    cband = rng.standard_normal((48, 5, 1)).astype(np.float32)
+    xc = F.f32_to_bf16(np.repeat(cband, 16, axis=2).reshape(48, 80))
+    q = Q.quantize_2d_block(xc, rounding=rounding, seed=77, offset=4)
+    c1 = Q.quantize_colwise(xc, rounding=rounding, seed=77, offset=4)
+    assert np.array_equal(q["col"]["codes"], c1["codes"]) and np.array_equal(q["col"]["scales"], c1["scales"])
+
+
+def test_2d_block_tile_scale_is_the_largest_1d_scale_and_rtne_planes_transpose():
+    # The scale code is monotone in the block maximum, so a tile's code is the largest of the 1D codes of
+    # its 16 row blocks and of its 16 column blocks; with RTNE the columnwise plane is the transpose of
+    # the rowwise plane (same element, same scale). Distinct magnitudes per tile row and column make a
+    # transposed or shifted tile index visible.
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((64, 96)).astype(np.float32) * np.exp(rng.uniform(-6, 6, (64, 1))).astype(np.float32)
+    x *= np.exp(rng.uniform(-4, 4, (1, 96))).astype(np.float32)
+    xb = F.f32_to_bf16(x)
+    q = Q.quantize_2d_block(xb)
+    r1, c1 = Q.quantize_rowwise(xb), Q.quantize_colwise(xb)
+    assert np.array_equal(q["tile_scales"], r1["scales"].reshape(4, 16, 6).max(axis=1))
+    assert np.array_equal(q["tile_scales"], c1["scales"].reshape(6, 16, 4).max(axis=1).T)
+    assert np.array_equal(F.unpack_nibbles(q["col"]["codes"]), F.unpack_nibbles(q["row"]["codes"]).T)
+    assert np.array_equal(q["col"]["scales"], np.repeat(q["tile_scales"].T, 16, axis=0))
+    # and the dequantized planes agree exactly
+    dr = Q.dequantize_rowwise(q["row"]["codes"], q["row"]["scales"], q["s_dec"])
+    dc = Q.dequantize_rowwise(q["col"]["codes"], q["col"]["scales"], q["s_dec"])
+    assert np.array_equal(dr, dc.T)
