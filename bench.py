@@ -40,12 +40,13 @@ def log(*a):
 class Case:
     """Device buffers and launch closures for one workload."""
 
-    def __init__(self, name, torch, q, workloads, fast_math=False, planes="col"):
+    def __init__(self, name, torch, q, workloads, fast_math=False, planes="col", tile16=False):
         import numpy as np
 
         self.name = name
         self.fast_math = fast_math
         self.planes = planes  # grouped: which planes a step writes
+        self.tile16 = tile16  # weight: one scale per 16 x 16 tile
         self.colwise = name != "grouped" or planes in ("col", "both")
         self.rowwise = name == "grouped" and planes in ("row", "both")
         self.w = w = workloads.make(name)
@@ -109,6 +110,8 @@ class Case:
                       "bias": w.beta is not None, "eps": w.eps})
         elif self.name == "weight":
             d.update({"op": "nvfp4 rowwise+columnwise (2D weight)", "seed": w.seed})
+            if self.tile16:
+                d["op"] = "nvfp4 rowwise+columnwise (2D weight), one scale per 16x16 tile"
         elif self.name == "grouped":
             d.update({"op": "grouped columnwise nvfp4 after 16-pt RHT", "groups": len(w.offsets) - 1,
                       "padded_tokens": self.mpad})
@@ -140,7 +143,8 @@ class Case:
         if self.name == "quantize":
             return q.nvfp4q_quantize(x, amax=amax, codes=o[0], scales=o[1])
         if self.name == "weight":
-            return q.nvfp4q_quantize_2d(x, amax=amax, rounding=w.rounding, seed=w.seed, offset=w.offset)
+            return q.nvfp4q_quantize_2d(x, amax=amax, rounding=w.rounding, seed=w.seed, offset=w.offset,
+                                        tile16=self.tile16)
         return q.nvfp4q_grouped(x, self.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, amax=amax,
                                 rounding=w.rounding, seed=w.seed, offset=w.offset, codes=o[0], scales=o[1],
                                 fast_math=self.fast_math, colwise=self.colwise, rowwise=self.rowwise,
@@ -227,9 +231,15 @@ def cpu_baseline(case, budget_s=12.0):
             elif name == "quantize":
                 oracle.quantize_rowwise(xs)
             else:
-                oracle.quantize_rowwise(xs, amax=np.float32(1.0), rounding=w.rounding, seed=w.seed, row_ids=rows)
-                oracle.quantize_colwise(w.x[:, rows], amax=np.float32(1.0), rounding=w.rounding, seed=w.seed,
-                                        col_ids=rows)
+                if case.tile16:
+                    r0 = rows[0] // 16 * 16
+                    oracle.quantize_2d_block(w.x[r0:r0 + len(rows)], amax=np.float32(1.0), rounding=w.rounding,
+                                             seed=w.seed, origin=(r0, 0), full=w.x.shape)
+                else:
+                    oracle.quantize_rowwise(xs, amax=np.float32(1.0), rounding=w.rounding, seed=w.seed,
+                                            row_ids=rows)
+                    oracle.quantize_colwise(w.x[:, rows], amax=np.float32(1.0), rounding=w.rounding, seed=w.seed,
+                                            col_ids=rows)
             done_bytes += case.bytes * len(rows) / R
             r0 = (r0 + chunk) % R
         passes += 1
@@ -302,9 +312,10 @@ def read_pmc(directory, counter):
     return out
 
 
-def traffic_key(config, fast_math=False, planes="col"):
+def traffic_key(config, fast_math=False, planes="col", tile16=False):
     """The profiles/traffic.json entry of a workload variant."""
-    return config + ("" if planes == "col" else "_" + planes) + ("_fast" if fast_math else "")
+    return (config + ("" if planes == "col" else "_" + planes) + ("_fast" if fast_math else "")
+            + ("_tile16" if tile16 else ""))
 
 
 def ingest_pmc(config, fetch_dir, write_dir, command, key=None):
@@ -390,6 +401,8 @@ def main():
                     help="grouped: NVFP4Q_FAST_MATH (no bf16 round-through of the transform's output)")
     ap.add_argument("--planes", default="col", choices=["col", "row", "both"],
                     help="grouped: the columnwise plane, the rowwise plane, or both in one pass")
+    ap.add_argument("--tile16", action="store_true",
+                    help="weight: NVFP4Q_SCALE_16X16 (one block scale per 16x16 tile, shared by both planes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time plain calls instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES",
@@ -403,7 +416,7 @@ def main():
 
     if args.ingest_pmc:
         ingest_pmc(args.config, *args.ingest_pmc, command=args.command,
-                   key=traffic_key(args.config, args.fast_math, args.planes))
+                   key=traffic_key(args.config, args.fast_math, args.planes, args.tile16))
         return
     if args.ingest_copy:
         ingest_copy(*args.ingest_copy, nbytes=args.copy_calibration or (256 << 20), command=args.command)
@@ -435,7 +448,9 @@ def main():
         raise SystemExit("--planes applies to the grouped workload (the others name their planes already)")
     if args.fast_math and args.planes == "row":
         raise SystemExit("--fast-math concerns the transform, which the rowwise plane does not take")
-    case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes)
+    if args.tile16 and args.config != "weight":
+        raise SystemExit("--tile16 applies to the weight workload (the 2D path)")
+    case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes, tile16=args.tile16)
     log(f"[bench] {case.describe()}")
 
     # whole step (amax + quantize), the figure the metric is quoted on
@@ -453,7 +468,7 @@ def main():
     else:
         kms = ms
     achieved = case.bytes / (kms * 1e-3) / 1e9
-    traffic = traffic_bytes(traffic_key(args.config, args.fast_math, args.planes))
+    traffic = traffic_bytes(traffic_key(args.config, args.fast_math, args.planes, args.tile16))
     out = {
         "metric": METRIC,
         "value": round(value, 2),

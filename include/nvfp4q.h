@@ -94,6 +94,10 @@ typedef enum { NVFP4Q_BF16 = 0 } nvfp4q_dtype;
  * nothing. Other bits: NVFP4Q_E_UNSUPPORTED. */
 typedef enum { NVFP4Q_RTNE = 0, NVFP4Q_SR = 1 } nvfp4q_rounding;
 #define NVFP4Q_FAST_MATH 0x100
+/* nvfp4q_quantize_2d only (other entry points: NVFP4Q_E_UNSUPPORTED): one
+ * E4M3 scale per 16 x 16 tile of x, used by both planes, so that a weight and
+ * its transpose decode to the same values. */
+#define NVFP4Q_SCALE_16X16 0x200
 
 /* One quantized plane. codes: device, [plane_rows][ld_codes] bytes, two E2M1
  * codes per byte, even element in the low nibble. scales: device,
@@ -182,6 +186,13 @@ nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, 
  *   rows % 16 == 0 when the columnwise plane is requested.
  *   SR: rowwise blocks use tag 0 and index row * (cols/16) + col/16;
  *   columnwise blocks use tag 1 and index col * (rows/16) + row/16.
+ *   NVFP4Q_SCALE_16X16 in `rounding`: the block amax is taken over the 16 x 16
+ *   tile (rows 16i.., columns 16j..) and every element of the tile is encoded
+ *   with that tile's scale in both planes; the scale arrays keep their layout
+ *   (the tile's code on each of its 16 rows, resp. 16 columns); rows % 16 == 0
+ *   also for a rowwise-only call. The pages measure "2D weights" and describe
+ *   columnwise reads sharing one amax and reciprocal without defining the
+ *   tile; this is the reading taken.
  *   [PR, Optimization 2 (2D weight kernel, staged columnwise reads);
  *    Performance (2D weights against a precomputed amax)]
  */

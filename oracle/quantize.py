@@ -187,7 +187,7 @@ def quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0):
     return {"row": row, "col": col, "amax": F32(a), "s_enc": row["s_enc"], "s_dec": row["s_dec"]}
 
 
-def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0):
+def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0, origin=(0, 0), full=None):
     """Rowwise and columnwise planes under one E4M3 scale per 16 x 16 tile (reading R-2dblk).
 
     PR, Optimization item 2 describes the 2D weight kernel's columnwise reads as
@@ -202,10 +202,18 @@ def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0):
     columnwise scales [K, M/16] on its 16 columns. SR bytes are drawn per plane
     exactly as in quantize_2d (tag 0 rowwise with block row*(K/16)+j, tag 1
     columnwise with block col*(M/16)+i).
+
+    origin, full (sampling only): x is the window of a [full] tensor whose first
+    element sits at row, column `origin` (multiples of 16); SR block indices are
+    then those of the full tensor, and amax must be given.
     """
     xf = _as_f32(x)
     M, K = xf.shape
     assert M % BLOCK == 0 and K % BLOCK == 0
+    r0, c0 = (int(v) for v in origin)
+    FM, FK = (M, K) if full is None else (int(v) for v in full)
+    assert r0 % BLOCK == 0 and c0 % BLOCK == 0 and r0 + M <= FM and c0 + K <= FK
+    assert full is None or amax is not None, "a sampled window needs the full tensor's amax"
     a = _amax(xf) if amax is None else F32(amax)
     s_enc, s_dec = global_scales(a)
     tiles = np.abs(xf).reshape(M // BLOCK, BLOCK, K // BLOCK, BLOCK)
@@ -215,8 +223,8 @@ def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0):
     row_sc = np.repeat(tsc, BLOCK, axis=0)                                                  # [M, K/16]
     rb = None
     if rounding == "sr":
-        blk = (np.arange(M, dtype=np.uint64)[:, None] * np.uint64(K // BLOCK)
-               + np.arange(K // BLOCK, dtype=np.uint64)[None, :])
+        blk = (np.arange(r0, r0 + M, dtype=np.uint64)[:, None] * np.uint64(FK // BLOCK)
+               + np.arange(c0 // BLOCK, (c0 + K) // BLOCK, dtype=np.uint64)[None, :])
         rb = block_random_bytes(blk, 0, seed, offset)
     rcodes = encode_blocks(xf.reshape(M, K // BLOCK, BLOCK), row_sc, s_dec, rounding, rb)
     # columnwise: block (c, i) of the transposed plane takes tile (i, c // 16)
@@ -224,8 +232,8 @@ def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0):
     col_sc = np.repeat(tsc.T, BLOCK, axis=0)                                                # [K, M/16]
     cb = None
     if rounding == "sr":
-        blk = (np.arange(K, dtype=np.uint64)[:, None] * np.uint64(M // BLOCK)
-               + np.arange(M // BLOCK, dtype=np.uint64)[None, :])
+        blk = (np.arange(c0, c0 + K, dtype=np.uint64)[:, None] * np.uint64(FM // BLOCK)
+               + np.arange(r0 // BLOCK, (r0 + M) // BLOCK, dtype=np.uint64)[None, :])
         cb = block_random_bytes(blk, 1, seed, offset)
     ccodes = encode_blocks(xt.reshape(K, M // BLOCK, BLOCK), col_sc, s_dec, rounding, cb)
     row = {"codes": pack_nibbles(rcodes.reshape(M, K)), "scales": row_sc.astype(np.uint8)}

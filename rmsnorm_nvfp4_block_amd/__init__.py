@@ -26,6 +26,7 @@ SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_gr
 
 RTNE, SR = 0, 1
 FAST_MATH = 0x100  # NVFP4Q_FAST_MATH, OR-ed into the rounding argument
+SCALE_16X16 = 0x200  # NVFP4Q_SCALE_16X16 (nvfp4q_quantize_2d only), OR-ed into the rounding argument
 
 
 class Plane(ctypes.Structure):
@@ -189,8 +190,12 @@ def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, 
     return {"codes": c, "scales": s, "amax": amax_out, "scale": scale_out, "y": y}
 
 
-def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=True, colwise=True):
-    """Rowwise and columnwise planes of bf16 x [rows, cols] under one per-tensor scale."""
+def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=True, colwise=True,
+                       tile16=False):
+    """Rowwise and columnwise planes of bf16 x [rows, cols] under one per-tensor scale.
+
+    tile16: NVFP4Q_SCALE_16X16 (one block scale per 16 x 16 tile, shared by both planes).
+    """
     import torch
 
     _check_bf16_2d(x)
@@ -207,7 +212,8 @@ def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=
     scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
     ws = workspace(x.device)
     st = lib.nvfp4q_quantize_2d(x.data_ptr(), 0, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
-                                ctypes.byref(rp), ctypes.byref(cp), _rounding(rounding),
+                                ctypes.byref(rp), ctypes.byref(cp),
+                                _rounding(rounding) | (SCALE_16X16 if tile16 else 0),
                                 ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(), _stream(x))
     _check(st)
     return {"row_codes": rc, "row_scales": rs, "col_codes": cc, "col_scales": cs, "amax": amax_out,

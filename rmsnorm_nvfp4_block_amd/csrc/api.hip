@@ -179,11 +179,11 @@ nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows
   TRY(check_input(x, dtype, rows, cols, ld_x));
   const bool has_row = row && row->codes, has_col = col && col->codes;
   if (!has_row && !has_col) return NVFP4Q_E_NULLPTR;
+  const bool tile16 = ((int)rounding & NVFP4Q_SCALE_16X16) != 0;
+  rounding = (nvfp4q_rounding)((int)rounding & ~NVFP4Q_SCALE_16X16);
   if (has_row) TRY(check_plane(row, rows, cols));
-  if (has_col) {
-    if (rows % 16 != 0) return NVFP4Q_E_SHAPE;
-    TRY(check_plane(col, cols, rows));
-  }
+  if ((has_col || tile16) && rows % 16 != 0) return NVFP4Q_E_SHAPE;
+  if (has_col) TRY(check_plane(col, cols, rows));
   TRY(check_rounding(rounding, rng));
   TRY(check_ws(workspace, workspace_bytes));
   const nvfp4q_global& gg = g ? *g : kNoGlobal;
@@ -202,6 +202,7 @@ nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows
   a.x = x; a.rows = rows; a.cols = cols; a.ld_x = ld_x;
   if (has_row) { a.rcodes = row->codes; a.rldc = row->ld_codes; a.rscales = row->scales; a.rlds = row->ld_scales; }
   if (has_col) { a.ccodes = col->codes; a.cldc = col->ld_codes; a.cscales = col->scales; a.clds = col->ld_scales; }
+  a.tile16 = tile16;
   a.ws = (Workspace*)workspace;
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
   a.sr = base_rounding(rounding) == NVFP4Q_SR;

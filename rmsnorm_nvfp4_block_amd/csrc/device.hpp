@@ -440,15 +440,14 @@ uint32_t xcd_chunk(uint64_t items);     // 0 when the plain order is selected
 uint32_t xcd_grid(uint64_t items);      // workgroups to launch for `items` work items
 
 
-// Encode one 16-element block held by one lane (fp32 values that are bf16
-// values): block scale from the block max, encode multiplier from the table,
-// 16 codes in two words (element 2i in the low nibble of byte i). SR draws one
-// Philox evaluation for the block: elements 0-3 take word 0, 4-7 word 1,
-// 8-11 word 2, 12-15 word 3.
+// The codes of one 16-element block held by one lane (fp32 values that are
+// bf16 values) under scale code sc: encode multiplier from the table, 16 codes
+// in two words (element 2i in the low nibble of byte i). SR draws one Philox
+// evaluation for the block: elements 0-3 take word 0, 4-7 word 1, 8-11 word 2,
+// 12-15 word 3.
 template <bool SR>
-__device__ __forceinline__ uint2 encode_block16(float v[16], GScale g, const float* rcp_tab, uint32_t& sc,
-                                                uint64_t blk, uint64_t seed, uint32_t offset, uint32_t tag) {
-  sc = block_scale(max16_abs(v), g.enc);
+__device__ __forceinline__ uint2 encode_with_scale(float v[16], uint32_t sc, const float* rcp_tab, uint64_t blk,
+                                                   uint64_t seed, uint32_t offset, uint32_t tag) {
   const float rc = rcp_tab[sc];
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
@@ -462,6 +461,14 @@ __device__ __forceinline__ uint2 encode_block16(float v[16], GScale g, const flo
     out.y = rtne_pack8(v + 8);
   }
   return out;
+}
+
+// Encode with the block's own scale (from its maximum).
+template <bool SR>
+__device__ __forceinline__ uint2 encode_block16(float v[16], GScale g, const float* rcp_tab, uint32_t& sc,
+                                                uint64_t blk, uint64_t seed, uint32_t offset, uint32_t tag) {
+  sc = block_scale(max16_abs(v), g.enc);
+  return encode_with_scale<SR>(v, sc, rcp_tab, blk, seed, offset, tag);
 }
 
 }  // namespace nvfp4q

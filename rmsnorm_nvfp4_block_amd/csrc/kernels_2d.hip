@@ -12,9 +12,14 @@
 //  * Columnwise: thread t owns columns 4 * (t / 8) .. +3 of rows
 //    16 * (t % 8) .. +15 (16 LDS reads of 8 bytes), i.e. four columnwise blocks;
 //    eight consecutive threads write 64 contiguous code bytes of one plane row.
+//  * 16 x 16 tile scales (NVFP4Q_SCALE_16X16): each wave's eight rows of a
+//    16-row band meet in a lane shuffle per 16-column block, the two waves of
+//    a band in LDS behind the staging barrier, and both planes encode with
+//    the tile's scale.
 // "[nvfp4_training] Optimize CuteDSL kernels for NVFP4 training", Optimization
 // item 2 (the 2D weight kernel: wide shared-memory reads instead of 16-bit
-// ones, paired columnwise reads) and item 5 (scale bytes).
+// ones, paired columnwise reads sharing one amax and reciprocal) and item 5
+// (scale bytes).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -30,14 +35,17 @@ __device__ __forceinline__ uint32_t swz_chunk(uint32_t chunk, uint32_t row) {
 }
 
 // T threads per tile: 128 / (T / 8) rows (rowwise) and 1024 / T columns
-// (columnwise) per thread.
-template <int T, bool ROW, bool COL, bool SR>
+// (columnwise) per thread. TILE: one scale per 16 x 16 tile.
+template <int T, bool ROW, bool COL, bool SR, bool TILE>
 __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles_c, uint32_t ntiles, uint32_t chunk) {
   constexpr int kRpt = kTileR / (T / 8);  // rows per thread
   constexpr int kRs = T / 8;              // row stride between a thread's rows
   constexpr int kCpt = 1024 / T;          // columns per thread (columnwise)
+  constexpr int kW = T / 64;              // waves; wave w holds rows 8w .. 8w + 7 (+ kRs j)
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileR * kRowBytes];
   __shared__ float rcp_tab[128];
+  // TILE: maximum of each wave's 8 rows of every 16-column block, per row slot j
+  __shared__ float part[TILE ? kRpt : 1][TILE ? kW : 1][8];
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   const int64_t ld_x = a.ld_x;
@@ -85,6 +93,22 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
         *reinterpret_cast<uint4*>(tile + lr * kRowBytes + swz_chunk(2 * bsub + h, lr) * 16) = q[j][h];
     }
   }
+  const uint32_t wid = t >> 6;
+  if constexpr (TILE) {
+    // lanes bsub + 8k, k = 0..7, hold the wave's 8 rows of block bsub
+#pragma unroll
+    for (int j = 0; j < kRpt; ++j) {
+      float v[16];
+      widen8(q[j][0], v);
+      widen8(q[j][1], v + 8);
+      float m = max16_abs(v);
+      m = fmaxf(m, __shfl_xor(m, 8, 64));
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if ((t & 63) < 8) part[j][wid][t & 7] = m;
+    }
+    __syncthreads();  // also the staging barrier of the columnwise plane
+  }
   // ---- rowwise plane from registers
   if constexpr (ROW) {
     // block index, code and scale addresses of row r0 once; rows 32 apart
@@ -102,7 +126,15 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
       widen8(q[j][0], v);
       widen8(q[j][1], v + 8);
       uint32_t sc;
-      const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, blk0 + (uint64_t)(kRs * j) * nbr, seed, offset, 0);
+      uint2 w;
+      if constexpr (TILE) {
+        // the row's 16-row band lies in waves 2 (wid / 2) and 2 (wid / 2) + 1
+        const uint32_t w0 = wid & ~1u;
+        sc = block_scale(fmaxf(part[j][w0][bsub], part[j][w0 + 1][bsub]), g.enc);
+        w = encode_with_scale<SR>(v, sc, rcp_tab, blk0 + (uint64_t)(kRs * j) * nbr, seed, offset, 0);
+      } else {
+        w = encode_block16<SR>(v, g, rcp_tab, sc, blk0 + (uint64_t)(kRs * j) * nbr, seed, offset, 0);
+      }
       if (ok) {
         *reinterpret_cast<uint2*>(cp + (int64_t)(kRs * j) * rldc) = w;
         sp[(int64_t)(kRs * j) * rlds] = (uint8_t)sc;
@@ -111,7 +143,7 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   }
   // ---- columnwise plane from the staged tile
   if constexpr (COL) {
-    __syncthreads();
+    if constexpr (!TILE) __syncthreads();
     const uint32_t mb = t & 7, cg = t >> 3;           // 8 row blocks x T/8 column groups
     const uint32_t lc = cg * kCpt;                     // first local column
     const uint32_t cchunk = lc >> 3;                   // its 16-byte chunk of a staged row
@@ -135,15 +167,19 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
     const uint64_t cblk0 = (uint64_t)gc0 * nbc + (grow >> 4);
     uint8_t* ccp = ccodes + (int64_t)gc0 * cldc + (grow >> 1);
     uint8_t* csp = cscales + (int64_t)gc0 * clds + (grow >> 4);
+    uint32_t tsc = 0;  // TILE: the scale of tile (band mb, column block lc / 16)
+    if constexpr (TILE) {
+      const uint32_t jj = (mb * 16) / kRs, w0 = (mb * 16 - jj * kRs) / 8;
+      tsc = block_scale(fmaxf(part[jj][w0][lc >> 4], part[jj][w0 + 1][lc >> 4]), g.enc);
+    }
 #pragma unroll
     for (int c = 0; c < kCpt; ++c) {
       const uint32_t gc = gc0 + c;
       float v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = (c & 1) ? bf_hi(d[i][c >> 1]) : bf_lo(d[i][c >> 1]);
-      float m = max16_abs(v);
-      uint32_t sc = block_scale(m, g.enc);
-      float rc = rcp_tab[sc];
+      const uint32_t sc = TILE ? tsc : block_scale(max16_abs(v), g.enc);
+      const float rc = rcp_tab[sc];
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
       uint2 out;
@@ -163,7 +199,7 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   }
 }
 
-template <int T, bool ROW, bool COL>
+template <int T, bool ROW, bool COL, bool TILE>
 void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
   const uint32_t tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
   const uint32_t tiles_c = (uint32_t)((a.cols + kTileC - 1) / kTileC);
@@ -171,8 +207,8 @@ void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
   // measured slower here (8192 x 8192 with SR: 97.5 vs 91.3 us per step).
   const uint32_t ntiles = tiles_r * tiles_c, chunk = 0;
   dim3 grid(ntiles), block(T);
-  if (a.sr) hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, true>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
-  else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+  if (a.sr) hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, true, TILE>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+  else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false, TILE>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
 }
 
 // 512 threads per tile (two rows and two columns each): the tile's LDS
@@ -180,7 +216,8 @@ void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
 // waves, 3 us slower on 8192 x 8192 with SR).
 template <bool ROW, bool COL>
 void launch_2d_rc(const TwoDArgs& a, hipStream_t s) {
-  launch_2d_t<512, ROW, COL>(a, s);
+  if (a.tile16) launch_2d_t<512, ROW, COL, true>(a, s);
+  else launch_2d_t<512, ROW, COL, false>(a, s);
 }
 
 }  // namespace

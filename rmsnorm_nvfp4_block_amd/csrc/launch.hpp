@@ -45,6 +45,7 @@ struct TwoDArgs {
   const float* amax_in;
   float* amax_out;
   float* scale_out;
+  bool tile16;  // one scale per 16 x 16 tile (both planes)
   bool sr;
   uint64_t seed;
   uint32_t offset;

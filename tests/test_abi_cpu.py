@@ -167,4 +167,17 @@ def test_rounding_option_bits(lib):
                                   ctypes.byref(p), None, None, rounding, ctypes.byref(r), FAKE, 1 << 16, None)
 
     assert grouped(q.RTNE | q.FAST_MATH) == 6 and grouped(q.SR | q.FAST_MATH) == 6
-    assert grouped(2) == 4 and grouped(0x200) == 4 and grouped(q.SR | 0x200) == 4
+    assert grouped(2) == 4 and grouped(0x400) == 4 and grouped(q.SR | 0x400) == 4
+    assert "#define NVFP4Q_SCALE_16X16 0x200" in hdr and q.SCALE_16X16 == 0x200
+    assert grouped(q.SCALE_16X16) == 4      # tile scales exist on the 2D path only
+
+    def two_d(rounding, rows=64, colp=True):
+        p = q.Plane(FAKE, 64, FAKE, 8)
+        return lib.nvfp4q_quantize_2d(FAKE, 0, rows, 32, 32, ctypes.byref(g), ctypes.byref(p),
+                                      ctypes.byref(p) if colp else None, rounding, ctypes.byref(r), FAKE, 1 << 8,
+                                      None)
+
+    assert two_d(q.SCALE_16X16) == 6 and two_d(q.SR | q.SCALE_16X16 | q.FAST_MATH) == 6
+    assert two_d(q.SCALE_16X16 | 0x400) == 4
+    assert two_d(q.SCALE_16X16, rows=24, colp=False) == 2   # tiles need rows % 16 == 0
+    assert two_d(q.RTNE, rows=24, colp=False) == 6          # 1D rowwise does not

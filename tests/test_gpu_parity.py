@@ -289,6 +289,82 @@ def test_2d_weight_8192x8192_sampled(gpu_lib):
     assert_f32_bits("scale", f32(got["scale"])[0], qr["s_dec"])
 
 
+def _tile16_input(rng, shape):
+    # rows and columns of different magnitudes, so that tile scales differ from the 1D block scales
+    R, C = shape
+    x = rng.standard_normal(shape).astype(np.float32) * np.float32(0.02)
+    x *= np.exp(rng.uniform(-3, 3, (R, 1))).astype(np.float32) * np.exp(rng.uniform(-3, 3, (1, C))).astype(np.float32)
+    return workloads.to_bf16_bits(x)
+
+
+def _tile16_compare(got, q, R, C, rowwise=True, colwise=True):
+    if rowwise:
+        assert_same_bits("row codes", np_u8(got["row_codes"], C // 2), q["row"]["codes"])
+        assert_same_bits("row scales", np_u8(got["row_scales"], C // 16), q["row"]["scales"])
+    if colwise:
+        assert_same_bits("col codes", np_u8(got["col_codes"], R // 2), q["col"]["codes"])
+        assert_same_bits("col scales", np_u8(got["col_scales"], R // 16), q["col"]["scales"])
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (64, 48), (256, 384), (144, 272), (16, 2064), (528, 16)])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_2d_tile16_small(gpu_lib, shape, rounding):
+    # NVFP4Q_SCALE_16X16 (reading R-2dblk): one scale per 16 x 16 tile in both planes; partial 128 x 128
+    # work tiles at the right and bottom edges.
+    rng = np.random.default_rng(shape[0] * 3 + shape[1])
+    x = _tile16_input(rng, shape)
+    got = gpu_lib.nvfp4q_quantize_2d(to_dev(x), rounding=rounding, seed=0x5EED, offset=4, tile16=True)
+    q = oracle.quantize_2d_block(x, rounding=rounding, seed=0x5EED, offset=4)
+    _tile16_compare(got, q, *shape)
+    assert_f32_bits("amax", f32(got["amax"])[0], q["amax"])
+    assert_f32_bits("scale", f32(got["scale"])[0], q["s_dec"])
+
+
+def test_2d_tile16_single_planes_and_given_amax(gpu_lib):
+    import torch
+
+    rng = np.random.default_rng(20)
+    x = _tile16_input(rng, (96, 160))
+    q = oracle.quantize_2d_block(x, rounding="sr", seed=3)
+    a = torch.tensor([q["amax"]], dtype=torch.float32, device="cuda")
+    r = gpu_lib.nvfp4q_quantize_2d(to_dev(x), rounding="sr", seed=3, colwise=False, tile16=True)
+    c = gpu_lib.nvfp4q_quantize_2d(to_dev(x), rounding="sr", seed=3, rowwise=False, amax=a, tile16=True)
+    _tile16_compare(r, q, 96, 160, colwise=False)
+    _tile16_compare(c, q, 96, 160, rowwise=False)
+    assert_f32_bits("scale", f32(c["scale"])[0], q["s_dec"])
+    # a zero tile next to a non-zero one, and a whole zero tensor
+    z = x.copy()
+    z[16:32, :] = 0
+    z[:, 32:48] = 0
+    got = gpu_lib.nvfp4q_quantize_2d(to_dev(z), rounding="rtne", tile16=True)
+    _tile16_compare(got, oracle.quantize_2d_block(z), 96, 160)
+    z[:] = 0
+    got = gpu_lib.nvfp4q_quantize_2d(to_dev(z), rounding="sr", seed=1, tile16=True)
+    _tile16_compare(got, oracle.quantize_2d_block(z, rounding="sr", seed=1), 96, 160)
+
+
+def test_2d_tile16_weight_8192x8192_sampled(gpu_lib):
+    # The weight workload with tile scales, checked on windows of 32 x 64 (two tile rows, four tile
+    # columns) at the corners, at work-tile boundaries and at random places.
+    w = workloads.weight_2d()
+    got = gpu_lib.nvfp4q_quantize_2d(to_dev(w.x), rounding="sr", seed=w.seed, offset=w.offset, tile16=True)
+    amax = np.float32(np.max(np.abs(F.bf16_to_f32(w.x))))
+    assert_f32_bits("amax", f32(got["amax"])[0], amax)
+    rc, rs = np_u8(got["row_codes"], 4096), np_u8(got["row_scales"], 512)
+    cc, cs = np_u8(got["col_codes"], 4096), np_u8(got["col_scales"], 512)
+    rng = np.random.default_rng(12)
+    origins = [(0, 0), (8160, 8128), (96, 112), (128, 128), (4064, 0)]
+    origins += [(int(a) * 16, int(b) * 16) for a, b in zip(rng.integers(0, 510, 6), rng.integers(0, 508, 6))]
+    for r0, c0 in origins:
+        q = oracle.quantize_2d_block(w.x[r0:r0 + 32, c0:c0 + 64], amax=amax, rounding="sr", seed=w.seed,
+                                     offset=w.offset, origin=(r0, c0), full=(8192, 8192))
+        where = f" at ({r0}, {c0})"
+        assert_same_bits("row codes" + where, rc[r0:r0 + 32, c0 // 2:c0 // 2 + 32], q["row"]["codes"])
+        assert_same_bits("row scales" + where, rs[r0:r0 + 32, c0 // 16:c0 // 16 + 4], q["row"]["scales"])
+        assert_same_bits("col codes" + where, cc[c0:c0 + 64, r0 // 2:r0 // 2 + 16], q["col"]["codes"])
+        assert_same_bits("col scales" + where, cs[c0:c0 + 64, r0 // 16:r0 // 16 + 2], q["col"]["scales"])
+
+
 # ---------------------------------------------------------------- grouped
 def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offset=2, groups=None, amax=None,
                    fast_math=False, colwise=True, rowwise=False, row_amax=None):

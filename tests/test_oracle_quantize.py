@@ -250,3 +250,18 @@ def test_2d_block_tile_scale_is_the_largest_1d_scale_and_rtne_planes_transpose()
     dr = Q.dequantize_rowwise(q["row"]["codes"], q["row"]["scales"], q["s_dec"])
     dc = Q.dequantize_rowwise(q["col"]["codes"], q["col"]["scales"], q["s_dec"])
     assert np.array_equal(dr, dc.T)
+
+
+def test_2d_block_window_matches_the_full_tensor():
+    # A 16-aligned window quantized on its own (with the full tensor's amax and origin) gives the window
+    # of the full planes: the sampled checks of large tensors rely on it.
+    rng = np.random.default_rng(33)
+    x = F.f32_to_bf16(rng.standard_normal((96, 128)).astype(np.float32))
+    full = Q.quantize_2d_block(x, rounding="sr", seed=9, offset=1)
+    w = Q.quantize_2d_block(x[32:64, 48:112], amax=full["amax"], rounding="sr", seed=9, offset=1,
+                            origin=(32, 48), full=(96, 128))
+    rc, cc = F.unpack_nibbles(full["row"]["codes"]), F.unpack_nibbles(full["col"]["codes"])
+    assert np.array_equal(F.unpack_nibbles(w["row"]["codes"]), rc[32:64, 48:112])
+    assert np.array_equal(w["row"]["scales"], full["row"]["scales"][32:64, 3:7])
+    assert np.array_equal(F.unpack_nibbles(w["col"]["codes"]), cc[48:112, 32:64])
+    assert np.array_equal(w["col"]["scales"], full["col"]["scales"][48:112, 2:4])
