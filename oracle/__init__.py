@@ -58,6 +58,9 @@ that implements it. Readings are:
              amax through R-bscale), used by every element of the tile in
              both planes; the planes keep the 1D scale layout with the
              tile's code repeated on its 16 rows / 16 columns.
+  R-experts  grouped 2D weights: expert e of E stacked [M, K] weights is the
+             2D quantization of its own weight under its own amax, SR tags
+             2e (rowwise) and 2e + 1 (columnwise); planes stacked by expert.
   R-group    each group is zero-padded to a multiple of 16 rows, groups are
              laid out back to back in one transposed plane; storage past the
              last padded column is never written.
@@ -69,7 +72,7 @@ from .formats import (  # noqa: F401
 from .philox import philox4x32_10  # noqa: F401
 from .quantize import (  # noqa: F401
     global_scales, block_scale_codes, encode_reciprocal, quantize_blocks, quantize_rowwise,
-    quantize_colwise, quantize_2d, quantize_2d_block, encode_blocks, dequantize_rowwise, sr_round,
+    quantize_colwise, quantize_2d, quantize_2d_block, quantize_2d_experts, encode_blocks, dequantize_rowwise, sr_round,
 )
 from .rmsnorm import rmsnorm_bf16, rmsnorm_quantize  # noqa: F401
 from .rht import rht16, rht16_f32  # noqa: F401

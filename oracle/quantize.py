@@ -162,7 +162,7 @@ def quantize_rowwise(x, amax=None, rounding="rtne", seed=0, offset=0, tag=0, row
     }
 
 
-def quantize_colwise(x, amax=None, rounding="rtne", seed=0, offset=0, col_ids=None):
+def quantize_colwise(x, amax=None, rounding="rtne", seed=0, offset=0, col_ids=None, tag=1):
     """Columnwise (transposed) NVFP4 of x[M, K]; reading R-col.
 
     Blocks are 16 consecutive rows of one column; the output plane is the
@@ -175,7 +175,7 @@ def quantize_colwise(x, amax=None, rounding="rtne", seed=0, offset=0, col_ids=No
     assert M % BLOCK == 0
     a = _amax(xf) if amax is None else F32(amax)
     return quantize_rowwise(np.ascontiguousarray(xf.T), amax=a, rounding=rounding, seed=seed,
-                            offset=offset, tag=1, row_ids=col_ids)
+                            offset=offset, tag=tag, row_ids=col_ids)
 
 
 def quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0):
@@ -187,7 +187,7 @@ def quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0):
     return {"row": row, "col": col, "amax": F32(a), "s_enc": row["s_enc"], "s_dec": row["s_dec"]}
 
 
-def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0, origin=(0, 0), full=None):
+def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0, origin=(0, 0), full=None, tags=(0, 1)):
     """Rowwise and columnwise planes under one E4M3 scale per 16 x 16 tile (reading R-2dblk).
 
     PR, Optimization item 2 describes the 2D weight kernel's columnwise reads as
@@ -225,7 +225,7 @@ def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0, origin=(0
     if rounding == "sr":
         blk = (np.arange(r0, r0 + M, dtype=np.uint64)[:, None] * np.uint64(FK // BLOCK)
                + np.arange(c0 // BLOCK, (c0 + K) // BLOCK, dtype=np.uint64)[None, :])
-        rb = block_random_bytes(blk, 0, seed, offset)
+        rb = block_random_bytes(blk, tags[0], seed, offset)
     rcodes = encode_blocks(xf.reshape(M, K // BLOCK, BLOCK), row_sc, s_dec, rounding, rb)
     # columnwise: block (c, i) of the transposed plane takes tile (i, c // 16)
     xt = np.ascontiguousarray(xf.T)
@@ -234,12 +234,45 @@ def quantize_2d_block(x, amax=None, rounding="rtne", seed=0, offset=0, origin=(0
     if rounding == "sr":
         blk = (np.arange(c0, c0 + K, dtype=np.uint64)[:, None] * np.uint64(FM // BLOCK)
                + np.arange(r0 // BLOCK, (r0 + M) // BLOCK, dtype=np.uint64)[None, :])
-        cb = block_random_bytes(blk, 1, seed, offset)
+        cb = block_random_bytes(blk, tags[1], seed, offset)
     ccodes = encode_blocks(xt.reshape(K, M // BLOCK, BLOCK), col_sc, s_dec, rounding, cb)
     row = {"codes": pack_nibbles(rcodes.reshape(M, K)), "scales": row_sc.astype(np.uint8)}
     col = {"codes": pack_nibbles(ccodes.reshape(K, M)), "scales": col_sc.astype(np.uint8)}
     return {"row": row, "col": col, "tile_scales": tsc, "amax": F32(a), "s_enc": F32(s_enc),
             "s_dec": F32(s_dec)}
+
+
+def quantize_2d_experts(x, experts, amax=None, rounding="rtne", seed=0, offset=0, tile16=False):
+    """Grouped 2D weights: E experts' [M, K] weights stacked as x[E*M, K], each with its own amax.
+
+    PR, Performance measures a grouped 2D weight kernel (E = 4) beside the
+    single-weight one without defining how experts are told apart. Reading
+    R-experts: expert e is quantize_2d (or quantize_2d_block with tile16) of its
+    own weight under its own amax (max |x_e|, or amax[e]), with SR tags 2e
+    (rowwise) and 2e + 1 (columnwise), so expert 0 is the single-weight call and
+    no two experts share a random stream. Planes are stacked: rowwise codes
+    [E*M, K/2], scales [E*M, K/16]; columnwise codes [E*K, M/2], scales
+    [E*K, M/16] (expert e's transposed plane in rows e*K .. e*K + K - 1).
+    """
+    xf = _as_f32(x)
+    EM, K = xf.shape
+    assert experts >= 1 and EM % experts == 0
+    M = EM // experts
+    outs = []
+    for e in range(experts):
+        xe = xf[e * M:(e + 1) * M]
+        a = _amax(xe) if amax is None else F32(np.asarray(amax, dtype=F32)[e])
+        if tile16:
+            q = quantize_2d_block(xe, amax=a, rounding=rounding, seed=seed, offset=offset, tags=(2 * e, 2 * e + 1))
+            outs.append((q["row"], q["col"], a, q["s_dec"]))
+        else:
+            r = quantize_rowwise(xe, amax=a, rounding=rounding, seed=seed, offset=offset, tag=2 * e)
+            c = quantize_colwise(xe, amax=a, rounding=rounding, seed=seed, offset=offset, tag=2 * e + 1)
+            outs.append((r, c, a, r["s_dec"]))
+    cat = np.concatenate
+    return {"row": {"codes": cat([o[0]["codes"] for o in outs]), "scales": cat([o[0]["scales"] for o in outs])},
+            "col": {"codes": cat([o[1]["codes"] for o in outs]), "scales": cat([o[1]["scales"] for o in outs])},
+            "amax": np.array([o[2] for o in outs], F32), "s_dec": np.array([o[3] for o in outs], F32)}
 
 
 def dequantize_rowwise(codes, scales, s_dec):

@@ -265,3 +265,35 @@ def test_2d_block_window_matches_the_full_tensor():
     assert np.array_equal(w["row"]["scales"], full["row"]["scales"][32:64, 3:7])
     assert np.array_equal(F.unpack_nibbles(w["col"]["codes"]), cc[48:112, 32:64])
     assert np.array_equal(w["col"]["scales"], full["col"]["scales"][48:112, 2:4])
+
+
+# ---------------------------------------------------------------- grouped 2D weights (reading R-experts)
+@pytest.mark.parametrize("tile16", [False, True])
+def test_2d_experts_expert_zero_is_the_single_weight(tile16):
+    rng = np.random.default_rng(34)
+    x = F.f32_to_bf16(rng.standard_normal((3 * 48, 64)).astype(np.float32))
+    q = Q.quantize_2d_experts(x, 3, rounding="sr", seed=5, offset=2, tile16=tile16)
+    one = (Q.quantize_2d_block if tile16 else Q.quantize_2d)(x[:48], rounding="sr", seed=5, offset=2)
+    assert np.array_equal(q["row"]["codes"][:48], one["row"]["codes"])
+    assert np.array_equal(q["row"]["scales"][:48], one["row"]["scales"])
+    assert np.array_equal(q["col"]["codes"][:64], one["col"]["codes"])
+    assert np.array_equal(q["col"]["scales"][:64], one["col"]["scales"])
+    assert q["amax"][0] == one["amax"]
+
+
+def test_2d_experts_own_amax_and_own_streams():
+    # Expert 1 is expert 0 times 2^-7: with its own amax every RTNE code and block scale is the same and
+    # S_dec is 2^-7 times expert 0's (a shared amax would shift its block scales). With SR the two
+    # experts' codes differ (tags 0/1 against 2/3) while their scales stay equal.
+    rng = np.random.default_rng(35)
+    x0 = rng.standard_normal((32, 48)).astype(np.float32)
+    x = F.f32_to_bf16(np.concatenate([x0, x0 * np.float32(2.0 ** -7)]))
+    q = Q.quantize_2d_experts(x, 2)
+    for plane in ("row", "col"):
+        h = q[plane]["codes"].shape[0] // 2
+        assert np.array_equal(q[plane]["codes"][:h], q[plane]["codes"][h:])
+        assert np.array_equal(q[plane]["scales"][:h], q[plane]["scales"][h:])
+    assert q["s_dec"][1] == q["s_dec"][0] * np.float32(2.0 ** -7)
+    s = Q.quantize_2d_experts(x, 2, rounding="sr", seed=8)
+    assert not np.array_equal(s["row"]["codes"][:32], s["row"]["codes"][32:])
+    assert np.array_equal(s["row"]["scales"][:32], s["row"]["scales"][32:])
