@@ -61,9 +61,11 @@ class Case:
         if name in ("quantize", "prefill", "decode"):
             out_bytes = R * C // 2 + R * C // 16
             param_bytes = (C * 2 if w.gamma is not None else 0) + (C * 2 if w.beta is not None else 0)
-        elif name == "weight":
+        elif name in ("weight", "experts"):
             out_bytes = 2 * (R * C // 2 + R * C // 16)
             param_bytes = 0
+            if name == "experts":      # per-expert amax and S_dec (the 2D call's 8 bytes are added below)
+                out_bytes += 8 * (w.experts - 1)
         else:  # grouped
             G = len(w.offsets) - 1
             counts = np.diff(w.offsets)
@@ -94,7 +96,7 @@ class Case:
             self.row_outs = [(torch.empty((R, ldr), dtype=torch.uint8, device=dev),
                               torch.empty((R, C // 16), dtype=torch.uint8, device=dev)) if self.rowwise else (None, None)
                              for _ in range(self.nsets)]
-        elif name == "weight":
+        elif name in ("weight", "experts"):
             self.outs = [None] * self.nsets
         else:
             ldc = (C // 2 + 15) // 16 * 16
@@ -108,8 +110,11 @@ class Case:
         if self.name in ("prefill", "decode"):
             d.update({"tokens": self.rows, "hidden": self.cols, "op": "rmsnorm+nvfp4 rowwise",
                       "bias": w.beta is not None, "eps": w.eps})
-        elif self.name == "weight":
+        elif self.name in ("weight", "experts"):
             d.update({"op": "nvfp4 rowwise+columnwise (2D weight)", "seed": w.seed})
+            if self.name == "experts":
+                d.update({"op": "grouped 2D weights: nvfp4 rowwise+columnwise of stacked expert weights, "
+                                "per-expert amax", "experts": w.experts, "rows": self.rows // w.experts})
             if self.tile16:
                 d["op"] = "nvfp4 rowwise+columnwise (2D weight), one scale per 16x16 tile"
         elif self.name == "grouped":
@@ -145,6 +150,9 @@ class Case:
         if self.name == "weight":
             return q.nvfp4q_quantize_2d(x, amax=amax, rounding=w.rounding, seed=w.seed, offset=w.offset,
                                         tile16=self.tile16)
+        if self.name == "experts":
+            return q.nvfp4q_quantize_2d_grouped(x, w.experts, amax=amax, rounding=w.rounding, seed=w.seed,
+                                                offset=w.offset, tile16=self.tile16)
         return q.nvfp4q_grouped(x, self.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, amax=amax,
                                 rounding=w.rounding, seed=w.seed, offset=w.offset, codes=o[0], scales=o[1],
                                 fast_math=self.fast_math, colwise=self.colwise, rowwise=self.rowwise,
@@ -223,6 +231,28 @@ def cpu_baseline(case, budget_s=12.0):
                                     colwise=case.colwise, rowwise=case.rowwise)
             n = int(w.offsets[g + 1] - w.offsets[g])
             done_bytes += case.bytes * n / R
+        elif name == "experts":
+            # a band of rows of one expert (rowwise plane) and the same share of its columns (columnwise)
+            Re = R // w.experts
+            e = r0 // Re
+            rows = np.arange(r0, min((e + 1) * Re, r0 + chunk))
+            xe = w.x[e * Re:(e + 1) * Re]
+            lr = rows - e * Re
+            ncol = max(16, len(rows) * C // Re)
+            c0 = (lr[0] * C // Re) // 16 * 16
+            cols = np.arange(c0, min(C, c0 + ncol))
+            if case.tile16:
+                b0 = lr[0] // 16 * 16
+                oracle.quantize_2d_block(xe[b0:b0 + len(rows) // 16 * 16 or 16], amax=np.float32(1.0),
+                                         rounding=w.rounding, seed=w.seed, origin=(b0, 0), full=xe.shape,
+                                         tags=(2 * e, 2 * e + 1))
+            else:
+                oracle.quantize_rowwise(xe[lr], amax=np.float32(1.0), rounding=w.rounding, seed=w.seed,
+                                        tag=2 * e, row_ids=lr)
+                oracle.quantize_colwise(xe[:, cols], amax=np.float32(1.0), rounding=w.rounding, seed=w.seed,
+                                        col_ids=cols, tag=2 * e + 1)
+            done_bytes += case.bytes * len(rows) / R
+            r0 = (rows[-1] + 1) % R
         else:
             rows = np.arange(r0, min(R, r0 + chunk))
             xs = w.x[rows]
@@ -232,9 +262,9 @@ def cpu_baseline(case, budget_s=12.0):
                 oracle.quantize_rowwise(xs)
             else:
                 if case.tile16:
-                    r0 = rows[0] // 16 * 16
-                    oracle.quantize_2d_block(w.x[r0:r0 + len(rows)], amax=np.float32(1.0), rounding=w.rounding,
-                                             seed=w.seed, origin=(r0, 0), full=w.x.shape)
+                    b0 = rows[0] // 16 * 16
+                    oracle.quantize_2d_block(w.x[b0:b0 + len(rows)], amax=np.float32(1.0), rounding=w.rounding,
+                                             seed=w.seed, origin=(b0, 0), full=w.x.shape)
                 else:
                     oracle.quantize_rowwise(xs, amax=np.float32(1.0), rounding=w.rounding, seed=w.seed,
                                             row_ids=rows)
@@ -248,6 +278,9 @@ def cpu_baseline(case, budget_s=12.0):
         sample = f"{passes} groups of the grouped workload, one oracle call each"
     elif name == "weight":
         sample = f"{passes} calls of {chunk} rows + {chunk} columns of the 2D workload (both planes)"
+    elif name == "experts":
+        sample = (f"{passes} calls of up to {chunk} rows of one expert + the same share of its columns "
+                  f"(both planes)")
     else:
         sample = f"{passes} calls of {min(chunk, R)} consecutive rows of the {name} workload"
     threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
@@ -268,6 +301,7 @@ DOMINANT = {
     "decode": ("stage", "k_rms_coop (encode mode)", r"k_rms_coop<\d+, \d+, \w+, \w+, 1, \w+>"),
     "quantize": ("stage", "k_quant_rows", r"k_quant_rows"),
     "weight": ("stage", "k_quant_2d", r"k_quant_2d"),
+    "experts": ("stage", "k_quant_2d", r"k_quant_2d"),
     "grouped": ("stage", "k_grouped_quant", r"k_grouped_quant"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -396,7 +430,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="prefill", choices=["quantize", "prefill", "decode", "weight", "grouped"])
+    ap.add_argument("--config", default="prefill", choices=["quantize", "prefill", "decode", "weight", "grouped", "experts"])
     ap.add_argument("--fast-math", action="store_true",
                     help="grouped: NVFP4Q_FAST_MATH (no bf16 round-through of the transform's output)")
     ap.add_argument("--planes", default="col", choices=["col", "row", "both"],
@@ -448,8 +482,8 @@ def main():
         raise SystemExit("--planes applies to the grouped workload (the others name their planes already)")
     if args.fast_math and args.planes == "row":
         raise SystemExit("--fast-math concerns the transform, which the rowwise plane does not take")
-    if args.tile16 and args.config != "weight":
-        raise SystemExit("--tile16 applies to the weight workload (the 2D path)")
+    if args.tile16 and args.config not in ("weight", "experts"):
+        raise SystemExit("--tile16 applies to the weight and experts workloads (the 2D path)")
     case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes, tile16=args.tile16)
     log(f"[bench] {case.describe()}")
 

@@ -203,6 +203,27 @@ nvfp4q_status nvfp4q_quantize_2d(const void *x, nvfp4q_dtype dtype, int64_t rows
                                  void *stream);
 
 /*
+ * nvfp4q_quantize_2d_grouped -- nvfp4q_quantize_2d of `experts` weights of
+ * [rows, cols] each, stacked in x as [experts * rows, cols] (expert e in rows
+ * e * rows ..), in one launch per pass, each weight under its own amax.
+ *   g: amax_in / amax_out / scale_out hold `experts` floats each.
+ *   row: rowwise plane of the stacked x ([experts * rows] plane rows).
+ *   col: the experts' columnwise planes stacked: [experts * cols] plane rows,
+ *     expert e's transposed plane in plane rows e * cols ..
+ *   SR: expert e uses tag 2e (rowwise) and 2e + 1 (columnwise) with the block
+ *   indices of nvfp4q_quantize_2d of its own weight, so expert 0 matches that
+ *   call and no two experts share a random stream. NVFP4Q_SCALE_16X16 as there.
+ *   1 <= experts <= 64, else NVFP4Q_E_SHAPE.
+ *   [PR, Performance (grouped 2D weights, E = 4 experts, against a
+ *    precomputed amax)]
+ */
+nvfp4q_status nvfp4q_quantize_2d_grouped(const void *x, nvfp4q_dtype dtype, int32_t experts, int64_t rows,
+                                         int64_t cols, int64_t ld_x, const nvfp4q_global *g,
+                                         const nvfp4q_plane *row, const nvfp4q_plane *col,
+                                         nvfp4q_rounding rounding, const nvfp4q_rng *rng, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
+/*
  * nvfp4q_grouped -- per-group NVFP4 of a packed [total_rows, cols] bf16
  * tensor: the columnwise plane, optionally after a 16-point random Hadamard
  * transform along the rows of each 16-row block, and/or the rowwise plane,

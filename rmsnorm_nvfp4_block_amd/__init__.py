@@ -14,14 +14,14 @@ from typing import Optional
 
 __all__ = [
     "load", "lib_path", "workspace", "NVFP4QError",
-    "nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_grouped",
+    "nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped", "nvfp4q_grouped",
     "nvfp4q_workspace_bytes", "nvfp4q_status_string", "SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libnvfp4q.so")
 
-SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_grouped",
+SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped", "nvfp4q_grouped",
            "nvfp4q_workspace_bytes", "nvfp4q_status_string", "nvfp4q_version")
 
 RTNE, SR = 0, 1
@@ -72,6 +72,9 @@ def load():
     lib.nvfp4q_quantize_2d.restype = ctypes.c_int
     lib.nvfp4q_quantize_2d.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(Global), P(Plane), P(Plane), ctypes.c_int,
                                        P(Rng), vp, ctypes.c_size_t, vp]
+    lib.nvfp4q_quantize_2d_grouped.restype = ctypes.c_int
+    lib.nvfp4q_quantize_2d_grouped.argtypes = [vp, ctypes.c_int, i32, i64, i64, i64, P(Global), P(Plane), P(Plane),
+                                               ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
     lib.nvfp4q_grouped.restype = ctypes.c_int
     lib.nvfp4q_grouped.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, ctypes.c_int, u32, P(Global),
                                    P(Plane), P(Global), P(Plane), ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
@@ -215,6 +218,41 @@ def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=
                                 ctypes.byref(rp), ctypes.byref(cp),
                                 _rounding(rounding) | (SCALE_16X16 if tile16 else 0),
                                 ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(), _stream(x))
+    _check(st)
+    return {"row_codes": rc, "row_scales": rs, "col_codes": cc, "col_scales": cs, "amax": amax_out,
+            "scale": scale_out}
+
+
+def nvfp4q_quantize_2d_grouped(x, experts, amax=None, rounding="rtne", seed=0, offset=0, rowwise=True,
+                               colwise=True, tile16=False):
+    """nvfp4q_quantize_2d of `experts` weights stacked in bf16 x [experts * rows, cols], each under its own amax.
+
+    amax: optional float32 CUDA tensor [experts]. Returns row_codes [experts * rows, ...], row_scales,
+    col_codes [experts * cols, ...] (expert e's transposed plane in rows e * cols ..), col_scales, and
+    amax / scale [experts].
+    """
+    import torch
+
+    _check_bf16_2d(x)
+    lib = load()
+    ER, C = x.shape
+    if experts < 1 or ER % experts != 0:
+        raise ValueError("x must stack `experts` weights of equal row count")
+    R = ER // experts
+    rc = rs = cc = cs = None
+    rp = Plane(None, 0, None, 0)
+    cp = Plane(None, 0, None, 0)
+    if rowwise:
+        rc, rs, rp = _plane(ER, C, x.device)
+    if colwise:
+        cc, cs, cp = _plane(experts * C, R, x.device)
+    amax_out = torch.empty(experts, dtype=torch.float32, device=x.device)
+    scale_out = torch.empty(experts, dtype=torch.float32, device=x.device)
+    ws = workspace(x.device)
+    st = lib.nvfp4q_quantize_2d_grouped(x.data_ptr(), 0, experts, R, C, x.stride(0),
+                                        ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(rp),
+                                        ctypes.byref(cp), _rounding(rounding) | (SCALE_16X16 if tile16 else 0),
+                                        ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(), _stream(x))
     _check(st)
     return {"row_codes": rc, "row_scales": rs, "col_codes": cc, "col_scales": cs, "amax": amax_out,
             "scale": scale_out}

@@ -172,34 +172,44 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   return done(streamed ? launch_rms_stream_quant(a, s) : launch_rmsnorm_pass(a, false, s, nullptr));
 }
 
-nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows, int64_t cols, int64_t ld_x,
-                                 const nvfp4q_global* g, const nvfp4q_plane* row, const nvfp4q_plane* col,
-                                 nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  TRY(check_input(x, dtype, rows, cols, ld_x));
+}  // extern "C"
+
+namespace {
+
+// nvfp4q_quantize_2d over `experts` stacked weights of `rows` rows each.
+nvfp4q_status quantize_2d_impl(const void* x, nvfp4q_dtype dtype, int experts, int64_t rows, int64_t cols,
+                               int64_t ld_x, const nvfp4q_global* g, const nvfp4q_plane* row,
+                               const nvfp4q_plane* col, nvfp4q_rounding rounding, const nvfp4q_rng* rng,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0) return NVFP4Q_E_SHAPE;
+  TRY(check_input(x, dtype, experts * rows, cols, ld_x));
   const bool has_row = row && row->codes, has_col = col && col->codes;
   if (!has_row && !has_col) return NVFP4Q_E_NULLPTR;
   const bool tile16 = ((int)rounding & NVFP4Q_SCALE_16X16) != 0;
   rounding = (nvfp4q_rounding)((int)rounding & ~NVFP4Q_SCALE_16X16);
-  if (has_row) TRY(check_plane(row, rows, cols));
+  if (has_row) TRY(check_plane(row, experts * rows, cols));
   if ((has_col || tile16) && rows % 16 != 0) return NVFP4Q_E_SHAPE;
-  if (has_col) TRY(check_plane(col, cols, rows));
+  if (has_col) {
+    if (experts * cols > 0x7FFFFFFF) return NVFP4Q_E_SHAPE;
+    TRY(check_plane(col, experts * cols, rows));
+  }
   TRY(check_rounding(rounding, rng));
   TRY(check_ws(workspace, workspace_bytes));
   const nvfp4q_global& gg = g ? *g : kNoGlobal;
   hipStream_t s = (hipStream_t)stream;
-  if (rows == 0) return done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s));
+  if (rows == 0) return done(launch_empty_scale(gg.amax_out, gg.scale_out, experts, s));
   uint32_t nparts = 0;
   if (!gg.amax_in) {
     RowArgs r = {};
     r.x = x; r.rows = rows; r.cols = cols; r.ld_x = ld_x;
     r.ws = (Workspace*)workspace;
-    hipError_t e = launch_amax_rows(r, s, &nparts);
+    hipError_t e = launch_amax_rows(r, s, &nparts, experts);
     if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
   }
   TwoDArgs a = {};
   a.nparts = nparts;
   a.x = x; a.rows = rows; a.cols = cols; a.ld_x = ld_x;
+  a.experts = experts;
   if (has_row) { a.rcodes = row->codes; a.rldc = row->ld_codes; a.rscales = row->scales; a.rlds = row->ld_scales; }
   if (has_col) { a.ccodes = col->codes; a.cldc = col->ld_codes; a.cscales = col->scales; a.clds = col->ld_scales; }
   a.tile16 = tile16;
@@ -208,6 +218,28 @@ nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows
   a.sr = base_rounding(rounding) == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   return done(launch_quant_2d(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4q_status nvfp4q_quantize_2d(const void* x, nvfp4q_dtype dtype, int64_t rows, int64_t cols, int64_t ld_x,
+                                 const nvfp4q_global* g, const nvfp4q_plane* row, const nvfp4q_plane* col,
+                                 nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return quantize_2d_impl(x, dtype, 1, rows, cols, ld_x, g, row, col, rounding, rng, workspace, workspace_bytes,
+                          stream);
+}
+
+nvfp4q_status nvfp4q_quantize_2d_grouped(const void* x, nvfp4q_dtype dtype, int32_t experts, int64_t rows,
+                                         int64_t cols, int64_t ld_x, const nvfp4q_global* g,
+                                         const nvfp4q_plane* row, const nvfp4q_plane* col,
+                                         nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (experts < 1 || experts > 64) return NVFP4Q_E_SHAPE;
+  return quantize_2d_impl(x, dtype, experts, rows, cols, ld_x, g, row, col, rounding, rng, workspace,
+                          workspace_bytes, stream);
 }
 
 nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_rows, int64_t cols, int64_t ld_x,

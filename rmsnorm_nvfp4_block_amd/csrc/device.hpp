@@ -361,10 +361,12 @@ __device__ __forceinline__ float reduce_partials(const Workspace* ws, uint32_t f
 
 // Per-tensor scales for an encode kernel, into every thread, and the encode
 // reciprocal table into LDS: from amax_in when given, otherwise the max of the
-// `nparts` partials of the amax pass. Workgroup 0 reports amax and S_dec.
+// `nparts` partials of the amax pass. Workgroup 0 of the tensor (blockIdx.x 0;
+// a launch over several tensors has one per blockIdx.y, and passes that
+// tensor's amax_out / scale_out) reports amax and S_dec.
 __device__ __forceinline__ GScale scales_from(float a, float* amax_out, float* scale_out, float* rcp_tab) {
   const GScale g = global_scale(a);
-  if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
     if (amax_out) *amax_out = a;
     if (scale_out) *scale_out = g.dec;
   }
@@ -375,8 +377,9 @@ __device__ __forceinline__ GScale scales_from(float a, float* amax_out, float* s
 
 template <int NW = kWavesPerWG>
 __device__ __forceinline__ GScale consume_scales(const Workspace* ws, uint32_t nparts, const float* amax_in,
-                                                 float* amax_out, float* scale_out, float* rcp_tab) {
-  return scales_from(amax_in ? *amax_in : reduce_partials<NW>(ws, 0, nparts), amax_out, scale_out, rcp_tab);
+                                                 float* amax_out, float* scale_out, float* rcp_tab,
+                                                 uint32_t first = 0) {
+  return scales_from(amax_in ? *amax_in : reduce_partials<NW>(ws, first, nparts), amax_out, scale_out, rcp_tab);
 }
 
 // The same in two steps, so that a kernel can issue these loads before its

@@ -12,6 +12,8 @@
 //  * Columnwise: thread t owns columns 4 * (t / 8) .. +3 of rows
 //    16 * (t % 8) .. +15 (16 LDS reads of 8 bytes), i.e. four columnwise blocks;
 //    eight consecutive threads write 64 contiguous code bytes of one plane row.
+//  * Several stacked weights (experts) in one launch: grid y is the expert;
+//    each has its own amax and SR tags 2e (rowwise) and 2e + 1 (columnwise).
 //  * 16 x 16 tile scales (NVFP4Q_SCALE_16X16): each wave's eight rows of a
 //    16-row band meet in a lane shuffle per 16-column block, the two waves of
 //    a band in LDS behind the staging barrier, and both planes encode with
@@ -46,14 +48,15 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   __shared__ float rcp_tab[128];
   // TILE: maximum of each wave's 8 rows of every 16-column block, per row slot j
   __shared__ float part[TILE ? kRpt : 1][TILE ? kW : 1][8];
-  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  const uint32_t e = blockIdx.y;  // expert
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   const int64_t ld_x = a.ld_x;
-  uint8_t* __restrict__ rcodes = a.rcodes;
-  uint8_t* __restrict__ rscales = a.rscales;
-  uint8_t* __restrict__ ccodes = a.ccodes;
-  uint8_t* __restrict__ cscales = a.cscales;
   const int64_t rldc = a.rldc, rlds = a.rlds, cldc = a.cldc, clds = a.clds;
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x + (int64_t)e * rows * ld_x;
+  uint8_t* __restrict__ rcodes = ROW ? a.rcodes + (int64_t)e * rows * rldc : nullptr;
+  uint8_t* __restrict__ rscales = ROW ? a.rscales + (int64_t)e * rows * rlds : nullptr;
+  uint8_t* __restrict__ ccodes = COL ? a.ccodes + (int64_t)e * cols * cldc : nullptr;
+  uint8_t* __restrict__ cscales = COL ? a.cscales + (int64_t)e * cols * clds : nullptr;
   const uint64_t seed = a.seed;
   const uint32_t offset = a.offset;
   const uint32_t t = threadIdx.x;
@@ -83,7 +86,9 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
       q[j][1] = ld16(xp + (int64_t)(kRs * j) * ld_x + 8, ok);
     }
   }
-  const GScale g = consume_scales<T / 64>(a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
+  const GScale g = consume_scales<T / 64>(a.ws, a.nparts, a.amax_in ? a.amax_in + e : nullptr,
+                                          a.amax_out ? a.amax_out + e : nullptr,
+                                          a.scale_out ? a.scale_out + e : nullptr, rcp_tab, e * a.nparts);
   if constexpr (COL) {
 #pragma unroll
     for (int j = 0; j < kRpt; ++j) {
@@ -131,9 +136,9 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
         // the row's 16-row band lies in waves 2 (wid / 2) and 2 (wid / 2) + 1
         const uint32_t w0 = wid & ~1u;
         sc = block_scale(fmaxf(part[j][w0][bsub], part[j][w0 + 1][bsub]), g.enc);
-        w = encode_with_scale<SR>(v, sc, rcp_tab, blk0 + (uint64_t)(kRs * j) * nbr, seed, offset, 0);
+        w = encode_with_scale<SR>(v, sc, rcp_tab, blk0 + (uint64_t)(kRs * j) * nbr, seed, offset, 2 * e);
       } else {
-        w = encode_block16<SR>(v, g, rcp_tab, sc, blk0 + (uint64_t)(kRs * j) * nbr, seed, offset, 0);
+        w = encode_block16<SR>(v, g, rcp_tab, sc, blk0 + (uint64_t)(kRs * j) * nbr, seed, offset, 2 * e);
       }
       if (ok) {
         *reinterpret_cast<uint2*>(cp + (int64_t)(kRs * j) * rldc) = w;
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
       for (int i = 0; i < 16; ++i) v[i] = v[i] * rc;
       uint2 out;
       if constexpr (SR) {
-        U4 w = block_random(cblk0 + (uint64_t)c * nbc, 1, seed, offset);
+        U4 w = block_random(cblk0 + (uint64_t)c * nbc, 2 * e + 1, seed, offset);
         out.x = sr_pack8(v, w.x, w.y);
         out.y = sr_pack8(v + 8, w.z, w.w);
       } else {
@@ -206,7 +211,7 @@ void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
   // Plain row-major tile order: the per-XCD ranges used by the grouped path
   // measured slower here (8192 x 8192 with SR: 97.5 vs 91.3 us per step).
   const uint32_t ntiles = tiles_r * tiles_c, chunk = 0;
-  dim3 grid(ntiles), block(T);
+  dim3 grid(ntiles, a.experts), block(T);
   if (a.sr) hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, true, TILE>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
   else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false, TILE>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
 }

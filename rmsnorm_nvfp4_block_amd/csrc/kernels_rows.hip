@@ -31,12 +31,13 @@ namespace nvfp4q {
 // A wave takes one span of kAmaxLoads * 512 columns of one row at a time and
 // issues all of its 16-byte loads at once (16 KB in flight per wave) through
 // a buffer resource that ends at the row's last column, so reads past cols
-// return zero without guards.
+// return zero without guards. A launch over several stacked tensors of `rows`
+// rows each (grid y = tensor) keeps one set of partials per tensor.
 constexpr int kAmaxLoads = 16;
 constexpr uint32_t kAmaxSpan = kAmaxLoads * 512;
 constexpr int kAmaxMaxWGs = 2048;
 __global__ __launch_bounds__(kThreads) void k_amax_rows(const RowArgs a) {
-  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x + (int64_t)blockIdx.y * a.rows * a.ld_x;
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)((blockIdx.x * kThreads + threadIdx.x) >> 6));
@@ -116,13 +117,13 @@ hipError_t launch_empty_scale(float* amax_out, float* scale_out, int n, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s, uint32_t* nparts) {
+hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s, uint32_t* nparts, int tensors) {
   const int64_t units = a.rows * ((a.cols + kAmaxSpan - 1) / kAmaxSpan);  // one per wave at most
   int64_t wgs = (units + kWavesPerWG - 1) / kWavesPerWG;
   if (wgs > kAmaxMaxWGs) wgs = kAmaxMaxWGs;
   if (wgs < 1) wgs = 1;
   *nparts = (uint32_t)wgs;
-  hipLaunchKernelGGL(k_amax_rows, dim3((uint32_t)wgs), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(k_amax_rows, dim3((uint32_t)wgs, (uint32_t)tensors), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ struct TwoDArgs {
   const float* amax_in;
   float* amax_out;
   float* scale_out;
+  int experts;   // stacked weights (grid y); rows is the rows of one weight
   bool tile16;  // one scale per 16 x 16 tile (both planes)
   bool sr;
   uint64_t seed;
@@ -85,8 +86,9 @@ struct GroupArgs {
 
 hipError_t launch_empty_scale(float* amax_out, float* scale_out, int n, hipStream_t s);
 // Amax pass over a [rows, cols] tensor; returns the number of partials it
-// writes through `nparts`.
-hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s, uint32_t* nparts);
+// writes through `nparts`. tensors > 1: that many stacked [rows, cols]
+// tensors, the partials of tensor e in slots e * nparts onwards.
+hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s, uint32_t* nparts, int tensors = 1);
 hipError_t launch_quant_rows(const RowArgs& a, hipStream_t s);
 // Two-pass RMSNorm: with amax_pass, the amax pass (sets *nparts); otherwise the
 // encode pass (reads a.nparts partials when a.amax_in is NULL).

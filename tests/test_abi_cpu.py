@@ -26,9 +26,10 @@ def lib():
     return q.load()
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     d = _declared()
-    for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_grouped"):
+    for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped",
+                 "nvfp4q_grouped"):
         assert name in d
 
 
@@ -40,7 +41,8 @@ def test_every_declared_symbol_is_exported(lib):
 def test_binding_names_match_the_abi():
     import rmsnorm_nvfp4_block_amd as q
 
-    for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_grouped"):
+    for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped",
+                 "nvfp4q_grouped"):
         assert callable(getattr(q, name))
 
 
@@ -126,6 +128,17 @@ def test_2d_and_grouped_validation(lib):
                                   ctypes.byref(r), FAKE, 1 << 16, None) == 2
     assert lib.nvfp4q_quantize_2d(FAKE, 0, 32, 32, 32, ctypes.byref(g), ctypes.byref(none), ctypes.byref(none), 0,
                                   ctypes.byref(r), FAKE, 1 << 16, None) == 1
+
+    def experts(e, rows=64, cols=32, rowp=row, colp=col, rounding=0):
+        return lib.nvfp4q_quantize_2d_grouped(FAKE, 0, e, rows, cols, cols, ctypes.byref(g), ctypes.byref(rowp),
+                                              ctypes.byref(colp), rounding, ctypes.byref(r), FAKE, 1 << 8, None)
+
+    big_row, big_col = q.Plane(FAKE, 16, FAKE, 2), q.Plane(FAKE, 32, FAKE, 4)
+    assert experts(0) == 2 and experts(65) == 2
+    assert experts(4, rowp=big_row, colp=big_col) == 6                   # valid; stops at the small workspace
+    assert experts(4, rows=24, rowp=big_row, colp=none) == 6             # rowwise only: rows need not be 16k
+    assert experts(4, rows=24, rowp=big_row, colp=big_col) == 2          # columnwise needs rows % 16 == 0
+    assert experts(4, rows=24, rowp=big_row, colp=none, rounding=0x200) == 2   # and so do tile scales
 
     def grouped(groups=4, rht=1, mask=0x1234, ldc=64, lds=8, offs=FAKE, rows=64, ld=32, colp=True, rowp=None):
         p = q.Plane(FAKE, ldc, FAKE, lds)

@@ -365,6 +365,65 @@ def test_2d_tile16_weight_8192x8192_sampled(gpu_lib):
         assert_same_bits("col scales" + where, cs[c0:c0 + 64, r0 // 16:r0 // 16 + 2], q["col"]["scales"])
 
 
+# ---------------------------------------------------------------- grouped 2D weights (reading R-experts)
+@pytest.mark.parametrize("experts,shape", [(1, (48, 80)), (3, (144, 272)), (4, (16, 2064))])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+@pytest.mark.parametrize("tile16", [False, True])
+def test_2d_experts_small(gpu_lib, experts, shape, rounding, tile16):
+    rng = np.random.default_rng(experts * 100 + shape[1])
+    x = np.concatenate([_tile16_input(rng, shape) for _ in range(experts)])
+    got = gpu_lib.nvfp4q_quantize_2d_grouped(to_dev(x), experts, rounding=rounding, seed=0xE0, offset=5,
+                                             tile16=tile16)
+    q = oracle.quantize_2d_experts(x, experts, rounding=rounding, seed=0xE0, offset=5, tile16=tile16)
+    R, C = shape
+    _tile16_compare(got, q, R, C)
+    for e in range(experts):
+        assert_f32_bits(f"expert {e} amax", f32(got["amax"])[e], q["amax"][e])
+        assert_f32_bits(f"expert {e} scale", f32(got["scale"])[e], q["s_dec"][e])
+
+
+def test_2d_experts_given_amax_and_single_planes(gpu_lib):
+    import torch
+
+    rng = np.random.default_rng(21)
+    x = np.concatenate([_tile16_input(rng, (64, 96)) for _ in range(4)])
+    amax = np.array([0.5, 3.0, 0.0, 1e-3], np.float32)
+    a = torch.tensor(amax, device="cuda")
+    q = oracle.quantize_2d_experts(x, 4, amax=amax, rounding="sr", seed=2)
+    r = gpu_lib.nvfp4q_quantize_2d_grouped(to_dev(x), 4, amax=a, rounding="sr", seed=2, colwise=False)
+    c = gpu_lib.nvfp4q_quantize_2d_grouped(to_dev(x), 4, amax=a, rounding="sr", seed=2, rowwise=False)
+    _tile16_compare(r, q, 64, 96, colwise=False)
+    _tile16_compare(c, q, 64, 96, rowwise=False)
+    for e in range(4):
+        assert_f32_bits(f"expert {e} scale", f32(c["scale"])[e], q["s_dec"][e])
+
+
+def test_2d_experts_4x4096x7168_sampled(gpu_lib):
+    # The grouped-weight workload (four stacked 4096 x 7168 weights, SR), checked on sampled rows and
+    # columns of every expert against the oracle's rowwise and columnwise planes with that expert's tags.
+    w = workloads.experts_2d()
+    E, R, C = w.experts, w.rows // w.experts, w.cols
+    got = gpu_lib.nvfp4q_quantize_2d_grouped(to_dev(w.x), E, rounding="sr", seed=w.seed, offset=w.offset)
+    rc, rs = np_u8(got["row_codes"], C // 2), np_u8(got["row_scales"], C // 16)
+    cc, cs = np_u8(got["col_codes"], R // 2), np_u8(got["col_scales"], R // 16)
+    rng = np.random.default_rng(13)
+    for e in range(E):
+        xe = w.x[e * R:(e + 1) * R]
+        amax = np.float32(np.max(np.abs(F.bf16_to_f32(xe))))
+        assert_f32_bits(f"expert {e} amax", f32(got["amax"])[e], amax)
+        rows = np.unique(np.concatenate([[0, 127, 128, R - 1], rng.choice(R, 12, replace=False)]))
+        cols = np.unique(np.concatenate([[0, 127, 128, C - 1], rng.choice(C, 12, replace=False)]))
+        qr = oracle.quantize_rowwise(xe[rows], amax=amax, rounding="sr", seed=w.seed, offset=w.offset,
+                                     tag=2 * e, row_ids=rows)
+        qc = oracle.quantize_colwise(xe[:, cols], amax=amax, rounding="sr", seed=w.seed, offset=w.offset,
+                                     col_ids=cols, tag=2 * e + 1)
+        assert_same_bits(f"expert {e} row codes", rc[e * R + rows], qr["codes"])
+        assert_same_bits(f"expert {e} row scales", rs[e * R + rows], qr["scales"])
+        assert_same_bits(f"expert {e} col codes", cc[e * C + cols], qc["codes"])
+        assert_same_bits(f"expert {e} col scales", cs[e * C + cols], qc["scales"])
+        assert_f32_bits(f"expert {e} scale", f32(got["scale"])[e], qr["s_dec"])
+
+
 # ---------------------------------------------------------------- grouped
 def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offset=2, groups=None, amax=None,
                    fast_math=False, colwise=True, rowwise=False, row_amax=None):

@@ -27,6 +27,7 @@ __all__ = [
     "decode",
     "weight_2d",
     "grouped_moe",
+    "experts_2d",
     "make",
     "NAMES",
     "SR_SEED",
@@ -61,6 +62,7 @@ class Workload:
     offsets: Optional[np.ndarray] = None  # int32 [G+1] for grouped inputs
     rht_mask: int = 0
     apply_rht: bool = False
+    experts: int = 1                    # stacked weights (grouped 2D weights)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -123,12 +125,24 @@ def grouped_moe(seed: int = 5, tokens: int = 16384, hidden: int = 7168, groups: 
                     colwise=True, offsets=offsets, rht_mask=mask, apply_rht=apply_rht)
 
 
+def experts_2d(seed: int = 6, experts: int = 4, rows: int = 4096, cols: int = 7168) -> Workload:
+    """Grouped 2D weights: `experts` stacked [rows, cols] weights (a DeepSeek-V3 style gate/up projection
+    of 2 x 2048 rows over hidden 7168, four local experts), expert e ~N(0, 0.02 s_e) with s_e drawn from
+    U(0.5, 2) so that the experts' amax differ; stochastic rounding."""
+    rng = np.random.default_rng(seed)
+    s = rng.uniform(0.5, 2.0, experts).astype(np.float32)
+    x = np.concatenate([_normal(rng, (rows, cols), std=0.02) * s[e] for e in range(experts)])
+    return Workload(f"experts_{experts}x{rows}x{cols}", to_bf16_bits(x), rounding="sr", colwise=True,
+                    experts=experts)
+
+
 NAMES = {
     "quantize": quantize_only,
     "prefill": prefill,
     "decode": decode,
     "weight": weight_2d,
     "grouped": grouped_moe,
+    "experts": experts_2d,
 }
 
 
