@@ -438,6 +438,8 @@ def main():
     ap.add_argument("--tile16", action="store_true",
                     help="weight: NVFP4Q_SCALE_16X16 (one block scale per 16x16 tile, shared by both planes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-only", action="store_true",
+                    help="time only the roofline kernel with a given amax (for kernel traces); no metric line")
     ap.add_argument("--eager", action="store_true", help="time plain calls instead of a HIP graph replay")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES",
                     help="only run plain copies of BYTES (for the counter calibration runs)")
@@ -487,12 +489,24 @@ def main():
     case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes, tile16=args.tile16)
     log(f"[bench] {case.describe()}")
 
+    how, kname, _ = DOMINANT[args.config]
+    if args.stage_only:
+        # for a kernel trace of the roofline kernel alone: one eager call for the amax, then its graph
+        if how != "stage":
+            raise SystemExit("--stage-only needs a workload whose roofline kernel is timed alone")
+        given = case.given(case.step(0))
+        torch.cuda.synchronize()
+        kms = time_steps(case, args.steps, args.warmup, given=given, eager=args.eager)
+        log(f"[bench] {kname} alone (given amax): {kms * 1e3:.2f} us/launch")
+        print(json.dumps({"stage_only": True, "config": case.describe(), "kernel": kname,
+                          "launch_us": round(kms * 1e3, 3), "bytes_per_launch": case.bytes}), flush=True)
+        return
+
     # whole step (amax + quantize), the figure the metric is quoted on
     ms = time_steps(case, args.steps, args.warmup, eager=args.eager)
     log(f"[bench] full step: {ms * 1e3:.2f} us/step")
     value = case.bytes / (ms * 1e-3) / 1e9
 
-    how, kname, _ = DOMINANT[args.config]
     if how == "stage":
         # the encode kernel alone against the amax the full step produced
         given = case.given(case.step(0))
