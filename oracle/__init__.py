@@ -61,6 +61,9 @@ that implements it. Readings are:
   R-experts  grouped 2D weights: expert e of E stacked [M, K] weights is the
              2D quantization of its own weight under its own amax, SR tags
              2e (rowwise) and 2e + 1 (columnwise); planes stacked by expert.
+  R-qk       QK norm: the RMSNorm formula above applied to each attention head
+             (64, 128 or 256 elements) of q and of k, each tensor with its own
+             weight of head_dim entries, output in the input's place.
   R-group    each group is zero-padded to a multiple of 16 rows, groups are
              laid out back to back in one transposed plane; storage past the
              last padded column is never written.
@@ -74,6 +77,6 @@ from .quantize import (  # noqa: F401
     global_scales, block_scale_codes, encode_reciprocal, quantize_blocks, quantize_rowwise,
     quantize_colwise, quantize_2d, quantize_2d_block, quantize_2d_experts, encode_blocks, dequantize_rowwise, sr_round,
 )
-from .rmsnorm import rmsnorm_bf16, rmsnorm_quantize  # noqa: F401
+from .rmsnorm import rmsnorm_bf16, rmsnorm_quantize, qk_norm  # noqa: F401
 from .rht import rht16, rht16_f32  # noqa: F401
 from .grouped import padded_offsets, grouped_quantize  # noqa: F401

@@ -44,3 +44,21 @@ def rmsnorm_quantize(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None
     q = quantize_rowwise(y, amax=amax, rounding=rounding, seed=seed, offset=offset, tag=0)
     q["y"] = y
     return q
+
+
+def qk_norm(q, k, q_weight, k_weight, head_dim, weight_offset=0.0, eps=1e-6):
+    """Per-head RMSNorm of the attention heads of q [T, Hq*D] and k [T, Hk*D] (reading R-qk).
+
+    Blog, QK Norm: the norm is applied per head (64, 128 or 256 elements), each
+    tensor with its own weight vector of head_dim entries, in place, through the
+    same formula as above: y = (w + c) * (x * r), r = rsqrt(sum x^2 / D + EPS),
+    cast back to the element type. This is rmsnorm_bf16 over rows of head_dim
+    elements. k may be None.
+    """
+    def one(x, w):
+        x = np.asarray(x, dtype=np.uint16)
+        T = x.shape[0]
+        assert x.shape[1] % head_dim == 0
+        return rmsnorm_bf16(x.reshape(-1, head_dim), w, None, weight_offset, eps).reshape(T, -1)
+
+    return one(q, q_weight), (None if k is None else one(k, k_weight))

@@ -209,3 +209,45 @@ def test_grouped_rowwise_uses_each_groups_own_amax_and_ignores_the_transform():
             # a block holding its group's amax gets the saturating scale code 0x7E (448)
             r, c = np.unravel_index(np.argmax(np.abs(xf[lo:hi])), xf[lo:hi].shape)
             assert a["row_scales"][lo + r, c // 16] == 0x7E
+
+
+# ---- QK norm (reading R-qk) ----
+
+def test_qk_norm_hand_head():
+    # One head of 64 with x = (3, 4, 0, ...): mean x^2 = 25/64, r = 8/5, so (3, 4) -> (4.8, 6.4), which
+    # round to the bfloat16 values 4.8125 and 6.40625 (without the square root r would be 64/25 and the
+    # outputs 7.68 and 10.24). The second head, x = 2 everywhere, gives 1 everywhere; with eps = 0 exactly.
+    x = np.zeros((1, 128), np.float32)
+    x[0, 0], x[0, 1] = 3.0, 4.0
+    x[0, 64:] = 2.0
+    w = _bits(np.ones(64))
+    y, _ = oracle.qk_norm(_bits(x), None, w, None, 64, eps=0.0)
+    yf = F.bf16_to_f32(y)[0]
+    assert yf[0] == 4.8125 and yf[1] == 6.40625 and np.all(yf[2:64] == 0.0)
+    assert np.all(yf[64:] == 1.0)
+
+
+def test_qk_norm_is_per_head_and_per_tensor_weight():
+    # Heads of very different sizes come out with unit RMS (weight 1, eps negligible), each head is
+    # unchanged by scaling it by a power of two, and k uses its own weight.
+    rng = np.random.default_rng(36)
+    T, Hq, Hk, D = 6, 4, 2, 128
+    scale = np.exp2(rng.integers(-12, 12, (T, Hq, 1))).astype(np.float32)
+    q = _bits((rng.standard_normal((T, Hq, D)) * scale).reshape(T, Hq * D))
+    k = _bits(rng.standard_normal((T, Hk * D)))
+    ones = _bits(np.ones(D))
+    kw = _bits(1.0 + 0.25 * rng.standard_normal(D))
+    yq, yk = oracle.qk_norm(q, k, ones, kw, D, eps=1e-30)
+    rms = np.sqrt(np.mean(F.bf16_to_f32(yq).astype(np.float64).reshape(T, Hq, D) ** 2, axis=-1))
+    assert np.all(np.abs(rms - 1.0) < 2.0 ** -7)
+    q2 = F.bf16_to_f32(q).reshape(T, Hq, D).copy()
+    q2[:, 1] *= np.float32(2.0 ** 5)
+    yq2, _ = oracle.qk_norm(_bits(q2.reshape(T, Hq * D)), None, ones, None, D, eps=1e-30)
+    assert np.array_equal(yq2, yq)
+    yk_plain, _ = oracle.qk_norm(k, None, ones, None, D, eps=1e-30)
+    kw64 = F.bf16_to_f32(kw).astype(np.float64)
+    unit = F.bf16_to_f32(yk_plain).astype(np.float64).reshape(T, Hk, D)
+    expect = F.f64_to_bf16((kw64 * unit).reshape(T, -1))
+    # k's weight applied per element of each head: within two bf16 roundings of w * (unit-weight output)
+    diff = np.abs(F.bf16_to_f32(yk).astype(np.float64) - F.bf16_to_f32(expect).astype(np.float64))
+    assert np.all(diff <= 2.0 ** -6 * np.abs(F.bf16_to_f32(expect)) + 1e-30)
