@@ -61,6 +61,10 @@ class Case:
         if name in ("quantize", "prefill", "decode"):
             out_bytes = R * C // 2 + R * C // 16
             param_bytes = (C * 2 if w.gamma is not None else 0) + (C * 2 if w.beta is not None else 0)
+        elif name == "qknorm":           # in place: q and k read and written once, two weights read
+            out_bytes = R * C * 2 + w.meta["k"].size * 4
+            param_bytes = 2 * 2 * w.meta["head_dim"]
+            x_bytes = R * C * 2
         elif name in ("weight", "experts"):
             out_bytes = 2 * (R * C // 2 + R * C // 16)
             param_bytes = 0
@@ -77,7 +81,7 @@ class Case:
             if self.rowwise:  # the rowwise plane and its per-group amax and S_dec
                 out_bytes += R * C // 2 + R * C // 16 + 8 * G
             param_bytes = 4 * (G + 1)
-        self.bytes = x_bytes + out_bytes + param_bytes + (8 if name != "grouped" else 0)
+        self.bytes = x_bytes + out_bytes + param_bytes + (8 if name not in ("grouped", "qknorm") else 0)
         set_bytes = x_bytes + out_bytes
         self.nsets = max(1, math.ceil(ROTATE_BYTES / set_bytes))
         x0 = d(w.x)
@@ -98,6 +102,11 @@ class Case:
                              for _ in range(self.nsets)]
         elif name in ("weight", "experts"):
             self.outs = [None] * self.nsets
+        elif name == "qknorm":
+            k0 = d(w.meta["k"])
+            self.ks = [k0] + [k0.clone() for _ in range(self.nsets - 1)]
+            self.outs = [None] * self.nsets
+            self.wk = d(w.meta["k_weight"])
         else:
             ldc = (C // 2 + 15) // 16 * 16
             self.outs = [(torch.empty((R, ldc), dtype=torch.uint8, device=dev),
@@ -110,6 +119,10 @@ class Case:
         if self.name in ("prefill", "decode"):
             d.update({"tokens": self.rows, "hidden": self.cols, "op": "rmsnorm+nvfp4 rowwise",
                       "bias": w.beta is not None, "eps": w.eps})
+        elif self.name == "qknorm":
+            d.update({"op": "per-head RMSNorm of q and k in place (QK norm)", "tokens": self.rows,
+                      "q_heads": self.cols // w.meta["head_dim"], "k_heads": w.meta["k"].shape[1] // w.meta["head_dim"],
+                      "head_dim": w.meta["head_dim"], "eps": w.eps})
         elif self.name in ("weight", "experts"):
             d.update({"op": "nvfp4 rowwise+columnwise (2D weight)", "seed": w.seed})
             if self.name == "experts":
@@ -150,6 +163,8 @@ class Case:
         if self.name == "weight":
             return q.nvfp4q_quantize_2d(x, amax=amax, rounding=w.rounding, seed=w.seed, offset=w.offset,
                                         tile16=self.tile16)
+        if self.name == "qknorm":
+            return q.nvfp4q_qk_norm(x, self.ks[i % self.nsets], self.gamma, self.wk, w.meta["head_dim"], eps=w.eps)
         if self.name == "experts":
             return q.nvfp4q_quantize_2d_grouped(x, w.experts, amax=amax, rounding=w.rounding, seed=w.seed,
                                                 offset=w.offset, tile16=self.tile16)
@@ -260,6 +275,8 @@ def cpu_baseline(case, budget_s=12.0):
                 oracle.rmsnorm_quantize(xs, w.gamma, w.beta, w.weight_offset, w.eps)
             elif name == "quantize":
                 oracle.quantize_rowwise(xs)
+            elif name == "qknorm":
+                oracle.qk_norm(xs, w.meta["k"][rows], w.gamma, w.meta["k_weight"], w.meta["head_dim"], eps=w.eps)
             else:
                 if case.tile16:
                     b0 = rows[0] // 16 * 16
@@ -302,6 +319,7 @@ DOMINANT = {
     "quantize": ("stage", "k_quant_rows", r"k_quant_rows"),
     "weight": ("stage", "k_quant_2d", r"k_quant_2d"),
     "experts": ("stage", "k_quant_2d", r"k_quant_2d"),
+    "qknorm": ("step", "k_qk_norm", r"k_qk_norm"),
     "grouped": ("stage", "k_grouped_quant", r"k_grouped_quant"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -430,7 +448,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="prefill", choices=["quantize", "prefill", "decode", "weight", "grouped", "experts"])
+    ap.add_argument("--config", default="prefill", choices=["quantize", "prefill", "decode", "weight", "grouped", "experts", "qknorm"])
     ap.add_argument("--fast-math", action="store_true",
                     help="grouped: NVFP4Q_FAST_MATH (no bf16 round-through of the transform's output)")
     ap.add_argument("--planes", default="col", choices=["col", "row", "both"],

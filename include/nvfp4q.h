@@ -224,6 +224,28 @@ nvfp4q_status nvfp4q_quantize_2d_grouped(const void *x, nvfp4q_dtype dtype, int3
                                          size_t workspace_bytes, void *stream);
 
 /*
+ * nvfp4q_qk_norm -- per-head RMSNorm of the attention heads of q and k, in
+ * place, one launch for both ("CuTeDSL at Perplexity", QK Norm):
+ *   y = bf16((w + c) * (x * r)),  r = 1 / sqrt(sum x^2 / head_dim + eps)
+ * over each head of head_dim (64, 128 or 256; else NVFP4Q_E_UNSUPPORTED)
+ * consecutive elements, fp32 arithmetic, written over x.
+ *   q: device bf16, `tokens` rows of q_heads * head_dim elements, row stride
+ *     ld_q elements (multiple of 8, 16-byte aligned); k likewise with k_heads
+ *     and ld_k. Either head count may be 0 (its pointers then unused), not
+ *     both.
+ *   q_weight, k_weight: device bf16 [head_dim], 16-byte aligned.
+ *   weight_offset: c, 0 or 1; eps >= 0 (float32).
+ *   No workspace; no output besides q and k. The pages fix no reduction
+ *   order: the sum of squares is an fp32 sum in DPP steps, r comes from
+ *   v_rsq_f32 (within 1 ulp), so y can differ from the exactly rounded value
+ *   by about one bf16 step.
+ */
+nvfp4q_status nvfp4q_qk_norm(void *q, void *k, nvfp4q_dtype dtype, int64_t tokens, int32_t q_heads,
+                             int32_t k_heads, int32_t head_dim, int64_t ld_q, int64_t ld_k,
+                             const void *q_weight, const void *k_weight, float weight_offset, float eps,
+                             void *stream);
+
+/*
  * nvfp4q_grouped -- per-group NVFP4 of a packed [total_rows, cols] bf16
  * tensor: the columnwise plane, optionally after a 16-point random Hadamard
  * transform along the rows of each 16-row block, and/or the rowwise plane,

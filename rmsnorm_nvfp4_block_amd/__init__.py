@@ -15,13 +15,14 @@ from typing import Optional
 __all__ = [
     "load", "lib_path", "workspace", "NVFP4QError",
     "nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped", "nvfp4q_grouped",
-    "nvfp4q_workspace_bytes", "nvfp4q_status_string", "SYMBOLS",
+    "nvfp4q_qk_norm", "nvfp4q_workspace_bytes", "nvfp4q_status_string", "SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libnvfp4q.so")
 
 SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped", "nvfp4q_grouped",
+           "nvfp4q_qk_norm",
            "nvfp4q_workspace_bytes", "nvfp4q_status_string", "nvfp4q_version")
 
 RTNE, SR = 0, 1
@@ -75,6 +76,8 @@ def load():
     lib.nvfp4q_quantize_2d_grouped.restype = ctypes.c_int
     lib.nvfp4q_quantize_2d_grouped.argtypes = [vp, ctypes.c_int, i32, i64, i64, i64, P(Global), P(Plane), P(Plane),
                                                ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
+    lib.nvfp4q_qk_norm.restype = ctypes.c_int
+    lib.nvfp4q_qk_norm.argtypes = [vp, vp, ctypes.c_int, i64, i32, i32, i32, i64, i64, vp, vp, f32, f32, vp]
     lib.nvfp4q_grouped.restype = ctypes.c_int
     lib.nvfp4q_grouped.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, ctypes.c_int, u32, P(Global),
                                    P(Plane), P(Global), P(Plane), ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
@@ -256,6 +259,37 @@ def nvfp4q_quantize_2d_grouped(x, experts, amax=None, rounding="rtne", seed=0, o
     _check(st)
     return {"row_codes": rc, "row_scales": rs, "col_codes": cc, "col_scales": cs, "amax": amax_out,
             "scale": scale_out}
+
+
+def nvfp4q_qk_norm(q, k, q_weight, k_weight, head_dim, weight_offset=0.0, eps=1e-6):
+    """Per-head RMSNorm of bf16 q [tokens, q_heads * head_dim] and k [tokens, k_heads * head_dim], in place.
+
+    Either of q and k (with its weight) may be None. Weights: bf16 [head_dim]. Returns (q, k).
+    """
+    import torch
+
+    ts = [t for t in (q, k) if t is not None]
+    if not ts:
+        raise ValueError("give q, k or both")
+    for t, w in ((q, q_weight), (k, k_weight)):
+        if t is None:
+            continue
+        _check_bf16_2d(t)
+        if t.shape[1] % head_dim:
+            raise ValueError("row length must be a multiple of head_dim")
+        if w is None or w.dtype != torch.bfloat16 or w.numel() != head_dim or not w.is_contiguous():
+            raise ValueError("weights must be contiguous bf16 vectors of head_dim elements")
+    if len(ts) == 2 and q.shape[0] != k.shape[0]:
+        raise ValueError("q and k need the same number of tokens")
+    lib = load()
+    hq = q.shape[1] // head_dim if q is not None else 0
+    hk = k.shape[1] // head_dim if k is not None else 0
+    st = lib.nvfp4q_qk_norm(_ptr(q), _ptr(k), 0, ts[0].shape[0], hq, hk, head_dim,
+                            q.stride(0) if q is not None else 0, k.stride(0) if k is not None else 0,
+                            _ptr(q_weight) if q is not None else None, _ptr(k_weight) if k is not None else None,
+                            float(weight_offset), float(eps), _stream(ts[0]))
+    _check(st)
+    return q, k
 
 
 def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr", seed=0, offset=0,

@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libnvfp4q.so")
 SOURCES = [
     "api.hip", "kernels_rows.hip", "kernels_rms_coop.hip",
     "kernels_rms_stream.hip",
-    "kernels_2d.hip", "kernels_grouped.hip",
+    "kernels_2d.hip", "kernels_grouped.hip", "kernels_qk.hip",
 ]
 ARCH = "gfx950"
 

@@ -242,6 +242,29 @@ nvfp4q_status nvfp4q_quantize_2d_grouped(const void* x, nvfp4q_dtype dtype, int3
                           workspace_bytes, stream);
 }
 
+nvfp4q_status nvfp4q_qk_norm(void* q, void* k, nvfp4q_dtype dtype, int64_t tokens, int32_t q_heads,
+                             int32_t k_heads, int32_t head_dim, int64_t ld_q, int64_t ld_k, const void* q_weight,
+                             const void* k_weight, float weight_offset, float eps, void* stream) {
+  if (dtype != NVFP4Q_BF16) return NVFP4Q_E_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return NVFP4Q_E_UNSUPPORTED;
+  if (tokens < 0 || q_heads < 0 || k_heads < 0 || q_heads + k_heads < 1) return NVFP4Q_E_SHAPE;
+  if (tokens > 0x7FFFFFFF || (int64_t)q_heads + k_heads > 65536) return NVFP4Q_E_SHAPE;
+  if (q_heads > 0 && ld_q < (int64_t)q_heads * head_dim) return NVFP4Q_E_SHAPE;
+  if (k_heads > 0 && ld_k < (int64_t)k_heads * head_dim) return NVFP4Q_E_SHAPE;
+  if (weight_offset != 0.0f && weight_offset != 1.0f) return NVFP4Q_E_UNSUPPORTED;
+  if (!(eps >= 0.0f)) return NVFP4Q_E_SHAPE;
+  if (tokens > 0 && q_heads > 0 && (!q || !q_weight)) return NVFP4Q_E_NULLPTR;
+  if (tokens > 0 && k_heads > 0 && (!k || !k_weight)) return NVFP4Q_E_NULLPTR;
+  if (q_heads > 0 && (!aligned(q, 16) || !aligned(q_weight, 16) || ld_q % 8 != 0)) return NVFP4Q_E_ALIGN;
+  if (k_heads > 0 && (!aligned(k, 16) || !aligned(k_weight, 16) || ld_k % 8 != 0)) return NVFP4Q_E_ALIGN;
+  QkArgs a = {};
+  a.q = q; a.k = k; a.wq = q_weight; a.wk = k_weight;
+  a.tokens = tokens; a.ldq = ld_q; a.ldk = ld_k;
+  a.hq = q_heads; a.hk = k_heads; a.d = head_dim;
+  a.woff = weight_offset; a.eps = eps;
+  return done(launch_qk_norm(a, (hipStream_t)stream));
+}
+
 nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_rows, int64_t cols, int64_t ld_x,
                              const int32_t* offsets, int32_t num_groups, int32_t* padded_offsets_out,
                              int apply_rht, uint32_t rht_sign_mask, const nvfp4q_global* g,

@@ -32,6 +32,17 @@ struct RowArgs {
   uint32_t offset;
 };
 
+// Arguments of the per-head QK norm (in place).
+struct QkArgs {
+  void* q;
+  void* k;
+  const void* wq;
+  const void* wk;
+  int64_t tokens, ldq, ldk;
+  int hq, hk, d;
+  float woff, eps;
+};
+
 // Arguments of the 2D (rowwise + columnwise) path.
 struct TwoDArgs {
   const void* x;
@@ -100,6 +111,7 @@ hipError_t launch_rms_stream_quant(const RowArgs& a, hipStream_t s);
 int rms_max_cols();
 
 hipError_t launch_quant_2d(const TwoDArgs& a, hipStream_t s);
+hipError_t launch_qk_norm(const QkArgs& a, hipStream_t s);
 
 // Grouped path; hipErrorInvalidValue when the tile grid exceeds the workspace.
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s);

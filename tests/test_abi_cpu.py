@@ -115,6 +115,20 @@ def test_rmsnorm_validation(lib):
     assert call(ws=None) == 6
 
 
+def test_qk_norm_validation(lib):
+    def call(d=128, hq=4, hk=2, ldq=512, ldk=256, q=FAKE, k=FAKE, wq=FAKE, wk=FAKE, woff=0.0, eps=1e-6, t=3):
+        return lib.nvfp4q_qk_norm(q, k, 0, t, hq, hk, d, ldq, ldk, wq, wk, woff, eps, None)
+
+    assert call(d=96) == 4 and call(d=512) == 4
+    assert call(hq=0, hk=0) == 2 and call(hq=-1) == 2
+    assert call(ldq=504) == 2 and call(ldk=248) == 2
+    assert call(q=None) == 1 and call(wk=None) == 1
+    assert call(q=FAKE + 8) == 3 and call(ldq=516) == 3
+    assert call(woff=0.5) == 4 and call(eps=-1.0) == 2
+    assert call(t=0, q=None, k=None, wq=None, wk=None) == 0      # nothing to do, nothing launched
+    assert call(hk=0, t=0, k=None, wk=None) == 0
+
+
 def test_2d_and_grouped_validation(lib):
     import rmsnorm_nvfp4_block_amd as q
 

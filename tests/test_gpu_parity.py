@@ -240,6 +240,52 @@ def test_rmsnorm_given_amax_and_y_only(gpu_lib):
     assert np.array_equal(to_np_bf16(y_only["y"]), to_np_bf16(got["y"]))
 
 
+# ---------------------------------------------------------------- QK norm (reading R-qk)
+def _check_qk(y_gpu, x, w, head_dim, woff, eps):
+    T = x.shape[0]
+    _, y64, _ = oracle.rmsnorm_bf16(x.reshape(-1, head_dim), w, None, woff, eps, return_f64=True)
+    yg = F.bf16_to_f32(y_gpu).astype(np.float64).reshape(-1, head_dim)
+    err = np.abs(yg - y64)
+    assert np.all(err <= 1e-2 * np.abs(y64) + 2.0 ** -20), f"QK norm error max {err.max()}"
+    ref, _ = oracle.qk_norm(x, None, w, None, head_dim, woff, eps)
+    assert ref.shape == (T, x.shape[1])
+
+
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
+@pytest.mark.parametrize("tokens,hq,hk", [(1, 4, 0), (7, 5, 3), (129, 32, 8), (3, 0, 2)])
+@pytest.mark.parametrize("woff", [0.0, 1.0])
+def test_qk_norm_small(gpu_lib, head_dim, tokens, hq, hk, woff):
+    import torch
+
+    rng = np.random.default_rng(head_dim + 10 * tokens + hq)
+    w = workloads.qk_heads(seed=int(rng.integers(1 << 20)), tokens=tokens, q_heads=max(hq, 1), k_heads=max(hk, 1),
+                           head_dim=head_dim)
+    q, k = w.x[:, :hq * head_dim], w.meta["k"][:, :hk * head_dim]
+    # rows padded by 24 elements: the padding must stay untouched
+    qd = torch.full((tokens, hq * head_dim + 24), 7.0, dtype=torch.bfloat16, device="cuda")
+    kd = torch.full((tokens, hk * head_dim + 24), 7.0, dtype=torch.bfloat16, device="cuda")
+    qd[:, :hq * head_dim] = to_dev(q)
+    kd[:, :hk * head_dim] = to_dev(k)
+    qv, kv = qd[:, :hq * head_dim], kd[:, :hk * head_dim]
+    gpu_lib.nvfp4q_qk_norm(qv if hq else None, kv if hk else None, to_dev(w.gamma) if hq else None,
+                           to_dev(w.meta["k_weight"]) if hk else None, head_dim, weight_offset=woff, eps=w.eps)
+    if hq:
+        _check_qk(to_np_bf16(qv), q, w.gamma, head_dim, woff, w.eps)
+    if hk:
+        _check_qk(to_np_bf16(kv), k, w.meta["k_weight"], head_dim, woff, w.eps)
+    assert torch.all(qd[:, hq * head_dim:] == 7.0) and torch.all(kd[:, hk * head_dim:] == 7.0)
+
+
+def test_qk_norm_4096_tokens_32q_8k_heads_of_128(gpu_lib):
+    w = workloads.qk_heads()
+    qd, kd = to_dev(w.x), to_dev(w.meta["k"])
+    gpu_lib.nvfp4q_qk_norm(qd, kd, to_dev(w.gamma), to_dev(w.meta["k_weight"]), 128, eps=w.eps)
+    rng = np.random.default_rng(15)
+    rows = np.unique(np.concatenate([[0, 1, 4095], rng.choice(4096, 200, replace=False)]))
+    _check_qk(to_np_bf16(qd)[rows], w.x[rows], w.gamma, 128, 0.0, w.eps)
+    _check_qk(to_np_bf16(kd)[rows], w.meta["k"][rows], w.meta["k_weight"], 128, 0.0, w.eps)
+
+
 # ---------------------------------------------------------------- 2D
 @pytest.mark.parametrize("shape", [(16, 16), (64, 48), (256, 384), (144, 272), (16, 2064), (528, 16)])
 @pytest.mark.parametrize("rounding", ["rtne", "sr"])

@@ -28,6 +28,7 @@ __all__ = [
     "weight_2d",
     "grouped_moe",
     "experts_2d",
+    "qk_heads",
     "make",
     "NAMES",
     "SR_SEED",
@@ -136,6 +137,20 @@ def experts_2d(seed: int = 6, experts: int = 4, rows: int = 4096, cols: int = 71
                     experts=experts)
 
 
+def qk_heads(seed: int = 7, tokens: int = 4096, q_heads: int = 32, k_heads: int = 8, head_dim: int = 128) -> Workload:
+    """QK norm: q [tokens, q_heads * head_dim] and k [tokens, k_heads * head_dim] (a Qwen3 style attention
+    layer: 32 query and 8 key heads of 128), x ~N(0, 1) times a per-(token, head) factor exp(U(-2, 2)); weights
+    1 + 0.1 N(0, 1), eps 1e-6. x holds q, gamma q's weight; meta holds k, k's weight and head_dim."""
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (tokens, q_heads, head_dim)) * np.exp(rng.uniform(-2, 2, (tokens, q_heads, 1))).astype(np.float32)
+    k = _normal(rng, (tokens, k_heads, head_dim)) * np.exp(rng.uniform(-2, 2, (tokens, k_heads, 1))).astype(np.float32)
+    wq = to_bf16_bits(1.0 + 0.1 * _normal(rng, (head_dim,)))
+    wk = to_bf16_bits(1.0 + 0.1 * _normal(rng, (head_dim,)))
+    return Workload(f"qknorm_{tokens}x{q_heads}+{k_heads}x{head_dim}", to_bf16_bits(q.reshape(tokens, -1)),
+                    gamma=wq, eps=1e-6,
+                    meta={"k": to_bf16_bits(k.reshape(tokens, -1)), "k_weight": wk, "head_dim": head_dim})
+
+
 NAMES = {
     "quantize": quantize_only,
     "prefill": prefill,
@@ -143,6 +158,7 @@ NAMES = {
     "weight": weight_2d,
     "grouped": grouped_moe,
     "experts": experts_2d,
+    "qknorm": qk_heads,
 }
 
 
