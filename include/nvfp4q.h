@@ -83,7 +83,12 @@ typedef enum {
   NVFP4Q_E_WORKSPACE = 6    /* workspace missing, misaligned or too small */
 } nvfp4q_status;
 
-typedef enum { NVFP4Q_BF16 = 0 } nvfp4q_dtype;
+/* Element type of the input. nvfp4q_quantize and nvfp4q_qk_norm take all
+ * three (the quantizer reads the values exactly as given; the QK norm writes
+ * its output in the input's type, rounded to nearest even); the other entry
+ * points take NVFP4Q_BF16 only (else NVFP4Q_E_UNSUPPORTED). Rows of x start
+ * 16-byte aligned: ld_x * element size is a multiple of 16. */
+typedef enum { NVFP4Q_BF16 = 0, NVFP4Q_FP16 = 1, NVFP4Q_FP32 = 2 } nvfp4q_dtype;
 
 /* Rounding of the E2M1 codes. NVFP4Q_FAST_MATH may be OR-ed into the value
  * passed as `rounding` ([PR, Fast math]): with the grouped transform on, the
@@ -138,8 +143,8 @@ const char *nvfp4q_status_string(nvfp4q_status s);
 int nvfp4q_version(void);
 
 /*
- * nvfp4q_quantize -- rowwise NVFP4 of a [rows, cols] bf16 tensor.
- *   x: device, rows x cols, row stride ld_x elements.
+ * nvfp4q_quantize -- rowwise NVFP4 of a [rows, cols] bf16, fp16 or fp32 tensor.
+ *   x: device, rows x cols of dtype, row stride ld_x elements.
  *   g: per-tensor scale (amax computed from x unless g->amax_in is given).
  *   row: the rowwise plane [rows][cols/2] codes, [rows][cols/16] scales.
  *   rounding: NVFP4Q_RTNE or NVFP4Q_SR (rng used, tag 0,
@@ -226,14 +231,15 @@ nvfp4q_status nvfp4q_quantize_2d_grouped(const void *x, nvfp4q_dtype dtype, int3
 /*
  * nvfp4q_qk_norm -- per-head RMSNorm of the attention heads of q and k, in
  * place, one launch for both ("CuTeDSL at Perplexity", QK Norm):
- *   y = bf16((w + c) * (x * r)),  r = 1 / sqrt(sum x^2 / head_dim + eps)
+ *   y = RN((w + c) * (x * r)),  r = 1 / sqrt(sum x^2 / head_dim + eps)
  * over each head of head_dim (64, 128 or 256; else NVFP4Q_E_UNSUPPORTED)
- * consecutive elements, fp32 arithmetic, written over x.
- *   q: device bf16, `tokens` rows of q_heads * head_dim elements, row stride
- *     ld_q elements (multiple of 8, 16-byte aligned); k likewise with k_heads
- *     and ld_k. Either head count may be 0 (its pointers then unused), not
+ * consecutive elements, fp32 arithmetic, rounded to nearest even in the
+ * input's type (fp32: not rounded further) and written over x.
+ *   q: device bf16, fp16 or fp32 (dtype), `tokens` rows of q_heads *
+ *     head_dim elements, row stride ld_q elements (16-byte aligned rows); k
+ *     likewise with k_heads and ld_k. Either head count may be 0 (its pointers then unused), not
  *     both.
- *   q_weight, k_weight: device bf16 [head_dim], 16-byte aligned.
+ *   q_weight, k_weight: device [head_dim] of the same dtype, 16-byte aligned.
  *   weight_offset: c, 0 or 1; eps >= 0 (float32).
  *   No workspace; no output besides q and k. The pages fix no reduction
  *   order: the sum of squares is an fp32 sum in DPP steps, r comes from

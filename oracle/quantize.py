@@ -130,7 +130,7 @@ def _amax(xf):
 
 
 def quantize_rowwise(x, amax=None, rounding="rtne", seed=0, offset=0, tag=0, row_ids=None):
-    """Rowwise NVFP4 of x[M, K] (bf16 bits or float32 holding bf16 values).
+    """Rowwise NVFP4 of x[M, K]: bf16 bits (uint16), or float16 / float32 values taken as they are.
 
     Blocks are 16 consecutive elements of a row. Reading R-blk: the SR block
     index is row * (K/16) + kb. Returns a dict with codes [M, K/2] (packed),

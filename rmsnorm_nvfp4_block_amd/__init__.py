@@ -134,6 +134,16 @@ def _check_bf16_2d(x):
         raise ValueError("x must be a 2-D row-contiguous bfloat16 CUDA tensor")
 
 
+def _dtype_code(x):
+    """nvfp4q_dtype of a 2-D row-contiguous CUDA tensor (bf16, fp16 or fp32)."""
+    import torch
+
+    codes = {torch.bfloat16: 0, torch.float16: 1, torch.float32: 2}
+    if x.dtype not in codes or x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a 2-D row-contiguous bfloat16, float16 or float32 CUDA tensor")
+    return codes[x.dtype]
+
+
 def _plane(rows: int, cols: int, device, codes=None, scales=None):
     """Allocate (or wrap) a plane of `rows` plane rows of `cols` elements."""
     import torch
@@ -151,17 +161,17 @@ def _global(amax_in, amax_out, scale_out):
 
 
 def nvfp4q_quantize(x, amax=None, rounding="rtne", seed=0, offset=0, codes=None, scales=None):
-    """Rowwise NVFP4 of a bf16 [rows, cols] tensor. Returns dict(codes, scales, amax, scale)."""
+    """Rowwise NVFP4 of a bf16, fp16 or fp32 [rows, cols] tensor. Returns dict(codes, scales, amax, scale)."""
     import torch
 
-    _check_bf16_2d(x)
+    dt = _dtype_code(x)
     lib = load()
     R, C = x.shape
     c, s, plane = _plane(R, C, x.device, codes, scales)
     amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
     scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
     ws = workspace(x.device)
-    st = lib.nvfp4q_quantize(x.data_ptr(), 0, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
+    st = lib.nvfp4q_quantize(x.data_ptr(), dt, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
                              ctypes.byref(plane), _rounding(rounding), ctypes.byref(Rng(seed, offset)),
                              ws.data_ptr(), ws.numel(), _stream(x))
     _check(st)
@@ -262,29 +272,30 @@ def nvfp4q_quantize_2d_grouped(x, experts, amax=None, rounding="rtne", seed=0, o
 
 
 def nvfp4q_qk_norm(q, k, q_weight, k_weight, head_dim, weight_offset=0.0, eps=1e-6):
-    """Per-head RMSNorm of bf16 q [tokens, q_heads * head_dim] and k [tokens, k_heads * head_dim], in place.
+    """Per-head RMSNorm of q [tokens, q_heads * head_dim] and k [tokens, k_heads * head_dim], in place.
 
-    Either of q and k (with its weight) may be None. Weights: bf16 [head_dim]. Returns (q, k).
+    bf16, fp16 or fp32 (q, k and both weights of one dtype). Either of q and k (with its weight) may be
+    None. Weights: [head_dim]. Returns (q, k).
     """
-    import torch
-
     ts = [t for t in (q, k) if t is not None]
     if not ts:
         raise ValueError("give q, k or both")
+    dt = _dtype_code(ts[0])
     for t, w in ((q, q_weight), (k, k_weight)):
         if t is None:
             continue
-        _check_bf16_2d(t)
+        if _dtype_code(t) != dt:
+            raise ValueError("q and k must share a dtype")
         if t.shape[1] % head_dim:
             raise ValueError("row length must be a multiple of head_dim")
-        if w is None or w.dtype != torch.bfloat16 or w.numel() != head_dim or not w.is_contiguous():
-            raise ValueError("weights must be contiguous bf16 vectors of head_dim elements")
+        if w is None or w.dtype != t.dtype or w.numel() != head_dim or not w.is_contiguous():
+            raise ValueError("weights must be contiguous vectors of head_dim elements of the input's dtype")
     if len(ts) == 2 and q.shape[0] != k.shape[0]:
         raise ValueError("q and k need the same number of tokens")
     lib = load()
     hq = q.shape[1] // head_dim if q is not None else 0
     hk = k.shape[1] // head_dim if k is not None else 0
-    st = lib.nvfp4q_qk_norm(_ptr(q), _ptr(k), 0, ts[0].shape[0], hq, hk, head_dim,
+    st = lib.nvfp4q_qk_norm(_ptr(q), _ptr(k), dt, ts[0].shape[0], hq, hk, head_dim,
                             q.stride(0) if q is not None else 0, k.stride(0) if k is not None else 0,
                             _ptr(q_weight) if q is not None else None, _ptr(k_weight) if k is not None else None,
                             float(weight_offset), float(eps), _stream(ts[0]))

@@ -20,12 +20,19 @@ nvfp4q_status check_ws(void* ws, size_t bytes) {
   return NVFP4Q_OK;
 }
 
-nvfp4q_status check_input(const void* x, nvfp4q_dtype dt, int64_t rows, int64_t cols, int64_t ld) {
-  if (dt != NVFP4Q_BF16) return NVFP4Q_E_UNSUPPORTED;
+// Bytes per element of a dtype (0: not a dtype).
+int dtype_size(nvfp4q_dtype dt) {
+  return dt == NVFP4Q_BF16 || dt == NVFP4Q_FP16 ? 2 : dt == NVFP4Q_FP32 ? 4 : 0;
+}
+
+// x: bf16 unless any_dtype (then bf16, fp16 or fp32); rows 16-byte aligned.
+nvfp4q_status check_input(const void* x, nvfp4q_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                          bool any_dtype = false) {
+  if (any_dtype ? dtype_size(dt) == 0 : dt != NVFP4Q_BF16) return NVFP4Q_E_UNSUPPORTED;
   if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld < cols) return NVFP4Q_E_SHAPE;
   if (rows > 0x7FFFFFFF || cols > 0x7FFFFFFF) return NVFP4Q_E_SHAPE;
   if (rows > 0 && !x) return NVFP4Q_E_NULLPTR;
-  if (!aligned(x, 16) || ld % 8 != 0) return NVFP4Q_E_ALIGN;
+  if (!aligned(x, 16) || (ld * dtype_size(dt)) % 16 != 0) return NVFP4Q_E_ALIGN;
   return NVFP4Q_OK;
 }
 
@@ -105,7 +112,7 @@ const char* nvfp4q_status_string(nvfp4q_status s) {
 nvfp4q_status nvfp4q_quantize(const void* x, nvfp4q_dtype dtype, int64_t rows, int64_t cols, int64_t ld_x,
                               const nvfp4q_global* g, const nvfp4q_plane* row, nvfp4q_rounding rounding,
                               const nvfp4q_rng* rng, void* workspace, size_t workspace_bytes, void* stream) {
-  TRY(check_input(x, dtype, rows, cols, ld_x));
+  TRY(check_input(x, dtype, rows, cols, ld_x, true));
   if (!row) return NVFP4Q_E_NULLPTR;
   TRY(check_plane(row, rows, cols));
   TRY(check_rounding(rounding, rng));
@@ -114,7 +121,7 @@ nvfp4q_status nvfp4q_quantize(const void* x, nvfp4q_dtype dtype, int64_t rows, i
   hipStream_t s = (hipStream_t)stream;
   if (rows == 0) return done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s));
   RowArgs a = {};
-  a.x = x; a.rows = rows; a.cols = cols; a.ld_x = ld_x;
+  a.x = x; a.dtype = (int)dtype; a.rows = rows; a.cols = cols; a.ld_x = ld_x;
   a.codes = row->codes; a.ldc = row->ld_codes; a.scales = row->scales; a.lds = row->ld_scales;
   a.ws = (Workspace*)workspace;
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
@@ -245,7 +252,7 @@ nvfp4q_status nvfp4q_quantize_2d_grouped(const void* x, nvfp4q_dtype dtype, int3
 nvfp4q_status nvfp4q_qk_norm(void* q, void* k, nvfp4q_dtype dtype, int64_t tokens, int32_t q_heads,
                              int32_t k_heads, int32_t head_dim, int64_t ld_q, int64_t ld_k, const void* q_weight,
                              const void* k_weight, float weight_offset, float eps, void* stream) {
-  if (dtype != NVFP4Q_BF16) return NVFP4Q_E_UNSUPPORTED;
+  if (dtype_size(dtype) == 0) return NVFP4Q_E_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return NVFP4Q_E_UNSUPPORTED;
   if (tokens < 0 || q_heads < 0 || k_heads < 0 || q_heads + k_heads < 1) return NVFP4Q_E_SHAPE;
   if (tokens > 0x7FFFFFFF || (int64_t)q_heads + k_heads > 65536) return NVFP4Q_E_SHAPE;
@@ -255,13 +262,15 @@ nvfp4q_status nvfp4q_qk_norm(void* q, void* k, nvfp4q_dtype dtype, int64_t token
   if (!(eps >= 0.0f)) return NVFP4Q_E_SHAPE;
   if (tokens > 0 && q_heads > 0 && (!q || !q_weight)) return NVFP4Q_E_NULLPTR;
   if (tokens > 0 && k_heads > 0 && (!k || !k_weight)) return NVFP4Q_E_NULLPTR;
-  if (q_heads > 0 && (!aligned(q, 16) || !aligned(q_weight, 16) || ld_q % 8 != 0)) return NVFP4Q_E_ALIGN;
-  if (k_heads > 0 && (!aligned(k, 16) || !aligned(k_weight, 16) || ld_k % 8 != 0)) return NVFP4Q_E_ALIGN;
+  const int es = dtype_size(dtype);
+  if (q_heads > 0 && (!aligned(q, 16) || !aligned(q_weight, 16) || (ld_q * es) % 16 != 0)) return NVFP4Q_E_ALIGN;
+  if (k_heads > 0 && (!aligned(k, 16) || !aligned(k_weight, 16) || (ld_k * es) % 16 != 0)) return NVFP4Q_E_ALIGN;
   QkArgs a = {};
   a.q = q; a.k = k; a.wq = q_weight; a.wk = k_weight;
   a.tokens = tokens; a.ldq = ld_q; a.ldk = ld_k;
   a.hq = q_heads; a.hk = k_heads; a.d = head_dim;
   a.woff = weight_offset; a.eps = eps;
+  a.dtype = (int)dtype;
   return done(launch_qk_norm(a, (hipStream_t)stream));
 }
 

@@ -34,12 +34,43 @@ __device__ __forceinline__ float head_sum(float v) {
   return v;
 }
 
-// E elements per lane (8, 16 or 32: one, two or four 16-byte loads).
-template <int D, int E>
+// 8 elements of type T to fp32 and back (round to nearest even).
+template <int T>
+__device__ __forceinline__ void widen_in8(const uint4* q, float v[8]) {
+  if constexpr (T == kInBF16) {
+    widen8(q[0], v);
+  } else if constexpr (T == kInFP16) {
+    widen8_h(q[0], v);
+  } else {
+    const uint32_t w[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  }
+}
+template <int T>
+__device__ __forceinline__ void narrow_out8(const float v[8], uint4* q) {
+  if constexpr (T == kInBF16) {
+    q[0] = pack8_bf16(v);
+  } else if constexpr (T == kInFP16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * i]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * i + 1]) << 16);
+    q[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    q[0] = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+    q[1] = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7]));
+  }
+}
+
+// E elements per lane (8, 16 or 32) of element type T.
+template <int D, int E, int T>
 __global__ __launch_bounds__(kThreads) void k_qk_norm(const QkArgs a) {
-  constexpr uint32_t kTph = D / E;      // lanes per head
-  constexpr uint32_t kHpw = 64 / kTph;  // heads per wave
-  constexpr int kL = E / 8;             // 16-byte loads per lane
+  constexpr uint32_t kTph = D / E;              // lanes per head
+  constexpr uint32_t kHpw = 64 / kTph;          // heads per wave
+  constexpr int kG = E / 8;                     // groups of 8 elements per lane
+  constexpr int kL = in_size<T>() / 2;          // 16-byte loads per group of 8
   const uint32_t lane = threadIdx.x & 63;
   const uint64_t wave = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const uint64_t head = wave * kHpw + lane / kTph;
@@ -49,28 +80,40 @@ __global__ __launch_bounds__(kThreads) void k_qk_norm(const QkArgs a) {
   const uint64_t t = live ? head / hpt : 0;
   const uint32_t j = live ? (uint32_t)(head - t * hpt) : 0;
   const bool isq = j < (uint32_t)a.hq;
-  uint16_t* x = isq ? (uint16_t*)a.q + (int64_t)t * a.ldq + (int64_t)j * D
-                    : (uint16_t*)a.k + (int64_t)t * a.ldk + (int64_t)(j - a.hq) * D;
-  x += sub * E;
-  const uint16_t* w = (const uint16_t*)(isq ? a.wq : a.wk) + sub * E;
-  uint4 xq[kL], wq[kL];
+  const int64_t el = isq ? (int64_t)t * a.ldq + (int64_t)j * D : (int64_t)t * a.ldk + (int64_t)(j - a.hq) * D;
+  char* x = (char*)(isq ? a.q : a.k) + (el + sub * E) * in_size<T>();
+  const char* w = (const char*)(isq ? a.wq : a.wk) + (size_t)sub * E * in_size<T>();
+  uint4 xq[kG * kL], wq[kG * kL];
 #pragma unroll
-  for (int l = 0; l < kL; ++l) xq[l] = ld16(x + 8 * l, live);
+  for (int l = 0; l < kG * kL; ++l) xq[l] = ld16(x + 16 * l, live);
 #pragma unroll
-  for (int l = 0; l < kL; ++l) wq[l] = ld16(w + 8 * l, live);
+  for (int l = 0; l < kG * kL; ++l) wq[l] = ld16(w + 16 * l, live);
+  float v[kG][8];
   float ss = 0.0f;
 #pragma unroll
-  for (int l = 0; l < kL; ++l) ss = sumsq8(xq[l], ss);
+  for (int gi = 0; gi < kG; ++gi) {
+    widen_in8<T>(xq + gi * kL, v[gi]);
+    if constexpr (T == kInBF16) {
+      ss = sumsq8(xq[gi], ss);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(v[gi][i], v[gi][i], ss);
+    }
+  }
   ss = head_sum<kTph>(ss);
   const float r = inv_rms(ss, 1.0f / (float)D, a.eps);
 #pragma unroll
-  for (int l = 0; l < kL; ++l) {
-    float v[8], g[8];
-    widen8(xq[l], v);
-    widen8(wq[l], g);
+  for (int gi = 0; gi < kG; ++gi) {
+    float g[8];
+    widen_in8<T>(wq + gi * kL, g);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (g[i] + a.woff) * (v[i] * r);
-    if (live) *reinterpret_cast<uint4*>(x + 8 * l) = pack8_bf16(v);
+    for (int i = 0; i < 8; ++i) v[gi][i] = (g[i] + a.woff) * (v[gi][i] * r);
+    uint4 o[kL];
+    narrow_out8<T>(v[gi], o);
+    if (live) {
+#pragma unroll
+      for (int l = 0; l < kL; ++l) *reinterpret_cast<uint4*>(x + 16 * (gi * kL + l)) = o[l];
+    }
   }
 }
 
@@ -84,21 +127,28 @@ int qk_epl() {
   return v;
 }
 
-template <int D, int E>
-hipError_t launch_qk_de(const QkArgs& a, hipStream_t s) {
+template <int D, int E, int T>
+hipError_t launch_qk_det(const QkArgs& a, hipStream_t s) {
   constexpr uint64_t kHpw = 64 / (D / E);
   const uint64_t heads = (uint64_t)a.tokens * (uint64_t)(a.hq + a.hk);
   const uint64_t waves = (heads + kHpw - 1) / kHpw;
   const uint64_t wgs = (waves + kWavesPerWG - 1) / kWavesPerWG;
   if (wgs == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_qk_norm<D, E>), dim3((uint32_t)wgs), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((k_qk_norm<D, E, T>), dim3((uint32_t)wgs), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D, int T>
+hipError_t launch_qk_dt(const QkArgs& a, hipStream_t s) {
+  if (qk_epl() == 16) return launch_qk_det<D, 16, T>(a, s);
+  return qk_epl() == 32 ? launch_qk_det<D, 32, T>(a, s) : launch_qk_det<D, 8, T>(a, s);
 }
 
 template <int D>
 hipError_t launch_qk_d(const QkArgs& a, hipStream_t s) {
-  if (qk_epl() == 16) return launch_qk_de<D, 16>(a, s);
-  return qk_epl() == 32 ? launch_qk_de<D, 32>(a, s) : launch_qk_de<D, 8>(a, s);
+  if (a.dtype == kInFP16) return launch_qk_dt<D, kInFP16>(a, s);
+  if (a.dtype == kInFP32) return launch_qk_dt<D, kInFP32>(a, s);
+  return launch_qk_dt<D, kInBF16>(a, s);
 }
 
 }  // namespace

@@ -30,8 +30,8 @@
 namespace nvfp4q {
 
 // ------------------------------------------------------------------ amax
-// A wave takes one span of kAmaxLoads * 512 columns of one row at a time and
-// issues all of its 16-byte loads at once (16 KB in flight per wave) through
+// A wave takes one span of 16 KB of one row at a time (8192 bf16 or fp16
+// columns, 4096 fp32) and issues all of its 16-byte loads at once through
 // a buffer resource that ends at the row's last column, so reads past cols
 // return zero without guards. A launch over several stacked tensors of `rows`
 // rows each (grid y = tensor) keeps one set of partials per tensor.
@@ -40,22 +40,23 @@ namespace nvfp4q {
 // Measured on 8192 x 8192 (full step): 2048 workgroups 89.6 us, 1024 86.0,
 // 512 85.8, 256 84.7, 192 88.1, 128 95.1.
 constexpr int kAmaxLoads = 16;
-constexpr uint32_t kAmaxSpan = kAmaxLoads * 512;
 constexpr int kAmaxMaxWGs = 256;
+template <int T>
 __global__ __launch_bounds__(kThreads) void k_amax_rows(const RowArgs a) {
-  const uint16_t* __restrict__ x = (const uint16_t*)a.x + (int64_t)blockIdx.y * a.rows * a.ld_x;
+  constexpr uint32_t kSpan = kAmaxLoads * 1024 / in_size<T>();  // elements per span (16 KB)
+  const char* __restrict__ x = (const char*)a.x + (int64_t)blockIdx.y * a.rows * a.ld_x * in_size<T>();
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)((blockIdx.x * kThreads + threadIdx.x) >> 6));
   const uint32_t nwaves = (gridDim.x * kThreads) >> 6;
-  const uint32_t ngrp = (cols + kAmaxSpan - 1) / kAmaxSpan;  // spans per row
+  const uint32_t ngrp = (cols + kSpan - 1) / kSpan;  // spans per row
   const uint64_t units = (uint64_t)rows * ngrp;
   float m = 0.0f;
   for (uint64_t u = wave; u < units; u += nwaves) {
-    const uint32_t r = (uint32_t)(u / ngrp), c0 = (uint32_t)(u - (uint64_t)r * ngrp) * kAmaxSpan;
-    const uint32_t left = cols - c0 < kAmaxSpan ? cols - c0 : kAmaxSpan;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)r * a.ld_x + c0), (short)0, (int)(left * 2), 0x00020000);
+    const uint32_t r = (uint32_t)(u / ngrp), c0 = (uint32_t)(u - (uint64_t)r * ngrp) * kSpan;
+    const uint32_t left = cols - c0 < kSpan ? cols - c0 : kSpan;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + ((int64_t)r * a.ld_x + c0) * in_size<T>()), (short)0, (int)(left * in_size<T>()), 0x00020000);
     uint4 q[kAmaxLoads];
 #pragma unroll
     for (int k = 0; k < kAmaxLoads; ++k) {
@@ -63,21 +64,17 @@ __global__ __launch_bounds__(kThreads) void k_amax_rows(const RowArgs a) {
       q[k] = make_uint4(t[0], t[1], t[2], t[3]);
     }
 #pragma unroll
-    for (int k = 0; k < kAmaxLoads; ++k) {
-      float v[8];
-      widen8(q[k], v);
-      m = fmaxf(m, max8_abs(v));
-    }
+    for (int k = 0; k < kAmaxLoads; ++k) m = fmaxf(m, max_abs16b<T>(q[k]));
   }
   publish_partial(a.ws, m);
 }
 
 // ------------------------------------------------------------------ quantize
-template <bool SR>
+template <bool SR, int T>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(const RowArgs a) {
   __shared__ float rcp_tab[128];
   const GScale g = consume_scales(a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
-  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  const char* __restrict__ x = (const char*)a.x;
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   const int lane = threadIdx.x & 63;
   const uint32_t wave = (blockIdx.x * kThreads + threadIdx.x) >> 6;
@@ -85,18 +82,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const RowArgs a) {
   const uint32_t nsc = (cols + kSuper - 1) / kSuper;
   const uint32_t nbr = cols >> 4;  // blocks per row
   for (uint32_t r = wave; r < rows; r += nwaves) {
-    const uint16_t* xr = x + (int64_t)r * a.ld_x;
+    const char* xr = x + (int64_t)r * a.ld_x * in_size<T>();
     uint8_t* cr = a.codes + (int64_t)r * a.ldc;
     uint8_t* sr = a.scales + (int64_t)r * a.lds;
     for (uint32_t s0 = 0; s0 < nsc; s0 += 2) {
-      Blk b[2];
+      Raw16<T> b[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) b[u] = load_blk<false>(xr, (s0 + u) * kSuper + lane * 16, (s0 + u) < nsc ? cols : 0);
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t col = (s0 + u) * kSuper + lane * 16;
+        b[u] = load_raw16<T>(xr, col, (s0 + u) < nsc && col < cols);
+      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const uint32_t col = (s0 + u) * kSuper + lane * 16;
         float v[16];
-        widen16(b[u], v);
+        widen_raw16<T>(b[u], v);
         uint32_t sc;
         const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)r * nbr + (col >> 4), a.seed, a.offset, 0);
         if ((s0 + u) < nsc && col < cols) {
@@ -135,19 +135,31 @@ int64_t amax_wgs() {
 }
 
 hipError_t launch_amax_rows(const RowArgs& a, hipStream_t s, uint32_t* nparts, int tensors) {
-  const int64_t units = a.rows * ((a.cols + kAmaxSpan - 1) / kAmaxSpan);  // one per wave at most
+  const int64_t span = kAmaxLoads * 1024 / (a.dtype == kInFP32 ? 4 : 2);  // elements per span
+  const int64_t units = a.rows * ((a.cols + span - 1) / span);  // one per wave at most
   int64_t wgs = (units + kWavesPerWG - 1) / kWavesPerWG;
   if (wgs > amax_wgs()) wgs = amax_wgs();
   if (wgs < 1) wgs = 1;
   *nparts = (uint32_t)wgs;
-  hipLaunchKernelGGL(k_amax_rows, dim3((uint32_t)wgs, (uint32_t)tensors), dim3(kThreads), 0, s, a);
+  const dim3 grid((uint32_t)wgs, (uint32_t)tensors);
+  if (a.dtype == kInFP16) hipLaunchKernelGGL(k_amax_rows<kInFP16>, grid, dim3(kThreads), 0, s, a);
+  else if (a.dtype == kInFP32) hipLaunchKernelGGL(k_amax_rows<kInFP32>, grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(k_amax_rows<kInBF16>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_rows(const RowArgs& a, hipStream_t s) {
   dim3 grid(grid_rows(a.rows)), block(kThreads);
-  if (a.sr) hipLaunchKernelGGL(k_quant_rows<true>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_quant_rows<false>, grid, block, 0, s, a);
+  if (a.dtype == kInFP16) {
+    if (a.sr) hipLaunchKernelGGL((k_quant_rows<true, kInFP16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_quant_rows<false, kInFP16>), grid, block, 0, s, a);
+  } else if (a.dtype == kInFP32) {
+    if (a.sr) hipLaunchKernelGGL((k_quant_rows<true, kInFP32>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_quant_rows<false, kInFP32>), grid, block, 0, s, a);
+  } else {
+    if (a.sr) hipLaunchKernelGGL((k_quant_rows<true, kInBF16>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_quant_rows<false, kInBF16>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ struct Workspace;
 // Arguments of the rowwise paths (quantize and RMSNorm).
 struct RowArgs {
   const void* x;
+  int dtype;  // element type of x (nvfp4q_dtype; bf16 except on the rowwise quantizer)
   int64_t rows, cols, ld_x;
   const void* gamma;
   const void* beta;
@@ -41,6 +42,7 @@ struct QkArgs {
   int64_t tokens, ldq, ldk;
   int hq, hk, d;
   float woff, eps;
+  int dtype;  // element type of q, k and the weights (nvfp4q_dtype)
 };
 
 // Arguments of the 2D (rowwise + columnwise) path.

@@ -35,6 +35,68 @@ __device__ __forceinline__ Blk load_blk(const uint16_t* xr, uint32_t col, uint32
   return b;
 }
 
+// ------------------------------------------------------------------ input types
+// Element types of x on the paths that take more than bf16 (the values of
+// nvfp4q_dtype): a 16-byte load holds 8 bf16 or fp16 values or 4 fp32 values.
+enum InType { kInBF16 = 0, kInFP16 = 1, kInFP32 = 2 };
+template <int T>
+constexpr int in_size() { return T == kInFP32 ? 4 : 2; }
+
+// The raw 16 elements of one block (two or four 16-byte loads).
+template <int T>
+struct Raw16 {
+  uint4 q[in_size<T>()];
+};
+// Elements col .. col + 15 of a row (zeros when !ok).
+template <int T>
+__device__ __forceinline__ Raw16<T> load_raw16(const void* xr, uint32_t col, bool ok) {
+  Raw16<T> b;
+  const char* p = (const char*)xr + (size_t)col * in_size<T>();
+#pragma unroll
+  for (int l = 0; l < in_size<T>(); ++l) b.q[l] = ld16(p + 16 * l, ok);
+  return b;
+}
+// fp16 pair to fp32 (exact).
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+__device__ __forceinline__ void widen8_h(const uint4 q, float v[8]) {
+  v[0] = h_lo(q.x); v[1] = h_hi(q.x);
+  v[2] = h_lo(q.y); v[3] = h_hi(q.y);
+  v[4] = h_lo(q.z); v[5] = h_hi(q.z);
+  v[6] = h_lo(q.w); v[7] = h_hi(q.w);
+}
+template <int T>
+__device__ __forceinline__ void widen_raw16(const Raw16<T>& b, float v[16]) {
+  if constexpr (T == kInBF16) {
+    widen8(b.q[0], v);
+    widen8(b.q[1], v + 8);
+  } else if constexpr (T == kInFP16) {
+    widen8_h(b.q[0], v);
+    widen8_h(b.q[1], v + 8);
+  } else {
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      v[4 * l] = __uint_as_float(b.q[l].x);
+      v[4 * l + 1] = __uint_as_float(b.q[l].y);
+      v[4 * l + 2] = __uint_as_float(b.q[l].z);
+      v[4 * l + 3] = __uint_as_float(b.q[l].w);
+    }
+  }
+}
+// max |v| over the values of one 16-byte load
+template <int T>
+__device__ __forceinline__ float max_abs16b(const uint4 q) {
+  if constexpr (T == kInFP32) {
+    return fmaxf(fmaxf(fabsf(__uint_as_float(q.x)), fabsf(__uint_as_float(q.y))),
+                 fmaxf(fabsf(__uint_as_float(q.z)), fabsf(__uint_as_float(q.w))));
+  } else {
+    float v[8];
+    if constexpr (T == kInBF16) widen8(q, v);
+    else widen8_h(q, v);
+    return max8_abs(v);
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 inline uint32_t grid_rows(int64_t rows, int64_t max_wgs = 4096) {
   int64_t wgs = (rows + kWavesPerWG - 1) / kWavesPerWG;

@@ -71,7 +71,11 @@ def _quant(lib, x=FAKE, dtype=0, rows=4, cols=32, ld=32, codes=FAKE, ldc=16, sca
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=1), 4),                  # only bf16
+    (dict(dtype=3), 4),                  # bf16, fp16 or fp32 only
+    (dict(dtype=1), 6),                  # fp16 accepted (stops at the small workspace)
+    (dict(dtype=2, ld=36), 6),           # fp32 rows of 144 bytes stay 16-byte aligned
+    (dict(dtype=2, ld=34), 3),           # 136-byte fp32 rows do not
+    (dict(dtype=1, ld=36), 3),           # 72-byte fp16 rows do not
     (dict(cols=24, ld=24), 2),           # cols % 16
     (dict(ld=16), 2),                    # ld < cols
     (dict(rows=-1), 2),
@@ -113,6 +117,25 @@ def test_rmsnorm_validation(lib):
     assert call(p=q.Plane(None, 0, None, 0), y=FAKE, ldy=16) == 2
     assert call(p=q.Plane(None, 0, None, 0), y=FAKE + 2, ldy=32) == 3
     assert call(ws=None) == 6
+
+
+def test_other_entry_points_take_bf16_only(lib):
+    import rmsnorm_nvfp4_block_amd as q
+
+    g = q.Global(None, None, None)
+    r = q.Rng(0, 0)
+    p = q.Plane(FAKE, 16, FAKE, 2)
+    for dt in (1, 2):
+        assert lib.rmsnorm_nvfp4q(FAKE, dt, 4, 32, 32, FAKE, None, 0.0, 1e-6, None, 0, ctypes.byref(g),
+                                  ctypes.byref(p), 0, ctypes.byref(r), FAKE, 1 << 20, None) == 4
+        assert lib.nvfp4q_quantize_2d(FAKE, dt, 32, 32, 32, ctypes.byref(g), ctypes.byref(p), None, 0,
+                                      ctypes.byref(r), FAKE, 1 << 20, None) == 4
+        assert lib.nvfp4q_grouped(FAKE, dt, 32, 32, 32, FAKE, 1, None, 1, 0, ctypes.byref(g), ctypes.byref(p),
+                                  None, None, 0, ctypes.byref(r), FAKE, 1 << 20, None) == 4
+    # the QK norm takes all three; an unknown dtype is refused before anything is launched
+    assert lib.nvfp4q_qk_norm(FAKE, None, 3, 3, 4, 0, 128, 512, 0, FAKE, None, 0.0, 1e-6, None) == 4
+    assert lib.nvfp4q_qk_norm(FAKE, None, 2, 3, 4, 0, 128, 510, 0, FAKE, None, 0.0, 1e-6, None) == 2
+    assert lib.nvfp4q_qk_norm(FAKE, None, 2, 3, 4, 0, 64, 258, 0, FAKE, None, 0.0, 1e-6, None) == 3
 
 
 def test_qk_norm_validation(lib):

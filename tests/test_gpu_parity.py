@@ -240,6 +240,64 @@ def test_rmsnorm_given_amax_and_y_only(gpu_lib):
     assert np.array_equal(to_np_bf16(y_only["y"]), to_np_bf16(got["y"]))
 
 
+# ---------------------------------------------------------------- fp16 / fp32 inputs
+@pytest.mark.parametrize("dtype", ["float16", "float32"])
+@pytest.mark.parametrize("shape", [(1, 16), (37, 272), (256, 1024), (5, 9232)])
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_quantize_fp16_fp32_inputs(gpu_lib, dtype, shape, rounding):
+    import torch
+
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-4, 4, (shape[0], 1)))).astype(np.float32)
+    x = x.astype(getattr(np, dtype))
+    got = gpu_lib.nvfp4q_quantize(torch.from_numpy(x).cuda(), rounding=rounding, seed=0xD7, offset=3)
+    q = oracle.quantize_rowwise(x, rounding=rounding, seed=0xD7, offset=3)
+    R, C = shape
+    assert_same_bits("codes", np_u8(got["codes"], C // 2), q["codes"])
+    assert_same_bits("scales", np_u8(got["scales"], C // 16), q["scales"])
+    assert_f32_bits("amax", f32(got["amax"])[0], q["amax"])
+    assert_f32_bits("scale", f32(got["scale"])[0], q["s_dec"])
+
+
+def test_quantize_fp32_given_amax_and_padded_rows(gpu_lib):
+    import torch
+
+    rng = np.random.default_rng(38)
+    x = rng.standard_normal((64, 200)).astype(np.float32)
+    xd = torch.from_numpy(x).cuda()[:, :192]           # rows of 200 floats (800 bytes, 16-byte aligned)
+    a = torch.tensor([1.5], dtype=torch.float32, device="cuda")
+    got = gpu_lib.nvfp4q_quantize(xd, amax=a, rounding="sr", seed=5)
+    q = oracle.quantize_rowwise(x[:, :192], amax=np.float32(1.5), rounding="sr", seed=5)
+    assert_same_bits("codes", np_u8(got["codes"], 96), q["codes"])
+    assert_same_bits("scales", np_u8(got["scales"], 12), q["scales"])
+
+
+@pytest.mark.parametrize("dtype", ["float16", "float32"])
+@pytest.mark.parametrize("head_dim", [64, 256])
+def test_qk_norm_fp16_fp32(gpu_lib, dtype, head_dim):
+    import torch
+
+    w = workloads.qk_heads(seed=head_dim, tokens=33, q_heads=6, k_heads=2, head_dim=head_dim)
+    tdt = getattr(torch, dtype)
+    qf, kf = F.bf16_to_f32(w.x), F.bf16_to_f32(w.meta["k"])
+    rng = np.random.default_rng(head_dim)
+    qf = qf * (1 + 2.0 ** -9 * rng.standard_normal(qf.shape)).astype(np.float32)   # not bf16-exact
+    qd, kd = torch.from_numpy(qf).to(tdt).cuda(), torch.from_numpy(kf).to(tdt).cuda()
+    wq = torch.from_numpy(F.bf16_to_f32(w.gamma)).to(tdt).cuda()
+    wk = torch.from_numpy(F.bf16_to_f32(w.meta["k_weight"])).to(tdt).cuda()
+    q_in = qd.double().cpu().numpy()
+    gpu_lib.nvfp4q_qk_norm(qd, kd, wq, wk, head_dim, eps=w.eps)
+    for got, x_in, wv in ((qd, q_in, wq), (kd, kf.astype(np.float64), wk)):
+        x64 = x_in.reshape(-1, head_dim)
+        r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=-1, keepdims=True) + float(np.float32(w.eps)))
+        y64 = wv.double().cpu().numpy()[None, :] * (x64 * r)
+        yg = got.double().cpu().numpy().reshape(-1, head_dim)
+        # fp16: the output rounding (half an ulp, 2^-11) plus the fp32 arithmetic; fp32: the arithmetic
+        # alone (a sum of at most 256 squares, v_rsq_f32 within 1 ulp, two products)
+        tol = 2.0 ** -9 if dtype == "float16" else 2.0 ** -14
+        assert np.all(np.abs(yg - y64) <= tol * np.abs(y64) + 2.0 ** -24), np.max(np.abs(yg - y64))
+
+
 # ---------------------------------------------------------------- QK norm (reading R-qk)
 def _check_qk(y_gpu, x, w, head_dim, woff, eps):
     T = x.shape[0]

@@ -297,3 +297,30 @@ def test_2d_experts_own_amax_and_own_streams():
     s = Q.quantize_2d_experts(x, 2, rounding="sr", seed=8)
     assert not np.array_equal(s["row"]["codes"][:32], s["row"]["codes"][32:])
     assert np.array_equal(s["row"]["scales"][:32], s["row"]["scales"][32:])
+
+
+# ---------------------------------------------------------------- fp16 / fp32 inputs
+def test_fp16_fp32_inputs_are_quantized_as_given():
+    # amax 2688 gives S_enc = S_dec = 1; the block max 6 gives scale 1 (E4M3 0x38) and multiplier 1.
+    # 2.5 + 2^-20 (fp32) and 2.5 + 2^-9 (fp16) lie just above the E2M1 tie between 2 and 3 and encode
+    # as 3 (code 5); rounded to bf16 first they would be the tie 2.5 itself, which goes to even (2, code 4).
+    a = np.float32(2688.0)
+    for dt, tiny in ((np.float32, 2.0 ** -20), (np.float16, 2.0 ** -9)):
+        x = np.zeros((1, 16), dt)
+        x[0, 0], x[0, 1] = 6.0, 2.5 + tiny
+        assert float(x[0, 1]) != 2.5
+        q = Q.quantize_rowwise(x, amax=a)
+        c = F.unpack_nibbles(q["codes"])[0]
+        assert int(q["scales"][0, 0]) == 0x38 and c[0] == 7 and c[1] == 5
+        qb = Q.quantize_rowwise(F.f32_to_bf16(x.astype(np.float32)), amax=a)
+        assert F.unpack_nibbles(qb["codes"])[0, 1] == 4
+    # values that bf16 holds exactly quantize the same from any of the three types
+    rng = np.random.default_rng(37)
+    xb = F.f32_to_bf16(rng.standard_normal((8, 64)).astype(np.float32))
+    ref = Q.quantize_rowwise(xb, rounding="sr", seed=3)
+    for dt in (np.float32, np.float16):
+        xf = F.bf16_to_f32(xb).astype(dt)
+        if dt == np.float16:
+            assert np.array_equal(xf.astype(np.float32), F.bf16_to_f32(xb))   # exact in fp16 too
+        q = Q.quantize_rowwise(xf, rounding="sr", seed=3)
+        assert np.array_equal(q["codes"], ref["codes"]) and np.array_equal(q["scales"], ref["scales"])
