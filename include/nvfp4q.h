@@ -187,7 +187,8 @@ nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, 
  * nvfp4q_quantize_2d -- rowwise and columnwise (transposed) planes of one
  * [rows, cols] bf16 tensor under one shared per-tensor scale (weights).
  *   row: rowwise plane or row->codes == NULL; col: columnwise plane
- *   [cols][rows/2] codes, [cols][rows/16] scales, or col->codes == NULL.
+ *   [cols][rows/2] codes, [cols][rows/16] scales, or col->codes == NULL
+ *   (with rows == 0 a given plane may have NULL pointers).
  *   rows % 16 == 0 when the columnwise plane is requested.
  *   SR: rowwise blocks use tag 0 and index row * (cols/16) + col/16;
  *   columnwise blocks use tag 1 and index col * (rows/16) + row/16.

@@ -36,10 +36,11 @@ nvfp4q_status check_input(const void* x, nvfp4q_dtype dt, int64_t rows, int64_t 
   return NVFP4Q_OK;
 }
 
-// A plane of `prows` plane rows holding `pcols` elements each (an empty plane
-// may have NULL pointers).
+// A plane of `prows` plane rows holding `pcols` elements each (an empty plane,
+// no rows or rows of no elements, may have NULL pointers).
 nvfp4q_status check_plane(const nvfp4q_plane* p, int64_t prows, int64_t pcols) {
-  if (prows > 0 && (!p->codes || !p->scales)) return NVFP4Q_E_NULLPTR;
+  if (prows == 0 || pcols == 0) return NVFP4Q_OK;  // nothing is written
+  if (!p->codes || !p->scales) return NVFP4Q_E_NULLPTR;
   if (p->ld_codes < pcols / 2 || p->ld_scales < pcols / 16) return NVFP4Q_E_SHAPE;
   if (!aligned(p->codes, 16) || p->ld_codes % 8 != 0) return NVFP4Q_E_ALIGN;
   return NVFP4Q_OK;
@@ -190,7 +191,8 @@ nvfp4q_status quantize_2d_impl(const void* x, nvfp4q_dtype dtype, int experts, i
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0) return NVFP4Q_E_SHAPE;
   TRY(check_input(x, dtype, experts * rows, cols, ld_x));
-  const bool has_row = row && row->codes, has_col = col && col->codes;
+  // planes of an empty input hold no bytes and may come with NULL pointers
+  const bool has_row = row && (row->codes || rows == 0), has_col = col && (col->codes || rows == 0);
   if (!has_row && !has_col) return NVFP4Q_E_NULLPTR;
   const bool tile16 = ((int)rounding & NVFP4Q_SCALE_16X16) != 0;
   rounding = (nvfp4q_rounding)((int)rounding & ~NVFP4Q_SCALE_16X16);
@@ -290,7 +292,7 @@ nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_ro
   if (ld_x > kGroupedMaxLd) return NVFP4Q_E_SHAPE;
   const int64_t cap = total_rows + 15 * (int64_t)num_groups;
   if (want_col) {
-    TRY(check_plane(col, cols, 0));
+    TRY(check_plane(col, cols, cap));  // codes and scales present (cap >= 15 > 0), alignment
     if (col->ld_codes * 2 < cap || col->ld_scales * 16 < cap) return NVFP4Q_E_SHAPE;
   }
   if (want_row) TRY(check_plane(row, total_rows, cols));

@@ -193,6 +193,12 @@ def test_2d_and_grouped_validation(lib):
     assert grouped(lds=7) == 2        # 16 * 7 < 124
     assert grouped(ld=(1 << 24) + 8) == 2   # row stride past the 32-bit offsets of the loads
     assert grouped(colp=False) == 1                                        # no plane at all
+    p_noscales = q.Plane(FAKE, 64, None, 8)
+    assert lib.nvfp4q_grouped(FAKE, 0, 64, 32, 32, FAKE, 4, None, 1, 0x1234, ctypes.byref(g),
+                              ctypes.byref(p_noscales), None, None, 1, ctypes.byref(r), FAKE, 1 << 16, None) == 1
+    # an empty 2D input may come with NULL plane pointers (rows of zero elements)
+    assert lib.nvfp4q_quantize_2d(FAKE, 0, 0, 32, 32, ctypes.byref(g), ctypes.byref(none), ctypes.byref(none), 0,
+                                  ctypes.byref(r), FAKE, 1 << 16, None) == 6
     assert grouped(colp=False, rowp=q.Plane(None, 16, None, 2)) == 1       # rows but no rowwise buffers
     assert grouped(colp=False, rowp=q.Plane(FAKE, 8, FAKE, 2)) == 2        # 8 < 32 / 2 code bytes per row
     assert grouped(colp=False, rowp=q.Plane(FAKE, 16, FAKE, 1)) == 2       # 1 < 32 / 16 scale bytes per row

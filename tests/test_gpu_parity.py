@@ -93,6 +93,30 @@ def test_quantize_zero_and_empty(gpu_lib):
     assert f32(got["amax"])[0] == 0.0 and f32(got["scale"])[0] == 1.0
 
 
+def test_empty_inputs_on_every_path(gpu_lib):
+    # no rows: every entry point reports amax 0 and S_dec 1 (per tensor, group or expert) and writes nothing
+    import torch
+
+    e = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    got = gpu_lib.rmsnorm_nvfp4q(e, g)
+    assert f32(got["amax"])[0] == 0.0 and f32(got["scale"])[0] == 1.0
+    got = gpu_lib.nvfp4q_quantize_2d(e, rounding="sr", seed=1)
+    assert f32(got["amax"])[0] == 0.0 and f32(got["scale"])[0] == 1.0
+    got = gpu_lib.nvfp4q_quantize_2d_grouped(e, 3)
+    assert np.all(f32(got["amax"]) == 0.0) and np.all(f32(got["scale"]) == 1.0)
+    offs = torch.zeros(5, dtype=torch.int32, device="cuda")
+    codes = torch.full((64, 32), 0xAA, dtype=torch.uint8, device="cuda")
+    scales = torch.full((64, 4), 0x55, dtype=torch.uint8, device="cuda")
+    got = gpu_lib.nvfp4q_grouped(e, offs, rounding="sr", seed=1, codes=codes, scales=scales, rowwise=True)
+    assert np.all(f32(got["amax"]) == 0.0) and np.all(f32(got["scale"]) == 1.0)
+    assert np.all(f32(got["row_amax"]) == 0.0) and np.all(f32(got["row_scale"]) == 1.0)
+    assert np.all(got["poff"].cpu().numpy() == 0)
+    assert np.all(np_u8(codes) == 0xAA) and np.all(np_u8(scales) == 0x55)
+    gpu_lib.nvfp4q_qk_norm(torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda"), None,
+                           torch.ones(128, dtype=torch.bfloat16, device="cuda"), None, 128)
+
+
 def test_golden_blocks(gpu_lib):
     import json, os, torch
 
