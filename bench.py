@@ -326,13 +326,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_digest():
-    """sha256 of the kernel sources and header: traffic figures are valid only for the code they were taken on."""
+    """sha256 of the device code (kernels_*.hip and the headers they include): traffic figures are valid only
+    for the kernels they were taken on. Host-only files (api.hip, the C header) do not enter."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rmsnorm_nvfp4_block_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
-    files.append(os.path.join(ROOT, "include", "nvfp4q.h"))
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                   if (f.startswith("kernels_") and f.endswith(".hip")) or f.endswith(".hpp"))
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
