@@ -23,6 +23,7 @@ CHILD_ENV = {
     "NVFP4Q_RMS_COOP_WGS": "3",
     "NVFP4Q_XCD_ORDER": "0",
     "NVFP4Q_RMS_ROWWAVE_MIN": "1",
+    "NVFP4Q_AMAX_WGS": "7",
 }
 
 
@@ -75,6 +76,18 @@ def run_all(q):
     out["g_scales"] = host(r["scales"])[:, : mpad // 16]
     for k in ("amax", "poff"):
         out["g_" + k] = host(r[k]).view(np.uint8)
+    r = q.nvfp4q_grouped(dev(x), torch.tensor(offsets, device="cuda"), apply_rht=True, rht_mask=0x3C5A,
+                         rounding="sr", seed=7, offset=3, rowwise=True)
+    for k in ("row_codes", "row_scales", "row_amax"):
+        out["gr_" + k] = host(r[k]).view(np.uint8)
+    x = _bf16(rng, (3 * 160, 272))
+    r = q.nvfp4q_quantize_2d_grouped(dev(x), 3, rounding="sr", seed=6, offset=1, tile16=True)
+    for k in ("row_codes", "row_scales", "col_codes", "col_scales", "amax"):
+        out["e_" + k] = host(r[k]).view(np.uint8)
+    xf = (rng.standard_normal((513, 1040)) * 4).astype(np.float32)
+    r = q.nvfp4q_quantize(torch.from_numpy(xf).cuda(), rounding="sr", seed=8)
+    for k in ("codes", "scales", "amax"):
+        out["qf_" + k] = host(r[k]).view(np.uint8)
     return out
 
 
