@@ -1,4 +1,4 @@
-"""Launch-geometry invariance (SURVEY O14): block indices and SR draws are functions of tile
+"""Launch-geometry invariance: block indices and SR draws are functions of tile
 coordinates, so other grid sizes, tile orders and encode mappings must give bit-identical outputs.
 
 The calls of tests/geometry_calls.py run here with the default launch settings and in a child process
