@@ -554,7 +554,7 @@ def test_2d_experts_4x4096x7168_sampled(gpu_lib):
 
 # ---------------------------------------------------------------- grouped
 def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offset=2, groups=None, amax=None,
-                   fast_math=False, colwise=True, rowwise=False, row_amax=None):
+                   fast_math=False, colwise=True, rowwise=False, row_amax=None, pad=0):
     import torch
 
     T, C = x.shape
@@ -567,7 +567,12 @@ def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offs
     rscales = torch.full((T, C // 16 + 3), 0x55, dtype=torch.uint8, device="cuda")
     a = None if amax is None else torch.tensor(amax, dtype=torch.float32, device="cuda")
     ra = None if row_amax is None else torch.tensor(row_amax, dtype=torch.float32, device="cuda")
-    got = gpu_lib.nvfp4q_grouped(to_dev(x), torch.tensor(offsets, dtype=torch.int32, device="cuda"),
+    xd = to_dev(x)
+    if pad:  # rows of x further apart than cols (a view into a wider buffer)
+        wide = torch.full((x.shape[0], x.shape[1] + pad), 3.0, dtype=torch.bfloat16, device="cuda")
+        wide[:, :x.shape[1]] = xd
+        xd = wide[:, :x.shape[1]]
+    got = gpu_lib.nvfp4q_grouped(xd, torch.tensor(offsets, dtype=torch.int32, device="cuda"),
                                  apply_rht=apply_rht, rht_mask=mask, amax=a, rounding=rounding, seed=seed,
                                  offset=offset, codes=codes, scales=scales, fast_math=fast_math, colwise=colwise,
                                  rowwise=rowwise, row_amax=ra, row_codes=rcodes, row_scales=rscales)
@@ -707,3 +712,11 @@ def test_grouped_moe_16384x7168_rowwise_sampled(gpu_lib):
     G = len(w.offsets) - 1
     _grouped_check(gpu_lib, w.x, w.offsets.tolist(), w.apply_rht, w.rht_mask, "sr", seed=w.seed,
                    offset=w.offset, groups=[1, 30, G - 1], rowwise=True)
+
+
+@pytest.mark.parametrize("rounding", ["rtne", "sr"])
+def test_grouped_padded_rows_both_planes(gpu_lib, rounding):
+    # x rows 40 elements apart beyond cols (the padding holds values that must not leak into any plane)
+    rng = np.random.default_rng(39)
+    x = _bf16(rng, (150, 272))
+    _grouped_check(gpu_lib, x, [0, 3, 3, 70, 150], True, 0x1E3C, rounding, rowwise=True, pad=40)
