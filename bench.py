@@ -40,13 +40,16 @@ def log(*a):
 class Case:
     """Device buffers and launch closures for one workload."""
 
-    def __init__(self, name, torch, q, workloads, fast_math=False, planes="col", tile16=False):
+    def __init__(self, name, torch, q, workloads, fast_math=False, planes="col", tile16=False, dtype="bf16"):
         import numpy as np
 
         self.name = name
         self.fast_math = fast_math
         self.planes = planes  # grouped: which planes a step writes
         self.tile16 = tile16  # weight: one scale per 16 x 16 tile
+        self.dtype = dtype    # quantize, qknorm: element type of the input
+        tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+        es = {"bf16": 2, "fp16": 2, "fp32": 4}[dtype]
         self.colwise = name != "grouped" or planes in ("col", "both")
         self.rowwise = name == "grouped" and planes in ("row", "both")
         self.w = w = workloads.make(name)
@@ -55,16 +58,18 @@ class Case:
         def d(bits):
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
+        def din(bits):  # an input of the requested type, from the workload's bf16 values (exact conversion)
+            return d(bits).to(tdt)
+
         R, C = w.x.shape
         self.rows, self.cols = R, C
-        x_bytes = R * C * 2
+        x_bytes = R * C * es
         if name in ("quantize", "prefill", "decode"):
             out_bytes = R * C // 2 + R * C // 16
             param_bytes = (C * 2 if w.gamma is not None else 0) + (C * 2 if w.beta is not None else 0)
         elif name == "qknorm":           # in place: q and k read and written once, two weights read
-            out_bytes = R * C * 2 + w.meta["k"].size * 4
-            param_bytes = 2 * 2 * w.meta["head_dim"]
-            x_bytes = R * C * 2
+            out_bytes = R * C * es + w.meta["k"].size * 2 * es
+            param_bytes = 2 * es * w.meta["head_dim"]
         elif name in ("weight", "experts"):
             out_bytes = 2 * (R * C // 2 + R * C // 16)
             param_bytes = 0
@@ -84,9 +89,9 @@ class Case:
         self.bytes = x_bytes + out_bytes + param_bytes + (8 if name not in ("grouped", "qknorm") else 0)
         set_bytes = x_bytes + out_bytes
         self.nsets = max(1, math.ceil(ROTATE_BYTES / set_bytes))
-        x0 = d(w.x)
+        x0 = din(w.x)
         self.xs = [x0] + [x0.clone() for _ in range(self.nsets - 1)]
-        self.gamma = d(w.gamma) if w.gamma is not None else None
+        self.gamma = (din if name == "qknorm" else d)(w.gamma) if w.gamma is not None else None
         self.beta = d(w.beta) if w.beta is not None else None
         self.q = q
         self.torch = torch
@@ -103,10 +108,10 @@ class Case:
         elif name in ("weight", "experts"):
             self.outs = [None] * self.nsets
         elif name == "qknorm":
-            k0 = d(w.meta["k"])
+            k0 = din(w.meta["k"])
             self.ks = [k0] + [k0.clone() for _ in range(self.nsets - 1)]
             self.outs = [None] * self.nsets
-            self.wk = d(w.meta["k_weight"])
+            self.wk = din(w.meta["k_weight"])
         else:
             ldc = (C // 2 + 15) // 16 * 16
             self.outs = [(torch.empty((R, ldc), dtype=torch.uint8, device=dev),
@@ -116,6 +121,8 @@ class Case:
         w = self.w
         d = {"workload": self.name, "rows": self.rows, "cols": self.cols, "rounding": w.rounding,
              "compulsory_bytes_per_step": self.bytes, "rotated_buffer_sets": self.nsets}
+        if self.dtype != "bf16":
+            d["input_dtype"] = self.dtype
         if self.name in ("prefill", "decode"):
             d.update({"tokens": self.rows, "hidden": self.cols, "op": "rmsnorm+nvfp4 rowwise",
                       "bias": w.beta is not None, "eps": w.eps})
@@ -274,7 +281,11 @@ def cpu_baseline(case, budget_s=12.0):
             if name in ("prefill", "decode"):
                 oracle.rmsnorm_quantize(xs, w.gamma, w.beta, w.weight_offset, w.eps)
             elif name == "quantize":
-                oracle.quantize_rowwise(xs)
+                if case.dtype == "bf16":
+                    oracle.quantize_rowwise(xs)
+                else:
+                    oracle.quantize_rowwise(oracle.bf16_to_f32(xs).astype(np.float16 if case.dtype == "fp16"
+                                                                          else np.float32))
             elif name == "qknorm":
                 oracle.qk_norm(xs, w.meta["k"][rows], w.gamma, w.meta["k_weight"], w.meta["head_dim"], eps=w.eps)
             else:
@@ -365,10 +376,10 @@ def read_pmc(directory, counter):
     return out
 
 
-def traffic_key(config, fast_math=False, planes="col", tile16=False):
+def traffic_key(config, fast_math=False, planes="col", tile16=False, dtype="bf16"):
     """The profiles/traffic.json entry of a workload variant."""
     return (config + ("" if planes == "col" else "_" + planes) + ("_fast" if fast_math else "")
-            + ("_tile16" if tile16 else ""))
+            + ("_tile16" if tile16 else "") + ("" if dtype == "bf16" else "_" + dtype))
 
 
 def ingest_pmc(config, fetch_dir, write_dir, command, key=None):
@@ -456,6 +467,8 @@ def main():
                     help="grouped: the columnwise plane, the rowwise plane, or both in one pass")
     ap.add_argument("--tile16", action="store_true",
                     help="weight: NVFP4Q_SCALE_16X16 (one block scale per 16x16 tile, shared by both planes)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16", "fp32"],
+                    help="quantize, qknorm: element type of the input (the workload's values, converted exactly)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-only", action="store_true",
                     help="time only the roofline kernel with a given amax (for kernel traces); no metric line")
@@ -471,7 +484,7 @@ def main():
 
     if args.ingest_pmc:
         ingest_pmc(args.config, *args.ingest_pmc, command=args.command,
-                   key=traffic_key(args.config, args.fast_math, args.planes, args.tile16))
+                   key=traffic_key(args.config, args.fast_math, args.planes, args.tile16, args.dtype))
         return
     if args.ingest_copy:
         ingest_copy(*args.ingest_copy, nbytes=args.copy_calibration or (256 << 20), command=args.command)
@@ -505,7 +518,10 @@ def main():
         raise SystemExit("--fast-math concerns the transform, which the rowwise plane does not take")
     if args.tile16 and args.config not in ("weight", "experts"):
         raise SystemExit("--tile16 applies to the weight and experts workloads (the 2D path)")
-    case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes, tile16=args.tile16)
+    if args.dtype != "bf16" and args.config not in ("quantize", "qknorm"):
+        raise SystemExit("--dtype applies to the quantize and qknorm workloads")
+    case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes, tile16=args.tile16,
+                dtype=args.dtype)
     log(f"[bench] {case.describe()}")
 
     how, kname, _ = DOMINANT[args.config]
@@ -535,7 +551,7 @@ def main():
     else:
         kms = ms
     achieved = case.bytes / (kms * 1e-3) / 1e9
-    traffic = traffic_bytes(traffic_key(args.config, args.fast_math, args.planes, args.tile16))
+    traffic = traffic_bytes(traffic_key(args.config, args.fast_math, args.planes, args.tile16, args.dtype))
     out = {
         "metric": METRIC,
         "value": round(value, 2),
