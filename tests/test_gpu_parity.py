@@ -169,6 +169,59 @@ def test_graph_capture_replays(gpu_lib):
         _check_rowwise(oracle.quantize_rowwise(x2), e, 1024, "eager")
 
 
+def test_graph_capture_replays_other_entry_points(gpu_lib):
+    # grouped (both planes, RHT, SR), stacked expert weights with tile scales, and the in-place QK norm,
+    # each captured once and replayed on changing inputs, with eager calls between the replays; every
+    # replay must equal an eager call on the same input
+    import torch
+    q = gpu_lib
+    rng = np.random.default_rng(40)
+    offs = torch.tensor([0, 5, 70, 70, 160], dtype=torch.int32, device="cuda")
+    xs = [_bf16(rng, (160, 272), sc) for sc in (1.0, 9.0, 0.01)]
+    ws = [np.concatenate([_bf16(rng, (48, 80), sc) for _ in range(3)]) for sc in (0.02, 3.0, 1e-3)]
+    qs = [_bf16(rng, (9, 4 * 128), sc) for sc in (1.0, 50.0, 0.1)]
+    wq = to_dev(workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(128)).astype(np.float32)))
+    xg, xw, xq = to_dev(xs[0]), to_dev(ws[0]), to_dev(qs[0])
+
+    def grouped(x):
+        return q.nvfp4q_grouped(x, offs, apply_rht=True, rht_mask=0x6B1D, rounding="sr", seed=4, rowwise=True)
+
+    def experts(x):
+        return q.nvfp4q_quantize_2d_grouped(x, 3, rounding="sr", seed=5, tile16=True)
+
+    grouped(xg), experts(xw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            og = grouped(xg)
+            oe = experts(xw)
+            q.nvfp4q_qk_norm(xq, None, wq, None, 128)
+    for rep in range(4):
+        i = rep % 3
+        xg.copy_(to_dev(xs[i]))
+        xw.copy_(to_dev(ws[i]))
+        xq.copy_(to_dev(qs[i]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rg, re = grouped(to_dev(xs[i])), experts(to_dev(ws[i]))
+        rq = to_dev(qs[i])
+        q.nvfp4q_qk_norm(rq, None, wq, None, 128)
+        torch.cuda.synchronize()
+        mp = int(rg["poff"][-1])
+        # planes compared over their written bytes (row padding of the allocations is never written)
+        assert torch.equal(og["row_codes"][:, :136], rg["row_codes"][:, :136]), f"replay {rep}: grouped row codes"
+        for k in ("row_scales", "amax", "row_amax", "poff"):
+            assert torch.equal(og[k], rg[k]), f"replay {rep}: grouped {k}"
+        assert torch.equal(og["codes"][:, :mp // 2], rg["codes"][:, :mp // 2]), f"replay {rep}: grouped codes"
+        assert torch.equal(og["scales"][:, :mp // 16], rg["scales"][:, :mp // 16]), f"replay {rep}: grouped scales"
+        for k, n in (("row_codes", 40), ("row_scales", 5), ("col_codes", 24), ("col_scales", 3), ("amax", 3)):
+            assert torch.equal(oe[k][..., :n], re[k][..., :n]), f"replay {rep}: experts {k}"
+        assert torch.equal(xq.view(torch.int16), rq.view(torch.int16)), f"replay {rep}: qk norm"
+
+
 # ---------------------------------------------------------------- RMSNorm
 def _check_rms(w, got, rounding="rtne", seed=0, offset=0, amax_given=None):
     """Contract rules for the fused path (see module docstring)."""
