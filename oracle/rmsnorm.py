@@ -22,25 +22,42 @@ from .formats import bf16_to_f32, f64_to_bf16
 from .quantize import quantize_rowwise
 
 
-def rmsnorm_bf16(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, return_f64=False):
-    """y = bf16_RNE((gamma + c) * (x * r) [+ beta]),  r = 1 / sqrt(mean_k x^2 + eps)."""
-    x64 = bf16_to_f32(x).astype(np.float64)
+def _f64(a):
+    """bf16 bits (uint16) or float16 / float32 values, as float64."""
+    a = np.asarray(a)
+    return bf16_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def round_to(y64, dtype):
+    """y rounded to nearest even in the output type: bf16 bits, or float16 / float32 values (reading R-dtype)."""
+    if dtype == "bf16":
+        return f64_to_bf16(y64)
+    return np.asarray(y64, dtype=np.float64).astype(np.float16 if dtype == "fp16" else np.float32)
+
+
+def rmsnorm_bf16(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, return_f64=False, out_dtype="bf16"):
+    """y = RN_T((gamma + c) * (x * r) [+ beta]),  r = 1 / sqrt(mean_k x^2 + eps), T = out_dtype.
+
+    x, gamma, beta: bf16 bits, or float16 / float32 values (the input's type is the output's type;
+    reading R-dtype). The default rounds to bfloat16, as the name says.
+    """
+    x64 = _f64(x)
     K = x64.shape[-1]
-    g64 = bf16_to_f32(gamma).astype(np.float64) + float(np.float32(weight_offset))
+    g64 = _f64(gamma) + float(np.float32(weight_offset))
     eps64 = float(np.float32(eps))
     ms = np.sum(x64 * x64, axis=-1, keepdims=True) / K
     r = 1.0 / np.sqrt(ms + eps64)
     y64 = g64 * (x64 * r)
     if beta is not None:
-        y64 = y64 + bf16_to_f32(beta).astype(np.float64)
-    y = f64_to_bf16(y64)
+        y64 = y64 + _f64(beta)
+    y = round_to(y64, out_dtype)
     return (y, y64, r[..., 0]) if return_f64 else y
 
 
 def rmsnorm_quantize(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None,
-                     rounding="rtne", seed=0, offset=0):
-    """Fused reference: RMSNorm to bfloat16, then rowwise NVFP4 of that bfloat16 tensor."""
-    y = rmsnorm_bf16(x, gamma, beta, weight_offset, eps)
+                     rounding="rtne", seed=0, offset=0, out_dtype="bf16"):
+    """Fused reference: RMSNorm to the input's type (bfloat16 by default), then rowwise NVFP4 of that tensor."""
+    y = rmsnorm_bf16(x, gamma, beta, weight_offset, eps, out_dtype=out_dtype)
     q = quantize_rowwise(y, amax=amax, rounding=rounding, seed=seed, offset=offset, tag=0)
     q["y"] = y
     return q

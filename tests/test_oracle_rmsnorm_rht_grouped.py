@@ -251,3 +251,24 @@ def test_qk_norm_is_per_head_and_per_tensor_weight():
     # k's weight applied per element of each head: within two bf16 roundings of w * (unit-weight output)
     diff = np.abs(F.bf16_to_f32(yk).astype(np.float64) - F.bf16_to_f32(expect).astype(np.float64))
     assert np.all(diff <= 2.0 ** -6 * np.abs(F.bf16_to_f32(expect)) + 1e-30)
+
+
+def test_rmsnorm_fp16_fp32_output_rounding():
+    # 16 columns x = (3, 4, 0, ...): mean x^2 = 25/16, r = 0.8, y = (2.4, 3.2, 0, ...) (eps 0). Rounded to
+    # fp16 (10 fraction bits): 2.4 = 1.2 * 2 -> 1.0011001101b * 2 = 2.400390625, 3.2 = 1.6 * 2 ->
+    # 1.1001100110b * 2 = 3.19921875; to fp32 the nearest floats of 2.4 and 3.2 (reading R-dtype).
+    for dt, expect in ((np.float16, (2.400390625, 3.19921875)), (np.float32, (np.float32(2.4), np.float32(3.2)))):
+        x = np.zeros((1, 16), dt)
+        x[0, 0], x[0, 1] = 3.0, 4.0
+        y = rmsnorm_bf16(x, np.ones(16, dt), None, 0.0, 0.0, out_dtype="fp16" if dt == np.float16 else "fp32")
+        assert y.dtype == dt and float(y[0, 0]) == float(expect[0]) and float(y[0, 1]) == float(expect[1])
+        assert np.all(y[0, 2:] == 0)
+    # bf16-exact fp32 input with fp32 output: the float64 value rounded once to fp32, which keeps
+    # digits the bf16 output rounds away
+    rng = np.random.default_rng(41)
+    xb = _bits(rng.standard_normal((4, 256)))
+    gb = _bits(1 + 0.1 * rng.standard_normal(256))
+    y32, y64, _ = rmsnorm_bf16(F.bf16_to_f32(xb), F.bf16_to_f32(gb), None, 0.0, 1e-6, return_f64=True,
+                               out_dtype="fp32")
+    assert np.array_equal(y32, y64.astype(np.float32))
+    assert not np.array_equal(y32, F.bf16_to_f32(rmsnorm_bf16(xb, gb, None, 0.0, 1e-6)))
