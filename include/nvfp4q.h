@@ -83,11 +83,13 @@ typedef enum {
   NVFP4Q_E_WORKSPACE = 6    /* workspace missing, misaligned or too small */
 } nvfp4q_status;
 
-/* Element type of the input. nvfp4q_quantize and nvfp4q_qk_norm take all
- * three (the quantizer reads the values exactly as given; the QK norm writes
- * its output in the input's type, rounded to nearest even); the other entry
- * points take NVFP4Q_BF16 only (else NVFP4Q_E_UNSUPPORTED). Rows of x start
- * 16-byte aligned: ld_x * element size is a multiple of 16. */
+/* Element type of the input. nvfp4q_quantize, rmsnorm_nvfp4q and
+ * nvfp4q_qk_norm take all three: the quantizer reads the values exactly as
+ * given; the norms take gamma (and beta) in the input's type and round their
+ * output y to nearest even in that type (fp32: not rounded further), and
+ * rmsnorm_nvfp4q quantizes that y. The 2D and grouped entry points take
+ * NVFP4Q_BF16 only (else NVFP4Q_E_UNSUPPORTED). Rows of x (and y) start
+ * 16-byte aligned: leading dimension * element size is a multiple of 16. */
 typedef enum { NVFP4Q_BF16 = 0, NVFP4Q_FP16 = 1, NVFP4Q_FP32 = 2 } nvfp4q_dtype;
 
 /* Rounding of the E2M1 codes. NVFP4Q_FAST_MATH may be OR-ed into the value

@@ -180,13 +180,17 @@ def nvfp4q_quantize(x, amax=None, rounding="rtne", seed=0, offset=0, codes=None,
 
 def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, rounding="rtne", seed=0, offset=0,
                    y_out=False, quantize=True, codes=None, scales=None):
-    """RMSNorm of bf16 x [tokens, hidden] then rowwise NVFP4 of the bf16 output.
+    """RMSNorm of x [tokens, hidden] (bf16, fp16 or fp32; gamma and beta of the same type) then rowwise NVFP4
+    of the output rounded in that type.
 
     Returns dict(codes, scales, amax, scale, y) (y only when y_out=True).
     """
     import torch
 
-    _check_bf16_2d(x)
+    dt = _dtype_code(x)
+    for p in (gamma, beta):
+        if p is not None and (p.dtype != x.dtype or not p.is_contiguous()):
+            raise ValueError("gamma and beta must be contiguous and of x's dtype")
     lib = load()
     T, H = x.shape
     y = torch.empty_like(x) if y_out else None
@@ -197,7 +201,7 @@ def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, 
     amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
     scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
     ws = workspace(x.device)
-    st = lib.rmsnorm_nvfp4q(x.data_ptr(), 0, T, H, x.stride(0), gamma.data_ptr(), _ptr(beta),
+    st = lib.rmsnorm_nvfp4q(x.data_ptr(), dt, T, H, x.stride(0), gamma.data_ptr(), _ptr(beta),
                             float(weight_offset), float(eps), _ptr(y), y.stride(0) if y is not None else 0,
                             ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(plane),
                             _rounding(rounding), ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(),

@@ -140,7 +140,7 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
                              int64_t ld_y, const nvfp4q_global* g, const nvfp4q_plane* row,
                              nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  TRY(check_input(x, dtype, tokens, hidden, ld_x));
+  TRY(check_input(x, dtype, tokens, hidden, ld_x, true));
   if (!gamma) return NVFP4Q_E_NULLPTR;
   if (!aligned(gamma, 16) || !aligned(beta, 16)) return NVFP4Q_E_ALIGN;
   if (weight_offset != 0.0f && weight_offset != 1.0f) return NVFP4Q_E_UNSUPPORTED;
@@ -151,7 +151,7 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   if (codes) TRY(check_plane(row, tokens, hidden));
   if (y_out) {
     if (ld_y < hidden) return NVFP4Q_E_SHAPE;
-    if (!aligned(y_out, 16) || ld_y % 8 != 0) return NVFP4Q_E_ALIGN;
+    if (!aligned(y_out, 16) || (ld_y * dtype_size(dtype)) % 16 != 0) return NVFP4Q_E_ALIGN;
   }
   TRY(check_rounding(rounding, rng));
   TRY(check_ws(workspace, workspace_bytes));
@@ -159,7 +159,7 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   hipStream_t s = (hipStream_t)stream;
   if (tokens == 0) return codes ? done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s)) : NVFP4Q_OK;
   RowArgs a = {};
-  a.x = x; a.rows = tokens; a.cols = hidden; a.ld_x = ld_x;
+  a.x = x; a.dtype = (int)dtype; a.rows = tokens; a.cols = hidden; a.ld_x = ld_x;
   a.gamma = gamma; a.beta = beta; a.woff = weight_offset; a.eps = eps;
   a.y = y_out; a.ld_y = ld_y;
   a.codes = codes ? row->codes : nullptr; a.ldc = codes ? row->ld_codes : 0;
@@ -170,7 +170,9 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   // With the amax pass and a row count that fits the workspace's row-scale
   // slots, the encode pass streams rows using the 1/rms the amax pass stored.
-  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled();
+  // (bf16 only: fp16 / fp32 inputs run the cooperative-row passes)
+  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled() &&
+                        dtype == NVFP4Q_BF16;
   if (streamed) a.rs = reinterpret_cast<float*>(static_cast<char*>(workspace) + offsetof(Workspace, partial)) + kRowPartials;
   if (codes && !a.amax_in) {
     const hipError_t e = (streamed && !beta) ? launch_rms_stream_amax(a, s, &a.nparts)

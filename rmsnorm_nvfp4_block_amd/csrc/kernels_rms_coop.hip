@@ -22,24 +22,37 @@ namespace {
 
 enum CoopMode { kCoopAmax = 0, kCoopEncode = 1, kCoopYOnly = 2 };
 
-// The wave's NPW superchunks of one row (zero past the row's end).
-template <int NPW, bool FULL>
+// The wave's NPW superchunks of one row (zero past the row's end), elements
+// of type T (bf16, fp16 or fp32).
+template <int NPW, bool FULL, int T>
 __device__ __forceinline__ void coop_load(const RowArgs& a, uint32_t row, uint32_t wid, int lane, uint32_t cols,
-                                          Blk (&q)[NPW]) {
-  const uint16_t* xr = (const uint16_t*)a.x + (int64_t)row * a.ld_x;
+                                          Raw16<T> (&q)[NPW]) {
+  const char* xr = (const char*)a.x + (int64_t)row * a.ld_x * in_size<T>();
 #pragma unroll
-  for (int j = 0; j < NPW; ++j) q[j] = load_blk<FULL>(xr, (wid + 4 * j) * kSuper + lane * 16, cols);
+  for (int j = 0; j < NPW; ++j) {
+    const uint32_t col = (wid + 4 * j) * kSuper + lane * 16;
+    q[j] = load_raw16<T>(xr, col, FULL || col < cols);
+  }
 }
 
 // One row: partial sums of squares, the barrier, 1/rms, then the mode's work.
 // Returns the contribution to the amax pass's maximum (kCoopAmax).
-template <int NPW, bool FULL, bool BIAS, int MODE, bool SR>
-__device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32_t k, const Blk (&q)[NPW],
+template <int NPW, bool FULL, bool BIAS, int MODE, bool SR, int T>
+__device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32_t k, const Raw16<T> (&q)[NPW],
                                           float (*ssp)[kWavesPerWG], const float* gsh, const float* bsh, GScale g,
                                           const float* rcp_tab, float inv_k, uint32_t wid, int lane, uint32_t cols) {
   float ss = 0.0f;
 #pragma unroll
-  for (int j = 0; j < NPW; ++j) ss = sumsq8(q[j].hi, sumsq8(q[j].lo, ss));
+  for (int j = 0; j < NPW; ++j) {
+    if constexpr (T == kInBF16) {
+      ss = sumsq8(q[j].q[1], sumsq8(q[j].q[0], ss));
+    } else {
+      float v[16];
+      widen_raw16<T>(q[j], v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+    }
+  }
   ss = wave_sum(ss);
   if (lane == 0) ssp[k & 1][wid] = ss;
   // Double-buffered partials: a wave writes row k + 1's partial only after
@@ -58,7 +71,7 @@ __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32
     const bool ok = FULL || col < cols;
     const uint32_t lcol = ok ? col : 0;
     float v[16], gv[16];
-    widen16(q[j], v);
+    widen_raw16<T>(q[j], v);
     lds16(gsh, lcol, gv);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = v[i] * gv[i];
@@ -79,15 +92,10 @@ __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32
     if constexpr (MODE == kCoopAmax) {
       mrow = fmaxf(mrow, max16_abs(v));
     } else {
-      const uint4 y0 = pack8_bf16(v), y1 = pack8_bf16(v + 8);
-      if (a.y != nullptr && ok) {
-        uint16_t* yr = (uint16_t*)a.y + (int64_t)row * a.ld_y + col;
-        *reinterpret_cast<uint4*>(yr) = y0;
-        *reinterpret_cast<uint4*>(yr + 8) = y1;
-      }
+      // y rounded in the input's type, stored when asked for; the quantizer takes the rounded values
+      void* yp = a.y != nullptr ? (char*)a.y + ((int64_t)row * a.ld_y + col) * in_size<T>() : nullptr;
+      round_store16<T>(v, yp, 0u, a.y != nullptr && ok);
       if constexpr (MODE == kCoopEncode) {
-        widen8(y0, v);
-        widen8(y1, v + 8);
         uint32_t sc;
         const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)row * nbr + (col >> 4), a.seed, a.offset, 0);
         if (ok) {
@@ -101,7 +109,7 @@ __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32
   return 0.0f;
 }
 
-template <int NPW, int D, bool FULL, bool BIAS, int MODE, bool SR>
+template <int NPW, int D, bool FULL, bool BIAS, int MODE, bool SR, int T>
 __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
   extern __shared__ float params[];  // gamma + c, then beta (param_floats(cols) each)
   __shared__ float ssp[2][kWavesPerWG];
@@ -115,15 +123,20 @@ __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
   // the prologue's loads first: loads complete in issue order
   PartialsPre pm;
   if constexpr (MODE == kCoopEncode) pm = partials_issue(a.ws, a.nparts, a.amax_in);
-  const ParamsPre pp = params_issue<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, cols);
+  ParamsPre pp;
+  if constexpr (T == kInBF16) pp = params_issue<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, cols);
   // unconditional fill (row index clamped to the workgroup's last row): a
   // fill that may be skipped would turn every later wait into a wait for all
-  Blk ring[D][NPW];
+  Raw16<T> ring[D][NPW];
 #pragma unroll
-  for (int d = 0; d < D; ++d) coop_load<NPW, FULL>(a, (uint32_t)d < nr ? b + d * G : last, wid, lane, cols, ring[d]);
+  for (int d = 0; d < D; ++d)
+    coop_load<NPW, FULL, T>(a, (uint32_t)d < nr ? b + d * G : last, wid, lane, cols, ring[d]);
   float* gsh = params;
   float* bsh = params + param_floats(cols);
-  params_finish<BIAS>(pp, (const uint16_t*)a.gamma, (const uint16_t*)a.beta, a.woff, cols, gsh, bsh);
+  if constexpr (T == kInBF16)
+    params_finish<BIAS>(pp, (const uint16_t*)a.gamma, (const uint16_t*)a.beta, a.woff, cols, gsh, bsh);
+  else
+    stage_params_t<BIAS, T>(a.gamma, a.beta, a.woff, cols, gsh, bsh);
   GScale g = {1.0f, 1.0f};
   if constexpr (MODE == kCoopEncode) g = partials_finish(pm, a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
   else __syncthreads();
@@ -135,23 +148,23 @@ __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const uint32_t kk = k + d;
-        mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g, rcp_tab,
+        mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g, rcp_tab,
                                                                inv_k, wid, lane, cols));
-        coop_load<NPW, FULL>(a, kk + D < nr ? b + (kk + D) * G : last, wid, lane, cols, ring[d]);
+        coop_load<NPW, FULL, T>(a, kk + D < nr ? b + (kk + D) * G : last, wid, lane, cols, ring[d]);
       }
     } else {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const uint32_t kk = k + d;
         if (kk < nr)
-          mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g,
+          mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g,
                                                                  rcp_tab, inv_k, wid, lane, cols));
       }
     }
   }
   if constexpr (MODE == kCoopAmax) {
     // max |bf16(y)| = bf16(max |y|): round-to-nearest-even is monotone.
-    publish_partial(a.ws, bf_lo(pack_bf16(mloc, mloc) & 0xFFFFu));
+    publish_partial(a.ws, round_t<T>(mloc));
   }
 }
 
@@ -168,27 +181,34 @@ int64_t coop_wgs() {
 // 4096 x 4096 prefill (11.3 us at two, 11.7-12.5 us deeper).
 constexpr int kCoopDepth = 2;
 
-template <int NPW, bool BIAS, int MODE, bool SR>
+template <int NPW, bool BIAS, int MODE, bool SR, int T>
 hipError_t launch_coop_t(const RowArgs& a, uint32_t wgs, hipStream_t s) {
   const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
   if (a.cols == (int64_t)NPW * 4 * kSuper)
-    hipLaunchKernelGGL((k_rms_coop<NPW, kCoopDepth, true, BIAS, MODE, SR>), dim3(wgs), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((k_rms_coop<NPW, kCoopDepth, true, BIAS, MODE, SR, T>), dim3(wgs), dim3(kThreads), lds, s, a);
   else
-    hipLaunchKernelGGL((k_rms_coop<NPW, kCoopDepth, false, BIAS, MODE, SR>), dim3(wgs), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((k_rms_coop<NPW, kCoopDepth, false, BIAS, MODE, SR, T>), dim3(wgs), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
-template <int NPW, bool BIAS>
+template <int NPW, bool BIAS, int T>
 hipError_t launch_coop_mode(const RowArgs& a, int mode, uint32_t wgs, hipStream_t s) {
-  if (mode == kCoopAmax) return launch_coop_t<NPW, BIAS, kCoopAmax, false>(a, wgs, s);
-  if (mode == kCoopYOnly) return launch_coop_t<NPW, BIAS, kCoopYOnly, false>(a, wgs, s);
-  if (a.sr) return launch_coop_t<NPW, BIAS, kCoopEncode, true>(a, wgs, s);
-  return launch_coop_t<NPW, BIAS, kCoopEncode, false>(a, wgs, s);
+  if (mode == kCoopAmax) return launch_coop_t<NPW, BIAS, kCoopAmax, false, T>(a, wgs, s);
+  if (mode == kCoopYOnly) return launch_coop_t<NPW, BIAS, kCoopYOnly, false, T>(a, wgs, s);
+  if (a.sr) return launch_coop_t<NPW, BIAS, kCoopEncode, true, T>(a, wgs, s);
+  return launch_coop_t<NPW, BIAS, kCoopEncode, false, T>(a, wgs, s);
+}
+
+template <int NPW, int T>
+hipError_t launch_coop_npw_t(const RowArgs& a, int mode, uint32_t wgs, hipStream_t s) {
+  return a.beta ? launch_coop_mode<NPW, true, T>(a, mode, wgs, s) : launch_coop_mode<NPW, false, T>(a, mode, wgs, s);
 }
 
 template <int NPW>
 hipError_t launch_coop_npw(const RowArgs& a, int mode, uint32_t wgs, hipStream_t s) {
-  return a.beta ? launch_coop_mode<NPW, true>(a, mode, wgs, s) : launch_coop_mode<NPW, false>(a, mode, wgs, s);
+  if (a.dtype == kInFP16) return launch_coop_npw_t<NPW, kInFP16>(a, mode, wgs, s);
+  if (a.dtype == kInFP32) return launch_coop_npw_t<NPW, kInFP32>(a, mode, wgs, s);
+  return launch_coop_npw_t<NPW, kInBF16>(a, mode, wgs, s);
 }
 
 }  // namespace

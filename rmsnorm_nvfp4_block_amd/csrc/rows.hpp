@@ -83,6 +83,64 @@ __device__ __forceinline__ void widen_raw16(const Raw16<T>& b, float v[16]) {
     }
   }
 }
+// 8 elements of type T at element index i of p, as fp32.
+template <int T>
+__device__ __forceinline__ void load8_t(const void* p, uint32_t i, float v[8]) {
+  const char* b = (const char*)p + (size_t)i * in_size<T>();
+  if constexpr (T == kInFP32) {
+    const uint4 a = *reinterpret_cast<const uint4*>(b), c = *reinterpret_cast<const uint4*>(b + 16);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(c.x); v[5] = __uint_as_float(c.y); v[6] = __uint_as_float(c.z); v[7] = __uint_as_float(c.w);
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(b);
+    if constexpr (T == kInBF16) widen8(a, v);
+    else widen8_h(a, v);
+  }
+}
+
+// 16 fp32 values rounded to nearest even in type T (fp32: unchanged), stored at
+// element index i of p when ok, and returned as fp32 in v (the rounded values).
+template <int T>
+__device__ __forceinline__ void round_store16(float v[16], void* p, uint32_t i, bool ok) {
+  char* b = (char*)p + (size_t)i * in_size<T>();
+  if constexpr (T == kInFP32) {
+    if (ok) {
+#pragma unroll
+      for (int l = 0; l < 4; ++l)
+        *reinterpret_cast<uint4*>(b + 16 * l) = make_uint4(__float_as_uint(v[4 * l]), __float_as_uint(v[4 * l + 1]),
+                                                           __float_as_uint(v[4 * l + 2]), __float_as_uint(v[4 * l + 3]));
+    }
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if constexpr (T == kInBF16) {
+        w[k] = pack_bf16(v[2 * k], v[2 * k + 1]);
+      } else {
+        w[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k + 1]) << 16);
+      }
+    }
+    if (ok) {
+      *reinterpret_cast<uint4*>(b) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(b + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[2 * k] = T == kInBF16 ? bf_lo(w[k]) : h_lo(w[k]);
+      v[2 * k + 1] = T == kInBF16 ? bf_hi(w[k]) : h_hi(w[k]);
+    }
+  }
+}
+
+// Round a (non-negative) fp32 value to nearest even in type T.
+template <int T>
+__device__ __forceinline__ float round_t(float m) {
+  if constexpr (T == kInBF16) return bf_lo(pack_bf16(m, m) & 0xFFFFu);
+  else if constexpr (T == kInFP16) return (float)(_Float16)m;
+  else return m;
+}
+
 // max |v| over the values of one 16-byte load
 template <int T>
 __device__ __forceinline__ float max_abs16b(const uint4 q) {
@@ -202,6 +260,27 @@ __device__ __forceinline__ void params_finish(const ParamsPre& p, const uint16_t
     uint4 bq = make_uint4(0u, 0u, 0u, 0u);
     if constexpr (BIAS) bq = *reinterpret_cast<const uint4*>(beta + c8 * 8);
     put_params<BIAS>(gq, bq, c8, woff, gsh, bsh);
+  }
+}
+
+// fp16 or fp32 row parameters (the input's type): a plain staging loop, 8
+// columns per step, into the same LDS layout.
+template <bool BIAS, int T>
+__device__ __forceinline__ void stage_params_t(const void* gamma, const void* beta, float woff, uint32_t cols,
+                                               float* gsh, float* bsh) {
+  for (uint32_t c8 = threadIdx.x; c8 * 8 < cols; c8 += kThreads) {
+    float gv[8], bv[8];
+    load8_t<T>(gamma, c8 * 8, gv);
+    if constexpr (BIAS) load8_t<T>(beta, c8 * 8, bv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gv[i] = gv[i] + woff;
+    const uint32_t i0 = pidx(c8 * 8), i1 = pidx(c8 * 8 + 4);
+    *reinterpret_cast<float4*>(gsh + i0) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+    *reinterpret_cast<float4*>(gsh + i1) = make_float4(gv[4], gv[5], gv[6], gv[7]);
+    if constexpr (BIAS) {
+      *reinterpret_cast<float4*>(bsh + i0) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+      *reinterpret_cast<float4*>(bsh + i1) = make_float4(bv[4], bv[5], bv[6], bv[7]);
+    }
   }
 }
 

@@ -120,6 +120,8 @@ def test_rmsnorm_validation(lib):
 
 
 def test_other_entry_points_take_bf16_only(lib):
+    # Every call here stops at validation: the workspace is too small (1 << 16 bytes, status 6) for the
+    # accepted dtypes, so nothing is ever launched on the fake pointers.
     import rmsnorm_nvfp4_block_amd as q
 
     g = q.Global(None, None, None)
@@ -127,11 +129,16 @@ def test_other_entry_points_take_bf16_only(lib):
     p = q.Plane(FAKE, 16, FAKE, 2)
     for dt in (1, 2):
         assert lib.rmsnorm_nvfp4q(FAKE, dt, 4, 32, 32, FAKE, None, 0.0, 1e-6, None, 0, ctypes.byref(g),
-                                  ctypes.byref(p), 0, ctypes.byref(r), FAKE, 1 << 20, None) == 4
+                                  ctypes.byref(p), 0, ctypes.byref(r), FAKE, 1 << 16, None) == 6   # fp16/fp32 taken
         assert lib.nvfp4q_quantize_2d(FAKE, dt, 32, 32, 32, ctypes.byref(g), ctypes.byref(p), None, 0,
-                                      ctypes.byref(r), FAKE, 1 << 20, None) == 4
+                                      ctypes.byref(r), FAKE, 1 << 16, None) == 4
         assert lib.nvfp4q_grouped(FAKE, dt, 32, 32, 32, FAKE, 1, None, 1, 0, ctypes.byref(g), ctypes.byref(p),
-                                  None, None, 0, ctypes.byref(r), FAKE, 1 << 20, None) == 4
+                                  None, None, 0, ctypes.byref(r), FAKE, 1 << 16, None) == 4
+    assert lib.rmsnorm_nvfp4q(FAKE, 3, 4, 32, 32, FAKE, None, 0.0, 1e-6, None, 0, ctypes.byref(g),
+                              ctypes.byref(p), 0, ctypes.byref(r), FAKE, 1 << 16, None) == 4
+    # fp32 y rows must stay 16-byte aligned: ld_y 34 floats = 136 bytes
+    assert lib.rmsnorm_nvfp4q(FAKE, 2, 4, 32, 32, FAKE, None, 0.0, 1e-6, FAKE, 34, ctypes.byref(g),
+                              ctypes.byref(p), 0, ctypes.byref(r), FAKE, 1 << 16, None) == 3
     # the QK norm takes all three; an unknown dtype is refused before anything is launched
     assert lib.nvfp4q_qk_norm(FAKE, None, 3, 3, 4, 0, 128, 512, 0, FAKE, None, 0.0, 1e-6, None) == 4
     assert lib.nvfp4q_qk_norm(FAKE, None, 2, 3, 4, 0, 128, 510, 0, FAKE, None, 0.0, 1e-6, None) == 2

@@ -350,6 +350,41 @@ def test_quantize_fp32_given_amax_and_padded_rows(gpu_lib):
 
 
 @pytest.mark.parametrize("dtype", ["float16", "float32"])
+@pytest.mark.parametrize("shape,bias,woff,rounding", [((8, 7168), True, 0.0, "rtne"), ((37, 1040), False, 1.0, "sr"),
+                                                      ((300, 4096), True, 1.0, "sr"), ((5, 16384), False, 0.0, "rtne")])
+def test_rmsnorm_fp16_fp32_inputs(gpu_lib, dtype, shape, bias, woff, rounding):
+    # reading R-dtype: gamma, beta and y in the input's type; y within the arithmetic tolerance of the
+    # float64 value, codes the exact quantization of the GPU's own y, and almost all codes equal to the
+    # quantization of the oracle's y
+    import torch
+
+    T, H = shape
+    rng = np.random.default_rng(T + H)
+    ndt = getattr(np, dtype)
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-3, 3, (T, 1)))).astype(ndt)
+    g = (1 + 0.1 * rng.standard_normal(H)).astype(ndt)
+    b = (0.01 * rng.standard_normal(H)).astype(ndt) if bias else None
+    tdev = lambda a: torch.from_numpy(a).cuda()
+    got = gpu_lib.rmsnorm_nvfp4q(tdev(x), tdev(g), tdev(b) if bias else None, weight_offset=woff, eps=1e-6,
+                                 rounding=rounding, seed=11, offset=2, y_out=True)
+    od = "fp16" if dtype == "float16" else "fp32"
+    y_ref, y64, _ = oracle.rmsnorm_bf16(x, g, b, woff, 1e-6, return_f64=True, out_dtype=od)
+    yg = got["y"].cpu().numpy()
+    assert yg.dtype == ndt
+    tol = 2.0 ** -9 if dtype == "float16" else 2.0 ** -14
+    err = np.abs(yg.astype(np.float64) - y64)
+    assert np.all(err <= tol * np.abs(y64) + 2.0 ** -24), f"y error max {err.max()}"
+    amax = np.float32(np.max(np.abs(yg.astype(np.float32))))
+    assert_f32_bits("amax", f32(got["amax"])[0], amax)
+    own = oracle.quantize_rowwise(yg, amax=amax, rounding=rounding, seed=11, offset=2)
+    assert_same_bits("codes (own y)", np_u8(got["codes"], H // 2), own["codes"])
+    assert_same_bits("scales (own y)", np_u8(got["scales"], H // 16), own["scales"])
+    ref = oracle.quantize_rowwise(y_ref, rounding=rounding, seed=11, offset=2)
+    n, ok = code_step_mismatch(np_u8(got["codes"], H // 2), ref["codes"])
+    assert ok and n <= 1e-3 * T * H, f"{n} codes differ from the float64 oracle"
+
+
+@pytest.mark.parametrize("dtype", ["float16", "float32"])
 @pytest.mark.parametrize("head_dim", [64, 256])
 def test_qk_norm_fp16_fp32(gpu_lib, dtype, head_dim):
     import torch
