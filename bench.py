@@ -47,7 +47,7 @@ class Case:
         self.fast_math = fast_math
         self.planes = planes  # grouped: which planes a step writes
         self.tile16 = tile16  # weight: one scale per 16 x 16 tile
-        self.dtype = dtype    # quantize, qknorm: element type of the input
+        self.dtype = dtype    # quantize, prefill, decode, qknorm: element type of the input
         tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
         es = {"bf16": 2, "fp16": 2, "fp32": 4}[dtype]
         self.colwise = name != "grouped" or planes in ("col", "both")
@@ -66,7 +66,7 @@ class Case:
         x_bytes = R * C * es
         if name in ("quantize", "prefill", "decode"):
             out_bytes = R * C // 2 + R * C // 16
-            param_bytes = (C * 2 if w.gamma is not None else 0) + (C * 2 if w.beta is not None else 0)
+            param_bytes = (C * es if w.gamma is not None else 0) + (C * es if w.beta is not None else 0)
         elif name == "qknorm":           # in place: q and k read and written once, two weights read
             out_bytes = R * C * es + w.meta["k"].size * 2 * es
             param_bytes = 2 * es * w.meta["head_dim"]
@@ -91,8 +91,8 @@ class Case:
         self.nsets = max(1, math.ceil(ROTATE_BYTES / set_bytes))
         x0 = din(w.x)
         self.xs = [x0] + [x0.clone() for _ in range(self.nsets - 1)]
-        self.gamma = (din if name == "qknorm" else d)(w.gamma) if w.gamma is not None else None
-        self.beta = d(w.beta) if w.beta is not None else None
+        self.gamma = din(w.gamma) if w.gamma is not None else None
+        self.beta = din(w.beta) if w.beta is not None else None
         self.q = q
         self.torch = torch
         if name == "grouped":
@@ -279,7 +279,13 @@ def cpu_baseline(case, budget_s=12.0):
             rows = np.arange(r0, min(R, r0 + chunk))
             xs = w.x[rows]
             if name in ("prefill", "decode"):
-                oracle.rmsnorm_quantize(xs, w.gamma, w.beta, w.weight_offset, w.eps)
+                if case.dtype == "bf16":
+                    oracle.rmsnorm_quantize(xs, w.gamma, w.beta, w.weight_offset, w.eps)
+                else:
+                    ndt = np.float16 if case.dtype == "fp16" else np.float32
+                    conv = lambda a: None if a is None else oracle.bf16_to_f32(a).astype(ndt)
+                    oracle.rmsnorm_quantize(conv(xs), conv(w.gamma), conv(w.beta), w.weight_offset, w.eps,
+                                            out_dtype=case.dtype)
             elif name == "quantize":
                 if case.dtype == "bf16":
                     oracle.quantize_rowwise(xs)
@@ -468,7 +474,8 @@ def main():
     ap.add_argument("--tile16", action="store_true",
                     help="weight: NVFP4Q_SCALE_16X16 (one block scale per 16x16 tile, shared by both planes)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16", "fp32"],
-                    help="quantize, qknorm: element type of the input (the workload's values, converted exactly)")
+                    help="quantize, prefill, decode, qknorm: element type of the input (the workload's values, "
+                         "converted exactly)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-only", action="store_true",
                     help="time only the roofline kernel with a given amax (for kernel traces); no metric line")
@@ -518,8 +525,8 @@ def main():
         raise SystemExit("--fast-math concerns the transform, which the rowwise plane does not take")
     if args.tile16 and args.config not in ("weight", "experts"):
         raise SystemExit("--tile16 applies to the weight and experts workloads (the 2D path)")
-    if args.dtype != "bf16" and args.config not in ("quantize", "qknorm"):
-        raise SystemExit("--dtype applies to the quantize and qknorm workloads")
+    if args.dtype != "bf16" and args.config not in ("quantize", "qknorm", "prefill", "decode"):
+        raise SystemExit("--dtype applies to the quantize, prefill, decode and qknorm workloads")
     case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes, tile16=args.tile16,
                 dtype=args.dtype)
     log(f"[bench] {case.describe()}")
