@@ -83,11 +83,12 @@ typedef enum {
   NVFP4Q_E_WORKSPACE = 6    /* workspace missing, misaligned or too small */
 } nvfp4q_status;
 
-/* Element type of the input. nvfp4q_quantize, rmsnorm_nvfp4q and
- * nvfp4q_qk_norm take all three: the quantizer reads the values exactly as
+/* Element type of the input. All entry points but nvfp4q_grouped take all
+ * three: the quantizer reads the values exactly as
  * given; the norms take gamma (and beta) in the input's type and round their
  * output y to nearest even in that type (fp32: not rounded further), and
- * rmsnorm_nvfp4q quantizes that y. The 2D and grouped entry points take
+ * rmsnorm_nvfp4q quantizes that y; the 2D entry points (single and
+ * grouped weights) quantize the values as given. nvfp4q_grouped takes
  * NVFP4Q_BF16 only (else NVFP4Q_E_UNSUPPORTED). Rows of x (and y) start
  * 16-byte aligned: leading dimension * element size is a multiple of 16. */
 typedef enum { NVFP4Q_BF16 = 0, NVFP4Q_FP16 = 1, NVFP4Q_FP32 = 2 } nvfp4q_dtype;

@@ -212,13 +212,13 @@ def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, 
 
 def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=True, colwise=True,
                        tile16=False):
-    """Rowwise and columnwise planes of bf16 x [rows, cols] under one per-tensor scale.
+    """Rowwise and columnwise planes of x [rows, cols] (bf16, fp16 or fp32) under one per-tensor scale.
 
     tile16: NVFP4Q_SCALE_16X16 (one block scale per 16 x 16 tile, shared by both planes).
     """
     import torch
 
-    _check_bf16_2d(x)
+    dt = _dtype_code(x)
     lib = load()
     R, C = x.shape
     rc = rs = cc = cs = None
@@ -231,7 +231,7 @@ def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=
     amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
     scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
     ws = workspace(x.device)
-    st = lib.nvfp4q_quantize_2d(x.data_ptr(), 0, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
+    st = lib.nvfp4q_quantize_2d(x.data_ptr(), dt, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
                                 ctypes.byref(rp), ctypes.byref(cp),
                                 _rounding(rounding) | (SCALE_16X16 if tile16 else 0),
                                 ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(), _stream(x))
@@ -242,7 +242,8 @@ def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=
 
 def nvfp4q_quantize_2d_grouped(x, experts, amax=None, rounding="rtne", seed=0, offset=0, rowwise=True,
                                colwise=True, tile16=False):
-    """nvfp4q_quantize_2d of `experts` weights stacked in bf16 x [experts * rows, cols], each under its own amax.
+    """nvfp4q_quantize_2d of `experts` weights stacked in x [experts * rows, cols] (bf16, fp16 or fp32), each
+    under its own amax.
 
     amax: optional float32 CUDA tensor [experts]. Returns row_codes [experts * rows, ...], row_scales,
     col_codes [experts * cols, ...] (expert e's transposed plane in rows e * cols ..), col_scales, and
@@ -250,7 +251,7 @@ def nvfp4q_quantize_2d_grouped(x, experts, amax=None, rounding="rtne", seed=0, o
     """
     import torch
 
-    _check_bf16_2d(x)
+    dt = _dtype_code(x)
     lib = load()
     ER, C = x.shape
     if experts < 1 or ER % experts != 0:
@@ -266,7 +267,7 @@ def nvfp4q_quantize_2d_grouped(x, experts, amax=None, rounding="rtne", seed=0, o
     amax_out = torch.empty(experts, dtype=torch.float32, device=x.device)
     scale_out = torch.empty(experts, dtype=torch.float32, device=x.device)
     ws = workspace(x.device)
-    st = lib.nvfp4q_quantize_2d_grouped(x.data_ptr(), 0, experts, R, C, x.stride(0),
+    st = lib.nvfp4q_quantize_2d_grouped(x.data_ptr(), dt, experts, R, C, x.stride(0),
                                         ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(rp),
                                         ctypes.byref(cp), _rounding(rounding) | (SCALE_16X16 if tile16 else 0),
                                         ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(), _stream(x))

@@ -192,7 +192,7 @@ nvfp4q_status quantize_2d_impl(const void* x, nvfp4q_dtype dtype, int experts, i
                                const nvfp4q_plane* col, nvfp4q_rounding rounding, const nvfp4q_rng* rng,
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0) return NVFP4Q_E_SHAPE;
-  TRY(check_input(x, dtype, experts * rows, cols, ld_x));
+  TRY(check_input(x, dtype, experts * rows, cols, ld_x, true));
   // planes of an empty input hold no bytes and may come with NULL pointers
   const bool has_row = row && (row->codes || rows == 0), has_col = col && (col->codes || rows == 0);
   if (!has_row && !has_col) return NVFP4Q_E_NULLPTR;
@@ -212,7 +212,7 @@ nvfp4q_status quantize_2d_impl(const void* x, nvfp4q_dtype dtype, int experts, i
   uint32_t nparts = 0;
   if (!gg.amax_in) {
     RowArgs r = {};
-    r.x = x; r.rows = rows; r.cols = cols; r.ld_x = ld_x;
+    r.x = x; r.dtype = (int)dtype; r.rows = rows; r.cols = cols; r.ld_x = ld_x;
     r.ws = (Workspace*)workspace;
     hipError_t e = launch_amax_rows(r, s, &nparts, experts);
     if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
@@ -221,6 +221,7 @@ nvfp4q_status quantize_2d_impl(const void* x, nvfp4q_dtype dtype, int experts, i
   a.nparts = nparts;
   a.x = x; a.rows = rows; a.cols = cols; a.ld_x = ld_x;
   a.experts = experts;
+  a.dtype = (int)dtype;
   if (has_row) { a.rcodes = row->codes; a.rldc = row->ld_codes; a.rscales = row->scales; a.rlds = row->ld_scales; }
   if (has_col) { a.ccodes = col->codes; a.cldc = col->ld_codes; a.cscales = col->scales; a.clds = col->ld_scales; }
   a.tile16 = tile16;

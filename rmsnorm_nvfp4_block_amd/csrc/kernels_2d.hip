@@ -22,28 +22,30 @@
 // item 2 (the 2D weight kernel: wide shared-memory reads instead of 16-bit
 // ones, paired columnwise reads sharing one amax and reciprocal) and item 5
 // (scale bytes).
-#include "device.hpp"
-#include "launch.hpp"
+#include "rows.hpp"
 
 namespace nvfp4q {
 
 namespace {
 
 constexpr int kTileR = 128, kTileC = 128;
-constexpr int kRowBytes = kTileC * 2;  // 256 B per staged row
 
 __device__ __forceinline__ uint32_t swz_chunk(uint32_t chunk, uint32_t row) {
   return chunk ^ (((row >> 4) & 3u) << 2);
 }
 
 // T threads per tile: 128 / (T / 8) rows (rowwise) and 1024 / T columns
-// (columnwise) per thread. TILE: one scale per 16 x 16 tile.
-template <int T, bool ROW, bool COL, bool SR, bool TILE>
+// (columnwise) per thread. TILE: one scale per 16 x 16 tile. DT: element type
+// of x (bf16, fp16 or fp32; an fp32 tile stages 64 KiB).
+template <int T, bool ROW, bool COL, bool SR, bool TILE, int DT>
 __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles_c, uint32_t ntiles, uint32_t chunk) {
   constexpr int kRpt = kTileR / (T / 8);  // rows per thread
   constexpr int kRs = T / 8;              // row stride between a thread's rows
   constexpr int kCpt = 1024 / T;          // columns per thread (columnwise)
   constexpr int kW = T / 64;              // waves; wave w holds rows 8w .. 8w + 7 (+ kRs j)
+  constexpr int kEs = in_size<DT>();      // bytes per element
+  constexpr int kRowBytes = kTileC * kEs; // per staged row
+  constexpr int kPerChunk = 16 / kEs;     // elements per 16-byte chunk
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTileR * kRowBytes];
   __shared__ float rcp_tab[128];
   // TILE: maximum of each wave's 8 rows of every 16-column block, per row slot j
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
   const int64_t ld_x = a.ld_x;
   const int64_t rldc = a.rldc, rlds = a.rlds, cldc = a.cldc, clds = a.clds;
-  const uint16_t* __restrict__ x = (const uint16_t*)a.x + (int64_t)e * rows * ld_x;
+  const char* __restrict__ x = (const char*)a.x + (int64_t)e * rows * ld_x * kEs;
   uint8_t* __restrict__ rcodes = ROW ? a.rcodes + (int64_t)e * rows * rldc : nullptr;
   uint8_t* __restrict__ rscales = ROW ? a.rscales + (int64_t)e * rows * rlds : nullptr;
   uint8_t* __restrict__ ccodes = COL ? a.ccodes + (int64_t)e * cols * cldc : nullptr;
@@ -65,25 +67,25 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   const uint32_t tr = item / tiles_c, tc = item - tr * tiles_c;
   const uint32_t row0 = tr * kTileR, col0 = tc * kTileC;
 
-  // ---- load kRpt rows x 32 B per thread
+  // ---- load kRpt rows x one 16-element block per thread
   const uint32_t bsub = t & 7, rsub = t >> 3;
   const uint32_t col = col0 + bsub * 16;
-  uint4 q[kRpt][2];
-  const uint16_t* xp = x + (int64_t)(row0 + rsub) * ld_x + col;
+  Raw16<DT> q[kRpt];
+  const char* xp = x + ((int64_t)(row0 + rsub) * ld_x + col) * kEs;
   if (row0 + kTileR <= rows && col0 + kTileC <= cols) {
     // a whole tile (all but the edge tiles): no guards, one base address
 #pragma unroll
-    for (int j = 0; j < kRpt; ++j) {
-      q[j][0] = *reinterpret_cast<const uint4*>(xp + (int64_t)(kRs * j) * ld_x);
-      q[j][1] = *reinterpret_cast<const uint4*>(xp + (int64_t)(kRs * j) * ld_x + 8);
-    }
+    for (int j = 0; j < kRpt; ++j)
+#pragma unroll
+      for (int l = 0; l < kEs; ++l)
+        q[j].q[l] = *reinterpret_cast<const uint4*>(xp + (int64_t)(kRs * j) * ld_x * kEs + 16 * l);
   } else {
 #pragma unroll
     for (int j = 0; j < kRpt; ++j) {
       const uint32_t r = row0 + rsub + kRs * j;
       const bool ok = r < rows && col < cols;
-      q[j][0] = ld16(xp + (int64_t)(kRs * j) * ld_x, ok);
-      q[j][1] = ld16(xp + (int64_t)(kRs * j) * ld_x + 8, ok);
+#pragma unroll
+      for (int l = 0; l < kEs; ++l) q[j].q[l] = ld16(xp + (int64_t)(kRs * j) * ld_x * kEs + 16 * l, ok);
     }
   }
   const GScale g = consume_scales<T / 64>(a.ws, a.nparts, a.amax_in ? a.amax_in + e : nullptr,
@@ -94,8 +96,8 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
     for (int j = 0; j < kRpt; ++j) {
       const uint32_t lr = rsub + kRs * j;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<uint4*>(tile + lr * kRowBytes + swz_chunk(2 * bsub + h, lr) * 16) = q[j][h];
+      for (int h = 0; h < kEs; ++h)
+        *reinterpret_cast<uint4*>(tile + lr * kRowBytes + swz_chunk(kEs * bsub + h, lr) * 16) = q[j].q[h];
     }
   }
   const uint32_t wid = t >> 6;
@@ -104,8 +106,7 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
 #pragma unroll
     for (int j = 0; j < kRpt; ++j) {
       float v[16];
-      widen8(q[j][0], v);
-      widen8(q[j][1], v + 8);
+      widen_raw16<DT>(q[j], v);
       float m = max16_abs(v);
       m = fmaxf(m, __shfl_xor(m, 8, 64));
       m = fmaxf(m, __shfl_xor(m, 16, 64));
@@ -128,8 +129,7 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
       const uint32_t r = r0 + kRs * j;
       const bool ok = r < rows && col < cols;
       float v[16];
-      widen8(q[j][0], v);
-      widen8(q[j][1], v + 8);
+      widen_raw16<DT>(q[j], v);
       uint32_t sc;
       uint2 w;
       if constexpr (TILE) {
@@ -151,13 +151,17 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
     if constexpr (!TILE) __syncthreads();
     const uint32_t mb = t & 7, cg = t >> 3;           // 8 row blocks x T/8 column groups
     const uint32_t lc = cg * kCpt;                     // first local column
-    const uint32_t cchunk = lc >> 3;                   // its 16-byte chunk of a staged row
-    uint32_t d[16][kCpt / 2];                          // bf16 pairs: columns lc + 2k, lc + 2k + 1
+    const uint32_t cchunk = lc / kPerChunk;            // its 16-byte chunk of a staged row
+    constexpr int kWords = kCpt * kEs / 4;             // 32-bit words of the thread's columns in one row
+    uint32_t d[16][kWords];                            // 2-byte types: pairs of columns; fp32: one each
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t lr = mb * 16 + i;
-      const uint8_t* src = tile + lr * kRowBytes + swz_chunk(cchunk, lr) * 16 + (lc & 7) * 2;
-      if constexpr (kCpt == 4) {
+      const uint8_t* src = tile + lr * kRowBytes + swz_chunk(cchunk, lr) * 16 + (lc % kPerChunk) * kEs;
+      if constexpr (kWords == 4) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src);
+        d[i][0] = u.x; d[i][1] = u.y; d[i][2] = u.z; d[i][3] = u.w;
+      } else if constexpr (kWords == 2) {
         const uint2 u = *reinterpret_cast<const uint2*>(src);
         d[i][0] = u.x;
         d[i][1] = u.y;
@@ -182,7 +186,11 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
       const uint32_t gc = gc0 + c;
       float v[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = (c & 1) ? bf_hi(d[i][c >> 1]) : bf_lo(d[i][c >> 1]);
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (DT == kInFP32) v[i] = __uint_as_float(d[i][c]);
+        else if constexpr (DT == kInFP16) v[i] = (c & 1) ? h_hi(d[i][c >> 1]) : h_lo(d[i][c >> 1]);
+        else v[i] = (c & 1) ? bf_hi(d[i][c >> 1]) : bf_lo(d[i][c >> 1]);
+      }
       const uint32_t sc = TILE ? tsc : block_scale(max16_abs(v), g.enc);
       const float rc = rcp_tab[sc];
 #pragma unroll
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   }
 }
 
-template <int T, bool ROW, bool COL, bool TILE>
+template <int T, bool ROW, bool COL, bool TILE, int DT>
 void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
   const uint32_t tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
   const uint32_t tiles_c = (uint32_t)((a.cols + kTileC - 1) / kTileC);
@@ -212,17 +220,24 @@ void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
   // measured slower here (8192 x 8192 with SR: 97.5 vs 91.3 us per step).
   const uint32_t ntiles = tiles_r * tiles_c, chunk = 0;
   dim3 grid(ntiles, a.experts), block(T);
-  if (a.sr) hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, true, TILE>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
-  else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false, TILE>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+  if (a.sr) hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, true, TILE, DT>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+  else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false, TILE, DT>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
 }
 
 // 512 threads per tile (two rows and two columns each): the tile's LDS
 // limits a CU to four workgroups, which then hold 32 waves (256 threads: 16
 // waves, 3 us slower on 8192 x 8192 with SR).
+template <bool ROW, bool COL, int DT>
+void launch_2d_rcd(const TwoDArgs& a, hipStream_t s) {
+  if (a.tile16) launch_2d_t<512, ROW, COL, true, DT>(a, s);
+  else launch_2d_t<512, ROW, COL, false, DT>(a, s);
+}
+
 template <bool ROW, bool COL>
 void launch_2d_rc(const TwoDArgs& a, hipStream_t s) {
-  if (a.tile16) launch_2d_t<512, ROW, COL, true>(a, s);
-  else launch_2d_t<512, ROW, COL, false>(a, s);
+  if (a.dtype == kInFP16) launch_2d_rcd<ROW, COL, kInFP16>(a, s);
+  else if (a.dtype == kInFP32) launch_2d_rcd<ROW, COL, kInFP32>(a, s);
+  else launch_2d_rcd<ROW, COL, kInBF16>(a, s);
 }
 
 }  // namespace

@@ -58,6 +58,7 @@ struct TwoDArgs {
   const float* amax_in;
   float* amax_out;
   float* scale_out;
+  int dtype;     // element type of x (nvfp4q_dtype)
   int experts;   // stacked weights (grid y); rows is the rows of one weight
   bool tile16;  // one scale per 16 x 16 tile (both planes)
   bool sr;

@@ -119,7 +119,7 @@ def test_rmsnorm_validation(lib):
     assert call(ws=None) == 6
 
 
-def test_other_entry_points_take_bf16_only(lib):
+def test_dtype_acceptance_per_entry_point(lib):
     # Every call here stops at validation: the workspace is too small (1 << 16 bytes, status 6) for the
     # accepted dtypes, so nothing is ever launched on the fake pointers.
     import rmsnorm_nvfp4_block_amd as q
@@ -131,7 +131,7 @@ def test_other_entry_points_take_bf16_only(lib):
         assert lib.rmsnorm_nvfp4q(FAKE, dt, 4, 32, 32, FAKE, None, 0.0, 1e-6, None, 0, ctypes.byref(g),
                                   ctypes.byref(p), 0, ctypes.byref(r), FAKE, 1 << 16, None) == 6   # fp16/fp32 taken
         assert lib.nvfp4q_quantize_2d(FAKE, dt, 32, 32, 32, ctypes.byref(g), ctypes.byref(p), None, 0,
-                                      ctypes.byref(r), FAKE, 1 << 16, None) == 4
+                                      ctypes.byref(r), FAKE, 1 << 16, None) == 6    # fp16/fp32 taken
         assert lib.nvfp4q_grouped(FAKE, dt, 32, 32, 32, FAKE, 1, None, 1, 0, ctypes.byref(g), ctypes.byref(p),
                                   None, None, 0, ctypes.byref(r), FAKE, 1 << 16, None) == 4
     assert lib.rmsnorm_nvfp4q(FAKE, 3, 4, 32, 32, FAKE, None, 0.0, 1e-6, None, 0, ctypes.byref(g),

@@ -581,6 +581,38 @@ def test_2d_tile16_weight_8192x8192_sampled(gpu_lib):
         assert_same_bits("col scales" + where, cs[c0:c0 + 64, r0 // 16:r0 // 16 + 2], q["col"]["scales"])
 
 
+@pytest.mark.parametrize("dtype", ["float16", "float32"])
+@pytest.mark.parametrize("shape", [(16, 16), (144, 272), (528, 16), (256, 384)])
+@pytest.mark.parametrize("rounding,tile16", [("rtne", False), ("sr", False), ("sr", True)])
+def test_2d_fp16_fp32_inputs(gpu_lib, dtype, shape, rounding, tile16):
+    # reading R-dtype on the 2D path: both planes quantize the input values as given (fp32 tiles stage
+    # 64 KiB in LDS); partial work tiles at the edges
+    import torch
+
+    rng = np.random.default_rng(shape[0] + 3 * shape[1] + (7 if tile16 else 0))
+    R, C = shape
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-3, 3, (R, 1)))
+         * np.exp(rng.uniform(-2, 2, (1, C)))).astype(getattr(np, dtype))
+    got = gpu_lib.nvfp4q_quantize_2d(torch.from_numpy(x).cuda(), rounding=rounding, seed=0x2D, offset=6,
+                                     tile16=tile16)
+    fn = oracle.quantize_2d_block if tile16 else oracle.quantize_2d
+    q = fn(x, rounding=rounding, seed=0x2D, offset=6)
+    _tile16_compare(got, q, R, C)
+    assert_f32_bits("amax", f32(got["amax"])[0], q["amax"])
+
+
+def test_2d_experts_fp32(gpu_lib):
+    import torch
+
+    rng = np.random.default_rng(42)
+    x = np.concatenate([(rng.standard_normal((64, 208)) * s).astype(np.float32) for s in (0.02, 5.0, 1e-3)])
+    got = gpu_lib.nvfp4q_quantize_2d_grouped(torch.from_numpy(x).cuda(), 3, rounding="sr", seed=9, tile16=True)
+    q = oracle.quantize_2d_experts(x, 3, rounding="sr", seed=9, tile16=True)
+    _tile16_compare(got, q, 64, 208)
+    for e in range(3):
+        assert_f32_bits(f"expert {e} amax", f32(got["amax"])[e], q["amax"][e])
+
+
 # ---------------------------------------------------------------- grouped 2D weights (reading R-experts)
 @pytest.mark.parametrize("experts,shape", [(1, (48, 80)), (3, (144, 272)), (4, (16, 2064))])
 @pytest.mark.parametrize("rounding", ["rtne", "sr"])
