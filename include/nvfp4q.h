@@ -84,13 +84,12 @@ typedef enum {
 } nvfp4q_status;
 
 /* Element type of the input. All entry points but nvfp4q_grouped take all
- * three: the quantizer reads the values exactly as
- * given; the norms take gamma (and beta) in the input's type and round their
- * output y to nearest even in that type (fp32: not rounded further), and
- * rmsnorm_nvfp4q quantizes that y; the 2D entry points (single and
- * grouped weights) quantize the values as given. nvfp4q_grouped takes
- * NVFP4Q_BF16 only (else NVFP4Q_E_UNSUPPORTED). Rows of x (and y) start
- * 16-byte aligned: leading dimension * element size is a multiple of 16. */
+ * three. The quantizers (rowwise and 2D) read the values exactly as given.
+ * The norms take gamma (and beta) in the input's type and round their output
+ * y to nearest even in that type (fp32: not rounded further); rmsnorm_nvfp4q
+ * quantizes that y. nvfp4q_grouped takes NVFP4Q_BF16 only (else
+ * NVFP4Q_E_UNSUPPORTED). Rows of x (and y) start 16-byte aligned: leading
+ * dimension * element size is a multiple of 16. */
 typedef enum { NVFP4Q_BF16 = 0, NVFP4Q_FP16 = 1, NVFP4Q_FP32 = 2 } nvfp4q_dtype;
 
 /* Rounding of the E2M1 codes. NVFP4Q_FAST_MATH may be OR-ed into the value
