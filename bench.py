@@ -317,6 +317,9 @@ def cpu_baseline(case, budget_s=12.0):
                   f"(both planes)")
     else:
         sample = f"{passes} calls of {min(chunk, R)} consecutive rows of the {name} workload"
+    if case.dtype != "bf16":
+        sample += (f" ({case.dtype} input" + ("" if name in ("quantize", "prefill", "decode") else
+                                            "; the oracle run on the bf16 values it was converted from") + ")")
     threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": sample + f"; {el:.1f} s, {done_bytes / 1e6:.1f} MB of compulsory bytes",
