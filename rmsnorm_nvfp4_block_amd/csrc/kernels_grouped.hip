@@ -1,5 +1,7 @@
 // Grouped (per-expert) columnwise NVFP4 for gfx950, optionally after a
-// 16-point random Hadamard transform along the tokens of each 16-token block.
+// 16-point random Hadamard transform along the tokens of each 16-token block,
+// and optionally the rowwise plane of the same rows (no transform, its own
+// per-group amax) from the same loads.
 //
 // Work unit: the padded token axis of all groups together is a sequence of
 // 16-token blocks (group g occupies blocks Poff_g/16 .. Poff_{g+1}/16 - 1).
@@ -17,8 +19,9 @@
 // and read zero without touching memory.
 //
 // Three kernels: the amax pass writes one partial maximum per (block, column
-// tile); a reduce kernel (one workgroup per group) takes each group's maximum
-// over its blocks' partials; the encode pass reads one amax per group, keeps
+// tile) and plane; a reduce kernel (one workgroup per group) takes each
+// group's maximum over its blocks' partials; the encode pass reads one amax
+// per group and plane, keeps
 // per-group encode reciprocal tables in LDS (two per wave, written and read by
 // that wave only), stages its codes and scales in LDS and writes them out in
 // coalesced pieces of the transposed planes.
@@ -27,7 +30,8 @@
 // allocation tail (stop at the last padded row, leave the tail untouched);
 // Config surface and AUTO (64 groups, device offsets); Fast math (the
 // transform's bf16 round-through on the columnwise path); Optimization item 3
-// (one Philox draw per 16-element block).
+// (one Philox draw per 16-element block); Performance (the grouped row +
+// column quantize).
 #include "device.hpp"
 #include "launch.hpp"
 
