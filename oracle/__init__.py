@@ -61,6 +61,10 @@ that implements it. Readings are:
   R-experts  grouped 2D weights: expert e of E stacked [M, K] weights is the
              2D quantization of its own weight under its own amax, SR tags
              2e (rowwise) and 2e + 1 (columnwise); planes stacked by expert.
+  R-dtype    fp16 / fp32 inputs: quantizers take the values as given; the
+             norms round y in the input's type; the grouped transform's
+             output is rounded through the input's type (bf16, fp16) or not
+             at all (fp32).
   R-qk       QK norm: the RMSNorm formula above applied to each attention head
              (64, 128 or 256 elements) of q and of k, each tensor with its own
              weight of head_dim entries, output in the input's place.

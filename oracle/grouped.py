@@ -55,10 +55,15 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
     index row * (K/16) + k/16 with the row's index in x. Adds row_codes
     [total_rows, K/2], row_scales [total_rows, K/16], row_amax, row_s_dec [G].
     colwise=False skips the columnwise plane (its arrays stay zero).
+    x may also hold float16 or float32 values (reading R-dtype): the transform's
+    output is then rounded through the input's type (fp16), or not at all (fp32).
     Returns dict with codes [K, Mpad/2], scales [K, Mpad/16], amax [G], s_enc [G],
     s_dec [G], poff [G+1].
     """
-    x = np.asarray(x, dtype=np.uint16)
+    x = np.asarray(x)
+    if x.dtype not in (np.float16, np.float32):
+        x = x.astype(np.uint16)
+    dt = {np.dtype(np.uint16): "bf16", np.dtype(np.float16): "fp16", np.dtype(np.float32): "fp32"}[x.dtype]
     T, K = x.shape
     off = np.asarray(offsets, dtype=np.int64)
     G = len(off) - 1
@@ -74,15 +79,18 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
     for g in (sel if colwise else ()):
         n = int(off[g + 1] - off[g])
         pg = int(poff[g + 1] - poff[g])
-        z = np.zeros((pg, K), dtype=np.uint16)
+        z = np.zeros((pg, K), dtype=x.dtype)
         z[:n] = x[off[g]:off[g + 1]]
         zt = np.ascontiguousarray(z.T).reshape(K, pg // 16, 16)     # column blocks along tokens
-        if apply_rht and fast_math:
-            zf = rht16_f32(bf16_to_f32(zt), rht_mask)
-        elif apply_rht:
+        zv = bf16_to_f32(zt) if dt == "bf16" else zt.astype(np.float32)
+        if apply_rht and (fast_math or dt == "fp32"):
+            zf = rht16_f32(zv, rht_mask)                       # no round-through (fast math; fp32 input)
+        elif apply_rht and dt == "bf16":
             zf = bf16_to_f32(rht16(zt, rht_mask))
+        elif apply_rht:                                        # fp16: round-through to fp16
+            zf = rht16_f32(zv, rht_mask).astype(np.float16).astype(np.float32)
         else:
-            zf = bf16_to_f32(zt)
+            zf = zv
         a = np.float32(np.max(np.abs(zf))) if zf.size else np.float32(0.0)
         if amax is not None:
             a = np.float32(np.asarray(amax, dtype=np.float32)[g])
@@ -108,7 +116,8 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
         for g in sel:
             lo, hi = int(off[g]), int(off[g + 1])
             seg = x[lo:hi]
-            a = (np.float32(np.max(np.abs(bf16_to_f32(seg)))) if hi > lo else np.float32(0.0)) \
+            segv = bf16_to_f32(seg) if dt == "bf16" else seg.astype(np.float32)
+            a = (np.float32(np.max(np.abs(segv))) if hi > lo else np.float32(0.0)) \
                 if row_amax is None else np.float32(np.asarray(row_amax, dtype=np.float32)[g])
             ra_out[g] = a
             rd_out[g] = global_scales(a)[1]

@@ -272,3 +272,24 @@ def test_rmsnorm_fp16_fp32_output_rounding():
                                out_dtype="fp32")
     assert np.array_equal(y32, y64.astype(np.float32))
     assert not np.array_equal(y32, F.bf16_to_f32(rmsnorm_bf16(xb, gb, None, 0.0, 1e-6)))
+
+
+def test_grouped_round_through_follows_the_input_type():
+    # One group of 16 tokens, column 0 = (1, 3 * 2^-11, 0, ...) along the tokens, no sign flips: every
+    # transform output is 0.25 (1 +- 3 * 2^-11) = 0.25 +- 3 * 2^-13. The largest, 0.25 + 1.5 * 2^-12, is a
+    # tie between two fp16 values and goes to the even one, 0.25 + 2^-11 = 0.25048828125; in bf16 (step
+    # 2^-9 above 0.25) it rounds to 0.25; fp32 input takes no round-through: 0.2503662109375 (reading
+    # R-dtype). The group amax shows which rounding ran.
+    x = np.zeros((16, 16), np.float32)
+    x[0, 0], x[1, 0] = 1.0, 3.0 * 2.0 ** -11
+    offs = np.array([0, 16], np.int32)
+    for xin, expect in ((x, 0.2503662109375), (x.astype(np.float16), 0.25048828125), (_bits(x), 0.25)):
+        q = grouped_quantize(xin, offs, apply_rht=True, rht_mask=0, rounding="rtne")
+        assert float(q["amax"][0]) == expect, (xin.dtype, float(q["amax"][0]))
+    # fp32 input equals the bf16 path in fast-math mode on bf16-exact values (neither rounds the output)
+    rng = np.random.default_rng(43)
+    xb = _bits(rng.standard_normal((40, 32)))
+    offs = np.array([0, 17, 40], np.int32)
+    a = grouped_quantize(F.bf16_to_f32(xb), offs, apply_rht=True, rht_mask=0x35A9, rounding="sr", seed=3)
+    b = grouped_quantize(xb, offs, apply_rht=True, rht_mask=0x35A9, rounding="sr", seed=3, fast_math=True)
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
