@@ -47,7 +47,7 @@ class Case:
         self.fast_math = fast_math
         self.planes = planes  # grouped: which planes a step writes
         self.tile16 = tile16  # weight: one scale per 16 x 16 tile
-        self.dtype = dtype    # element type of the input (all workloads but grouped)
+        self.dtype = dtype    # element type of the input
         tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
         es = {"bf16": 2, "fp16": 2, "fp32": 4}[dtype]
         self.colwise = name != "grouped" or planes in ("col", "both")
@@ -477,7 +477,7 @@ def main():
     ap.add_argument("--tile16", action="store_true",
                     help="weight: NVFP4Q_SCALE_16X16 (one block scale per 16x16 tile, shared by both planes)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16", "fp32"],
-                    help="element type of the input (the workload's values, converted exactly; not grouped)")
+                    help="element type of the input (the workload's values, converted exactly)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-only", action="store_true",
                     help="time only the roofline kernel with a given amax (for kernel traces); no metric line")
@@ -527,8 +527,6 @@ def main():
         raise SystemExit("--fast-math concerns the transform, which the rowwise plane does not take")
     if args.tile16 and args.config not in ("weight", "experts"):
         raise SystemExit("--tile16 applies to the weight and experts workloads (the 2D path)")
-    if args.dtype != "bf16" and args.config == "grouped":
-        raise SystemExit("--dtype: the grouped path takes bf16 only")
     case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes, tile16=args.tile16,
                 dtype=args.dtype)
     log(f"[bench] {case.describe()}")

@@ -83,13 +83,13 @@ typedef enum {
   NVFP4Q_E_WORKSPACE = 6    /* workspace missing, misaligned or too small */
 } nvfp4q_status;
 
-/* Element type of the input. All entry points but nvfp4q_grouped take all
- * three. The quantizers (rowwise and 2D) read the values exactly as given.
- * The norms take gamma (and beta) in the input's type and round their output
- * y to nearest even in that type (fp32: not rounded further); rmsnorm_nvfp4q
- * quantizes that y. nvfp4q_grouped takes NVFP4Q_BF16 only (else
- * NVFP4Q_E_UNSUPPORTED). Rows of x (and y) start 16-byte aligned: leading
- * dimension * element size is a multiple of 16. */
+/* Element type of the input; every entry point takes all three. The
+ * quantizers (rowwise, 2D, grouped) read the values exactly as given; the
+ * grouped transform rounds its output through the input's type (bf16, fp16;
+ * fp32: not at all). The norms take gamma (and beta) in the input's type and
+ * round their output y to nearest even in that type (fp32: not rounded
+ * further); rmsnorm_nvfp4q quantizes that y. Rows of x (and y) start 16-byte
+ * aligned: leading dimension * element size is a multiple of 16. */
 typedef enum { NVFP4Q_BF16 = 0, NVFP4Q_FP16 = 1, NVFP4Q_FP32 = 2 } nvfp4q_dtype;
 
 /* Rounding of the E2M1 codes. NVFP4Q_FAST_MATH may be OR-ed into the value
@@ -290,8 +290,10 @@ nvfp4q_status nvfp4q_qk_norm(void *q, void *k, nvfp4q_dtype dtype, int64_t token
  *   per 16-row block x 128-column tile and plane; shapes needing more slots
  *   than the workspace holds (planes * floor((total_rows + 15 G) / 16) *
  *   ceil(cols / 128) + 128 > 262112) return NVFP4Q_E_UNSUPPORTED.
- *   ld_x above 2^24 returns NVFP4Q_E_SHAPE (the kernels address 32 rows of x
- *   with 32-bit byte offsets).
+ *   A row stride above 2^25 bytes (ld_x above 2^24 for bf16 / fp16, 2^23 for
+ *   fp32) returns NVFP4Q_E_SHAPE (the kernels address 32 rows of x with
+ *   32-bit byte offsets). fp16 / fp32 input: the transform's output is
+ *   rounded through the input's type (fp16), or not at all (fp32).
  *   [PR, Optimization 2, 3, 5; Fast math (bf16 round-through of the
  *    transform); Config surface and AUTO (64 groups, device offsets)]
  */

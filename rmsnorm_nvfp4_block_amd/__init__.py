@@ -311,7 +311,7 @@ def nvfp4q_qk_norm(q, k, q_weight, k_weight, head_dim, weight_offset=0.0, eps=1e
 def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr", seed=0, offset=0,
                    codes=None, scales=None, fast_math=False, colwise=True, rowwise=False, row_amax=None,
                    row_codes=None, row_scales=None):
-    """Per-group NVFP4 of bf16 x [total_rows, cols]: the columnwise plane (optionally
+    """Per-group NVFP4 of x [total_rows, cols] (bf16, fp16 or fp32): the columnwise plane (optionally
     after the 16-point RHT) and/or the rowwise plane (no transform), one amax per
     group and plane.
 
@@ -324,7 +324,7 @@ def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="
     """
     import torch
 
-    _check_bf16_2d(x)
+    dt = _dtype_code(x)
     if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1:
         raise ValueError("offsets must be a 1-D int32 CUDA tensor")
     if not colwise and not rowwise:
@@ -354,7 +354,7 @@ def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="
     ws = workspace(x.device)
     gcol = _global(amax, amax_out, scale_out) if colwise else None
     grow = _global(row_amax, ramax_out, rscale_out) if rowwise else None
-    st = lib.nvfp4q_grouped(x.data_ptr(), 0, T, C, x.stride(0), offsets.data_ptr(), G, poff.data_ptr(),
+    st = lib.nvfp4q_grouped(x.data_ptr(), dt, T, C, x.stride(0), offsets.data_ptr(), G, poff.data_ptr(),
                             1 if apply_rht else 0, int(rht_mask),
                             ctypes.byref(gcol) if gcol is not None else None,
                             ctypes.byref(plane) if plane is not None else None,

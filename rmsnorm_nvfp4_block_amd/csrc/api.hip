@@ -285,14 +285,14 @@ nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_ro
                              const nvfp4q_plane* col, const nvfp4q_global* g_row, const nvfp4q_plane* row,
                              nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  TRY(check_input(x, dtype, total_rows, cols, ld_x));
+  TRY(check_input(x, dtype, total_rows, cols, ld_x, true));
   // an empty rowwise plane (no rows) may come with NULL pointers
   const bool want_col = col && col->codes, want_row = row && (row->codes || total_rows == 0);
   if (!offsets || (!want_col && !want_row)) return NVFP4Q_E_NULLPTR;
   if (num_groups < 1 || num_groups > 64) return NVFP4Q_E_SHAPE;
   if (apply_rht != 0 && apply_rht != 1) return NVFP4Q_E_UNSUPPORTED;
   if (rht_sign_mask > 0xFFFFu) return NVFP4Q_E_UNSUPPORTED;
-  if (ld_x > kGroupedMaxLd) return NVFP4Q_E_SHAPE;
+  if (ld_x * dtype_size(dtype) > 2 * kGroupedMaxLd) return NVFP4Q_E_SHAPE;
   const int64_t cap = total_rows + 15 * (int64_t)num_groups;
   if (want_col) {
     TRY(check_plane(col, cols, cap));  // codes and scales present (cap >= 15 > 0), alignment
@@ -308,7 +308,7 @@ nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_ro
       grouped_partials(total_rows, cols, num_groups, (col_amax ? 1 : 0) + (row_amax ? 1 : 0)) > kPartials)
     return NVFP4Q_E_UNSUPPORTED;
   GroupArgs a = {};
-  a.x = x; a.rows = total_rows; a.cols = cols; a.ld_x = ld_x;
+  a.x = x; a.dtype = (int)dtype; a.rows = total_rows; a.cols = cols; a.ld_x = ld_x;
   a.offsets = offsets; a.groups = num_groups; a.poff_out = padded_offsets_out;
   a.rht = apply_rht != 0; a.mask = rht_sign_mask;
   a.col = want_col;

@@ -32,8 +32,7 @@
 // transform's bf16 round-through on the columnwise path); Optimization item 3
 // (one Philox draw per 16-element block); Performance (the grouped row +
 // column quantize).
-#include "device.hpp"
-#include "launch.hpp"
+#include "rows.hpp"
 
 namespace nvfp4q {
 
@@ -108,10 +107,12 @@ __device__ __forceinline__ Blk16 locate(const GroupScan& q, int groups, uint32_t
 
 // A buffer resource over x from row `row` to the end of x (record count
 // capped below kOutOfRange).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_from_row(const uint16_t* x, int64_t ld_x, int rows, int row) {
-  int64_t left = ((int64_t)rows - row) * ld_x * 2;
-  left = left < 0 ? 0 : left > (int64_t)(kOutOfRange - 16) ? (int64_t)(kOutOfRange - 16) : left;
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(x + (int64_t)row * ld_x), (short)0, (int)left, 0x00020000);
+template <int DT>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t x_from_row(const void* x, int64_t ld_x, int rows, int row) {
+  int64_t left = ((int64_t)rows - row) * ld_x * in_size<DT>();
+  left = left < 0 ? 0 : left > (int64_t)(kOutOfRange - 32) ? (int64_t)(kOutOfRange - 32) : left;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)x + (int64_t)row * ld_x * in_size<DT>()), (short)0,
+                                           (int)left, 0x00020000);
 }
 
 // Work items: a workgroup takes 4 consecutive block pairs (wave w: pair
@@ -149,37 +150,46 @@ __device__ __forceinline__ Item item_of(uint32_t ctile, uint32_t pair, const Gro
   return it;
 }
 
-// The lane's 16 tokens x CPL columns as bf16 pairs: r[i][j] holds columns
-// 2j, 2j + 1 of token row i.
-template <int CPL>
-using Tile = uint32_t[16][CPL / 2];
+// The lane's 16 tokens x CPL columns of element type DT: 2-byte types as
+// pairs (r[i][j] holds columns 2j, 2j + 1 of token row i), fp32 one per word.
+template <int CPL, int DT>
+using Tile = uint32_t[16][CPL * in_size<DT>() / 4];
 
 // Issues the item's loads: one resource based at the first block's first row,
 // row offsets in the per-lane offset (so the range check covers them).
-template <int CPL>
-__device__ __forceinline__ void load_item(const uint16_t* __restrict__ x, int64_t ld_x, int rows, const Item& it,
-                                          bool live, Tile<CPL>& r) {
+template <int CPL, int DT>
+__device__ __forceinline__ void load_item(const void* __restrict__ x, int64_t ld_x, int rows, const Item& it,
+                                          bool live, Tile<CPL, DT>& r) {
+  constexpr uint32_t kEs = in_size<DT>();
+  constexpr int kBytes = CPL * kEs;  // per token row and lane: 8, 16 or 32
   const bool h = (threadIdx.x >> 5) & 1;
   // first row in x of each block: its group's row0 plus the block's first
   // token within the group
   const int t0a = (int)(it.tb0 * 16u) - it.b0.start, t0b = (int)((it.tb0 + 1) * 16u) - it.b1.start;
   const int ra = it.b0.valid ? it.b0.row0 + t0a : 0;
   const int rb = it.b1.row0 + t0b;
-  const __amdgpu_buffer_rsrc_t rs = x_from_row(x, ld_x, rows, ra);
-  const uint32_t ldb = (uint32_t)ld_x * 2u;
+  const __amdgpu_buffer_rsrc_t rs = x_from_row<DT>(x, ld_x, rows, ra);
+  const uint32_t ldb = (uint32_t)ld_x * kEs;
   // real tokens of the lane's block (none for an item that is only a refill
   // past the end of a run: its loads are issued but read nothing)
   const int left = live && it.ok ? (h ? it.b1.n - t0b : it.b0.n - t0a) : 0;
-  const uint32_t v0 = (uint32_t)(h ? rb - ra : 0) * ldb + it.col * 2u;
+  const uint32_t v0 = (uint32_t)(h ? rb - ra : 0) * ldb + it.col * kEs;
+  static_assert(CPL == 4 || CPL == 8, "4 or 8 columns per lane");
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t off = i < left ? v0 + (uint32_t)i * ldb : kOutOfRange;
-    if constexpr (CPL == 8) {
+    if constexpr (kBytes == 32) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16u * hh, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[i][4 * hh + j] = t[j];
+      }
+    } else if constexpr (kBytes == 16) {
       const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) r[i][j] = t[j];
     } else {
-      static_assert(CPL == 4, "4 or 8 columns per lane");
       const auto t = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
       r[i][0] = t[0];
       r[i][1] = t[1];
@@ -188,23 +198,42 @@ __device__ __forceinline__ void load_item(const uint16_t* __restrict__ x, int64_
 }
 
 // Column c of the lane's tile as fp32.
-template <int CPL>
-__device__ __forceinline__ void column(const Tile<CPL>& r, int c, float v[16]) {
+template <int CPL, int DT>
+__device__ __forceinline__ void column(const Tile<CPL, DT>& r, int c, float v[16]) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = (c & 1) ? bf_hi(r[i][c >> 1]) : bf_lo(r[i][c >> 1]);
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (DT == kInFP32) v[i] = __uint_as_float(r[i][c]);
+    else if constexpr (DT == kInFP16) v[i] = (c & 1) ? h_hi(r[i][c >> 1]) : h_lo(r[i][c >> 1]);
+    else v[i] = (c & 1) ? bf_hi(r[i][c >> 1]) : bf_lo(r[i][c >> 1]);
+  }
+}
+
+// The transform's output rounded through the input's type (bf16, fp16; fp32:
+// unchanged), two values at a time.
+template <int DT>
+__device__ __forceinline__ void round_through2(float& a, float& b) {
+  if constexpr (DT == kInBF16) {
+    const uint32_t p = pack_bf16(a, b);
+    a = bf_lo(p);
+    b = bf_hi(p);
+  } else if constexpr (DT == kInFP16) {
+    a = (float)(_Float16)a;
+    b = (float)(_Float16)b;
+  }
 }
 
 // D: flips the sign of token row i of the lane's tile where bit i of the mask
-// is set: one XOR with 0x80008000 per bf16 pair (the bf16 sign bit becomes
-// the fp32 sign bit when the value is widened). The mask is wave-uniform, so
-// the per-row constants are scalar.
-template <int CPL>
-__device__ __forceinline__ void apply_signs(Tile<CPL>& r, uint32_t mask) {
+// is set: one XOR with 0x80008000 per 2-byte pair, 0x80000000 per fp32 word
+// (the element's sign bit becomes the fp32 sign bit when it is widened). The
+// mask is wave-uniform, so the per-row constants are scalar.
+template <int CPL, int DT>
+__device__ __forceinline__ void apply_signs(Tile<CPL, DT>& r, uint32_t mask) {
+  constexpr uint32_t kSign = DT == kInFP32 ? 0x80000000u : 0x80008000u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const uint32_t f = ((mask >> i) & 1u) ? 0x80008000u : 0u;
+    const uint32_t f = ((mask >> i) & 1u) ? kSign : 0u;
 #pragma unroll
-    for (int j = 0; j < CPL / 2; ++j) r[i][j] ^= f;
+    for (int j = 0; j < CPL * in_size<DT>() / 4; ++j) r[i][j] ^= f;
   }
 }
 
@@ -240,12 +269,12 @@ __device__ __forceinline__ uint32_t pk_max_mag(uint32_t acc, uint32_t w) {
   return __builtin_bit_cast(uint32_t, m);
 }
 
-// Pass 1: per-(block, column tile) maxima. COL: of the (transformed,
-// bf16-rounded) columnwise values, into partial[tb * ntc + ctile]. ROW: of
-// |x| itself (the rowwise plane has no transform), into partial[rbase + tb *
-// ntc + ctile].
-template <int CPL, bool RHT, bool FAST, bool COL, bool ROW>
-__global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict__ x, int rows, uint32_t cols,
+// Pass 1: per-(block, column tile) maxima. COL: of the (transformed, rounded
+// through the input's type) columnwise values, into partial[tb * ntc +
+// ctile]. ROW: of |x| itself (the rowwise plane has no transform), into
+// partial[rbase + tb * ntc + ctile].
+template <int CPL, bool RHT, bool FAST, bool COL, bool ROW, int DT>
+__global__ __launch_bounds__(kT) void k_grouped_amax(const void* __restrict__ x, int rows, uint32_t cols,
                                                      int64_t ld_x, const int32_t* __restrict__ offsets, int groups,
                                                      uint32_t mask, Workspace* ws, uint32_t nq, uint32_t ntc,
                                                      uint32_t npairs, uint32_t nb_max, uint32_t chunk, uint32_t rbase) {
@@ -257,26 +286,37 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
   const GroupScan q = group_scan(offsets, groups, rows);
   const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
   const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
-  Tile<CPL> r;
-  load_item<CPL>(x, ld_x, rows, it, true, r);
+  Tile<CPL, DT> r;
+  load_item<CPL, DT>(x, ld_x, rows, it, true, r);
   const bool writer = (threadIdx.x & 31) == 0 && it.tb < nb_max;
   if constexpr (ROW) {
-    uint32_t mm = 0;
+    float mr;
+    if constexpr (DT == kInFP32) {
+      uint32_t mm = 0;  // magnitude bits: their u32 order is the order of |x|
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int j = 0; j < CPL / 2; ++j) mm = pk_max_mag(mm, r[i][j]);
-    const uint32_t hi = mm >> 16, lo = mm & 0xFFFFu;
-    const float mr = half_wave_max(__uint_as_float((hi > lo ? hi : lo) << 16));  // lanes without data: 0
+        for (int j = 0; j < CPL; ++j) mm = max(mm, r[i][j] & 0x7FFFFFFFu);
+      mr = __uint_as_float(mm);
+    } else {
+      uint32_t mm = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < CPL / 2; ++j) mm = pk_max_mag(mm, r[i][j]);
+      const uint32_t hi = mm >> 16, lo = mm & 0xFFFFu, m16 = hi > lo ? hi : lo;
+      mr = DT == kInBF16 ? __uint_as_float(m16 << 16) : h_lo(m16);
+    }
+    mr = half_wave_max(mr);  // lanes without data: 0
     if (writer) ws->partial[rbase + it.tb * ntc + it.ctile] = mr;
   }
   if constexpr (COL) {
-    if constexpr (RHT) apply_signs<CPL>(r, mask);
+    if constexpr (RHT) apply_signs<CPL, DT>(r, mask);
     float m = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       float v16[16];
-      column<CPL>(r, c, v16);
+      column<CPL, DT>(r, c, v16);
       if constexpr (RHT) {
         // The last stage only feeds the maximum: max(|RN(a + b)|, |RN(a - b)|)
         // = RN(|a| + |b|), since one of a + b, a - b has magnitude |a| + |b|,
@@ -290,9 +330,9 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const uint16_t* __restrict_
         m = fmaxf(m, max16_abs(v16));
       }
     }
-    // max |bf16(0.25 y)| = bf16(0.25 max |y|): scaling by 0.25 and
-    // round-to-nearest-even are both monotone (fast math: no bf16 rounding).
-    if constexpr (RHT) m = FAST ? m * 0.25f : bf_lo(pack_bf16(m * 0.25f, 0.0f) & 0xFFFFu);
+    // max |RN_T(0.25 y)| = RN_T(0.25 max |y|): scaling by 0.25 and
+    // round-to-nearest-even are both monotone (fast math, fp32: no rounding).
+    if constexpr (RHT) m = FAST ? m * 0.25f : round_t<DT>(m * 0.25f);
     m = half_wave_max(m);  // lanes without data hold zeros
     if (writer) ws->partial[it.tb * ntc + it.ctile] = m;
   }
@@ -387,22 +427,31 @@ struct GroupTabs {
 // and the tables stay normal. Outside that range the unfolded path runs.
 __device__ __forceinline__ bool fold_ok(float amax) { return amax >= 0x1p-90f && amax <= 0x1p120f; }
 
-template <int CPL, bool RHT, bool SR, bool FOLD, bool FAST>
-__device__ __forceinline__ void encode_columns(Tile<CPL>& r, const float* tab, float enc, uint64_t blk, uint64_t nbp,
-                                               uint8_t* cst, uint8_t* sst, uint64_t seed, uint32_t offset) {
+template <int CPL, bool RHT, bool SR, bool FOLD, bool FAST, int DT>
+__device__ __forceinline__ void encode_columns(Tile<CPL, DT>& r, const float* tab, float enc, uint64_t blk,
+                                               uint64_t nbp, uint8_t* cst, uint8_t* sst, uint64_t seed,
+                                               uint32_t offset) {
+  static_assert(!FOLD || FAST || DT == kInBF16, "the fold is exact only for a bf16 round-through");
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     float v16[16];
-    column<CPL>(r, c, v16);
+    column<CPL, DT>(r, c, v16);
     if constexpr (RHT) {
       fwht16(v16);
       if constexpr (!FAST) {
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const uint32_t p =
-              FOLD ? pack_bf16(v16[i], v16[i + 1]) : pack_bf16(v16[i] * 0.25f, v16[i + 1] * 0.25f);
-          v16[i] = bf_lo(p);
-          v16[i + 1] = bf_hi(p);
+          if constexpr (DT == kInBF16) {
+            const uint32_t p =
+                FOLD ? pack_bf16(v16[i], v16[i + 1]) : pack_bf16(v16[i] * 0.25f, v16[i + 1] * 0.25f);
+            v16[i] = bf_lo(p);
+            v16[i + 1] = bf_hi(p);
+          } else {
+            float a = v16[i] * 0.25f, b = v16[i + 1] * 0.25f;
+            round_through2<DT>(a, b);
+            v16[i] = a;
+            v16[i + 1] = b;
+          }
         }
       } else if constexpr (!FOLD) {
 #pragma unroll
@@ -430,10 +479,12 @@ __device__ __forceinline__ void encode_columns(Tile<CPL>& r, const float* tab, f
   }
 }
 
-template <int CPL, bool RHT, bool SR, bool FAST>
-__device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32_t mask, const float* gam,
+template <int CPL, bool RHT, bool SR, bool FAST, int DT>
+__device__ __forceinline__ void encode_item(const Item& it, Tile<CPL, DT>& r, uint32_t mask, const float* gam,
                                             GroupTabs& gt, float* tabs, Stage<CPL>& st, uint32_t mpad,
                                             uint64_t seed, uint32_t offset) {
+  // the 0.25 folds exactly into a bf16 round-through, or where no round-through runs
+  constexpr bool kCanFold = FAST || DT == kInBF16;
   const uint32_t lane = threadIdx.x & 63, half = lane >> 5;
   const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (it.b0.g != gt.g0 || it.b1.g != gt.g1) {
@@ -442,7 +493,7 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32
     const float a0 = gam[gt.g0], a1 = gam[gt.g1];
     gt.s0 = global_scale(a0);
     gt.s1 = global_scale(a1);
-    gt.fold = RHT && fold_ok(a0) && fold_ok(a1);
+    gt.fold = kCanFold && RHT && fold_ok(a0) && fold_ok(a1);
     const float f = gt.fold ? 0.25f : 1.0f;
     // the wave's own tables: its LDS writes precede its reads
     tabs[lane] = encode_mult(lane, gt.s0.dec) * f;
@@ -450,7 +501,7 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32
     tabs[128 + lane] = encode_mult(lane, gt.s1.dec) * f;
     tabs[128 + lane + 64] = encode_mult(lane + 64, gt.s1.dec) * f;
   }
-  if constexpr (RHT) apply_signs<CPL>(r, mask);
+  if constexpr (RHT) apply_signs<CPL, DT>(r, mask);
   const float* tab = tabs + half * 128;
   const float enc = half ? gt.s1.enc : gt.s0.enc;
   const uint64_t nbp = (uint64_t)(mpad >> 4);  // blocks per plane row
@@ -461,9 +512,9 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL>& r, uint32
   uint8_t* cst = st.codes + (lane & 31) * CPL * kStagePitch + 8 * j;
   uint8_t* sst = st.scales + (lane & 31) * CPL * kItemBlocks + j;
   if (RHT && gt.fold)
-    encode_columns<CPL, RHT, SR, true, FAST>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
+    encode_columns<CPL, RHT, SR, kCanFold, FAST, DT>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
   else
-    encode_columns<CPL, RHT, SR, false, FAST>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
+    encode_columns<CPL, RHT, SR, false, FAST, DT>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
 }
 
 // Write-out of a staged item: plane rows of column tile ctile, blocks
@@ -496,8 +547,8 @@ __device__ __forceinline__ void write_item(const Stage<CPL>& st, uint32_t ctile,
 // scale). SR: for the token pair (i, i + 8) the even lane draws block i and the
 // odd lane block i + 8, and each passes the other the two Philox words it needs
 // (elements 0..7 of a block use words 0 and 1, elements 8..15 words 2 and 3).
-template <bool SR>
-__device__ __forceinline__ void encode_rows(const Tile<8>& r, uint32_t col, bool ok, int row_first, int left,
+template <bool SR, int DT>
+__device__ __forceinline__ void encode_rows(const Tile<8, DT>& r, uint32_t col, bool ok, int row_first, int left,
                                             const float* tab, float enc, uint32_t cols,
                                             uint8_t* __restrict__ rcodes, int64_t rldc,
                                             uint8_t* __restrict__ rscales, int64_t rlds, uint64_t seed,
@@ -521,7 +572,14 @@ __device__ __forceinline__ void encode_rows(const Tile<8>& r, uint32_t col, bool
     for (int h = 0; h < 2; ++h) {
       const int t = i + 8 * h;
       float v[8];
-      widen8(make_uint4(r[t][0], r[t][1], r[t][2], r[t][3]), v);
+      if constexpr (DT == kInFP32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(r[t][e]);
+      } else if constexpr (DT == kInFP16) {
+        widen8_h(make_uint4(r[t][0], r[t][1], r[t][2], r[t][3]), v);
+      } else {
+        widen8(make_uint4(r[t][0], r[t][1], r[t][2], r[t][3]), v);
+      }
       float m = max8_abs(v);
       m = fmaxf(m, swap_pair(m));
       const uint32_t sc = block_scale(m, enc);
@@ -542,8 +600,8 @@ __device__ __forceinline__ void encode_rows(const Tile<8>& r, uint32_t col, bool
 // Encode kernel. COL: the columnwise plane (transform if RHT), staged and
 // written as described above. ROW: the rowwise plane (CPL 8: a lane pair
 // holds one 16-column block of each of its 16 token rows).
-template <int CPL, bool RHT, bool SR, bool FAST, bool COL, bool ROW>
-__global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(const uint16_t* __restrict__ x, const GroupArgs a,
+template <int CPL, bool RHT, bool SR, bool FAST, bool COL, bool ROW, int DT>
+__global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(const void* __restrict__ x, const GroupArgs a,
                                                                  const Workspace* ws, int64_t cap, uint32_t nbg,
                                                                  uint32_t ntc, uint32_t npairs, uint32_t chunk) {
   static_assert(!ROW || CPL == 8, "the rowwise encode pairs lanes of 8 columns");
@@ -575,8 +633,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(const uint16_t*
   const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
   if (pair < npairs) {  // wave-uniform; every wave reaches the barrier below
     const Item it = item_of<CPL>(ctile, pair, q, a.groups, mpad, cols);
-    Tile<CPL> r;
-    load_item<CPL>(x, a.ld_x, (int)rows, it, true, r);
+    Tile<CPL, DT> r;
+    load_item<CPL, DT>(x, a.ld_x, (int)rows, it, true, r);
     if constexpr (ROW) {
       const float* gr = a.ramax_in ? a.ramax_in : ws->partial + kGroupAmaxRow;
       const GScale s0 = global_scale(gr[it.b0.g]), s1 = global_scale(gr[it.b1.g]);
@@ -588,14 +646,14 @@ __global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(const uint16_t*
       const int t0 = (int)(it.tb * 16u) - (half ? it.b1.start : it.b0.start);
       const int row_first = (half ? it.b1.row0 : it.b0.row0) + t0;
       const int left = (half ? it.b1.n : it.b0.n) - t0;  // real tokens of the lane's block
-      encode_rows<SR>(r, it.col, it.ok, row_first, left, rt + half * 128, half ? s1.enc : s0.enc, cols, a.rcodes,
+      encode_rows<SR, DT>(r, it.col, it.ok, row_first, left, rt + half * 128, half ? s1.enc : s0.enc, cols, a.rcodes,
                       a.rldc, a.rscales, a.rlds, a.seed, a.offset);
     }
     if constexpr (COL) {
       GroupTabs gt;
       gt.g0 = -1;
       gt.g1 = -1;
-      encode_item<CPL, RHT, SR, FAST>(it, r, a.mask, a.amax_in ? a.amax_in : ws->partial + kGroupAmax, gt,
+      encode_item<CPL, RHT, SR, FAST, DT>(it, r, a.mask, a.amax_in ? a.amax_in : ws->partial + kGroupAmax, gt,
                                       &rcp_tab[wid][0][0], stage, mpad, a.seed, a.offset);
     }
   }
@@ -636,37 +694,56 @@ Geo geo_of(int64_t cols, uint32_t nb_max) {
 
 // Amax pass and reduce kernel for the planes whose amax is not given (COL,
 // ROW); rowwise partials follow the columnwise ones when both are computed.
-template <int CPLA, bool RHT, bool FAST, bool COL, bool ROW>
+template <int CPLA, bool RHT, bool FAST, bool COL, bool ROW, int DT>
 void launch_amax(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
   const Geo g = geo_of<CPLA>(a.cols, nb_max);
   const uint32_t lim = nb_max * g.ntc, rbase = COL ? lim : 0;
-  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT, FAST, COL, ROW>), g.grid, dim3(kT), 0, s, (const uint16_t*)a.x,
-                     (int)a.rows, (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.ws, g.nq, g.ntc, g.npairs,
-                     nb_max, g.chunk, rbase);
+  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT, FAST, COL, ROW, DT>), g.grid, dim3(kT), 0, s, a.x, (int)a.rows,
+                     (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.ws, g.nq, g.ntc, g.npairs, nb_max,
+                     g.chunk, rbase);
   hipLaunchKernelGGL((k_grouped_reduce<COL, ROW>), dim3(a.groups), dim3(kReduceThreads), 0, s, a.offsets, a.groups,
                      (int)a.rows, a.ws, g.ntc, lim, rbase, a.amax_out, a.scale_out, a.ramax_out, a.rscale_out);
 }
 
-template <int CPLE, bool RHT, bool SR, bool FAST, bool COL, bool ROW>
+template <int CPLE, bool RHT, bool SR, bool FAST, bool COL, bool ROW, int DT>
 void launch_quant(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
   const int64_t cap = COL ? (a.ldc * 2 < a.lds * 16 ? a.ldc * 2 : a.lds * 16) : 0;
   const uint32_t npairs = (nb_max + 1) / 2 < 1 ? 1 : (nb_max + 1) / 2;
   const uint32_t nbg = (npairs + kQuantWaves - 1) / kQuantWaves;  // items per column tile
   const uint32_t ntc = tiles_of<CPLE>(a.cols);
   const uint32_t chunk = xcd_chunk((uint64_t)nbg * ntc);
-  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR, FAST, COL, ROW>), dim3(xcd_grid((uint64_t)nbg * ntc)),
-                     dim3(kQuantThreads), 0, s, (const uint16_t*)a.x, a, a.ws, cap, nbg, ntc, npairs, chunk);
+  hipLaunchKernelGGL((k_grouped_quant<CPLE, RHT, SR, FAST, COL, ROW, DT>), dim3(xcd_grid((uint64_t)nbg * ntc)),
+                     dim3(kQuantThreads), 0, s, a.x, a, a.ws, cap, nbg, ntc, npairs, chunk);
 }
 
-template <bool RHT, bool FAST, bool COL, bool ROW>
+template <bool RHT, bool FAST, bool COL, bool ROW, int DT>
 void launch_planes(const GroupArgs& a, hipStream_t s) {
   const uint32_t nb_max = (uint32_t)grouped_blocks(a.rows, a.groups);
   const bool col_amax = COL && !a.amax_in, row_amax = ROW && !a.ramax_in;
-  if (col_amax && row_amax) launch_amax<kCplAmax, RHT, FAST, true, true>(a, nb_max, s);
-  else if (col_amax) launch_amax<kCplAmax, RHT, FAST, true, false>(a, nb_max, s);
-  else if (row_amax) launch_amax<kCplAmax, false, false, false, true>(a, nb_max, s);
-  if (a.sr) launch_quant<kCplQuant, RHT, true, FAST, COL, ROW>(a, nb_max, s);
-  else launch_quant<kCplQuant, RHT, false, FAST, COL, ROW>(a, nb_max, s);
+  if (col_amax && row_amax) launch_amax<kCplAmax, RHT, FAST, true, true, DT>(a, nb_max, s);
+  else if (col_amax) launch_amax<kCplAmax, RHT, FAST, true, false, DT>(a, nb_max, s);
+  else if (row_amax) launch_amax<kCplAmax, false, false, false, true, DT>(a, nb_max, s);
+  if (a.sr) launch_quant<kCplQuant, RHT, true, FAST, COL, ROW, DT>(a, nb_max, s);
+  else launch_quant<kCplQuant, RHT, false, FAST, COL, ROW, DT>(a, nb_max, s);
+}
+
+// FAST (no round-through of the transform's output) exists only with the
+// transform and a columnwise plane; the rowwise plane alone has no transform.
+// fp32 input has no round-through either: it always takes the FAST kernels.
+template <int DT>
+void launch_grouped_t(const GroupArgs& a, hipStream_t s) {
+  const bool fast = a.fast || DT == kInFP32;
+  if (a.col && a.row) {
+    if (a.rht && fast) launch_planes<true, true, true, true, DT>(a, s);
+    else if (a.rht) launch_planes<true, false, true, true, DT>(a, s);
+    else launch_planes<false, false, true, true, DT>(a, s);
+  } else if (a.col) {
+    if (a.rht && fast) launch_planes<true, true, true, false, DT>(a, s);
+    else if (a.rht) launch_planes<true, false, true, false, DT>(a, s);
+    else launch_planes<false, false, true, false, DT>(a, s);
+  } else {
+    launch_planes<false, false, false, true, DT>(a, s);
+  }
 }
 
 }  // namespace
@@ -678,20 +755,10 @@ int64_t grouped_partials(int64_t rows, int64_t cols, int groups, int planes) {
   return planes * grouped_blocks(rows, groups) * tiles_of<kCplAmax>(cols) + 128;
 }
 
-// FAST (no bf16 round-through of the transform's output) exists only with the
-// transform and a columnwise plane; the rowwise plane alone has no transform.
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {
-  if (a.col && a.row) {
-    if (a.rht && a.fast) launch_planes<true, true, true, true>(a, s);
-    else if (a.rht) launch_planes<true, false, true, true>(a, s);
-    else launch_planes<false, false, true, true>(a, s);
-  } else if (a.col) {
-    if (a.rht && a.fast) launch_planes<true, true, true, false>(a, s);
-    else if (a.rht) launch_planes<true, false, true, false>(a, s);
-    else launch_planes<false, false, true, false>(a, s);
-  } else {
-    launch_planes<false, false, false, true>(a, s);
-  }
+  if (a.dtype == kInFP16) launch_grouped_t<kInFP16>(a, s);
+  else if (a.dtype == kInFP32) launch_grouped_t<kInFP32>(a, s);
+  else launch_grouped_t<kInBF16>(a, s);
   return hipGetLastError();
 }
 

@@ -66,13 +66,15 @@ struct TwoDArgs {
   uint32_t offset;
 };
 
-// Largest row stride (elements) of the grouped path's input: its loads reach
-// 32 rows past a base row with 32-bit byte offsets.
+// Largest row stride of the grouped path's input in 2-byte elements (2^25
+// bytes; fp32 rows: half as many elements): its loads reach 32 rows past a
+// base row with 32-bit byte offsets.
 constexpr int64_t kGroupedMaxLd = (int64_t)1 << 24;
 
 // Arguments of the grouped path (columnwise and/or rowwise planes).
 struct GroupArgs {
   const void* x;
+  int dtype;  // element type of x (nvfp4q_dtype)
   int64_t rows, cols, ld_x;
   const int32_t* offsets;
   int32_t groups;

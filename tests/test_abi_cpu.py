@@ -132,8 +132,9 @@ def test_dtype_acceptance_per_entry_point(lib):
                                   ctypes.byref(p), 0, ctypes.byref(r), FAKE, 1 << 16, None) == 6   # fp16/fp32 taken
         assert lib.nvfp4q_quantize_2d(FAKE, dt, 32, 32, 32, ctypes.byref(g), ctypes.byref(p), None, 0,
                                       ctypes.byref(r), FAKE, 1 << 16, None) == 6    # fp16/fp32 taken
-        assert lib.nvfp4q_grouped(FAKE, dt, 32, 32, 32, FAKE, 1, None, 1, 0, ctypes.byref(g), ctypes.byref(p),
-                                  None, None, 0, ctypes.byref(r), FAKE, 1 << 16, None) == 4
+        pg = q.Plane(FAKE, 32, FAKE, 4)
+        assert lib.nvfp4q_grouped(FAKE, dt, 32, 32, 32, FAKE, 1, None, 1, 0, ctypes.byref(g), ctypes.byref(pg),
+                                  None, None, 0, ctypes.byref(r), FAKE, 1 << 16, None) == 6    # fp16/fp32 taken
     assert lib.rmsnorm_nvfp4q(FAKE, 3, 4, 32, 32, FAKE, None, 0.0, 1e-6, None, 0, ctypes.byref(g),
                               ctypes.byref(p), 0, ctypes.byref(r), FAKE, 1 << 16, None) == 4
     # fp32 y rows must stay 16-byte aligned: ld_y 34 floats = 136 bytes

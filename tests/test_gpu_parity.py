@@ -687,9 +687,9 @@ def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offs
     rscales = torch.full((T, C // 16 + 3), 0x55, dtype=torch.uint8, device="cuda")
     a = None if amax is None else torch.tensor(amax, dtype=torch.float32, device="cuda")
     ra = None if row_amax is None else torch.tensor(row_amax, dtype=torch.float32, device="cuda")
-    xd = to_dev(x)
+    xd = to_dev(x) if x.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(x)).cuda()
     if pad:  # rows of x further apart than cols (a view into a wider buffer)
-        wide = torch.full((x.shape[0], x.shape[1] + pad), 3.0, dtype=torch.bfloat16, device="cuda")
+        wide = torch.full((x.shape[0], x.shape[1] + pad), 3.0, dtype=xd.dtype, device="cuda")
         wide[:, :x.shape[1]] = xd
         xd = wide[:, :x.shape[1]]
     got = gpu_lib.nvfp4q_grouped(xd, torch.tensor(offsets, dtype=torch.int32, device="cuda"),
@@ -840,3 +840,26 @@ def test_grouped_padded_rows_both_planes(gpu_lib, rounding):
     rng = np.random.default_rng(39)
     x = _bf16(rng, (150, 272))
     _grouped_check(gpu_lib, x, [0, 3, 3, 70, 150], True, 0x1E3C, rounding, rowwise=True, pad=40)
+
+
+@pytest.mark.parametrize("dtype", ["float16", "float32"])
+@pytest.mark.parametrize("apply_rht,rounding,fast", [(True, "sr", False), (True, "rtne", False), (False, "sr", False),
+                                                      (True, "sr", True)])
+def test_grouped_fp16_fp32_inputs(gpu_lib, dtype, apply_rht, rounding, fast):
+    # reading R-dtype on the grouped path: the transform's output rounded through fp16, or not at all for
+    # fp32; both planes, ragged and empty groups, padded rows
+    rng = np.random.default_rng(44)
+    x = (rng.standard_normal((203, 272)) * np.exp(rng.uniform(-2, 2, (203, 1)))).astype(getattr(np, dtype))
+    _grouped_check(gpu_lib, x, [0, 0, 5, 21, 21, 150, 203], apply_rht, 0x9C35, rounding, rowwise=True,
+                   fast_math=fast, pad=24)
+
+
+def test_grouped_fp16_small_and_large_groups(gpu_lib):
+    # fp16 groups near the ends of its range (no fold of the 0.25 through an fp16 round-through): the
+    # transform's outputs of the small group are fp16 subnormals
+    rng = np.random.default_rng(45)
+    parts = [(rng.standard_normal((40, 96)) * 2e-5).astype(np.float16),
+             (rng.standard_normal((37, 96)) * 1e4).astype(np.float16),
+             rng.standard_normal((19, 96)).astype(np.float16)]
+    x = np.concatenate(parts)
+    _grouped_check(gpu_lib, x, [0, 40, 77, 96], True, 0x6A5C, "sr", rowwise=True)
