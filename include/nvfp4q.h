@@ -76,7 +76,8 @@ extern "C" {
 typedef enum {
   NVFP4Q_OK = 0,
   NVFP4Q_E_NULLPTR = 1,     /* a required pointer is NULL */
-  NVFP4Q_E_SHAPE = 2,       /* a size or leading dimension breaks the shape rules */
+  NVFP4Q_E_SHAPE = 2,       /* a size or leading dimension breaks the shape rules
+                               (every leading dimension is at most 2^40) */
   NVFP4Q_E_ALIGN = 3,       /* a pointer or leading dimension breaks the alignment rules */
   NVFP4Q_E_UNSUPPORTED = 4, /* dtype, rounding mode or option not built */
   NVFP4Q_E_LAUNCH = 5,      /* a kernel launch failed on the HIP side */

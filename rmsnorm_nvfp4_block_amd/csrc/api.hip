@@ -15,6 +15,10 @@ namespace {
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Largest leading dimension accepted (elements or bytes): far beyond any
+// device allocation, and small enough that row * ld never overflows int64.
+constexpr int64_t kMaxLd = int64_t(1) << 40;
+
 nvfp4q_status check_ws(void* ws, size_t bytes) {
   if (!ws || bytes < sizeof(Workspace) || !aligned(ws, 256)) return NVFP4Q_E_WORKSPACE;
   return NVFP4Q_OK;
@@ -29,7 +33,7 @@ int dtype_size(nvfp4q_dtype dt) {
 nvfp4q_status check_input(const void* x, nvfp4q_dtype dt, int64_t rows, int64_t cols, int64_t ld,
                           bool any_dtype = false) {
   if (any_dtype ? dtype_size(dt) == 0 : dt != NVFP4Q_BF16) return NVFP4Q_E_UNSUPPORTED;
-  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld < cols) return NVFP4Q_E_SHAPE;
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld < cols || ld > kMaxLd) return NVFP4Q_E_SHAPE;
   if (rows > 0x7FFFFFFF || cols > 0x7FFFFFFF) return NVFP4Q_E_SHAPE;
   if (rows > 0 && !x) return NVFP4Q_E_NULLPTR;
   if (!aligned(x, 16) || (ld * dtype_size(dt)) % 16 != 0) return NVFP4Q_E_ALIGN;
@@ -42,6 +46,7 @@ nvfp4q_status check_plane(const nvfp4q_plane* p, int64_t prows, int64_t pcols) {
   if (prows == 0 || pcols == 0) return NVFP4Q_OK;  // nothing is written
   if (!p->codes || !p->scales) return NVFP4Q_E_NULLPTR;
   if (p->ld_codes < pcols / 2 || p->ld_scales < pcols / 16) return NVFP4Q_E_SHAPE;
+  if (p->ld_codes > kMaxLd || p->ld_scales > kMaxLd) return NVFP4Q_E_SHAPE;
   if (!aligned(p->codes, 16) || p->ld_codes % 8 != 0) return NVFP4Q_E_ALIGN;
   return NVFP4Q_OK;
 }
@@ -150,7 +155,7 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   if (!codes && !y_out) return NVFP4Q_E_NULLPTR;
   if (codes) TRY(check_plane(row, tokens, hidden));
   if (y_out) {
-    if (ld_y < hidden) return NVFP4Q_E_SHAPE;
+    if (ld_y < hidden || ld_y > kMaxLd) return NVFP4Q_E_SHAPE;
     if (!aligned(y_out, 16) || (ld_y * dtype_size(dtype)) % 16 != 0) return NVFP4Q_E_ALIGN;
   }
   TRY(check_rounding(rounding, rng));
@@ -263,6 +268,7 @@ nvfp4q_status nvfp4q_qk_norm(void* q, void* k, nvfp4q_dtype dtype, int64_t token
   if (tokens > 0x7FFFFFFF || (int64_t)q_heads + k_heads > 65536) return NVFP4Q_E_SHAPE;
   if (q_heads > 0 && ld_q < (int64_t)q_heads * head_dim) return NVFP4Q_E_SHAPE;
   if (k_heads > 0 && ld_k < (int64_t)k_heads * head_dim) return NVFP4Q_E_SHAPE;
+  if (ld_q > kMaxLd || ld_k > kMaxLd) return NVFP4Q_E_SHAPE;
   if (weight_offset != 0.0f && weight_offset != 1.0f) return NVFP4Q_E_UNSUPPORTED;
   if (!(eps >= 0.0f)) return NVFP4Q_E_SHAPE;
   if (tokens > 0 && q_heads > 0 && (!q || !q_weight)) return NVFP4Q_E_NULLPTR;

@@ -78,6 +78,9 @@ def _quant(lib, x=FAKE, dtype=0, rows=4, cols=32, ld=32, codes=FAKE, ldc=16, sca
     (dict(dtype=1, ld=36), 3),           # 72-byte fp16 rows do not
     (dict(cols=24, ld=24), 2),           # cols % 16
     (dict(ld=16), 2),                    # ld < cols
+    (dict(ld=1 << 41), 2),               # leading dimensions stop at 2^40
+    (dict(ldc=1 << 41), 2),
+    (dict(lds=1 << 41), 2),
     (dict(rows=-1), 2),
     (dict(x=0), 1),                      # NULL input
     (dict(x=FAKE + 2), 3),               # misaligned input
@@ -116,6 +119,7 @@ def test_rmsnorm_validation(lib):
     assert call(p=q.Plane(None, 0, None, 0)) == 1                               # nothing to produce
     assert call(p=q.Plane(None, 0, None, 0), y=FAKE, ldy=16) == 2
     assert call(p=q.Plane(None, 0, None, 0), y=FAKE + 2, ldy=32) == 3
+    assert call(p=q.Plane(None, 0, None, 0), y=FAKE, ldy=1 << 41) == 2
     assert call(ws=None) == 6
 
 
@@ -178,6 +182,7 @@ def test_qk_norm_validation(lib):
     assert call(ldq=504) == 2 and call(ldk=248) == 2
     assert call(q=None) == 1 and call(wk=None) == 1
     assert call(q=FAKE + 8) == 3 and call(ldq=516) == 3
+    assert call(ldq=1 << 41) == 2 and call(ldk=1 << 41) == 2
     assert call(woff=0.5) == 4 and call(eps=-1.0) == 2
     assert call(t=0, q=None, k=None, wq=None, wk=None) == 0      # nothing to do, nothing launched
     assert call(hk=0, t=0, k=None, wk=None) == 0
