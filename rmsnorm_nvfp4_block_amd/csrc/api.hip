@@ -175,9 +175,7 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   // With the amax pass and a row count that fits the workspace's row-scale
   // slots, the encode pass streams rows using the 1/rms the amax pass stored.
-  // (bf16 only: fp16 / fp32 inputs run the cooperative-row passes)
-  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled() &&
-                        dtype == NVFP4Q_BF16;
+  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled();
   if (streamed) a.rs = reinterpret_cast<float*>(static_cast<char*>(workspace) + offsetof(Workspace, partial)) + kRowPartials;
   if (codes && !a.amax_in) {
     const hipError_t e = (streamed && !beta) ? launch_rms_stream_amax(a, s, &a.nparts)

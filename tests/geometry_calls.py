@@ -40,32 +40,51 @@ def run_all(q):
     def host(t):
         return t.cpu().numpy() if t is not None else None
 
+    def plane(t, width):
+        # plane rows are padded to a multiple of 16 bytes; the padding is never written
+        return host(t)[:, :width]
+
     out = {}
     rng = np.random.default_rng(31)
     x = _bf16(rng, (1536, 2048))
     g = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(2048)).astype(np.float32))
     r = q.rmsnorm_nvfp4q(dev(x), dev(g), eps=1e-6, y_out=True)
-    for k in ("codes", "scales", "amax", "scale", "y"):
-        out["rms_" + k] = host(r[k]).view(np.uint8) if k != "y" else host(r[k].view(torch.int16))
+    out["rms_codes"], out["rms_scales"] = plane(r["codes"], 1024), plane(r["scales"], 128)
+    for k in ("amax", "scale"):
+        out["rms_" + k] = host(r[k]).view(np.uint8)
+    out["rms_y"] = host(r["y"].view(torch.int16))
     x = _bf16(rng, (300, 1024), 2.0)
     g = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(1024)).astype(np.float32))
     b = workloads.to_bf16_bits((0.01 * rng.standard_normal(1024)).astype(np.float32))
     r = q.rmsnorm_nvfp4q(dev(x), dev(g), dev(b), eps=1e-6, rounding="sr", seed=9, offset=4)
-    for k in ("codes", "scales", "amax", "scale"):
+    out["rmsb_codes"], out["rmsb_scales"] = plane(r["codes"], 512), plane(r["scales"], 64)
+    for k in ("amax", "scale"):
         out["rmsb_" + k] = host(r[k]).view(np.uint8)
     x = _bf16(rng, (700, 4096))
     g = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(4096)).astype(np.float32))
     r = q.rmsnorm_nvfp4q(dev(x), dev(g), eps=1e-6, amax=torch.tensor([5.5], device="cuda"))
-    for k in ("codes", "scales"):
-        out["rmsa_" + k] = host(r[k]).view(np.uint8)
+    out["rmsa_codes"], out["rmsa_scales"] = plane(r["codes"], 2048), plane(r["scales"], 256)
+    for dt in ("float16", "float32"):
+        tdt = getattr(torch, dt)
+        x = torch.from_numpy((rng.standard_normal((520, 1040)) * 2).astype(np.float32)).to(tdt).cuda()
+        g = torch.from_numpy((1 + 0.1 * rng.standard_normal(1040)).astype(np.float32)).to(tdt).cuda()
+        b = torch.from_numpy((0.01 * rng.standard_normal(1040)).astype(np.float32)).to(tdt).cuda()
+        for bias in (False, True):
+            r = q.rmsnorm_nvfp4q(x, g, b if bias else None, eps=1e-6, y_out=True, rounding="sr", seed=2, offset=6)
+            key = f"rms_{dt}_{int(bias)}_"
+            out[key + "codes"], out[key + "scales"] = plane(r["codes"], 520), plane(r["scales"], 65)
+            for k in ("amax", "scale"):
+                out[key + k] = host(r[k]).view(np.uint8)
+            out[key + "y"] = host(r["y"]).view(np.uint8)
     x = _bf16(rng, (777, 1536), 3.0)
     r = q.nvfp4q_quantize(dev(x), rounding="sr", seed=3, offset=1)
-    for k in ("codes", "scales", "amax"):
-        out["q_" + k] = host(r[k]).view(np.uint8)
+    out["q_codes"], out["q_scales"] = plane(r["codes"], 768), plane(r["scales"], 96)
+    out["q_amax"] = host(r["amax"]).view(np.uint8)
     x = _bf16(rng, (640, 384))
     r = q.nvfp4q_quantize_2d(dev(x), rounding="sr", seed=5, offset=2)
-    for k in ("row_codes", "row_scales", "col_codes", "col_scales", "amax"):
-        out["2d_" + k] = host(r[k]).view(np.uint8)
+    out["2d_row_codes"], out["2d_row_scales"] = plane(r["row_codes"], 192), plane(r["row_scales"], 24)
+    out["2d_col_codes"], out["2d_col_scales"] = plane(r["col_codes"], 320), plane(r["col_scales"], 40)
+    out["2d_amax"] = host(r["amax"]).view(np.uint8)
     counts = rng.multinomial(1000, np.full(8, 1 / 8))
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     x = _bf16(rng, (1000, 512))
@@ -78,16 +97,17 @@ def run_all(q):
         out["g_" + k] = host(r[k]).view(np.uint8)
     r = q.nvfp4q_grouped(dev(x), torch.tensor(offsets, device="cuda"), apply_rht=True, rht_mask=0x3C5A,
                          rounding="sr", seed=7, offset=3, rowwise=True)
-    for k in ("row_codes", "row_scales", "row_amax"):
-        out["gr_" + k] = host(r[k]).view(np.uint8)
+    out["gr_row_codes"], out["gr_row_scales"] = plane(r["row_codes"], 256), plane(r["row_scales"], 32)
+    out["gr_row_amax"] = host(r["row_amax"]).view(np.uint8)
     x = _bf16(rng, (3 * 160, 272))
     r = q.nvfp4q_quantize_2d_grouped(dev(x), 3, rounding="sr", seed=6, offset=1, tile16=True)
-    for k in ("row_codes", "row_scales", "col_codes", "col_scales", "amax"):
-        out["e_" + k] = host(r[k]).view(np.uint8)
+    out["e_row_codes"], out["e_row_scales"] = plane(r["row_codes"], 136), plane(r["row_scales"], 17)
+    out["e_col_codes"], out["e_col_scales"] = plane(r["col_codes"], 80), plane(r["col_scales"], 10)
+    out["e_amax"] = host(r["amax"]).view(np.uint8)
     xf = (rng.standard_normal((513, 1040)) * 4).astype(np.float32)
     r = q.nvfp4q_quantize(torch.from_numpy(xf).cuda(), rounding="sr", seed=8)
-    for k in ("codes", "scales", "amax"):
-        out["qf_" + k] = host(r[k]).view(np.uint8)
+    out["qf_codes"], out["qf_scales"] = plane(r["codes"], 520), plane(r["scales"], 65)
+    out["qf_amax"] = host(r["amax"]).view(np.uint8)
     return out
 
 
