@@ -99,8 +99,9 @@ __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32
         uint32_t sc;
         const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)row * nbr + (col >> 4), a.seed, a.offset, 0);
         if (ok) {
-          *reinterpret_cast<uint2*>(a.codes + (int64_t)row * a.ldc + (col >> 1)) = w;
-          a.scales[(int64_t)row * a.lds + (col >> 4)] = (uint8_t)sc;
+          __builtin_nontemporal_store((uint64_t)w.x | ((uint64_t)w.y << 32),
+                                      reinterpret_cast<uint64_t*>(a.codes + (int64_t)row * a.ldc + (col >> 1)));
+          __builtin_nontemporal_store((uint8_t)sc, a.scales + (int64_t)row * a.lds + (col >> 4));
         }
       }
     }
