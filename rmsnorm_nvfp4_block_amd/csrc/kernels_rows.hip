@@ -100,8 +100,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const RowArgs a) {
         uint32_t sc;
         const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)r * nbr + (col >> 4), a.seed, a.offset, 0);
         if ((s0 + u) < nsc && col < cols) {
-          *reinterpret_cast<uint2*>(cr + (col >> 1)) = w;
-          sr[col >> 4] = (uint8_t)sc;
+          __builtin_nontemporal_store((uint64_t)w.x | ((uint64_t)w.y << 32), reinterpret_cast<uint64_t*>(cr + (col >> 1)));
+          __builtin_nontemporal_store((uint8_t)sc, sr + (col >> 4));
         }
       }
     }
