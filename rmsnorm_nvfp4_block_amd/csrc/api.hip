@@ -72,7 +72,7 @@ nvfp4q_status done(hipError_t e) { return e == hipSuccess ? NVFP4Q_OK : NVFP4Q_E
 
 const nvfp4q_global kNoGlobal = {nullptr, nullptr, nullptr};
 
-// NVFP4Q_RMS_STREAM=0 selects the full-row RMSNorm encode pass everywhere
+// NVFP4Q_RMS_STREAM=0 selects the cooperative-row RMSNorm encode pass everywhere
 // (for comparison; both give identical results).
 bool rms_stream_enabled() {
   static const bool on = [] {

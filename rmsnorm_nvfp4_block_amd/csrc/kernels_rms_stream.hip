@@ -1,8 +1,9 @@
 // Streaming form of the two RMSNorm + rowwise NVFP4 passes.
 //
-// The full-row kernels hold a whole token row in registers because 1/rms is
-// known only after the row's sum of squares. Here the amax pass writes each
-// row's 1/rms into the workspace, so neither pass needs a whole row at once:
+// A row's 1/rms is known only after its whole sum of squares; the
+// cooperative-row kernels (kernels_rms_coop.hip) meet that with a workgroup
+// barrier per row. Here the amax pass writes each row's 1/rms into the
+// workspace, so the encode pass reads it back and no pass waits on a row:
 // a wave walks its rows one 1024-column superchunk at a time (lane l: the
 // 16-element block at columns 16l..16l+15) with kDepth superchunks in flight,
 // and compute overlaps the loads of the superchunks behind it.
@@ -13,10 +14,11 @@
 //    RN(max * r) joins the wave's maximum. Since y = RN(RN(x * g) * r) is
 //    monotone in |RN(x * g)| for the row's fixed r > 0, that is the row's
 //    max |y|. With a bias the max depends on r element by element; that case
-//    keeps the full-row amax pass (which also stores r).
-//  * Encode pass: y = RN(RN(x * g) * r) [+ beta, fused], rounded to bf16, then
-//    the block encode, as in the full-row pass; codes leave with non-temporal
-//    stores (they are not read again by this call). Lane k of a wave holds r
+//    keeps the cooperative-row amax pass (which also stores r).
+//  * Encode pass: y = RN(RN(x * g) * r) [+ beta, fused], rounded to the
+//    input's type, then the block encode, as in the cooperative-row pass;
+//    codes and scale bytes leave with non-temporal stores (they are not read
+//    again by this call). Lane k of a wave holds r
 //    of the wave's k-th row (a wave has at most 64 rows; the launcher sizes
 //    the grid for it).
 //

@@ -12,29 +12,6 @@ namespace nvfp4q {
 constexpr int kThreads = kWGThreads;
 constexpr uint32_t kSuper = 1024;  // columns per superchunk (64 lanes x 16)
 
-struct Blk {
-  uint4 lo, hi;  // 16 bf16 values of one block
-};
-
-__device__ __forceinline__ void widen16(const Blk& b, float v[16]) {
-  widen8(b.lo, v);
-  widen8(b.hi, v + 8);
-}
-
-// The lane's block at column `col` of a row (zero when outside the row).
-template <bool FULL>
-__device__ __forceinline__ Blk load_blk(const uint16_t* xr, uint32_t col, uint32_t cols) {
-  Blk b;
-  if (FULL) {
-    b.lo = *reinterpret_cast<const uint4*>(xr + col);
-    b.hi = *reinterpret_cast<const uint4*>(xr + col + 8);
-  } else {
-    b.lo = ld16(xr + col, col < cols);
-    b.hi = ld16(xr + col + 8, col < cols);
-  }
-  return b;
-}
-
 // ------------------------------------------------------------------ input types
 // Element types of x on the paths that take more than bf16 (the values of
 // nvfp4q_dtype): a 16-byte load holds 8 bf16 or fp16 values or 4 fp32 values.
