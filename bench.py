@@ -345,9 +345,21 @@ DOMINANT = {
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+def _code_only(text):
+    """Source text without // comments, trailing blanks and empty lines (a comment edit keeps the digest)."""
+    out = []
+    for line in text.splitlines():
+        i = line.find("//")
+        line = (line if i < 0 else line[:i]).rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
 def source_digest():
-    """sha256 of the device code (kernels_*.hip and the headers they include): traffic figures are valid only
-    for the kernels they were taken on. Host-only files (api.hip, the C header) do not enter."""
+    """sha256 of the device code (kernels_*.hip and the headers they include, comments left out): traffic
+    figures are valid only for the kernels they were taken on. Host-only files (api.hip, the C header) do
+    not enter."""
     import hashlib
 
     h = hashlib.sha256()
@@ -356,8 +368,8 @@ def source_digest():
                    if (f.startswith("kernels_") and f.endswith(".hip")) or f.endswith(".hpp"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
