@@ -18,9 +18,8 @@
 //  * Encode pass: y = RN(RN(x * g) * r) [+ beta, fused], rounded to the
 //    input's type, then the block encode, as in the cooperative-row pass;
 //    codes and scale bytes leave with non-temporal stores (they are not read
-//    again by this call). Lane k of a wave holds r
-//    of the wave's k-th row (a wave has at most 64 rows; the launcher sizes
-//    the grid for it).
+//    again by this call). Lane k of a wave holds r of the wave's k-th row (a
+//    wave has at most 64 rows; the launcher sizes the grid for it).
 //
 // The ring of superchunks is refilled only in iterations that have a next
 // one, and the last iteration issues no loads: a refill that may or may not
