@@ -179,7 +179,7 @@ int64_t coop_wgs() {
 }
 
 // Two rows in flight per workgroup: three or four measured slower on the
-// 4096 x 4096 prefill (11.3 us at two, 11.7-12.5 us deeper).
+// 4096 x 4096 prefill (10.7 us at two, 11.3-11.5 us at three or four).
 constexpr int kCoopDepth = 2;
 
 template <int NPW, bool BIAS, int MODE, bool SR, int T>
