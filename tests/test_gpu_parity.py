@@ -352,7 +352,8 @@ def test_quantize_fp32_given_amax_and_padded_rows(gpu_lib):
 @pytest.mark.parametrize("dtype", ["float16", "float32"])
 @pytest.mark.parametrize("shape,bias,woff,rounding", [((8, 7168), True, 0.0, "rtne"), ((37, 1040), False, 1.0, "sr"),
                                                       ((300, 4096), True, 1.0, "sr"), ((5, 16384), False, 0.0, "rtne"),
-                                                      ((2304, 1040), False, 0.0, "rtne"), ((2080, 2048), True, 1.0, "sr")])
+                                                      ((2304, 1040), False, 0.0, "rtne"), ((2080, 2048), True, 1.0, "sr"),
+                                                      ((2048, 2048), False, 0.0, "sr")])
 def test_rmsnorm_fp16_fp32_inputs(gpu_lib, dtype, shape, bias, woff, rounding):
     # reading R-dtype: gamma, beta and y in the input's type; y within the arithmetic tolerance of the
     # float64 value, codes the exact quantization of the GPU's own y, and almost all codes equal to the
