@@ -55,13 +55,14 @@
  *     access.
  *   - Shapes: elements per row (`cols`, `hidden`) must be a multiple of 16;
  *     a columnwise plane needs rows % 16 == 0 (except grouped mode, which pads
- *     each group). Leading dimensions are in elements for bf16 tensors and in
- *     bytes for code and scale planes. Input and bf16 output pointers must be
- *     16-byte aligned with ld a multiple of 8 elements; code planes 16-byte
+ *     each group). Leading dimensions are in elements for input and output
+ *     tensors (x, y, q, k) and in bytes for code and scale planes. Input and
+ *     output tensors start 16-byte aligned and their rows stay so (leading
+ *     dimension times element size a multiple of 16); code planes are 16-byte
  *     aligned with ld_codes a multiple of 8 bytes. Scale planes have no
  *     alignment rule.
- *   - Only bfloat16 input is built (NVFP4Q_BF16); anything else returns
- *     NVFP4Q_E_UNSUPPORTED.
+ *   - Element types: every entry point takes bfloat16, float16 and float32
+ *     input (nvfp4q_dtype); any other value returns NVFP4Q_E_UNSUPPORTED.
  */
 #ifndef NVFP4Q_H
 #define NVFP4Q_H
@@ -162,17 +163,27 @@ nvfp4q_status nvfp4q_quantize(const void *x, nvfp4q_dtype dtype, int64_t rows, i
 
 /*
  * rmsnorm_nvfp4q -- per-token RMSNorm feeding rowwise NVFP4.
- *   y = bf16_rne((gamma + weight_offset) * (x * r) [+ beta]),
- *   r = 1 / sqrt(sum_k x_k^2 / hidden + eps), evaluated in fp32;
- *   the quantizer consumes the bf16 y and amax = max |y|.
+ *   y = RN_T((gamma + weight_offset) * (x * r) [+ beta]),
+ *   r = 1 / sqrt(sum_k x_k^2 / hidden + eps),
+ *   T the input's element type (bf16, fp16; for fp32 input y is the fp32
+ *   result); the quantizer consumes that y and amax = max |y|.
+ *   fp32 evaluation: g = RN(gamma + weight_offset) per column, the sum of
+ *   squares ss in fp32, r = v_rsq_f32(RN(RN(ss * RN(1 / hidden)) + eps))
+ *   (within 1 ulp),
+ *   then y = RN_T(RN(RN(x * g) * r)), or with beta
+ *   y = RN_T(fma(RN(x * g), r, beta)) (one rounding for the product and the
+ *   sum). The order of the sum of squares is not fixed: y may differ from the
+ *   exactly rounded value by one step of T where the exact value lies next to
+ *   a rounding boundary.
  *   [Blog, QK Norm: rsqrt of the mean square plus EPS, weight plus a
- *   compile-time WEIGHT_BIAS, cast back to the element type]
- *   x: device [tokens, hidden] bf16, row stride ld_x.
- *   gamma: device [hidden] bf16 (required). beta: device [hidden] bf16 or
- *     NULL (no-bias variant, compiled separately).
+ *   compile-time WEIGHT_BIAS, cast back to the element type; Configuration
+ *   space: the input and output type is a knob]
+ *   x: device [tokens, hidden] of `dtype`, row stride ld_x.
+ *   gamma: device [hidden] of `dtype` (required). beta: device [hidden] of
+ *     `dtype`, or NULL (no-bias variant, compiled separately).
  *   weight_offset: added to gamma (the page's WEIGHT_BIAS); must be 0 or 1.
  *   eps: added to the mean square.
- *   y_out: device [tokens, hidden] bf16 with row stride ld_y, or NULL.
+ *   y_out: device [tokens, hidden] of `dtype` with row stride ld_y, or NULL.
  *   row: the rowwise plane, or row->codes == NULL to produce only y_out.
  *   rounding / rng as for nvfp4q_quantize.
  *   g: as for nvfp4q_quantize; with g->amax_in the call is one pass over x
@@ -188,7 +199,8 @@ nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, 
 
 /*
  * nvfp4q_quantize_2d -- rowwise and columnwise (transposed) planes of one
- * [rows, cols] bf16 tensor under one shared per-tensor scale (weights).
+ * [rows, cols] tensor (bf16, fp16 or fp32) under one shared per-tensor scale
+ * (weights).
  *   row: rowwise plane or row->codes == NULL; col: columnwise plane
  *   [cols][rows/2] codes, [cols][rows/16] scales, or col->codes == NULL
  *   (with rows == 0 a given plane may have NULL pointers).
@@ -256,8 +268,8 @@ nvfp4q_status nvfp4q_qk_norm(void *q, void *k, nvfp4q_dtype dtype, int64_t token
                              void *stream);
 
 /*
- * nvfp4q_grouped -- per-group NVFP4 of a packed [total_rows, cols] bf16
- * tensor: the columnwise plane, optionally after a 16-point random Hadamard
+ * nvfp4q_grouped -- per-group NVFP4 of a packed [total_rows, cols] tensor
+ * (bf16, fp16 or fp32): the columnwise plane, optionally after a 16-point random Hadamard
  * transform along the rows of each 16-row block, and/or the rowwise plane,
  * each with one global scale per group, from one read of x.
  *   offsets: device int32 [num_groups + 1]; offsets[0] = 0, non-decreasing,

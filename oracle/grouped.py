@@ -41,7 +41,7 @@ def padded_offsets(offsets) -> np.ndarray:
 
 def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="sr",
                      seed=0, offset=0, groups=None, fast_math=False, rowwise=False, row_amax=None,
-                     colwise=True):
+                     colwise=True, ends_only=False):
     """Reference for the grouped path: the columnwise plane, optionally the rowwise one.
 
     x: bf16 bits [total_rows, K]. offsets: int32 [G+1]. amax: optional float32 [G].
@@ -55,6 +55,9 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
     index row * (K/16) + k/16 with the row's index in x. Adds row_codes
     [total_rows, K/2], row_scales [total_rows, K/16], row_amax, row_s_dec [G].
     colwise=False skips the columnwise plane (its arrays stay zero).
+    ends_only: quantize only the first and the last 16-token block of each computed
+    group in the columnwise plane (for sampling large inputs; the group amax still
+    covers every block of the group; the other blocks' bytes stay zero).
     x may also hold float16 or float32 values (reading R-dtype): the transform's
     output is then rounded through the input's type (fp16), or not at all (fp32).
     Returns dict with codes [K, Mpad/2], scales [K, Mpad/16], amax [G], s_enc [G],
@@ -98,11 +101,20 @@ def grouped_quantize(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding
         amax_out[g], s_enc_out[g], s_dec_out[g] = a, s_enc, s_dec
         if pg == 0:
             continue
+        nb = pg // 16
+        sel_b = sorted({0, nb - 1}) if ends_only else list(range(nb))   # the blocks quantized
         rb = None
         if rounding == "sr":
             blk = (np.arange(K, dtype=np.uint64)[:, None] * np.uint64(mpad // 16)
-                   + np.uint64(poff[g] // 16) + np.arange(pg // 16, dtype=np.uint64)[None, :])
+                   + np.uint64(poff[g] // 16) + np.asarray(sel_b, dtype=np.uint64)[None, :])
             rb = block_random_bytes(blk, 1, seed, offset)
+        if ends_only:
+            c, sc = quantize_blocks(zf[:, sel_b], s_enc, s_dec, rounding, rb)
+            for j, b in enumerate(sel_b):
+                t0 = int(poff[g]) + 16 * b
+                codes[:, t0 // 2:t0 // 2 + 8] = pack_nibbles(c[:, j].reshape(K, 16))
+                scales[:, t0 // 16] = sc[:, j]
+            continue
         c, sc = quantize_blocks(zf, s_enc, s_dec, rounding, rb)
         codes[:, poff[g] // 2:(poff[g] + pg) // 2] = pack_nibbles(c.reshape(K, pg))
         scales[:, poff[g] // 16:(poff[g] + pg) // 16] = sc

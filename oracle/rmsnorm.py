@@ -63,6 +63,14 @@ def rmsnorm_quantize(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None
     return q
 
 
+def _kind(a):
+    """Element type of an oracle array: bf16 bits (uint16), float16 or float32 values."""
+    a = np.asarray(a)
+    kinds = {np.dtype(np.uint16): "bf16", np.dtype(np.float16): "fp16", np.dtype(np.float32): "fp32"}
+    assert a.dtype in kinds, "bf16 bits (uint16), float16 or float32 expected"
+    return kinds[a.dtype]
+
+
 def qk_norm(q, k, q_weight, k_weight, head_dim, weight_offset=0.0, eps=1e-6):
     """Per-head RMSNorm of the attention heads of q [T, Hq*D] and k [T, Hk*D] (reading R-qk).
 
@@ -70,12 +78,16 @@ def qk_norm(q, k, q_weight, k_weight, head_dim, weight_offset=0.0, eps=1e-6):
     tensor with its own weight vector of head_dim entries, in place, through the
     same formula as above: y = (w + c) * (x * r), r = rsqrt(sum x^2 / D + EPS),
     cast back to the element type. This is rmsnorm_bf16 over rows of head_dim
-    elements. k may be None.
+    elements, rounded once to the input's type (Blog, Configuration space: the
+    I/O type is a knob; reading R-dtype): q, k and the weights are bf16 bits
+    (uint16), float16 or float32 values, all of one type. k may be None.
     """
     def one(x, w):
-        x = np.asarray(x, dtype=np.uint16)
+        x = np.asarray(x)
+        kind = _kind(x)
+        assert _kind(w) == kind, "the weight has the type of its tensor"
         T = x.shape[0]
         assert x.shape[1] % head_dim == 0
-        return rmsnorm_bf16(x.reshape(-1, head_dim), w, None, weight_offset, eps).reshape(T, -1)
+        return rmsnorm_bf16(x.reshape(-1, head_dim), w, None, weight_offset, eps, out_dtype=kind).reshape(T, -1)
 
     return one(q, q_weight), (None if k is None else one(k, k_weight))

@@ -101,14 +101,31 @@ def _check(status: int):
 _ws = {}
 
 
-def workspace(device=None):
-    """Per-device zero-filled workspace, allocated once (torch memory) and reused on every call."""
+def _alloc_workspace(dev):
+    """Device memory for one workspace (torch's allocator; the library needs no initialization of it)."""
     import torch
 
-    dev = torch.device("cuda", torch.cuda.current_device() if device is None else torch.device(device).index or 0)
-    if dev not in _ws:
-        _ws[dev] = torch.zeros(max(nvfp4q_workspace_bytes(), 4096), dtype=torch.uint8, device=dev)
-    return _ws[dev]
+    return torch.empty(max(nvfp4q_workspace_bytes(), 4096), dtype=torch.uint8, device=dev)
+
+
+def workspace(device=None, stream=None):
+    """The workspace for calls enqueued on `stream` (a HIP stream handle; default: torch's current stream
+    on the device): one per (device, stream), allocated on first use and reused by every later call on
+    that stream, which the stream orders. Calls on different streams get different workspaces, so they
+    may run at the same time (the C ABI requires that of concurrent calls)."""
+    import torch
+
+    if device is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    else:
+        dev = torch.device(device)
+        dev = torch.device("cuda", dev.index if dev.index is not None else torch.cuda.current_device())
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    key = (dev.index, int(stream))
+    if key not in _ws:
+        _ws[key] = _alloc_workspace(dev)
+    return _ws[key]
 
 
 def _ptr(t) -> Optional[int]:
@@ -125,13 +142,6 @@ def _rounding(r: str) -> int:
     if r not in ("rtne", "sr"):
         raise ValueError(f"rounding must be 'rtne' or 'sr', not {r!r}")
     return SR if r == "sr" else RTNE
-
-
-def _check_bf16_2d(x):
-    import torch
-
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1 or not x.is_cuda:
-        raise ValueError("x must be a 2-D row-contiguous bfloat16 CUDA tensor")
 
 
 def _dtype_code(x):
@@ -170,7 +180,7 @@ def nvfp4q_quantize(x, amax=None, rounding="rtne", seed=0, offset=0, codes=None,
     c, s, plane = _plane(R, C, x.device, codes, scales)
     amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
     scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
-    ws = workspace(x.device)
+    ws = workspace(x.device, _stream(x))
     st = lib.nvfp4q_quantize(x.data_ptr(), dt, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
                              ctypes.byref(plane), _rounding(rounding), ctypes.byref(Rng(seed, offset)),
                              ws.data_ptr(), ws.numel(), _stream(x))
@@ -200,7 +210,7 @@ def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, 
         c, s, plane = None, None, Plane(None, 0, None, 0)
     amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
     scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
-    ws = workspace(x.device)
+    ws = workspace(x.device, _stream(x))
     st = lib.rmsnorm_nvfp4q(x.data_ptr(), dt, T, H, x.stride(0), gamma.data_ptr(), _ptr(beta),
                             float(weight_offset), float(eps), _ptr(y), y.stride(0) if y is not None else 0,
                             ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(plane),
@@ -230,7 +240,7 @@ def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=
         cc, cs, cp = _plane(C, R, x.device)
     amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
     scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
-    ws = workspace(x.device)
+    ws = workspace(x.device, _stream(x))
     st = lib.nvfp4q_quantize_2d(x.data_ptr(), dt, R, C, x.stride(0), ctypes.byref(_global(amax, amax_out, scale_out)),
                                 ctypes.byref(rp), ctypes.byref(cp),
                                 _rounding(rounding) | (SCALE_16X16 if tile16 else 0),
@@ -266,7 +276,7 @@ def nvfp4q_quantize_2d_grouped(x, experts, amax=None, rounding="rtne", seed=0, o
         cc, cs, cp = _plane(experts * C, R, x.device)
     amax_out = torch.empty(experts, dtype=torch.float32, device=x.device)
     scale_out = torch.empty(experts, dtype=torch.float32, device=x.device)
-    ws = workspace(x.device)
+    ws = workspace(x.device, _stream(x))
     st = lib.nvfp4q_quantize_2d_grouped(x.data_ptr(), dt, experts, R, C, x.stride(0),
                                         ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(rp),
                                         ctypes.byref(cp), _rounding(rounding) | (SCALE_16X16 if tile16 else 0),
@@ -351,7 +361,7 @@ def nvfp4q_grouped(x, offsets, apply_rht=True, rht_mask=0, amax=None, rounding="
         ramax_out = torch.empty(G, dtype=torch.float32, device=x.device)
         rscale_out = torch.empty(G, dtype=torch.float32, device=x.device)
     poff = torch.empty(G + 1, dtype=torch.int32, device=x.device)
-    ws = workspace(x.device)
+    ws = workspace(x.device, _stream(x))
     gcol = _global(amax, amax_out, scale_out) if colwise else None
     grow = _global(row_amax, ramax_out, rscale_out) if rowwise else None
     st = lib.nvfp4q_grouped(x.data_ptr(), dt, T, C, x.stride(0), offsets.data_ptr(), G, poff.data_ptr(),

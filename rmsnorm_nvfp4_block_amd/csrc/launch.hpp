@@ -11,7 +11,7 @@ struct Workspace;
 // Arguments of the rowwise paths (quantize and RMSNorm).
 struct RowArgs {
   const void* x;
-  int dtype;  // element type of x (nvfp4q_dtype; bf16 except on the rowwise quantizer)
+  int dtype;  // element type of x, gamma, beta and y (nvfp4q_dtype)
   int64_t rows, cols, ld_x;
   const void* gamma;
   const void* beta;

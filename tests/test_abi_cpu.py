@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "nvfp4q.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(nvfp4q_\w+|rmsnorm_nvfp4q)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(nvfp4q_\w+|rmsnorm_nvfp4q\w*)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     d = _declared()
     for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped",
-                 "nvfp4q_grouped"):
+                 "nvfp4q_grouped", "nvfp4q_qk_norm"):
         assert name in d
 
 
@@ -42,7 +42,7 @@ def test_binding_names_match_the_abi():
     import rmsnorm_nvfp4_block_amd as q
 
     for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped",
-                 "nvfp4q_grouped"):
+                 "nvfp4q_grouped", "nvfp4q_qk_norm"):
         assert callable(getattr(q, name))
 
 
@@ -273,3 +273,27 @@ def test_rounding_option_bits(lib):
     assert two_d(q.SCALE_16X16 | 0x400) == 4
     assert two_d(q.SCALE_16X16, rows=24, colp=False) == 2   # tiles need rows % 16 == 0
     assert two_d(q.RTNE, rows=24, colp=False) == 6          # 1D rowwise does not
+
+
+def test_binding_keeps_one_workspace_per_stream(monkeypatch):
+    """The Python binding gives calls on different streams different workspaces (calls that may overlap
+    must not share one), and reuses a stream's workspace for every later call on it."""
+    import torch
+
+    import rmsnorm_nvfp4_block_amd as q
+
+    made = []
+
+    def fake_alloc(dev):
+        made.append(dev)
+        return object()
+
+    monkeypatch.setattr(q, "_alloc_workspace", fake_alloc)
+    monkeypatch.setattr(q, "_ws", {})
+    dev = torch.device("cuda", 0)
+    a, b = q.workspace(dev, stream=0x1000), q.workspace(dev, stream=0x2000)
+    assert a is not b
+    assert q.workspace(dev, stream=0x1000) is a and q.workspace(dev, stream=0x2000) is b
+    assert q.workspace(torch.device("cuda", 1), stream=0x1000) is not a   # per device as well
+    assert len(made) == 3
+

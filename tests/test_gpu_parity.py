@@ -5,7 +5,11 @@ amax and S_dec. The fused RMSNorm path follows the rules of its contract: y
 within 1e-2 relative (+2^-20 absolute) of the float64 oracle; the codes equal,
 bit for bit, the oracle's quantization of the GPU's own bf16 y; against the
 float64 oracle at most 1e-4 of the codes differ, each by at most one magnitude
-step. Full-size workloads are checked on sampled rows, columns or groups.
+step, and only in blocks whose rounded y differs. The norms' rounded outputs
+(RMSNorm y in bf16 or fp16, QK norm) are, element by element, the
+round-to-nearest-even of a value within the fp32 arithmetic's error bound of the
+exact one, hence within one step of the oracle's output; fp32 outputs lie within
+that bound. Full-size workloads are checked on sampled rows, columns or groups.
 """
 import numpy as np
 import pytest
@@ -13,7 +17,8 @@ import pytest
 import oracle
 import workloads
 from oracle import formats as F
-from tests.gpu_helpers import (assert_f32_bits, assert_same_bits, code_step_mismatch, f32, np_u8, to_dev,
+from tests.gpu_helpers import (REL_ERR_QK, REL_ERR_RMSNORM, assert_code_diffs_follow_y, assert_f32_bits,
+                               assert_rounded_output, assert_same_bits, code_step_mismatch, f32, np_u8, to_dev,
                                to_np_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -231,6 +236,9 @@ def _check_rms(w, got, rounding="rtne", seed=0, offset=0, amax_given=None):
     yg = F.bf16_to_f32(y_gpu).astype(np.float64)
     err = np.abs(yg - y64)
     assert np.all(err <= 1e-2 * np.abs(y64) + 2.0 ** -20), f"y error max {err.max()}"
+    # y is the bf16 rounding of a value within the fp32 arithmetic's error bound of the exact one
+    b64 = None if w.beta is None else F.bf16_to_f32(w.beta).astype(np.float64)[None, :]
+    assert_rounded_output("y", y_gpu, y_ref, y64, "bf16", REL_ERR_RMSNORM, b64)
     # codes are the exact quantization of the GPU's own y
     amax = amax_given if amax_given is not None else np.float32(np.max(np.abs(yg)))
     q_own = oracle.quantize_rowwise(y_gpu, amax=amax, rounding=rounding, seed=seed, offset=offset)
@@ -240,6 +248,8 @@ def _check_rms(w, got, rounding="rtne", seed=0, offset=0, amax_given=None):
     n, ok = code_step_mismatch(np_u8(got["codes"], cols // 2), q_ref["codes"])
     assert ok, "a code differs by more than one step"
     assert n <= 1e-4 * w.rows * cols, f"{n} codes differ from the float64 oracle"
+    assert_code_diffs_follow_y("codes", np_u8(got["codes"], cols // 2), q_ref["codes"], y_gpu, y_ref, amax,
+                               q_ref["amax"])
     return n
 
 
@@ -373,9 +383,8 @@ def test_rmsnorm_fp16_fp32_inputs(gpu_lib, dtype, shape, bias, woff, rounding):
     y_ref, y64, _ = oracle.rmsnorm_bf16(x, g, b, woff, 1e-6, return_f64=True, out_dtype=od)
     yg = got["y"].cpu().numpy()
     assert yg.dtype == ndt
-    tol = 2.0 ** -9 if dtype == "float16" else 2.0 ** -14
-    err = np.abs(yg.astype(np.float64) - y64)
-    assert np.all(err <= tol * np.abs(y64) + 2.0 ** -24), f"y error max {err.max()}"
+    b64 = None if b is None else b.astype(np.float64)[None, :]
+    assert_rounded_output("y", yg, y_ref, y64, od, REL_ERR_RMSNORM, b64)
     amax = np.float32(np.max(np.abs(yg.astype(np.float32))))
     assert_f32_bits("amax", f32(got["amax"])[0], amax)
     own = oracle.quantize_rowwise(yg, amax=amax, rounding=rounding, seed=11, offset=2)
@@ -383,12 +392,17 @@ def test_rmsnorm_fp16_fp32_inputs(gpu_lib, dtype, shape, bias, woff, rounding):
     assert_same_bits("scales (own y)", np_u8(got["scales"], H // 16), own["scales"])
     ref = oracle.quantize_rowwise(y_ref, rounding=rounding, seed=11, offset=2)
     n, ok = code_step_mismatch(np_u8(got["codes"], H // 2), ref["codes"])
-    assert ok and n <= 1e-3 * T * H, f"{n} codes differ from the float64 oracle"
+    assert ok and n <= 1e-4 * T * H, f"{n} codes differ from the float64 oracle"
+    assert_code_diffs_follow_y("codes", np_u8(got["codes"], H // 2), ref["codes"], yg, y_ref, amax, ref["amax"])
 
 
 @pytest.mark.parametrize("dtype", ["float16", "float32"])
 @pytest.mark.parametrize("head_dim", [64, 256])
-def test_qk_norm_fp16_fp32(gpu_lib, dtype, head_dim):
+@pytest.mark.parametrize("woff", [0.0, 1.0])
+def test_qk_norm_fp16_fp32(gpu_lib, dtype, head_dim, woff):
+    # reading R-dtype: the oracle's QK norm in the input's type; fp16 output within one step of the
+    # oracle's rounding (and a rounding of a value within the fp32 arithmetic's bound), fp32 within that
+    # bound of the exact value
     import torch
 
     w = workloads.qk_heads(seed=head_dim, tokens=33, q_heads=6, k_heads=2, head_dim=head_dim)
@@ -399,28 +413,30 @@ def test_qk_norm_fp16_fp32(gpu_lib, dtype, head_dim):
     qd, kd = torch.from_numpy(qf).to(tdt).cuda(), torch.from_numpy(kf).to(tdt).cuda()
     wq = torch.from_numpy(F.bf16_to_f32(w.gamma)).to(tdt).cuda()
     wk = torch.from_numpy(F.bf16_to_f32(w.meta["k_weight"])).to(tdt).cuda()
-    q_in = qd.double().cpu().numpy()
-    gpu_lib.nvfp4q_qk_norm(qd, kd, wq, wk, head_dim, eps=w.eps)
-    for got, x_in, wv in ((qd, q_in, wq), (kd, kf.astype(np.float64), wk)):
-        x64 = x_in.reshape(-1, head_dim)
-        r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=-1, keepdims=True) + float(np.float32(w.eps)))
-        y64 = wv.double().cpu().numpy()[None, :] * (x64 * r)
-        yg = got.double().cpu().numpy().reshape(-1, head_dim)
-        # fp16: the output rounding (half an ulp, 2^-11) plus the fp32 arithmetic; fp32: the arithmetic
-        # alone (a sum of at most 256 squares, v_rsq_f32 within 1 ulp, two products)
-        tol = 2.0 ** -9 if dtype == "float16" else 2.0 ** -14
-        assert np.all(np.abs(yg - y64) <= tol * np.abs(y64) + 2.0 ** -24), np.max(np.abs(yg - y64))
+    q_in, k_in = qd.cpu().numpy(), kd.cpu().numpy()          # exactly the values the kernel reads
+    wq_in, wk_in = wq.cpu().numpy(), wk.cpu().numpy()
+    gpu_lib.nvfp4q_qk_norm(qd, kd, wq, wk, head_dim, weight_offset=woff, eps=w.eps)
+    yq_ref, yk_ref = oracle.qk_norm(q_in, k_in, wq_in, wk_in, head_dim, weight_offset=woff, eps=w.eps)
+    od = "fp16" if dtype == "float16" else "fp32"
+    for name, got, ref, x_in, wv in (("q", qd, yq_ref, q_in, wq_in), ("k", kd, yk_ref, k_in, wk_in)):
+        _, y64, _ = oracle.rmsnorm_bf16(x_in.reshape(-1, head_dim), wv, None, woff, w.eps, return_f64=True,
+                                        out_dtype=od)
+        yg = got.cpu().numpy().reshape(-1, head_dim)
+        assert_rounded_output(name, yg, ref.reshape(-1, head_dim), y64, od, REL_ERR_QK)
 
 
 # ---------------------------------------------------------------- QK norm (reading R-qk)
 def _check_qk(y_gpu, x, w, head_dim, woff, eps):
-    T = x.shape[0]
+    """bf16 QK norm: within 1e-2 of the exact value, and the bf16 rounding of a value within the fp32
+    arithmetic's error bound, so within one bf16 step of the oracle's output."""
     _, y64, _ = oracle.rmsnorm_bf16(x.reshape(-1, head_dim), w, None, woff, eps, return_f64=True)
     yg = F.bf16_to_f32(y_gpu).astype(np.float64).reshape(-1, head_dim)
     err = np.abs(yg - y64)
     assert np.all(err <= 1e-2 * np.abs(y64) + 2.0 ** -20), f"QK norm error max {err.max()}"
     ref, _ = oracle.qk_norm(x, None, w, None, head_dim, woff, eps)
-    assert ref.shape == (T, x.shape[1])
+    assert ref.shape == x.shape
+    assert_rounded_output("qk", np.asarray(y_gpu).reshape(-1, head_dim), ref.reshape(-1, head_dim), y64, "bf16",
+                          REL_ERR_QK)
 
 
 @pytest.mark.parametrize("head_dim", [64, 128, 256])
@@ -496,8 +512,12 @@ def test_2d_weight_8192x8192_sampled(gpu_lib):
     amax = np.float32(np.max(np.abs(F.bf16_to_f32(w.x))))
     assert_f32_bits("amax", f32(got["amax"])[0], amax)
     rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 8191], rng.choice(8192, 40, replace=False)]))
-    cols = np.unique(np.concatenate([[0, 1, 127, 128, 8191], rng.choice(8192, 40, replace=False)]))
+    # one row and one column in every 128-row and 128-column band of the tile grid, both edges of the
+    # first band and of the tensor, and some more at random
+    bands = np.arange(0, 8192, 128) + rng.integers(0, 128, 64)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 8191], bands, rng.choice(8192, 24, replace=False)]))
+    bands = np.arange(0, 8192, 128) + rng.integers(0, 128, 64)
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, 8191], bands, rng.choice(8192, 24, replace=False)]))
     qr = oracle.quantize_rowwise(w.x[rows], amax=amax, rounding="sr", seed=w.seed, offset=w.offset, row_ids=rows)
     qc = oracle.quantize_colwise(w.x[:, cols], amax=amax, rounding="sr", seed=w.seed, offset=w.offset, col_ids=cols)
     assert_same_bits("row codes", np_u8(got["row_codes"], 4096)[rows], qr["codes"])
@@ -795,6 +815,31 @@ def test_grouped_moe_16384x7168_sampled(gpu_lib):
     G = len(w.offsets) - 1
     _grouped_check(gpu_lib, w.x, w.offsets.tolist(), w.apply_rht, w.rht_mask, "sr", seed=w.seed,
                    offset=w.offset, groups=[0, 17, 40, G - 1])
+
+
+def test_grouped_moe_16384x7168_every_group_ends(gpu_lib):
+    """Every group of the full-size workload: its amax and S_dec, and the codes and scales of its first and
+    last 16-token block (the blocks next to the group boundaries) in every column."""
+    import torch
+
+    w = workloads.grouped_moe()
+    G = len(w.offsets) - 1
+    got = gpu_lib.nvfp4q_grouped(to_dev(w.x), torch.tensor(w.offsets, dtype=torch.int32, device="cuda"),
+                                 apply_rht=w.apply_rht, rht_mask=w.rht_mask, rounding="sr", seed=w.seed,
+                                 offset=w.offset)
+    ref = oracle.grouped_quantize(w.x, w.offsets, apply_rht=w.apply_rht, rht_mask=w.rht_mask, rounding="sr",
+                                  seed=w.seed, offset=w.offset, ends_only=True)
+    poff = ref["poff"]
+    assert np.array_equal(got["poff"].cpu().numpy(), poff)
+    gc, gs = np_u8(got["codes"]), np_u8(got["scales"])
+    for g in range(G):
+        assert_f32_bits(f"group {g} amax", f32(got["amax"])[g], ref["amax"][g])
+        assert_f32_bits(f"group {g} scale", f32(got["scale"])[g], ref["s_dec"][g])
+        a0, a1 = int(poff[g]), int(poff[g + 1])
+        for t0 in sorted({a0, a1 - 16} if a1 > a0 else set()):
+            assert_same_bits(f"group {g} block at {t0} codes", gc[:, t0 // 2:t0 // 2 + 8],
+                             ref["codes"][:, t0 // 2:t0 // 2 + 8])
+            assert_same_bits(f"group {g} block at {t0} scales", gs[:, t0 // 16], ref["scales"][:, t0 // 16])
 
 
 @pytest.mark.parametrize("apply_rht", [True, False])

@@ -227,6 +227,27 @@ def test_qk_norm_hand_head():
     assert np.all(yf[64:] == 1.0)
 
 
+def test_qk_norm_hand_head_fp16_fp32():
+    # The same heads in fp16 and fp32 (reading R-dtype: one rounding to the input's type). (3, 4) -> (4.8,
+    # 6.4) exactly; 4.8 = 1.2 * 4 with 1.2 = 1.0011001100|1100...b, which rounds up to 1.0011001101b in
+    # fp16's 10 fraction bits: 4.80078125 (truncation would give 4.796875); 6.4 = 1.1001100110|0110...b * 4
+    # rounds down to 6.3984375. fp32 gives the nearest floats of 4.8 and 6.4. With k's weight 0.5 and
+    # weight offset c = 1 the second head (x = 2, r = 1/2) becomes (0.5 + 1) * 1 = 1.5 in both types.
+    for dt, e0, e1 in ((np.float16, 4.80078125, 6.3984375), (np.float32, float(np.float32(4.8)),
+                                                              float(np.float32(6.4)))):
+        x = np.zeros((1, 128), dt)
+        x[0, 0], x[0, 1] = 3.0, 4.0
+        x[0, 64:] = 2.0
+        yq, yk = oracle.qk_norm(x, x, np.ones(64, dt), np.full(64, 0.5, dt), 64, eps=0.0)
+        assert yq.dtype == dt and yk.dtype == dt
+        assert float(yq[0, 0]) == e0 and float(yq[0, 1]) == e1 and np.all(yq[0, 2:64] == 0)
+        assert np.all(yq[0, 64:] == 1.0)
+        yq1, yk1 = oracle.qk_norm(x, x, np.ones(64, dt), np.full(64, 0.5, dt), 64, weight_offset=1.0, eps=0.0)
+        assert np.all(yk1[0, 64:] == 1.5) and np.all(yq1[0, 64:] == 2.0)
+    with pytest.raises(AssertionError):  # mixed types are not one of the library's configurations
+        oracle.qk_norm(np.zeros((1, 64), np.float16), None, np.ones(64, np.float32), None, 64)
+
+
 def test_qk_norm_is_per_head_and_per_tensor_weight():
     # Heads of very different sizes come out with unit RMS (weight 1, eps negligible), each head is
     # unchanged by scaling it by a power of two, and k uses its own weight.
@@ -293,3 +314,23 @@ def test_grouped_round_through_follows_the_input_type():
     a = grouped_quantize(F.bf16_to_f32(xb), offs, apply_rht=True, rht_mask=0x35A9, rounding="sr", seed=3)
     b = grouped_quantize(xb, offs, apply_rht=True, rht_mask=0x35A9, rounding="sr", seed=3, fast_math=True)
     assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+
+
+def test_grouped_ends_only_sampling_matches_the_full_call():
+    # the sampling option of the grouped oracle computes the same bytes for the blocks it keeps, and the
+    # same group amax (which still covers every block)
+    rng = np.random.default_rng(3)
+    counts = rng.multinomial(700, np.full(8, 1 / 8))
+    counts[2], counts[5] = 0, 5
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = _bits(rng.standard_normal((int(off[-1]), 64)))
+    for r in ("rtne", "sr"):
+        full = grouped_quantize(x, off, True, 0x1234, rounding=r, seed=5, offset=1)
+        ends = grouped_quantize(x, off, True, 0x1234, rounding=r, seed=5, offset=1, ends_only=True)
+        assert np.array_equal(full["amax"], ends["amax"])
+        poff = full["poff"]
+        for g in range(8):
+            a0, a1 = int(poff[g]), int(poff[g + 1])
+            for t0 in ({a0, a1 - 16} if a1 > a0 else set()):
+                assert np.array_equal(full["codes"][:, t0 // 2:t0 // 2 + 8], ends["codes"][:, t0 // 2:t0 // 2 + 8])
+                assert np.array_equal(full["scales"][:, t0 // 16], ends["scales"][:, t0 // 16])
