@@ -198,6 +198,26 @@ nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, 
                              void *stream);
 
 /*
+ * rmsnorm_nvfp4q_noalloc -- rmsnorm_nvfp4q without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the library's own
+ * static 1 MiB device array stands in for the workspace. Arguments, results
+ * and errors are those of rmsnorm_nvfp4q (the same kernels run); nothing is
+ * allocated or freed, and every shape rmsnorm_nvfp4q accepts fits the array
+ * (that path needs a constant 1 MiB). The array exists once per GPU, is held
+ * until the process ends, and keeps the last call's contents, which no call
+ * reads before writing them; calls that can overlap on one GPU (different
+ * streams, or different host threads on one device) race on it and must not
+ * be issued. NVFP4Q_E_LAUNCH if the array's device address cannot be looked
+ * up on the current device.
+ */
+nvfp4q_status rmsnorm_nvfp4q_noalloc(const void *x, nvfp4q_dtype dtype, int64_t tokens, int64_t hidden,
+                                     int64_t ld_x, const void *gamma, const void *beta, float weight_offset,
+                                     float eps, void *y_out, int64_t ld_y, const nvfp4q_global *g,
+                                     const nvfp4q_plane *row, nvfp4q_rounding rounding,
+                                     const nvfp4q_rng *rng, void *stream);
+
+/*
  * nvfp4q_quantize_2d -- rowwise and columnwise (transposed) planes of one
  * [rows, cols] tensor (bf16, fp16 or fp32) under one shared per-tensor scale
  * (weights).

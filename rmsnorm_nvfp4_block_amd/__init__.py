@@ -15,14 +15,14 @@ from typing import Optional
 __all__ = [
     "load", "lib_path", "workspace", "NVFP4QError",
     "nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped", "nvfp4q_grouped",
-    "nvfp4q_qk_norm", "nvfp4q_workspace_bytes", "nvfp4q_status_string", "SYMBOLS",
+    "nvfp4q_qk_norm", "rmsnorm_nvfp4q_noalloc", "nvfp4q_workspace_bytes", "nvfp4q_status_string", "SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libnvfp4q.so")
 
 SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped", "nvfp4q_grouped",
-           "nvfp4q_qk_norm",
+           "nvfp4q_qk_norm", "rmsnorm_nvfp4q_noalloc",
            "nvfp4q_workspace_bytes", "nvfp4q_status_string", "nvfp4q_version")
 
 RTNE, SR = 0, 1
@@ -70,6 +70,9 @@ def load():
     lib.rmsnorm_nvfp4q.restype = ctypes.c_int
     lib.rmsnorm_nvfp4q.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, f32, f32, vp, i64, P(Global), P(Plane),
                                    ctypes.c_int, P(Rng), vp, ctypes.c_size_t, vp]
+    lib.rmsnorm_nvfp4q_noalloc.restype = ctypes.c_int
+    lib.rmsnorm_nvfp4q_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, f32, f32, vp, i64, P(Global),
+                                           P(Plane), ctypes.c_int, P(Rng), vp]
     lib.nvfp4q_quantize_2d.restype = ctypes.c_int
     lib.nvfp4q_quantize_2d.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(Global), P(Plane), P(Plane), ctypes.c_int,
                                        P(Rng), vp, ctypes.c_size_t, vp]
@@ -218,6 +221,36 @@ def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, 
                             _stream(x))
     _check(st)
     return {"codes": c, "scales": s, "amax": amax_out, "scale": scale_out, "y": y}
+
+
+def rmsnorm_nvfp4q_noalloc(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, rounding="rtne", seed=0,
+                           offset=0, y_out=None, codes=None, scales=None, amax_out=None, scale_out=None):
+    """rmsnorm_nvfp4q through the entry point that allocates nothing (the library's static workspace).
+
+    Outputs are the caller's: pass y_out, codes / scales, amax_out / scale_out tensors to make the call
+    allocate nothing on the Python side either (any left as None is allocated here, before the call).
+    Returns dict(codes, scales, amax, scale, y).
+    """
+    import torch
+
+    dt = _dtype_code(x)
+    for p in (gamma, beta):
+        if p is not None and (p.dtype != x.dtype or not p.is_contiguous()):
+            raise ValueError("gamma and beta must be contiguous and of x's dtype")
+    lib = load()
+    T, H = x.shape
+    c, s, plane = _plane(T, H, x.device, codes, scales)
+    if amax_out is None:
+        amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    if scale_out is None:
+        scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    st = lib.rmsnorm_nvfp4q_noalloc(x.data_ptr(), dt, T, H, x.stride(0), gamma.data_ptr(), _ptr(beta),
+                                    float(weight_offset), float(eps), _ptr(y_out),
+                                    y_out.stride(0) if y_out is not None else 0,
+                                    ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(plane),
+                                    _rounding(rounding), ctypes.byref(Rng(seed, offset)), _stream(x))
+    _check(st)
+    return {"codes": c, "scales": s, "amax": amax_out, "scale": scale_out, "y": y_out}
 
 
 def nvfp4q_quantize_2d(x, amax=None, rounding="rtne", seed=0, offset=0, rowwise=True, colwise=True,

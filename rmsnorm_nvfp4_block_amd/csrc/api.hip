@@ -8,6 +8,7 @@
 
 #include <cstddef>
 #include <cstdlib>
+#include <mutex>
 
 using namespace nvfp4q;
 
@@ -82,6 +83,83 @@ bool rms_stream_enabled() {
   return on;
 }
 
+// The no-allocation entry point's workspace: a file-scope device array, one
+// per GPU (each device that loads the library holds its own copy until the
+// process ends). Host code never passes the array's name to a kernel (on the
+// host it only stands for the symbol); its device address is looked up once
+// per device with hipGetSymbolAddress, with that device current, and kept.
+constexpr size_t kScratchBytes = sizeof(Workspace);  // 1 MiB: what every rmsnorm_nvfp4q call needs
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+static_assert(kScratchBytes >= sizeof(Workspace), "the static workspace holds one workspace");
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`; NVFP4Q_E_LAUNCH if the device or the
+// lookup fails, NVFP4Q_E_UNSUPPORTED for device ordinals past kMaxDevices.
+nvfp4q_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return NVFP4Q_E_LAUNCH;
+  if (dev >= kMaxDevices) return NVFP4Q_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NVFP4Q_E_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return NVFP4Q_OK;
+}
+
+// rmsnorm_nvfp4q on the caller's workspace, or (use_static) on the static
+// one; either is checked or looked up after the other arguments pass.
+nvfp4q_status rmsnorm_impl(const void* x, nvfp4q_dtype dtype, int64_t tokens, int64_t hidden, int64_t ld_x,
+                           const void* gamma, const void* beta, float weight_offset, float eps, void* y_out,
+                           int64_t ld_y, const nvfp4q_global* g, const nvfp4q_plane* row, nvfp4q_rounding rounding,
+                           const nvfp4q_rng* rng, void* workspace, size_t workspace_bytes, bool use_static,
+                           void* stream) {
+  TRY(check_input(x, dtype, tokens, hidden, ld_x, true));
+  if (!gamma) return NVFP4Q_E_NULLPTR;
+  if (!aligned(gamma, 16) || !aligned(beta, 16)) return NVFP4Q_E_ALIGN;
+  if (weight_offset != 0.0f && weight_offset != 1.0f) return NVFP4Q_E_UNSUPPORTED;
+  if (!(eps >= 0.0f)) return NVFP4Q_E_SHAPE;
+  if (hidden > rms_max_cols()) return NVFP4Q_E_UNSUPPORTED;
+  const bool codes = row && (row->codes || tokens == 0);
+  if (!codes && !y_out) return NVFP4Q_E_NULLPTR;
+  if (codes) TRY(check_plane(row, tokens, hidden));
+  if (y_out) {
+    if (ld_y < hidden || ld_y > kMaxLd) return NVFP4Q_E_SHAPE;
+    if (!aligned(y_out, 16) || (ld_y * dtype_size(dtype)) % 16 != 0) return NVFP4Q_E_ALIGN;
+  }
+  TRY(check_rounding(rounding, rng));
+  if (use_static) TRY(static_scratch(&workspace));
+  else TRY(check_ws(workspace, workspace_bytes));
+  const nvfp4q_global& gg = g ? *g : kNoGlobal;
+  hipStream_t s = (hipStream_t)stream;
+  if (tokens == 0) return codes ? done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s)) : NVFP4Q_OK;
+  RowArgs a = {};
+  a.x = x; a.dtype = (int)dtype; a.rows = tokens; a.cols = hidden; a.ld_x = ld_x;
+  a.gamma = gamma; a.beta = beta; a.woff = weight_offset; a.eps = eps;
+  a.y = y_out; a.ld_y = ld_y;
+  a.codes = codes ? row->codes : nullptr; a.ldc = codes ? row->ld_codes : 0;
+  a.scales = codes ? row->scales : nullptr; a.lds = codes ? row->ld_scales : 0;
+  a.ws = (Workspace*)workspace;
+  a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
+  a.sr = base_rounding(rounding) == NVFP4Q_SR;
+  a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
+  // With the amax pass and a row count that fits the workspace's row-scale
+  // slots, the encode pass streams rows using the 1/rms the amax pass stored.
+  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled();
+  if (streamed) a.rs = reinterpret_cast<float*>(static_cast<char*>(workspace) + offsetof(Workspace, partial)) + kRowPartials;
+  if (codes && !a.amax_in) {
+    const hipError_t e = (streamed && !beta) ? launch_rms_stream_amax(a, s, &a.nparts)
+                                           : launch_rmsnorm_pass(a, true, s, &a.nparts);
+    if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
+  }
+  return done(streamed ? launch_rms_stream_quant(a, s) : launch_rmsnorm_pass(a, false, s, nullptr));
+}
+
 }  // namespace
 
 namespace nvfp4q {
@@ -145,44 +223,17 @@ nvfp4q_status rmsnorm_nvfp4q(const void* x, nvfp4q_dtype dtype, int64_t tokens, 
                              int64_t ld_y, const nvfp4q_global* g, const nvfp4q_plane* row,
                              nvfp4q_rounding rounding, const nvfp4q_rng* rng, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  TRY(check_input(x, dtype, tokens, hidden, ld_x, true));
-  if (!gamma) return NVFP4Q_E_NULLPTR;
-  if (!aligned(gamma, 16) || !aligned(beta, 16)) return NVFP4Q_E_ALIGN;
-  if (weight_offset != 0.0f && weight_offset != 1.0f) return NVFP4Q_E_UNSUPPORTED;
-  if (!(eps >= 0.0f)) return NVFP4Q_E_SHAPE;
-  if (hidden > rms_max_cols()) return NVFP4Q_E_UNSUPPORTED;
-  const bool codes = row && (row->codes || tokens == 0);
-  if (!codes && !y_out) return NVFP4Q_E_NULLPTR;
-  if (codes) TRY(check_plane(row, tokens, hidden));
-  if (y_out) {
-    if (ld_y < hidden || ld_y > kMaxLd) return NVFP4Q_E_SHAPE;
-    if (!aligned(y_out, 16) || (ld_y * dtype_size(dtype)) % 16 != 0) return NVFP4Q_E_ALIGN;
-  }
-  TRY(check_rounding(rounding, rng));
-  TRY(check_ws(workspace, workspace_bytes));
-  const nvfp4q_global& gg = g ? *g : kNoGlobal;
-  hipStream_t s = (hipStream_t)stream;
-  if (tokens == 0) return codes ? done(launch_empty_scale(gg.amax_out, gg.scale_out, 1, s)) : NVFP4Q_OK;
-  RowArgs a = {};
-  a.x = x; a.dtype = (int)dtype; a.rows = tokens; a.cols = hidden; a.ld_x = ld_x;
-  a.gamma = gamma; a.beta = beta; a.woff = weight_offset; a.eps = eps;
-  a.y = y_out; a.ld_y = ld_y;
-  a.codes = codes ? row->codes : nullptr; a.ldc = codes ? row->ld_codes : 0;
-  a.scales = codes ? row->scales : nullptr; a.lds = codes ? row->ld_scales : 0;
-  a.ws = (Workspace*)workspace;
-  a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
-  a.sr = base_rounding(rounding) == NVFP4Q_SR;
-  a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
-  // With the amax pass and a row count that fits the workspace's row-scale
-  // slots, the encode pass streams rows using the 1/rms the amax pass stored.
-  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled();
-  if (streamed) a.rs = reinterpret_cast<float*>(static_cast<char*>(workspace) + offsetof(Workspace, partial)) + kRowPartials;
-  if (codes && !a.amax_in) {
-    const hipError_t e = (streamed && !beta) ? launch_rms_stream_amax(a, s, &a.nparts)
-                                           : launch_rmsnorm_pass(a, true, s, &a.nparts);
-    if (e != hipSuccess) return NVFP4Q_E_LAUNCH;
-  }
-  return done(streamed ? launch_rms_stream_quant(a, s) : launch_rmsnorm_pass(a, false, s, nullptr));
+  return rmsnorm_impl(x, dtype, tokens, hidden, ld_x, gamma, beta, weight_offset, eps, y_out, ld_y, g, row,
+                      rounding, rng, workspace, workspace_bytes, false, stream);
+}
+
+nvfp4q_status rmsnorm_nvfp4q_noalloc(const void* x, nvfp4q_dtype dtype, int64_t tokens, int64_t hidden,
+                                     int64_t ld_x, const void* gamma, const void* beta, float weight_offset,
+                                     float eps, void* y_out, int64_t ld_y, const nvfp4q_global* g,
+                                     const nvfp4q_plane* row, nvfp4q_rounding rounding, const nvfp4q_rng* rng,
+                                     void* stream) {
+  return rmsnorm_impl(x, dtype, tokens, hidden, ld_x, gamma, beta, weight_offset, eps, y_out, ld_y, g, row,
+                      rounding, rng, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

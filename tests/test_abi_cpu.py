@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     d = _declared()
     for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped",
-                 "nvfp4q_grouped", "nvfp4q_qk_norm"):
+                 "nvfp4q_grouped", "nvfp4q_qk_norm", "rmsnorm_nvfp4q_noalloc"):
         assert name in d
 
 
@@ -42,7 +42,7 @@ def test_binding_names_match_the_abi():
     import rmsnorm_nvfp4_block_amd as q
 
     for name in ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped",
-                 "nvfp4q_grouped", "nvfp4q_qk_norm"):
+                 "nvfp4q_grouped", "nvfp4q_qk_norm", "rmsnorm_nvfp4q_noalloc"):
         assert callable(getattr(q, name))
 
 
@@ -297,3 +297,26 @@ def test_binding_keeps_one_workspace_per_stream(monkeypatch):
     assert q.workspace(torch.device("cuda", 1), stream=0x1000) is not a   # per device as well
     assert len(made) == 3
 
+
+def test_rmsnorm_noalloc_validation(lib):
+    """The no-allocation entry point validates like rmsnorm_nvfp4q, before it looks up its static
+    workspace (so on a host without a GPU these calls never reach the device)."""
+    import rmsnorm_nvfp4_block_amd as q
+
+    plane = q.Plane(FAKE, 16, FAKE, 2)
+    g = q.Global(None, None, None)
+    r = q.Rng(0, 0)
+
+    def call(x=FAKE, dtype=0, gamma=FAKE, beta=None, woff=0.0, eps=1e-6, hidden=32, p=plane, rnd=0):
+        return lib.rmsnorm_nvfp4q_noalloc(x, dtype, 4, hidden, hidden, gamma, beta, woff, eps, None, 0,
+                                          ctypes.byref(g), ctypes.byref(p), rnd, ctypes.byref(r), None)
+
+    assert call(gamma=None) == 1
+    assert call(x=FAKE + 2) == 3
+    assert call(dtype=3) == 4
+    assert call(beta=FAKE + 4) == 3
+    assert call(woff=0.5) == 4
+    assert call(eps=-1.0) == 2
+    assert call(hidden=40) == 2
+    assert call(p=q.Plane(None, 0, None, 0)) == 1
+    assert call(rnd=2) == 4
