@@ -314,6 +314,49 @@ def test_rmsnorm_prefill_given_amax(gpu_lib):
     _check_rms(w, got, amax_given=np.float32(q["amax"]))
 
 
+@pytest.mark.parametrize("shape,dtype,bias,woff,rounding", [((2048, 4096), "bf16", False, 0.0, "rtne"),
+                                                            ((2304, 3088), "bf16", True, 1.0, "sr"),
+                                                            ((2050, 8192), "fp16", False, 0.0, "rtne"),
+                                                            ((2100, 7184), "bf16", True, 0.0, "sr"),
+                                                            ((2048, 4096), "fp32", False, 1.0, "rtne"),
+                                                            ((4100, 4096), "bf16", False, 0.0, "sr")])
+def test_rmsnorm_given_amax_large(gpu_lib, shape, dtype, bias, woff, rounding):
+    """A given amax (one pass over x, each row's 1/rms taken in the same pass) on prefill-sized inputs:
+    ragged last superchunks, rows of up to 8192 columns, several rows per workgroup, all input types."""
+    import torch
+
+    T, H = shape
+    rng = np.random.default_rng(T * 3 + H)
+    x32 = (rng.standard_normal(shape) * np.exp(rng.uniform(-2, 2, (T, 1)))).astype(np.float32)
+    g32 = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    b32 = (0.01 * rng.standard_normal(H)).astype(np.float32) if bias else None
+    if dtype == "bf16":
+        conv = lambda a: None if a is None else workloads.to_bf16_bits(a)
+        dev = lambda a: None if a is None else to_dev(a)
+    else:
+        ndt = np.float16 if dtype == "fp16" else np.float32
+        conv = lambda a: None if a is None else a.astype(ndt)
+        dev = lambda a: None if a is None else torch.from_numpy(a).cuda()
+    x, g, b = conv(x32), conv(g32), conv(b32)
+    y_ref, y64, _ = oracle.rmsnorm_bf16(x, g, b, woff, 1e-6, return_f64=True, out_dtype=dtype)
+    ref = oracle.quantize_rowwise(y_ref, rounding=rounding, seed=3, offset=1)
+    a = torch.tensor([ref["amax"]], dtype=torch.float32, device="cuda")
+    got = gpu_lib.rmsnorm_nvfp4q(dev(x), dev(g), dev(b), weight_offset=woff, eps=1e-6, amax=a, rounding=rounding,
+                                 seed=3, offset=1, y_out=True)
+    yg = to_np_bf16(got["y"]) if dtype == "bf16" else got["y"].cpu().numpy()
+    b64 = None
+    if b is not None:
+        b64 = (F.bf16_to_f32(b) if dtype == "bf16" else b.astype(np.float32)).astype(np.float64)[None, :]
+    assert_rounded_output("y", yg, y_ref, y64, dtype, REL_ERR_RMSNORM, b64)
+    own = oracle.quantize_rowwise(yg, amax=np.float32(ref["amax"]), rounding=rounding, seed=3, offset=1)
+    assert_same_bits("codes (own y)", np_u8(got["codes"], H // 2), own["codes"])
+    assert_same_bits("scales (own y)", np_u8(got["scales"], H // 16), own["scales"])
+    n, ok = code_step_mismatch(np_u8(got["codes"], H // 2), ref["codes"])
+    assert ok and n <= 1e-4 * T * H, f"{n} codes differ from the float64 oracle"
+    assert_code_diffs_follow_y("codes", np_u8(got["codes"], H // 2), ref["codes"], yg, y_ref, ref["amax"],
+                               ref["amax"])
+
+
 def test_rmsnorm_given_amax_and_y_only(gpu_lib):
     import torch
 
