@@ -319,10 +319,9 @@ nvfp4q_status nvfp4q_qk_norm(void *q, void *k, nvfp4q_dtype dtype, int64_t token
  *     no rowwise plane. At least one plane must be given.
  *   SR: columnwise tag 1, block index = plane_row * (Poff[G] / 16) +
  *   plane_col / 16; rowwise tag 0, block index = row * (cols / 16) + col / 16.
- *   Without amax_in (for a requested plane) the amax pass keeps one partial
- *   per 16-row block x 128-column tile and plane; shapes needing more slots
- *   than the workspace holds (planes * floor((total_rows + 15 G) / 16) *
- *   ceil(cols / 128) + 128 > 262112) return NVFP4Q_E_UNSUPPORTED.
+ *   Without amax_in (for a requested plane) the amax pass keeps one maximum
+ *   per group for each of its workgroups (at most 1024) in the workspace, so
+ *   the workspace bounds no input size.
  *   A row stride above 2^25 bytes (ld_x above 2^24 for bf16 / fp16, 2^23 for
  *   fp32) returns NVFP4Q_E_SHAPE (the kernels address 32 rows of x with
  *   32-bit byte offsets). fp16 / fp32 input: the transform's output is

@@ -358,10 +358,6 @@ nvfp4q_status nvfp4q_grouped(const void* x, nvfp4q_dtype dtype, int64_t total_ro
   TRY(check_ws(workspace, workspace_bytes));
   const nvfp4q_global& gg = g ? *g : kNoGlobal;
   const nvfp4q_global& gr = g_row ? *g_row : kNoGlobal;
-  const bool col_amax = want_col && !gg.amax_in, row_amax = want_row && !gr.amax_in;
-  if ((col_amax || row_amax) &&
-      grouped_partials(total_rows, cols, num_groups, (col_amax ? 1 : 0) + (row_amax ? 1 : 0)) > kPartials)
-    return NVFP4Q_E_UNSUPPORTED;
   GroupArgs a = {};
   a.x = x; a.dtype = (int)dtype; a.rows = total_rows; a.cols = cols; a.ld_x = ld_x;
   a.offsets = offsets; a.groups = num_groups; a.poff_out = padded_offsets_out;

@@ -269,103 +269,114 @@ __device__ __forceinline__ uint32_t pk_max_mag(uint32_t acc, uint32_t w) {
   return __builtin_bit_cast(uint32_t, m);
 }
 
-// Pass 1: per-(block, column tile) maxima. COL: of the (transformed, rounded
-// through the input's type) columnwise values, into partial[tb * ntc +
-// ctile]. ROW: of |x| itself (the rowwise plane has no transform), into
-// partial[rbase + tb * ntc + ctile].
+// Pass 1: per-group maxima. The launch has at most kAmaxGrid workgroups; each
+// takes work items (4 block pairs x one column tile) in a grid-stride loop and
+// keeps the maximum of every group it meets in LDS (non-negative floats
+// compare like their bit patterns, so an LDS integer maximum suffices). At the
+// end workgroup w writes its 64 group maxima into partial[w * 64 + g] (COL: of
+// the transformed values, rounded through the input's type) and, for the
+// rowwise plane (ROW: of |x| itself, no transform), into
+// partial[rbase + w * 64 + g]; groups it never met get 0. The workspace thus
+// holds grid x 64 slots per plane whatever the size of x.
+constexpr int kAmaxGrid = 1024;
+static_assert(2 * kAmaxGrid * 64 + 128 <= kPartials, "both planes' group maxima fit the workspace");
+
 template <int CPL, bool RHT, bool FAST, bool COL, bool ROW, int DT>
 __global__ __launch_bounds__(kT) void k_grouped_amax(const void* __restrict__ x, int rows, uint32_t cols,
                                                      int64_t ld_x, const int32_t* __restrict__ offsets, int groups,
                                                      uint32_t mask, Workspace* ws, uint32_t nq, uint32_t ntc,
-                                                     uint32_t npairs, uint32_t nb_max, uint32_t chunk, uint32_t rbase) {
-  const uint32_t v = xcd_work_item(chunk);
-  if (v >= nq * ntc) return;
-  uint32_t ctile, pair;
-  wg_item(v, nq, ctile, pair);
-  if (pair >= npairs) return;
+                                                     uint32_t npairs, uint32_t nb_max, uint32_t rbase) {
+  __shared__ uint32_t gmc[64], gmr[64];  // group maxima (fp32 bits) of this workgroup, columnwise / rowwise
+  if (threadIdx.x < 64) {
+    gmc[threadIdx.x] = 0u;
+    gmr[threadIdx.x] = 0u;
+  }
+  __syncthreads();
   const GroupScan q = group_scan(offsets, groups, rows);
   const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
-  const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
-  Tile<CPL, DT> r;
-  load_item<CPL, DT>(x, ld_x, rows, it, true, r);
-  const bool writer = (threadIdx.x & 31) == 0 && it.tb < nb_max;
-  if constexpr (ROW) {
-    float mr;
-    if constexpr (DT == kInFP32) {
-      uint32_t mm = 0;  // magnitude bits: their u32 order is the order of |x|
+  const uint32_t half = (threadIdx.x >> 5) & 1;
+  for (uint32_t v = blockIdx.x; v < nq * ntc; v += gridDim.x) {
+    uint32_t ctile, pair;
+    wg_item(v, nq, ctile, pair);
+    if (pair >= npairs) continue;  // wave-uniform; no barrier in the loop
+    const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
+    Tile<CPL, DT> r;
+    load_item<CPL, DT>(x, ld_x, rows, it, true, r);
+    // the half-wave's block and group (lane 0 of the half publishes)
+    const bool writer = (threadIdx.x & 31) == 0 && it.tb < nb_max && (half ? it.b1.valid : it.b0.valid);
+    const int g = half ? it.b1.g : it.b0.g;
+    if constexpr (ROW) {
+      float mr;
+      if constexpr (DT == kInFP32) {
+        uint32_t mm = 0;  // magnitude bits: their u32 order is the order of |x|
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < 16; ++i)
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) mm = max(mm, r[i][j] & 0x7FFFFFFFu);
-      mr = __uint_as_float(mm);
-    } else {
-      uint32_t mm = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int j = 0; j < CPL / 2; ++j) mm = pk_max_mag(mm, r[i][j]);
-      const uint32_t hi = mm >> 16, lo = mm & 0xFFFFu, m16 = hi > lo ? hi : lo;
-      mr = DT == kInBF16 ? __uint_as_float(m16 << 16) : h_lo(m16);
-    }
-    mr = half_wave_max(mr);  // lanes without data: 0
-    if (writer) ws->partial[rbase + it.tb * ntc + it.ctile] = mr;
-  }
-  if constexpr (COL) {
-    if constexpr (RHT) apply_signs<CPL, DT>(r, mask);
-    float m = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      float v16[16];
-      column<CPL, DT>(r, c, v16);
-      if constexpr (RHT) {
-        // The last stage only feeds the maximum: max(|RN(a + b)|, |RN(a - b)|)
-        // = RN(|a| + |b|), since one of a + b, a - b has magnitude |a| + |b|,
-        // the other at most that, and rounding is odd and monotone.
-        fwht16<3>(v16);
-        float s8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s8[i] = fabsf(v16[i]) + fabsf(v16[i + 8]);
-        m = fmaxf(m, max8_abs(s8));
+          for (int j = 0; j < CPL; ++j) mm = max(mm, r[i][j] & 0x7FFFFFFFu);
+        mr = __uint_as_float(mm);
       } else {
-        m = fmaxf(m, max16_abs(v16));
+        uint32_t mm = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int j = 0; j < CPL / 2; ++j) mm = pk_max_mag(mm, r[i][j]);
+        const uint32_t hi = mm >> 16, lo = mm & 0xFFFFu, m16 = hi > lo ? hi : lo;
+        mr = DT == kInBF16 ? __uint_as_float(m16 << 16) : h_lo(m16);
       }
+      mr = half_wave_max(mr);  // lanes without data: 0
+      if (writer) atomicMax(&gmr[g], __float_as_uint(mr));
     }
-    // max |RN_T(0.25 y)| = RN_T(0.25 max |y|): scaling by 0.25 and
-    // round-to-nearest-even are both monotone (fast math, fp32: no rounding).
-    if constexpr (RHT) m = FAST ? m * 0.25f : round_t<DT>(m * 0.25f);
-    m = half_wave_max(m);  // lanes without data hold zeros
-    if (writer) ws->partial[it.tb * ntc + it.ctile] = m;
+    if constexpr (COL) {
+      if constexpr (RHT) apply_signs<CPL, DT>(r, mask);
+      float m = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        float v16[16];
+        column<CPL, DT>(r, c, v16);
+        if constexpr (RHT) {
+          // The last stage only feeds the maximum: max(|RN(a + b)|, |RN(a - b)|)
+          // = RN(|a| + |b|), since one of a + b, a - b has magnitude |a| + |b|,
+          // the other at most that, and rounding is odd and monotone.
+          fwht16<3>(v16);
+          float s8[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s8[i] = fabsf(v16[i]) + fabsf(v16[i + 8]);
+          m = fmaxf(m, max8_abs(s8));
+        } else {
+          m = fmaxf(m, max16_abs(v16));
+        }
+      }
+      // max |RN_T(0.25 y)| = RN_T(0.25 max |y|): scaling by 0.25 and
+      // round-to-nearest-even are both monotone (fast math, fp32: no rounding).
+      if constexpr (RHT) m = FAST ? m * 0.25f : round_t<DT>(m * 0.25f);
+      m = half_wave_max(m);  // lanes without data hold zeros
+      if (writer) atomicMax(&gmc[g], __float_as_uint(m));
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    if (COL) ws->partial[blockIdx.x * 64 + threadIdx.x] = __uint_as_float(gmc[threadIdx.x]);
+    if (ROW) ws->partial[rbase + blockIdx.x * 64 + threadIdx.x] = __uint_as_float(gmr[threadIdx.x]);
   }
 }
 
-// Between the passes, one workgroup per group: the maximum of the partials of
-// the group's blocks over every column tile (contiguous slots, clamped to the
-// lim slots per plane the amax pass writes), into the workspace for the encode
-// pass and into amax_out / scale_out (rowwise: from rbase on, into ramax_out /
-// rscale_out). Empty groups get 0.
+// Between the passes, one workgroup per group: the maximum of the group's
+// slots over the amax pass's workgroups (nwg of them), into the workspace for
+// the encode pass and into amax_out / scale_out (rowwise: from rbase on, into
+// ramax_out / rscale_out).
 constexpr int kReduceThreads = 512;
 template <bool COL, bool ROW>
-__global__ __launch_bounds__(kReduceThreads) void k_grouped_reduce(const int32_t* __restrict__ offsets, int groups,
-                                                                   int rows, Workspace* ws, uint32_t ntc,
-                                                                   uint32_t lim, uint32_t rbase, float* amax_out,
-                                                                   float* scale_out, float* ramax_out,
-                                                                   float* rscale_out) {
+__global__ __launch_bounds__(kReduceThreads) void k_grouped_reduce(Workspace* ws, uint32_t nwg, uint32_t rbase,
+                                                                   float* amax_out, float* scale_out,
+                                                                   float* ramax_out, float* rscale_out) {
   const int g = blockIdx.x;
-  const GroupScan q = group_scan(offsets, groups, rows);
-  const uint32_t lo = min(((uint32_t)lane_int(q.ps - q.p, g) >> 4) * ntc, lim);
-  const uint32_t n = min(((uint32_t)lane_int(q.p, g) >> 4) * ntc, lim - lo);
   auto reduce = [&](const float* src) {
     float m = 0.0f;
-    for (uint32_t i = threadIdx.x; i < n; i += 4 * kReduceThreads) {
-      float t[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) t[u] = i + u * kReduceThreads < n ? src[i + u * kReduceThreads] : 0.0f;
-      m = fmaxf(fmaxf(m, fmaxf(t[0], t[1])), fmaxf(t[2], t[3]));
-    }
+    for (uint32_t w = threadIdx.x; w < nwg; w += kReduceThreads) m = fmaxf(m, src[w * 64 + g]);
     return wg_max<kReduceThreads / 64>(m);
   };
   if constexpr (COL) {
-    const float m = reduce(ws->partial + lo);
+    const float m = reduce(ws->partial);
     if (threadIdx.x == 0) {
       ws->partial[kGroupAmax + g] = m;
       if (amax_out) amax_out[g] = m;
@@ -373,7 +384,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_grouped_reduce(const int32_t
     }
   }
   if constexpr (ROW) {
-    const float m = reduce(ws->partial + rbase + lo);
+    const float m = reduce(ws->partial + rbase);
     if (threadIdx.x == 0) {
       ws->partial[kGroupAmaxRow + g] = m;
       if (ramax_out) ramax_out[g] = m;
@@ -693,16 +704,18 @@ Geo geo_of(int64_t cols, uint32_t nb_max) {
 }
 
 // Amax pass and reduce kernel for the planes whose amax is not given (COL,
-// ROW); rowwise partials follow the columnwise ones when both are computed.
+// ROW); rowwise slots follow the columnwise ones when both are computed.
 template <int CPLA, bool RHT, bool FAST, bool COL, bool ROW, int DT>
 void launch_amax(const GroupArgs& a, uint32_t nb_max, hipStream_t s) {
   const Geo g = geo_of<CPLA>(a.cols, nb_max);
-  const uint32_t lim = nb_max * g.ntc, rbase = COL ? lim : 0;
-  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT, FAST, COL, ROW, DT>), g.grid, dim3(kT), 0, s, a.x, (int)a.rows,
+  const uint64_t items = (uint64_t)g.nq * g.ntc;
+  const uint32_t nwg = (uint32_t)(items < (uint64_t)kAmaxGrid ? items : kAmaxGrid);
+  const uint32_t rbase = COL ? nwg * 64 : 0;
+  hipLaunchKernelGGL((k_grouped_amax<CPLA, RHT, FAST, COL, ROW, DT>), dim3(nwg), dim3(kT), 0, s, a.x, (int)a.rows,
                      (uint32_t)a.cols, a.ld_x, a.offsets, a.groups, a.mask, a.ws, g.nq, g.ntc, g.npairs, nb_max,
-                     g.chunk, rbase);
-  hipLaunchKernelGGL((k_grouped_reduce<COL, ROW>), dim3(a.groups), dim3(kReduceThreads), 0, s, a.offsets, a.groups,
-                     (int)a.rows, a.ws, g.ntc, lim, rbase, a.amax_out, a.scale_out, a.ramax_out, a.rscale_out);
+                     rbase);
+  hipLaunchKernelGGL((k_grouped_reduce<COL, ROW>), dim3(a.groups), dim3(kReduceThreads), 0, s, a.ws, nwg, rbase,
+                     a.amax_out, a.scale_out, a.ramax_out, a.rscale_out);
 }
 
 template <int CPLE, bool RHT, bool SR, bool FAST, bool COL, bool ROW, int DT>
@@ -748,11 +761,14 @@ void launch_grouped_t(const GroupArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Workspace slots the grouped path needs: the amax pass's partials, one per
-// (padded token block, column tile) and plane, then the per-group amax of
-// both planes.
+// Workspace slots the grouped path needs: 64 per amax workgroup (at most
+// kAmaxGrid) and plane, then the per-group amax of both planes; independent of
+// the size of x.
 int64_t grouped_partials(int64_t rows, int64_t cols, int groups, int planes) {
-  return planes * grouped_blocks(rows, groups) * tiles_of<kCplAmax>(cols) + 128;
+  (void)rows;
+  (void)cols;
+  (void)groups;
+  return (int64_t)planes * kAmaxGrid * 64 + 128;
 }
 
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s) {

@@ -118,9 +118,10 @@ int rms_max_cols();
 hipError_t launch_quant_2d(const TwoDArgs& a, hipStream_t s);
 hipError_t launch_qk_norm(const QkArgs& a, hipStream_t s);
 
-// Grouped path; hipErrorInvalidValue when the tile grid exceeds the workspace.
+// Grouped path.
 hipError_t launch_grouped(const GroupArgs& a, hipStream_t s);
-// Workspace slots the grouped path's amax pass needs for `planes` planes.
+// Workspace slots the grouped path's amax pass needs for `planes` planes (a
+// bound independent of the size of x).
 int64_t grouped_partials(int64_t rows, int64_t cols, int groups, int planes);
 
 }  // namespace nvfp4q

@@ -150,29 +150,6 @@ def test_dtype_acceptance_per_entry_point(lib):
     assert lib.nvfp4q_qk_norm(FAKE, None, 2, 3, 4, 0, 64, 258, 0, FAKE, None, 0.0, 1e-6, None) == 3
 
 
-def test_grouped_partials_capacity(lib):
-    # the amax pass keeps planes * floor((rows + 15 G) / 16) * ceil(cols / 128) partials + 128 slots of
-    # 262112; a call past that returns NVFP4Q_E_UNSUPPORTED before anything is launched (workspace of full
-    # size, so the capacity check is the one that stops it)
-    import rmsnorm_nvfp4_block_amd as q
-
-    g = q.Global(None, None, None)
-    r = q.Rng(0, 0)
-
-    def call(rows, cols, rowwise):
-        cap = rows + 15
-        col = q.Plane(FAKE, (cap // 2 + 15) // 16 * 16, FAKE, (cap + 15) // 16)
-        row = q.Plane(FAKE, cols // 2, FAKE, cols // 16)
-        return lib.nvfp4q_grouped(FAKE, 0, rows, cols, cols, FAKE, 1, None, 1, 0, ctypes.byref(g),
-                                  ctypes.byref(col), ctypes.byref(g) if rowwise else None,
-                                  ctypes.byref(row) if rowwise else None, 1, ctypes.byref(r), FAKE, 1 << 20, None)
-
-    # one plane: 16385 blocks x 16 tiles = 262160 > 261984 slots
-    assert call(16385 * 16 - 15, 2048, False) == 4
-    # two planes: 8193 blocks x 16 tiles x 2 = 262176
-    assert call(8193 * 16 - 15, 2048, True) == 4
-
-
 def test_qk_norm_validation(lib):
     def call(d=128, hq=4, hk=2, ldq=512, ldk=256, q=FAKE, k=FAKE, wq=FAKE, wk=FAKE, woff=0.0, eps=1e-6, t=3):
         return lib.nvfp4q_qk_norm(q, k, 0, t, hq, hk, d, ldq, ldk, wq, wk, woff, eps, None)

@@ -739,7 +739,7 @@ def test_2d_experts_4x4096x7168_sampled(gpu_lib):
 
 # ---------------------------------------------------------------- grouped
 def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offset=2, groups=None, amax=None,
-                   fast_math=False, colwise=True, rowwise=False, row_amax=None, pad=0):
+                   fast_math=False, colwise=True, rowwise=False, row_amax=None, pad=0, amax_all=False):
     import torch
 
     T, C = x.shape
@@ -784,6 +784,19 @@ def _grouped_check(gpu_lib, x, offsets, apply_rht, mask, rounding, seed=21, offs
             assert_same_bits(f"group {g} row scales", rs[r0:r1, :C // 16], ref["row_scales"][r0:r1])
             assert_f32_bits(f"group {g} row amax", f32(got["row_amax"])[g], ref["row_amax"][g])
             assert_f32_bits(f"group {g} row scale", f32(got["row_scale"])[g], ref["row_s_dec"][g])
+    if amax_all:
+        # every group's rowwise amax (a plain max |x|), and each group's S_dec as the scale rule of its amax
+        xf = F.bf16_to_f32(x) if x.dtype == np.uint16 else x.astype(np.float32)
+        for g in range(G):
+            r0, r1 = int(offsets[g]), int(offsets[g + 1])
+            a = np.float32(np.max(np.abs(xf[r0:r1]))) if r1 > r0 else np.float32(0.0)
+            if rowwise:
+                assert_f32_bits(f"group {g} row amax", f32(got["row_amax"])[g], a)
+                assert_f32_bits(f"group {g} row scale", f32(got["row_scale"])[g],
+                                oracle.global_scales(f32(got["row_amax"])[g])[1])
+            if colwise:
+                assert_f32_bits(f"group {g} scale", f32(got["scale"])[g],
+                                oracle.global_scales(f32(got["amax"])[g])[1])
     if colwise:
         # the tail past the last padded column is never written
         assert np.all(gc[:, mpad // 2:] == 0xAA) and np.all(gs[:, mpad // 16:] == 0x55)
@@ -858,6 +871,16 @@ def test_grouped_moe_16384x7168_sampled(gpu_lib):
     G = len(w.offsets) - 1
     _grouped_check(gpu_lib, w.x, w.offsets.tolist(), w.apply_rht, w.rht_mask, "sr", seed=w.seed,
                    offset=w.offset, groups=[0, 17, 40, G - 1])
+
+
+@pytest.mark.timeout(400)
+def test_grouped_moe_131072x7168_both_planes_sampled(gpu_lib):
+    """131072 tokens x hidden 7168 (1.9 GB of bf16) in 64 groups, both planes with their amax passes: the
+    workspace bounds no input size. Groups 0, 31 and 63 against the oracle (codes, scales, amax and S_dec of
+    both planes), every group's rowwise amax, every S_dec against its amax, the untouched tails."""
+    w = workloads.grouped_moe(tokens=131072)
+    _grouped_check(gpu_lib, w.x, w.offsets.tolist(), w.apply_rht, w.rht_mask, "sr", seed=w.seed,
+                   offset=w.offset, groups=[0, 31, 63], rowwise=True, amax_all=True)
 
 
 def test_grouped_moe_16384x7168_every_group_ends(gpu_lib):
