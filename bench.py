@@ -121,8 +121,7 @@ class Case:
         w = self.w
         d = {"workload": self.name, "rows": self.rows, "cols": self.cols, "rounding": w.rounding,
              "compulsory_bytes_per_step": self.bytes, "rotated_buffer_sets": self.nsets}
-        if self.dtype != "bf16":
-            d["input_dtype"] = self.dtype
+        d["input_dtype"] = self.dtype
         if self.name in ("prefill", "decode"):
             d.update({"tokens": self.rows, "hidden": self.cols, "op": "rmsnorm+nvfp4 rowwise",
                       "bias": w.beta is not None, "eps": w.eps})
@@ -184,28 +183,32 @@ class Case:
 
 
 # ----------------------------------------------------------------------------- timing
-def time_steps(case, steps, warmup, given=None, eager=False):
-    """Average ms per step over `steps` timed steps.
+def time_steps(case, steps, warmup, given=None, eager=False, passes=3):
+    """Median over `passes` timed passes of the average ms per step over `steps` steps.
 
     The steps are captured once in a HIP graph (the library allocates nothing and
-    records no memsets, so a call is capture-safe) and the graph is replayed
-    between two synchronizations with HIP events around it, on the stream the
+    records no memsets, so a call is capture-safe). A pass replays a graph of
+    `warmup` untimed steps and then the graph of `steps` timed steps between two
+    synchronizations, with HIP events around the timed replay on the stream the
     kernels run on. This removes the Python and launch overhead of each call,
     which would otherwise exceed the GPU time of a step. `eager` times plain
-    calls instead.
+    calls instead. Returns (median ms per step, the passes' ms per step).
     """
     torch = case.torch
+    per_pass = []
     if eager:
-        for i in range(warmup):
-            case.step(i, given)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            case.step(warmup + i, given)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        for _ in range(passes):
+            for i in range(warmup):
+                case.step(i, given)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                case.step(warmup + i, given)
+            e1.record()
+            torch.cuda.synchronize()
+            per_pass.append(e0.elapsed_time(e1) / steps)
+        return sorted(per_pass)[len(per_pass) // 2], per_pass
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -220,14 +223,28 @@ def time_steps(case, steps, warmup, given=None, eager=False):
             for i in range(steps):
                 case.step(i, given)
         torch.cuda.synchronize()
-        gw.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        gt.replay()
-        e1.record(s)
-        torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+        for _ in range(passes):
+            gw.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            gt.replay()
+            e1.record(s)
+            torch.cuda.synchronize()
+            per_pass.append(e0.elapsed_time(e1) / steps)
+    return sorted(per_pass)[len(per_pass) // 2], per_pass
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(case, budget_s=12.0):
@@ -323,7 +340,7 @@ def cpu_baseline(case, budget_s=12.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": sample + f"; {el:.1f} s, {done_bytes / 1e6:.1f} MB of compulsory bytes",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 # ----------------------------------------------------------------------------- roofline
@@ -550,25 +567,28 @@ def main():
             raise SystemExit("--stage-only needs a workload whose roofline kernel is timed alone")
         given = case.given(case.step(0))
         torch.cuda.synchronize()
-        kms = time_steps(case, args.steps, args.warmup, given=given, eager=args.eager)
-        log(f"[bench] {kname} alone (given amax): {kms * 1e3:.2f} us/launch")
+        kms, kpass = time_steps(case, args.steps, args.warmup, given=given, eager=args.eager)
+        log(f"[bench] {kname} alone (given amax): {kms * 1e3:.2f} us/launch (median of {len(kpass)} passes)")
         print(json.dumps({"stage_only": True, "config": case.describe(), "kernel": kname,
-                          "launch_us": round(kms * 1e3, 3), "bytes_per_launch": case.bytes}), flush=True)
+                          "launch_us": round(kms * 1e3, 3), "pass_us": [round(t * 1e3, 3) for t in kpass],
+                          "bytes_per_launch": case.bytes}), flush=True)
         return
 
     # whole step (amax + quantize), the figure the metric is quoted on
-    ms = time_steps(case, args.steps, args.warmup, eager=args.eager)
-    log(f"[bench] full step: {ms * 1e3:.2f} us/step")
+    ms, spass = time_steps(case, args.steps, args.warmup, eager=args.eager)
+    log(f"[bench] full step: {ms * 1e3:.2f} us/step (median of {len(spass)} passes: "
+        + ", ".join(f"{t * 1e3:.2f}" for t in spass) + ")")
     value = case.bytes / (ms * 1e-3) / 1e9
 
     if how == "stage":
         # the encode kernel alone against the amax the full step produced
         given = case.given(case.step(0))
         torch.cuda.synchronize()
-        kms = time_steps(case, args.steps, args.warmup, given=given, eager=args.eager)
-        log(f"[bench] {kname} alone (given amax): {kms * 1e3:.2f} us/launch")
+        kms, kpass = time_steps(case, args.steps, args.warmup, given=given, eager=args.eager)
+        log(f"[bench] {kname} alone (given amax): {kms * 1e3:.2f} us/launch (median of {len(kpass)} passes: "
+            + ", ".join(f"{t * 1e3:.2f}" for t in kpass) + ")")
     else:
-        kms = ms
+        kms, kpass = ms, spass
     achieved = case.bytes / (kms * 1e-3) / 1e9
     traffic = traffic_bytes(traffic_key(args.config, args.fast_math, args.planes, args.tile16, args.dtype))
     out = {
@@ -585,8 +605,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
-        "config": dict(case.describe(), timing="hip graph of `steps` steps, replayed once between syncs"
-                       if not args.eager else "eager calls"),
+        "config": dict(case.describe(), timing=("median of 3 passes; a pass replays a graph of `warmup` steps, "
+                                                "then times a graph of `steps` steps between syncs")
+                       if not args.eager else "median of 3 passes of `warmup` + `steps` eager calls"),
+        "pass_ms_per_step": [round(t, 5) for t in spass],
         "roofline": {
             "bound": "hbm",
             "kernel": kname + (" (one step)" if how == "step" else ", launched with a precomputed amax"),
@@ -596,6 +618,7 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": round(traffic) if traffic is not None else None,
             "launch_us": round(kms * 1e3, 3),
+            "pass_launch_us": [round(t * 1e3, 3) for t in kpass],
             "bytes_per_launch": case.bytes,
         },
     }

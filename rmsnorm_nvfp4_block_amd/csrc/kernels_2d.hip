@@ -37,8 +37,32 @@ __device__ __forceinline__ uint32_t swz_chunk(uint32_t chunk, uint32_t row) {
 // T threads per tile: 128 / (T / 8) rows (rowwise) and 1024 / T columns
 // (columnwise) per thread. TILE: one scale per 16 x 16 tile. DT: element type
 // of x (bf16, fp16 or fp32; an fp32 tile stages 64 KiB).
+// Tile order. Plain (gcols == 0): workgroup b takes tile b, row-major. Grouped
+// by XCD (gcols = column count of 4 x 4 tile groups): the dispatcher sends
+// workgroup b to XCD b mod 8, and the k-th workgroup of an XCD takes tile
+// k mod 16 (row-major) of group 8 (k / 16) + b mod 8, so the 16 tiles of a
+// 512 x 512 group run together on one XCD. Every 128-byte code line and every
+// 32 bytes of a scale row that the group writes then come from one L2, where
+// the pieces of neighbouring tiles merge before they leave it.
+struct TileOrder {
+  uint32_t tiles_r, tiles_c, gcols, ngroups;
+};
+__device__ __forceinline__ bool tile_of(const TileOrder o, uint32_t& tr, uint32_t& tc) {
+  const uint32_t b = blockIdx.x;
+  if (o.gcols == 0) {
+    tr = b / o.tiles_c;
+    tc = b - tr * o.tiles_c;
+    return tr < o.tiles_r;
+  }
+  const uint32_t k = b / kXcds, gi = (k / 16) * kXcds + b % kXcds, u = k % 16;
+  const uint32_t gr = gi / o.gcols, gc = gi - gr * o.gcols;
+  tr = gr * 4 + u / 4;
+  tc = gc * 4 + u % 4;
+  return gi < o.ngroups && tr < o.tiles_r && tc < o.tiles_c;
+}
+
 template <int T, bool ROW, bool COL, bool SR, bool TILE, int DT>
-__global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles_c, uint32_t ntiles, uint32_t chunk) {
+__global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, const TileOrder order) {
   constexpr int kRpt = kTileR / (T / 8);  // rows per thread
   constexpr int kRs = T / 8;              // row stride between a thread's rows
   constexpr int kCpt = 1024 / T;          // columns per thread (columnwise)
@@ -62,9 +86,8 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   const uint64_t seed = a.seed;
   const uint32_t offset = a.offset;
   const uint32_t t = threadIdx.x;
-  const uint32_t item = xcd_work_item(chunk);  // row-major tile index, contiguous per XCD
-  if (item >= ntiles) return;                  // idle: no barrier or partial depends on it
-  const uint32_t tr = item / tiles_c, tc = item - tr * tiles_c;
+  uint32_t tr, tc;
+  if (!tile_of(order, tr, tc)) return;  // idle: no barrier or partial depends on it
   const uint32_t row0 = tr * kTileR, col0 = tc * kTileC;
 
   // ---- load kRpt rows x one 16-element block per thread
@@ -212,16 +235,32 @@ __global__ __launch_bounds__(T) void k_quant_2d(const TwoDArgs a, uint32_t tiles
   }
 }
 
+// NVFP4Q_2D_ORDER=0 selects the plain row-major tile order (for comparison);
+// default: 4 x 4 tile groups per XCD.
+bool order_2d() {
+  static const bool v = [] {
+    const char* e = getenv("NVFP4Q_2D_ORDER");
+    return e == nullptr || atoi(e) != 0;
+  }();
+  return v;
+}
+
 template <int T, bool ROW, bool COL, bool TILE, int DT>
 void launch_2d_t(const TwoDArgs& a, hipStream_t s) {
-  const uint32_t tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
-  const uint32_t tiles_c = (uint32_t)((a.cols + kTileC - 1) / kTileC);
-  // Plain row-major tile order: the per-XCD ranges used by the grouped path
-  // measured slower here (8192 x 8192 with SR: 97.5 vs 91.3 us per step).
-  const uint32_t ntiles = tiles_r * tiles_c, chunk = 0;
-  dim3 grid(ntiles, a.experts), block(T);
-  if (a.sr) hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, true, TILE, DT>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
-  else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false, TILE, DT>), grid, block, 0, s, a, tiles_c, ntiles, chunk);
+  TileOrder o;
+  o.tiles_r = (uint32_t)((a.rows + kTileR - 1) / kTileR);
+  o.tiles_c = (uint32_t)((a.cols + kTileC - 1) / kTileC);
+  uint32_t wgs = o.tiles_r * o.tiles_c;
+  o.gcols = 0;
+  o.ngroups = 0;
+  if (order_2d()) {
+    o.gcols = (o.tiles_c + 3) / 4;
+    o.ngroups = (o.tiles_r + 3) / 4 * o.gcols;
+    wgs = (o.ngroups + kXcds - 1) / kXcds * kXcds * 16;
+  }
+  dim3 grid(wgs, a.experts), block(T);
+  if (a.sr) hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, true, TILE, DT>), grid, block, 0, s, a, o);
+  else hipLaunchKernelGGL((k_quant_2d<T, ROW, COL, false, TILE, DT>), grid, block, 0, s, a, o);
 }
 
 // 512 threads per tile (two rows and two columns each): the tile's LDS
