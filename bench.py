@@ -493,6 +493,154 @@ def copy_calibration(torch, nbytes, reps):
 
 
 # ----------------------------------------------------------------------------- main
+# ----------------------------------------------------------------------------- ceilings
+def _graph_time(torch, step, steps, warmup, passes=3):
+    """Median over `passes` of the ms per call of `step(i)`, captured `steps` times in a HIP graph
+    (the same protocol as time_steps)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    per = []
+    with torch.cuda.stream(s):
+        for i in range(3):
+            step(i, s)
+        torch.cuda.synchronize()
+        gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=s):
+            for i in range(max(warmup, 1)):
+                step(i, s)
+        with torch.cuda.graph(gt, stream=s):
+            for i in range(steps):
+                step(i, s)
+        torch.cuda.synchronize()
+        for _ in range(passes):
+            gw.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            gt.replay()
+            e1.record(s)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / steps)
+    return sorted(per)[len(per) // 2], per
+
+
+def ceilings(torch, steps, warmup):
+    """Probe kernels with the traffic of the library's passes and none of their arithmetic
+    (libnvfp4q_ceilings.so): what a pass of that shape can reach here. Prints one JSON line."""
+    import ctypes
+
+    path = os.path.join(ROOT, "rmsnorm_nvfp4_block_amd", "libnvfp4q_ceilings.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} not found: build it with `python -m rmsnorm_nvfp4_block_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, u64, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
+    lib.ceil_read.argtypes = [vp, u64, vp, vp]
+    lib.ceil_mix.argtypes = [vp, u64, vp, vp, vp]
+    lib.ceil_fused.argtypes = [vp, u32, vp, vp, vp, u32, vp]
+    lib.ceil_rowmix.argtypes = [vp, u32, vp, vp, vp]
+    lib.ceil_fused_ws_bytes.restype = u64
+    lib.ceil_empty.argtypes = [u32, u32, ctypes.c_int, vp]
+    for f in (lib.ceil_read, lib.ceil_mix, lib.ceil_rowmix, lib.ceil_fused, lib.ceil_empty):
+        f.restype = ctypes.c_int
+
+    def ok(rc, what):
+        if rc != 0:
+            raise SystemExit(f"{what}: hip error {rc}")
+
+    out = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    results = []
+
+    def record(name, shape, nbytes, ms, per, **extra):
+        r = {"probe": name, "shape": shape, "bytes": nbytes, "us": round(ms * 1e3, 3),
+             "pass_us": [round(t * 1e3, 3) for t in per], "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+             "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        r.update(extra)
+        results.append(r)
+        log(f"[ceilings] {name:9s} {shape:12s} {r['us']:9.2f} us  {r['GBps']:8.1f} GB/s  ({r['frac']:.3f} of peak)")
+
+    for rows, cols in ((4096, 4096), (8192, 8192), (16384, 7168)):
+        shape = f"{rows}x{cols}"
+        xb = rows * cols * 2
+        nsets = max(2, -(-ROTATE_BYTES // xb))
+        xs = [torch.empty(xb // 2, dtype=torch.int16, device="cuda").random_(-32768, 32767) for _ in range(nsets)]
+        nblk = rows * cols // 16
+        cs = [torch.empty(nblk * 8, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+        ss = [torch.empty(nblk, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+
+        def rd(i, st):
+            ok(lib.ceil_read(xs[i % nsets].data_ptr(), xb, out.data_ptr(), st.cuda_stream), "ceil_read")
+
+        def mx(i, st):
+            j = i % nsets
+            ok(lib.ceil_mix(xs[j].data_ptr(), nblk, cs[j].data_ptr(), ss[j].data_ptr(), st.cuda_stream), "ceil_mix")
+
+        def two(i, st):
+            rd(i, st)
+            mx(i, st)
+
+        ms, per = _graph_time(torch, rd, steps, warmup)
+        record("read", shape, xb, ms, per, pattern="one 8 KiB span per wave (64 lanes x 8 loads of 16 B)")
+        ms, per = _graph_time(torch, mx, steps, warmup)
+        record("mix", shape, nblk * 41, ms, per,
+               pattern="per 16-element block: 2 x 16 B loads, 8 B + 1 B non-temporal stores")
+        if (rows, cols) == (4096, 4096):
+            ms, per = _graph_time(torch, two, steps, warmup)
+            record("two-pass", shape, xb + nblk * 41, ms, per,
+                   pattern="read, then mix over the same x (two launches per step)")
+
+            def rmx(i, st):
+                j = i % nsets
+                ok(lib.ceil_rowmix(xs[j].data_ptr(), rows, cs[j].data_ptr(), ss[j].data_ptr(), st.cuda_stream),
+                   "ceil_rowmix")
+
+            def two_rows(i, st):
+                rd(i, st)
+                rmx(i, st)
+
+            ms, per = _graph_time(torch, rmx, steps, warmup)
+            record("rowmix", shape, nblk * 41, ms, per,
+                   pattern="the mix traffic in the rowwise encode's layout (one row per wave, 8 loads in flight)")
+            ms, per = _graph_time(torch, two_rows, steps, warmup)
+            record("two-pass-rows", shape, xb + nblk * 41, ms, per,
+                   pattern="read, then rowmix over the same x: each row on the same wave (and XCD) in both")
+            ws = torch.zeros(lib.ceil_fused_ws_bytes(), dtype=torch.uint8, device="cuda")
+
+            def fused(i, st):
+                j = i % nsets
+                ok(lib.ceil_fused(xs[j].data_ptr(), rows, cs[j].data_ptr(), ss[j].data_ptr(), ws.data_ptr(),
+                                  1 << 20, st.cuda_stream), "ceil_fused")
+
+            ms, per = _graph_time(torch, fused, steps, warmup)
+            err = int(ws[4:8].view(torch.int32).item())
+            record("fused", shape, xb + nblk * 9, ms, per, wait_gave_up=bool(err),
+                   pattern="one launch: rows in registers, grid-wide maximum through per-workgroup slots, stores")
+        del xs, cs, ss
+        torch.cuda.empty_cache()
+
+    # launch cost of an empty 1024 x 256 kernel: in a graph, and eager (plain vs cooperative)
+    n = 200
+    ms, per = _graph_time(torch, lambda i, st: ok(lib.ceil_empty(1, 1024, 0, st.cuda_stream), "ceil_empty"),
+                          n, warmup)
+    launches = {"graph_plain_us": round(ms * 1e3, 3)}
+    for coop in (0, 1):
+        st = torch.cuda.Stream()
+        ok(lib.ceil_empty(8, 1024, coop, st.cuda_stream), "ceil_empty")
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            ok(lib.ceil_empty(n, 1024, coop, st.cuda_stream), "ceil_empty")
+            e1.record(st)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) / n)
+        launches["eager_cooperative_us" if coop else "eager_plain_us"] = round(sorted(t)[1] * 1e3, 3)
+    log(f"[ceilings] empty 1024x256 kernel per launch: {launches}")
+    print(json.dumps({"ceilings": results, "empty_kernel_launch": launches, "steps": steps, "warmup": warmup,
+                      "timing": "median of 3 passes of a graph of `steps` calls (launch costs: see keys)"}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -511,6 +659,8 @@ def main():
     ap.add_argument("--stage-only", action="store_true",
                     help="time only the roofline kernel with a given amax (for kernel traces); no metric line")
     ap.add_argument("--eager", action="store_true", help="time plain calls instead of a HIP graph replay")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only run the probe kernels (read, traffic mix, two-pass, one-launch barrier, launch cost)")
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES",
                     help="only run plain copies of BYTES (for the counter calibration runs)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -541,6 +691,10 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration, 8)
+        return
+    if args.ceilings:
+        torch.cuda.set_device(0)
+        ceilings(torch, args.steps, args.warmup)
         return
 
     import rmsnorm_nvfp4_block_amd as q

@@ -2,7 +2,9 @@
 
 Usage: ``python -m rmsnorm_nvfp4_block_amd.build`` (or ``build()`` from Python).
 Each ``.hip`` translation unit is compiled in parallel into ``_build/`` and
-linked into ``rmsnorm_nvfp4_block_amd/libnvfp4q.so``. Flags: -O3, gfx950 only,
+linked into ``rmsnorm_nvfp4_block_amd/libnvfp4q.so``; the measurement probes
+(``csrc/ceilings.hip``, used only by ``bench.py --ceilings``) go into
+``libnvfp4q_ceilings.so`` beside it. Flags: -O3, gfx950 only,
 no FMA contraction (the quantizer's products must round on their own), NaN
 handling off (inputs are finite by contract; it removes NaN canonicalization
 around max), and the packed-FP32 feature disabled for all device code.
@@ -20,6 +22,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnvfp4q.so")
+CEIL_LIB = os.path.join(HERE, "libnvfp4q_ceilings.so")
+CEIL_SOURCES = ["ceilings.hip"]
 SOURCES = [
     "api.hip", "kernels_rows.hip", "kernels_rms_coop.hip",
     "kernels_rms_stream.hip",
@@ -50,18 +54,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEIL_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CEIL_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CEIL_LIB)
     return LIB
 
 

@@ -297,3 +297,19 @@ def test_rmsnorm_noalloc_validation(lib):
     assert call(hidden=40) == 2
     assert call(p=q.Plane(None, 0, None, 0)) == 1
     assert call(rnd=2) == 4
+
+
+def test_ceilings_probe_library_exports():
+    """The probe kernels bench.py --ceilings runs are built beside the library and export their entry points."""
+    import ctypes
+    import os
+
+    import rmsnorm_nvfp4_block_amd as q
+
+    path = os.path.join(os.path.dirname(q.lib_path), "libnvfp4q_ceilings.so")
+    assert os.path.exists(path), "build the library first"
+    lib = ctypes.CDLL(path)
+    for name in ("ceil_read", "ceil_mix", "ceil_rowmix", "ceil_fused", "ceil_fused_ws_bytes", "ceil_empty"):
+        assert hasattr(lib, name), name
+    lib.ceil_fused_ws_bytes.restype = ctypes.c_uint64
+    assert lib.ceil_fused_ws_bytes() == 128 + 8 * 4096
