@@ -82,7 +82,9 @@ typedef enum {
   NVFP4Q_E_ALIGN = 3,       /* a pointer or leading dimension breaks the alignment rules */
   NVFP4Q_E_UNSUPPORTED = 4, /* dtype, rounding mode or option not built */
   NVFP4Q_E_LAUNCH = 5,      /* a kernel launch failed on the HIP side */
-  NVFP4Q_E_WORKSPACE = 6    /* workspace missing, misaligned or too small */
+  NVFP4Q_E_WORKSPACE = 6,   /* workspace missing, misaligned or too small */
+  NVFP4Q_STATUS_MAX_ENUM = 0x7FFFFFFF /* not a status: every enum here is a 32-bit
+                                         type that holds any non-negative int */
 } nvfp4q_status;
 
 /* Element type of the input; every entry point takes all three. The
@@ -92,7 +94,7 @@ typedef enum {
  * round their output y to nearest even in that type (fp32: not rounded
  * further); rmsnorm_nvfp4q quantizes that y. Rows of x (and y) start 16-byte
  * aligned: leading dimension * element size is a multiple of 16. */
-typedef enum { NVFP4Q_BF16 = 0, NVFP4Q_FP16 = 1, NVFP4Q_FP32 = 2 } nvfp4q_dtype;
+typedef enum { NVFP4Q_BF16 = 0, NVFP4Q_FP16 = 1, NVFP4Q_FP32 = 2, NVFP4Q_DTYPE_MAX_ENUM = 0x7FFFFFFF } nvfp4q_dtype;
 
 /* Rounding of the E2M1 codes. NVFP4Q_FAST_MATH may be OR-ed into the value
  * passed as `rounding` ([PR, Fast math]): with the grouped transform on, the
@@ -101,7 +103,7 @@ typedef enum { NVFP4Q_BF16 = 0, NVFP4Q_FP16 = 1, NVFP4Q_FP32 = 2 } nvfp4q_dtype;
  * comes from a 127-entry table per workgroup, so an approximate reciprocal
  * would save nothing). On paths without the transform the flag changes
  * nothing. Other bits: NVFP4Q_E_UNSUPPORTED. */
-typedef enum { NVFP4Q_RTNE = 0, NVFP4Q_SR = 1 } nvfp4q_rounding;
+typedef enum { NVFP4Q_RTNE = 0, NVFP4Q_SR = 1, NVFP4Q_ROUNDING_MAX_ENUM = 0x7FFFFFFF } nvfp4q_rounding;
 #define NVFP4Q_FAST_MATH 0x100
 /* nvfp4q_quantize_2d only (other entry points: NVFP4Q_E_UNSUPPORTED): one
  * E4M3 scale per 16 x 16 tile of x, used by both planes, so that a weight and
@@ -140,7 +142,8 @@ typedef struct {
 /* Bytes of workspace every entry point needs (a constant, 1 MiB). */
 size_t nvfp4q_workspace_bytes(void);
 
-/* Static description of a status code; never NULL. */
+/* Static description of a status code (any int value; unknown ones get
+ * "unknown status"); never NULL. */
 const char *nvfp4q_status_string(nvfp4q_status s);
 
 /* ABI version: 1. */

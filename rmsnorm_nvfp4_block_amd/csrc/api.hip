@@ -8,6 +8,7 @@
 
 #include <cstddef>
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 using namespace nvfp4q;
@@ -181,7 +182,9 @@ size_t nvfp4q_workspace_bytes(void) { return sizeof(Workspace); }
 int nvfp4q_version(void) { return 1; }
 
 const char* nvfp4q_status_string(nvfp4q_status s) {
-  switch (s) {
+  int v;  // read as an int: a caller may pass any code
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case NVFP4Q_OK: return "ok";
     case NVFP4Q_E_NULLPTR: return "a required pointer is NULL";
     case NVFP4Q_E_SHAPE: return "a size or leading dimension breaks the shape rules";

@@ -306,7 +306,7 @@ def test_ceilings_probe_library_exports():
 
     import rmsnorm_nvfp4_block_amd as q
 
-    path = os.path.join(os.path.dirname(q.lib_path), "libnvfp4q_ceilings.so")
+    path = os.path.join(os.path.dirname(os.path.abspath(q.__file__)), "libnvfp4q_ceilings.so")
     assert os.path.exists(path), "build the library first"
     lib = ctypes.CDLL(path)
     for name in ("ceil_read", "ceil_mix", "ceil_rowmix", "ceil_fused", "ceil_fused_ws_bytes", "ceil_empty"):
