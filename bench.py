@@ -432,6 +432,13 @@ def ingest_pmc(config, fetch_dir, write_dir, command, key=None):
                 k = entry["kernels"].setdefault(name.split("(")[0], {})
                 k[counter.lower() + "_kib"] = sum(vals) / len(vals)
                 k["dispatches"] = len(vals)
+    # the library's other kernels of the same run (the full step's passes), for reference only
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for name, vals in read_pmc(d, counter).items():
+            if "nvfp4q::" in name and not pat.search(name):
+                k = entry.setdefault("other_kernels", {}).setdefault(name.split("(")[0], {})
+                k[counter.lower() + "_kib"] = sum(vals) / len(vals)
+                k["dispatches"] = len(vals)
     if not entry["kernels"]:
         raise SystemExit("no dispatch of the dominant kernel in the counter files")
     if DOMINANT[config][0] == "stage" and len(entry["kernels"]) != 1:

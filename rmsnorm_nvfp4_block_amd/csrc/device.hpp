@@ -208,8 +208,11 @@ __device__ __forceinline__ uint32_t rand_second(uint32_t w) {
 // for the second elements (high nibbles kept).
 __device__ __forceinline__ uint32_t sr_pack8(const float v[8], uint32_t w0, uint32_t w1) {
   const f32x2 p0 = {v[0], v[1]}, p1 = {v[2], v[3]}, p2 = {v[4], v[5]}, p3 = {v[6], v[7]};
-  uint32_t a = sr_byte<0>(0u, p0, rand_first<0>(w0));
-  uint32_t b = sr_byte<0>(0u, p0, rand_second<1>(w0));
+  // every byte of a and b is written below, so their first `old` can be any
+  // value: the random operand itself, which is dead afterwards (no copy of a zero)
+  const uint32_t ra = rand_first<0>(w0), rb = rand_second<1>(w0);
+  uint32_t a = sr_byte<0>(ra, p0, ra);
+  uint32_t b = sr_byte<0>(rb, p0, rb);
   a = sr_byte<1>(a, p1, rand_first<2>(w0));
   b = sr_byte<1>(b, p1, rand_second<3>(w0));
   a = sr_byte<2>(a, p2, rand_first<0>(w1));
@@ -221,7 +224,8 @@ __device__ __forceinline__ uint32_t sr_pack8(const float v[8], uint32_t w0, uint
 
 // Eight RTNE codes packed in a word.
 __device__ __forceinline__ uint32_t rtne_pack8(const float v[8]) {
-  uint32_t out = 0;
+  // every byte is written, so the first `old` can be any value: v[0]'s bits
+  uint32_t out = __float_as_uint(v[0]);
   out = e2m1x2<0>(out, v[0], v[1]);
   out = e2m1x2<1>(out, v[2], v[3]);
   out = e2m1x2<2>(out, v[4], v[5]);
