@@ -199,6 +199,13 @@ __device__ __forceinline__ uint32_t rand_first(uint32_t w) {
 // element, which the instruction shifts left by one).
 template <int K>
 __device__ __forceinline__ uint32_t rand_second(uint32_t w) {
+  if constexpr (K == 1) {
+    // one shift with the byte selected as its source operand (SDWA)
+    uint32_t r;
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(23u), "v"(w));
+    return r;
+  }
   return ((w >> (8 * K)) & 0xFFu) << 23;
 }
 

@@ -536,17 +536,24 @@ __device__ __forceinline__ void write_item(const Stage<CPL>& st, uint32_t ctile,
                                            uint32_t mpad, int64_t cap, uint8_t* __restrict__ codes, int64_t ldc,
                                            uint8_t* __restrict__ scales, int64_t lds) {
   constexpr int kRows = 32 * CPL;
+  constexpr int kRowStep = kQuantThreads / kItemBlocks;  // plane rows between a thread's stores
   const uint32_t row0 = ctile * kRows, blkb = bg * kItemBlocks;
   const int64_t nvalid = min((int64_t)(mpad >> 4), cap >> 4) - (int64_t)blkb;  // valid blocks of the item
+  // thread t: block jj = t mod 8 of plane rows t / 8 + 32 k; the byte offsets advance by whole row steps
+  const uint32_t rr0 = threadIdx.x / kItemBlocks, jj = threadIdx.x % kItemBlocks;
+  const bool jok = (int64_t)jj < nvalid;
+  int64_t co = (int64_t)(row0 + rr0) * ldc + (int64_t)(blkb + jj) * 8;
+  int64_t so = (int64_t)(row0 + rr0) * lds + blkb + jj;
+  const int64_t cstep = (int64_t)kRowStep * ldc, sstep = (int64_t)kRowStep * lds;
 #pragma unroll
-  for (int k = 0; k < kRows * kItemBlocks / kQuantThreads; ++k) {
-    const uint32_t i = threadIdx.x + k * kQuantThreads;
-    const uint32_t rr = i / kItemBlocks, jj = i % kItemBlocks;
-    if (row0 + rr < cols && (int64_t)jj < nvalid) {
-      *reinterpret_cast<uint2*>(codes + (int64_t)(row0 + rr) * ldc + (int64_t)(blkb + jj) * 8) =
-          *reinterpret_cast<const uint2*>(st.codes + rr * kStagePitch + jj * 8);
-      scales[(int64_t)(row0 + rr) * lds + blkb + jj] = st.scales[rr * kItemBlocks + jj];
+  for (int k = 0; k < kRows / kRowStep; ++k) {
+    const uint32_t rr = rr0 + k * kRowStep;
+    if (jok && row0 + rr < cols) {
+      *reinterpret_cast<uint2*>(codes + co) = *reinterpret_cast<const uint2*>(st.codes + rr * kStagePitch + jj * 8);
+      scales[so] = st.scales[rr * kItemBlocks + jj];
     }
+    co += cstep;
+    so += sstep;
   }
 }
 
