@@ -40,12 +40,14 @@ def log(*a):
 class Case:
     """Device buffers and launch closures for one workload."""
 
-    def __init__(self, name, torch, q, workloads, fast_math=False, planes="col", tile16=False, dtype="bf16"):
+    def __init__(self, name, torch, q, workloads, fast_math=False, planes="col", tile16=False, dtype="bf16",
+                 one_launch=False):
         import numpy as np
 
         self.name = name
         self.fast_math = fast_math
         self.planes = planes  # grouped: which planes a step writes
+        self.one_launch = one_launch
         self.tile16 = tile16  # weight: one scale per 16 x 16 tile
         self.dtype = dtype    # element type of the input
         tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
@@ -125,6 +127,8 @@ class Case:
         if self.name in ("prefill", "decode"):
             d.update({"tokens": self.rows, "hidden": self.cols, "op": "rmsnorm+nvfp4 rowwise",
                       "bias": w.beta is not None, "eps": w.eps})
+            if self.one_launch:
+                d["one_launch"] = "NVFP4Q_ONE_LAUNCH: the amax found inside one launch (at most 64 tokens)"
         elif self.name == "qknorm":
             d.update({"op": "per-head RMSNorm of q and k in place (QK norm)", "tokens": self.rows,
                       "q_heads": self.cols // w.meta["head_dim"], "k_heads": w.meta["k"].shape[1] // w.meta["head_dim"],
@@ -163,7 +167,8 @@ class Case:
         x = self.xs[i % self.nsets]
         o = self.outs[i % self.nsets]
         if self.name in ("prefill", "decode"):
-            return q.rmsnorm_nvfp4q(x, self.gamma, self.beta, eps=w.eps, amax=amax, codes=o[0], scales=o[1])
+            return q.rmsnorm_nvfp4q(x, self.gamma, self.beta, eps=w.eps, amax=amax, codes=o[0], scales=o[1],
+                                    one_launch=self.one_launch)
         if self.name == "quantize":
             return q.nvfp4q_quantize(x, amax=amax, codes=o[0], scales=o[1])
         if self.name == "weight":
@@ -662,6 +667,8 @@ def main():
                     help="weight: NVFP4Q_SCALE_16X16 (one block scale per 16x16 tile, shared by both planes)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16", "fp32"],
                     help="element type of the input (the workload's values, converted exactly)")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="prefill/decode: NVFP4Q_ONE_LAUNCH (one launch meeting on the amax inside it, <= 64 tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-only", action="store_true",
                     help="time only the roofline kernel with a given amax (for kernel traces); no metric line")
@@ -717,8 +724,10 @@ def main():
         raise SystemExit("--fast-math concerns the transform, which the rowwise plane does not take")
     if args.tile16 and args.config not in ("weight", "experts"):
         raise SystemExit("--tile16 applies to the weight and experts workloads (the 2D path)")
+    if args.one_launch and args.config not in ("prefill", "decode"):
+        raise SystemExit("--one-launch applies to the RMSNorm workloads (prefill, decode)")
     case = Case(args.config, torch, q, workloads, fast_math=args.fast_math, planes=args.planes, tile16=args.tile16,
-                dtype=args.dtype)
+                dtype=args.dtype, one_launch=args.one_launch)
     log(f"[bench] {case.describe()}")
 
     how, kname, _ = DOMINANT[args.config]

@@ -41,14 +41,16 @@
  *     synchronizes; all work is enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream), so calls may be captured in a HIP graph.
  *   - `workspace` is device scratch memory of at least nvfp4q_workspace_bytes()
- *     bytes (1 MiB), 256-byte aligned, owned by the caller. Its contents need no
- *     initialization and carry nothing from one call to the next (an amax pass
- *     writes per-workgroup partial maxima there, and for RMSNorm each row's
- *     1/rms, and the encode pass of the same call reads them; every slot read
- *     is written earlier in the same call), so one workspace serves any number
- *     of calls that
- *     are ordered on one stream; calls that can run at the same time (different
- *     streams) need different workspaces.
+ *     bytes (1 MiB), 256-byte aligned, owned by the caller. Its first 640
+ *     bytes hold the state of NVFP4Q_ONE_LAUNCH calls: before the first such
+ *     call they must hold zeros (any one 32-bit value repeated also works),
+ *     and from then on only the library writes them. The rest needs no
+ *     initialization and carries nothing from one call to the next (an amax
+ *     pass writes per-workgroup partial maxima there, and for RMSNorm each
+ *     row's 1/rms, and the encode pass of the same call reads them; every such
+ *     slot read is written earlier in the same call). One workspace serves any
+ *     number of calls that are ordered on one stream; calls that can run at
+ *     the same time (different streams) need different workspaces.
  *   - Errors are returned synchronously, before anything is enqueued, except
  *     NVFP4Q_E_LAUNCH. Device-side data that break a stated rule (for example
  *     decreasing group offsets) give unspecified output but no out-of-bounds
@@ -109,6 +111,17 @@ typedef enum { NVFP4Q_RTNE = 0, NVFP4Q_SR = 1, NVFP4Q_ROUNDING_MAX_ENUM = 0x7FFF
  * E4M3 scale per 16 x 16 tile of x, used by both planes, so that a weight and
  * its transpose decode to the same values. */
 #define NVFP4Q_SCALE_16X16 0x200
+/* rmsnorm_nvfp4q and rmsnorm_nvfp4q_noalloc only (other entry points:
+ * NVFP4Q_E_UNSUPPORTED): with codes, at most 64 tokens and no given amax, one
+ * launch (one workgroup per token) whose workgroups meet on the amax inside
+ * it ([Blog] Grid synchronization) instead of an amax pass and an encode pass;
+ * same results. It keeps state in the workspace's first 640 bytes (see the
+ * workspace convention). Measured on MI355X it is not faster than the two
+ * launches (8 x 7168 with a bias, graph replay: 6.87 us per call against
+ * 6.86 us; the wait for every workgroup's maximum costs what the second
+ * launch does), so it is an option, not the default; otherwise it changes
+ * nothing. */
+#define NVFP4Q_ONE_LAUNCH 0x400
 
 /* One quantized plane. codes: device, [plane_rows][ld_codes] bytes, two E2M1
  * codes per byte, even element in the low nibble. scales: device,
@@ -191,7 +204,8 @@ nvfp4q_status nvfp4q_quantize(const void *x, nvfp4q_dtype dtype, int64_t rows, i
  *   rounding / rng as for nvfp4q_quantize.
  *   g: as for nvfp4q_quantize; with g->amax_in the call is one pass over x
  *     (the amax is not computed), otherwise an amax pass precedes the encode
- *     pass. hidden <= 16384 (NVFP4Q_E_UNSUPPORTED above that).
+ *     pass (or, with NVFP4Q_ONE_LAUNCH and at most 64 tokens, one launch).
+ *     hidden <= 16384 (NVFP4Q_E_UNSUPPORTED above that).
  */
 nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, int64_t hidden,
                              int64_t ld_x, const void *gamma, const void *beta, float weight_offset,
@@ -208,8 +222,9 @@ nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, 
  * and errors are those of rmsnorm_nvfp4q (the same kernels run); nothing is
  * allocated or freed, and every shape rmsnorm_nvfp4q accepts fits the array
  * (that path needs a constant 1 MiB). The array exists once per GPU, is held
- * until the process ends, and keeps the last call's contents, which no call
- * reads before writing them; calls that can overlap on one GPU (different
+ * until the process ends, starts as zeros, and keeps the last call's contents
+ * (its first 640 bytes the NVFP4Q_ONE_LAUNCH state, as for a workspace; no
+ * call reads the rest before writing it); calls that can overlap on one GPU (different
  * streams, or different host threads on one device) race on it and must not
  * be issued. NVFP4Q_E_LAUNCH if the array's device address cannot be looked
  * up on the current device.

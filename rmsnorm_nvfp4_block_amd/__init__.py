@@ -28,6 +28,7 @@ SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_qu
 RTNE, SR = 0, 1
 FAST_MATH = 0x100  # NVFP4Q_FAST_MATH, OR-ed into the rounding argument
 SCALE_16X16 = 0x200  # NVFP4Q_SCALE_16X16 (nvfp4q_quantize_2d only), OR-ed into the rounding argument
+ONE_LAUNCH = 0x400  # NVFP4Q_ONE_LAUNCH (the RMSNorm entry points only), OR-ed into the rounding argument
 
 
 class Plane(ctypes.Structure):
@@ -105,10 +106,10 @@ _ws = {}
 
 
 def _alloc_workspace(dev):
-    """Device memory for one workspace (torch's allocator; the library needs no initialization of it)."""
+    """Device memory for one workspace from torch's allocator, zero-filled as the C ABI asks before first use."""
     import torch
 
-    return torch.empty(max(nvfp4q_workspace_bytes(), 4096), dtype=torch.uint8, device=dev)
+    return torch.zeros(max(nvfp4q_workspace_bytes(), 4096), dtype=torch.uint8, device=dev)
 
 
 def workspace(device=None, stream=None):
@@ -192,9 +193,10 @@ def nvfp4q_quantize(x, amax=None, rounding="rtne", seed=0, offset=0, codes=None,
 
 
 def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, rounding="rtne", seed=0, offset=0,
-                   y_out=False, quantize=True, codes=None, scales=None):
+                   y_out=False, quantize=True, codes=None, scales=None, one_launch=False):
     """RMSNorm of x [tokens, hidden] (bf16, fp16 or fp32; gamma and beta of the same type) then rowwise NVFP4
-    of the output rounded in that type.
+    of the output rounded in that type. one_launch: NVFP4Q_ONE_LAUNCH (at most 64 tokens and no given amax:
+    one launch that meets on the amax inside it; same results).
 
     Returns dict(codes, scales, amax, scale, y) (y only when y_out=True).
     """
@@ -217,14 +219,15 @@ def rmsnorm_nvfp4q(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, 
     st = lib.rmsnorm_nvfp4q(x.data_ptr(), dt, T, H, x.stride(0), gamma.data_ptr(), _ptr(beta),
                             float(weight_offset), float(eps), _ptr(y), y.stride(0) if y is not None else 0,
                             ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(plane),
-                            _rounding(rounding), ctypes.byref(Rng(seed, offset)), ws.data_ptr(), ws.numel(),
-                            _stream(x))
+                            _rounding(rounding) | (ONE_LAUNCH if one_launch else 0), ctypes.byref(Rng(seed, offset)),
+                            ws.data_ptr(), ws.numel(), _stream(x))
     _check(st)
     return {"codes": c, "scales": s, "amax": amax_out, "scale": scale_out, "y": y}
 
 
 def rmsnorm_nvfp4q_noalloc(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, amax=None, rounding="rtne", seed=0,
-                           offset=0, y_out=None, codes=None, scales=None, amax_out=None, scale_out=None):
+                           offset=0, y_out=None, codes=None, scales=None, amax_out=None, scale_out=None,
+                           one_launch=False):
     """rmsnorm_nvfp4q through the entry point that allocates nothing (the library's static workspace).
 
     Outputs are the caller's: pass y_out, codes / scales, amax_out / scale_out tensors to make the call
@@ -248,7 +251,8 @@ def rmsnorm_nvfp4q_noalloc(x, gamma, beta=None, weight_offset=0.0, eps=1e-6, ama
                                     float(weight_offset), float(eps), _ptr(y_out),
                                     y_out.stride(0) if y_out is not None else 0,
                                     ctypes.byref(_global(amax, amax_out, scale_out)), ctypes.byref(plane),
-                                    _rounding(rounding), ctypes.byref(Rng(seed, offset)), _stream(x))
+                                    _rounding(rounding) | (ONE_LAUNCH if one_launch else 0),
+                                    ctypes.byref(Rng(seed, offset)), _stream(x))
     _check(st)
     return {"codes": c, "scales": s, "amax": amax_out, "scale": scale_out, "y": y_out}
 

@@ -84,6 +84,7 @@ bool rms_stream_enabled() {
   return on;
 }
 
+
 // The no-allocation entry point's workspace: a file-scope device array, one
 // per GPU (each device that loads the library holds its own copy until the
 // process ends). Host code never passes the array's name to a kernel (on the
@@ -121,6 +122,8 @@ nvfp4q_status rmsnorm_impl(const void* x, nvfp4q_dtype dtype, int64_t tokens, in
                            const nvfp4q_rng* rng, void* workspace, size_t workspace_bytes, bool use_static,
                            void* stream) {
   TRY(check_input(x, dtype, tokens, hidden, ld_x, true));
+  const bool one_launch = ((int)rounding & NVFP4Q_ONE_LAUNCH) != 0;
+  rounding = (nvfp4q_rounding)((int)rounding & ~NVFP4Q_ONE_LAUNCH);
   if (!gamma) return NVFP4Q_E_NULLPTR;
   if (!aligned(gamma, 16) || !aligned(beta, 16)) return NVFP4Q_E_ALIGN;
   if (weight_offset != 0.0f && weight_offset != 1.0f) return NVFP4Q_E_UNSUPPORTED;
@@ -149,6 +152,9 @@ nvfp4q_status rmsnorm_impl(const void* x, nvfp4q_dtype dtype, int64_t tokens, in
   a.amax_in = gg.amax_in; a.amax_out = gg.amax_out; a.scale_out = gg.scale_out;
   a.sr = base_rounding(rounding) == NVFP4Q_SR;
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
+  // NVFP4Q_ONE_LAUNCH, a few rows and no given amax: one launch whose
+  // workgroups meet on the amax inside it.
+  if (one_launch && codes && !a.amax_in && tokens <= rms_fused_max_rows()) return done(launch_rms_fused(a, s));
   // With the amax pass and a row count that fits the workspace's row-scale
   // slots, the encode pass streams rows using the 1/rms the amax pass stored.
   const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled();

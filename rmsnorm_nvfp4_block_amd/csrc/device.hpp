@@ -23,18 +23,27 @@ constexpr float kFltMax = 3.40282347e+38f;
 // An amax pass writes one partial maximum per workgroup into `partial` with a
 // plain store; the encode pass that follows reduces the partials it needs at its
 // start (the kernel boundary orders the two). Every slot an encode pass reads is
-// written earlier in the same call, so the buffer carries no state between
-// calls and needs no reset, and no workgroup waits on another.
+// written earlier in the same call, so `partial` carries no state between
+// calls and needs no reset.
 //
 // The rowwise RMSNorm amax pass launches at most kRowPartials workgroups and
 // also leaves each row's 1/rms in partial[kRowPartials + row] (rows up to
 // kRowScaleCap), so that the encode pass can stream the row in pieces.
-constexpr int kPartials = 262144 - 32;
+//
+// The one-launch RMSNorm for a few rows (at most kBarrierSlots workgroups, all
+// resident at once) meets inside the kernel instead (grid_max below): status[0]
+// counts its completed calls, slot[w] holds (that count + 1, workgroup w's
+// maximum), status[1] is set if a wait ever gave up. These words carry state
+// from call to call: they must start equal (zeros) and only that kernel
+// writes them.
+constexpr int kBarrierSlots = 64;
+constexpr int kPartials = 262144 - 32 - 2 * kBarrierSlots;
 constexpr int kRowPartials = 4096;
 constexpr int kRowScaleCap = kPartials - kRowPartials;
 struct Workspace {
-  uint32_t status[32];          // reserved (one 128-byte line)
-  float partial[kPartials];     // per-workgroup partial maxima of the last amax pass
+  uint32_t status[32];             // [0] one-launch calls completed, [1] a wait gave up; the rest reserved
+  uint64_t slot[kBarrierSlots];    // one-launch: (calls completed + 1) << 32 | the workgroup's maximum
+  float partial[kPartials];        // per-workgroup partial maxima of the last amax pass
 };
 static_assert(sizeof(Workspace) == 1 << 20, "workspace layout");
 
@@ -433,6 +442,50 @@ __device__ __forceinline__ void publish_partial(Workspace* ws, float m) {
 __device__ __forceinline__ void publish_partial_at(Workspace* ws, float m, uint32_t slot) {
   m = wg_max(m);
   if (threadIdx.x == 0) ws->partial[slot] = m;
+}
+
+// ---------------------------------------------------------------- one launch
+// The maximum of m over all workgroups of a launch, inside the launch ("CuTeDSL
+// at Perplexity", Grid synchronization), for launches of at most kBarrierSlots
+// workgroups that are all resident at once. Every workgroup read `epoch` =
+// status[0] at its start; it publishes (epoch + 1, its maximum) in its slot
+// with one device-scope atomic store, and its first wave polls every slot with
+// device-scope atomic loads until all carry epoch + 1 (non-negative floats
+// compare like their bit patterns). Workgroup 0 then advances status[0]: every
+// workgroup has read the old value before any slot can show the new one. A
+// wait is bounded by spin_limit polls; past it status[1] is set and the
+// maximum of the slots seen is used (the output is then unspecified, but every
+// wave ends). All threads call; m >= 0.
+__device__ __forceinline__ float grid_max(Workspace* ws, uint32_t epoch, float m, uint32_t spin_limit) {
+  __shared__ float gm;
+  m = wg_max(m);
+  const uint32_t tag = epoch + 1u;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&ws->slot[blockIdx.x], ((uint64_t)tag << 32) | __float_as_uint(m), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x < 64) {
+    const uint32_t lane = threadIdx.x;
+    bool done = lane >= gridDim.x;
+    uint64_t v = 0;
+    for (uint32_t spins = 0;; ++spins) {
+      if (!done) {
+        v = __hip_atomic_load(&ws->slot[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        done = (uint32_t)(v >> 32) == tag;
+      }
+      if (__all(done)) break;
+      if (spins >= spin_limit) {
+        if (lane == 0) __hip_atomic_store(&ws->status[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const float x = wave_max(lane < gridDim.x ? __uint_as_float((uint32_t)v) : 0.0f);
+    if (lane == 0) gm = x;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(&ws->status[0], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return gm;
 }
 
 // ---------------------------------------------------------------- XCD order

@@ -169,6 +169,147 @@ __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
   }
 }
 
+// One launch for a few rows (grid = rows <= kBarrierSlots): workgroup b
+// normalizes row b as in coop_row (the four waves' partial sums of squares
+// meet in LDS), keeps y (rounded to T, packed) and each block's max |y| in
+// registers, takes the tensor's maximum with grid_max, and encodes. The
+// amax pass, its kernel boundary and the encode pass's second read of x are
+// gone; the price is one device-scope round trip per workgroup.
+template <int NPW, bool FULL, bool BIAS, bool SR, int T>
+__global__ __launch_bounds__(kThreads) void k_rms_fused(const RowArgs a, uint32_t spin_limit) {
+  constexpr int kW = T == kInFP32 ? 16 : 8;  // words of y per block
+  extern __shared__ float params[];  // gamma + c, then beta (param_floats(cols) each)
+  __shared__ float ssp[kWavesPerWG];
+  __shared__ float rcp_tab[128];
+  const uint32_t cols = (uint32_t)a.cols, row = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t epoch = __hip_atomic_load(&a.ws->status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  ParamsPre pp;
+  if constexpr (T == kInBF16) pp = params_issue<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, cols);
+  Raw16<T> q[NPW];
+  coop_load<NPW, FULL, T>(a, row, wid, lane, cols, q);
+  float* gsh = params;
+  float* bsh = params + param_floats(cols);
+  if constexpr (T == kInBF16)
+    params_finish<BIAS>(pp, (const uint16_t*)a.gamma, (const uint16_t*)a.beta, a.woff, cols, gsh, bsh);
+  else
+    stage_params_t<BIAS, T>(a.gamma, a.beta, a.woff, cols, gsh, bsh);
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    if constexpr (T == kInBF16) {
+      ss = sumsq8(q[j].q[1], sumsq8(q[j].q[0], ss));
+    } else {
+      float v[16];
+      widen_raw16<T>(q[j], v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) ssp[wid] = ss;
+  __syncthreads();  // the partial sums, and gamma (and beta) in LDS
+  const float r = inv_rms((ssp[0] + ssp[1]) + (ssp[2] + ssp[3]), 1.0f / (float)cols, a.eps);
+  // y in T and each block's max |y| (= RN_T(max |v|): the rounding is monotone and odd)
+  uint32_t yw[NPW][kW];
+  float bm[NPW];
+  float mrow = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const uint32_t col = (wid + 4 * j) * kSuper + lane * 16;
+    const bool ok = FULL || col < cols;
+    const uint32_t lcol = ok ? col : 0;
+    float v[16], gv[16];
+    widen_raw16<T>(q[j], v);
+    lds16(gsh, lcol, gv);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = v[i] * gv[i];
+    if constexpr (BIAS) {
+      float bv[16];
+      lds16(bsh, lcol, bv);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(v[i], r, bv[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = v[i] * r;
+    }
+    bm[j] = round_t<T>(max16_abs(v));
+    mrow = fmaxf(mrow, bm[j]);
+#pragma unroll
+    for (int k = 0; k < kW; ++k) {
+      if constexpr (T == kInFP32)
+        yw[j][k] = __float_as_uint(v[k]);
+      else if constexpr (T == kInBF16)
+        yw[j][k] = pack_bf16(v[2 * k], v[2 * k + 1]);
+      else
+        yw[j][k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k + 1]) << 16);
+    }
+    if (a.y != nullptr && ok) {
+      char* yp = (char*)a.y + ((int64_t)row * a.ld_y + col) * in_size<T>();
+#pragma unroll
+      for (int l = 0; l < kW / 4; ++l)
+        *reinterpret_cast<uint4*>(yp + 16 * l) = make_uint4(yw[j][4 * l], yw[j][4 * l + 1], yw[j][4 * l + 2],
+                                                            yw[j][4 * l + 3]);
+    }
+  }
+  const float amax = grid_max(a.ws, epoch, mrow, spin_limit);
+  const GScale g = scales_from(amax, a.amax_out, a.scale_out, rcp_tab);
+  const uint32_t nbr = cols >> 4;
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const uint32_t col = (wid + 4 * j) * kSuper + lane * 16;
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if constexpr (T == kInFP32) {
+        v[2 * k] = __uint_as_float(yw[j][2 * k]);
+        v[2 * k + 1] = __uint_as_float(yw[j][2 * k + 1]);
+      } else {
+        v[2 * k] = T == kInBF16 ? bf_lo(yw[j][k]) : h_lo(yw[j][k]);
+        v[2 * k + 1] = T == kInBF16 ? bf_hi(yw[j][k]) : h_hi(yw[j][k]);
+      }
+    }
+    const uint32_t sc = block_scale(bm[j], g.enc);
+    const uint2 w = encode_with_scale<SR>(v, sc, rcp_tab, (uint64_t)row * nbr + (col >> 4), a.seed, a.offset, 0);
+    if (FULL || col < cols) {
+      __builtin_nontemporal_store((uint64_t)w.x | ((uint64_t)w.y << 32),
+                                  reinterpret_cast<uint64_t*>(a.codes + (int64_t)row * a.ldc + (col >> 1)));
+      __builtin_nontemporal_store((uint8_t)sc, a.scales + (int64_t)row * a.lds + (col >> 4));
+    }
+  }
+}
+
+// Bounded waits of the one-launch kernel: 2^20 polls (each a device-scope load
+// and a 64-cycle sleep, about a second in all), far past any wait the launch's
+// resident workgroups can need.
+constexpr uint32_t kFusedSpinLimit = 1u << 20;
+
+template <int NPW, bool BIAS, bool SR, int T>
+hipError_t launch_fused_t(const RowArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
+  const dim3 grid((uint32_t)a.rows), block(kThreads);
+  if (a.cols == (int64_t)NPW * 4 * kSuper)
+    hipLaunchKernelGGL((k_rms_fused<NPW, true, BIAS, SR, T>), grid, block, lds, s, a, kFusedSpinLimit);
+  else
+    hipLaunchKernelGGL((k_rms_fused<NPW, false, BIAS, SR, T>), grid, block, lds, s, a, kFusedSpinLimit);
+  return hipGetLastError();
+}
+
+template <int NPW, int T>
+hipError_t launch_fused_npw_t(const RowArgs& a, hipStream_t s) {
+  if (a.beta) return a.sr ? launch_fused_t<NPW, true, true, T>(a, s) : launch_fused_t<NPW, true, false, T>(a, s);
+  return a.sr ? launch_fused_t<NPW, false, true, T>(a, s) : launch_fused_t<NPW, false, false, T>(a, s);
+}
+
+template <int NPW>
+hipError_t launch_fused_npw(const RowArgs& a, hipStream_t s) {
+  if (a.dtype == kInFP16) return launch_fused_npw_t<NPW, kInFP16>(a, s);
+  if (a.dtype == kInFP32) return launch_fused_npw_t<NPW, kInFP32>(a, s);
+  return launch_fused_npw_t<NPW, kInBF16>(a, s);
+}
+
 // Workgroups per launch: min(rows, NVFP4Q_RMS_COOP_WGS), default 1024.
 int64_t coop_wgs() {
   static int64_t v = [] {
@@ -215,6 +356,17 @@ hipError_t launch_coop_npw(const RowArgs& a, int mode, uint32_t wgs, hipStream_t
 }  // namespace
 
 int rms_max_cols() { return 16 * kSuper; }
+
+int rms_fused_max_rows() { return kBarrierSlots; }
+
+hipError_t launch_rms_fused(const RowArgs& a, hipStream_t s) {
+  if (a.rows < 1 || a.rows > kBarrierSlots || a.codes == nullptr) return hipErrorInvalidValue;
+  const int64_t nsc = (a.cols + kSuper - 1) / kSuper;
+  if (nsc <= 4) return launch_fused_npw<1>(a, s);
+  if (nsc <= 8) return launch_fused_npw<2>(a, s);
+  if (nsc <= 16) return launch_fused_npw<4>(a, s);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, uint32_t* nparts) {
   int64_t wgs = a.rows < coop_wgs() ? a.rows : coop_wgs();

@@ -114,6 +114,11 @@ hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, 
 hipError_t launch_rms_stream_amax(const RowArgs& a, hipStream_t s, uint32_t* nparts);
 hipError_t launch_rms_stream_quant(const RowArgs& a, hipStream_t s);
 int rms_max_cols();
+// One-launch RMSNorm + rowwise encode for at most rms_fused_max_rows() rows
+// (codes required, amax computed in the launch; uses and advances the
+// workspace's one-launch state words).
+hipError_t launch_rms_fused(const RowArgs& a, hipStream_t s);
+int rms_fused_max_rows();
 
 hipError_t launch_quant_2d(const TwoDArgs& a, hipStream_t s);
 hipError_t launch_qk_norm(const QkArgs& a, hipStream_t s);

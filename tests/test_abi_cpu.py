@@ -247,7 +247,17 @@ def test_rounding_option_bits(lib):
                                       None)
 
     assert two_d(q.SCALE_16X16) == 6 and two_d(q.SR | q.SCALE_16X16 | q.FAST_MATH) == 6
-    assert two_d(q.SCALE_16X16 | 0x400) == 4
+    assert two_d(q.SCALE_16X16 | 0x400) == 4   # NVFP4Q_ONE_LAUNCH belongs to the RMSNorm entry points
+    assert "#define NVFP4Q_ONE_LAUNCH 0x400" in hdr and q.ONE_LAUNCH == 0x400
+
+    def rms(rounding):
+        p = q.Plane(FAKE, 16, FAKE, 2)
+        return lib.rmsnorm_nvfp4q(FAKE, 0, 8, 32, 32, FAKE, None, ctypes.c_float(0.0), ctypes.c_float(1e-6),
+                                  None, 0, ctypes.byref(g), ctypes.byref(p), rounding, ctypes.byref(r), FAKE, 1 << 8,
+                                  None)
+
+    assert rms(q.ONE_LAUNCH) == 6 and rms(q.SR | q.ONE_LAUNCH) == 6   # accepted: stops at the small workspace
+    assert rms(q.ONE_LAUNCH | q.SCALE_16X16) == 4
     assert two_d(q.SCALE_16X16, rows=24, colp=False) == 2   # tiles need rows % 16 == 0
     assert two_d(q.RTNE, rows=24, colp=False) == 6          # 1D rowwise does not
 

@@ -260,6 +260,66 @@ def test_rmsnorm_decode_8x7168(gpu_lib, seed):
     _check_rms(w, got)
 
 
+def _one_launch_state(gpu_lib):
+    """(calls completed, a wait gave up) of the workspace's one-launch state words (its first two int32)."""
+    import torch
+
+    st = gpu_lib.workspace()[:8].view(torch.int32).cpu().numpy()
+    return int(st[0]), int(st[1])
+
+
+@pytest.mark.parametrize("shape,bias,woff,rounding", [((1, 16), False, 0.0, "rtne"), ((8, 7168), True, 0.0, "sr"),
+                                                      ((17, 4112), True, 1.0, "rtne"), ((64, 16384), False, 0.0, "sr"),
+                                                      ((64, 1040), True, 0.0, "rtne"), ((63, 8192), False, 1.0, "rtne")])
+def test_rmsnorm_one_launch_rows(gpu_lib, shape, bias, woff, rounding):
+    """NVFP4Q_ONE_LAUNCH with at most 64 rows and no given amax: one launch whose workgroups meet on the amax
+    inside it. Parity as for the two passes; the workspace's one-launch counter advances by one per call and
+    no wait gave up."""
+    rng = np.random.default_rng(sum(shape))
+    T, H = shape
+    w = workloads.Workload("t", _bf16(rng, shape, 1.3), gamma=_bf16(rng, (H,), 0.4),
+                           beta=_bf16(rng, (H,), 0.1) if bias else None, weight_offset=woff, eps=1e-6)
+    e0, _ = _one_launch_state(gpu_lib)
+    got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), to_dev(w.beta) if bias else None,
+                                 weight_offset=woff, eps=w.eps, y_out=True, rounding=rounding, seed=7, offset=1,
+                                 one_launch=True)
+    _check_rms(w, got, rounding, 7, 1)
+    e1, err = _one_launch_state(gpu_lib)
+    assert err == 0 and e1 == e0 + 1
+
+
+def test_rmsnorm_one_launch_equals_given_amax_pass(gpu_lib):
+    """The one-launch result equals the single-pass encode given the amax it found, and the two-pass result:
+    same y, codes and scales bit for bit (all normalize a row the same way; only where the amax comes from
+    differs)."""
+    import torch
+
+    w = workloads.decode(seed=11)
+    x, g, b = to_dev(w.x), to_dev(w.gamma), to_dev(w.beta)
+    one = gpu_lib.rmsnorm_nvfp4q(x, g, b, eps=w.eps, y_out=True, rounding="sr", seed=3, offset=4, one_launch=True)
+    passes = gpu_lib.rmsnorm_nvfp4q(x, g, b, eps=w.eps, y_out=True, rounding="sr", seed=3, offset=4)
+    two = gpu_lib.rmsnorm_nvfp4q(x, g, b, eps=w.eps, y_out=True, rounding="sr", seed=3, offset=4,
+                                 amax=one["amax"].clone())
+    torch.cuda.synchronize()
+    for k in ("y", "codes", "scales", "amax", "scale"):
+        assert torch.equal(one[k].view(torch.uint8), two[k].view(torch.uint8)), k
+        assert torch.equal(one[k].view(torch.uint8), passes[k].view(torch.uint8)), k
+
+
+def test_rmsnorm_one_launch_between_other_calls(gpu_lib):
+    """The one-launch state survives other entry points on the same workspace, and grids of different sizes
+    follow each other (64, 5, 64 workgroups: slots a smaller grid left stale are waited for, not trusted)."""
+    for k, rows in enumerate([64, 5, 64]):
+        rng = np.random.default_rng(100 + k)
+        w = workloads.Workload("t", _bf16(rng, (rows, 2048), 1.0), gamma=_bf16(rng, (2048,), 0.5), eps=1e-6)
+        got = gpu_lib.rmsnorm_nvfp4q(to_dev(w.x), to_dev(w.gamma), eps=w.eps, y_out=True, one_launch=True)
+        _check_rms(w, got)
+        # other entry points write their partial maxima into the same workspace
+        gpu_lib.nvfp4q_quantize_2d(to_dev(_bf16(rng, (1024, 2048), 2.0)))
+        gpu_lib.rmsnorm_nvfp4q(to_dev(_bf16(rng, (300, 2048), 1.0)), to_dev(w.gamma), eps=1e-6)
+    assert _one_launch_state(gpu_lib)[1] == 0
+
+
 @pytest.mark.parametrize("seed", [2, 224])
 def test_rmsnorm_prefill_4096x4096(gpu_lib, seed):
     w = workloads.prefill(seed=seed)

@@ -54,3 +54,13 @@ def test_noalloc_two_calls_second_smaller(gpu_lib):
         x = workloads.to_bf16_bits((rng.standard_normal((T, H)) * 3).astype(np.float32))
         g = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
         _compare(gpu_lib, to_dev(x), to_dev(g), None, eps=1e-6, weight_offset=1.0)
+
+
+def test_noalloc_one_launch(gpu_lib):
+    # NVFP4Q_ONE_LAUNCH on the static array (its state words start as zeros): the same outputs as the
+    # caller-workspace call, twice, the second on fewer rows
+    rng = np.random.default_rng(21)
+    for T, H in ((64, 4096), (8, 7168)):
+        x = workloads.to_bf16_bits((rng.standard_normal((T, H)) * 2).astype(np.float32))
+        g = workloads.to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+        _compare(gpu_lib, to_dev(x), to_dev(g), None, eps=1e-6, one_launch=True)
