@@ -133,3 +133,19 @@ def test_block_bytes_layout():
     b = block_random_bytes(np.array([7], np.uint64), 1, 0x5EED, 9)[0]
     for j in range(16):
         assert b[j] == (int(w[j >> 2]) >> (8 * (j & 3))) & 0xFF
+
+
+def test_block_bytes_are_the_rocrand_output_in_memory_order():
+    # Reading R-sr, stated the other way round: element j of a block takes byte j of the generator's 128-bit
+    # output as it lies in memory (four little-endian 32-bit words), here produced by rocRAND's engine for
+    # the block's counter (block lo, block hi, tag, offset) and key (seed lo, seed hi). A byte or word order
+    # mistake in the oracle (big-endian bytes, reversed words, a shifted lane) fails this.
+    cases = [(0x5EED, 7, 1, 9), (0x1234567890ABCDEF, (3 << 32) | 0xFFFFFFF0, 0, 0), (1, 123456, 1, 77)]
+    with tempfile.TemporaryDirectory() as tmp:
+        exe = _rocrand_binary(tmp)
+        for seed, blk, tag, offset in cases:
+            out = subprocess.run([exe, str(seed), str(blk & 0xFFFFFFFF), str(blk >> 32), str(tag), str(offset)],
+                                 check=True, capture_output=True, text=True).stdout.split()
+            mem = np.array([int(v) for v in out], dtype="<u4").tobytes()
+            got = block_random_bytes(np.array([blk], np.uint64), tag, seed, offset)[0]
+            assert bytes(got.tolist()) == mem, (seed, blk, tag, offset)
