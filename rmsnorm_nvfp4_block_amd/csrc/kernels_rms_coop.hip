@@ -184,7 +184,9 @@ __global__ __launch_bounds__(kThreads) void k_rms_fused(const RowArgs a, uint32_
   const uint32_t cols = (uint32_t)a.cols, row = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const uint32_t wid = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const uint32_t epoch = __hip_atomic_load(&a.ws->status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the call counter: only the first wave publishes, polls and advances it
+  uint32_t epoch = 0;
+  if (wid == 0) epoch = __hip_atomic_load(&a.ws->status[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   ParamsPre pp;
   if constexpr (T == kInBF16) pp = params_issue<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, cols);
   Raw16<T> q[NPW];
