@@ -288,6 +288,17 @@ def test_rmsnorm_one_launch_rows(gpu_lib, shape, bias, woff, rounding):
     assert err == 0 and e1 == e0 + 1
 
 
+@pytest.mark.parametrize("dtype", ["float16", "float32"])
+@pytest.mark.parametrize("shape,bias,woff,rounding", [((8, 7168), True, 0.0, "sr"), ((37, 1040), False, 1.0, "rtne"),
+                                                      ((5, 16384), True, 1.0, "sr")])
+def test_rmsnorm_one_launch_fp16_fp32(gpu_lib, dtype, shape, bias, woff, rounding):
+    """NVFP4Q_ONE_LAUNCH with fp16 and fp32 input: the fp16/fp32 contract rules (reading R-dtype)."""
+    e0, _ = _one_launch_state(gpu_lib)
+    test_rmsnorm_fp16_fp32_inputs(gpu_lib, dtype, shape, bias, woff, rounding, one_launch=True)
+    e1, err = _one_launch_state(gpu_lib)
+    assert err == 0 and e1 == e0 + 1
+
+
 def test_rmsnorm_one_launch_equals_given_amax_pass(gpu_lib):
     """The one-launch result equals the single-pass encode given the amax it found, and the two-pass result:
     same y, codes and scales bit for bit (all normalize a row the same way; only where the amax comes from
@@ -467,7 +478,7 @@ def test_quantize_fp32_given_amax_and_padded_rows(gpu_lib):
                                                       ((300, 4096), True, 1.0, "sr"), ((5, 16384), False, 0.0, "rtne"),
                                                       ((2304, 1040), False, 0.0, "rtne"), ((2080, 2048), True, 1.0, "sr"),
                                                       ((2048, 2048), False, 0.0, "sr")])
-def test_rmsnorm_fp16_fp32_inputs(gpu_lib, dtype, shape, bias, woff, rounding):
+def test_rmsnorm_fp16_fp32_inputs(gpu_lib, dtype, shape, bias, woff, rounding, one_launch=False):
     # reading R-dtype: gamma, beta and y in the input's type; y within the arithmetic tolerance of the
     # float64 value, codes the exact quantization of the GPU's own y, and almost all codes equal to the
     # quantization of the oracle's y
@@ -481,7 +492,7 @@ def test_rmsnorm_fp16_fp32_inputs(gpu_lib, dtype, shape, bias, woff, rounding):
     b = (0.01 * rng.standard_normal(H)).astype(ndt) if bias else None
     tdev = lambda a: torch.from_numpy(a).cuda()
     got = gpu_lib.rmsnorm_nvfp4q(tdev(x), tdev(g), tdev(b) if bias else None, weight_offset=woff, eps=1e-6,
-                                 rounding=rounding, seed=11, offset=2, y_out=True)
+                                 rounding=rounding, seed=11, offset=2, y_out=True, one_launch=one_launch)
     od = "fp16" if dtype == "float16" else "fp32"
     y_ref, y64, _ = oracle.rmsnorm_bf16(x, g, b, woff, 1e-6, return_f64=True, out_dtype=od)
     yg = got["y"].cpu().numpy()
@@ -1036,3 +1047,48 @@ def test_grouped_fp16_small_and_large_groups(gpu_lib):
              rng.standard_normal((19, 96)).astype(np.float16)]
     x = np.concatenate(parts)
     _grouped_check(gpu_lib, x, [0, 40, 77, 96], True, 0x6A5C, "sr", rowwise=True)
+
+
+def test_ceiling_probes_run(gpu_lib):
+    """The probe kernels of bench.py --ceilings on a small input: the read pass leaves its output alone
+    (written only for one particular value), the mix and row-layout passes write what they load, and the
+    one-launch barrier's waits end without giving up (its call counter advances once per launch)."""
+    import ctypes
+    import os
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(gpu_lib.__file__)), "libnvfp4q_ceilings.so"))
+    vp, u64, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
+    lib.ceil_read.argtypes = [vp, u64, vp, vp]
+    lib.ceil_mix.argtypes = [vp, u64, vp, vp, vp]
+    lib.ceil_rowmix.argtypes = [vp, u32, vp, vp, vp]
+    lib.ceil_fused.argtypes = [vp, u32, vp, vp, vp, u32, vp]
+    lib.ceil_fused_ws_bytes.restype = u64
+    rows = 64
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy(rng.integers(0, 1 << 16, size=rows * 4096, dtype=np.uint16).view(np.int16)).cuda()
+    nblk = rows * 256
+    st = torch.cuda.current_stream().cuda_stream
+    out = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    assert lib.ceil_read(x.data_ptr(), x.numel() * 2, out.data_ptr(), st) == 0
+    codes = torch.zeros(nblk * 8, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(nblk, dtype=torch.uint8, device="cuda")
+    assert lib.ceil_mix(x.data_ptr(), nblk, codes.data_ptr(), scales.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    w = x.view(torch.int32).cpu().numpy().view(np.uint32).reshape(nblk, 8)
+    hi = w[:, 0] ^ w[:, 1] ^ w[:, 4] ^ w[:, 5]
+    lo = w[:, 2] ^ w[:, 3] ^ w[:, 6] ^ w[:, 7]
+    expect = (hi.astype(np.uint64) << np.uint64(32)) | lo.astype(np.uint64)
+    assert np.array_equal(codes.cpu().numpy().view(np.uint64), expect)
+    c2 = torch.zeros_like(codes)
+    assert lib.ceil_rowmix(x.data_ptr(), rows, c2.data_ptr(), scales.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(c2, codes)   # the same blocks, loaded in the row layout
+    ws = torch.zeros(lib.ceil_fused_ws_bytes(), dtype=torch.uint8, device="cuda")
+    c3 = torch.zeros_like(codes)
+    for k in range(3):
+        assert lib.ceil_fused(x.data_ptr(), rows, c3.data_ptr(), scales.data_ptr(), ws.data_ptr(), 1 << 20, st) == 0
+    torch.cuda.synchronize()
+    epoch, err = ws[:8].view(torch.int32).cpu().numpy()
+    assert err == 0 and epoch == 3
