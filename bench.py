@@ -551,8 +551,10 @@ def ceilings(torch, steps, warmup):
     lib.ceil_fused.argtypes = [vp, u32, vp, vp, vp, u32, vp]
     lib.ceil_rowmix.argtypes = [vp, u32, vp, vp, vp]
     lib.ceil_fused_ws_bytes.restype = u64
+    lib.ceil_fused_count.argtypes = [vp, u32, vp, vp, vp, u32, ctypes.c_int, vp]
+    lib.ceil_fused_count_ws_bytes.restype = u64
     lib.ceil_empty.argtypes = [u32, u32, ctypes.c_int, vp]
-    for f in (lib.ceil_read, lib.ceil_mix, lib.ceil_rowmix, lib.ceil_fused, lib.ceil_empty):
+    for f in (lib.ceil_read, lib.ceil_mix, lib.ceil_rowmix, lib.ceil_fused, lib.ceil_fused_count, lib.ceil_empty):
         f.restype = ctypes.c_int
 
     def ok(rc, what):
@@ -626,8 +628,53 @@ def ceilings(torch, steps, warmup):
             err = int(ws[4:8].view(torch.int32).item())
             record("fused", shape, xb + nblk * 9, ms, per, wait_gave_up=bool(err),
                    pattern="one launch: rows in registers, grid-wide maximum through per-workgroup slots, stores")
+            wc = torch.zeros(lib.ceil_fused_count_ws_bytes(), dtype=torch.uint8, device="cuda")
+            for mode, name, pat in ((0, "fused-count", "one launch: grid-wide maximum through one arrival counter "
+                                     "and one atomic maximum (release / acquire), stores"),
+                                    (2, "fused-count-relaxed", "as fused-count with relaxed atomics (the arrival "
+                                     "issued after the maximum's atomic returned)"),
+                                    (3, "fused-slots-all", "per-workgroup slots, each workgroup polling all of "
+                                     "them with every load of a round in flight"),
+                                    (4, "fused-flags", "per-workgroup slots read by workgroup 0, which raises one "
+                                     "flag per 64 workgroups; the others poll their flag"),
+                                    (1, "fused-nowait", "one launch, no grid-wide wait (each workgroup's own "
+                                     "maximum): the shape's floor")):
+                def fc(i, st, mode=mode):
+                    j = i % nsets
+                    ok(lib.ceil_fused_count(xs[j].data_ptr(), rows, cs[j].data_ptr(), ss[j].data_ptr(),
+                                            wc.data_ptr(), 1 << 20, mode, st.cuda_stream), "ceil_fused_count")
+
+                ms, per = _graph_time(torch, fc, steps, warmup)
+                err = int(wc[4:8].view(torch.int32).item())
+                record(name, shape, xb + nblk * 9, ms, per, wait_gave_up=bool(err), pattern=pat)
         del xs, cs, ss
         torch.cuda.empty_cache()
+
+    # issue cost of single VALU instructions: 2048 x 256 threads (8 waves per SIMD), 4096 iterations of
+    # 8 independent instructions per lane
+    lib.ceil_rate_kinds.restype = ctypes.c_int
+    lib.ceil_rate_name.restype = ctypes.c_char_p
+    lib.ceil_rate_name.argtypes = [ctypes.c_int]
+    lib.ceil_rate.argtypes = [ctypes.c_int, u32, u32, vp, vp]
+    lib.ceil_rate.restype = ctypes.c_int
+    grid, iters = 2048, 4096
+    rout = torch.zeros(grid * 256, dtype=torch.int32, device="cuda")
+    simds = torch.cuda.get_device_properties(0).multi_processor_count * 4
+    winst = grid * 4 * iters * 8
+    rates = []
+    for kind in range(lib.ceil_rate_kinds()):  # one untimed round first (clocks settle)
+        ok(lib.ceil_rate(kind, grid, iters, rout.data_ptr(), torch.cuda.current_stream().cuda_stream), "ceil_rate")
+    torch.cuda.synchronize()
+    for kind in range(lib.ceil_rate_kinds()):
+        name = lib.ceil_rate_name(kind).decode()
+        ms, per = _graph_time(torch, lambda i, st, kind=kind: ok(lib.ceil_rate(kind, grid, iters, rout.data_ptr(),
+                                                                                st.cuda_stream), "ceil_rate"), 5, 1)
+        rates.append({"instruction": name, "ns_per_wave_instruction_per_simd": round(ms * 1e6 * simds / winst, 4)})
+    base = rates[0]["ns_per_wave_instruction_per_simd"]
+    for r in rates:
+        r["vs_v_add_u32"] = round(r["ns_per_wave_instruction_per_simd"] / base, 2)
+        log(f"[ceilings] issue {r['instruction']:30s} {r['ns_per_wave_instruction_per_simd']:.3f} ns per wave "
+            f"instruction and SIMD ({r['vs_v_add_u32']:.2f} x v_add_u32)")
 
     # launch cost of an empty 1024 x 256 kernel: in a graph, and eager (plain vs cooperative)
     n = 200
@@ -648,7 +695,8 @@ def ceilings(torch, steps, warmup):
             t.append(e0.elapsed_time(e1) / n)
         launches["eager_cooperative_us" if coop else "eager_plain_us"] = round(sorted(t)[1] * 1e3, 3)
     log(f"[ceilings] empty 1024x256 kernel per launch: {launches}")
-    print(json.dumps({"ceilings": results, "empty_kernel_launch": launches, "steps": steps, "warmup": warmup,
+    print(json.dumps({"ceilings": results, "valu_issue": rates, "empty_kernel_launch": launches, "steps": steps,
+                      "warmup": warmup,
                       "timing": "median of 3 passes of a graph of `steps` calls (launch costs: see keys)"}),
           flush=True)
 

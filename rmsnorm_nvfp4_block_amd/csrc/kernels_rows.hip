@@ -20,8 +20,11 @@
 // The amax pass and the encode pass are two launches: the kernel boundary is
 // the grid-wide barrier between them ("CuTeDSL at Perplexity", grid
 // synchronization). A single launch with an in-kernel grid barrier was
-// measured slower on MI355X: cooperative launches add about 20 us between
-// kernels, and the barrier is a chain of device-scope atomic round trips.
+// measured slower on MI355X: a cooperative launch costs about 20 us, and even
+// with the whole grid resident every form of the wait tried (tagged slots,
+// per-group flags, one arrival counter) costs more than the 1.6 us of a
+// kernel boundary in a graph, since it is a chain of device-scope round trips
+// through memory (the probe kernels of bench.py --ceilings).
 // The RMSNorm passes are in kernels_rms_stream.hip and kernels_rms_coop.hip.
 #include "rows.hpp"
 

@@ -319,7 +319,24 @@ def test_ceilings_probe_library_exports():
     path = os.path.join(os.path.dirname(os.path.abspath(q.__file__)), "libnvfp4q_ceilings.so")
     assert os.path.exists(path), "build the library first"
     lib = ctypes.CDLL(path)
-    for name in ("ceil_read", "ceil_mix", "ceil_rowmix", "ceil_fused", "ceil_fused_ws_bytes", "ceil_empty"):
+    for name in ("ceil_read", "ceil_mix", "ceil_rowmix", "ceil_fused", "ceil_fused_ws_bytes", "ceil_fused_count",
+                 "ceil_fused_count_ws_bytes", "ceil_rate", "ceil_rate_kinds", "ceil_rate_name", "ceil_empty"):
         assert hasattr(lib, name), name
     lib.ceil_fused_ws_bytes.restype = ctypes.c_uint64
     assert lib.ceil_fused_ws_bytes() == 128 + 8 * 4096
+    # counter form: header line, two count lines, two maximum lines, 64 flag lines, 4096 slots
+    lib.ceil_fused_count_ws_bytes.restype = ctypes.c_uint64
+    assert lib.ceil_fused_count_ws_bytes() == 128 + 2 * 128 + 2 * 128 + 64 * 128 + 8 * 4096
+    # argument checks come before any runtime call (hipErrorInvalidValue = 1)
+    vp, u32 = ctypes.c_void_p, ctypes.c_uint32
+    lib.ceil_fused_count.argtypes = [vp, u32, vp, vp, vp, u32, ctypes.c_int, vp]
+    assert lib.ceil_fused_count(None, 64, None, None, None, 1, 5, None) == 1
+    assert lib.ceil_fused_count(None, 63, None, None, None, 1, 0, None) == 1
+    lib.ceil_rate_name.restype = ctypes.c_char_p
+    lib.ceil_rate_name.argtypes = [ctypes.c_int]
+    n = lib.ceil_rate_kinds()
+    names = [lib.ceil_rate_name(k).decode() for k in range(n)]
+    assert n == 16 and names[0] == "v_add_u32" and len(set(names)) == n
+    assert lib.ceil_rate_name(n) is None and lib.ceil_rate_name(-1) is None
+    lib.ceil_rate.argtypes = [ctypes.c_int, u32, u32, vp, vp]
+    assert lib.ceil_rate(n, 1, 1, None, None) == 1

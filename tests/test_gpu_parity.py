@@ -1052,7 +1052,8 @@ def test_grouped_fp16_small_and_large_groups(gpu_lib):
 def test_ceiling_probes_run(gpu_lib):
     """The probe kernels of bench.py --ceilings on a small input: the read pass leaves its output alone
     (written only for one particular value), the mix and row-layout passes write what they load, and the
-    one-launch barrier's waits end without giving up (its call counter advances once per launch)."""
+    one-launch barriers' waits end without giving up (each call counter advances once per launch) and
+    every workgroup stores with the grid's maximum (with each workgroup's own in the form without a wait)."""
     import ctypes
     import os
 
@@ -1092,3 +1093,28 @@ def test_ceiling_probes_run(gpu_lib):
     torch.cuda.synchronize()
     epoch, err = ws[:8].view(torch.int32).cpu().numpy()
     assert err == 0 and epoch == 3
+    # the other forms of the grid-wide maximum: each stored code word carries the maximum it used
+    lib.ceil_fused_count.argtypes = [vp, u32, vp, vp, vp, u32, ctypes.c_int, vp]
+    lib.ceil_fused_count_ws_bytes.restype = u64
+    mag = (x.view(torch.int16).cpu().numpy().view(np.uint16) & 0x7FFF).astype(np.uint32).reshape(rows, 4096)
+    g_all = np.uint64(mag.max())
+    g_wg = np.repeat(mag.reshape(rows // 4, -1).max(axis=1), 4 * 256).astype(np.uint64)  # 4 rows per workgroup
+    wc = torch.zeros(lib.ceil_fused_count_ws_bytes(), dtype=torch.uint8, device="cuda")
+    calls = 0
+    for mode in (0, 2, 3, 4, 1):
+        c4 = torch.zeros_like(codes)
+        for k in range(3):
+            assert lib.ceil_fused_count(x.data_ptr(), rows, c4.data_ptr(), scales.data_ptr(), wc.data_ptr(), 1 << 20,
+                                        mode, st) == 0
+            calls += mode != 1
+        torch.cuda.synchronize()
+        g = g_wg if mode == 1 else g_all
+        assert np.array_equal(c4.cpu().numpy().view(np.uint64), expect ^ (g << np.uint64(32))), mode
+        epoch, err = wc[:8].view(torch.int32).cpu().numpy()
+        assert err == 0 and epoch == calls, mode
+    # the issue-rate kernels (registers only) run for every instruction kind
+    lib.ceil_rate.argtypes = [ctypes.c_int, u32, u32, vp, vp]
+    rout = torch.zeros(8 * 256, dtype=torch.int32, device="cuda")
+    for kind in range(lib.ceil_rate_kinds()):
+        assert lib.ceil_rate(kind, 8, 16, rout.data_ptr(), st) == 0
+    torch.cuda.synchronize()
