@@ -195,6 +195,10 @@ __device__ __forceinline__ void load_item(const void* __restrict__ x, int64_t ld
       r[i][1] = t[1];
     }
   }
+  // Every load of the item is issued before any of its data is used: left to
+  // itself the scheduler moved the first uses in among the loads, and the waits
+  // they need held the last loads back until the first had landed.
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Column c of the lane's tile as fp32.
@@ -205,6 +209,29 @@ __device__ __forceinline__ void column(const Tile<CPL, DT>& r, int c, float v[16
     if constexpr (DT == kInFP32) v[i] = __uint_as_float(r[i][c]);
     else if constexpr (DT == kInFP16) v[i] = (c & 1) ? h_hi(r[i][c >> 1]) : h_lo(r[i][c >> 1]);
     else v[i] = (c & 1) ? bf_hi(r[i][c >> 1]) : bf_lo(r[i][c >> 1]);
+  }
+}
+
+// Column c of the lane's tile as fp32 with the transform's sign diagonal D
+// applied: token row i changes sign where bit i of the mask is set. For bf16
+// the flip rides on the widening: the low element is (w << 16) + 2^31 (adding
+// 2^31 flips bit 31 alone), the high one (w & 0xFFFF0000) ^ 2^31 (one
+// three-input logic instruction); fp16 and fp32 flip the widened word. The
+// mask is wave-uniform, so the per-row constants are scalar.
+template <int CPL, int DT>
+__device__ __forceinline__ void column_signed(const Tile<CPL, DT>& r, int c, uint32_t mask, float v[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t s = ((mask >> i) & 1u) << 31;
+    if constexpr (DT == kInBF16) {
+      const uint32_t w = r[i][c >> 1];
+      v[i] = (c & 1) ? __uint_as_float((w & 0xFFFF0000u) ^ s) : __uint_as_float((w << 16) + s);
+    } else if constexpr (DT == kInFP32) {
+      v[i] = __uint_as_float(r[i][c] ^ s);
+    } else {
+      const float h = (c & 1) ? h_hi(r[i][c >> 1]) : h_lo(r[i][c >> 1]);
+      v[i] = __uint_as_float(__float_as_uint(h) ^ s);
+    }
   }
 }
 
@@ -219,21 +246,6 @@ __device__ __forceinline__ void round_through2(float& a, float& b) {
   } else if constexpr (DT == kInFP16) {
     a = (float)(_Float16)a;
     b = (float)(_Float16)b;
-  }
-}
-
-// D: flips the sign of token row i of the lane's tile where bit i of the mask
-// is set: one XOR with 0x80008000 per 2-byte pair, 0x80000000 per fp32 word
-// (the element's sign bit becomes the fp32 sign bit when it is widened). The
-// mask is wave-uniform, so the per-row constants are scalar.
-template <int CPL, int DT>
-__device__ __forceinline__ void apply_signs(Tile<CPL, DT>& r, uint32_t mask) {
-  constexpr uint32_t kSign = DT == kInFP32 ? 0x80000000u : 0x80008000u;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t f = ((mask >> i) & 1u) ? kSign : 0u;
-#pragma unroll
-    for (int j = 0; j < CPL * in_size<DT>() / 4; ++j) r[i][j] ^= f;
   }
 }
 
@@ -281,6 +293,65 @@ __device__ __forceinline__ uint32_t pk_max_mag(uint32_t acc, uint32_t w) {
 constexpr int kAmaxGrid = 1024;
 static_assert(2 * kAmaxGrid * 64 + 128 <= kPartials, "both planes' group maxima fit the workspace");
 
+// One work item of the amax pass: the group maxima of the lane's blocks
+// (columnwise: of the transform's output; rowwise: of |x|) into the
+// workgroup's LDS slots gmc / gmr.
+template <int CPL, bool RHT, bool FAST, bool COL, bool ROW, int DT>
+__device__ __forceinline__ void amax_item(const Item& it, const Tile<CPL, DT>& r, uint32_t mask, uint32_t nb_max,
+                                          uint32_t* gmc, uint32_t* gmr) {
+  const uint32_t half = (threadIdx.x >> 5) & 1;
+  // the half-wave's block and group (lane 0 of the half publishes)
+  const bool writer = (threadIdx.x & 31) == 0 && it.tb < nb_max && (half ? it.b1.valid : it.b0.valid);
+  const int g = half ? it.b1.g : it.b0.g;
+  if constexpr (ROW) {
+    float mr;
+    if constexpr (DT == kInFP32) {
+      uint32_t mm = 0;  // magnitude bits: their u32 order is the order of |x|
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) mm = max(mm, r[i][j] & 0x7FFFFFFFu);
+      mr = __uint_as_float(mm);
+    } else {
+      uint32_t mm = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < CPL / 2; ++j) mm = pk_max_mag(mm, r[i][j]);
+      const uint32_t hi = mm >> 16, lo = mm & 0xFFFFu, m16 = hi > lo ? hi : lo;
+      mr = DT == kInBF16 ? __uint_as_float(m16 << 16) : h_lo(m16);
+    }
+    mr = half_wave_max(mr);  // lanes without data: 0
+    if (writer) atomicMax(&gmr[g], __float_as_uint(mr));
+  }
+  if constexpr (COL) {
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      float v16[16];
+      if constexpr (RHT) column_signed<CPL, DT>(r, c, mask, v16);
+      else column<CPL, DT>(r, c, v16);
+      if constexpr (RHT) {
+        // The last stage only feeds the maximum: max(|RN(a + b)|, |RN(a - b)|)
+        // = RN(|a| + |b|), since one of a + b, a - b has magnitude |a| + |b|,
+        // the other at most that, and rounding is odd and monotone.
+        fwht16<3>(v16);
+        float s8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s8[i] = fabsf(v16[i]) + fabsf(v16[i + 8]);
+        m = fmaxf(m, max8_abs(s8));
+      } else {
+        m = fmaxf(m, max16_abs(v16));
+      }
+    }
+    // max |RN_T(0.25 y)| = RN_T(0.25 max |y|): scaling by 0.25 and
+    // round-to-nearest-even are both monotone (fast math, fp32: no rounding).
+    if constexpr (RHT) m = FAST ? m * 0.25f : round_t<DT>(m * 0.25f);
+    m = half_wave_max(m);  // lanes without data hold zeros
+    if (writer) atomicMax(&gmc[g], __float_as_uint(m));
+  }
+}
+
 template <int CPL, bool RHT, bool FAST, bool COL, bool ROW, int DT>
 __global__ __launch_bounds__(kT) void k_grouped_amax(const void* __restrict__ x, int rows, uint32_t cols,
                                                      int64_t ld_x, const int32_t* __restrict__ offsets, int groups,
@@ -294,65 +365,22 @@ __global__ __launch_bounds__(kT) void k_grouped_amax(const void* __restrict__ x,
   __syncthreads();
   const GroupScan q = group_scan(offsets, groups, rows);
   const uint32_t mpad = (uint32_t)lane_int(q.ps, 63);
-  const uint32_t half = (threadIdx.x >> 5) & 1;
-  for (uint32_t v = blockIdx.x; v < nq * ntc; v += gridDim.x) {
-    uint32_t ctile, pair;
-    wg_item(v, nq, ctile, pair);
-    if (pair >= npairs) continue;  // wave-uniform; no barrier in the loop
-    const Item it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
-    Tile<CPL, DT> r;
-    load_item<CPL, DT>(x, ld_x, rows, it, true, r);
-    // the half-wave's block and group (lane 0 of the half publishes)
-    const bool writer = (threadIdx.x & 31) == 0 && it.tb < nb_max && (half ? it.b1.valid : it.b0.valid);
-    const int g = half ? it.b1.g : it.b0.g;
-    if constexpr (ROW) {
-      float mr;
-      if constexpr (DT == kInFP32) {
-        uint32_t mm = 0;  // magnitude bits: their u32 order is the order of |x|
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) mm = max(mm, r[i][j] & 0x7FFFFFFFu);
-        mr = __uint_as_float(mm);
-      } else {
-        uint32_t mm = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-#pragma unroll
-          for (int j = 0; j < CPL / 2; ++j) mm = pk_max_mag(mm, r[i][j]);
-        const uint32_t hi = mm >> 16, lo = mm & 0xFFFFu, m16 = hi > lo ? hi : lo;
-        mr = DT == kInBF16 ? __uint_as_float(m16 << 16) : h_lo(m16);
-      }
-      mr = half_wave_max(mr);  // lanes without data: 0
-      if (writer) atomicMax(&gmr[g], __float_as_uint(mr));
-    }
-    if constexpr (COL) {
-      if constexpr (RHT) apply_signs<CPL, DT>(r, mask);
-      float m = 0.0f;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        float v16[16];
-        column<CPL, DT>(r, c, v16);
-        if constexpr (RHT) {
-          // The last stage only feeds the maximum: max(|RN(a + b)|, |RN(a - b)|)
-          // = RN(|a| + |b|), since one of a + b, a - b has magnitude |a| + |b|,
-          // the other at most that, and rounding is odd and monotone.
-          fwht16<3>(v16);
-          float s8[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) s8[i] = fabsf(v16[i]) + fabsf(v16[i + 8]);
-          m = fmaxf(m, max8_abs(s8));
-        } else {
-          m = fmaxf(m, max16_abs(v16));
-        }
-      }
-      // max |RN_T(0.25 y)| = RN_T(0.25 max |y|): scaling by 0.25 and
-      // round-to-nearest-even are both monotone (fast math, fp32: no rounding).
-      if constexpr (RHT) m = FAST ? m * 0.25f : round_t<DT>(m * 0.25f);
-      m = half_wave_max(m);  // lanes without data hold zeros
-      if (writer) atomicMax(&gmc[g], __float_as_uint(m));
-    }
-  }
+  const uint32_t nitems = nq * ntc, G = gridDim.x;
+  // Item v's loads are issued into a tile (none read memory when the wave has
+  // no block pair there); returns whether the wave has work in it.
+  // Wave-uniform.
+  auto fetch = [&](uint32_t v, Item& it, Tile<CPL, DT>& r) -> bool {
+    uint32_t ctile = 0, pair = 0;
+    if (v < nitems) wg_item(v, nq, ctile, pair);
+    const bool live = v < nitems && pair < npairs;
+    it = item_of<CPL>(ctile, pair, q, groups, mpad, cols);
+    load_item<CPL, DT>(x, ld_x, rows, it, live, r);
+    return live;
+  };
+  Tile<CPL, DT> r;
+  Item it;
+  for (uint32_t v = blockIdx.x; v < nitems; v += G)
+    if (fetch(v, it, r)) amax_item<CPL, RHT, FAST, COL, ROW, DT>(it, r, mask, nb_max, gmc, gmr);
   __syncthreads();
   if (threadIdx.x < 64) {
     if (COL) ws->partial[blockIdx.x * 64 + threadIdx.x] = __uint_as_float(gmc[threadIdx.x]);
@@ -439,14 +467,15 @@ struct GroupTabs {
 __device__ __forceinline__ bool fold_ok(float amax) { return amax >= 0x1p-90f && amax <= 0x1p120f; }
 
 template <int CPL, bool RHT, bool SR, bool FOLD, bool FAST, int DT>
-__device__ __forceinline__ void encode_columns(Tile<CPL, DT>& r, const float* tab, float enc, uint64_t blk,
-                                               uint64_t nbp, uint8_t* cst, uint8_t* sst, uint64_t seed,
-                                               uint32_t offset) {
+__device__ __forceinline__ void encode_columns(Tile<CPL, DT>& r, uint32_t mask, const float* tab, float enc,
+                                               uint64_t blk, uint64_t nbp, uint8_t* cst, uint8_t* sst,
+                                               uint64_t seed, uint32_t offset) {
   static_assert(!FOLD || FAST || DT == kInBF16, "the fold is exact only for a bf16 round-through");
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     float v16[16];
-    column<CPL, DT>(r, c, v16);
+    if constexpr (RHT) column_signed<CPL, DT>(r, c, mask, v16);
+    else column<CPL, DT>(r, c, v16);
     if constexpr (RHT) {
       fwht16(v16);
       if constexpr (!FAST) {
@@ -512,7 +541,6 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL, DT>& r, ui
     tabs[128 + lane] = encode_mult(lane, gt.s1.dec) * f;
     tabs[128 + lane + 64] = encode_mult(lane + 64, gt.s1.dec) * f;
   }
-  if constexpr (RHT) apply_signs<CPL, DT>(r, mask);
   const float* tab = tabs + half * 128;
   const float enc = half ? gt.s1.enc : gt.s0.enc;
   const uint64_t nbp = (uint64_t)(mpad >> 4);  // blocks per plane row
@@ -523,9 +551,9 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL, DT>& r, ui
   uint8_t* cst = st.codes + (lane & 31) * CPL * kStagePitch + 8 * j;
   uint8_t* sst = st.scales + (lane & 31) * CPL * kItemBlocks + j;
   if (RHT && gt.fold)
-    encode_columns<CPL, RHT, SR, kCanFold, FAST, DT>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
+    encode_columns<CPL, RHT, SR, kCanFold, FAST, DT>(r, mask, tab, enc, blk, nbp, cst, sst, seed, offset);
   else
-    encode_columns<CPL, RHT, SR, false, FAST, DT>(r, tab, enc, blk, nbp, cst, sst, seed, offset);
+    encode_columns<CPL, RHT, SR, false, FAST, DT>(r, mask, tab, enc, blk, nbp, cst, sst, seed, offset);
 }
 
 // Write-out of a staged item: plane rows of column tile ctile, blocks
