@@ -378,16 +378,30 @@ def _code_only(text):
     return "\n".join(out)
 
 
-def source_digest():
-    """sha256 of the device code (kernels_*.hip and the headers they include, comments left out): traffic
-    figures are valid only for the kernels they were taken on. Host-only files (api.hip, the C header) do
-    not enter."""
+# The kernel sources each workload's passes are built from; the shared device headers (*.hpp) count for all.
+DIGEST_SOURCES = {
+    "prefill": ("kernels_rms_stream.hip", "kernels_rms_coop.hip"),
+    "decode": ("kernels_rms_stream.hip", "kernels_rms_coop.hip"),
+    "quantize": ("kernels_rows.hip",),
+    "weight": ("kernels_2d.hip", "kernels_rows.hip"),
+    "experts": ("kernels_2d.hip", "kernels_rows.hip"),
+    "grouped": ("kernels_grouped.hip",),
+    "qknorm": ("kernels_qk.hip",),
+}
+
+
+def source_digest(workload=None):
+    """sha256 of the device code a workload's kernels come from (its kernels_*.hip files and the shared
+    headers, comments left out; with no workload, every kernels_*.hip): traffic figures are valid only for the
+    kernels they were taken on. Host-only files (api.hip, the C header) do not enter."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rmsnorm_nvfp4_block_amd", "csrc")
+    names = DIGEST_SOURCES[workload] if workload else None
     files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
-                   if (f.startswith("kernels_") and f.endswith(".hip")) or f.endswith(".hpp"))
+                   if f.endswith(".hpp") or (f.startswith("kernels_") and f.endswith(".hip")
+                                             and (names is None or f in names)))
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, encoding="utf-8") as fh:
@@ -430,7 +444,7 @@ def ingest_pmc(config, fetch_dir, write_dir, command, key=None):
     import re
 
     pat = re.compile(DOMINANT[config][2])
-    entry = {"kernels": {}, "source_sha256": source_digest(), "command": command}
+    entry = {"kernels": {}, "source_sha256": source_digest(config), "command": command}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         for name, vals in read_pmc(d, counter).items():
             if pat.search(name):
@@ -488,7 +502,7 @@ def traffic_bytes(config):
     with open(TRAFFIC_FILE) as fh:
         d = json.load(fh)
     e, cal = d.get(config), d.get("copy_calibration")
-    if not e or not cal or e.get("source_sha256") != source_digest():
+    if not e or not cal or e.get("source_sha256") != source_digest(config.split("_")[0]):
         return None
     return e["fetch_kib"] * 1024.0 * cal["fetch_factor"] + e["write_kib"] * 1024.0 * cal["write_factor"]
 
