@@ -162,6 +162,13 @@ const char *nvfp4q_status_string(nvfp4q_status s);
 /* ABI version: 1. */
 int nvfp4q_version(void);
 
+/* The sha256 (64 lowercase hex digits) of the sources this library was built
+ * from: every file of the package's csrc/ directory and of include/, in name
+ * order, as rmsnorm_nvfp4_block_amd/build.py computes it; "unknown" when the
+ * library was built without it. Lets a caller check that a prebuilt library
+ * matches the sources beside it. A static string, never NULL. */
+const char *nvfp4q_source_sha256(void);
+
 /*
  * nvfp4q_quantize -- rowwise NVFP4 of a [rows, cols] bf16, fp16 or fp32 tensor.
  *   x: device, rows x cols of dtype, row stride ld_x elements.

@@ -16,6 +16,7 @@ __all__ = [
     "load", "lib_path", "workspace", "NVFP4QError",
     "nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped", "nvfp4q_grouped",
     "nvfp4q_qk_norm", "rmsnorm_nvfp4q_noalloc", "nvfp4q_workspace_bytes", "nvfp4q_status_string", "SYMBOLS",
+    "library_source_sha256",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -23,7 +24,7 @@ lib_path = os.path.join(_HERE, "libnvfp4q.so")
 
 SYMBOLS = ("nvfp4q_quantize", "rmsnorm_nvfp4q", "nvfp4q_quantize_2d", "nvfp4q_quantize_2d_grouped", "nvfp4q_grouped",
            "nvfp4q_qk_norm", "rmsnorm_nvfp4q_noalloc",
-           "nvfp4q_workspace_bytes", "nvfp4q_status_string", "nvfp4q_version")
+           "nvfp4q_workspace_bytes", "nvfp4q_status_string", "nvfp4q_version", "nvfp4q_source_sha256")
 
 RTNE, SR = 0, 1
 FAST_MATH = 0x100  # NVFP4Q_FAST_MATH, OR-ed into the rounding argument
@@ -65,6 +66,7 @@ def load():
     lib.nvfp4q_status_string.restype = ctypes.c_char_p
     lib.nvfp4q_status_string.argtypes = [ctypes.c_int]
     lib.nvfp4q_version.restype = ctypes.c_int
+    lib.nvfp4q_source_sha256.restype = ctypes.c_char_p
     lib.nvfp4q_quantize.restype = ctypes.c_int
     lib.nvfp4q_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, P(Global), P(Plane), ctypes.c_int, P(Rng),
                                     vp, ctypes.c_size_t, vp]
@@ -110,6 +112,12 @@ def _alloc_workspace(dev):
     import torch
 
     return torch.zeros(max(nvfp4q_workspace_bytes(), 4096), dtype=torch.uint8, device=dev)
+
+
+def library_source_sha256() -> str:
+    """The sha256 of the sources the loaded library was built from (``nvfp4q_source_sha256``); compare with
+    ``rmsnorm_nvfp4_block_amd.build.source_digest()`` of the tree."""
+    return load().nvfp4q_source_sha256().decode()
 
 
 def workspace(device=None, stream=None):

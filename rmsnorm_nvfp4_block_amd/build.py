@@ -7,7 +7,10 @@ AddressSanitizer and UndefinedBehaviorSanitizer on its host code only (into
 the C ABI (``tests/test_abi_cpu.py``: argument validation, nothing launched)
 against it with the sanitizer runtime preloaded. It needs no GPU.
 Each ``.hip`` translation unit is compiled in parallel into ``_build/`` and
-linked into ``rmsnorm_nvfp4_block_amd/libnvfp4q.so``; the measurement probes
+linked into ``rmsnorm_nvfp4_block_amd/libnvfp4q.so``, which carries the sha256 of
+the sources it was built from (``source_digest()``: every file of ``csrc/`` and
+``include/``; ``nvfp4q_source_sha256()`` in the C ABI), so a prebuilt library
+can be checked against the tree; the measurement probes
 (``csrc/ceilings.hip``, used only by ``bench.py --ceilings``) go into
 ``libnvfp4q_ceilings.so`` beside it. Flags: -O3, gfx950 only,
 no FMA contraction (the quantizer's products must round on their own), NaN
@@ -43,6 +46,23 @@ COMMON = [
 ]
 
 
+def source_digest() -> str:
+    """sha256 over the library's sources: every file of csrc/ and include/, by name and content."""
+    import hashlib
+
+    h = hashlib.sha256()
+    inc = os.path.join(ROOT, "include")
+    for d in (CSRC, inc):
+        for f in sorted(os.listdir(d)):
+            path = os.path.join(d, f)
+            if os.path.isfile(path) and f.endswith((".hip", ".hpp", ".h")):
+                h.update(f.encode() + b"\0")
+                with open(path, "rb") as fh:
+                    h.update(fh.read())
+                h.update(b"\0")
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(p):
@@ -50,9 +70,9 @@ def hipcc() -> str:
     return p
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, f'-DNVFP4Q_SOURCE_SHA256="{digest}"', "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")
@@ -71,8 +91,9 @@ def _link(objs, lib: str) -> None:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = SOURCES + CEIL_SOURCES
+    digest = source_digest()
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, digest), srcs))
     _link(objs[:len(SOURCES)], LIB)
     _link(objs[len(SOURCES):], CEIL_LIB)
     if verbose:
@@ -102,10 +123,12 @@ def sanitize_check() -> int:
     """Host-sanitized build of the library, then the CPU ABI tests against it. Returns pytest's status."""
     out = os.path.join(BUILD, "sanitize")
     os.makedirs(out, exist_ok=True)
+    digest = source_digest()
 
     def comp(src: str) -> str:
         obj = os.path.join(out, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc(), *COMMON, *SANITIZE, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *COMMON, *SANITIZE, f'-DNVFP4Q_SOURCE_SHA256="{digest}"', "-c", os.path.join(CSRC, src),
+               "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")

@@ -187,6 +187,13 @@ size_t nvfp4q_workspace_bytes(void) { return sizeof(Workspace); }
 
 int nvfp4q_version(void) { return 1; }
 
+// The build passes the sha256 of the sources (every file of csrc/ and
+// include/); a library built any other way says so.
+#ifndef NVFP4Q_SOURCE_SHA256
+#define NVFP4Q_SOURCE_SHA256 "unknown"
+#endif
+const char* nvfp4q_source_sha256(void) { return NVFP4Q_SOURCE_SHA256; }
+
 const char* nvfp4q_status_string(nvfp4q_status s) {
   int v;  // read as an int: a caller may pass any code
   std::memcpy(&v, &s, sizeof v);

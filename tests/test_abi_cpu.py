@@ -56,6 +56,16 @@ def test_status_strings_and_workspace(lib):
     assert q.nvfp4q_status_string(99) == "unknown status"
 
 
+def test_library_was_built_from_these_sources():
+    """The library names the sha256 of the sources it was built from; it is the tree's (rebuild if not)."""
+    import rmsnorm_nvfp4_block_amd as q
+    from rmsnorm_nvfp4_block_amd import build
+
+    got = q.library_source_sha256()
+    assert len(got) == 64 and int(got, 16) >= 0
+    assert got == build.source_digest(), "libnvfp4q.so is older than its sources: rebuild it"
+
+
 FAKE = 0x100000  # 16-byte aligned, never dereferenced: every call fails validation
 
 

@@ -26,6 +26,13 @@ pytestmark = pytest.mark.gpu
 SEEDS = [0, 1, 2, 224]
 
 
+def test_gpu_library_was_built_from_these_sources(gpu_lib):
+    """The library the GPU tests load was built from the sources of this tree (its embedded digest)."""
+    from rmsnorm_nvfp4_block_amd import build
+
+    assert gpu_lib.library_source_sha256() == build.source_digest(), "libnvfp4q.so is older than its sources"
+
+
 def _bf16(rng, shape, scale=1.0):
     return workloads.to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
 
