@@ -18,13 +18,13 @@
 // past its group's end, and lanes without data, take an offset past the range
 // and read zero without touching memory.
 //
-// Three kernels: the amax pass writes one partial maximum per (block, column
-// tile) and plane; a reduce kernel (one workgroup per group) takes each
-// group's maximum over its blocks' partials; the encode pass reads one amax
-// per group and plane, keeps
-// per-group encode reciprocal tables in LDS (two per wave, written and read by
-// that wave only), stages its codes and scales in LDS and writes them out in
-// coalesced pieces of the transposed planes.
+// Three kernels: the amax pass (a grid-stride loop of at most 1024
+// workgroups) keeps the maximum of every group it meets in LDS and writes 64
+// slots per workgroup and plane; a reduce kernel (one workgroup per group)
+// takes each group's maximum over those slots; the encode pass reads one amax
+// per group and plane, keeps per-group encode reciprocal tables in LDS (two
+// per wave, written and read by that wave only), stages its codes and scales
+// in LDS and writes them out in coalesced pieces of the transposed planes.
 //
 // "[nvfp4_training] Optimize CuteDSL kernels for NVFP4 training": Grouped
 // allocation tail (stop at the last padded row, leave the tail untouched);
