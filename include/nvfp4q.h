@@ -112,8 +112,8 @@ typedef enum { NVFP4Q_RTNE = 0, NVFP4Q_SR = 1, NVFP4Q_ROUNDING_MAX_ENUM = 0x7FFF
  * its transpose decode to the same values. */
 #define NVFP4Q_SCALE_16X16 0x200
 /* rmsnorm_nvfp4q and rmsnorm_nvfp4q_noalloc only (other entry points:
- * NVFP4Q_E_UNSUPPORTED): with codes, at most 64 tokens and no given amax, one
- * launch (one workgroup per token) whose workgroups meet on the amax inside
+ * NVFP4Q_E_UNSUPPORTED): with codes, at most 64 tokens, hidden <= 16384 and
+ * no given amax, one launch (one workgroup per token) whose workgroups meet on the amax inside
  * it ([Blog] Grid synchronization) instead of an amax pass and an encode pass;
  * same results. It keeps state in the workspace's first 640 bytes (see the
  * workspace convention). Measured on MI355X it is not faster than the two
@@ -212,7 +212,9 @@ nvfp4q_status nvfp4q_quantize(const void *x, nvfp4q_dtype dtype, int64_t rows, i
  *   g: as for nvfp4q_quantize; with g->amax_in the call is one pass over x
  *     (the amax is not computed), otherwise an amax pass precedes the encode
  *     pass (or, with NVFP4Q_ONE_LAUNCH and at most 64 tokens, one launch).
- *     hidden <= 16384 (NVFP4Q_E_UNSUPPORTED above that).
+ *     hidden <= 32768 for bf16 and fp16, <= 16384 for fp32
+ *     (NVFP4Q_E_UNSUPPORTED above that); rows wider than 16384 take the
+ *     cooperative-row passes with gamma and beta read where they are used.
  */
 nvfp4q_status rmsnorm_nvfp4q(const void *x, nvfp4q_dtype dtype, int64_t tokens, int64_t hidden,
                              int64_t ld_x, const void *gamma, const void *beta, float weight_offset,

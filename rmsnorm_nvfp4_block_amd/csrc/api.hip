@@ -128,7 +128,7 @@ nvfp4q_status rmsnorm_impl(const void* x, nvfp4q_dtype dtype, int64_t tokens, in
   if (!aligned(gamma, 16) || !aligned(beta, 16)) return NVFP4Q_E_ALIGN;
   if (weight_offset != 0.0f && weight_offset != 1.0f) return NVFP4Q_E_UNSUPPORTED;
   if (!(eps >= 0.0f)) return NVFP4Q_E_SHAPE;
-  if (hidden > rms_max_cols()) return NVFP4Q_E_UNSUPPORTED;
+  if (hidden > rms_max_cols((int)dtype)) return NVFP4Q_E_UNSUPPORTED;
   const bool codes = row && (row->codes || tokens == 0);
   if (!codes && !y_out) return NVFP4Q_E_NULLPTR;
   if (codes) TRY(check_plane(row, tokens, hidden));
@@ -154,10 +154,12 @@ nvfp4q_status rmsnorm_impl(const void* x, nvfp4q_dtype dtype, int64_t tokens, in
   a.seed = rng ? rng->seed : 0; a.offset = rng ? rng->offset : 0;
   // NVFP4Q_ONE_LAUNCH, a few rows and no given amax: one launch whose
   // workgroups meet on the amax inside it.
-  if (one_launch && codes && !a.amax_in && tokens <= rms_fused_max_rows()) return done(launch_rms_fused(a, s));
+  const bool staged = hidden <= rms_stage_max_cols();  // gamma and beta fit the LDS stage
+  if (one_launch && codes && !a.amax_in && tokens <= rms_fused_max_rows() && staged)
+    return done(launch_rms_fused(a, s));
   // With the amax pass and a row count that fits the workspace's row-scale
   // slots, the encode pass streams rows using the 1/rms the amax pass stored.
-  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && rms_stream_enabled();
+  const bool streamed = codes && !a.amax_in && tokens <= kRowScaleCap && staged && rms_stream_enabled();
   if (streamed) a.rs = reinterpret_cast<float*>(static_cast<char*>(workspace) + offsetof(Workspace, partial)) + kRowPartials;
   if (codes && !a.amax_in) {
     const hipError_t e = (streamed && !beta) ? launch_rms_stream_amax(a, s, &a.nparts)

@@ -11,6 +11,11 @@
 // holds one superchunk per row and per slot instead of a whole row, and rows
 // complete in the order their loads were issued.
 //
+// Rows of more than 16 superchunks (16384 < hidden <= 32768, 2-byte input
+// types) take eight superchunks per wave and one row in flight, with gamma and
+// beta read from global memory where they are used (PG) instead of staged in
+// LDS: staged as fp32 they would need up to 256 KiB.
+//
 // "CuTeDSL at Perplexity", QK Norm (the normalization: r = 1/sqrt(mean x^2 +
 // eps), y = RN((gamma + c) x r) [+ beta]) and Prefill and decode (one token
 // row per thread group, reductions kept inside the group).
@@ -35,9 +40,31 @@ __device__ __forceinline__ void coop_load(const RowArgs& a, uint32_t row, uint32
   }
 }
 
+// gamma + c (and beta) of the lane's block at column `col`: from the LDS
+// stage, or (PG) read from global memory and widened here, with the same
+// fp32 arithmetic as the stage.
+template <bool PG, bool BIAS, int T>
+__device__ __forceinline__ void block_params(const RowArgs& a, const float* gsh, const float* bsh, uint32_t col,
+                                             bool ok, float (&gv)[16], float (&bv)[16]) {
+  if constexpr (PG) {
+    const Raw16<T> gq = load_raw16<T>(a.gamma, col, ok);
+    widen_raw16<T>(gq, gv);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) gv[i] = gv[i] + a.woff;
+    if constexpr (BIAS) {
+      const Raw16<T> bq = load_raw16<T>(a.beta, col, ok);
+      widen_raw16<T>(bq, bv);
+    }
+  } else {
+    const uint32_t lcol = ok ? col : 0;
+    lds16(gsh, lcol, gv);
+    if constexpr (BIAS) lds16(bsh, lcol, bv);
+  }
+}
+
 // One row: partial sums of squares, the barrier, 1/rms, then the mode's work.
 // Returns the contribution to the amax pass's maximum (kCoopAmax).
-template <int NPW, bool FULL, bool BIAS, int MODE, bool SR, int T>
+template <int NPW, bool FULL, bool BIAS, int MODE, bool SR, int T, bool PG>
 __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32_t k, const Raw16<T> (&q)[NPW],
                                           float (*ssp)[kWavesPerWG], const float* gsh, const float* bsh, GScale g,
                                           const float* rcp_tab, float inv_k, uint32_t wid, int lane, uint32_t cols) {
@@ -69,10 +96,9 @@ __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32
   for (int j = 0; j < NPW; ++j) {
     const uint32_t col = (wid + 4 * j) * kSuper + lane * 16;
     const bool ok = FULL || col < cols;
-    const uint32_t lcol = ok ? col : 0;
-    float v[16], gv[16];
+    float v[16], gv[16], bv[16];
+    block_params<PG, BIAS, T>(a, gsh, bsh, col, ok, gv, bv);
     widen_raw16<T>(q[j], v);
-    lds16(gsh, lcol, gv);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = v[i] * gv[i];
     if constexpr (MODE == kCoopAmax && !BIAS) {
@@ -81,8 +107,6 @@ __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32
       continue;
     }
     if constexpr (BIAS) {
-      float bv[16];
-      lds16(bsh, lcol, bv);
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = __builtin_fmaf(v[i], r, bv[i]);
     } else {
@@ -110,9 +134,9 @@ __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32
   return 0.0f;
 }
 
-template <int NPW, int D, bool FULL, bool BIAS, int MODE, bool SR, int T>
+template <int NPW, int D, bool FULL, bool BIAS, int MODE, bool SR, int T, bool PG>
 __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
-  extern __shared__ float params[];  // gamma + c, then beta (param_floats(cols) each)
+  extern __shared__ float params[];  // gamma + c, then beta (param_floats(cols) each); none with PG
   __shared__ float ssp[2][kWavesPerWG];
   __shared__ float rcp_tab[128];
   const uint32_t rows = (uint32_t)a.rows, cols = (uint32_t)a.cols;
@@ -125,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
   PartialsPre pm;
   if constexpr (MODE == kCoopEncode) pm = partials_issue(a.ws, a.nparts, a.amax_in);
   ParamsPre pp;
-  if constexpr (T == kInBF16) pp = params_issue<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, cols);
+  if constexpr (T == kInBF16 && !PG) pp = params_issue<BIAS>((const uint16_t*)a.gamma, (const uint16_t*)a.beta, cols);
   // unconditional fill (row index clamped to the workgroup's last row): a
   // fill that may be skipped would turn every later wait into a wait for all
   Raw16<T> ring[D][NPW];
@@ -134,10 +158,12 @@ __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
     coop_load<NPW, FULL, T>(a, (uint32_t)d < nr ? b + d * G : last, wid, lane, cols, ring[d]);
   float* gsh = params;
   float* bsh = params + param_floats(cols);
-  if constexpr (T == kInBF16)
+  if constexpr (PG) {
+  } else if constexpr (T == kInBF16) {
     params_finish<BIAS>(pp, (const uint16_t*)a.gamma, (const uint16_t*)a.beta, a.woff, cols, gsh, bsh);
-  else
+  } else {
     stage_params_t<BIAS, T>(a.gamma, a.beta, a.woff, cols, gsh, bsh);
+  }
   GScale g = {1.0f, 1.0f};
   if constexpr (MODE == kCoopEncode) g = partials_finish(pm, a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
   else __syncthreads();
@@ -149,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const uint32_t kk = k + d;
-        mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g, rcp_tab,
+        mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T, PG>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g, rcp_tab,
                                                                inv_k, wid, lane, cols));
         coop_load<NPW, FULL, T>(a, kk + D < nr ? b + (kk + D) * G : last, wid, lane, cols, ring[d]);
       }
@@ -158,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
       for (int d = 0; d < D; ++d) {
         const uint32_t kk = k + d;
         if (kk < nr)
-          mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g,
+          mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T, PG>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g,
                                                                  rcp_tab, inv_k, wid, lane, cols));
       }
     }
@@ -325,13 +351,17 @@ int64_t coop_wgs() {
 // 4096 x 4096 prefill (10.7 us at two, 11.3-11.5 us at three or four).
 constexpr int kCoopDepth = 2;
 
+// Up to 16 superchunks per row: gamma and beta staged in LDS, two rows in
+// flight; more (NPW 8): read where used (PG), one row in flight.
 template <int NPW, bool BIAS, int MODE, bool SR, int T>
 hipError_t launch_coop_t(const RowArgs& a, uint32_t wgs, hipStream_t s) {
-  const size_t lds = (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
+  constexpr bool kPG = NPW > 4;
+  constexpr int kD = kPG ? 1 : kCoopDepth;
+  const size_t lds = kPG ? 0 : (size_t)param_floats((uint32_t)a.cols) * sizeof(float) * (BIAS ? 2 : 1);
   if (a.cols == (int64_t)NPW * 4 * kSuper)
-    hipLaunchKernelGGL((k_rms_coop<NPW, kCoopDepth, true, BIAS, MODE, SR, T>), dim3(wgs), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((k_rms_coop<NPW, kD, true, BIAS, MODE, SR, T, kPG>), dim3(wgs), dim3(kThreads), lds, s, a);
   else
-    hipLaunchKernelGGL((k_rms_coop<NPW, kCoopDepth, false, BIAS, MODE, SR, T>), dim3(wgs), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((k_rms_coop<NPW, kD, false, BIAS, MODE, SR, T, kPG>), dim3(wgs), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -351,13 +381,18 @@ hipError_t launch_coop_npw_t(const RowArgs& a, int mode, uint32_t wgs, hipStream
 template <int NPW>
 hipError_t launch_coop_npw(const RowArgs& a, int mode, uint32_t wgs, hipStream_t s) {
   if (a.dtype == kInFP16) return launch_coop_npw_t<NPW, kInFP16>(a, mode, wgs, s);
-  if (a.dtype == kInFP32) return launch_coop_npw_t<NPW, kInFP32>(a, mode, wgs, s);
+  if constexpr (NPW <= 4) {
+    if (a.dtype == kInFP32) return launch_coop_npw_t<NPW, kInFP32>(a, mode, wgs, s);
+  } else {
+    if (a.dtype == kInFP32) return hipErrorInvalidValue;  // rows of 4-byte values stop at 16 superchunks
+  }
   return launch_coop_npw_t<NPW, kInBF16>(a, mode, wgs, s);
 }
 
 }  // namespace
 
-int rms_max_cols() { return 16 * kSuper; }
+int rms_max_cols(int dtype) { return (dtype == kInFP32 ? 16 : 32) * kSuper; }
+int rms_stage_max_cols() { return 16 * kSuper; }
 
 int rms_fused_max_rows() { return kBarrierSlots; }
 
@@ -380,6 +415,7 @@ hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, 
   if (nsc <= 4) return launch_coop_npw<1>(a, mode, (uint32_t)wgs, s);
   if (nsc <= 8) return launch_coop_npw<2>(a, mode, (uint32_t)wgs, s);
   if (nsc <= 16) return launch_coop_npw<4>(a, mode, (uint32_t)wgs, s);
+  if (nsc <= 32) return launch_coop_npw<8>(a, mode, (uint32_t)wgs, s);
   return hipErrorInvalidValue;
 }
 

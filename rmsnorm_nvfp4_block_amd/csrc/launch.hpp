@@ -113,7 +113,12 @@ hipError_t launch_rmsnorm_pass(const RowArgs& a, bool amax_pass, hipStream_t s, 
 // also writes a.rs, and the encode pass, which reads it.
 hipError_t launch_rms_stream_amax(const RowArgs& a, hipStream_t s, uint32_t* nparts);
 hipError_t launch_rms_stream_quant(const RowArgs& a, hipStream_t s);
-int rms_max_cols();
+// Widest row of input type `dtype` the RMSNorm passes take (2-byte types
+// 32768, fp32 16384), and the widest whose gamma and beta the streaming and
+// one-launch kernels stage in LDS (16384): wider rows take the
+// cooperative-row passes.
+int rms_max_cols(int dtype);
+int rms_stage_max_cols();
 // One-launch RMSNorm + rowwise encode for at most rms_fused_max_rows() rows
 // (codes required, amax computed in the launch; uses and advances the
 // workspace's one-launch state words).

@@ -116,8 +116,8 @@ def test_rmsnorm_validation(lib):
     g = q.Global(None, None, None)
     r = q.Rng(0, 0)
 
-    def call(gamma=FAKE, beta=None, woff=0.0, eps=1e-6, y=None, ldy=0, hidden=32, p=plane, ws=FAKE):
-        return lib.rmsnorm_nvfp4q(FAKE, 0, 4, hidden, hidden, gamma, beta, woff, eps, y, ldy, ctypes.byref(g),
+    def call(gamma=FAKE, beta=None, woff=0.0, eps=1e-6, y=None, ldy=0, hidden=32, p=plane, ws=FAKE, dtype=0):
+        return lib.rmsnorm_nvfp4q(FAKE, dtype, 4, hidden, hidden, gamma, beta, woff, eps, y, ldy, ctypes.byref(g),
                                   ctypes.byref(p), 0, ctypes.byref(r), ws, 1 << 16, None)
 
     assert call(gamma=None) == 1
@@ -125,7 +125,9 @@ def test_rmsnorm_validation(lib):
     assert call(woff=0.5) == 4
     assert call(eps=-1.0) == 2
     assert call(hidden=40) == 2
-    assert call(hidden=32 * 512 + 16, p=q.Plane(FAKE, 8208, FAKE, 1026)) == 4   # beyond the register-resident row
+    # rows beyond 32 superchunks (2-byte types) or 16 (fp32)
+    assert call(hidden=32 * 1024 + 16, p=q.Plane(FAKE, 16392, FAKE, 2050)) == 4
+    assert call(hidden=16 * 1024 + 16, p=q.Plane(FAKE, 8208, FAKE, 1026), dtype=2) == 4
     assert call(p=q.Plane(None, 0, None, 0)) == 1                               # nothing to produce
     assert call(p=q.Plane(None, 0, None, 0), y=FAKE, ldy=16) == 2
     assert call(p=q.Plane(None, 0, None, 0), y=FAKE + 2, ldy=32) == 3

@@ -359,6 +359,38 @@ def test_rmsnorm_ragged(gpu_lib, shape, bias, woff, rounding):
     _check_rms(w, got, rounding, 11, 1)
 
 
+@pytest.mark.parametrize("shape,bias,woff,rounding", [((3, 32768), False, 0.0, "rtne"), ((5, 20000), True, 1.0, "sr"),
+                                                      ((2, 16400), True, 0.0, "rtne"), ((70, 18432), False, 0.0, "sr")])
+def test_rmsnorm_wide_rows(gpu_lib, shape, bias, woff, rounding):
+    """Rows of 16384 < hidden <= 32768: cooperative-row passes with eight superchunks per wave and gamma and
+    beta read where they are used (also for a row count the streaming passes would take)."""
+    import torch
+
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    T, H = shape
+    w = workloads.Workload("t", _bf16(rng, shape, 2.0), gamma=_bf16(rng, (H,), 0.3),
+                           beta=_bf16(rng, (H,), 0.05) if bias else None, weight_offset=woff, eps=1e-5)
+    args = (to_dev(w.x), to_dev(w.gamma), to_dev(w.beta) if bias else None)
+    kw = dict(weight_offset=woff, eps=w.eps, y_out=True, rounding=rounding, seed=11, offset=1)
+    got = gpu_lib.rmsnorm_nvfp4q(*args, **kw)
+    _check_rms(w, got, rounding, 11, 1)
+    valid = {"y": None, "codes": H // 2, "scales": H // 16, "amax": None, "scale": None}  # bytes past: padding
+    u8 = lambda r, k: np_u8(r[k].view(torch.uint8), valid[k])
+    # the one-launch option does not apply to rows this wide: the same two passes run
+    one = gpu_lib.rmsnorm_nvfp4q(*args, one_launch=True, **kw)
+    for k in valid:
+        assert np.array_equal(u8(one, k), u8(got, k)), k
+    # given the amax it found, the single-pass encode gives the same y, codes and scales
+    giv = gpu_lib.rmsnorm_nvfp4q(*args, amax=got["amax"].clone(), **kw)
+    for k in ("y", "codes", "scales"):
+        assert np.array_equal(u8(giv, k), u8(got, k)), k
+
+
+def test_rmsnorm_wide_rows_fp16(gpu_lib):
+    """fp16 rows of 24576 with a bias, against the oracle in fp16 (reading R-dtype)."""
+    test_rmsnorm_fp16_fp32_inputs(gpu_lib, "float16", (3, 24576), True, 0.0, "sr")
+
+
 @pytest.mark.parametrize("shape,bias,woff,rounding", [((24579, 32), False, 0.0, "rtne"), ((8197, 1040), True, 1.0, "sr"),
                                                       ((8197, 1040), False, 1.0, "rtne")])
 def test_rmsnorm_many_rows_per_wave(gpu_lib, shape, bias, woff, rounding):
