@@ -356,8 +356,8 @@ def cpu_baseline(case, budget_s=12.0):
 # encode that a given amax selects, since the full step's encode pass reads the
 # amax pass's per-row 1/rms). "step": both passes timed together.
 DOMINANT = {
-    "prefill": ("stage", "k_rms_coop (encode mode)", r"k_rms_coop<\d+, \d+, \w+, \w+, 1, \w+(, \d+)?>"),
-    "decode": ("stage", "k_rms_coop (encode mode)", r"k_rms_coop<\d+, \d+, \w+, \w+, 1, \w+(, \d+)?>"),
+    "prefill": ("stage", "k_rms_coop (encode mode)", r"k_rms_coop<\d+, \d+, \w+, \w+, 1, \w+(, \d+)?(, \w+)?>"),
+    "decode": ("stage", "k_rms_coop (encode mode)", r"k_rms_coop<\d+, \d+, \w+, \w+, 1, \w+(, \d+)?(, \w+)?>"),
     "quantize": ("stage", "k_quant_rows", r"k_quant_rows"),
     "weight": ("stage", "k_quant_2d", r"k_quant_2d"),
     "experts": ("stage", "k_quant_2d", r"k_quant_2d"),
