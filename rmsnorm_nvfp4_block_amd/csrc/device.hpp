@@ -59,13 +59,32 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// float32 rounded to nearest even in bf16, returned as float32: the same
+// conversion with +0 in the low half leaves exactly the bf16 value's float32
+// bits (one instruction, where packing a pair and widening both halves takes
+// three for two values).
+__device__ __forceinline__ float bf16_round(float a) {
+  f32x2 v = {0.0f, a};
+  return __builtin_bit_cast(float, __builtin_convertvector(v, bf16x2));
+}
+
+// A 64-bit value that is the same for every lane, kept in scalar registers
+// (the compiler otherwise folds a row's offset into per-lane 64-bit address
+// math).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ---------------------------------------------------------------- FP8 / FP4
 // E4M3 code of a non-negative float: round to nearest even, saturating at 448.
 // v_cvt_pk_fp8_f32 rounds to nearest even over [0, 448] including subnormals
 // (checked exhaustively); the clamp supplies the saturation.
 __device__ __forceinline__ uint32_t e4m3_code(float s) {
   s = fminf(s, 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s, s, 0, false) & 0xFFu;
+  // both halves of the destination word are written: any `old` value serves (s's bits: no zero to copy)
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s, s, __float_as_int(s), false) & 0xFFu;
 }
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
   return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);

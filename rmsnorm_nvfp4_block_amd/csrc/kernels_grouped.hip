@@ -240,9 +240,8 @@ __device__ __forceinline__ void column_signed(const Tile<CPL, DT>& r, int c, uin
 template <int DT>
 __device__ __forceinline__ void round_through2(float& a, float& b) {
   if constexpr (DT == kInBF16) {
-    const uint32_t p = pack_bf16(a, b);
-    a = bf_lo(p);
-    b = bf_hi(p);
+    a = bf16_round(a);
+    b = bf16_round(b);
   } else if constexpr (DT == kInFP16) {
     a = (float)(_Float16)a;
     b = (float)(_Float16)b;
@@ -482,10 +481,8 @@ __device__ __forceinline__ void encode_columns(Tile<CPL, DT>& r, uint32_t mask, 
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           if constexpr (DT == kInBF16) {
-            const uint32_t p =
-                FOLD ? pack_bf16(v16[i], v16[i + 1]) : pack_bf16(v16[i] * 0.25f, v16[i + 1] * 0.25f);
-            v16[i] = bf_lo(p);
-            v16[i + 1] = bf_hi(p);
+            v16[i] = bf16_round(FOLD ? v16[i] : v16[i] * 0.25f);
+            v16[i + 1] = bf16_round(FOLD ? v16[i + 1] : v16[i + 1] * 0.25f);
           } else {
             float a = v16[i] * 0.25f, b = v16[i + 1] * 0.25f;
             round_through2<DT>(a, b);

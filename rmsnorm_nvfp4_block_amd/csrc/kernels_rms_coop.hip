@@ -19,6 +19,8 @@
 // "CuTeDSL at Perplexity", QK Norm (the normalization: r = 1/sqrt(mean x^2 +
 // eps), y = RN((gamma + c) x r) [+ beta]) and Prefill and decode (one token
 // row per thread group, reductions kept inside the group).
+#include <type_traits>
+
 #include "rows.hpp"
 
 namespace nvfp4q {
@@ -64,7 +66,9 @@ __device__ __forceinline__ void block_params(const RowArgs& a, const float* gsh,
 
 // One row: partial sums of squares, the barrier, 1/rms, then the mode's work.
 // Returns the contribution to the amax pass's maximum (kCoopAmax).
-template <int NPW, bool FULL, bool BIAS, int MODE, bool SR, int T, bool PG>
+// Y: y is stored (a compile-time choice: encode mode when y is asked for,
+// y-only mode always).
+template <int NPW, bool FULL, bool BIAS, int MODE, bool SR, int T, bool PG, bool Y>
 __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32_t k, const Raw16<T> (&q)[NPW],
                                           float (*ssp)[kWavesPerWG], const float* gsh, const float* bsh, GScale g,
                                           const float* rcp_tab, float inv_k, uint32_t wid, int lane, uint32_t cols) {
@@ -117,15 +121,17 @@ __device__ __forceinline__ float coop_row(const RowArgs& a, uint32_t row, uint32
       mrow = fmaxf(mrow, max16_abs(v));
     } else {
       // y rounded in the input's type, stored when asked for; the quantizer takes the rounded values
-      void* yp = a.y != nullptr ? (char*)a.y + ((int64_t)row * a.ld_y + col) * in_size<T>() : nullptr;
-      round_store16<T>(v, yp, 0u, a.y != nullptr && ok);
+      if constexpr (Y) round_store16<T>(v, (char*)a.y + ((int64_t)row * a.ld_y + col) * in_size<T>(), 0u, ok);
+      else round16<T>(v);
       if constexpr (MODE == kCoopEncode) {
         uint32_t sc;
         const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)row * nbr + (col >> 4), a.seed, a.offset, 0);
         if (ok) {
+          // the row's plane addresses kept scalar, the lane's part a 32-bit offset
+          const int64_t coff = uniform_i64((int64_t)row * a.ldc), soff = uniform_i64((int64_t)row * a.lds);
           __builtin_nontemporal_store((uint64_t)w.x | ((uint64_t)w.y << 32),
-                                      reinterpret_cast<uint64_t*>(a.codes + (int64_t)row * a.ldc + (col >> 1)));
-          __builtin_nontemporal_store((uint8_t)sc, a.scales + (int64_t)row * a.lds + (col >> 4));
+                                      reinterpret_cast<uint64_t*>(a.codes + coff + (col >> 1)));
+          __builtin_nontemporal_store((uint8_t)sc, a.scales + soff + (col >> 4));
         }
       }
     }
@@ -169,26 +175,35 @@ __global__ __launch_bounds__(kThreads) void k_rms_coop(const RowArgs a) {
   else __syncthreads();
   const float inv_k = 1.0f / (float)cols;
   float mloc = 0.0f;
-  for (uint32_t k = 0; k < nr; k += D) {
-    if (k + D < nr) {
-      // a slot is refilled (row k + D + d, clamped) as soon as its row is done
+  // the rows, with y stored or not as a compile-time choice (the encode mode
+  // takes y only when asked; the y-only mode always stores it)
+  auto rows_loop = [&](auto ytag) {
+    constexpr bool Y = decltype(ytag)::value;
+    for (uint32_t k = 0; k < nr; k += D) {
+      if (k + D < nr) {
+        // a slot is refilled (row k + D + d, clamped) as soon as its row is done
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const uint32_t kk = k + d;
-        mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T, PG>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g, rcp_tab,
-                                                               inv_k, wid, lane, cols));
-        coop_load<NPW, FULL, T>(a, kk + D < nr ? b + (kk + D) * G : last, wid, lane, cols, ring[d]);
-      }
-    } else {
+        for (int d = 0; d < D; ++d) {
+          const uint32_t kk = k + d;
+          mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T, PG, Y>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g,
+                                                                        rcp_tab, inv_k, wid, lane, cols));
+          coop_load<NPW, FULL, T>(a, kk + D < nr ? b + (kk + D) * G : last, wid, lane, cols, ring[d]);
+        }
+      } else {
 #pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const uint32_t kk = k + d;
-        if (kk < nr)
-          mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T, PG>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g,
-                                                                 rcp_tab, inv_k, wid, lane, cols));
+        for (int d = 0; d < D; ++d) {
+          const uint32_t kk = k + d;
+          if (kk < nr)
+            mloc = fmaxf(mloc, coop_row<NPW, FULL, BIAS, MODE, SR, T, PG, Y>(a, b + kk * G, kk, ring[d], ssp, gsh, bsh, g,
+                                                                          rcp_tab, inv_k, wid, lane, cols));
+        }
       }
     }
-  }
+  };
+  if constexpr (MODE == kCoopYOnly) rows_loop(std::true_type{});
+  else if constexpr (MODE == kCoopAmax) rows_loop(std::false_type{});
+  else if (a.y != nullptr) rows_loop(std::true_type{});
+  else rows_loop(std::false_type{});
   if constexpr (MODE == kCoopAmax) {
     // max |bf16(y)| = bf16(max |y|): round-to-nearest-even is monotone.
     publish_partial(a.ws, round_t<T>(mloc));

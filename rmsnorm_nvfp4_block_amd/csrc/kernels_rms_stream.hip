@@ -33,6 +33,8 @@
 //
 // "CuTeDSL at Perplexity", QK Norm (the normalization) and grid
 // synchronization (the kernel boundary between the amax and the encode pass).
+#include <type_traits>
+
 #include "rows.hpp"
 
 namespace nvfp4q {
@@ -189,11 +191,16 @@ __global__ __launch_bounds__(kThreads) void k_rms_amax_stream(const RowArgs a) {
 // ------------------------------------------------------------------ encode pass
 // y = v rounded to nearest even in T, stored at (row, col) of y when y is
 // asked for and the block is inside the row; v becomes the rounded values.
-template <int T>
+// (Y: y is asked for, a compile-time choice of the caller.)
+template <int T, bool Y>
 __device__ __forceinline__ void round_y(const RowArgs& a, float (&v)[16], uint32_t row, uint32_t col, bool ok) {
+  if constexpr (!Y) {
+    round16<T>(v);
+    return;
+  }
   if constexpr (T == kInBF16) {
     const uint4 y0 = pack8_bf16(v), y1 = pack8_bf16(v + 8);
-    if (a.y != nullptr && ok) {
+    if (ok) {
       uint16_t* yr = (uint16_t*)a.y + (int64_t)row * a.ld_y + col;
       *reinterpret_cast<uint4*>(yr) = y0;
       *reinterpret_cast<uint4*>(yr + 8) = y1;
@@ -201,8 +208,7 @@ __device__ __forceinline__ void round_y(const RowArgs& a, float (&v)[16], uint32
     widen8(y0, v);
     widen8(y1, v + 8);
   } else {
-    void* yp = a.y != nullptr ? (char*)a.y + ((int64_t)row * a.ld_y + col) * in_size<T>() : nullptr;
-    round_store16<T>(v, yp, 0u, a.y != nullptr && ok);
+    round_store16<T>(v, (char*)a.y + ((int64_t)row * a.ld_y + col) * in_size<T>(), 0u, ok);
   }
 }
 
@@ -227,7 +233,8 @@ __device__ __forceinline__ void quant_item(const RowArgs& a, float (&v)[16], uin
     for (int k = 0; k < 16; ++k) v[k] = v[k] * r;
   }
   // y rounded in T, stored when asked for; the quantizer takes the rounded values
-  round_y<T>(a, v, row, col, ok);
+  if (a.y != nullptr) round_y<T, true>(a, v, row, col, ok);
+  else round_y<T, false>(a, v, row, col, ok);
   uint32_t sc;
   const uint2 w = encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)row * (cols >> 4) + (col >> 4), a.seed, a.offset, 0);
   if (ok) {
@@ -237,7 +244,7 @@ __device__ __forceinline__ void quant_item(const RowArgs& a, float (&v)[16], uin
 }
 
 // One block of the row-per-wave encode pass (gamma + c and beta from LDS).
-template <bool FULL, bool BIAS, bool SR, int T>
+template <bool FULL, bool BIAS, bool SR, int T, bool Y>
 __device__ __forceinline__ void quant_item_rw(const RowArgs& a, const Raw16<T>& b, const Cursor& pc, float r_lane,
                                            const float* gsh, const float* bsh, GScale g, const float* rcp_tab,
                                            uint32_t cols, int lane) {
@@ -259,7 +266,7 @@ __device__ __forceinline__ void quant_item_rw(const RowArgs& a, const Raw16<T>& 
 #pragma unroll
     for (int k = 0; k < 16; ++k) v[k] = v[k] * r;
   }
-  round_y<T>(a, v, pc.row, col, ok);
+  round_y<T, Y>(a, v, pc.row, col, ok);
   uint32_t sc;
   const uint2 w =
       encode_block16<SR>(v, g, rcp_tab, sc, (uint64_t)pc.row * (cols >> 4) + (col >> 4), a.seed, a.offset, 0);
@@ -298,24 +305,30 @@ __global__ __launch_bounds__(kThreads) void k_rms_quant_rowwave(const RowArgs a)
   stage_finish<BIAS, T>(pp, a, cols, gsh, bsh);
   const GScale g = partials_finish(pm, a.ws, a.nparts, a.amax_in, a.amax_out, a.scale_out, rcp_tab);
   Cursor pc{wave, 0, 0};
-  for (uint32_t base = 0; base < n; base += kDepth) {
-    if (base + kDepth < n) {
+  // the items, with y stored or not as a compile-time choice
+  auto items = [&](auto ytag) {
+    constexpr bool Y = decltype(ytag)::value;
+    for (uint32_t base = 0; base < n; base += kDepth) {
+      if (base + kDepth < n) {
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        quant_item_rw<FULL, BIAS, SR, T>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
-        refill<FULL, T>(a, ring[d], ld, base + kDepth + d, n, nsc, nwaves, cols, lane);
-        pc.next(nsc, nwaves);
-      }
-    } else {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        if (base + d < n) {
-          quant_item_rw<FULL, BIAS, SR, T>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
+        for (int d = 0; d < kDepth; ++d) {
+          quant_item_rw<FULL, BIAS, SR, T, Y>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
+          refill<FULL, T>(a, ring[d], ld, base + kDepth + d, n, nsc, nwaves, cols, lane);
           pc.next(nsc, nwaves);
+        }
+      } else {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+          if (base + d < n) {
+            quant_item_rw<FULL, BIAS, SR, T, Y>(a, ring[d], pc, r_lane, gsh, bsh, g, rcp_tab, cols, lane);
+            pc.next(nsc, nwaves);
+          }
         }
       }
     }
-  }
+  };
+  if (a.y != nullptr) items(std::true_type{});
+  else items(std::false_type{});
 }
 
 // Encode pass, one superchunk column per wave (for few rows: decode-sized

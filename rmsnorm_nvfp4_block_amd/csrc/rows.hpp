@@ -75,6 +75,17 @@ __device__ __forceinline__ void load8_t(const void* p, uint32_t i, float v[8]) {
   }
 }
 
+// 16 fp32 values rounded to nearest even in type T (fp32: unchanged), in place,
+// when the rounded values are not stored.
+template <int T>
+__device__ __forceinline__ void round16(float v[16]) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if constexpr (T == kInBF16) v[k] = bf16_round(v[k]);
+    else if constexpr (T == kInFP16) v[k] = (float)(_Float16)v[k];
+  }
+}
+
 // 16 fp32 values rounded to nearest even in type T (fp32: unchanged), stored at
 // element index i of p when ok, and returned as fp32 in v (the rounded values).
 template <int T>
