@@ -240,6 +240,54 @@ def time_steps(case, steps, warmup, given=None, eager=False, passes=3):
     return sorted(per_pass)[len(per_pass) // 2], per_pass
 
 
+def compare_builds(case, libs, steps, warmup, reps, stage=False):
+    """Median us per step of each library build on the same case, in one process: the library is swapped
+    in the binding, a warm-up graph and a timed graph of `steps` steps are captured per library, and the
+    timed replays alternate between libraries `reps` times (order reversed every other round), so that
+    slow drifts of the box fall on every build alike. Box-to-box spread is several percent; the spread
+    within one such run is well under one."""
+    import statistics
+
+    torch, q = case.torch, case.q
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for lp in libs:
+        q._lib = None
+        q.lib_path = os.path.abspath(lp)
+        q.load()
+        with torch.cuda.stream(s):
+            given = case.given(case.step(0)) if stage else None
+            for i in range(3):
+                case.step(i, given)
+            torch.cuda.synchronize()
+            gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gw, stream=s):
+                for i in range(max(warmup, 1)):
+                    case.step(i, given)
+            with torch.cuda.graph(gt, stream=s):
+                for i in range(steps):
+                    case.step(i, given)
+            torch.cuda.synchronize()
+        graphs.append((lp, gw, gt))
+    times = {lp: [] for lp in libs}
+    with torch.cuda.stream(s):
+        for r in range(reps):
+            for lp, gw, gt in (graphs if r % 2 == 0 else graphs[::-1]):
+                gw.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                gt.replay()
+                e1.record(s)
+                torch.cuda.synchronize()
+                times[lp].append(e0.elapsed_time(e1) / steps * 1e3)
+    print(json.dumps({"compare": case.describe()["workload"], "timed": "roofline kernel, given amax" if stage
+                      else "full step", "unit": "us per step", "steps": steps, "reps": reps,
+                      "median": {lp: round(statistics.median(v), 3) for lp, v in times.items()},
+                      "all": {lp: [round(x, 3) for x in v] for lp, v in times.items()}}))
+
+
 def cpu_model():
     """The host CPU's model name, from /proc/cpuinfo."""
     try:
@@ -744,6 +792,11 @@ def main():
     ap.add_argument("--ingest-copy", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="record the copy calibration from two rocprofv3 --pmc runs of --copy-calibration")
     ap.add_argument("--command", default="", help="the command the ingested counter runs used")
+    ap.add_argument("--compare", nargs="+", metavar="LIB",
+                    help="time this build's library against other builds of it (paths to libnvfp4q.so) in one "
+                         "process: a graph per library, replays alternated --reps times (with --stage-only: "
+                         "the roofline kernel with a given amax); one JSON line of per-library medians")
+    ap.add_argument("--reps", type=int, default=9, help="--compare: alternated replays per library")
     args = ap.parse_args()
 
     if args.ingest_pmc:
@@ -793,6 +846,10 @@ def main():
     log(f"[bench] {case.describe()}")
 
     how, kname, _ = DOMINANT[args.config]
+    if args.compare:
+        compare_builds(case, [q.lib_path] + args.compare, args.steps, args.warmup, args.reps,
+                       stage=args.stage_only and how == "stage")
+        return
     if args.stage_only:
         # for a kernel trace of the roofline kernel alone: one eager call for the amax, then its graph
         if how != "stage":
