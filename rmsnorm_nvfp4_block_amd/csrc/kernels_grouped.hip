@@ -711,9 +711,11 @@ __global__ __launch_bounds__(kQuantThreads) void k_grouped_quant(const void* __r
 int64_t grouped_blocks(int64_t rows, int groups) { return (rows + 15 * (int64_t)groups) / 16; }
 
 // Columns per lane: the amax pass 4 (65 registers, many waves per SIMD for
-// its loads), the encode 8 (measured on the 16384 x 7168 workload: the 4/4,
-// 4/8, 8/4 and 8/8 pairs were within 2 us, 4/8 fastest).
-constexpr int kCplAmax = 4, kCplQuant = 8;
+// its loads); the encode 4 for the columnwise plane alone (87 registers, five
+// waves per SIMD: on the 16384 x 7168 workload the encode alone takes
+// 74.0 us against 76.4 us with 8, the full step the same) and 8 when it also
+// writes the rowwise plane (a lane pair's 16 columns form one rowwise block).
+constexpr int kCplAmax = 4, kCplQuant = 4, kCplQuantRows = 8;
 
 template <int CPL>
 uint32_t tiles_of(int64_t cols) { return (uint32_t)((cols + 32 * CPL - 1) / (32 * CPL)); }
@@ -768,8 +770,9 @@ void launch_planes(const GroupArgs& a, hipStream_t s) {
   if (col_amax && row_amax) launch_amax<kCplAmax, RHT, FAST, true, true, DT>(a, nb_max, s);
   else if (col_amax) launch_amax<kCplAmax, RHT, FAST, true, false, DT>(a, nb_max, s);
   else if (row_amax) launch_amax<kCplAmax, false, false, false, true, DT>(a, nb_max, s);
-  if (a.sr) launch_quant<kCplQuant, RHT, true, FAST, COL, ROW, DT>(a, nb_max, s);
-  else launch_quant<kCplQuant, RHT, false, FAST, COL, ROW, DT>(a, nb_max, s);
+  constexpr int kC = ROW ? kCplQuantRows : kCplQuant;
+  if (a.sr) launch_quant<kC, RHT, true, FAST, COL, ROW, DT>(a, nb_max, s);
+  else launch_quant<kC, RHT, false, FAST, COL, ROW, DT>(a, nb_max, s);
 }
 
 // FAST (no round-through of the transform's output) exists only with the
