@@ -480,6 +480,40 @@ def test_rmsnorm_given_amax_and_y_only(gpu_lib):
     assert np.array_equal(to_np_bf16(y_only["y"]), to_np_bf16(got["y"]))
 
 
+# The norm's codes without y output come from a separate compile-time branch of every RMSNorm encode (y is
+# rounded there without being packed for a store); they must equal, bit for bit, the codes of the same call
+# with y, which the tests above check against the oracle.
+@pytest.mark.parametrize("rows,cols,bias,dtype,rounding,given,one", [
+    (4096, 4096, False, "bfloat16", "rtne", False, False),  # streaming passes, one row per wave
+    (4096, 4096, False, "bfloat16", "rtne", True, False),   # cooperative rows, given amax
+    (2048, 8192, False, "bfloat16", "sr", True, False),     # cooperative rows, two superchunks per wave
+    (2304, 5120, True, "bfloat16", "sr", False, False),     # bias amax pass, row-per-wave encode
+    (300, 2560, True, "bfloat16", "rtne", False, False),    # few rows: superchunk-column encode
+    (8, 7168, True, "bfloat16", "rtne", False, True),       # one launch
+    (64, 20480, True, "bfloat16", "rtne", False, False),    # wide rows (parameters read where used)
+    (2048, 4096, False, "float16", "sr", False, False),
+    (1024, 3072, True, "float32", "rtne", True, False),
+])
+def test_rmsnorm_codes_without_y(gpu_lib, rows, cols, bias, dtype, rounding, given, one):
+    import torch
+
+    rng = np.random.default_rng(rows + cols)
+    tdt = getattr(torch, dtype)
+    x = torch.from_numpy(rng.standard_normal((rows, cols)).astype(np.float32)).to(tdt).cuda()
+    g = torch.from_numpy((1 + 0.1 * rng.standard_normal(cols)).astype(np.float32)).to(tdt).cuda()
+    b = torch.from_numpy((0.01 * rng.standard_normal(cols)).astype(np.float32)).to(tdt).cuda() if bias else None
+    kw = dict(eps=1e-6, rounding=rounding, seed=5, offset=3, one_launch=one)
+    with_y = gpu_lib.rmsnorm_nvfp4q(x, g, b, y_out=True, **kw)
+    if given:
+        kw["amax"] = with_y["amax"].clone()
+        with_y = gpu_lib.rmsnorm_nvfp4q(x, g, b, y_out=True, **kw)
+    no_y = gpu_lib.rmsnorm_nvfp4q(x, g, b, **kw)
+    assert torch.equal(no_y["codes"][:, : cols // 2], with_y["codes"][:, : cols // 2]), "codes differ with and without y"
+    assert torch.equal(no_y["scales"][:, : cols // 16], with_y["scales"][:, : cols // 16]), "scales differ"
+    for k in ("amax", "scale"):
+        assert torch.equal(no_y[k], with_y[k]), f"{k} differs between the calls with and without y"
+
+
 # ---------------------------------------------------------------- fp16 / fp32 inputs
 @pytest.mark.parametrize("dtype", ["float16", "float32"])
 @pytest.mark.parametrize("shape", [(1, 16), (37, 272), (256, 1024), (5, 9232)])
