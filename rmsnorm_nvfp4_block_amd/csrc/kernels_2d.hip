@@ -1,16 +1,16 @@
 // 2D NVFP4 for gfx950: rowwise and columnwise (transposed) planes of one bf16
 // tensor under one per-tensor scale, read once from HBM.
 //
-// One workgroup (256 threads) owns a 128 x 128 tile.
+// One workgroup (512 threads) owns a 128 x 128 tile.
 //  * Load: thread t reads one rowwise 16-element block (two adjacent 16-byte
-//    loads) of rows t/8 + 32j, j = 0..3, so a wave reads 8 rows x 256 B per
+//    loads) of rows t/8 + 64j, j = 0..1, so a wave reads 8 rows x 256 B per
 //    instruction pair. The block's amax, scale and codes are computed in-lane;
 //    rowwise codes leave as 8-byte stores, 64 contiguous bytes per row.
 //  * The raw tile is staged in LDS (32 KiB) with the 16-byte chunk index of a
 //    row XOR-ed by 4 * ((row / 16) mod 4), which spreads the eight 16-row
 //    blocks a wave reads at one time over all banks.
-//  * Columnwise: thread t owns columns 4 * (t / 8) .. +3 of rows
-//    16 * (t % 8) .. +15 (16 LDS reads of 8 bytes), i.e. four columnwise blocks;
+//  * Columnwise: thread t owns columns 2 * (t / 8) .. +1 of rows
+//    16 * (t % 8) .. +15 (16 LDS reads of 4 bytes), i.e. two columnwise blocks;
 //    eight consecutive threads write 64 contiguous code bytes of one plane row.
 //  * Several stacked weights (experts) in one launch: grid y is the expert;
 //    each has its own amax and SR tags 2e (rowwise) and 2e + 1 (columnwise).
