@@ -529,16 +529,20 @@ __device__ __forceinline__ void encode_item(const Item& it, Tile<CPL, DT>& r, ui
     gt.g1 = it.b1.g;
     const float a0 = gam[gt.g0], a1 = gam[gt.g1];
     gt.s0 = global_scale(a0);
-    gt.s1 = global_scale(a1);
+    // both blocks in one group (most pairs): one set of scales and one table
+    if (gt.g1 != gt.g0) gt.s1 = global_scale(a1);
+    else gt.s1 = gt.s0;
     gt.fold = kCanFold && RHT && fold_ok(a0) && fold_ok(a1);
     const float f = gt.fold ? 0.25f : 1.0f;
     // the wave's own tables: its LDS writes precede its reads
     tabs[lane] = encode_mult(lane, gt.s0.dec) * f;
     tabs[lane + 64] = encode_mult(lane + 64, gt.s0.dec) * f;
-    tabs[128 + lane] = encode_mult(lane, gt.s1.dec) * f;
-    tabs[128 + lane + 64] = encode_mult(lane + 64, gt.s1.dec) * f;
+    if (gt.g1 != gt.g0) {
+      tabs[128 + lane] = encode_mult(lane, gt.s1.dec) * f;
+      tabs[128 + lane + 64] = encode_mult(lane + 64, gt.s1.dec) * f;
+    }
   }
-  const float* tab = tabs + half * 128;
+  const float* tab = tabs + (gt.g1 != gt.g0 ? half * 128 : 0);
   const float enc = half ? gt.s1.enc : gt.s0.enc;
   const uint64_t nbp = (uint64_t)(mpad >> 4);  // blocks per plane row
   const uint64_t blk = (uint64_t)it.col * nbp + it.tb;
