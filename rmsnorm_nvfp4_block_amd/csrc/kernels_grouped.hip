@@ -56,6 +56,19 @@ constexpr int kGroupAmaxRow = kPartials - 64;
 struct GroupScan {
   int lo, n, p, ps;
 };
+// Inclusive prefix sum over the 64 lanes by DPP: shifts by 1, 2, 4 and 8
+// within each 16-lane row (lanes shifted in from outside the row add 0), then
+// each row adds the totals of the rows before it through the row broadcasts
+// (no LDS round trips, which a lane shuffle takes).
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast15, 0xA, 0xF, false);  // row 0's total into row 1, row 2's into 3
+  v += __builtin_amdgcn_update_dpp(0, v, kDppBcast31, 0xC, 0xF, false);  // rows 0-1's total into rows 2 and 3
+  return v;
+}
 __device__ __forceinline__ GroupScan group_scan(const int32_t* __restrict__ offsets, int groups, int rows) {
   const int lane = threadIdx.x & 63;
   GroupScan s;
@@ -66,12 +79,7 @@ __device__ __forceinline__ GroupScan group_scan(const int32_t* __restrict__ offs
     s.n = min(max(offsets[lane + 1], s.lo), rows) - s.lo;
   }
   s.p = (s.n + 15) & ~15;
-  s.ps = s.p;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int a = __shfl_up(s.ps, o, 64);
-    if (lane >= o) s.ps += a;
-  }
+  s.ps = wave_prefix_sum(s.p);
   return s;
 }
 
